@@ -1,0 +1,100 @@
+/*
+ * CPU oracle of the H2O decode step -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 reference of what one decode step computes for one
+ * (sequence, KV head) unit: append the new token, attend with every query
+ * head of the unit's group, add each softmax weight to the token's cumulative
+ * score, then evict down to the budget outside the sinks and the recent
+ * window (H2O) or, for Random Attention, evict generated tokens at random.
+ * Only the tests, the package's smoke check and the benchmark's CPU baseline
+ * may load it.  It shares no code with the GPU library.
+ *
+ * Sources (titles of the pages the method is described on):
+ *   "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of LLMs"
+ *       (summary page) -- the greedy step over S_{i-1} + {i} with budget K.
+ *   "Attention Sinks and KV cache eviction: why a sliding window is not
+ *       enough" -- sec. 4.1 (4 sink tokens + recent window), sec. 4.2
+ *       (cumulative score over decode steps, top-k of the middle region,
+ *       sinks + heavy hitters + recent kept).
+ *   "KV Cache compression and selective retention: StreamingLLM vs H2O"
+ *       -- the cache-manager listing (4 sinks, heavy hitters by top-k of the
+ *       middle scores, recent rows kept).
+ *   "Random Attention: rethinking KV cache eviction" -- method (prompt kept,
+ *       per-head uniform random eviction of generated tokens) and the
+ *       integration notes (period K, buffer r).
+ */
+#ifndef H2O_ORACLE_H
+#define H2O_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_H2O = 0, ORC_RANDOM = 1 };
+enum { ORC_OK = 0, ORC_EARG = -1, ORC_ECHECK = -2, ORC_ENOMEM = -3 };
+
+typedef struct {
+    int head_dim;      /* D */
+    int group;         /* G: query heads per KV head */
+    double scale;      /* logit scale; 0 -> 1/sqrt(D) */
+    int selector;      /* ORC_H2O or ORC_RANDOM */
+    int n_sink;        /* H2O: positions 0..n_sink-1 are never evicted */
+    int budget_fixed;  /* H2O: > 0 -> budget K fixed ...            */
+    int hh_fixed;      /*        ... with this many heavy hitters   */
+    int budget_num;    /* H2O: else K_t = floor(len*num/den),       */
+    int budget_den;    /*      HH_t = floor((K_t - n_sink)/2)       */
+    int rand_k;        /* Random: generated tokens kept after an event (K) */
+    int rand_r;        /* Random: buffer r; an event fires at K + r generated */
+    uint64_t seed;     /* Random: Philox key word 0 */
+} orc_cfg;
+
+typedef struct orc_unit orc_unit;
+
+/* Budget K_t, heavy hitters HH_t and recent window W_t at current length len. */
+void orc_schedule(const orc_cfg *c, int len, int *K, int *HH, int *W);
+
+/* New unit: sequence b, KV head h, prompt rows pk/pv [prompt_len][D] (fp64),
+ * optional initial scores [prompt_len]; cap = most positions it will ever see. */
+orc_unit *orc_new(const orc_cfg *c, int b, int h, int prompt_len, int cap,
+                  const double *pk, const double *pv, const double *init_scores);
+void orc_free(orc_unit *u);
+
+/* Append position t = current length, attend with q [G][D] over the retained
+ * set, write out [G][D] and (optionally) probs [G][n_att] in ascending
+ * position order, and (H2O) add the weights to the scores.  Returns n_att. */
+int orc_attend(orc_unit *u, const double *q, const double *k, const double *v,
+               double *out, double *probs);
+
+/* The victims the method picks after orc_attend, in eviction order.
+ * Returns e >= 0; *tau = score of the e-th victim (H2O; 0 if e == 0). */
+int orc_select(orc_unit *u, int32_t *victims, double *tau);
+
+/* Evict exactly these positions (the oracle's own pick, or an accepted
+ * near-tie alternative).  Each must be retained and evictable. */
+int orc_evict(orc_unit *u, const int32_t *victims, int e);
+
+/* Post-step invariants: budget, sinks, recent window / prompt, score mass. */
+int orc_check(const orc_unit *u);
+
+/* attend + select + evict + check with the oracle's own choice. */
+int orc_step(orc_unit *u, const double *q, const double *k, const double *v, double *out);
+
+/* Retained positions ascending (pos), their scores, evicted mass.  Returns count. */
+int orc_state(const orc_unit *u, int32_t *pos, double *scores, double *evicted_mass);
+
+/* Score of any position ever seen (frozen once evicted). */
+double orc_score_of(const orc_unit *u, int pos);
+int orc_length(const orc_unit *u);
+
+/* orc_step on n units, spread over nthreads POSIX threads; returns first error. */
+int orc_step_many(orc_unit **u, int n, const double *const *q, const double *const *k,
+                  const double *const *v, double *const *out, int nthreads);
+
+/* Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11). */
+void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,370 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every ``pin_*`` takes a loaded oracle library and raises AssertionError (or the
+oracle's own OracleError) when the oracle disagrees with the pin.  They are run
+on the real oracle by test_oracle_pins.py and on deliberately broken copies of
+it by test_oracle_mutants.py, which checks that each planted mistake is caught.
+
+Independent references used here: torch's scaled_dot_product_attention and
+softmax (fp64, CPU), torch.topk, numpy.lexsort, numpy.random.Philox, brute
+force over subsets, closed forms the pages state (StreamingLLM's sinks + window,
+the sliding window, full attention when nothing is evicted), and fixtures under
+tests/golden/.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+M64 = 1 << 64
+
+
+def _unit(lib, cfg, pk, pv, cap, b=0, h=0, init=None):
+    return O.Unit(cfg, b, h, pk, pv, cap, init_scores=init, lib=lib)
+
+
+def _sdpa(q, Kr, Vr, scale=None):
+    """torch fp64 attention of G queries over one shared K/V: q [G][D], Kr/Vr [n][D]."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, :, None, :]
+    G = qt.shape[1]
+    kt = torch.from_numpy(np.asarray(Kr, np.float64))[None, None].expand(1, G, -1, -1)
+    vt = torch.from_numpy(np.asarray(Vr, np.float64))[None, None].expand(1, G, -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return o[0, :, 0, :].numpy()
+
+
+def _softmax_rows(q, Kr, scale):
+    s = torch.from_numpy(np.asarray(q, np.float64)) @ torch.from_numpy(np.asarray(Kr, np.float64)).T
+    return torch.softmax(s * scale, dim=-1).numpy()
+
+
+def _philox_np(ctr, key):
+    """numpy's Philox4x64-10 block at counter ctr (numpy bumps its counter first)."""
+    c0, c1, c2, c3 = (int(x) for x in ctr)
+    v = (c0 + c1 * M64 + c2 * M64 ** 2 + c3 * M64 ** 3 - 1) % M64 ** 4
+    c = np.array([(v >> (64 * i)) % M64 for i in range(4)], dtype=np.uint64)
+    g = np.random.Philox(key=np.array([k % M64 for k in key], dtype=np.uint64), counter=c)
+    return [int(x) for x in g.random_raw(4)]
+
+
+# ---------------------------------------------------------------- attention
+def pin_attention_full_cache(lib):
+    """Budget >= length: nothing is evicted and every step is plain decode
+    attention over all positions (torch SDPA), its weights are torch softmax
+    rows, and each position's score is the sum of its weights over steps and
+    query heads."""
+    rng = np.random.default_rng(11)
+    D, G, P, steps = 16, 3, 9, 12
+    for scale in (0.0, 0.3):
+        cfg = O.make_cfg(head_dim=D, group=G, scale=scale, n_sink=4, budget_fixed=1000,
+                         hh_fixed=992)
+        pk, pv = rng.standard_normal((P, D)), rng.standard_normal((P, D))
+        u = _unit(lib, cfg, pk, pv, P + steps)
+        Kall, Vall = [*pk], [*pv]
+        acc = np.zeros(P + steps)
+        sc = scale if scale else 1.0 / np.sqrt(D)
+        for s in range(steps):
+            q = rng.standard_normal((G, D))
+            k, v = rng.standard_normal(D), rng.standard_normal(D)
+            Kall.append(k)
+            Vall.append(v)
+            out, probs = u.attend(q, k, v, want_probs=True)
+            ref = _sdpa(q, np.array(Kall), np.array(Vall), scale=scale if scale else None)
+            assert np.max(np.abs(out - ref)) < 1e-12, "attention output != torch SDPA"
+            rows = _softmax_rows(q, np.array(Kall), sc)
+            assert np.max(np.abs(probs - rows)) < 1e-14, "weights != torch softmax"
+            assert np.max(np.abs(probs.sum(axis=1) - 1.0)) < 1e-12
+            acc[:len(Kall)] += rows.sum(axis=0)
+            vic, _ = u.select()
+            assert len(vic) == 0, "evicted although budget >= length"
+            u.evict(vic)
+            u.check()
+        pos, scores, em = u.state()
+        assert list(pos) == list(range(P + steps)), "full cache lost a position"
+        assert np.max(np.abs(scores - acc)) < 1e-12, "scores != summed softmax weights"
+        assert em == 0.0
+
+
+# ------------------------------------------------- scores + selection, H2O
+def _budget_20pct(length, n_sink=4):
+    K = length // 5
+    HH = (K - n_sink) // 2
+    return K, HH, K - n_sink - HH
+
+
+def pin_scores_and_selection_recomputed(lib):
+    """20 % budget over a ragged trace: the test keeps its own scores (torch
+    softmax over the retained set, summed over the group's query heads) and its
+    own selection (numpy.lexsort: score ascending, then position descending,
+    over the candidates outside sinks and recent window).  The oracle must
+    agree on the retained set, every score and the evicted mass, and the mass
+    must add up to G * steps."""
+    rng = np.random.default_rng(12)
+    D, G, P, steps = 8, 2, 57, 41
+    cfg = O.make_cfg(head_dim=D, group=G, n_sink=4, budget_num=1, budget_den=5)
+    pk, pv = rng.standard_normal((P, D)), rng.standard_normal((P, D))
+    pk[3] += 2.5  # a heavy direction on a few keys
+    u = _unit(lib, cfg, pk, pv, P + steps)
+    Kall, live = [*pk], set(range(P))
+    score = {p: 0.0 for p in range(P)}
+    evicted = 0.0
+    scale = 1.0 / np.sqrt(D)
+    for s in range(steps):
+        t = P + s
+        q = rng.standard_normal((G, D)) + 0.5
+        k, v = rng.standard_normal(D), rng.standard_normal(D)
+        Kall.append(k)
+        live.add(t)
+        score[t] = 0.0
+        R = sorted(live)
+        rows = _softmax_rows(q, np.array([Kall[p] for p in R]), scale)
+        for i, p in enumerate(R):
+            score[p] += rows[:, i].sum()
+        out = u.attend(q, k, v)
+        length = t + 1
+        K, HH, W = _budget_20pct(length)
+        e = len(R) - K
+        vic_ref = []
+        if e > 0:
+            cands = [p for p in R if 4 <= p < length - W]
+            order = np.lexsort((-np.array(cands), np.array([score[p] for p in cands])))
+            vic_ref = [cands[i] for i in order[:e]]
+        vic, _ = u.select()
+        assert sorted(vic) == sorted(vic_ref), f"step {s}: victims differ"
+        u.evict(vic)
+        u.check()
+        for p in vic_ref:
+            live.discard(p)
+            evicted += score[p]
+        pos, sc, em = u.state()
+        assert list(pos) == sorted(live)
+        assert np.max(np.abs(sc - np.array([score[p] for p in pos]))) < 1e-12
+        assert abs(em - evicted) < 1e-12
+        assert abs(sc.sum() + em - G * (s + 1)) < 1e-9, "retained + evicted mass != G*steps"
+        assert len(pos) <= K
+
+
+def pin_streaming_llm_and_sliding_window(lib):
+    """No heavy hitters: 4 sinks + the last W positions (StreamingLLM, the
+    attention-sinks page sec. 4.1); no sinks either: the last W only (sliding
+    window, sec. 2.1).  Closed forms, whatever the values."""
+    rng = np.random.default_rng(13)
+    D, P, steps = 6, 30, 25
+    for n_sink, W in ((4, 8), (0, 10)):
+        cfg = O.make_cfg(head_dim=D, n_sink=n_sink, budget_fixed=n_sink + W, hh_fixed=0)
+        u = _unit(lib, cfg, rng.standard_normal((P, D)), rng.standard_normal((P, D)), P + steps)
+        for s in range(steps):
+            u.step(rng.standard_normal((1, D)), rng.standard_normal(D), rng.standard_normal(D))
+            length = P + s + 1
+            pos, _, _ = u.state()
+            expect = list(range(n_sink)) + list(range(length - W, length))
+            assert list(pos) == expect, f"sinks={n_sink} W={W} step {s}"
+
+
+def pin_greedy_equals_bruteforce(lib):
+    """H2O's greedy step (the H2O summary page): with an additive set score,
+    the evicted set must be the one that leaves the largest retained score.
+    Brute force over every e-subset of the candidates, on tiny inputs."""
+    rng = np.random.default_rng(14)
+    D, P, steps = 4, 12, 10
+    cfg = O.make_cfg(head_dim=D, n_sink=1, budget_fixed=8, hh_fixed=3)
+    u = _unit(lib, cfg, rng.standard_normal((P, D)), rng.standard_normal((P, D)), P + steps)
+    for s in range(steps):
+        u.attend(rng.standard_normal((1, D)) * 1.5, rng.standard_normal(D), rng.standard_normal(D))
+        length = P + s + 1
+        pos, sc, _ = u.state()
+        W = 8 - 1 - 3
+        cands = [(p, x) for p, x in zip(pos, sc) if 1 <= p < length - W]
+        e = len(pos) - 8
+        best, best_kept = None, -np.inf
+        for sub in itertools.combinations(range(len(cands)), max(e, 0)):
+            kept = sum(x for i, (_, x) in enumerate(cands) if i not in sub)
+            if kept > best_kept:
+                best, best_kept = sub, kept
+        vic, _ = u.select()
+        assert sorted(vic) == sorted(cands[i][0] for i in best), f"step {s}"
+        u.evict(vic)
+
+
+def pin_topk_middle_region(lib):
+    """The cache-manager listing of the StreamingLLM-vs-H2O article: keep the
+    first n_sink rows, the last n_recent rows and torch.topk(middle scores,
+    n_heavy) of the rows in between.  At a bulk eviction from a full prompt
+    the oracle must keep exactly that set."""
+    rng = np.random.default_rng(15)
+    D, P = 8, 40
+    cfg = O.make_cfg(head_dim=D, n_sink=4, budget_fixed=15, hh_fixed=6)
+    u = _unit(lib, cfg, rng.standard_normal((P, D)), rng.standard_normal((P, D)), P + 4,
+              init=rng.random(P))
+    u.attend(rng.standard_normal((1, D)), rng.standard_normal(D), rng.standard_normal(D))
+    pos, sc, _ = u.state()
+    length = P + 1
+    mid = torch.from_numpy(sc[4:length - 5])
+    hh = (torch.topk(mid, 6).indices + 4).tolist()
+    expect = sorted(list(range(4)) + hh + list(range(length - 5, length)))
+    vic, _ = u.select()
+    u.evict(vic)
+    pos, _, _ = u.state()
+    assert list(pos) == expect
+
+
+def pin_tie_break_lower_position_kept(lib):
+    """Equal scores: the lower position is retained (ties resolved by
+    numpy.lexsort on (score, -position)).  Identical keys give every token the
+    same weight, so all candidates tie."""
+    D, P = 4, 20
+    key = np.array([0.5, -1.0, 0.25, 2.0])
+    pk = np.tile(key, (P, 1))
+    pv = np.arange(P * D, dtype=np.float64).reshape(P, D)
+    cfg = O.make_cfg(head_dim=D, n_sink=2, budget_fixed=8, hh_fixed=3)
+    u = _unit(lib, cfg, pk, pv, P + 2)
+    u.attend(np.ones((1, D)), key, np.zeros(D))
+    pos, sc, _ = u.state()
+    assert np.all(sc == sc[0])
+    length = P + 1
+    cands = np.array([p for p in pos if 2 <= p < length - 3])
+    order = np.lexsort((-cands, sc[cands]))
+    e = len(pos) - 8
+    vic, _ = u.select()
+    assert sorted(vic) == sorted(cands[order[:e]].tolist())
+    u.evict(vic)
+    pos, _, _ = u.state()
+    assert list(pos) == [0, 1, 2, 3, 4, 18, 19, 20]
+
+
+# ------------------------------------------------------------ Random selector
+def pin_philox_matches_numpy(lib):
+    """The oracle's own Philox4x64-10 against numpy.random.Philox."""
+    for key in ([5, 0], [0xC4, 0], [2 ** 63 + 7, 99]):
+        for ctr in ([0, 0, 0, 0], [3, 7, 4223, 2050], [2 ** 64 - 1, 5, 6, 7], [31, 7, 32767, 32766]):
+            assert O.philox4x64_10(ctr, key, lib=lib) == _philox_np(ctr, key)
+
+
+def pin_random_victims_are_smallest_philox_words(lib):
+    """Random Attention: the prompt is kept; when the generated tokens reach
+    K + r, the r evicted are those with the smallest Philox word 0 at counter
+    (sequence, head, step, position), key (seed, 0) -- computed here with
+    numpy's Philox -- ties to the higher position."""
+    rng = np.random.default_rng(16)
+    D, P, Kk, r, seed = 4, 5, 6, 3, 0xC4
+    b, h = 3, 1
+    cfg = O.make_cfg(head_dim=D, group=2, selector=O.ORC_RANDOM, rand_k=Kk, rand_r=r, seed=seed)
+    u = _unit(lib, cfg, rng.standard_normal((P, D)), rng.standard_normal((P, D)), P + 40, b=b, h=h)
+    events = 0
+    for s in range(40):
+        t = P + s
+        u.attend(rng.standard_normal((2, D)), rng.standard_normal(D), rng.standard_normal(D))
+        pos, _, _ = u.state()
+        gen = [p for p in pos if p >= P]
+        vic, _ = u.select()
+        if len(gen) == Kk + r:
+            words = np.array([_philox_np([b, h, t, p], [seed, 0])[0] for p in gen], dtype=np.uint64)
+            order = np.lexsort((-np.array(gen), words))
+            assert sorted(vic) == sorted(np.array(gen)[order[:r]].tolist())
+            events += 1
+        else:
+            assert len(vic) == 0
+        u.evict(vic)
+        u.check()
+        pos, _, _ = u.state()
+        assert set(range(P)) <= set(pos), "prompt token evicted"
+        assert len([p for p in pos if p >= P]) < Kk + r
+    assert events == 11
+
+
+def pin_random_uniform_and_independent(lib):
+    """Per head, uniform: every one of the K + r candidates is evicted with
+    probability r / (K + r); two heads of one sequence choose independently
+    (expected overlap r^2 / (K + r))."""
+    D, Kk, r = 2, 12, 4
+    n_units = 1200
+    counts = np.zeros(Kk + r)
+    overlaps = []
+    cfg = O.make_cfg(head_dim=D, selector=O.ORC_RANDOM, rand_k=Kk, rand_r=r, seed=77)
+    z = np.zeros(D)
+    for b in range(n_units // 2):
+        sets = []
+        for h in range(2):
+            u = _unit(lib, cfg, np.zeros((1, D)), np.zeros((1, D)), Kk + r + 2, b=b, h=h)
+            for s in range(Kk + r):
+                u.attend(np.zeros((1, D)), z, z)
+            vic, _ = u.select()
+            assert len(vic) == r
+            counts[np.asarray(vic) - 1] += 1
+            sets.append(set(vic.tolist()))
+        overlaps.append(len(sets[0] & sets[1]))
+    p = r / (Kk + r)
+    expect = n_units * p
+    sd = np.sqrt(n_units * p * (1 - p))
+    assert np.all(np.abs(counts - expect) < 5 * sd), counts
+    chi2 = float(np.sum((counts - expect) ** 2 / (expect * (1 - p))))
+    assert chi2 < 45.0, chi2  # 15 dof; p ~ 1e-4
+    mean_overlap = np.mean(overlaps)
+    hyper_sd = np.sqrt(r * p * (1 - p) * (Kk / (Kk + r - 1)) / len(overlaps))
+    assert abs(mean_overlap - r * p) < 5 * hyper_sd, mean_overlap
+
+
+# ------------------------------------------------------------- golden files
+def pin_golden_streaming_layout(lib):
+    """tests/golden/streaming_llm_layout.json: the sink + window layout the
+    attention-sinks page draws in sec. 4.1."""
+    with open(os.path.join(GOLDEN, "streaming_llm_layout.json")) as f:
+        g = json.load(f)
+    rng = np.random.default_rng(17)
+    D, N, W, S = 4, g["length"], g["window"], g["n_sink"]
+    P = N - 1
+    cfg = O.make_cfg(head_dim=D, n_sink=S, budget_fixed=S + W, hh_fixed=0)
+    u = _unit(lib, cfg, rng.standard_normal((P, D)), rng.standard_normal((P, D)), N)
+    u.step(rng.standard_normal((1, D)), rng.standard_normal(D), rng.standard_normal(D))
+    pos, _, _ = u.state()
+    assert list(pos) == g["retained"]
+
+
+def pin_golden_cache_manager_sizes(lib):
+    """tests/golden/cache_manager_defaults.json: the StreamingLLM-vs-H2O
+    article's manager (4 sinks, 512 heavy hitters, 512 recent) leaves the
+    cache unchanged while the length is within 4 + 512 + 512, and past it
+    keeps exactly 4 sink, 512 heavy-hitter and 512 recent rows."""
+    with open(os.path.join(GOLDEN, "cache_manager_defaults.json")) as f:
+        g = json.load(f)
+    S, HH, R = g["num_sink_tokens"], g["num_heavy_hitters"], g["num_recent_tokens"]
+    cap = g["max_capacity"]
+    rng = np.random.default_rng(18)
+    D = 2
+    P = cap - 1
+    cfg = O.make_cfg(head_dim=D, n_sink=S, budget_fixed=cap, hh_fixed=HH)
+    u = _unit(lib, cfg, rng.standard_normal((P, D)), rng.standard_normal((P, D)), cap + 3)
+    u.step(rng.standard_normal((1, D)), rng.standard_normal(D), rng.standard_normal(D))
+    pos, _, _ = u.state()
+    assert list(pos) == list(range(cap)), "evicted at length == capacity"
+    for _ in range(2):
+        u.step(rng.standard_normal((1, D)), rng.standard_normal(D), rng.standard_normal(D))
+        length = u.length()
+        pos, _, _ = u.state()
+        assert len(pos) == cap
+        sinks = [p for p in pos if p < S]
+        recent = [p for p in pos if p >= length - R]
+        heavy = [p for p in pos if S <= p < length - R]
+        assert (len(sinks), len(heavy), len(recent)) == tuple(g["layout_sizes"])
+
+
+ALL_PINS = [
+    pin_attention_full_cache,
+    pin_scores_and_selection_recomputed,
+    pin_streaming_llm_and_sliding_window,
+    pin_greedy_equals_bruteforce,
+    pin_topk_middle_region,
+    pin_tie_break_lower_position_kept,
+    pin_philox_matches_numpy,
+    pin_random_victims_are_smallest_philox_words,
+    pin_random_uniform_and_independent,
+    pin_golden_streaming_layout,
+    pin_golden_cache_manager_sizes,
+]

@@ -1,0 +1,71 @@
+"""Plant mistakes in copies of the oracle (CPU only) and check the pins catch each.
+
+Every mutant is the oracle source with one plausible slip -- a dropped term, a
+wrong sign or index, a swapped operand, a reversed tie rule, an off-by-one in
+the window -- compiled to a temporary library.  At least one pin in
+oracle_pins.ALL_PINS must fail on it; otherwise the pins would not notice that
+mistake in the real oracle either.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle as O
+import oracle_pins as P
+from oracle.build import CFLAGS, HERE
+
+SRC = os.path.join(HERE, "h2o_oracle.c")
+
+MUTANTS = {
+    "drop_scale": ("s *= u->c.scale;", ""),
+    "softmax_sign": ("exp(u->w[i] - m)", "exp(m - u->w[i])"),
+    "value_rows_are_keys": ("const double *vj = u->V +", "const double *vj = u->K +"),
+    "slot_index_for_position": ("const double *kj = u->K + (size_t)u->R[i] * D;",
+                                "const double *kj = u->K + (size_t)i * D;"),
+    "score_only_first_query_head": ("if (u->c.selector == ORC_H2O)\n            for (int i = 0; i < n; ++i) u->score",
+                                    "if (u->c.selector == ORC_H2O && g == 0)\n            for (int i = 0; i < n; ++i) u->score"),
+    "score_missing_new_token": ("for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];",
+                                "for (int i = 0; i < n - 1; ++i) u->score[u->R[i]] += u->w[i];"),
+    "tie_keeps_higher_position": ("    return (x->pos > y->pos) ? -1 : (x->pos < y->pos) ? 1 : 0;\n}\n\nstatic int cmp_key",
+                                  "    return (x->pos < y->pos) ? -1 : (x->pos > y->pos) ? 1 : 0;\n}\n\nstatic int cmp_key"),
+    "evict_highest_score": ("    if (x->score < y->score) return -1;\n    if (x->score > y->score) return 1;",
+                            "    if (x->score > y->score) return -1;\n    if (x->score < y->score) return 1;"),
+    "recent_window_off_by_one": ("if (p >= u->c.n_sink && p < len - W) {", "if (p >= u->c.n_sink && p <= len - W) {"),
+    "sink_off_by_one": ("if (p >= u->c.n_sink && p < len - W) {", "if (p > u->c.n_sink && p < len - W) {"),
+    "evict_count_off_by_one": ("        e = n - K;\n", "        e = n - K - 1;\n"),
+    "hh_split_rounds_up": ("hh = (k - c->n_sink) / 2;", "hh = (k - c->n_sink + 1) / 2;"),
+    "philox_key_word": ("uint64_t y0 = hi1 ^ x1 ^ k0", "uint64_t y0 = hi1 ^ x1 ^ k1"),
+    "philox_weyl_before_first_round": ("        if (r > 0) {\n            k0 += W0;", "        if (r >= 0) {\n            k0 += W0;"),
+    "random_evicts_prompt": ("if (u->R[i] >= u->prompt_len) {", "if (u->R[i] >= 0) {"),
+    "random_counter_step_word": ("(uint64_t)u->h, (uint64_t)t,", "(uint64_t)u->h, (uint64_t)(t + 1),"),
+    "random_largest_words": ("    if (x->key < y->key) return -1;\n    if (x->key > y->key) return 1;",
+                             "    if (x->key > y->key) return -1;\n    if (x->key < y->key) return 1;"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    d = tmp_path_factory.mktemp("oracle_mutants")
+    shutil.copy(os.path.join(HERE, "h2o_oracle.h"), d / "h2o_oracle.h")
+    return d
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique in the oracle"
+    path = mutant_dir / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib_path = str(mutant_dir / f"lib{name}.so")
+    subprocess.run(["gcc", *CFLAGS, "-I", str(mutant_dir), "-o", lib_path, str(path), "-lm"],
+                   check=True, capture_output=True)
+    lib = O.load(lib_path)
+    for pin in P.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, O.OracleError):
+            return
+    pytest.fail(f"no pin caught mutant {name}")
