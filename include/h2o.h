@@ -1,0 +1,157 @@
+/*
+ * h2o.h -- C ABI of the MI355X (gfx950) H2O decode-step library (libh2o.so).
+ *
+ * One decode step for a batch of sequences, per (sequence b, KV head h):
+ *   a1 append   the new token's key/value becomes a retained slot;
+ *   a2-a4       its G query heads attend over the retained keys/values
+ *               (q.K, softmax, P.V);
+ *   a5 (H2O)    every softmax weight is added to its token's cumulative score,
+ *               the G weights of a GQA group summed into the shared KV head;
+ *   a6 select   H2O: the lowest-score tokens outside the sink tokens and the
+ *               recent window are evicted down to the budget K_t;
+ *               Random Attention: when the retained generated tokens reach
+ *               K + r, r of them are evicted uniformly at random per head
+ *               (the prompt is never evicted);
+ *   a7 compact  the retained slots are made contiguous again in place
+ *               (paged layout: whole 16-token pages are released).
+ *
+ * Where the operation is defined (titles of the pages describing the method):
+ *   "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of LLMs",
+ *       summary -- budget K, the greedy eviction over S_{i-1} + {i} by
+ *       cumulative attention (Algorithm 1 as summarised there).
+ *   "Attention Sinks and KV cache eviction: why a sliding window is not
+ *       enough" -- sec. 3.1 (softmax weights of one query sum to one),
+ *       sec. 4.1 (four sink tokens kept for good), sec. 4.2 (scores summed
+ *       over decode steps; sinks + top-k heavy hitters + recent window kept),
+ *       sec. 5 (16-token KV blocks), sec. 6.2 (per-token fp32 score state).
+ *   "KV Cache compression and selective retention: StreamingLLM vs H2O" --
+ *       cache-manager listing: evict(key_cache, value_cache, scores) with
+ *       4 sinks + heavy hitters + recent rows, [B, H, S, D] layout.
+ *   "Random Attention: rethinking KV cache eviction" -- method modules 1-3
+ *       and the integration notes (keep the prompt; per-head uniform random
+ *       eviction; eviction period K and buffer r).
+ *
+ * Conventions
+ *   - Every call except h2o_read_indices and h2o_destroy is asynchronous on
+ *     `stream` (a hipStream_t; NULL = the device's null stream).  Pointers
+ *     named "device" must stay valid until the stream has run the work.
+ *   - Layouts (row-major): q and out [B][Hq][D] fp32; k_new, v_new
+ *     [B][Hkv][D] in kv_dtype (bf16 = raw bf16 bits); query head j belongs to
+ *     KV head j / G, G = Hq / Hkv.
+ *   - Positions: sequence b's prompt holds positions 0..P_b-1; its s-th
+ *     decode step (s = 0, 1, ...) appends position t = P_b + s.  All sequences
+ *     step together.
+ *   - Supported shapes: (kv_dtype, head_dim) = (H2O_BF16, 128) or
+ *     (H2O_F32, 64); G in {1, 2, 4, 8}.
+ *   - Errors: every call returns an h2o_status.  Arguments are validated
+ *     before anything is enqueued; on error nothing is enqueued and the
+ *     context is unchanged (H2O_EDEVICE aside).  h2o_last_error() gives the
+ *     message.  One context must not be used from two threads at once;
+ *     different contexts are independent.
+ *   - Ownership: the library owns the context and all its device state
+ *     (allocated with hipMalloc on the device current at h2o_init);
+ *     h2o_destroy frees it.  The caller owns every pointer it passes.
+ */
+#ifndef H2O_H
+#define H2O_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct h2o_ctx h2o_ctx;
+
+typedef enum {
+    H2O_OK = 0,
+    H2O_EINVAL = -1,   /* bad argument or unsupported configuration */
+    H2O_ENOMEM = -2,   /* device memory or KV page pool exhausted */
+    H2O_EDEVICE = -3,  /* a HIP call failed (message kept) */
+    H2O_ESTATE = -4    /* call out of order (e.g. h2o_step while a compaction is pending) */
+} h2o_status;
+
+enum { H2O_SEL_H2O = 0, H2O_SEL_RANDOM = 1 };
+enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F64 = 2 };
+
+typedef struct {
+    int32_t batch;         /* B sequences */
+    int32_t n_q_heads;     /* Hq */
+    int32_t n_kv_heads;    /* Hkv; Hq must be a multiple */
+    int32_t head_dim;      /* D */
+    int32_t kv_dtype;      /* H2O_BF16 or H2O_F32 */
+    int32_t score_dtype;   /* H2O: H2O_F32 or H2O_F64 cumulative scores */
+    float scale;           /* logit scale; 0 -> 1/sqrt(D) */
+    int32_t selector;      /* H2O_SEL_H2O or H2O_SEL_RANDOM */
+    int32_t n_sink;        /* H2O: positions 0..n_sink-1 are never evicted (4 on the pages) */
+    int32_t budget_fixed;  /* H2O: > 0 -> fixed budget K ...                          */
+    int32_t hh_fixed;      /*        ... of which hh_fixed heavy hitters; recent window
+                                     W = K - n_sink - hh_fixed                         */
+    int32_t budget_num;    /* H2O: else K_t = floor(len * num / den) with len = t + 1, */
+    int32_t budget_den;    /*      HH_t = floor((K_t - n_sink) / 2), W_t = the rest    */
+    int32_t rand_k;        /* Random: generated tokens kept after an eviction (K) */
+    int32_t rand_r;        /* Random: buffer r; r tokens are evicted at K + r */
+    uint64_t seed;         /* Random: Philox4x64-10 key word 0 */
+    int32_t page_size;     /* 0 = contiguous slots per (b, h); 16 = paged */
+    int32_t max_pages;     /* paged: size of the page pool (pages of Hkv x 16 tokens) */
+    int32_t max_len;       /* most positions any sequence will reach (prompt + steps) */
+} h2o_config;
+
+/* Create a context and load the prompts.
+ *   prompt_len  host [B]: P_b >= 1.
+ *   prompt_k/v  device, packed [sum_b P_b][Hkv][D] in kv_dtype, sequences in order.
+ *   init_scores device [sum_b P_b][Hkv] fp64 initial cumulative scores, or NULL = 0.
+ * The prompts are copied; the caller may reuse its buffers once the stream has
+ * run the copy.  On success *out receives the context.
+ * Errors: H2O_EINVAL (config/shape), H2O_ENOMEM (device memory or page pool),
+ * H2O_EDEVICE. */
+int h2o_init(h2o_ctx **out, const h2o_config *cfg, const int32_t *prompt_len,
+             const void *prompt_k, const void *prompt_v, const double *init_scores,
+             void *stream);
+
+/* One decode step, steps a1-a6: append, attend, accumulate (H2O), select.
+ *   q    device [B][Hq][D] fp32       k_new, v_new device [B][Hkv][D] kv_dtype
+ *   out  device [B][Hq][D] fp32 attention output over the pre-eviction set.
+ * The victims are recorded; h2o_compact must follow before the next step or read.
+ * Errors: H2O_EINVAL (a sequence would pass max_len), H2O_ENOMEM (no free page
+ * for the append), H2O_ESTATE (a compaction is pending), H2O_EDEVICE. */
+int h2o_step(h2o_ctx *ctx, const float *q, const void *k_new, const void *v_new, float *out,
+             void *stream);
+
+/* Step a7 for the pending step: move retained slots into the victims' holes,
+ * set the retained counts, release pages no longer used.
+ * Errors: H2O_ESTATE (no step pending), H2O_EDEVICE. */
+int h2o_compact(h2o_ctx *ctx, void *stream);
+
+/* Steps a1-a7 in one launch where the selection allows it: the same result as
+ * h2o_step followed by h2o_compact.  Leaves nothing pending. */
+int h2o_step_compact(h2o_ctx *ctx, const float *q, const void *k_new, const void *v_new,
+                     float *out, void *stream);
+
+/* Read the retained state back to the host; waits for `stream`.
+ *   pos           host [B][Hkv][cap]: retained positions of each (b, h), ascending
+ *                 (entries past the count are set to -1).
+ *   count         host [B]: retained tokens per sequence (equal for all its heads).
+ *   scores        host [B][Hkv][cap] fp64, aligned with pos; NULL to skip.
+ *   evicted_mass  host [B][Hkv] fp64 summed scores of evicted tokens; NULL to skip.
+ *   cap           entries per (b, h) in pos/scores; must be >= every count.
+ * Errors: H2O_EINVAL (cap too small), H2O_ESTATE (a compaction is pending),
+ * H2O_EDEVICE. */
+int h2o_read_indices(h2o_ctx *ctx, int32_t *pos, int32_t *count, double *scores,
+                     double *evicted_mass, size_t cap, void *stream);
+
+/* Slot capacity per (b, h) unit and the current step index s (host-side, no sync). */
+int h2o_info(const h2o_ctx *ctx, int32_t *slot_capacity, int32_t *steps_done,
+             int32_t *pages_in_use);
+
+/* Free the context and its device memory (waits for the device). NULL is a no-op. */
+void h2o_destroy(h2o_ctx *ctx);
+
+/* Message of the last error on ctx, or of the last failed h2o_init when ctx is NULL. */
+const char *h2o_last_error(const h2o_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H2O_H */

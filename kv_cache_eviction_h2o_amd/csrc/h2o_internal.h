@@ -1,0 +1,122 @@
+// Internal interface between the host runtime (h2o_runtime.cpp) and the
+// gfx950 kernels (h2o_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace h2o {
+
+constexpr int kPageShift = 4;           // 16-token KV pages
+constexpr int kPageSize = 1 << kPageShift;
+constexpr int kRowBytes = 256;          // one K or V row: 128 x bf16 or 64 x fp32
+constexpr int kRowVecs = kRowBytes / 16;  // 16-byte vectors per row = lanes per row
+constexpr int kMaxArgBatch = 256;       // paged: per-sequence new page ids travel in the kernel args
+constexpr int kLogitLdsBytes = 64 * 1024;  // logits kept in LDS up to this size per unit
+
+// Error bits a kernel may raise in State::err (checked by h2o_read_indices).
+enum : int { kErrSelectCount = 1, kErrNoCandidate = 2, kErrCompact = 4 };
+
+struct Geometry {
+    int B, Hq, Hkv, G, D;
+    int cap;        // slots per (b, h) unit (contiguous layout stride; scratch sizing)
+    int paged;      // 1 = 16-token pages through the block table
+    int maxp;       // paged: block-table row length (pages per sequence)
+    int kv_bf16;    // 1 = bf16 rows, 0 = fp32 rows
+    int score_f64;  // 1 = fp64 cumulative scores, 0 = fp32
+};
+
+struct State {  // device pointers owned by the context
+    void* kc;          // K rows
+    void* vc;          // V rows
+    void* sc;          // cumulative scores (H2O)
+    int32_t* ps;       // position of each slot; -1 marks a victim awaiting compaction
+    int32_t* cnt;      // [B*Hkv] slots in use
+    double* emass;     // [B*Hkv] evicted score mass
+    int32_t* vinfo;    // [B*Hkv][2] pending (e, victim slot) for the compaction kernel
+    int32_t* bt;       // paged: [B][maxp] page of each 16-slot block
+    const int32_t* t0; // [B] prompt lengths
+    const int64_t* poff;  // [B+1] prompt offsets into the packed prompt arrays
+    float* lscr;       // [B*Hkv][G][cap] logits when they do not fit LDS (or null)
+    int32_t* iscr;     // [B*Hkv][2*cap] hole / live lists for bulk compaction
+    int32_t* err;      // error bits
+};
+
+struct Sched {
+    int selector;  // 0 = H2O, 1 = Random
+    int n_sink, budget_fixed, hh_fixed, budget_num, budget_den;
+    int rand_k, rand_r;
+    unsigned long long seed;
+};
+
+// Budget K_t, heavy hitters HH_t and recent window W_t at length len = t + 1.
+__host__ __device__ inline void schedule(const Sched& s, int len, int& K, int& HH, int& W)
+{
+    if (s.budget_fixed > 0) {
+        K = s.budget_fixed;
+        HH = s.hh_fixed;
+    } else {
+        K = (int)(((long long)len * s.budget_num) / s.budget_den);
+        HH = (K - s.n_sink) / 2;
+    }
+    W = K - s.n_sink - HH;
+}
+
+// Tokens to evict at the step that appends position t, with n_att retained
+// slots after the append and prompt length P.
+__host__ __device__ inline int evict_count(const Sched& s, int t, int P, int n_att)
+{
+    if (s.selector == 0) {
+        int K, HH, W;
+        schedule(s, t + 1, K, HH, W);
+        return n_att > K ? n_att - K : 0;
+    }
+    return (n_att - P == s.rand_k + s.rand_r) ? s.rand_r : 0;
+}
+
+struct StepArgs {
+    Geometry g;
+    State s;
+    Sched sc;
+    const float* q;
+    const void* kn;
+    const void* vn;
+    float* out;
+    float qscale;   // logit scale * log2(e): logits are kept in the log2 domain
+    int step;       // decode steps done before this one: t_b = P_b + step
+    int fused;      // 1: the select's holes are filled in the same launch
+    int lds_n;      // logit row stride in LDS (>= max n_att of the launch)
+    int npg_lds;    // paged: block-table entries staged in LDS per unit
+    int32_t newpage[kMaxArgBatch];  // paged: page for the append slot of sequence b, or -1
+};
+
+struct CompactArgs {
+    Geometry g;
+    State s;
+};
+
+struct LoadArgs {
+    Geometry g;
+    State s;
+    const void* pk;
+    const void* pv;
+    const double* init_scores;
+};
+
+struct GatherArgs {
+    Geometry g;
+    State s;
+    int selector;
+    int capo;         // entries per unit in the staging buffers
+    int32_t* opos;    // [B*Hkv][capo]
+    double* osc;      // [B*Hkv][capo]
+};
+
+// Launchers (h2o_kernels.hip).  Each returns the launch's hipError_t.
+hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st);
+hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
+hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+
+}  // namespace h2o

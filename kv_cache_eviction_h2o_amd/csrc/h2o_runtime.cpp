@@ -1,0 +1,529 @@
+// Host runtime of libh2o.so: the C ABI declared in include/h2o.h.
+//
+// The host keeps a mirror of every sequence's position and retained count.
+// Because the budget schedule depends only on (position, configuration), the
+// host knows each step's eviction count e_b -- and so the page demand of the
+// paged layout -- without reading anything back from the device: a step is
+// pure enqueue work.  Pages are handed out and taken back here; a new page id
+// travels to the kernel in its arguments.
+#include "h2o.h"
+#include "h2o_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+using namespace h2o;
+
+struct h2o_ctx {
+    h2o_config cfg{};
+    Geometry g{};
+    State s{};
+    Sched sc{};
+    int device = 0;
+    float qscale = 0.f;
+    std::vector<int> plen;    // P_b
+    std::vector<int> count;   // retained slots per sequence (all its heads)
+    int step = 0;             // decode steps completed
+    bool pending = false;     // h2o_step done, h2o_compact not yet
+    std::vector<int> pend_e;  // e_b of the pending step
+    std::vector<std::vector<int>> pages;  // paged: page ids of each sequence, in slot order
+    std::vector<int> free_pages;
+    std::vector<void*> allocs;
+    std::string err;
+};
+
+namespace {
+
+std::mutex g_err_mu;
+std::string g_init_err;
+
+int fail(h2o_ctx* c, int code, const std::string& msg)
+{
+    if (c) {
+        c->err = msg;
+    } else {
+        std::lock_guard<std::mutex> lk(g_err_mu);
+        g_init_err = msg;
+    }
+    return code;
+}
+
+int hip_fail(h2o_ctx* c, hipError_t e, const char* what)
+{
+    std::string m = std::string(what) + ": " + hipGetErrorString(e);
+    return fail(c, e == hipErrorOutOfMemory ? H2O_ENOMEM : H2O_EDEVICE, m);
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) (void)hipSetDevice(dev);
+    }
+    ~DeviceGuard()
+    {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+Sched make_sched(const h2o_config& c)
+{
+    Sched s{};
+    s.selector = c.selector;
+    s.n_sink = c.n_sink;
+    s.budget_fixed = c.budget_fixed;
+    s.hh_fixed = c.hh_fixed;
+    s.budget_num = c.budget_num;
+    s.budget_den = c.budget_den;
+    s.rand_k = c.rand_k;
+    s.rand_r = c.rand_r;
+    s.seed = (unsigned long long)c.seed;
+    return s;
+}
+
+// Most slots a (b, h) unit can hold during the run (the pre-eviction set).
+long long slot_capacity(const h2o_config& c, int maxP)
+{
+    long long cap;
+    if (c.selector == H2O_SEL_H2O) {
+        long long kmax = c.budget_fixed > 0 ? c.budget_fixed
+                                             : ((long long)c.max_len * c.budget_num) / c.budget_den;
+        cap = std::max<long long>(maxP, kmax) + 1;
+    } else {
+        cap = (long long)maxP + c.rand_k + c.rand_r;
+    }
+    return std::min<long long>(cap, c.max_len);
+}
+
+int validate(const h2o_config* c, const int32_t* plen, std::string& why)
+{
+    auto bad = [&](const char* m) {
+        why = m;
+        return H2O_EINVAL;
+    };
+    if (!c || !plen) return bad("null config or prompt_len");
+    if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1) return bad("batch and heads must be >= 1");
+    if (c->n_q_heads % c->n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return bad("query group size must be 1, 2, 4 or 8");
+    const bool bf = c->kv_dtype == H2O_BF16, f32 = c->kv_dtype == H2O_F32;
+    if (!(bf && c->head_dim == 128) && !(f32 && c->head_dim == 64))
+        return bad("supported (kv_dtype, head_dim): (bf16, 128) or (f32, 64)");
+    if (!(c->scale >= 0.f) || !std::isfinite(c->scale)) return bad("scale must be finite and >= 0");
+    if (c->max_len < 2) return bad("max_len must be >= 2");
+    int maxP = 0;
+    for (int b = 0; b < c->batch; ++b) {
+        if (plen[b] < 1) return bad("every prompt length must be >= 1");
+        if (plen[b] >= c->max_len) return bad("prompt length must be < max_len");
+        maxP = std::max(maxP, (int)plen[b]);
+    }
+    if (c->selector == H2O_SEL_H2O) {
+        if (c->score_dtype != H2O_F32 && c->score_dtype != H2O_F64)
+            return bad("score_dtype must be f32 or f64");
+        if (c->n_sink < 0) return bad("n_sink must be >= 0");
+        if (c->budget_fixed > 0) {
+            if (c->hh_fixed < 0 || c->budget_fixed - c->n_sink - c->hh_fixed < 0)
+                return bad("fixed budget needs 0 <= hh_fixed <= budget_fixed - n_sink");
+        } else {
+            if (c->budget_den <= 0 || c->budget_num <= 0 || c->budget_num > c->budget_den)
+                return bad("proportional budget needs 0 < budget_num <= budget_den");
+            // K_t is non-decreasing; the first step of the shortest prompt is the smallest.
+            int minP = maxP;
+            for (int b = 0; b < c->batch; ++b) minP = std::min(minP, (int)plen[b]);
+            const long long k0 = ((long long)(minP + 1) * c->budget_num) / c->budget_den;
+            if (k0 < (long long)c->n_sink + 1) return bad("budget at the first step is below n_sink + 1");
+        }
+        if (c->budget_fixed > 0 && c->budget_fixed < 1) return bad("budget must be >= 1");
+    } else if (c->selector == H2O_SEL_RANDOM) {
+        if (c->rand_k < 0 || c->rand_r < 1) return bad("Random needs rand_k >= 0 and rand_r >= 1");
+    } else {
+        return bad("unknown selector");
+    }
+    if (c->page_size != 0 && c->page_size != kPageSize) return bad("page_size must be 0 or 16");
+    if (c->page_size) {
+        if (!bf) return bad("the paged layout needs bf16 rows");
+        if (c->batch > kMaxArgBatch) return bad("paged layout supports at most 256 sequences");
+        if (c->max_pages < 1) return bad("paged layout needs max_pages >= 1");
+    }
+    const long long cap = slot_capacity(*c, maxP);
+    if (cap > (1LL << 30)) return bad("slot capacity too large");
+    return H2O_OK;
+}
+
+template <typename T>
+int dalloc(h2o_ctx* c, T** p, size_t bytes, const char* what)
+{
+    *p = nullptr;
+    if (bytes == 0) return H2O_OK;
+    void* v = nullptr;
+    hipError_t e = hipMalloc(&v, bytes);
+    if (e != hipSuccess) return hip_fail(c, e, what);
+    c->allocs.push_back(v);
+    *p = (T*)v;
+    return H2O_OK;
+}
+
+void release_pages(h2o_ctx* c, int b)
+{
+    const size_t need = (size_t)((c->count[b] + kPageSize - 1) >> kPageShift);
+    auto& pg = c->pages[b];
+    while (pg.size() > need) {
+        c->free_pages.push_back(pg.back());
+        pg.pop_back();
+    }
+}
+
+void free_all(h2o_ctx* c)
+{
+    for (void* p : c->allocs) (void)hipFree(p);
+    c->allocs.clear();
+}
+
+int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* out, void* stream,
+            bool fused)
+{
+    if (!c) return H2O_EINVAL;
+    if (c->pending) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
+    if (!q || !kn || !vn || !out) return fail(c, H2O_EINVAL, "null q, k_new, v_new or out");
+    const int B = c->g.B;
+    std::vector<int> e(B);
+    int max_n_att = 0;
+    for (int b = 0; b < B; ++b) {
+        const int t = c->plen[b] + c->step;
+        if (t + 1 > c->cfg.max_len) return fail(c, H2O_EINVAL, "a sequence would pass max_len");
+        const int n_att = c->count[b] + 1;
+        if (n_att > c->g.cap) return fail(c, H2O_EINVAL, "slot capacity exceeded");
+        e[b] = evict_count(c->sc, t, c->plen[b], n_att);
+        max_n_att = std::max(max_n_att, n_att);
+    }
+    DeviceGuard dg(c->device);
+    StepArgs a{};
+    a.g = c->g;
+    a.s = c->s;
+    a.sc = c->sc;
+    a.q = q;
+    a.kn = kn;
+    a.vn = vn;
+    a.out = out;
+    a.qscale = c->qscale;
+    a.step = c->step;
+    a.fused = fused ? 1 : 0;
+    a.lds_n = (max_n_att + 3) & ~3;
+    a.npg_lds = (max_n_att + kPageSize - 1) >> kPageShift;
+    for (int i = 0; i < kMaxArgBatch; ++i) a.newpage[i] = -1;
+    std::vector<int> got;  // pages taken in this call (rolled back on failure)
+    if (c->g.paged) {
+        int demand = 0;
+        std::vector<char> need(B, 0);
+        for (int b = 0; b < B; ++b) {
+            const bool inplace = fused && c->sc.selector == H2O_SEL_H2O && e[b] == 1;
+            const int n = c->count[b];
+            if (!inplace && (n & (kPageSize - 1)) == 0 && (size_t)(n >> kPageShift) == c->pages[b].size()) {
+                need[b] = 1;
+                ++demand;
+            }
+        }
+        if ((size_t)demand > c->free_pages.size())
+            return fail(c, H2O_ENOMEM, "KV page pool exhausted");
+        for (int b = 0; b < B; ++b)
+            if (need[b]) {
+                const int p = c->free_pages.back();
+                c->free_pages.pop_back();
+                c->pages[b].push_back(p);
+                a.newpage[b] = p;
+            }
+    }
+    hipError_t err = launch_step(a, max_n_att, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(c, err, "step kernel launch");
+    if (fused) {
+        for (int b = 0; b < B; ++b) {
+            c->count[b] = c->count[b] + 1 - e[b];
+            if (c->g.paged) release_pages(c, b);
+        }
+        c->step += 1;
+    } else {
+        c->pending = true;
+        c->pend_e = e;
+    }
+    return H2O_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, const void* prompt_k,
+             const void* prompt_v, const double* init_scores, void* stream)
+{
+    if (!out) return fail(nullptr, H2O_EINVAL, "null output pointer");
+    *out = nullptr;
+    std::string why;
+    int rc = validate(cfg, prompt_len, why);
+    if (rc != H2O_OK) return fail(nullptr, rc, why);
+    if (!prompt_k || !prompt_v) return fail(nullptr, H2O_EINVAL, "null prompt_k or prompt_v");
+
+    h2o_ctx* c = new h2o_ctx();
+    c->cfg = *cfg;
+    const int B = cfg->batch, Hkv = cfg->n_kv_heads;
+    c->plen.assign(prompt_len, prompt_len + B);
+    c->count = c->plen;
+    int maxP = *std::max_element(c->plen.begin(), c->plen.end());
+    long long sumP = 0;
+    for (int p : c->plen) sumP += p;
+
+    Geometry& g = c->g;
+    g.B = B;
+    g.Hq = cfg->n_q_heads;
+    g.Hkv = Hkv;
+    g.G = cfg->n_q_heads / Hkv;
+    g.D = cfg->head_dim;
+    g.cap = (int)slot_capacity(*cfg, maxP);
+    g.paged = cfg->page_size ? 1 : 0;
+    g.maxp = g.paged ? (g.cap + kPageSize - 1) / kPageSize : 0;
+    g.kv_bf16 = cfg->kv_dtype == H2O_BF16;
+    g.score_f64 = cfg->selector == H2O_SEL_H2O && cfg->score_dtype == H2O_F64;
+    c->sc = make_sched(*cfg);
+    const double scale = cfg->scale > 0.f ? (double)cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
+    c->qscale = (float)(scale * 1.4426950408889634);  // log2(e)
+
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        return fail(nullptr, H2O_EDEVICE, "no HIP device");
+    }
+
+    // paged: the prompts' pages, from the pool
+    size_t slots_total;
+    if (g.paged) {
+        long long demand = 0;
+        for (int p : c->plen) demand += (p + kPageSize - 1) / kPageSize;
+        if (demand > cfg->max_pages) {
+            delete c;
+            return fail(nullptr, H2O_ENOMEM, "KV page pool too small for the prompts");
+        }
+        for (int p = cfg->max_pages - 1; p >= 0; --p) c->free_pages.push_back(p);
+        c->pages.resize(B);
+        for (int b = 0; b < B; ++b) {
+            const int np = (c->plen[b] + kPageSize - 1) / kPageSize;
+            for (int i = 0; i < np; ++i) {
+                c->pages[b].push_back(c->free_pages.back());
+                c->free_pages.pop_back();
+            }
+        }
+        slots_total = (size_t)cfg->max_pages * Hkv * kPageSize;
+    } else {
+        slots_total = (size_t)B * Hkv * g.cap;
+    }
+
+    const size_t units = (size_t)B * Hkv;
+    const size_t sw = g.score_f64 ? 8 : 4;
+    State& s = c->s;
+    int32_t* t0 = nullptr;
+    int64_t* poff = nullptr;
+    if ((rc = dalloc(c, &s.kc, slots_total * kRowBytes, "alloc K cache")) ||
+        (rc = dalloc(c, &s.vc, slots_total * kRowBytes, "alloc V cache")) ||
+        (cfg->selector == H2O_SEL_H2O && (rc = dalloc(c, &s.sc, slots_total * sw, "alloc scores"))) ||
+        (rc = dalloc(c, &s.ps, slots_total * 4, "alloc positions")) ||
+        (rc = dalloc(c, &s.cnt, units * 4, "alloc counts")) ||
+        (rc = dalloc(c, &s.emass, units * 8, "alloc evicted mass")) ||
+        (rc = dalloc(c, &s.vinfo, units * 8, "alloc victim info")) ||
+        (rc = dalloc(c, &s.err, 4, "alloc error word")) ||
+        (rc = dalloc(c, &t0, (size_t)B * 4, "alloc prompt lengths")) ||
+        (rc = dalloc(c, &poff, (size_t)(B + 1) * 8, "alloc prompt offsets")) ||
+        (rc = dalloc(c, &s.iscr, units * 2 * (size_t)g.cap * 4, "alloc compaction lists")) ||
+        (g.paged && (rc = dalloc(c, &s.bt, (size_t)B * g.maxp * 4, "alloc block table"))) ||
+        ((size_t)g.G * g.cap * 4 > (size_t)kLogitLdsBytes &&
+         (rc = dalloc(c, &s.lscr, units * g.G * (size_t)g.cap * 4, "alloc logit scratch")))) {
+        std::string why_alloc = c->err;
+        free_all(c);
+        delete c;
+        return fail(nullptr, rc, why_alloc);
+    }
+    s.t0 = t0;
+    s.poff = poff;
+
+    std::vector<int64_t> off(B + 1, 0);
+    for (int b = 0; b < B; ++b) off[b + 1] = off[b] + c->plen[b];
+    hipError_t e;
+    if ((e = hipMemcpy(t0, c->plen.data(), (size_t)B * 4, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(poff, off.data(), (size_t)(B + 1) * 8, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemset(s.err, 0, 4)) != hipSuccess) {
+        int r = hip_fail(nullptr, e, "init upload");
+        free_all(c);
+        delete c;
+        return r;
+    }
+    if (g.paged) {
+        std::vector<int32_t> bt((size_t)B * g.maxp, -1);
+        for (int b = 0; b < B; ++b)
+            for (size_t i = 0; i < c->pages[b].size(); ++i) bt[(size_t)b * g.maxp + i] = c->pages[b][i];
+        if ((e = hipMemcpy(s.bt, bt.data(), bt.size() * 4, hipMemcpyHostToDevice)) != hipSuccess) {
+            int r = hip_fail(nullptr, e, "block table upload");
+            free_all(c);
+            delete c;
+            return r;
+        }
+    }
+    LoadArgs la{};
+    la.g = g;
+    la.s = s;
+    la.pk = prompt_k;
+    la.pv = prompt_v;
+    la.init_scores = init_scores;
+    if ((e = launch_load(la, maxP, (hipStream_t)stream)) != hipSuccess) {
+        int r = hip_fail(nullptr, e, "prompt load launch");
+        free_all(c);
+        delete c;
+        return r;
+    }
+    (void)sumP;
+    *out = c;
+    return H2O_OK;
+}
+
+int h2o_step(h2o_ctx* ctx, const float* q, const void* k_new, const void* v_new, float* out,
+             void* stream)
+{
+    return do_step(ctx, q, k_new, v_new, out, stream, false);
+}
+
+int h2o_step_compact(h2o_ctx* ctx, const float* q, const void* k_new, const void* v_new, float* out,
+                     void* stream)
+{
+    return do_step(ctx, q, k_new, v_new, out, stream, true);
+}
+
+int h2o_compact(h2o_ctx* c, void* stream)
+{
+    if (!c) return H2O_EINVAL;
+    if (!c->pending) return fail(c, H2O_ESTATE, "no step is pending compaction");
+    DeviceGuard dg(c->device);
+    CompactArgs a{};
+    a.g = c->g;
+    a.s = c->s;
+    hipError_t err = launch_compact(a, c->g.cap, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(c, err, "compact kernel launch");
+    for (int b = 0; b < c->g.B; ++b) {
+        c->count[b] = c->count[b] + 1 - c->pend_e[b];
+        if (c->g.paged) release_pages(c, b);
+    }
+    c->pending = false;
+    c->step += 1;
+    return H2O_OK;
+}
+
+int h2o_read_indices(h2o_ctx* c, int32_t* pos, int32_t* count, double* scores, double* evicted_mass,
+                     size_t cap, void* stream)
+{
+    if (!c) return H2O_EINVAL;
+    if (c->pending) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
+    if (!pos || !count) return fail(c, H2O_EINVAL, "null pos or count");
+    const int B = c->g.B, Hkv = c->g.Hkv;
+    int maxc = 0;
+    for (int b = 0; b < B; ++b) maxc = std::max(maxc, c->count[b]);
+    if (cap < (size_t)maxc || cap == 0 || cap > (size_t)(1 << 30))
+        return fail(c, H2O_EINVAL, "cap is smaller than a retained count");
+    DeviceGuard dg(c->device);
+    const size_t units = (size_t)B * Hkv;
+    int32_t* dpos = nullptr;
+    double* dsc = nullptr;
+    hipError_t e;
+    if ((e = hipMalloc(&dpos, units * cap * 4)) != hipSuccess) return hip_fail(c, e, "read staging");
+    if ((e = hipMalloc(&dsc, units * cap * 8)) != hipSuccess) {
+        (void)hipFree(dpos);
+        return hip_fail(c, e, "read staging");
+    }
+    GatherArgs ga{};
+    ga.g = c->g;
+    ga.s = c->s;
+    ga.selector = c->sc.selector;
+    ga.capo = (int)cap;
+    ga.opos = dpos;
+    ga.osc = dsc;
+    std::vector<int32_t> hpos(units * cap), dcnt(units);
+    std::vector<double> hsc(units * cap), hem(units);
+    int32_t herr = 0;
+    hipStream_t st = (hipStream_t)stream;
+    if ((e = launch_gather(ga, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(hpos.data(), dpos, units * cap * 4, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(hsc.data(), dsc, units * cap * 8, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(dcnt.data(), c->s.cnt, units * 4, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(hem.data(), c->s.emass, units * 8, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(&herr, c->s.err, 4, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess) {
+        (void)hipFree(dpos);
+        (void)hipFree(dsc);
+        return hip_fail(c, e, "read back");
+    }
+    (void)hipFree(dpos);
+    (void)hipFree(dsc);
+    if (herr) {
+        char m[96];
+        std::snprintf(m, sizeof m, "kernel consistency check failed (error bits 0x%x)", herr);
+        return fail(c, H2O_EDEVICE, m);
+    }
+    std::vector<int> order;
+    for (size_t u = 0; u < units; ++u) {
+        const int b = (int)(u / Hkv);
+        const int n = c->count[b];
+        if (dcnt[u] != n) return fail(c, H2O_EDEVICE, "device retained count differs from the schedule");
+        order.resize(n);
+        for (int i = 0; i < n; ++i) order[i] = i;
+        const int32_t* P = &hpos[u * cap];
+        std::sort(order.begin(), order.end(), [&](int x, int y) { return P[x] < P[y]; });
+        for (int i = 0; i < n; ++i) {
+            pos[u * cap + i] = P[order[i]];
+            if (scores) scores[u * cap + i] = hsc[u * cap + order[i]];
+        }
+        for (size_t i = n; i < cap; ++i) {
+            pos[u * cap + i] = -1;
+            if (scores) scores[u * cap + i] = 0.0;
+        }
+        if (evicted_mass) evicted_mass[u] = hem[u];
+    }
+    for (int b = 0; b < B; ++b) count[b] = c->count[b];
+    return H2O_OK;
+}
+
+int h2o_info(const h2o_ctx* c, int32_t* slot_capacity, int32_t* steps_done, int32_t* pages_in_use)
+{
+    if (!c) return H2O_EINVAL;
+    if (slot_capacity) *slot_capacity = c->g.cap;
+    if (steps_done) *steps_done = c->step;
+    if (pages_in_use) {
+        long long n = 0;
+        for (const auto& p : c->pages) n += (long long)p.size();
+        *pages_in_use = (int32_t)n;
+    }
+    return H2O_OK;
+}
+
+void h2o_destroy(h2o_ctx* c)
+{
+    if (!c) return;
+    {
+        DeviceGuard dg(c->device);
+        (void)hipDeviceSynchronize();
+        free_all(c);
+    }
+    delete c;
+}
+
+const char* h2o_last_error(const h2o_ctx* c)
+{
+    if (c) return c->err.c_str();
+    std::lock_guard<std::mutex> lk(g_err_mu);
+    static thread_local std::string copy;
+    copy = g_init_err;
+    return copy.c_str();
+}
+
+}  // extern "C"

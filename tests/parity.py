@@ -1,0 +1,156 @@
+"""GPU path vs CPU oracle, step by step, on the same seeded inputs.
+
+Acceptance (per step, per checked (sequence, KV head) unit):
+* attention output: for each query head, max_d |gpu - oracle| <= 2e-3 * max_d |oracle|;
+* retained set: equal to the oracle's, except that a different victim set is
+  accepted when it has the same size, only evictable tokens, and every token in
+  the symmetric difference has an oracle score within 1e-5 of the oracle's
+  e-th smallest candidate score (a near-tie the fp32 path may resolve either
+  way); the oracle then adopts the GPU's set so later steps stay comparable.
+  Random Attention has no exemption: its sets must be identical;
+* cumulative scores of the retained tokens: |gpu - oracle| <= 2e-3 * oracle + 1e-9;
+* evicted mass: |gpu - oracle| <= 2e-3 * max(1, oracle).
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle as O
+from kv_cache_eviction_h2o_amd import synth as S
+from kv_cache_eviction_h2o_amd import workloads as WL
+
+OUT_TOL = 2e-3
+SCORE_TOL = 2e-3
+GAP = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, kv_dtype):
+    import torch
+    if kv_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+@dataclass
+class ParityReport:
+    steps: int = 0
+    units: int = 0
+    adopted: int = 0
+    max_out_err: float = 0.0
+    max_score_err: float = 0.0
+    evictions: int = 0
+    notes: list = field(default_factory=list)
+
+
+def make_cache(w: WL.Workload, lens, n_steps: int, layer: int = 0, init_scores=None):
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+    K, V = S.prompt_kv(w.recipe, layer, lens, w.n_kv_heads)
+    max_len = max(lens) + n_steps + 1
+    cfg = L.config_from_workload(w, max_len=max_len)
+    if w.page_size:
+        cfg.max_pages = L.pages_needed(lens, n_steps, cfg)
+    isc = None
+    if init_scores is not None:
+        isc = torch.from_numpy(np.ascontiguousarray(init_scores, dtype=np.float64)).cuda()
+    cache = L.H2OCache(cfg, lens, to_dev(K, w.kv_dtype), to_dev(V, w.kv_dtype), init_scores=isc)
+    return cache, K, V
+
+
+def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=True, layer=0,
+               init_scores=None, read_every=1, check_scores=True) -> ParityReport:
+    """Run n_steps on the GPU and in the oracle (for `units`, default all)."""
+    import torch
+    lens = list(lens) if lens is not None else WL.prompt_lengths(w)
+    B, Hq, Hkv, G, D = w.batch, w.n_q_heads, w.n_kv_heads, w.group, w.head_dim
+    assert len(lens) == B
+    say(f"[parity] {w.name} B={B} Hq={Hq} Hkv={Hkv} D={D} lens={lens[:6]}{'...' if B > 6 else ''} "
+        f"steps={n_steps} fused={fused} units={'all' if units is None else len(units)}")
+    cache, K, V = make_cache(w, lens, n_steps, layer, init_scores)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    units = [(b, h) for b in range(B) for h in range(Hkv)] if units is None else list(units)
+    ocfg = O.cfg_from_workload(w)
+    orc = {}
+    for (b, h) in units:
+        isc = None if init_scores is None else init_scores[off[b]:off[b + 1], h]
+        orc[(b, h)] = O.Unit(ocfg, b, h, S.cache_to_f64(w.recipe, K[off[b]:off[b + 1], h]),
+                             S.cache_to_f64(w.recipe, V[off[b]:off[b + 1], h]),
+                             lens[b] + n_steps + 1, init_scores=isc)
+    rep = ParityReport(units=len(units))
+    cap = cache.info()[0]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    win = 256
+    for s0 in range(0, n_steps, win):
+        ns = min(win, n_steps - s0)
+        q, k, v = S.step_window(w.recipe, layer, [p + s0 for p in lens], ns, Hq, Hkv)
+        qd = torch.from_numpy(q).cuda()
+        kd, vd = to_dev(k, w.kv_dtype), to_dev(v, w.kv_dtype)
+        for i in range(ns):
+            s = s0 + i
+            if fused:
+                cache.step_compact(qd[i], kd[i], vd[i], out)
+            else:
+                cache.step(qd[i], kd[i], vd[i], out)
+                cache.compact()
+            check = (s % read_every == 0) or s == n_steps - 1
+            if not check:
+                # the oracle still has to take the step (its own choice)
+                for (b, h) in units:
+                    orc[(b, h)].step(q[i, b, h * G:(h + 1) * G], S.cache_to_f64(w.recipe, k[i, b, h]),
+                                     S.cache_to_f64(w.recipe, v[i, b, h]))
+                continue
+            o_gpu = out.cpu().numpy()
+            pos, cnt, sc, em = cache.read_indices(cap)
+            for (b, h) in units:
+                u = orc[(b, h)]
+                o_ref = u.attend(q[i, b, h * G:(h + 1) * G], S.cache_to_f64(w.recipe, k[i, b, h]),
+                                 S.cache_to_f64(w.recipe, v[i, b, h]))
+                og = o_gpu[b, h * G:(h + 1) * G].astype(np.float64)
+                err = np.max(np.abs(og - o_ref), axis=1) / np.maximum(np.max(np.abs(o_ref), axis=1), 1e-30)
+                rep.max_out_err = max(rep.max_out_err, float(err.max()))
+                assert np.all(err <= OUT_TOL), f"step {s} unit {(b, h)}: output rel err {err.max():.3g}"
+                pre_pos, _, _ = u.state()
+                vic, tau = u.select()
+                n = int(cnt[b])
+                gpos = pos[b, h, :n]
+                gset = set(gpos.tolist())
+                assert gset <= set(pre_pos.tolist()), f"step {s} unit {(b, h)}: GPU retains unknown positions"
+                gvic = sorted(set(pre_pos.tolist()) - gset)
+                if sorted(vic.tolist()) != gvic:
+                    diff = set(vic.tolist()) ^ set(gvic)
+                    ok = (w.selector == "h2o" and len(gvic) == len(vic)
+                          and all(abs(u.score_of(p) - tau) < GAP for p in diff))
+                    assert ok, (f"step {s} unit {(b, h)}: victims differ: oracle-only "
+                                f"{sorted(set(vic.tolist()) - set(gvic))[:8]} gpu-only "
+                                f"{sorted(set(gvic) - set(vic.tolist()))[:8]} tau={tau}")
+                    u.evict(np.array(gvic, dtype=np.int32))
+                    rep.adopted += 1
+                else:
+                    u.evict(vic)
+                u.check()
+                rep.evictions += len(gvic)
+                o_pos, o_sc, o_em = u.state()
+                assert np.array_equal(o_pos, gpos), f"step {s} unit {(b, h)}: retained sets differ"
+                if check_scores and w.selector == "h2o":
+                    g_sc = sc[b, h, :n]
+                    serr = np.abs(g_sc - o_sc)
+                    assert np.all(serr <= SCORE_TOL * np.abs(o_sc) + 1e-9), \
+                        f"step {s} unit {(b, h)}: score err {np.max(serr / (np.abs(o_sc) + 1e-9)):.3g}"
+                    rep.max_score_err = max(rep.max_score_err,
+                                            float(np.max(serr / np.maximum(np.abs(o_sc), 1e-30))))
+                    assert abs(em[b, h] - o_em) <= SCORE_TOL * max(1.0, o_em), \
+                        f"step {s} unit {(b, h)}: evicted mass {em[b, h]} vs {o_em}"
+            rep.steps += 1
+    cache.close()
+    say(f"[parity] ok: checked {rep.steps} steps x {rep.units} units, max out err "
+        f"{rep.max_out_err:.2e}, max score err {rep.max_score_err:.2e}, evictions {rep.evictions}, "
+        f"near-ties adopted {rep.adopted}")
+    return rep

@@ -1,0 +1,129 @@
+"""The C-ABI library on the CPU: it loads, exports what include/h2o.h declares,
+its struct layout matches the binding, and it validates before touching a device."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cache_eviction_h2o_amd import _lib as L
+from kv_cache_eviction_h2o_amd.build import INCLUDE, LIB, build
+
+HEADER = os.path.join(INCLUDE, "h2o.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        build()
+    return L.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h2o_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree_on_symbols():
+    assert declared_functions() == sorted(L.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (h2o_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_config_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in L.H2OConfig._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "h2o.h"', "int main(void){",
+            'printf("%zu\\n", sizeof(h2o_config));']
+    prog += [f'printf("%zu\\n", offsetof(h2o_config, {f}));' for f in fields]
+    prog += ["return 0;}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", INCLUDE, "-o", str(exe), str(src)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == C.sizeof(L.H2OConfig)
+    assert vals[1:] == [getattr(L.H2OConfig, f).offset for f in fields]
+
+
+def _init(lib, cfg, lens):
+    ctx = C.c_void_p()
+    arr = (C.c_int32 * len(lens))(*lens)
+    rc = lib.h2o_init(C.byref(ctx), C.byref(cfg), arr, C.c_void_p(16), C.c_void_p(16), None, None)
+    return rc, ctx
+
+
+GOOD = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kv_dtype="bf16", score_dtype="f32",
+            budget_fixed=64, hh_fixed=28, max_len=4096)
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(n_q_heads=7), "multiple"),
+    (dict(n_q_heads=6), "group size"),
+    (dict(n_q_heads=32, n_kv_heads=2), "group size"),
+    (dict(head_dim=64), "head_dim"),
+    (dict(kv_dtype="f32", head_dim=128), "head_dim"),
+    (dict(hh_fixed=61), "hh_fixed"),
+    (dict(budget_fixed=0, budget_num=3, budget_den=2), "proportional"),
+    (dict(budget_fixed=0, budget_num=1, budget_den=500), "below n_sink"),
+    (dict(selector="random", rand_r=0), "Random"),
+    (dict(page_size=8), "page_size"),
+    (dict(page_size=16, max_pages=0), "max_pages"),
+    (dict(page_size=16, kv_dtype="f32", head_dim=64, max_pages=64), "bf16"),
+    (dict(max_len=100), "max_len"),
+    (dict(scale=-1.0), "scale"),
+])
+def test_invalid_config_rejected_before_device(lib, bad, msg):
+    cfg = L.make_config(**{**GOOD, **bad})
+    rc, ctx = _init(lib, cfg, [100, 200])
+    assert rc == L.H2O_EINVAL
+    assert not ctx.value
+    assert msg in lib.h2o_last_error(None).decode()
+
+
+def test_invalid_prompt_lengths_rejected(lib):
+    cfg = L.make_config(**GOOD)
+    assert _init(lib, cfg, [0, 10])[0] == L.H2O_EINVAL
+    assert _init(lib, cfg, [10, 4096])[0] == L.H2O_EINVAL
+
+
+def test_null_arguments(lib):
+    assert lib.h2o_step(None, None, None, None, None, None) == L.H2O_EINVAL
+    assert lib.h2o_step_compact(None, None, None, None, None, None) == L.H2O_EINVAL
+    assert lib.h2o_compact(None, None) == L.H2O_EINVAL
+    assert lib.h2o_info(None, None, None, None) == L.H2O_EINVAL
+    lib.h2o_destroy(None)
+    cfg = L.make_config(**GOOD)
+    arr = (C.c_int32 * 2)(10, 20)
+    assert lib.h2o_init(None, C.byref(cfg), arr, None, None, None, None) == L.H2O_EINVAL
+    ctx = C.c_void_p()
+    assert lib.h2o_init(C.byref(ctx), C.byref(cfg), arr, None, None, None, None) == L.H2O_EINVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("kv_cache_eviction_h2o_amd._lib")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load_library(str(tmp_path / "nope.so"))
+    finally:
+        mod._lib = saved
+
+
+def test_page_pool_sizing_host_logic():
+    cfg = L.make_config(**{**GOOD, "budget_fixed": 0, "budget_num": 1, "budget_den": 5,
+                           "page_size": 16, "max_pages": 1, "max_len": 70000})
+    lens = [4096, 65536]
+    need = L.pages_needed(lens, 65, cfg)
+    assert need >= sum((p + 15) // 16 for p in lens)

@@ -1,0 +1,122 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Every case runs the same seeded inputs through both, step by step; see
+parity.py for the acceptance rule.  Shapes: the five workloads, reduced where
+the oracle would take too long over the whole trace, plus full-shape runs
+checked on sampled units, plus the degenerate cases of the method.
+"""
+import numpy as np
+import pytest
+
+from kv_cache_eviction_h2o_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_eviction_h2o_amd import _lib
+    _lib.load_library()
+
+
+def P():
+    import parity
+    return parity
+
+
+# ------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("fused", [True, False], ids=["step_compact", "step+compact"])
+def test_tiny_h2o_full_trace(fused):
+    rep = P().run_parity(WL.TINY_H2O, WL.TINY_H2O.decode_steps, fused=fused)
+    assert rep.steps == 256 and rep.evictions > 0
+
+
+def test_opt_layer_reduced_full_trace():
+    w = WL.OPT_LAYER.scaled(batch=2, n_q_heads=8, n_kv_heads=8)
+    rep = P().run_parity(w, w.decode_steps)
+    assert rep.evictions > 0
+
+
+def test_opt_layer_full_shape_sampled_units():
+    w = WL.OPT_LAYER
+    units = [(0, 0), (3, 17), (7, 31), (5, 4)]
+    P().run_parity(w, 160, units=units)
+
+
+def test_llama_gqa_reduced():
+    # prompt above the 1028 budget so the first step bulk-evicts, then one per step
+    w = WL.LLAMA_GQA.scaled(batch=1, prompt_len=1100)
+    rep = P().run_parity(w, 96)
+    assert rep.evictions >= 73 * 8
+
+
+def test_llama_gqa_full_shape_sampled_units():
+    w = WL.LLAMA_GQA.scaled(prompt_len=1040)
+    P().run_parity(w, 24, units=[(0, 0), (9, 5), (15, 7)])
+
+
+def test_random_attention_reduced():
+    w = WL.RANDOM_ATTN.scaled(batch=2, n_q_heads=8, n_kv_heads=2, rand_k=64, rand_r=16,
+                              prompt_len=40)
+    rep = P().run_parity(w, 200)
+    assert rep.evictions == 4 * 8 * 16  # 4 units x 8 events x r
+
+
+def test_random_attention_full_shape_sampled_units():
+    w = WL.RANDOM_ATTN.scaled(rand_k=256)
+    rep = P().run_parity(w, 400, units=[(0, 0), (31, 7), (12, 3)])
+    assert rep.evictions == 3 * 128  # the event at 384 generated tokens
+
+
+def test_paged_mixed_reduced():
+    w = WL.PAGED_MIXED.scaled(batch=4, n_q_heads=4, n_kv_heads=4)
+    P().run_parity(w, 40, lens=[300, 517, 1024, 2000])
+
+
+def test_paged_mixed_reduced_unfused():
+    w = WL.PAGED_MIXED.scaled(batch=3, n_q_heads=2, n_kv_heads=2)
+    P().run_parity(w, 40, lens=[64, 255, 1500], fused=False)
+
+
+# ------------------------------------------------------------- edge cases
+def test_budget_above_length_is_full_attention():
+    w = WL.TINY_H2O.scaled(budget_fixed=4096, hh_fixed=2000)
+    rep = P().run_parity(w, 64)
+    assert rep.evictions == 0
+
+
+def test_ragged_prompts_fixed_budget():
+    w = WL.TINY_H2O.scaled(batch=4)
+    rep = P().run_parity(w, 80, lens=[20, 63, 64, 150])
+    assert rep.evictions > 0
+
+
+def test_sliding_window_and_zero_recent_window():
+    # no sinks, no heavy hitters: the last W positions only
+    P().run_parity(WL.TINY_H2O.scaled(n_sink=0, budget_fixed=40, hh_fixed=0), 50)
+    # W = 0: the new token is itself a candidate and may go at once
+    P().run_parity(WL.TINY_H2O.scaled(budget_fixed=24, hh_fixed=20), 50)
+
+
+def test_gqa_group_of_two_bf16():
+    w = WL.OPT_LAYER.scaled(batch=2, n_q_heads=4, n_kv_heads=2)
+    P().run_parity(w, 60, lens=[200, 333])
+
+
+def test_unfused_bulk_and_random():
+    w = WL.OPT_LAYER.scaled(batch=1, n_q_heads=4, n_kv_heads=4)
+    P().run_parity(w, 30, lens=[700], fused=False)
+    wr = WL.RANDOM_ATTN.scaled(batch=2, n_q_heads=4, n_kv_heads=2, rand_k=20, rand_r=5,
+                               prompt_len=16)
+    P().run_parity(wr, 60, fused=False)
+
+
+def test_initial_scores():
+    w = WL.TINY_H2O.scaled(batch=2)
+    lens = [100, 90]
+    rng = np.random.default_rng(5)
+    init = rng.random((sum(lens), w.n_kv_heads)) * 0.01
+    P().run_parity(w, 40, lens=lens, init_scores=init)
