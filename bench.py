@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the H2O decode step (attention + evict + compact) on one MI355X.
+
+Default workload: an OPT-6.7B-shaped layer (batch 8, 32 heads x 128, bf16 K/V,
+fp32 cumulative scores, 4 sinks, budget 20 % of the current length split
+between heavy hitters and the recent window), prompt 1024 then 1024 decode
+steps, stepped through 32 independent layer instances in turn as one decode
+step of the model does (so the working set leaves the 256 MB Infinity Cache).
+The timed window starts at decode step 512 of the trace; the steps before it
+are run untimed to reach that state.
+
+Metric: retained KV tokens processed per second (a retained token counts once
+per sequence per layer-step), with the step's algorithmic bytes as a fraction
+of the 8 TB/s HBM peak.  `roofline` reports the step kernel alone: algorithmic
+bytes per launch over its mean duration, timed with HIP events recorded on the
+launch stream around every launch of the timed region.  `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from kv_cache_eviction_h2o_amd import metrics as M  # noqa: E402
+from kv_cache_eviction_h2o_amd import synth as S  # noqa: E402
+from kv_cache_eviction_h2o_amd import workloads as WL  # noqa: E402
+
+METRIC = "retained KV tokens processed/sec per decode step (attn+evict+compact); % HBM peak"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc", "h2o_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default=WL.OPT_LAYER.name,
+                    choices=[w.name for w in WL.ALL if w.page_size == 0])
+    ap.add_argument("--layers", type=int, default=0, help="layer instances (0 = workload default)")
+    ap.add_argument("--window-start", type=int, default=512,
+                    help="decode step at which the timed window starts")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--events", choices=["launch", "step", "none"], default="launch",
+                    help="HIP events around every step-kernel launch (default), around every "
+                         "decode step, or none")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Timing events straight from the HIP runtime, created without the
+    system-scope fence so a marker between two kernels does not write back L2."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        self.lib = C.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self.lib.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self):
+        e = C.c_void_p()
+        if self.lib.hipEventCreateWithFlags(C.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+
+    def record(self, e, stream):
+        if self.lib.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_s(self, e0, e1) -> float:
+        ms = C.c_float()
+        if self.lib.hipEventElapsedTime(C.byref(ms), e0, e1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e-3
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def retained_schedule(w, P: int, n_steps: int):
+    """n_att (slots attended) at each decode step for one sequence with prompt P.
+
+    Host arithmetic mirroring the budget rule: the count after a step is
+    min(n_att, K_t) for H2O and drops by r at each Random Attention event."""
+    out = np.empty(n_steps, dtype=np.int64)
+    count = P
+    for s in range(n_steps):
+        t = P + s
+        n_att = count + 1
+        out[s] = n_att
+        if w.selector == "h2o":
+            K = w.budget_fixed if w.budget_fixed > 0 else ((t + 1) * w.budget_num) // w.budget_den
+            count = min(n_att, K)
+        else:
+            count = n_att - (w.rand_r if n_att - P == w.rand_k + w.rand_r else 0)
+    return out
+
+
+def traffic_from_profiles(workload: str):
+    """Measured HBM bytes per launch from a committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"h2o_step_kernel_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, n_att: int, seconds: float):
+    """The fp64 oracle (as it stands) on one layer of the workload at the
+    window's retained length, all host cores, for about `seconds`."""
+    import oracle as O
+    B, Hkv, Hq, G, D = w.batch, w.n_kv_heads, w.n_q_heads, w.group, w.head_dim
+    K = n_att - 1  # fixed budget: every step attends n_att slots and evicts one
+    ws = w.scaled(budget_fixed=K, hh_fixed=(K - w.n_sink) // 2)
+    lens = [K] * B
+    Kp, Vp = S.prompt_kv(w.recipe, 0, lens, Hkv)
+    cfg = O.cfg_from_workload(ws)
+    max_steps = 4096
+    units = []
+    for b in range(B):
+        for h in range(Hkv):
+            units.append(O.Unit(cfg, b, h, S.cache_to_f64(w.recipe, Kp[b * K:(b + 1) * K, h]),
+                                S.cache_to_f64(w.recipe, Vp[b * K:(b + 1) * K, h]), K + max_steps + 1))
+    threads = min(os.cpu_count() or 1, len(units))
+    done, t_used = 0, 0.0
+    win = 32
+    while t_used < seconds and done < max_steps:
+        q, k, v = S.step_window(w.recipe, 0, [K + done] * B, win, Hq, Hkv)
+        for i in range(win):
+            qs = [q[i, b, h * G:(h + 1) * G] for b in range(B) for h in range(Hkv)]
+            ks = [S.cache_to_f64(w.recipe, k[i, b, h]) for b in range(B) for h in range(Hkv)]
+            vs = [S.cache_to_f64(w.recipe, v[i, b, h]) for b in range(B) for h in range(Hkv)]
+            qs = [np.ascontiguousarray(x, np.float64) for x in qs]
+            t0 = time.perf_counter()
+            O.step_many(units, qs, ks, vs, threads)
+            t_used += time.perf_counter() - t0
+            done += 1
+            if t_used >= seconds:
+                break
+    tokens = done * B * n_att
+    return {"value": tokens / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"one layer ({B} sequences x {Hkv} KV heads) at the window's retained "
+                       f"length n_att={n_att}, {done} decode steps, fp64 oracle on {threads} "
+                       f"threads; {t_used:.1f} s of CPU step time (input conversion excluded)")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build runs the decode step on a single MI355X "
+              f"and has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+
+    w = next(x for x in WL.ALL if x.name == args.workload)
+    layers = args.layers or w.layers
+    K_steps, W_steps = args.steps, args.warmup
+    s0 = min(args.window_start, w.decode_steps - K_steps)
+    if s0 < W_steps or K_steps < 1:
+        raise SystemExit("window does not fit the trace: lower --steps or --warmup")
+    total_steps = s0 + K_steps
+    lens = WL.prompt_lengths(w)
+    B, Hq, Hkv, D, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    dev = torch.device("cuda")
+    lib = L.load_library()
+    stream = torch.cuda.current_stream()
+    sh = C.c_void_p(stream.cuda_stream)
+
+    # ---- set-up (untimed): layer instances, inputs of every step in HBM
+    t_setup = time.perf_counter()
+    caches, qs, ks, vs, outs = [], [], [], [], []
+    max_len = max(lens) + w.decode_steps + 1
+    for l in range(layers):
+        pk, pv = S.device_prompt_kv(w.recipe, l, lens, Hkv, dev)
+        cfg = L.config_from_workload(w, max_len=max_len)
+        caches.append(L.H2OCache(cfg, lens, pk, pv))
+        q, k, v = S.device_step_window(w.recipe, l, lens, total_steps, Hq, Hkv, dev)
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+        outs.append(torch.empty((B, Hq, D), dtype=torch.float32, device=dev))
+        del pk, pv
+    torch.cuda.synchronize()
+    q_stride, kv_stride = B * Hq * D * 4, B * Hkv * D * (2 if w.kv_dtype == "bf16" else 4)
+    ctxs = [c.ctx for c in caches]
+    qb = [q.data_ptr() for q in qs]
+    kb = [k.data_ptr() for k in ks]
+    vb = [v.data_ptr() for v in vs]
+    ob = [o.data_ptr() for o in outs]
+    step_fn = lib.h2o_step_compact
+
+    hev = HipEvents()
+
+    def run_step(s, evs=None):
+        for l in range(layers):
+            if evs is not None and (events == "launch" or l == 0):
+                hev.record(evs[l][0], sh)
+            rc = step_fn(ctxs[l], C.c_void_p(qb[l] + s * q_stride), C.c_void_p(kb[l] + s * kv_stride),
+                         C.c_void_p(vb[l] + s * kv_stride), C.c_void_p(ob[l]), sh)
+            if evs is not None and (events == "launch" or l == layers - 1):
+                hev.record(evs[l][1], sh)
+            if rc != 0:
+                raise L.H2OError(rc, lib.h2o_last_error(ctxs[l]).decode())
+
+    for s in range(0, s0):  # reach the window (the last W of these are the warm-up)
+        run_step(s)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        bcp = torch.empty_like(a)
+        torch.cuda.synchronize()
+        bcp.copy_(a)
+        torch.cuda.synchronize()
+        del a, bcp
+
+    # ---- timed region
+    events = args.events
+    use_ev = events != "none"
+    evs = [[(hev.create(), hev.create()) for _ in range(layers)]
+           for _ in range(K_steps)] if use_ev else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        run_step(s0 + i, evs[i] if use_ev else None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # ---- accounting
+    sched = np.stack([retained_schedule(w, P, total_steps) for P in lens])  # [B][steps]
+    win = sched[:, s0:s0 + K_steps]  # n_att per sequence per timed step
+    tokens = float(win.sum()) * layers
+    value = tokens / elapsed
+    sbytes = 8 if w.score_dtype == "f64" else 4
+    if w.selector == "random":
+        sbytes = 0
+    kv_elem = 2 if w.kv_dtype == "bf16" else 4
+    launch_b = np.array([M.launch_bytes(win[:, i], n_kv_heads=Hkv, head_dim=D, kv_elem=kv_elem,
+                                        group=G, score_bytes=sbytes) for i in range(K_steps)])
+    step_bytes = float(launch_b.sum()) * layers
+    roof = None
+    if use_ev:
+        if events == "launch":
+            dur = np.array([[hev.elapsed_s(e0, e1) for (e0, e1) in evs[i]] for i in range(K_steps)])
+        else:  # one bracket per decode step: launches back to back, gaps included
+            dur = np.array([[hev.elapsed_s(evs[i][0][0], evs[i][layers - 1][1]) / layers] * layers
+                            for i in range(K_steps)])
+        for row in evs:
+            for (e0, e1) in row:
+                hev.destroy(e0)
+                hev.destroy(e1)
+        achieved = float((launch_b[:, None] * np.ones((1, layers))).sum() / dur.sum()) / 1e9
+        traffic = traffic_from_profiles(w.name)
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "h2o step kernel (h2o_step_compact launch)", "timing": events,
+                "mean_launch_us": round(float(dur.mean()) * 1e6, 3),
+                "algorithmic_bytes_per_launch": int(launch_b.mean())}
+
+    # sanity: the library's counts equal the schedule used for the accounting
+    _, cnt, _, _ = caches[0].read_indices()
+    if w.selector == "h2o":
+        def budget(length):
+            return w.budget_fixed if w.budget_fixed > 0 else length * w.budget_num // w.budget_den
+        expect = np.array([min(int(sched[b, -1]), budget(lens[b] + total_steps)) for b in range(B)])
+    else:
+        last = sched[:, -1]
+        expect = last - np.where(last - np.array(lens) == w.rand_k + w.rand_r, w.rand_r, 0)
+    if not np.array_equal(cnt, expect):
+        raise SystemExit(f"retained counts {cnt[:4]} differ from the schedule {expect[:4]}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, int(np.round(win.mean())), args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K_steps, "warmup": W_steps, "ms_per_step": round(elapsed / K_steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "kv_dtype": w.kv_dtype, "score_dtype": w.score_dtype if sbytes else None,
+                   "layers": layers, "prompt_len": lens[0] if len(set(lens)) == 1 else "mixed",
+                   "window_steps": [s0, s0 + K_steps], "mean_n_att": round(float(win.mean()), 1),
+                   "entry_point": "h2o_step_compact", "parallelism": "single GPU"},
+        "hbm_frac_step": round(step_bytes / elapsed / (HBM_PEAK_GBS * 1e9), 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+        "kernel_source_sha256_16": kernel_hash(),
+    }
+    for c in caches:
+        c.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

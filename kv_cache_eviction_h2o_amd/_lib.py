@@ -50,6 +50,10 @@ def load_library(path: str = LIB):
     global _lib
     if _lib is not None:
         return _lib
+    try:  # load torch's HIP runtime first so the library binds to that same runtime
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build the HIP library first "
                            "(python -c 'import __graft_entry__ as g; g.build()')")

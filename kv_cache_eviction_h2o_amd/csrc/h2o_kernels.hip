@@ -221,7 +221,10 @@ __device__ void radix_select(KeyFn key_of, int n_att, int e, int d0, RadixSmem& 
         for (int j = tid; j < n_att; j += NT) {
             unsigned w[3];
             if (key_of(j, w) && (w[0] & m0) == p0 && (w[1] & m1) == p1 && (w[2] & m2) == p2)
-                atomicAdd(&rs.hist[(w[wi] >> sh) & 255u], 1u);
+            {
+                const unsigned word = wi == 2 ? w[2] : (wi == 1 ? w[1] : w[0]);
+                atomicAdd(&rs.hist[(word >> sh) & 255u], 1u);
+            }
         }
         __syncthreads();
         if (tid < 64) {
@@ -338,8 +341,10 @@ struct SlotMap {
 // ------------------------------------------------------------- step kernel
 template <int G>
 struct StepTune {
-    static constexpr int NT = G <= 2 ? 512 : 256;  // threads per unit
-    static constexpr int U = G <= 2 ? 4 : 2;       // rows in flight per lane group
+    static constexpr int NT = G <= 2 ? 512 : 256;             // threads per unit
+    static constexpr int U = G <= 2 ? 4 : (G == 4 ? 4 : 2);   // rows per lane group per batch
+    static constexpr int PF = G <= 2 ? 2 : 5;                 // slots per thread whose score and
+                                                              // position are fetched up front
 };
 
 template <typename Row, int G, typename ST, bool PAGED, bool LLDS>
@@ -347,6 +352,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
 {
     constexpr int NT = StepTune<G>::NT;
     constexpr int U = StepTune<G>::U;
+    constexpr int PF = StepTune<G>::PF;
     constexpr int EPL = Row::EPL;
     constexpr int NGRP = NT / 16;
     constexpr int NW = NT / 64;
@@ -408,25 +414,68 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     }
 
     // ---- phase 1: q.K, online softmax, P.V over the n_att slots -----------
-    float qr[G][EPL];
+    // Loads are issued in the order their data is needed (q and the new token,
+    // then the first batch of K and V rows, then phase 2's scores): the vector
+    // memory counter retires in order, so waiting for an early load never
+    // waits for the ones behind it.
+    ST* scp = reinterpret_cast<ST*>(S.sc);
+    int32_t* psp = S.ps;
+    float4 qraw[G][EPL / 4];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const float4* qp = reinterpret_cast<const float4*>(
             a.q + ((size_t)b * gm.Hq + (size_t)h * G + g) * DR + sub * EPL);
 #pragma unroll
-        for (int i = 0; i < EPL / 4; ++i) {
-            const float4 v = qp[i];
-            qr[g][4 * i + 0] = v.x * a.qscale;
-            qr[g][4 * i + 1] = v.y * a.qscale;
-            qr[g][4 * i + 2] = v.z * a.qscale;
-            qr[g][4 * i + 3] = v.w * a.qscale;
-        }
+        for (int i = 0; i < EPL / 4; ++i) qraw[g][i] = qp[i];
     }
     const uint4 knr = reinterpret_cast<const uint4*>(a.kn)[(size_t)unit * kRowVecs + sub];
     const uint4 vnr = reinterpret_cast<const uint4*>(a.vn)[(size_t)unit * kRowVecs + sub];
     const uint4* kc = reinterpret_cast<const uint4*>(S.kc);
     const uint4* vc = reinterpret_cast<const uint4*>(S.vc);
+    __builtin_amdgcn_sched_barrier(0);  // keep q and the new token ahead of the K/V stream
 
+    // Every load below is unconditional: rows past the retained ones read
+    // slot 0 (a cache hit) and are replaced at use.  Conditional loads would
+    // make the compiler's wait counts conservative at the join points and
+    // serialise the pipeline.
+    auto load_batch = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U]) {
+        size_t r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + grp + NGRP * u;
+            r[u] = sidx(j < n ? j : 0) * kRowVecs + sub;
+            kr[u] = kc[r[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) vr[u] = vc[r[u]];
+    };
+    uint4 ka[U], va[U], kb[U], vb[U];
+    load_batch(0, ka, va);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // scores and positions of this thread's first PF phase-2 slots
+    ST pf_s[PF];
+    int pf_p[PF];
+    if (h2o) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int j = tid + k * NT;
+            const size_t si = sidx(j < n ? j : 0);
+            pf_s[k] = scp[si];
+            pf_p[k] = psp[si];
+        }
+    }
+
+    float qr[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i) {
+            qr[g][4 * i + 0] = qraw[g][i].x * a.qscale;
+            qr[g][4 * i + 1] = qraw[g][i].y * a.qscale;
+            qr[g][4 * i + 2] = qraw[g][i].z * a.qscale;
+            qr[g][4 * i + 3] = qraw[g][i].w * a.qscale;
+        }
     float m[G], l[G], o[G][EPL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -436,25 +485,15 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         for (int i = 0; i < EPL; ++i) o[g][i] = 0.f;
     }
 
-    for (int base = 0; base < n_att; base += NGRP * U) {
-        uint4 kr[U], vr[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = base + grp + NGRP * u;
-            if (j < n) {
-                const size_t r = sidx(j) * kRowVecs + sub;
-                kr[u] = kc[r];
-                vr[u] = vc[r];
-            } else {
-                kr[u] = knr;
-                vr[u] = vnr;
-            }
-        }
+    // one batch: logits (K), running max, then P.V (V)
+    auto process = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
         float s[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int j = base + grp + NGRP * u;
             float kx[EPL];
-            Row::unpack(kr[u], kx);
+            Row::unpack(j < n ? kr[u] : (j == n ? knr : zero), kx);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float acc = 0.f;
@@ -462,7 +501,6 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                 for (int i = 0; i < EPL; ++i) acc = fmaf(qr[g][i], kx[i], acc);
                 s[u][g] = sum16(acc);
             }
-            const int j = base + grp + NGRP * u;
             if (j < n_att) {
                 if (h2o) {
 #pragma unroll
@@ -489,8 +527,9 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int j = base + grp + NGRP * u;
             float vx[EPL];
-            Row::unpack(vr[u], vx);
+            Row::unpack(j < n ? vr[u] : (j == n ? vnr : zero), vx);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float p = (s[u][g] == -INFINITY) ? 0.f : fast_exp2(s[u][g] - m[g]);
@@ -499,15 +538,31 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                 for (int i = 0; i < EPL; ++i) o[g][i] = fmaf(p, vx[i], o[g][i]);
             }
         }
-        if (!inplace_new) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (base + grp + NGRP * u == n) {
-                    const size_t r = sidx(n) * kRowVecs + sub;
-                    reinterpret_cast<uint4*>(S.kc)[r] = knr;
-                    reinterpret_cast<uint4*>(S.vc)[r] = vnr;
-                }
-        }
+    };
+    // Batch b+1 is requested before batch b is consumed.  Two register sets
+    // alternate (no copies, which would wait for the loads in flight) and the
+    // tail is peeled so that the loop body holds no conditional load.
+    constexpr int BR = NGRP * U;  // rows per batch
+    const int nbatch = (n_att + BR - 1) / BR;
+    int bi = 0;
+    for (; bi + 2 < nbatch; bi += 2) {
+        load_batch((bi + 1) * BR, kb, vb);
+        process(bi * BR, ka, va);
+        load_batch((bi + 2) * BR, ka, va);
+        process((bi + 1) * BR, kb, vb);
+    }
+    if (bi + 1 < nbatch) {
+        load_batch((bi + 1) * BR, kb, vb);
+        process(bi * BR, ka, va);
+        process((bi + 1) * BR, kb, vb);
+    } else {
+        process(bi * BR, ka, va);
+    }
+    // the new token's row goes to slot n unless it fills a victim's hole later
+    if (!inplace_new && tid < 16) {
+        const size_t r = sidx(n) * kRowVecs + sub;
+        reinterpret_cast<uint4*>(S.kc)[r] = knr;
+        reinterpret_cast<uint4*>(S.vc)[r] = vnr;
     }
 
     // combine the four lane groups of each wave, then the waves in LDS
@@ -567,8 +622,6 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     }
     __syncthreads();
 
-    ST* scp = reinterpret_cast<ST*>(S.sc);
-    int32_t* psp = S.ps;
     int K = 0, HH = 0, W = 0;
     if (h2o) schedule(a.sc, t + 1, K, HH, W);
     const int lo_c = a.sc.n_sink, hi_c = t + 1 - W;  // H2O candidates: lo_c <= pos < hi_c
@@ -577,21 +630,17 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     if (h2o) {
         ST bs = (ST)0;
         int bp = -1, bj = -1;
-        for (int j = tid; j < n_att; j += NT) {
+        // slot j: add its weights of this step (summed over the group) to its
+        // score; the new token (j == n) starts from zero
+        auto visit = [&](int j, ST old, int pos) {
             float p = 0.f;
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 p += fast_exp2(logit[(size_t)g * lstride + j] - s_M[g]) * s_invL[g];
-            ST nw;
-            int pos;
+            const ST nw = old + (ST)p;
             if (j < n) {
-                const size_t si = sidx(j);
-                nw = scp[si] + (ST)p;
-                pos = psp[si];
-                scp[si] = nw;
+                scp[sidx(j)] = nw;
             } else {
-                nw = (ST)p;
-                pos = t;
                 s_new_score = nw;
                 if (!inplace_new) {
                     const size_t si = sidx(n);
@@ -605,6 +654,19 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                     bp = pos;
                     bj = j;
                 }
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int j = tid + k * NT;
+            if (j < n_att) visit(j, j < n ? pf_s[k] : (ST)0, j < n ? pf_p[k] : t);
+        }
+        for (int j = tid + PF * NT; j < n_att; j += NT) {
+            if (j < n) {
+                const size_t si = sidx(j);
+                visit(j, scp[si], psp[si]);
+            } else {
+                visit(j, (ST)0, t);
             }
         }
         if (e == 1) {
@@ -870,10 +932,12 @@ template <typename Row, int G, typename ST, bool PAGED, bool LLDS>
 hipError_t launch_step_t(const StepArgs& a, size_t dyn, hipStream_t st)
 {
     auto k = step_kernel<Row, G, ST, PAGED, LLDS>;
-    if (dyn > 48 * 1024) {
+    static size_t dyn_set = 48 * 1024;  // largest dynamic LDS size granted so far
+    if (dyn > dyn_set) {
         hipError_t err = hipFuncSetAttribute((const void*)k,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (err != hipSuccess) return err;
+        dyn_set = dyn;
     }
     hipLaunchKernelGGL(k, dim3(a.g.B * a.g.Hkv), dim3(StepTune<G>::NT), dyn, st, a);
     return hipGetLastError();

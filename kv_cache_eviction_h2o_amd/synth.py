@@ -210,3 +210,58 @@ def uniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     """n integer lengths uniform on [lo, hi] (inclusive), from their own Philox stream."""
     g = np.random.Generator(np.random.Philox(key=np.array([seed, 0xFFFF], dtype=np.uint64)))
     return g.integers(lo, hi + 1, size=n).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Device-side drawing of the same recipe, for workloads too large to draw on
+# the host (the benchmark's many layer instances).  The normals come from
+# torch's seeded GPU generator, so the values differ from the numpy streams
+# above; the structure (u, boost mask and magnitudes, rounding) is identical.
+def _torch_seed(seed: int, kind: int, layer: int, b: int) -> int:
+    w1 = int(stream_key(seed, kind, layer, b, 0, 0)[1])
+    return (seed * 0x9E3779B97F4A7C15 + w1) & 0x7FFFFFFFFFFFFFFF
+
+
+def device_prompt_kv(r: Recipe, layer: int, prompt_lens, n_kv_heads: int, device="cuda"):
+    """Packed prompts [sum P_b][Hkv][D] as torch device tensors (bf16 or fp32)."""
+    import torch
+    lens = [int(x) for x in prompt_lens]
+    D = r.head_dim
+    dt = torch.bfloat16 if r.kv_dtype == "bf16" else torch.float32
+    u = torch.from_numpy(unit_vector(r)).to(device)
+    K = torch.empty((sum(lens), n_kv_heads, D), dtype=dt, device=device)
+    V = torch.empty_like(K)
+    off = 0
+    for b, P in enumerate(lens):
+        mag = torch.from_numpy(boost_magnitudes(r, layer, b, 0, P)).to(device)
+        g = torch.Generator(device=device)
+        g.manual_seed(_torch_seed(r.seed, KIND_K, layer, b))
+        k = torch.randn((P, n_kv_heads, D), generator=g, device=device, dtype=torch.float32)
+        K[off:off + P] = (k + mag[:, None, None] * u).to(dt)
+        g.manual_seed(_torch_seed(r.seed, KIND_V, layer, b))
+        V[off:off + P] = torch.randn((P, n_kv_heads, D), generator=g, device=device,
+                                     dtype=torch.float32).to(dt)
+        off += P
+    return K, V
+
+
+def device_step_window(r: Recipe, layer: int, t0, n_steps: int, n_q_heads: int, n_kv_heads: int,
+                       device="cuda"):
+    """Inputs of n_steps decode steps as device tensors:
+    q [n][B][Hq][D] fp32, k and v [n][B][Hkv][D] in the cache dtype."""
+    import torch
+    t0 = [int(x) for x in t0]
+    B, D = len(t0), r.head_dim
+    dt = torch.bfloat16 if r.kv_dtype == "bf16" else torch.float32
+    u = torch.from_numpy(unit_vector(r)).to(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(r.seed, KIND_Q, layer, t0[0]))
+    q = torch.randn((n_steps, B, n_q_heads, D), generator=g, device=device) + r.q_boost * u
+    mag = torch.stack([torch.from_numpy(boost_magnitudes(r, layer, b, t0[b], t0[b] + n_steps))
+                       for b in range(B)], dim=1).to(device)  # [n][B]
+    g.manual_seed(_torch_seed(r.seed, KIND_K, layer, 4095))
+    k = torch.randn((n_steps, B, n_kv_heads, D), generator=g, device=device)
+    k = (k + mag[:, :, None, None] * u).to(dt)
+    g.manual_seed(_torch_seed(r.seed, KIND_V, layer, 4095))
+    v = torch.randn((n_steps, B, n_kv_heads, D), generator=g, device=device).to(dt)
+    return q.contiguous(), k.contiguous(), v.contiguous()
