@@ -12,7 +12,8 @@ constexpr int kPageShift = 4;           // 16-token KV pages
 constexpr int kPageSize = 1 << kPageShift;
 constexpr int kRowBytes = 256;          // one K or V row: 128 x bf16 or 64 x fp32
 constexpr int kRowVecs = kRowBytes / 16;  // 16-byte vectors per row = lanes per row
-constexpr int kMaxArgBatch = 256;       // paged: per-sequence new page ids travel in the kernel args
+constexpr int kMaxArgBatch = 128;       // per-sequence step parameters travel in the kernel args
+                                        // (larger batches read them from device memory)
 constexpr int kLogitLdsBytes = 64 * 1024;  // logits kept in LDS up to this size per unit
 
 // Error bits a kernel may raise in State::err (checked by h2o_read_indices).
@@ -88,6 +89,9 @@ struct StepArgs {
     int fused;      // 1: the select's holes are filled in the same launch
     int lds_n;      // logit row stride in LDS (>= max n_att of the launch)
     int npg_lds;    // paged: block-table entries staged in LDS per unit
+    int seq_in_args;                // 1: seq_n / seq_p below are valid (B <= kMaxArgBatch)
+    int32_t seq_n[kMaxArgBatch];    // retained slots of sequence b before the step
+    int32_t seq_p[kMaxArgBatch];    // prompt length of sequence b
     int32_t newpage[kMaxArgBatch];  // paged: page for the append slot of sequence b, or -1
 };
 

@@ -79,7 +79,62 @@ __device__ inline float sum16(float v)
     return v;
 }
 
+// sum16 of N independent values, one DPP stage at a time across them so the
+// wait states each DPP read needs are filled by the other rows' work.
+template <int N>
+__device__ inline void sum16_n(float (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0xB1>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0x4E>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0x141>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0x140>(v[i]);
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-row exchange within a wave (gfx950 permlane swaps).  Swapping a value
+// with itself leaves, in every lane, the pair (own row's value, partner row's
+// value) in some order; a commutative combine of the pair then gives every
+// lane the result for rows {r, r^1} (x16) or halves {lo, hi} (x32).
+struct Pair {
+    unsigned a, b;
+};
+__device__ inline Pair xrow16(unsigned v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return {r[0], r[1]};
+}
+__device__ inline Pair xrow32(unsigned v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return {r[0], r[1]};
+}
+
+// Raw buffer access (gfx9 family resource word 3): reads past num_records
+// bytes return zero without touching memory.
+constexpr int kBufWord3 = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    uint4 v;
+    __builtin_memcpy(&v, &x, 16);
+    return v;
+}
+
+// Barrier for exchanges through LDS only: waits for this wave's LDS accesses,
+// not for its global stores (which __syncthreads' release fence would wait for).
+__device__ inline void lds_barrier()
+{
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 struct ScanSmem {
     int wsum[16];
@@ -146,6 +201,81 @@ __device__ int block_sum_i32(int v, int* sh)
     for (int i = 0; i < NW; ++i) s += sh[i];
     __syncthreads();
     return s;  // valid in every thread
+}
+
+// ------------------------------------------------------------- wave arg-min
+// (score, position, slot) triples; smaller score wins, equal scores go to the
+// higher position (so the lower position is kept); slot < 0 = no candidate.
+template <typename ST>
+__device__ inline void take_better(ST& bs, int& bp, int& bj, ST os, int op, int oj)
+{
+    if (oj >= 0 && (bj < 0 || os < bs || (os == bs && op > bp))) {
+        bs = os;
+        bp = op;
+        bj = oj;
+    }
+}
+
+template <int CTRL>
+__device__ inline int dpp_i(int v)
+{
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
+template <int CTRL, typename ST>
+__device__ inline ST dpp_s(ST v)
+{
+    if constexpr (sizeof(ST) == 4) {
+        return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+    } else {
+        const long long u = __double_as_longlong(v);
+        const int lo = dpp_i<CTRL>((int)(u & 0xffffffffll)), hi = dpp_i<CTRL>((int)(u >> 32));
+        return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+    }
+}
+
+template <int CTRL, typename ST>
+__device__ inline void argmin_step(ST& bs, int& bp, int& bj)
+{
+    take_better(bs, bp, bj, dpp_s<CTRL>(bs), dpp_i<CTRL>(bp), dpp_i<CTRL>(bj));
+}
+
+// Every lane ends with the wave's best: four DPP stages within each row of
+// 16 lanes (quad_perm 1,0,3,2 / 2,3,0,1, row_half_mirror, row_mirror), then
+// two lane shuffles across the rows.
+template <bool X32, typename ST>
+__device__ inline void argmin_xrow(ST& bs, int& bp, int& bj)
+{
+    auto sw = [](unsigned v) { return X32 ? xrow32(v) : xrow16(v); };
+    const Pair p = sw((unsigned)bp), j = sw((unsigned)bj);
+    ST s0, s1;
+    if constexpr (sizeof(ST) == 4) {
+        const Pair q = sw(__float_as_uint(bs));
+        s0 = __uint_as_float(q.a);
+        s1 = __uint_as_float(q.b);
+    } else {
+        const unsigned long long u = (unsigned long long)__double_as_longlong(bs);
+        const Pair lo = sw((unsigned)u), hi = sw((unsigned)(u >> 32));
+        s0 = __longlong_as_double((long long)(((unsigned long long)hi.a << 32) | lo.a));
+        s1 = __longlong_as_double((long long)(((unsigned long long)hi.b << 32) | lo.b));
+    }
+    ST rs = s0;
+    int rp = (int)p.a, rj = (int)j.a;
+    take_better(rs, rp, rj, s1, (int)p.b, (int)j.b);
+    bs = rs;
+    bp = rp;
+    bj = rj;
+}
+
+template <typename ST>
+__device__ inline void wave_argmin(ST& bs, int& bp, int& bj)
+{
+    argmin_step<0xB1>(bs, bp, bj);
+    argmin_step<0x4E>(bs, bp, bj);
+    argmin_step<0x141>(bs, bp, bj);
+    argmin_step<0x140>(bs, bp, bj);
+    argmin_xrow<false>(bs, bp, bj);
+    argmin_xrow<true>(bs, bp, bj);
 }
 
 // ------------------------------------------------------------------ Philox
@@ -361,12 +491,9 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     extern __shared__ __align__(16) unsigned char dsm[];
     __shared__ float red_m[NW][G], red_l[NW][G];
     __shared__ __align__(16) float red_o[NW][G][DR];
-    __shared__ float s_M[G], s_invL[G];
     __shared__ ST s_new_score;
     __shared__ ST s_bs[NW];
     __shared__ int s_bp[NW], s_bj[NW];
-    __shared__ int s_vj;
-    __shared__ ST s_vs;
     __shared__ double s_dsum[NW];
     __shared__ int s_isum[NW];
     __shared__ ScanSmem s_scan;
@@ -378,9 +505,11 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     const int b = unit / gm.Hkv, h = unit - b * gm.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, sub = tid & 15, grp = tid >> 4;
 
-    const int P = S.t0[b];
+    // the host knows every sequence's prompt length and retained count: taking
+    // them from the arguments saves a dependent memory round trip at the start
+    const int P = a.seq_in_args ? a.seq_p[b] : S.t0[b];
     const int t = P + a.step;
-    const int n = S.cnt[unit];
+    const int n = a.seq_in_args ? a.seq_n[b] : S.cnt[unit];
     const int n_att = n + 1;
     const bool h2o = a.sc.selector == 0;
     const int e = evict_count(a.sc, t, P, n_att);
@@ -432,22 +561,40 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     const uint4 vnr = reinterpret_cast<const uint4*>(a.vn)[(size_t)unit * kRowVecs + sub];
     const uint4* kc = reinterpret_cast<const uint4*>(S.kc);
     const uint4* vc = reinterpret_cast<const uint4*>(S.vc);
+    // evicted mass of the unit, read now so its update at the end is no round trip
+    const double emass0 = S.emass[unit];
     __builtin_amdgcn_sched_barrier(0);  // keep q and the new token ahead of the K/V stream
 
-    // Every load below is unconditional: rows past the retained ones read
-    // slot 0 (a cache hit) and are replaced at use.  Conditional loads would
-    // make the compiler's wait counts conservative at the join points and
-    // serialise the pipeline.
+    // Rows j >= n are masked out by their logit; the new token (j == n) is
+    // folded in after the loop.  Every load is unconditional (a conditional
+    // load would make the compiler's wait counts conservative at the join and
+    // serialise the pipeline).  Contiguous layout: raw buffer loads over the
+    // unit's n rows, so rows past them read as zero without a memory access.
+    // Paged layout: rows past n read slot 0 (a cache hit).
+    __amdgpu_buffer_rsrc_t rk, rv;
+    if constexpr (!PAGED) {
+        const size_t ub = sidx.base * kRowBytes;
+        rk = make_rsrc(reinterpret_cast<const char*>(S.kc) + ub, (unsigned)n * kRowBytes);
+        rv = make_rsrc(reinterpret_cast<const char*>(S.vc) + ub, (unsigned)n * kRowBytes);
+    }
     auto load_batch = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U]) {
-        size_t r[U];
+        if constexpr (!PAGED) {
+            const unsigned off0 = (unsigned)(base + grp) * kRowBytes + (unsigned)sub * 16u;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = base + grp + NGRP * u;
-            r[u] = sidx(j < n ? j : 0) * kRowVecs + sub;
-            kr[u] = kc[r[u]];
+            for (int u = 0; u < U; ++u) kr[u] = buf_load16(rk, off0 + (unsigned)(u * NGRP * kRowBytes));
+#pragma unroll
+            for (int u = 0; u < U; ++u) vr[u] = buf_load16(rv, off0 + (unsigned)(u * NGRP * kRowBytes));
+        } else {
+            size_t r[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = base + grp + NGRP * u;
+                r[u] = sidx(j < n ? j : 0) * kRowVecs + sub;
+                kr[u] = kc[r[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) vr[u] = vc[r[u]];
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) vr[u] = vc[r[u]];
     };
     uint4 ka[U], va[U], kb[U], vb[U];
     load_batch(0, ka, va);
@@ -476,32 +623,71 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
             qr[g][4 * i + 2] = qraw[g][i].z * a.qscale;
             qr[g][4 * i + 3] = qraw[g][i].w * a.qscale;
         }
+    // running max starts at a finite floor: a lane group that owns no valid
+    // row keeps m = floor, l = 0, and 2^(-inf - floor) = 0 for masked rows
+    constexpr float kMaxFloor = -1e30f;
     float m[G], l[G], o[G][EPL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
+        m[g] = kMaxFloor;
         l[g] = 0.f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) o[g][i] = 0.f;
     }
 
-    // one batch: logits (K), running max, then P.V (V)
+    // logits of nr rows (K), running max, then P.V (V); rows with !valid[u]
+    // take no weight
+    auto accumulate = [&](float (&s)[U][G], const uint4 (&vr)[U], int nr) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float mx = m[g];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (u < nr) mx = fmaxf(mx, s[u][g]);
+            const float al = fast_exp2(m[g] - mx);
+            l[g] *= al;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) o[g][i] *= al;
+            m[g] = mx;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u >= nr) continue;
+            float vx[EPL];
+            Row::unpack(vr[u], vx);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float p = fast_exp2(s[u][g] - m[g]);  // 2^-inf = 0 for masked rows
+                l[g] += p;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) o[g][i] = fmaf(p, vx[i], o[g][i]);
+            }
+        }
+    };
+    auto logits = [&](const uint4 (&kr)[U], float (&s)[U][G]) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float acc[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float kx[EPL];
+                Row::unpack(kr[u], kx);
+                acc[u] = 0.f;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) acc[u] = fmaf(qr[g][i], kx[i], acc[u]);
+            }
+            sum16_n<U>(acc);
+#pragma unroll
+            for (int u = 0; u < U; ++u) s[u][g] = acc[u];
+        }
+    };
     auto process = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
-        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
         float s[U][G];
+        logits(kr, s);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + grp + NGRP * u;
-            float kx[EPL];
-            Row::unpack(j < n ? kr[u] : (j == n ? knr : zero), kx);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) acc = fmaf(qr[g][i], kx[i], acc);
-                s[u][g] = sum16(acc);
-            }
-            if (j < n_att) {
+            if (j < n) {
                 if (h2o) {
 #pragma unroll
                     for (int g = 0; g < G; ++g)
@@ -512,33 +698,26 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                 for (int g = 0; g < G; ++g) s[u][g] = -INFINITY;
             }
         }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float mx = m[g];
-#pragma unroll
-            for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][g]);
-            if (mx != -INFINITY) {
-                const float al = fast_exp2(m[g] - mx);
-                l[g] *= al;
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) o[g][i] *= al;
-                m[g] = mx;
-            }
-        }
+        accumulate(s, vr, U);
+    };
+    // the new token (position t, slot n) is lane group 0's first row; this
+    // runs while the first K/V batch is still in flight
+    if (grp == 0) {
+        uint4 kn1[U], vn1[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int j = base + grp + NGRP * u;
-            float vx[EPL];
-            Row::unpack(j < n ? vr[u] : (j == n ? vnr : zero), vx);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float p = (s[u][g] == -INFINITY) ? 0.f : fast_exp2(s[u][g] - m[g]);
-                l[g] += p;
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) o[g][i] = fmaf(p, vx[i], o[g][i]);
-            }
+            kn1[u] = knr;
+            vn1[u] = vnr;
         }
-    };
+        float s1[U][G];
+        logits(kn1, s1);
+        if (h2o) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                if (sub == g) logit[(size_t)g * lstride + n] = s1[0][g];
+        }
+        accumulate(s1, vn1, 1);
+    }
     // Batch b+1 is requested before batch b is consumed.  Two register sets
     // alternate (no copies, which would wait for the loads in flight) and the
     // tail is peeled so that the loop body holds no conditional load.
@@ -565,24 +744,27 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         reinterpret_cast<uint4*>(S.vc)[r] = vnr;
     }
 
-    // combine the four lane groups of each wave, then the waves in LDS
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
+    // merge the four lane groups (rows) of each wave with permlane swaps,
+    // then the waves through LDS: one barrier, after which every thread
+    // derives the normaliser itself
+    auto merge = [&](auto xrow) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float mo = __shfl_xor(m[g], off), lo = __shfl_xor(l[g], off);
-            const float M = fmaxf(m[g], mo);
-            const float a1 = (M == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
-            const float a2 = (M == -INFINITY) ? 0.f : fast_exp2(mo - M);
-            l[g] = l[g] * a1 + lo * a2;
+            const Pair pm = xrow(__float_as_uint(m[g])), pl = xrow(__float_as_uint(l[g]));
+            const float m0 = __uint_as_float(pm.a), m1 = __uint_as_float(pm.b);
+            const float M = fmaxf(m0, m1);
+            const float a0 = fast_exp2(m0 - M), a1 = fast_exp2(m1 - M);
+            l[g] = __uint_as_float(pl.a) * a0 + __uint_as_float(pl.b) * a1;
 #pragma unroll
             for (int i = 0; i < EPL; ++i) {
-                const float oo = __shfl_xor(o[g][i], off);
-                o[g][i] = o[g][i] * a1 + oo * a2;
+                const Pair po = xrow(__float_as_uint(o[g][i]));
+                o[g][i] = __uint_as_float(po.a) * a0 + __uint_as_float(po.b) * a1;
             }
             m[g] = M;
         }
-    }
+    };
+    merge([](unsigned v) { return xrow16(v); });
+    merge([](unsigned v) { return xrow32(v); });
     if (lane < 16) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -594,33 +776,38 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
             }
         }
     }
-    __syncthreads();
+    // logits kept in global scratch (very long units) need the full fence
+    if constexpr (LLDS) lds_barrier(); else __syncthreads();
+    float Mg[G], invLg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float M = kMaxFloor;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][g]);
+        float L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) L += red_l[ww][g] * fast_exp2(red_m[ww][g] - M);
+        Mg[g] = M;
+        invLg[g] = 1.0f / L;
+    }
     for (int idx = tid; idx < G * 16; idx += NT) {
         const int g = idx >> 4, sb = idx & 15;
-        float M = -INFINITY;
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][g]);
-        float L = 0.f, acc[EPL];
+        float acc[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+#pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-            const float f = (red_m[ww][g] == -INFINITY) ? 0.f : fast_exp2(red_m[ww][g] - M);
-            L += red_l[ww][g] * f;
+            const float f = fast_exp2(red_m[ww][g] - Mg[g]);
 #pragma unroll
             for (int i = 0; i < EPL; ++i) acc[i] += red_o[ww][g][sb * EPL + i] * f;
         }
-        const float inv = 1.0f / L;
         float4* op = reinterpret_cast<float4*>(a.out + ((size_t)b * gm.Hq + (size_t)h * G + g) * DR +
                                                sb * EPL);
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i)
-            op[i] = make_float4(acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv,
-                                acc[4 * i + 3] * inv);
-        if (sb == 0) {
-            s_M[g] = M;
-            s_invL[g] = inv;
-        }
+            op[i] = make_float4(acc[4 * i] * invLg[g], acc[4 * i + 1] * invLg[g],
+                                acc[4 * i + 2] * invLg[g], acc[4 * i + 3] * invLg[g]);
     }
-    __syncthreads();
 
     int K = 0, HH = 0, W = 0;
     if (h2o) schedule(a.sc, t + 1, K, HH, W);
@@ -636,7 +823,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
             float p = 0.f;
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                p += fast_exp2(logit[(size_t)g * lstride + j] - s_M[g]) * s_invL[g];
+                p += fast_exp2(logit[(size_t)g * lstride + j] - Mg[g]) * invLg[g];
             const ST nw = old + (ST)p;
             if (j < n) {
                 scp[sidx(j)] = nw;
@@ -670,43 +857,26 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
             }
         }
         if (e == 1) {
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const ST os = __shfl_xor(bs, off);
-                const int op = __shfl_xor(bp, off), oj = __shfl_xor(bj, off);
-                if (oj >= 0 && (bj < 0 || os < bs || (os == bs && op > bp))) {
-                    bs = os;
-                    bp = op;
-                    bj = oj;
-                }
-            }
+            wave_argmin(bs, bp, bj);
             if (lane == 0) {
                 s_bs[w] = bs;
                 s_bp[w] = bp;
                 s_bj[w] = bj;
             }
-            __syncthreads();
-            if (tid == 0) {
-                ST vs = (ST)0;
-                int vp = -1, vj = -1;
-                for (int ww = 0; ww < NW; ++ww) {
-                    const int oj = s_bj[ww];
-                    if (oj >= 0 && (vj < 0 || s_bs[ww] < vs || (s_bs[ww] == vs && s_bp[ww] > vp))) {
-                        vs = s_bs[ww];
-                        vp = s_bp[ww];
-                        vj = oj;
-                    }
-                }
-                s_vj = vj;
-                s_vs = vs;
-            }
-            __syncthreads();
-            const int vj = s_vj;
+            lds_barrier();
+            ST vs = s_bs[0];
+            int vp = s_bp[0], vjj = s_bj[0];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) take_better(vs, vp, vjj, s_bs[ww], s_bp[ww], s_bj[ww]);
+            const int vj = vjj;
             if (vj < 0) {
                 if (tid == 0) atomicOr(S.err, kErrNoCandidate);
                 return;
             }
-            if (tid == 0) S.emass[unit] += (double)s_vs;
+            if (tid == 0) S.emass[unit] = emass0 + (double)vs;
+            // the victim slot's score / position are written by the thread that
+            // wrote its updated score above: same thread, same address, in order
+            const bool owner = (vj - tid) % NT == 0;
             if (a.fused) {
                 if (vj != n) {
                     if (tid < 16) {
@@ -714,17 +884,19 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                         reinterpret_cast<uint4*>(S.kc)[r] = knr;
                         reinterpret_cast<uint4*>(S.vc)[r] = vnr;
                     }
-                    if (tid == 0) {
+                    if (owner) {
                         scp[sidx(vj)] = s_new_score;
                         psp[sidx(vj)] = t;
                     }
                 }
                 // the count stays n: one in, one out
-            } else if (tid == 0) {
-                psp[sidx(vj)] = -1;
-                S.vinfo[2 * unit] = 1;
-                S.vinfo[2 * unit + 1] = vj;
-                S.cnt[unit] = n_att;
+            } else {
+                if (owner) psp[sidx(vj)] = -1;
+                if (tid == 0) {
+                    S.vinfo[2 * unit] = 1;
+                    S.vinfo[2 * unit + 1] = vj;
+                    S.cnt[unit] = n_att;
+                }
             }
             return;
         }
@@ -801,7 +973,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     const double vm = block_sum_f64<NT>(vmass, s_dsum);
     if (tid == 0) {
         if (nv_all != e) atomicOr(S.err, kErrSelectCount);
-        if (h2o) S.emass[unit] += vm;
+        if (h2o) S.emass[unit] = emass0 + vm;
     }
     if (a.fused) {
         __syncthreads();

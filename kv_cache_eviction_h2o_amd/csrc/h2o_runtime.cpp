@@ -151,7 +151,7 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     if (c->page_size != 0 && c->page_size != kPageSize) return bad("page_size must be 0 or 16");
     if (c->page_size) {
         if (!bf) return bad("the paged layout needs bf16 rows");
-        if (c->batch > kMaxArgBatch) return bad("paged layout supports at most 256 sequences");
+        if (c->batch > kMaxArgBatch) return bad("paged layout supports at most 128 sequences");
         if (c->max_pages < 1) return bad("paged layout needs max_pages >= 1");
     }
     const long long cap = slot_capacity(*c, maxP);
@@ -220,6 +220,12 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     a.lds_n = (max_n_att + 3) & ~3;
     a.npg_lds = (max_n_att + kPageSize - 1) >> kPageShift;
     for (int i = 0; i < kMaxArgBatch; ++i) a.newpage[i] = -1;
+    a.seq_in_args = B <= kMaxArgBatch ? 1 : 0;
+    if (a.seq_in_args)
+        for (int b = 0; b < B; ++b) {
+            a.seq_n[b] = c->count[b];
+            a.seq_p[b] = c->plen[b];
+        }
     std::vector<int> got;  // pages taken in this call (rolled back on failure)
     if (c->g.paged) {
         int demand = 0;
