@@ -13,7 +13,9 @@ Metric: retained KV tokens processed per second (a retained token counts once
 per sequence per layer-step), with the step's algorithmic bytes as a fraction
 of the 8 TB/s HBM peak.  `roofline` reports the step kernel alone: algorithmic
 bytes per launch over its mean duration, timed with HIP events recorded on the
-launch stream around every launch of the timed region.  `cpu_baseline` times
+launch stream around every decode step of the timed region (each step is the
+layers' launches back to back, so this per-launch time includes the short
+dispatch gap between launches).  `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -45,8 +47,48 @@ KERNEL_SRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc", "h2o_kernel
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def summarize(args) -> None:
+    """Markdown summary of rocprofv3 CSV output for the step kernel (see --help)."""
+    import csv
+    n_last = args.steps * (args.layers or 32)
+    out = [f"kernel_source_sha256_16: {kernel_hash()}"]
+    if args.summarize_trace:
+        rows = [r for r in csv.DictReader(open(args.summarize_trace)) if "step_kernel" in r["Kernel_Name"]]
+        d = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows], dtype=np.float64)
+        s0 = np.array([int(r["Start_Timestamp"]) for r in rows], dtype=np.int64)
+        e0 = np.array([int(r["End_Timestamp"]) for r in rows], dtype=np.int64)
+        w = d[-n_last:]
+        gaps = (s0[-n_last + 1:] - e0[-n_last:-1]) / 1e3
+        out += [f"step_kernel launches in trace: {len(d)}",
+                f"all launches: mean {d.mean() / 1e3:.3f} us",
+                f"timed window (last {n_last} launches): mean {w.mean() / 1e3:.3f} us, "
+                f"median {np.median(w) / 1e3:.3f} us, p10 {np.percentile(w, 10) / 1e3:.3f} us, "
+                f"p90 {np.percentile(w, 90) / 1e3:.3f} us",
+                f"timed window gap between consecutive launches: mean {gaps.mean():.3f} us"]
+    if args.summarize_counters:
+        fetch_csv, write_csv = args.summarize_counters
+        res = {}
+        for name, f in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+            rows = list(csv.DictReader(open(f)))
+            st = [float(r["Counter_Value"]) for r in rows if "step_kernel" in r["Kernel_Name"]
+                  and r["Counter_Name"] == name]
+            cal = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+                      and r["Counter_Name"] == name)
+            factor = (1 << 20) / cal  # KiB that a 1 GiB device-to-device copy moves, per side
+            res[name] = (np.mean(st[-n_last:]), factor, cal)
+            out.append(f"{name}: timed-window mean {res[name][0]:.1f} KiB per launch; the 1 GiB "
+                       f"copy reads {cal:.1f} KiB on this counter -> scale x{factor:.4f}")
+        hbm = sum(v * f * 1024 for v, f, _ in res.values())
+        out.append(f"hbm_bytes_per_launch: {hbm:.6e}")
+    print("\n".join(out))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print a summary of a rocprofv3 kernel trace of this benchmark and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="with FETCH_SIZE / WRITE_SIZE counter CSVs: HBM bytes per launch")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
@@ -57,9 +99,11 @@ def parse():
                     help="decode step at which the timed window starts")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--events", choices=["launch", "step", "none"], default="launch",
-                    help="HIP events around every step-kernel launch (default), around every "
-                         "decode step, or none")
+    ap.add_argument("--events", choices=["step", "launch", "none"], default="step",
+                    help="HIP events around every decode step (default: its layer launches run "
+                         "back to back, so the per-launch time is the step time over the layers, "
+                         "dispatch gaps included), around every launch (markers between kernels "
+                         "slow the step), or none")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -176,6 +220,9 @@ def cpu_baseline(w, n_att: int, seconds: float):
 
 def main():
     args = parse()
+    if args.summarize_trace or args.summarize_counters:
+        summarize(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: this build runs the decode step on a single MI355X "
