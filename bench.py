@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=WL.OPT_LAYER.name,
-                    choices=[w.name for w in WL.ALL if w.page_size == 0])
+                    choices=[w.name for w in WL.ALL])
     ap.add_argument("--layers", type=int, default=0, help="layer instances (0 = workload default)")
     ap.add_argument("--window-start", type=int, default=512,
                     help="decode step at which the timed window starts")
@@ -253,6 +253,8 @@ def main():
     for l in range(layers):
         pk, pv = S.device_prompt_kv(w.recipe, l, lens, Hkv, dev)
         cfg = L.config_from_workload(w, max_len=max_len)
+        if w.page_size:
+            cfg.max_pages = L.pages_needed(lens, w.decode_steps, cfg)
         caches.append(L.H2OCache(cfg, lens, pk, pv))
         q, k, v = S.device_step_window(w.recipe, l, lens, total_steps, Hq, Hkv, dev)
         qs.append(q)

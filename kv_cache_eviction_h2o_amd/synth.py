@@ -217,8 +217,8 @@ def uniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
 # the host (the benchmark's many layer instances).  The normals come from
 # torch's seeded GPU generator, so the values differ from the numpy streams
 # above; the structure (u, boost mask and magnitudes, rounding) is identical.
-def _torch_seed(seed: int, kind: int, layer: int, b: int) -> int:
-    w1 = int(stream_key(seed, kind, layer, b, 0, 0)[1])
+def _torch_seed(seed: int, kind: int, layer: int, b: int, block: int = 0) -> int:
+    w1 = int(stream_key(seed, kind, layer, b, 0, block)[1])
     return (seed * 0x9E3779B97F4A7C15 + w1) & 0x7FFFFFFFFFFFFFFF
 
 
@@ -255,13 +255,14 @@ def device_step_window(r: Recipe, layer: int, t0, n_steps: int, n_q_heads: int, 
     dt = torch.bfloat16 if r.kv_dtype == "bf16" else torch.float32
     u = torch.from_numpy(unit_vector(r)).to(device)
     g = torch.Generator(device=device)
-    g.manual_seed(_torch_seed(r.seed, KIND_Q, layer, t0[0]))
+    blk = t0[0] % (1 << 20)  # the window's first position names its streams
+    g.manual_seed(_torch_seed(r.seed, KIND_Q, layer, 0, blk))
     q = torch.randn((n_steps, B, n_q_heads, D), generator=g, device=device) + r.q_boost * u
     mag = torch.stack([torch.from_numpy(boost_magnitudes(r, layer, b, t0[b], t0[b] + n_steps))
                        for b in range(B)], dim=1).to(device)  # [n][B]
-    g.manual_seed(_torch_seed(r.seed, KIND_K, layer, 4095))
+    g.manual_seed(_torch_seed(r.seed, KIND_K, layer, 4095, blk))
     k = torch.randn((n_steps, B, n_kv_heads, D), generator=g, device=device)
     k = (k + mag[:, :, None, None] * u).to(dt)
-    g.manual_seed(_torch_seed(r.seed, KIND_V, layer, 4095))
+    g.manual_seed(_torch_seed(r.seed, KIND_V, layer, 4095, blk))
     v = torch.randn((n_steps, B, n_kv_heads, D), generator=g, device=device).to(dt)
     return q.contiguous(), k.contiguous(), v.contiguous()
