@@ -1,0 +1,731 @@
+// Device-side building blocks shared by the decode-step kernels
+// (h2o_kernels.hip: FMA path; h2o_mfma.hip: matrix-core path): lane and wave
+// reductions, raw buffer loads, workgroup scans, the arg-min and radix
+// selections, Philox4x64-10, the two K/V slot layouts, the hole fill, and the
+// part of the step that follows the softmax statistics (score accumulation,
+// selection, eviction bookkeeping and in-place compaction).
+#pragma once
+
+#include "h2o_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+namespace h2o {
+namespace {
+
+// ---------------------------------------------------------------- row formats
+struct RowBf16 {  // 8 bf16 per 16-byte vector; widening is exact
+    static constexpr int EPL = 8;
+    __device__ static inline void unpack(const uint4& r, float (&x)[8])
+    {
+        x[0] = __uint_as_float(r.x << 16);
+        x[1] = __uint_as_float(r.x & 0xffff0000u);
+        x[2] = __uint_as_float(r.y << 16);
+        x[3] = __uint_as_float(r.y & 0xffff0000u);
+        x[4] = __uint_as_float(r.z << 16);
+        x[5] = __uint_as_float(r.z & 0xffff0000u);
+        x[6] = __uint_as_float(r.w << 16);
+        x[7] = __uint_as_float(r.w & 0xffff0000u);
+    }
+};
+
+struct RowF32 {  // 4 fp32 per 16-byte vector
+    static constexpr int EPL = 4;
+    __device__ static inline void unpack(const uint4& r, float (&x)[4])
+    {
+        x[0] = __uint_as_float(r.x);
+        x[1] = __uint_as_float(r.y);
+        x[2] = __uint_as_float(r.z);
+        x[3] = __uint_as_float(r.w);
+    }
+};
+
+// -------------------------------------------------------------- reductions
+template <int CTRL>
+__device__ inline float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each row of 16 lanes, result in every lane of the row:
+// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror.
+__device__ inline float sum16(float v)
+{
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
+    return v;
+}
+
+// sum16 of N independent values, one DPP stage at a time across them so the
+// wait states each DPP read needs are filled by the other rows' work.
+template <int N>
+__device__ inline void sum16_n(float (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0xB1>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0x4E>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0x141>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<0x140>(v[i]);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-row exchange within a wave (gfx950 permlane swaps).  Swapping a value
+// with itself leaves, in every lane, the pair (own row's value, partner row's
+// value) in some order; a commutative combine of the pair then gives every
+// lane the result for rows {r, r^1} (x16) or halves {lo, hi} (x32).
+struct Pair {
+    unsigned a, b;
+};
+__device__ inline Pair xrow16(unsigned v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return {r[0], r[1]};
+}
+__device__ inline Pair xrow32(unsigned v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return {r[0], r[1]};
+}
+
+// Raw buffer access (gfx9 family resource word 3): reads past num_records
+// bytes return zero without touching memory.
+constexpr int kBufWord3 = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    uint4 v;
+    __builtin_memcpy(&v, &x, 16);
+    return v;
+}
+
+// Barrier for exchanges through LDS only: waits for this wave's LDS accesses,
+// not for its global stores (which __syncthreads' release fence would wait for).
+__device__ inline void lds_barrier()
+{
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct ScanSmem {
+    int wsum[16];
+    int total;
+};
+
+// Exclusive scan of one int per thread over the workgroup; returns the
+// thread's offset, *total receives the sum.  Contains barriers.
+template <int NT>
+__device__ int block_excl_scan(int v, ScanSmem& ss, int* total)
+{
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    if (lane == 63) ss.wsum[w] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < NW; ++i) {
+            const int x = ss.wsum[i];
+            ss.wsum[i] = run;
+            run += x;
+        }
+        ss.total = run;
+    }
+    __syncthreads();
+    const int r = ss.wsum[w] + inc - v;
+    *total = ss.total;
+    __syncthreads();
+    return r;
+}
+
+template <int NT>
+__device__ double block_sum_f64(double v, double* sh)
+{
+    constexpr int NW = NT / 64;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < NW; ++i) s += sh[i];
+    __syncthreads();
+    return s;  // valid in thread 0
+}
+
+template <int NT>
+__device__ int block_sum_i32(int v, int* sh)
+{
+    constexpr int NW = NT / 64;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    int s = 0;
+    for (int i = 0; i < NW; ++i) s += sh[i];
+    __syncthreads();
+    return s;  // valid in every thread
+}
+
+// ------------------------------------------------------------- wave arg-min
+// (score, position, slot) triples; smaller score wins, equal scores go to the
+// higher position (so the lower position is kept); slot < 0 = no candidate.
+template <typename ST>
+__device__ inline void take_better(ST& bs, int& bp, int& bj, ST os, int op, int oj)
+{
+    if (oj >= 0 && (bj < 0 || os < bs || (os == bs && op > bp))) {
+        bs = os;
+        bp = op;
+        bj = oj;
+    }
+}
+
+template <int CTRL>
+__device__ inline int dpp_i(int v)
+{
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
+template <int CTRL, typename ST>
+__device__ inline ST dpp_s(ST v)
+{
+    if constexpr (sizeof(ST) == 4) {
+        return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+    } else {
+        const long long u = __double_as_longlong(v);
+        const int lo = dpp_i<CTRL>((int)(u & 0xffffffffll)), hi = dpp_i<CTRL>((int)(u >> 32));
+        return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+    }
+}
+
+template <int CTRL, typename ST>
+__device__ inline void argmin_step(ST& bs, int& bp, int& bj)
+{
+    take_better(bs, bp, bj, dpp_s<CTRL>(bs), dpp_i<CTRL>(bp), dpp_i<CTRL>(bj));
+}
+
+// Every lane ends with the wave's best: four DPP stages within each row of
+// 16 lanes (quad_perm 1,0,3,2 / 2,3,0,1, row_half_mirror, row_mirror), then
+// two lane shuffles across the rows.
+template <bool X32, typename ST>
+__device__ inline void argmin_xrow(ST& bs, int& bp, int& bj)
+{
+    auto sw = [](unsigned v) { return X32 ? xrow32(v) : xrow16(v); };
+    const Pair p = sw((unsigned)bp), j = sw((unsigned)bj);
+    ST s0, s1;
+    if constexpr (sizeof(ST) == 4) {
+        const Pair q = sw(__float_as_uint(bs));
+        s0 = __uint_as_float(q.a);
+        s1 = __uint_as_float(q.b);
+    } else {
+        const unsigned long long u = (unsigned long long)__double_as_longlong(bs);
+        const Pair lo = sw((unsigned)u), hi = sw((unsigned)(u >> 32));
+        s0 = __longlong_as_double((long long)(((unsigned long long)hi.a << 32) | lo.a));
+        s1 = __longlong_as_double((long long)(((unsigned long long)hi.b << 32) | lo.b));
+    }
+    ST rs = s0;
+    int rp = (int)p.a, rj = (int)j.a;
+    take_better(rs, rp, rj, s1, (int)p.b, (int)j.b);
+    bs = rs;
+    bp = rp;
+    bj = rj;
+}
+
+template <typename ST>
+__device__ inline void wave_argmin(ST& bs, int& bp, int& bj)
+{
+    argmin_step<0xB1>(bs, bp, bj);
+    argmin_step<0x4E>(bs, bp, bj);
+    argmin_step<0x141>(bs, bp, bj);
+    argmin_step<0x140>(bs, bp, bj);
+    argmin_xrow<false>(bs, bp, bj);
+    argmin_xrow<true>(bs, bp, bj);
+}
+
+// ------------------------------------------------------------------ Philox
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): word 0 of the block at
+// counter (c0, c1, c2, c3) under key (k0, k1).
+__device__ inline unsigned long long philox_word0(unsigned long long c0, unsigned long long c1,
+                                                  unsigned long long c2, unsigned long long c3,
+                                                  unsigned long long k0, unsigned long long k1)
+{
+    constexpr unsigned long long M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    constexpr unsigned long long W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const unsigned long long hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+        const unsigned long long hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        const unsigned long long y0 = hi1 ^ c1 ^ k0, y2 = hi0 ^ c3 ^ k1;
+        c0 = y0;
+        c1 = lo1;
+        c2 = y2;
+        c3 = lo0;
+    }
+    return c0;
+}
+
+// Order-preserving unsigned image of a float / double (for radix keys).
+__device__ inline unsigned ord32(float f)
+{
+    const unsigned u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline unsigned long long ord64(double f)
+{
+    const unsigned long long u = (unsigned long long)__double_as_longlong(f);
+    return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+
+// ----------------------------------------------------------- radix select
+// Workgroup radix select of the e smallest 96-bit keys (w[2] most
+// significant) among the candidates key_of() accepts, 8 bits per pass,
+// starting at digit d0 (digits 0..3 of w[2], 4..7 of w[1], 8..11 of w[0]).
+// Keys are unique (the low word holds ~position).  On return the selected
+// prefix p[] / mask mk[] satisfy: victim <=> (w & mk) <= p lexicographically.
+struct RadixSmem {
+    unsigned hist[256];
+    unsigned p[3], mk[3];
+    unsigned rem, sel_bin, sel_below, sel_cnt;
+    int done;
+};
+
+template <int NT, typename KeyFn>
+__device__ void radix_select(KeyFn key_of, int n_att, int e, int d0, RadixSmem& rs)
+{
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        rs.p[0] = rs.p[1] = rs.p[2] = 0;
+        rs.mk[0] = rs.mk[1] = rs.mk[2] = 0;
+        rs.rem = (unsigned)e;
+        rs.sel_bin = rs.sel_below = rs.sel_cnt = 0;
+        rs.done = 0;
+    }
+    __syncthreads();
+    for (int d = d0; d < 12; ++d) {
+        for (int i = tid; i < 256; i += NT) rs.hist[i] = 0;
+        __syncthreads();
+        const int wi = 2 - (d >> 2);
+        const int sh = 24 - 8 * (d & 3);
+        const unsigned p0 = rs.p[0], p1 = rs.p[1], p2 = rs.p[2];
+        const unsigned m0 = rs.mk[0], m1 = rs.mk[1], m2 = rs.mk[2];
+        for (int j = tid; j < n_att; j += NT) {
+            unsigned w[3];
+            if (key_of(j, w) && (w[0] & m0) == p0 && (w[1] & m1) == p1 && (w[2] & m2) == p2)
+            {
+                const unsigned word = wi == 2 ? w[2] : (wi == 1 ? w[1] : w[0]);
+                atomicAdd(&rs.hist[(word >> sh) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            unsigned c[4], loc = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[k] = rs.hist[tid * 4 + k];
+                loc += c[k];
+            }
+            unsigned inc = loc;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned y = __shfl_up(inc, off);
+                if (tid >= off) inc += y;
+            }
+            unsigned run = inc - loc;
+            const unsigned rem = rs.rem;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (run < rem && rem <= run + c[k]) {
+                    rs.sel_bin = (unsigned)(tid * 4 + k);
+                    rs.sel_below = run;
+                    rs.sel_cnt = c[k];
+                }
+                run += c[k];
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            rs.rem -= rs.sel_below;
+            rs.p[wi] |= rs.sel_bin << sh;
+            rs.mk[wi] |= 255u << sh;
+            if (rs.sel_cnt == rs.rem) rs.done = 1;
+        }
+        __syncthreads();
+        if (rs.done) break;
+    }
+}
+
+__device__ inline bool key_le(const unsigned (&w)[3], const RadixSmem& rs)
+{
+    const unsigned a2 = w[2] & rs.mk[2], a1 = w[1] & rs.mk[1], a0 = w[0] & rs.mk[0];
+    if (a2 != rs.p[2]) return a2 < rs.p[2];
+    if (a1 != rs.p[1]) return a1 < rs.p[1];
+    return a0 <= rs.p[0];
+}
+
+// ------------------------------------------------------------- hole fill
+// Writes, in slot order, the slots j in [lo, hi) for which pred(j) holds into
+// list[0..count), returns count (in every thread).  Contains barriers.
+template <int NT, typename Pred>
+__device__ int collect(int lo, int hi, Pred pred, int32_t* list, ScanSmem& ss)
+{
+    const int n = hi > lo ? hi - lo : 0;
+    const int chunk = (n + NT - 1) / NT;
+    const int a = lo + (int)threadIdx.x * chunk;
+    const int z = min(hi, a + chunk);
+    int c = 0;
+    for (int j = a; j < z; ++j) c += pred(j) ? 1 : 0;
+    int total;
+    int off = block_excl_scan<NT>(c, ss, &total);
+    for (int j = a; j < z; ++j)
+        if (pred(j)) list[off++] = j;
+    return total;
+}
+
+template <bool PAGED>
+struct SlotMap {
+    size_t base;        // contiguous: first slot of the unit
+    const int32_t* bt;  // paged: the sequence's block-table row
+    int h, Hkv;
+    __device__ inline size_t operator()(int slot) const
+    {
+        if constexpr (PAGED)
+            return ((size_t)bt[slot >> kPageShift] * Hkv + h) * kPageSize + (slot & (kPageSize - 1));
+        else
+            return base + (size_t)slot;
+    }
+};
+
+// ------------------------------------------------------- K/V slot layouts
+// A slot index si (the unit's first slot + slot, or the page-derived index)
+// names one token's K row and V row.  Rows move as 16 chunks of 16 bytes;
+// chunk c holds elements 8c..8c+7 (bf16) or 4c..4c+3 (fp32).
+//
+// KvRows: the K row of slot si is 16-byte vectors [16 si, 16 si + 16); V alike.
+struct KvRows {
+    __device__ static inline size_t kvec(size_t si, int c) { return si * kRowVecs + (size_t)c; }
+    __device__ static inline void store(void* kc, void* vc, size_t si, int c, uint4 k, uint4 v)
+    {
+        reinterpret_cast<uint4*>(kc)[kvec(si, c)] = k;
+        reinterpret_cast<uint4*>(vc)[kvec(si, c)] = v;
+    }
+    __device__ static inline void copy(void* kc, void* vc, size_t src, size_t dst, int c)
+    {
+        uint4* K = reinterpret_cast<uint4*>(kc);
+        uint4* V = reinterpret_cast<uint4*>(vc);
+        K[kvec(dst, c)] = K[kvec(src, c)];
+        V[kvec(dst, c)] = V[kvec(src, c)];
+    }
+};
+
+// KvTiles (bf16 rows of 128, contiguous slots, unit capacity a multiple of
+// 32): the operand orders of the 16x16x32 bf16 matrix instruction.
+//   K: 16-slot blocks laid out [chunk c][slot % 16][16 B]: a wave's 16-byte
+//      load at vector (block * 256 + kb * 64 + lane) gives lane l the d range
+//      32 kb + 8 (l / 16) .. +8 of slot l % 16 -- a 16 x 32 A operand.
+//   V: 32-slot blocks laid out [d / 16][lane group q][d % 16][8 slots], lane
+//      group q holding slots {4q..4q+3, 16+4q..16+4q+3} in that order: the
+//      load at vector (block * 512 + db * 64 + lane) gives lane l, for
+//      d = 16 db + l % 16, the 8 slots of its group -- a 16 x 32 A operand
+//      of V^T whose k order matches the logit tile's C layout.
+// Each wave-wide load reads 1 KB in one piece.
+struct KvTiles {
+    __device__ static inline size_t kvec(size_t si, int c)
+    {
+        return (si >> 4) * 256 + (size_t)c * 16 + (si & 15);
+    }
+    __device__ static inline size_t velem(size_t si, int d)
+    {
+        const unsigned u = (unsigned)(si & 31);
+        return (si >> 5) * 4096 +
+               (size_t)((d >> 4) * 512 + (int)((u & 15) >> 2) * 128 + (d & 15) * 8 +
+                        (int)(((u >> 4) << 2) | (u & 3)));
+    }
+    __device__ static inline void store(void* kc, void* vc, size_t si, int c, uint4 k, uint4 v)
+    {
+        reinterpret_cast<uint4*>(kc)[kvec(si, c)] = k;
+        unsigned short* V = reinterpret_cast<unsigned short*>(vc);
+        const unsigned w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) V[velem(si, 8 * c + e)] = (unsigned short)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+    __device__ static inline void copy(void* kc, void* vc, size_t src, size_t dst, int c)
+    {
+        uint4* K = reinterpret_cast<uint4*>(kc);
+        K[kvec(dst, c)] = K[kvec(src, c)];
+        unsigned short* V = reinterpret_cast<unsigned short*>(vc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) V[velem(dst, 8 * c + e)] = V[velem(src, 8 * c + e)];
+    }
+};
+
+// In-place compaction of one unit: live slots of [n2, n_att) move into the
+// holes (ps == -1) of [0, n2), n2 = n_att - e.  Sources and destinations are
+// disjoint, so every move is independent.  Contains barriers.
+template <int NT, typename ST, typename KV, typename SlotFn>
+__device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n_att, int e,
+                           bool has_scores, ScanSmem& ss)
+{
+    const int n2 = n_att - e;
+    int32_t* hl = s.iscr + (size_t)unit * 2 * cap;
+    int32_t* ll = hl + cap;
+    int32_t* ps = s.ps;
+    const int nh = collect<NT>(0, n2, [&](int j) { return ps[sidx(j)] < 0; }, hl, ss);
+    const int nl = collect<NT>(n2, n_att, [&](int j) { return ps[sidx(j)] >= 0; }, ll, ss);
+    __syncthreads();
+    if (nh != nl) {
+        if (threadIdx.x == 0) atomicOr(s.err, kErrCompact);
+        return;
+    }
+    ST* sc = (ST*)s.sc;
+    const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;
+    for (int i = grp; i < nh; i += NT / 16) {
+        const size_t src = sidx(ll[i]), dst = sidx(hl[i]);
+        KV::copy(s.kc, s.vc, src, dst, sub);
+        if (sub == 0) {
+            if (has_scores) sc[dst] = sc[src];
+            ps[dst] = ps[src];
+        }
+    }
+}
+
+
+// ------------------------------------------------------------ step tail
+// Shared memory of the tail.
+template <typename ST, int NW>
+struct TailSmem {
+    ST new_score;
+    ST bs[NW];
+    int bp[NW], bj[NW];
+    double dsum[NW];
+    int isum[NW];
+    ScanSmem scan;
+    RadixSmem rad;
+};
+
+// Everything the step does once the softmax maximum Mg and normaliser 1/L
+// of every query head of the group are known (all threads call it):
+//   H2O: p = 2^(s - M) / L per slot (logits in the log2 domain at
+//        logit[g * lstride + j], the new token at j = n), summed over the
+//        group, added to the cumulative score; with one token to go, the
+//        arg-min over the candidates (score ascending, position descending)
+//        names the victim, which the new token replaces in place when fused.
+//   bulk (e > 1, Random Attention events): radix select of the e smallest
+//        keys, victims marked, holes filled when fused.
+// pf_s / pf_p: score and position of slots tid + k * NT (k < PF), fetched
+// early by the caller; knr / vnr: chunk tid of the new token's K / V row in
+// threads tid < 16; emass0: the unit's evicted mass before the step.
+// Definitions: "Attention Sinks and KV cache eviction" sec. 4.2 (cumulative
+// score; sinks, heavy hitters and recent window), "H2O: Heavy-Hitter Oracle"
+// (greedy eviction under budget K), "Random Attention" (method).
+template <int NT, int G, int PF, typename ST, bool PAGED, typename KV>
+__device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, TailSmem<ST, NT / 64>& sm,
+                                 int unit, int b, int h, int P, int t, int n, int e, bool inplace_new,
+                                 const float* logit, int lstride, const float (&Mg)[G],
+                                 const float (&invLg)[G], const ST (&pf_s)[PF], const int (&pf_p)[PF],
+                                 uint4 knr, uint4 vnr, double emass0)
+{
+    constexpr int NW = NT / 64;
+    const Geometry& gm = a.g;
+    const State& S = a.s;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, sub = tid & 15;
+    const int n_att = n + 1;
+    const bool h2o = a.sc.selector == 0;
+    ST* scp = reinterpret_cast<ST*>(S.sc);
+    int32_t* psp = S.ps;
+
+    int K = 0, HH = 0, W = 0;
+    if (h2o) schedule(a.sc, t + 1, K, HH, W);
+    const int lo_c = a.sc.n_sink, hi_c = t + 1 - W;  // H2O candidates: lo_c <= pos < hi_c
+
+    // ---- phase 2 (H2O): accumulate scores; arg-min when one token goes ---
+    if (h2o) {
+        ST bs = (ST)0;
+        int bp = -1, bj = -1;
+        // slot j: add its weights of this step (summed over the group) to its
+        // score; the new token (j == n) starts from zero
+        auto visit = [&](int j, ST old, int pos) {
+            float p = 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                p += fast_exp2(logit[(size_t)g * lstride + j] - Mg[g]) * invLg[g];
+            const ST nw = old + (ST)p;
+            if (j < n) {
+                scp[sidx(j)] = nw;
+            } else {
+                sm.new_score = nw;
+                if (!inplace_new) {
+                    const size_t si = sidx(n);
+                    scp[si] = nw;
+                    psp[si] = t;
+                }
+            }
+            if (e == 1 && pos >= lo_c && pos < hi_c) {
+                if (bj < 0 || nw < bs || (nw == bs && pos > bp)) {
+                    bs = nw;
+                    bp = pos;
+                    bj = j;
+                }
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int j = tid + k * NT;
+            if (j < n_att) visit(j, j < n ? pf_s[k] : (ST)0, j < n ? pf_p[k] : t);
+        }
+        for (int j = tid + PF * NT; j < n_att; j += NT) {
+            if (j < n) {
+                const size_t si = sidx(j);
+                visit(j, scp[si], psp[si]);
+            } else {
+                visit(j, (ST)0, t);
+            }
+        }
+        if (e == 1) {
+            wave_argmin(bs, bp, bj);
+            if (lane == 0) {
+                sm.bs[w] = bs;
+                sm.bp[w] = bp;
+                sm.bj[w] = bj;
+            }
+            lds_barrier();
+            ST vs = sm.bs[0];
+            int vp = sm.bp[0], vjj = sm.bj[0];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) take_better(vs, vp, vjj, sm.bs[ww], sm.bp[ww], sm.bj[ww]);
+            const int vj = vjj;
+            if (vj < 0) {
+                if (tid == 0) atomicOr(S.err, kErrNoCandidate);
+                return;
+            }
+            if (tid == 0) S.emass[unit] = emass0 + (double)vs;
+            // the victim slot's score / position are written by the thread that
+            // wrote its updated score above: same thread, same address, in order
+            const bool owner = (vj - tid) % NT == 0;
+            if (a.fused) {
+                if (vj != n) {
+                    if (tid < 16) KV::store(S.kc, S.vc, sidx(vj), sub, knr, vnr);
+                    if (owner) {
+                        scp[sidx(vj)] = sm.new_score;
+                        psp[sidx(vj)] = t;
+                    }
+                }
+                // the count stays n: one in, one out
+            } else {
+                if (owner) psp[sidx(vj)] = -1;
+                if (tid == 0) {
+                    S.vinfo[2 * unit] = 1;
+                    S.vinfo[2 * unit + 1] = vj;
+                    S.cnt[unit] = n_att;
+                }
+            }
+            return;
+        }
+    } else if (tid == 0) {
+        psp[sidx(n)] = t;  // Random: no score pass; record the appended position
+    }
+
+    if (e == 0) {
+        if (tid == 0) {
+            S.cnt[unit] = n_att;
+            if (!a.fused) {
+                S.vinfo[2 * unit] = 0;
+                S.vinfo[2 * unit + 1] = -1;
+            }
+        }
+        return;
+    }
+
+    // ---- phase 3: bulk selection (e > 1, or a Random Attention event) -----
+    __syncthreads();
+    int d0;
+    double vmass = 0.0;
+    int nv = 0;
+    if (h2o) {
+        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
+            const size_t si = sidx(j);
+            const int pos = psp[si];
+            if (pos < lo_c || pos >= hi_c) return false;
+            if constexpr (sizeof(ST) == 4) {
+                wk[2] = 0;
+                wk[1] = ord32((float)scp[si]);
+            } else {
+                const unsigned long long u = ord64((double)scp[si]);
+                wk[2] = (unsigned)(u >> 32);
+                wk[1] = (unsigned)u;
+            }
+            wk[0] = ~(unsigned)pos;
+            return true;
+        };
+        d0 = sizeof(ST) == 4 ? 4 : 0;
+        radix_select<NT>(key_of, n_att, e, d0, sm.rad);
+        for (int j = tid; j < n_att; j += NT) {
+            unsigned wk[3];
+            if (key_of(j, wk) && key_le(wk, sm.rad)) {
+                const size_t si = sidx(j);
+                vmass += (double)scp[si];
+                psp[si] = -1;
+                ++nv;
+            }
+        }
+    } else {
+        const unsigned long long k0 = a.sc.seed;
+        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
+            const int pos = psp[sidx(j)];
+            if (pos < P) return false;
+            const unsigned long long x =
+                philox_word0((unsigned long long)b, (unsigned long long)h, (unsigned long long)t,
+                             (unsigned long long)pos, k0, 0ull);
+            wk[2] = (unsigned)(x >> 32);
+            wk[1] = (unsigned)x;
+            wk[0] = ~(unsigned)pos;
+            return true;
+        };
+        radix_select<NT>(key_of, n_att, e, 0, sm.rad);
+        for (int j = tid; j < n_att; j += NT) {
+            unsigned wk[3];
+            if (key_of(j, wk) && key_le(wk, sm.rad)) {
+                psp[sidx(j)] = -1;
+                ++nv;
+            }
+        }
+    }
+    const int nv_all = block_sum_i32<NT>(nv, sm.isum);
+    const double vm = block_sum_f64<NT>(vmass, sm.dsum);
+    if (tid == 0) {
+        if (nv_all != e) atomicOr(S.err, kErrSelectCount);
+        if (h2o) S.emass[unit] = emass0 + vm;
+    }
+    if (a.fused) {
+        __syncthreads();
+        fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, h2o, sm.scan);
+        if (tid == 0) S.cnt[unit] = n_att - e;
+    } else if (tid == 0) {
+        S.vinfo[2 * unit] = e;
+        S.vinfo[2 * unit + 1] = -1;
+        S.cnt[unit] = n_att;
+    }
+}
+
+}  // namespace
+}  // namespace h2o

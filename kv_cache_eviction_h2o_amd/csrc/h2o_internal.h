@@ -26,6 +26,8 @@ struct Geometry {
     int maxp;       // paged: block-table row length (pages per sequence)
     int kv_bf16;    // 1 = bf16 rows, 0 = fp32 rows
     int score_f64;  // 1 = fp64 cumulative scores, 0 = fp32
+    int kv_tiles;   // 1 = K/V in matrix-instruction operand order (bf16, head_dim 128,
+                    //     contiguous, cap a multiple of 32, GQA group of 4 or 8)
 };
 
 struct State {  // device pointers owned by the context
@@ -117,8 +119,9 @@ struct GatherArgs {
     double* osc;      // [B*Hkv][capo]
 };
 
-// Launchers (h2o_kernels.hip).  Each returns the launch's hipError_t.
+// Launchers (h2o_kernels.hip unless noted).  Each returns the launch's hipError_t.
 hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st);
+hipError_t launch_step_mfma(const StepArgs& a, int max_n_att, hipStream_t st);  // h2o_mfma.hip
 hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);

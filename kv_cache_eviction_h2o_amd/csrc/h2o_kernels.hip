@@ -25,448 +25,10 @@
 // greedy eviction of the lowest cumulative score); "Random Attention"
 // method (prompt kept, per-head uniform eviction, period K with buffer r);
 // Philox4x64-10 from Salmon et al., SC'11.
-#include "h2o_internal.h"
-
-#include <hip/hip_runtime.h>
-
-#include <type_traits>
+#include "h2o_device.h"
 
 namespace h2o {
 namespace {
-
-// ---------------------------------------------------------------- row formats
-struct RowBf16 {  // 8 bf16 per 16-byte vector; widening is exact
-    static constexpr int EPL = 8;
-    __device__ static inline void unpack(const uint4& r, float (&x)[8])
-    {
-        x[0] = __uint_as_float(r.x << 16);
-        x[1] = __uint_as_float(r.x & 0xffff0000u);
-        x[2] = __uint_as_float(r.y << 16);
-        x[3] = __uint_as_float(r.y & 0xffff0000u);
-        x[4] = __uint_as_float(r.z << 16);
-        x[5] = __uint_as_float(r.z & 0xffff0000u);
-        x[6] = __uint_as_float(r.w << 16);
-        x[7] = __uint_as_float(r.w & 0xffff0000u);
-    }
-};
-
-struct RowF32 {  // 4 fp32 per 16-byte vector
-    static constexpr int EPL = 4;
-    __device__ static inline void unpack(const uint4& r, float (&x)[4])
-    {
-        x[0] = __uint_as_float(r.x);
-        x[1] = __uint_as_float(r.y);
-        x[2] = __uint_as_float(r.z);
-        x[3] = __uint_as_float(r.w);
-    }
-};
-
-// -------------------------------------------------------------- reductions
-template <int CTRL>
-__device__ inline float dpp(float v)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over each row of 16 lanes, result in every lane of the row:
-// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror.
-__device__ inline float sum16(float v)
-{
-    v += dpp<0xB1>(v);
-    v += dpp<0x4E>(v);
-    v += dpp<0x141>(v);
-    v += dpp<0x140>(v);
-    return v;
-}
-
-// sum16 of N independent values, one DPP stage at a time across them so the
-// wait states each DPP read needs are filled by the other rows' work.
-template <int N>
-__device__ inline void sum16_n(float (&v)[N])
-{
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp<0xB1>(v[i]);
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp<0x4E>(v[i]);
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp<0x141>(v[i]);
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp<0x140>(v[i]);
-}
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Cross-row exchange within a wave (gfx950 permlane swaps).  Swapping a value
-// with itself leaves, in every lane, the pair (own row's value, partner row's
-// value) in some order; a commutative combine of the pair then gives every
-// lane the result for rows {r, r^1} (x16) or halves {lo, hi} (x32).
-struct Pair {
-    unsigned a, b;
-};
-__device__ inline Pair xrow16(unsigned v)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return {r[0], r[1]};
-}
-__device__ inline Pair xrow32(unsigned v)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return {r[0], r[1]};
-}
-
-// Raw buffer access (gfx9 family resource word 3): reads past num_records
-// bytes return zero without touching memory.
-constexpr int kBufWord3 = 0x00020000;
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
-}
-__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off)
-{
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    uint4 v;
-    __builtin_memcpy(&v, &x, 16);
-    return v;
-}
-
-// Barrier for exchanges through LDS only: waits for this wave's LDS accesses,
-// not for its global stores (which __syncthreads' release fence would wait for).
-__device__ inline void lds_barrier()
-{
-    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-struct ScanSmem {
-    int wsum[16];
-    int total;
-};
-
-// Exclusive scan of one int per thread over the workgroup; returns the
-// thread's offset, *total receives the sum.  Contains barriers.
-template <int NT>
-__device__ int block_excl_scan(int v, ScanSmem& ss, int* total)
-{
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(inc, off);
-        if (lane >= off) inc += y;
-    }
-    if (lane == 63) ss.wsum[w] = inc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int i = 0; i < NW; ++i) {
-            const int x = ss.wsum[i];
-            ss.wsum[i] = run;
-            run += x;
-        }
-        ss.total = run;
-    }
-    __syncthreads();
-    const int r = ss.wsum[w] + inc - v;
-    *total = ss.total;
-    __syncthreads();
-    return r;
-}
-
-template <int NT>
-__device__ double block_sum_f64(double v, double* sh)
-{
-    constexpr int NW = NT / 64;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) sh[w] = v;
-    __syncthreads();
-    double s = 0.0;
-    if (threadIdx.x == 0)
-        for (int i = 0; i < NW; ++i) s += sh[i];
-    __syncthreads();
-    return s;  // valid in thread 0
-}
-
-template <int NT>
-__device__ int block_sum_i32(int v, int* sh)
-{
-    constexpr int NW = NT / 64;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) sh[w] = v;
-    __syncthreads();
-    int s = 0;
-    for (int i = 0; i < NW; ++i) s += sh[i];
-    __syncthreads();
-    return s;  // valid in every thread
-}
-
-// ------------------------------------------------------------- wave arg-min
-// (score, position, slot) triples; smaller score wins, equal scores go to the
-// higher position (so the lower position is kept); slot < 0 = no candidate.
-template <typename ST>
-__device__ inline void take_better(ST& bs, int& bp, int& bj, ST os, int op, int oj)
-{
-    if (oj >= 0 && (bj < 0 || os < bs || (os == bs && op > bp))) {
-        bs = os;
-        bp = op;
-        bj = oj;
-    }
-}
-
-template <int CTRL>
-__device__ inline int dpp_i(int v)
-{
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
-}
-
-template <int CTRL, typename ST>
-__device__ inline ST dpp_s(ST v)
-{
-    if constexpr (sizeof(ST) == 4) {
-        return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
-    } else {
-        const long long u = __double_as_longlong(v);
-        const int lo = dpp_i<CTRL>((int)(u & 0xffffffffll)), hi = dpp_i<CTRL>((int)(u >> 32));
-        return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-    }
-}
-
-template <int CTRL, typename ST>
-__device__ inline void argmin_step(ST& bs, int& bp, int& bj)
-{
-    take_better(bs, bp, bj, dpp_s<CTRL>(bs), dpp_i<CTRL>(bp), dpp_i<CTRL>(bj));
-}
-
-// Every lane ends with the wave's best: four DPP stages within each row of
-// 16 lanes (quad_perm 1,0,3,2 / 2,3,0,1, row_half_mirror, row_mirror), then
-// two lane shuffles across the rows.
-template <bool X32, typename ST>
-__device__ inline void argmin_xrow(ST& bs, int& bp, int& bj)
-{
-    auto sw = [](unsigned v) { return X32 ? xrow32(v) : xrow16(v); };
-    const Pair p = sw((unsigned)bp), j = sw((unsigned)bj);
-    ST s0, s1;
-    if constexpr (sizeof(ST) == 4) {
-        const Pair q = sw(__float_as_uint(bs));
-        s0 = __uint_as_float(q.a);
-        s1 = __uint_as_float(q.b);
-    } else {
-        const unsigned long long u = (unsigned long long)__double_as_longlong(bs);
-        const Pair lo = sw((unsigned)u), hi = sw((unsigned)(u >> 32));
-        s0 = __longlong_as_double((long long)(((unsigned long long)hi.a << 32) | lo.a));
-        s1 = __longlong_as_double((long long)(((unsigned long long)hi.b << 32) | lo.b));
-    }
-    ST rs = s0;
-    int rp = (int)p.a, rj = (int)j.a;
-    take_better(rs, rp, rj, s1, (int)p.b, (int)j.b);
-    bs = rs;
-    bp = rp;
-    bj = rj;
-}
-
-template <typename ST>
-__device__ inline void wave_argmin(ST& bs, int& bp, int& bj)
-{
-    argmin_step<0xB1>(bs, bp, bj);
-    argmin_step<0x4E>(bs, bp, bj);
-    argmin_step<0x141>(bs, bp, bj);
-    argmin_step<0x140>(bs, bp, bj);
-    argmin_xrow<false>(bs, bp, bj);
-    argmin_xrow<true>(bs, bp, bj);
-}
-
-// ------------------------------------------------------------------ Philox
-// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): word 0 of the block at
-// counter (c0, c1, c2, c3) under key (k0, k1).
-__device__ inline unsigned long long philox_word0(unsigned long long c0, unsigned long long c1,
-                                                  unsigned long long c2, unsigned long long c3,
-                                                  unsigned long long k0, unsigned long long k1)
-{
-    constexpr unsigned long long M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-    constexpr unsigned long long W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r > 0) {
-            k0 += W0;
-            k1 += W1;
-        }
-        const unsigned long long hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-        const unsigned long long hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
-        const unsigned long long y0 = hi1 ^ c1 ^ k0, y2 = hi0 ^ c3 ^ k1;
-        c0 = y0;
-        c1 = lo1;
-        c2 = y2;
-        c3 = lo0;
-    }
-    return c0;
-}
-
-// Order-preserving unsigned image of a float / double (for radix keys).
-__device__ inline unsigned ord32(float f)
-{
-    const unsigned u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ inline unsigned long long ord64(double f)
-{
-    const unsigned long long u = (unsigned long long)__double_as_longlong(f);
-    return (u >> 63) ? ~u : (u | (1ull << 63));
-}
-
-// ----------------------------------------------------------- radix select
-// Workgroup radix select of the e smallest 96-bit keys (w[2] most
-// significant) among the candidates key_of() accepts, 8 bits per pass,
-// starting at digit d0 (digits 0..3 of w[2], 4..7 of w[1], 8..11 of w[0]).
-// Keys are unique (the low word holds ~position).  On return the selected
-// prefix p[] / mask mk[] satisfy: victim <=> (w & mk) <= p lexicographically.
-struct RadixSmem {
-    unsigned hist[256];
-    unsigned p[3], mk[3];
-    unsigned rem, sel_bin, sel_below, sel_cnt;
-    int done;
-};
-
-template <int NT, typename KeyFn>
-__device__ void radix_select(KeyFn key_of, int n_att, int e, int d0, RadixSmem& rs)
-{
-    const int tid = threadIdx.x;
-    if (tid == 0) {
-        rs.p[0] = rs.p[1] = rs.p[2] = 0;
-        rs.mk[0] = rs.mk[1] = rs.mk[2] = 0;
-        rs.rem = (unsigned)e;
-        rs.sel_bin = rs.sel_below = rs.sel_cnt = 0;
-        rs.done = 0;
-    }
-    __syncthreads();
-    for (int d = d0; d < 12; ++d) {
-        for (int i = tid; i < 256; i += NT) rs.hist[i] = 0;
-        __syncthreads();
-        const int wi = 2 - (d >> 2);
-        const int sh = 24 - 8 * (d & 3);
-        const unsigned p0 = rs.p[0], p1 = rs.p[1], p2 = rs.p[2];
-        const unsigned m0 = rs.mk[0], m1 = rs.mk[1], m2 = rs.mk[2];
-        for (int j = tid; j < n_att; j += NT) {
-            unsigned w[3];
-            if (key_of(j, w) && (w[0] & m0) == p0 && (w[1] & m1) == p1 && (w[2] & m2) == p2)
-            {
-                const unsigned word = wi == 2 ? w[2] : (wi == 1 ? w[1] : w[0]);
-                atomicAdd(&rs.hist[(word >> sh) & 255u], 1u);
-            }
-        }
-        __syncthreads();
-        if (tid < 64) {
-            unsigned c[4], loc = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                c[k] = rs.hist[tid * 4 + k];
-                loc += c[k];
-            }
-            unsigned inc = loc;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const unsigned y = __shfl_up(inc, off);
-                if (tid >= off) inc += y;
-            }
-            unsigned run = inc - loc;
-            const unsigned rem = rs.rem;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if (run < rem && rem <= run + c[k]) {
-                    rs.sel_bin = (unsigned)(tid * 4 + k);
-                    rs.sel_below = run;
-                    rs.sel_cnt = c[k];
-                }
-                run += c[k];
-            }
-        }
-        __syncthreads();
-        if (tid == 0) {
-            rs.rem -= rs.sel_below;
-            rs.p[wi] |= rs.sel_bin << sh;
-            rs.mk[wi] |= 255u << sh;
-            if (rs.sel_cnt == rs.rem) rs.done = 1;
-        }
-        __syncthreads();
-        if (rs.done) break;
-    }
-}
-
-__device__ inline bool key_le(const unsigned (&w)[3], const RadixSmem& rs)
-{
-    const unsigned a2 = w[2] & rs.mk[2], a1 = w[1] & rs.mk[1], a0 = w[0] & rs.mk[0];
-    if (a2 != rs.p[2]) return a2 < rs.p[2];
-    if (a1 != rs.p[1]) return a1 < rs.p[1];
-    return a0 <= rs.p[0];
-}
-
-// ------------------------------------------------------------- hole fill
-// Writes, in slot order, the slots j in [lo, hi) for which pred(j) holds into
-// list[0..count), returns count (in every thread).  Contains barriers.
-template <int NT, typename Pred>
-__device__ int collect(int lo, int hi, Pred pred, int32_t* list, ScanSmem& ss)
-{
-    const int n = hi > lo ? hi - lo : 0;
-    const int chunk = (n + NT - 1) / NT;
-    const int a = lo + (int)threadIdx.x * chunk;
-    const int z = min(hi, a + chunk);
-    int c = 0;
-    for (int j = a; j < z; ++j) c += pred(j) ? 1 : 0;
-    int total;
-    int off = block_excl_scan<NT>(c, ss, &total);
-    for (int j = a; j < z; ++j)
-        if (pred(j)) list[off++] = j;
-    return total;
-}
-
-// In-place compaction of one unit: live slots of [n2, n_att) move into the
-// holes (ps == -1) of [0, n2), n2 = n_att - e.  Sources and destinations are
-// disjoint, so every move is independent.  Contains barriers.
-template <int NT, typename ST, typename SlotFn>
-__device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n_att, int e,
-                           bool has_scores, ScanSmem& ss)
-{
-    const int n2 = n_att - e;
-    int32_t* hl = s.iscr + (size_t)unit * 2 * cap;
-    int32_t* ll = hl + cap;
-    int32_t* ps = s.ps;
-    const int nh = collect<NT>(0, n2, [&](int j) { return ps[sidx(j)] < 0; }, hl, ss);
-    const int nl = collect<NT>(n2, n_att, [&](int j) { return ps[sidx(j)] >= 0; }, ll, ss);
-    __syncthreads();
-    if (nh != nl) {
-        if (threadIdx.x == 0) atomicOr(s.err, kErrCompact);
-        return;
-    }
-    uint4* kc = (uint4*)s.kc;
-    uint4* vc = (uint4*)s.vc;
-    ST* sc = (ST*)s.sc;
-    const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;
-    for (int i = grp; i < nh; i += NT / 16) {
-        const size_t src = sidx(ll[i]), dst = sidx(hl[i]);
-        kc[dst * kRowVecs + sub] = kc[src * kRowVecs + sub];
-        vc[dst * kRowVecs + sub] = vc[src * kRowVecs + sub];
-        if (sub == 0) {
-            if (has_scores) sc[dst] = sc[src];
-            ps[dst] = ps[src];
-        }
-    }
-}
-
-template <bool PAGED>
-struct SlotMap {
-    size_t base;        // contiguous: first slot of the unit
-    const int32_t* bt;  // paged: the sequence's block-table row
-    int h, Hkv;
-    __device__ inline size_t operator()(int slot) const
-    {
-        if constexpr (PAGED)
-            return ((size_t)bt[slot >> kPageShift] * Hkv + h) * kPageSize + (slot & (kPageSize - 1));
-        else
-            return base + (size_t)slot;
-    }
-};
 
 // ------------------------------------------------------------- step kernel
 template <int G>
@@ -491,13 +53,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     extern __shared__ __align__(16) unsigned char dsm[];
     __shared__ float red_m[NW][G], red_l[NW][G];
     __shared__ __align__(16) float red_o[NW][G][DR];
-    __shared__ ST s_new_score;
-    __shared__ ST s_bs[NW];
-    __shared__ int s_bp[NW], s_bj[NW];
-    __shared__ double s_dsum[NW];
-    __shared__ int s_isum[NW];
-    __shared__ ScanSmem s_scan;
-    __shared__ RadixSmem s_rad;
+    __shared__ TailSmem<ST, NW> tsm;
 
     const Geometry& gm = a.g;
     const State& S = a.s;
@@ -738,11 +294,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         process(bi * BR, ka, va);
     }
     // the new token's row goes to slot n unless it fills a victim's hole later
-    if (!inplace_new && tid < 16) {
-        const size_t r = sidx(n) * kRowVecs + sub;
-        reinterpret_cast<uint4*>(S.kc)[r] = knr;
-        reinterpret_cast<uint4*>(S.vc)[r] = vnr;
-    }
+    if (!inplace_new && tid < 16) KvRows::store(S.kc, S.vc, sidx(n), sub, knr, vnr);
 
     // merge the four lane groups (rows) of each wave with permlane swaps,
     // then the waves through LDS: one barrier, after which every thread
@@ -809,187 +361,14 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                                 acc[4 * i + 2] * invLg[g], acc[4 * i + 3] * invLg[g]);
     }
 
-    int K = 0, HH = 0, W = 0;
-    if (h2o) schedule(a.sc, t + 1, K, HH, W);
-    const int lo_c = a.sc.n_sink, hi_c = t + 1 - W;  // H2O candidates: lo_c <= pos < hi_c
-
-    // ---- phase 2 (H2O): accumulate scores; arg-min when one token goes ---
-    if (h2o) {
-        ST bs = (ST)0;
-        int bp = -1, bj = -1;
-        // slot j: add its weights of this step (summed over the group) to its
-        // score; the new token (j == n) starts from zero
-        auto visit = [&](int j, ST old, int pos) {
-            float p = 0.f;
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-                p += fast_exp2(logit[(size_t)g * lstride + j] - Mg[g]) * invLg[g];
-            const ST nw = old + (ST)p;
-            if (j < n) {
-                scp[sidx(j)] = nw;
-            } else {
-                s_new_score = nw;
-                if (!inplace_new) {
-                    const size_t si = sidx(n);
-                    scp[si] = nw;
-                    psp[si] = t;
-                }
-            }
-            if (e == 1 && pos >= lo_c && pos < hi_c) {
-                if (bj < 0 || nw < bs || (nw == bs && pos > bp)) {
-                    bs = nw;
-                    bp = pos;
-                    bj = j;
-                }
-            }
-        };
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
-            const int j = tid + k * NT;
-            if (j < n_att) visit(j, j < n ? pf_s[k] : (ST)0, j < n ? pf_p[k] : t);
-        }
-        for (int j = tid + PF * NT; j < n_att; j += NT) {
-            if (j < n) {
-                const size_t si = sidx(j);
-                visit(j, scp[si], psp[si]);
-            } else {
-                visit(j, (ST)0, t);
-            }
-        }
-        if (e == 1) {
-            wave_argmin(bs, bp, bj);
-            if (lane == 0) {
-                s_bs[w] = bs;
-                s_bp[w] = bp;
-                s_bj[w] = bj;
-            }
-            lds_barrier();
-            ST vs = s_bs[0];
-            int vp = s_bp[0], vjj = s_bj[0];
-#pragma unroll
-            for (int ww = 1; ww < NW; ++ww) take_better(vs, vp, vjj, s_bs[ww], s_bp[ww], s_bj[ww]);
-            const int vj = vjj;
-            if (vj < 0) {
-                if (tid == 0) atomicOr(S.err, kErrNoCandidate);
-                return;
-            }
-            if (tid == 0) S.emass[unit] = emass0 + (double)vs;
-            // the victim slot's score / position are written by the thread that
-            // wrote its updated score above: same thread, same address, in order
-            const bool owner = (vj - tid) % NT == 0;
-            if (a.fused) {
-                if (vj != n) {
-                    if (tid < 16) {
-                        const size_t r = sidx(vj) * kRowVecs + sub;
-                        reinterpret_cast<uint4*>(S.kc)[r] = knr;
-                        reinterpret_cast<uint4*>(S.vc)[r] = vnr;
-                    }
-                    if (owner) {
-                        scp[sidx(vj)] = s_new_score;
-                        psp[sidx(vj)] = t;
-                    }
-                }
-                // the count stays n: one in, one out
-            } else {
-                if (owner) psp[sidx(vj)] = -1;
-                if (tid == 0) {
-                    S.vinfo[2 * unit] = 1;
-                    S.vinfo[2 * unit + 1] = vj;
-                    S.cnt[unit] = n_att;
-                }
-            }
-            return;
-        }
-    } else if (tid == 0) {
-        psp[sidx(n)] = t;  // Random: no score pass; record the appended position
-    }
-
-    if (e == 0) {
-        if (tid == 0) {
-            S.cnt[unit] = n_att;
-            if (!a.fused) {
-                S.vinfo[2 * unit] = 0;
-                S.vinfo[2 * unit + 1] = -1;
-            }
-        }
-        return;
-    }
-
-    // ---- phase 3: bulk selection (e > 1, or a Random Attention event) -----
-    __syncthreads();
-    int d0;
-    double vmass = 0.0;
-    int nv = 0;
-    if (h2o) {
-        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
-            const size_t si = sidx(j);
-            const int pos = psp[si];
-            if (pos < lo_c || pos >= hi_c) return false;
-            if constexpr (sizeof(ST) == 4) {
-                wk[2] = 0;
-                wk[1] = ord32((float)scp[si]);
-            } else {
-                const unsigned long long u = ord64((double)scp[si]);
-                wk[2] = (unsigned)(u >> 32);
-                wk[1] = (unsigned)u;
-            }
-            wk[0] = ~(unsigned)pos;
-            return true;
-        };
-        d0 = sizeof(ST) == 4 ? 4 : 0;
-        radix_select<NT>(key_of, n_att, e, d0, s_rad);
-        for (int j = tid; j < n_att; j += NT) {
-            unsigned wk[3];
-            if (key_of(j, wk) && key_le(wk, s_rad)) {
-                const size_t si = sidx(j);
-                vmass += (double)scp[si];
-                psp[si] = -1;
-                ++nv;
-            }
-        }
-    } else {
-        const unsigned long long k0 = a.sc.seed;
-        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
-            const int pos = psp[sidx(j)];
-            if (pos < P) return false;
-            const unsigned long long x =
-                philox_word0((unsigned long long)b, (unsigned long long)h, (unsigned long long)t,
-                             (unsigned long long)pos, k0, 0ull);
-            wk[2] = (unsigned)(x >> 32);
-            wk[1] = (unsigned)x;
-            wk[0] = ~(unsigned)pos;
-            return true;
-        };
-        radix_select<NT>(key_of, n_att, e, 0, s_rad);
-        for (int j = tid; j < n_att; j += NT) {
-            unsigned wk[3];
-            if (key_of(j, wk) && key_le(wk, s_rad)) {
-                psp[sidx(j)] = -1;
-                ++nv;
-            }
-        }
-    }
-    const int nv_all = block_sum_i32<NT>(nv, s_isum);
-    const double vm = block_sum_f64<NT>(vmass, s_dsum);
-    if (tid == 0) {
-        if (nv_all != e) atomicOr(S.err, kErrSelectCount);
-        if (h2o) S.emass[unit] = emass0 + vm;
-    }
-    if (a.fused) {
-        __syncthreads();
-        fill_holes<NT, ST>(S, sidx, unit, gm.cap, n_att, e, h2o, s_scan);
-        if (tid == 0) S.cnt[unit] = n_att - e;
-    } else if (tid == 0) {
-        S.vinfo[2 * unit] = e;
-        S.vinfo[2 * unit + 1] = -1;
-        S.cnt[unit] = n_att;
-    }
+    step_tail<NT, G, PF, ST, PAGED, KvRows>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit,
+                                            lstride, Mg, invLg, pf_s, pf_p, knr, vnr, emass0);
 }
 
 // ---------------------------------------------------------- compact kernel
 constexpr int kCompactNT = 256;
 
-template <typename ST, bool PAGED>
+template <typename ST, bool PAGED, typename KV>
 __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a)
 {
     __shared__ ScanSmem s_scan;
@@ -1011,19 +390,14 @@ __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a
         if (v != last && v >= 0) {
             const int sub = threadIdx.x & 15;
             const size_t src = sidx(last), dst = sidx(v);
-            if (threadIdx.x < 16) {
-                uint4* kc = (uint4*)S.kc;
-                uint4* vc = (uint4*)S.vc;
-                kc[dst * kRowVecs + sub] = kc[src * kRowVecs + sub];
-                vc[dst * kRowVecs + sub] = vc[src * kRowVecs + sub];
-            }
+            if (threadIdx.x < 16) KV::copy(S.kc, S.vc, src, dst, sub);
             if (threadIdx.x == 0) {
                 if (has_scores) ((ST*)S.sc)[dst] = ((ST*)S.sc)[src];
                 S.ps[dst] = S.ps[src];
             }
         }
     } else {
-        fill_holes<kCompactNT, ST>(S, sidx, unit, gm.cap, n_att, e, has_scores, s_scan);
+        fill_holes<kCompactNT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, has_scores, s_scan);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1034,7 +408,7 @@ __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a
 }
 
 // ------------------------------------------------------------- prompt load
-template <typename ST, bool PAGED>
+template <typename ST, bool PAGED, typename KV>
 __global__ void __launch_bounds__(256) load_kernel(const LoadArgs a)
 {
     const Geometry& gm = a.g;
@@ -1055,8 +429,8 @@ __global__ void __launch_bounds__(256) load_kernel(const LoadArgs a)
     sidx.Hkv = gm.Hkv;
     const size_t src = ((size_t)(S.poff[b] + tok) * gm.Hkv + h) * kRowVecs + c;
     const size_t si = sidx(tok);
-    reinterpret_cast<uint4*>(S.kc)[si * kRowVecs + c] = reinterpret_cast<const uint4*>(a.pk)[src];
-    reinterpret_cast<uint4*>(S.vc)[si * kRowVecs + c] = reinterpret_cast<const uint4*>(a.pv)[src];
+    KV::store(S.kc, S.vc, si, c, reinterpret_cast<const uint4*>(a.pk)[src],
+              reinterpret_cast<const uint4*>(a.pv)[src]);
     if (c == 0) {
         if (S.sc)
             ((ST*)S.sc)[si] = a.init_scores
@@ -1145,6 +519,7 @@ hipError_t dispatch_g(const StepArgs& a, bool llds, size_t dyn, hipStream_t st)
 
 hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st)
 {
+    if (a.g.kv_tiles) return launch_step_mfma(a, max_n_att, st);
     const bool llds = (size_t)a.g.G * (size_t)max_n_att * 4 <= (size_t)kLogitLdsBytes;
     size_t dyn = 0;
     if (llds) dyn += (size_t)a.g.G * (size_t)a.lds_n * 4;
@@ -1163,11 +538,14 @@ hipError_t launch_compact(const CompactArgs& a, int /*max_slots*/, hipStream_t s
 {
     const dim3 grid(a.g.B * a.g.Hkv), block(kCompactNT);
     if (a.g.paged) {
-        if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((compact_kernel<float, true>), grid, block, 0, st, a);
+        if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, true, KvRows>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((compact_kernel<float, true, KvRows>), grid, block, 0, st, a);
+    } else if (a.g.kv_tiles) {
+        if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, false, KvTiles>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((compact_kernel<float, false, KvTiles>), grid, block, 0, st, a);
     } else {
-        if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, false>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((compact_kernel<float, false>), grid, block, 0, st, a);
+        if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, false, KvRows>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((compact_kernel<float, false, KvRows>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }
@@ -1177,11 +555,14 @@ hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st)
     const long long per_seq = (long long)max_prompt * a.g.Hkv * kRowVecs;
     const dim3 grid((unsigned)((per_seq + 255) / 256), a.g.B), block(256);
     if (a.g.paged) {
-        if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((load_kernel<float, true>), grid, block, 0, st, a);
+        if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, true, KvRows>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((load_kernel<float, true, KvRows>), grid, block, 0, st, a);
+    } else if (a.g.kv_tiles) {
+        if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, false, KvTiles>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((load_kernel<float, false, KvTiles>), grid, block, 0, st, a);
     } else {
-        if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, false>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((load_kernel<float, false>), grid, block, 0, st, a);
+        if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, false, KvRows>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((load_kernel<float, false, KvRows>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }
@@ -1200,3 +581,4 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t st)
 }
 
 }  // namespace h2o
+

@@ -1,0 +1,402 @@
+// Matrix-core decode step for GQA groups of 4 or 8 query heads per KV head
+// (bf16 K/V rows of 128, contiguous slots in the KvTiles layout).
+//
+// With G query heads sharing one KV head, q.K over a tile of slots is a
+// (slots x 128) by (128 x G) product and P.V a (128 x slots) by (slots x G)
+// one, so both run on v_mfma_f32_16x16x32_bf16.  q and the softmax weights p
+// are fp32: each value x is split into bf16 parts hi = bf16(x) and
+// lo = bf16(x - hi) (x = hi + lo to about 2^-16 relative), hi of head g in B
+// column g and lo in column g + 8.  K and V enter exactly (bf16), products
+// are exact and the sums fp32, so the logits and the output keep about
+// 16 significant bits of q and p.
+//
+// One workgroup of 8 waves owns one (sequence, KV head) unit.  Wave w takes
+// the 32-slot tiles w, w + 8, w + 16, ... and, per tile:
+//   S  = K_tile (32 x 128) . [q_hi | q_lo]^T     two 16-slot C blocks, 4 k-steps each
+//   s  = S[:, g] + S[:, g + 8]                   DPP row rotate by 8
+//   online softmax per head: running max / sum / output, the tile maximum
+//        across the wave's four lane groups by permlane swaps
+//   O += V_tile^T (128 x 32) . [p_hi | p_lo]     8 d-blocks, 1 k-step each
+// The logit tile's C layout (lane l: slots 4(l/16)+r and 16+4(l/16)+r of
+// column l%16) already is the layout of the P^T B operand, and the V tiles
+// list each lane group's slots in that order, so p never moves between
+// lanes.  K and V tiles are read with wave-wide 16-byte loads of 1 KB each,
+// two tiles in flight per wave.  The new token (slot n, from k_new / v_new)
+// seeds the running state of the wave that owns slot n's tile.  The waves
+// then merge through LDS and the shared tail (h2o_device.h) accumulates
+// scores, selects and compacts.
+//
+// Definitions followed: "Attention Sinks and KV cache eviction" sec. 3.1
+// (softmax attention of the new query over the kept keys and values),
+// sec. 1.1 (grouped-query attention: a group of query heads shares one KV
+// head) and sec. 4.2 (cumulative score summed over the decode steps).
+#include "h2o_device.h"
+
+namespace h2o {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kMNT = 512;  // threads per unit (8 waves, 2 per SIMD)
+constexpr int kMNW = kMNT / 64;
+constexpr int kMPF = 3;    // slots per thread whose score and position are fetched up front
+constexpr int kTile = 32;  // slots per tile
+
+__device__ inline bf16x8 as_bf16x8(const uint4& v)
+{
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ inline f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The bf16 part of x that a B column holds: x rounded to bf16 (hi column) or
+// the rounding residual rounded to bf16 (lo column).
+__device__ inline __bf16 split_part(float x, bool lo)
+{
+    const __bf16 hi = (__bf16)x;
+    return lo ? (__bf16)(x - (float)hi) : hi;
+}
+
+__device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+struct MTile {
+    uint4 k[8];  // [half * 4 + kb]: slots 16 half .. +16, d 32 kb .. +32
+    uint4 v[8];  // [db]: d 16 db .. +16, the lane group's 8 slots
+};
+
+template <int G, typename ST, bool LLDS>
+__global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
+{
+    static_assert(G == 4 || G == 8, "the matrix-core step takes GQA groups of 4 or 8");
+    constexpr int NT = kMNT, NW = kMNW, PF = kMPF, D = 128;
+    constexpr float kMaxFloor = -1e30f;
+
+    extern __shared__ __align__(16) unsigned char dsm[];
+    __shared__ float red_m[NW][G], red_l[NW][G];
+    __shared__ __align__(16) float red_o[NW][G][D];
+    __shared__ TailSmem<ST, NW> tsm;
+
+    const Geometry& gm = a.g;
+    const State& S = a.s;
+    const int unit = blockIdx.x;
+    const int b = unit / gm.Hkv, h = unit - b * gm.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lc = lane & 15, lg = lane >> 4;  // C column, lane group
+    const int head = lc & 7;                   // query head of column lc (a real head when < G)
+    const bool lo_col = lc >= 8;
+
+    const int P = a.seq_in_args ? a.seq_p[b] : S.t0[b];
+    const int t = P + a.step;
+    const int n = a.seq_in_args ? a.seq_n[b] : S.cnt[unit];
+    const bool h2o = a.sc.selector == 0;
+    const int e = evict_count(a.sc, t, P, n + 1);
+    const bool inplace_new = a.fused && h2o && e == 1;
+
+    float* logit = LLDS ? reinterpret_cast<float*>(dsm) : S.lscr + (size_t)unit * G * gm.cap;
+    const int lstride = LLDS ? a.lds_n : gm.cap;
+    SlotMap<false> sidx;
+    sidx.base = (size_t)unit * gm.cap;
+    sidx.h = h;
+    sidx.Hkv = gm.Hkv;
+    sidx.bt = nullptr;
+    ST* scp = reinterpret_cast<ST*>(S.sc);
+    int32_t* psp = S.ps;
+
+    // ---- loads, issued in the order their data is needed ------------------
+    // q of column lc's head: lane (lg, lc) holds d = 32 kb + 8 lg + i
+    const int qh = head < G ? head : 0;
+    const float4* qp =
+        reinterpret_cast<const float4*>(a.q + ((size_t)b * gm.Hq + (size_t)h * G + qh) * D);
+    float4 qraw[8];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        qraw[2 * kb] = qp[8 * kb + 2 * lg];
+        qraw[2 * kb + 1] = qp[8 * kb + 2 * lg + 1];
+    }
+    // the new token: K as an A operand whose 16 rows are all that token, V at
+    // the d = 16 db + 4 lg + r this lane accumulates, and chunk tid % 16 of
+    // both rows for the slot write
+    const uint4* knp = reinterpret_cast<const uint4*>(a.kn) + (size_t)unit * kRowVecs;
+    const uint4* vnp = reinterpret_cast<const uint4*>(a.vn) + (size_t)unit * kRowVecs;
+    uint4 kn4[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) kn4[kb] = knp[4 * kb + lg];
+    const uint2* vn2 = reinterpret_cast<const uint2*>(vnp);
+    uint2 vn8[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vn8[db] = vn2[4 * db + lg];
+    const uint4 knr = knp[tid & 15];
+    const uint4 vnr = vnp[tid & 15];
+    const double emass0 = S.emass[unit];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // K / V tiles through raw buffer loads over the unit's first ntiles
+    // tiles: a tile index past them reads zeros without a memory access
+    const int ntiles = (n + kTile - 1) / kTile;
+    const size_t ub = (size_t)unit * gm.cap * kRowBytes;
+    const unsigned tile_bytes = (unsigned)kTile * kRowBytes;
+    const auto rk = make_rsrc(reinterpret_cast<const char*>(S.kc) + ub, (unsigned)ntiles * tile_bytes);
+    const auto rv = make_rsrc(reinterpret_cast<const char*>(S.vc) + ub, (unsigned)ntiles * tile_bytes);
+    auto load_tile = [&](int tl, MTile& T) {
+        const unsigned base = (unsigned)tl * tile_bytes + (unsigned)lane * 16u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) T.k[i] = buf_load16(rk, base + (unsigned)i * 1024u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) T.v[i] = buf_load16(rv, base + (unsigned)i * 1024u);
+    };
+    const int cnt = w < ntiles ? (ntiles - 1 - w) / NW + 1 : 0;  // this wave's tiles
+    MTile TA, TB;
+    load_tile(w, TA);
+    load_tile(w + NW, TB);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // scores and positions of this thread's first PF phase-2 slots
+    ST pf_s[PF];
+    int pf_p[PF];
+    if (h2o) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int j = tid + k * NT;
+            const size_t si = sidx(j < n ? j : 0);
+            pf_s[k] = scp[si];
+            pf_p[k] = psp[si];
+        }
+    }
+
+    // B operand of q.K: column lc = hi (lc < 8) or lo part of head lc & 7
+    bf16x8 qop[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const float x[8] = {qraw[2 * kb].x, qraw[2 * kb].y, qraw[2 * kb].z, qraw[2 * kb].w,
+                            qraw[2 * kb + 1].x, qraw[2 * kb + 1].y, qraw[2 * kb + 1].z, qraw[2 * kb + 1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            qop[kb][i] = head < G ? split_part(x[i] * a.qscale, lo_col) : (__bf16)0.0f;
+    }
+
+    // the new token's logit (every row of the product is that token)
+    f32x4 cn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) cn = mma(as_bf16x8(kn4[kb]), qop[kb], cn);
+    const float s_new = cn[0] + dpp<0x128>(cn[0]);  // row_ror:8 adds the lo column
+
+    // running state; the owner of slot n's tile starts from the new token
+    // alone: m = its logit, weight 1 (counted once, in lane group 0), O = its
+    // V row in the hi columns
+    const bool own_new = w == (n / kTile) % NW;
+    float m = own_new ? s_new : kMaxFloor;
+    float l = (own_new && lg == 0) ? 1.f : 0.f;
+    f32x4 O[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        const bool take = own_new && !lo_col;
+        O[db][0] = take ? bf16_lo(vn8[db].x) : 0.f;
+        O[db][1] = take ? bf16_hi(vn8[db].x) : 0.f;
+        O[db][2] = take ? bf16_lo(vn8[db].y) : 0.f;
+        O[db][3] = take ? bf16_hi(vn8[db].y) : 0.f;
+    }
+
+    auto process = [&](int tl, MTile& T) {
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) c0 = mma(as_bf16x8(T.k[kb]), qop[kb], c0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) c1 = mma(as_bf16x8(T.k[4 + kb]), qop[kb], c1);
+        float s[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = c0[r] + dpp<0x128>(c0[r]);
+            s[4 + r] = c1[r] + dpp<0x128>(c1[r]);
+        }
+        // slots at or past n take no weight (their K / V may be stale)
+        const int j0 = tl * kTile + 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (j0 + r >= n) s[r] = -INFINITY;
+            if (j0 + 16 + r >= n) s[4 + r] = -INFINITY;
+        }
+        if (h2o && lc < G) {
+            float4* lp = reinterpret_cast<float4*>(logit + (size_t)lc * lstride + j0);
+            lp[0] = make_float4(s[0], s[1], s[2], s[3]);
+            lp[4] = make_float4(s[4], s[5], s[6], s[7]);
+        }
+        float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                         fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+        {
+            const Pair x = xrow16(__float_as_uint(mx));
+            mx = fmaxf(__uint_as_float(x.a), __uint_as_float(x.b));
+        }
+        {
+            const Pair x = xrow32(__float_as_uint(mx));
+            mx = fmaxf(__uint_as_float(x.a), __uint_as_float(x.b));
+        }
+        const float mn = fmaxf(m, mx);
+        const float al = fast_exp2(m - mn);
+        m = mn;
+        l *= al;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[db][r] *= al;
+        bf16x8 pb;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float p = fast_exp2(s[k] - mn);  // 2^-inf = 0 for masked slots
+            l += p;
+            pb[k] = split_part(p, lo_col);
+        }
+        // the last, partial tile: zero V of the slots past n so stale values
+        // cannot reach the sum through 0 * inf
+        if (tl == ntiles - 1 && (n % kTile) != 0) {
+            const int lim = n - tl * kTile;
+            unsigned mk[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int s0 = (2 * k < 4 ? 4 * lg + 2 * k : 16 + 4 * lg + 2 * k - 4);
+                mk[k] = (s0 < lim ? 0xffffu : 0u) | (s0 + 1 < lim ? 0xffff0000u : 0u);
+            }
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                T.v[db].x &= mk[0];
+                T.v[db].y &= mk[1];
+                T.v[db].z &= mk[2];
+                T.v[db].w &= mk[3];
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < 8; ++db) O[db] = mma(as_bf16x8(T.v[db]), pb, O[db]);
+    };
+
+    // two tiles in flight: the registers of the tile just consumed take the
+    // tile after next; the tail is peeled so the loop holds no conditional load
+    int i = 0;
+    for (; i + 2 < cnt; i += 2) {
+        process(w + NW * i, TA);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(w + NW * (i + 2), TA);
+        __builtin_amdgcn_sched_barrier(0);
+        process(w + NW * (i + 1), TB);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(w + NW * (i + 3), TB);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < cnt) process(w + NW * i, TA);
+    if (i + 1 < cnt) process(w + NW * (i + 1), TB);
+    // after this wave's own tile stores (slot n may lie in its last tile)
+    if (h2o && own_new && lc < G && lg == 0) logit[(size_t)lc * lstride + n] = s_new;
+
+    // ---- merge: lane groups (sum of l), hi + lo columns, then waves -------
+    {
+        const Pair x = xrow16(__float_as_uint(l));
+        l = __uint_as_float(x.a) + __uint_as_float(x.b);
+    }
+    {
+        const Pair x = xrow32(__float_as_uint(l));
+        l = __uint_as_float(x.a) + __uint_as_float(x.b);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[db][r] += dpp<0x128>(O[db][r]);
+    if (lc < G) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            *reinterpret_cast<float4*>(&red_o[w][lc][16 * db + 4 * lg]) =
+                make_float4(O[db][0], O[db][1], O[db][2], O[db][3]);
+        if (lg == 0) {
+            red_m[w][lc] = m;
+            red_l[w][lc] = l;
+        }
+    }
+    // logits kept in global scratch (very long units) need the full fence
+    if constexpr (LLDS) lds_barrier(); else __syncthreads();
+    float Mg[G], invLg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float M = kMaxFloor;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][g]);
+        float L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) L += red_l[ww][g] * fast_exp2(red_m[ww][g] - M);
+        Mg[g] = M;
+        invLg[g] = 1.0f / L;
+    }
+    if (tid < G * (D / 4)) {
+        const int g = tid / (D / 4), d4 = (tid % (D / 4)) * 4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float f = fast_exp2(red_m[ww][g] - Mg[g]);
+            const float4 v = *reinterpret_cast<const float4*>(&red_o[ww][g][d4]);
+            acc.x += v.x * f;
+            acc.y += v.y * f;
+            acc.z += v.z * f;
+            acc.w += v.w * f;
+        }
+        const float il = invLg[g];
+        *reinterpret_cast<float4*>(a.out + ((size_t)b * gm.Hq + (size_t)h * G + g) * D + d4) =
+            make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
+    }
+    // the new token's rows go to slot n unless they fill a victim's hole later
+    if (!inplace_new && tid < 16) KvTiles::store(S.kc, S.vc, sidx(n), tid, knr, vnr);
+
+    step_tail<NT, G, PF, ST, false, KvTiles>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit,
+                                             lstride, Mg, invLg, pf_s, pf_p, knr, vnr, emass0);
+}
+
+template <int G, typename ST, bool LLDS>
+hipError_t launch_mfma_t(const StepArgs& a, size_t dyn, hipStream_t st)
+{
+    auto k = mfma_step_kernel<G, ST, LLDS>;
+    static size_t dyn_set = 48 * 1024;  // largest dynamic LDS size granted so far
+    if (dyn > dyn_set) {
+        hipError_t err = hipFuncSetAttribute((const void*)k,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (err != hipSuccess) return err;
+        dyn_set = dyn;
+    }
+    hipLaunchKernelGGL(k, dim3(a.g.B * a.g.Hkv), dim3(kMNT), dyn, st, a);
+    return hipGetLastError();
+}
+
+template <int G, typename ST>
+hipError_t launch_mfma_g(const StepArgs& a, bool llds, size_t dyn, hipStream_t st)
+{
+    return llds ? launch_mfma_t<G, ST, true>(a, dyn, st) : launch_mfma_t<G, ST, false>(a, 0, st);
+}
+
+template <typename ST>
+hipError_t launch_mfma_s(const StepArgs& a, bool llds, size_t dyn, hipStream_t st)
+{
+    return a.g.G == 4 ? launch_mfma_g<4, ST>(a, llds, dyn, st) : launch_mfma_g<8, ST>(a, llds, dyn, st);
+}
+
+}  // namespace
+
+hipError_t launch_step_mfma(const StepArgs& a0, int max_n_att, hipStream_t st)
+{
+    const Geometry& g = a0.g;
+    if (!g.kv_tiles || !g.kv_bf16 || g.D != 128 || g.paged || (g.G != 4 && g.G != 8) ||
+        (g.cap % kTile) != 0)
+        return hipErrorInvalidValue;
+    StepArgs a = a0;
+    a.lds_n = (max_n_att + kTile - 1) / kTile * kTile;  // whole tiles of logits
+    bool llds = true;
+    size_t dyn = 0;
+    if (a.sc.selector == 0) {  // H2O keeps the logits for the score pass
+        llds = (size_t)g.G * a.lds_n * 4 <= (size_t)kLogitLdsBytes;
+        if (llds) dyn = (size_t)g.G * a.lds_n * 4;
+        else if (a.s.lscr == nullptr) return hipErrorInvalidValue;
+    }
+    return g.score_f64 ? launch_mfma_s<double>(a, llds, dyn, st) : launch_mfma_s<float>(a, llds, dyn, st);
+}
+
+}  // namespace h2o

@@ -297,6 +297,10 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
     g.maxp = g.paged ? (g.cap + kPageSize - 1) / kPageSize : 0;
     g.kv_bf16 = cfg->kv_dtype == H2O_BF16;
     g.score_f64 = cfg->selector == H2O_SEL_H2O && cfg->score_dtype == H2O_F64;
+    // GQA groups of 4 or 8 over bf16 rows of 128 run on the matrix cores, with
+    // K / V stored in operand order in whole 32-slot tiles
+    g.kv_tiles = g.kv_bf16 && g.D == 128 && !g.paged && (g.G == 4 || g.G == 8);
+    if (g.kv_tiles) g.cap = (g.cap + 31) & ~31;
     c->sc = make_sched(*cfg);
     const double scale = cfg->scale > 0.f ? (double)cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
     c->qscale = (float)(scale * 1.4426950408889634);  // log2(e)
