@@ -63,9 +63,11 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
 
     // the host knows every sequence's prompt length and retained count: taking
     // them from the arguments saves a dependent memory round trip at the start
-    const int P = a.seq_in_args ? a.seq_p[b] : S.t0[b];
+    // uniform over the workgroup: readfirstlane keeps them (and the buffer
+    // descriptors built from them) in scalar registers
+    const int P = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_p[b] : S.t0[b]);
     const int t = P + a.step;
-    const int n = a.seq_in_args ? a.seq_n[b] : S.cnt[unit];
+    const int n = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_n[b] : S.cnt[unit]);
     const int n_att = n + 1;
     const bool h2o = a.sc.selector == 0;
     const int e = evict_count(a.sc, t, P, n_att);

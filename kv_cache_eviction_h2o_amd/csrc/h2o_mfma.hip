@@ -87,14 +87,17 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     const State& S = a.s;
     const int unit = blockIdx.x;
     const int b = unit / gm.Hkv, h = unit - b * gm.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar)
     const int lc = lane & 15, lg = lane >> 4;  // C column, lane group
     const int head = lc & 7;                   // query head of column lc (a real head when < G)
     const bool lo_col = lc >= 8;
 
-    const int P = a.seq_in_args ? a.seq_p[b] : S.t0[b];
+    // uniform over the workgroup: readfirstlane keeps them (and the buffer
+    // descriptors built from them) in scalar registers
+    const int P = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_p[b] : S.t0[b]);
     const int t = P + a.step;
-    const int n = a.seq_in_args ? a.seq_n[b] : S.cnt[unit];
+    const int n = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_n[b] : S.cnt[unit]);
     const bool h2o = a.sc.selector == 0;
     const int e = evict_count(a.sc, t, P, n + 1);
     const bool inplace_new = a.fused && h2o && e == 1;
@@ -135,6 +138,12 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     const uint4 knr = knp[tid & 15];
     const uint4 vnr = vnp[tid & 15];
     const double emass0 = S.emass[unit];
+    // every wave's q and new-token loads enter the memory queues before any
+    // tile load of the workgroup (the older wave of each SIMD would otherwise
+    // issue all of its tile loads first and the younger one's q would wait
+    // behind them); a bare barrier: nothing waits for the data here
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // K / V tiles through raw buffer loads over the unit's first ntiles
@@ -317,33 +326,46 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     }
     // logits kept in global scratch (very long units) need the full fence
     if constexpr (LLDS) lds_barrier(); else __syncthreads();
+    // one lane per (wave, head) pair (lane i: wave (i % NP) / G, head i % G)
+    // reduces over the waves by butterflies; M_g, 1/L_g and the per-wave
+    // factors 2^(m - M_g) are then read from those lanes into scalars
+    constexpr int NP = NW * G;  // 32 or 64 pairs
+    const int pi = lane % NP;
+    const float mi = red_m[pi / G][pi % G], li = red_l[pi / G][pi % G];
+    float Mx = mi;
+#pragma unroll
+    for (int x = G; x < NP; x <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, x));
+    const float fi = fast_exp2(mi - Mx);
+    float Lx = li * fi;
+#pragma unroll
+    for (int x = G; x < NP; x <<= 1) Lx += __shfl_xor(Lx, x);
+    const float il_x = 1.0f / Lx;
+    auto bcast = [](float v, int src) {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+    };
     float Mg[G], invLg[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        float M = kMaxFloor;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][g]);
-        float L = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) L += red_l[ww][g] * fast_exp2(red_m[ww][g] - M);
-        Mg[g] = M;
-        invLg[g] = 1.0f / L;
+        Mg[g] = bcast(Mx, g);
+        invLg[g] = bcast(il_x, g);
     }
-    if (tid < G * (D / 4)) {
-        const int g = tid / (D / 4), d4 = (tid % (D / 4)) * 4;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    // output: NW / G waves per head, each a contiguous part of the row
+    {
+        constexpr int WPH = NW / G, DPW = D / WPH, EPT = DPW / 64;
+        const int g = w / WPH, d0 = (w % WPH) * DPW + lane * EPT;
+        float acc[EPT];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-            const float f = fast_exp2(red_m[ww][g] - Mg[g]);
-            const float4 v = *reinterpret_cast<const float4*>(&red_o[ww][g][d4]);
-            acc.x += v.x * f;
-            acc.y += v.y * f;
-            acc.z += v.z * f;
-            acc.w += v.w * f;
+            const float f = bcast(fi, ww * G + g);
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) acc[k] += red_o[ww][g][d0 + k] * f;
         }
-        const float il = invLg[g];
-        *reinterpret_cast<float4*>(a.out + ((size_t)b * gm.Hq + (size_t)h * G + g) * D + d4) =
-            make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
+        const float il = bcast(il_x, g);
+        float* op = a.out + ((size_t)b * gm.Hq + (size_t)h * G + g) * D + d0;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) op[k] = acc[k] * il;
     }
     // the new token's rows go to slot n unless they fill a victim's hole later
     if (!inplace_new && tid < 16) KvTiles::store(S.kc, S.vc, sidx(n), tid, knr, vnr);
