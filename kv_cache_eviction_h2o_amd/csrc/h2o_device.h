@@ -186,15 +186,16 @@ __device__ int block_sum_i32(int v, int* sh)
 
 // ------------------------------------------------------------- wave arg-min
 // (score, position, slot) triples; smaller score wins, equal scores go to the
-// higher position (so the lower position is kept); slot < 0 = no candidate.
+// higher position (so the lower position is kept).  "No candidate" is
+// (+inf, -1, -1): every candidate beats it, a +inf score through the higher
+// position.  Branch-free: the compare masks feed selects.
 template <typename ST>
 __device__ inline void take_better(ST& bs, int& bp, int& bj, ST os, int op, int oj)
 {
-    if (oj >= 0 && (bj < 0 || os < bs || (os == bs && op > bp))) {
-        bs = os;
-        bp = op;
-        bj = oj;
-    }
+    const bool take = (os < bs) | ((os == bs) & (op > bp));
+    bs = take ? os : bs;
+    bp = take ? op : bp;
+    bj = take ? oj : bj;
 }
 
 template <int CTRL>
@@ -560,7 +561,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
 
     // ---- phase 2 (H2O): accumulate scores; arg-min when one token goes ---
     if (h2o) {
-        ST bs = (ST)0;
+        ST bs = (ST)INFINITY;
         int bp = -1, bj = -1;
         // slot j: add its weights of this step (summed over the group) to its
         // score; the new token (j == n) starts from zero
@@ -580,13 +581,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
                     psp[si] = t;
                 }
             }
-            if (e == 1 && pos >= lo_c && pos < hi_c) {
-                if (bj < 0 || nw < bs || (nw == bs && pos > bp)) {
-                    bs = nw;
-                    bp = pos;
-                    bj = j;
-                }
-            }
+            if (e == 1 && pos >= lo_c && pos < hi_c) take_better(bs, bp, bj, nw, pos, j);
         };
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
@@ -609,11 +604,23 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
                 sm.bj[w] = bj;
             }
             lds_barrier();
-            ST vs = sm.bs[0];
-            int vp = sm.bp[0], vjj = sm.bj[0];
-#pragma unroll
-            for (int ww = 1; ww < NW; ++ww) take_better(vs, vp, vjj, sm.bs[ww], sm.bp[ww], sm.bj[ww]);
-            const int vj = vjj;
+            // lanes 0..NW-1 of every wave take one wave's best; three DPP
+            // stages within 8 lanes leave the workgroup's best in lane 0
+            static_assert(NW <= 8, "cross-wave arg-min covers up to 8 waves");
+            ST vs = lane < NW ? sm.bs[lane] : (ST)INFINITY;
+            int vp = lane < NW ? sm.bp[lane] : -1, vjj = lane < NW ? sm.bj[lane] : -1;
+            argmin_step<0xB1>(vs, vp, vjj);
+            argmin_step<0x4E>(vs, vp, vjj);
+            argmin_step<0x141>(vs, vp, vjj);
+            if constexpr (sizeof(ST) == 4) {
+                vs = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vs)));
+            } else {
+                const long long u = __double_as_longlong(vs);
+                const int lo = __builtin_amdgcn_readfirstlane((int)(u & 0xffffffffll));
+                const int hi = __builtin_amdgcn_readfirstlane((int)(u >> 32));
+                vs = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+            }
+            const int vj = __builtin_amdgcn_readfirstlane(vjj);
             if (vj < 0) {
                 if (tid == 0) atomicOr(S.err, kErrNoCandidate);
                 return;

@@ -10,8 +10,10 @@
 // are exact and the sums fp32, so the logits and the output keep about
 // 16 significant bits of q and p.
 //
-// One workgroup of 8 waves owns one (sequence, KV head) unit.  Wave w takes
-// the 32-slot tiles w, w + 8, w + 16, ... and, per tile:
+// One workgroup of 8 waves owns one (sequence, KV head) unit.  Wave w starts
+// on the 32-slot tiles w and w + 8 and then takes the next unclaimed tile from
+// an LDS counter each time it frees a register set (waves the memory system
+// serves faster take more tiles).  Per tile:
 //   S  = K_tile (32 x 128) . [q_hi | q_lo]^T     two 16-slot C blocks, 4 k-steps each
 //   s  = S[:, g] + S[:, g + 8]                   DPP row rotate by 8
 //   online softmax per head: running max / sum / output, the tile maximum
@@ -22,7 +24,8 @@
 // list each lane group's slots in that order, so p never moves between
 // lanes.  K and V tiles are read with wave-wide 16-byte loads of 1 KB each,
 // two tiles in flight per wave.  The new token (slot n, from k_new / v_new)
-// seeds the running state of the wave that owns slot n's tile.  The waves
+// seeds the running state of wave 0; every wave knows its logit, so the wave
+// that stores the tile holding slot n stores that logit there.  The waves
 // then merge through LDS and the shared tail (h2o_device.h) accumulates
 // scores, selects and compacts.
 //
@@ -82,6 +85,7 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     __shared__ float red_m[NW][G], red_l[NW][G];
     __shared__ __align__(16) float red_o[NW][G][D];
     __shared__ TailSmem<ST, NW> tsm;
+    __shared__ int s_next;  // next unclaimed tile
 
     const Geometry& gm = a.g;
     const State& S = a.s;
@@ -138,12 +142,13 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     const uint4 knr = knp[tid & 15];
     const uint4 vnr = vnp[tid & 15];
     const double emass0 = S.emass[unit];
+    if (tid == 0) s_next = 2 * NW;  // tiles 0 .. 2 NW - 1 are handed out statically
     // every wave's q and new-token loads enter the memory queues before any
     // tile load of the workgroup (the older wave of each SIMD would otherwise
     // issue all of its tile loads first and the younger one's q would wait
-    // behind them); a bare barrier: nothing waits for the data here
+    // behind them); the barrier waits for LDS only, not for that data
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // K / V tiles through raw buffer loads over the unit's first ntiles
@@ -160,10 +165,10 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
 #pragma unroll
         for (int i = 0; i < 8; ++i) T.v[i] = buf_load16(rv, base + (unsigned)i * 1024u);
     };
-    const int cnt = w < ntiles ? (ntiles - 1 - w) / NW + 1 : 0;  // this wave's tiles
     MTile TA, TB;
-    load_tile(w, TA);
-    load_tile(w + NW, TB);
+    int ta = w, tb = w + NW;
+    load_tile(ta, TA);
+    load_tile(tb, TB);
     __builtin_amdgcn_sched_barrier(0);
 
     // scores and positions of this thread's first PF phase-2 slots
@@ -196,10 +201,9 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     for (int kb = 0; kb < 4; ++kb) cn = mma(as_bf16x8(kn4[kb]), qop[kb], cn);
     const float s_new = cn[0] + dpp<0x128>(cn[0]);  // row_ror:8 adds the lo column
 
-    // running state; the owner of slot n's tile starts from the new token
-    // alone: m = its logit, weight 1 (counted once, in lane group 0), O = its
-    // V row in the hi columns
-    const bool own_new = w == (n / kTile) % NW;
+    // running state; wave 0 starts from the new token alone: m = its logit,
+    // weight 1 (counted once, in lane group 0), O = its V row in the hi columns
+    const bool own_new = w == 0;
     float m = own_new ? s_new : kMaxFloor;
     float l = (own_new && lg == 0) ? 1.f : 0.f;
     f32x4 O[8];
@@ -231,10 +235,12 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
             if (j0 + r >= n) s[r] = -INFINITY;
             if (j0 + 16 + r >= n) s[4 + r] = -INFINITY;
         }
-        if (h2o && lc < G) {
+        if (h2o && lc < G) {  // slot n of this tile (if any) takes the new token's logit
             float4* lp = reinterpret_cast<float4*>(logit + (size_t)lc * lstride + j0);
-            lp[0] = make_float4(s[0], s[1], s[2], s[3]);
-            lp[4] = make_float4(s[4], s[5], s[6], s[7]);
+            lp[0] = make_float4(j0 == n ? s_new : s[0], j0 + 1 == n ? s_new : s[1],
+                                j0 + 2 == n ? s_new : s[2], j0 + 3 == n ? s_new : s[3]);
+            lp[4] = make_float4(j0 + 16 == n ? s_new : s[4], j0 + 17 == n ? s_new : s[5],
+                                j0 + 18 == n ? s_new : s[6], j0 + 19 == n ? s_new : s[7]);
         }
         float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                          fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
@@ -284,22 +290,32 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     };
 
     // two tiles in flight: the registers of the tile just consumed take the
-    // tile after next; the tail is peeled so the loop holds no conditional load
-    int i = 0;
-    for (; i + 2 < cnt; i += 2) {
-        process(w + NW * i, TA);
+    // next unclaimed tile.  Claims only grow and the tile checked is always
+    // the smaller of the two held, so the first one past the end ends the
+    // loop; a load past the end reads zeros without a memory access.
+    auto claim = [&]() {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&s_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    for (;;) {
+        if (ta >= ntiles) break;
+        const int na = claim();
+        process(ta, TA);
+        ta = na;
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(w + NW * (i + 2), TA);
+        load_tile(ta, TA);
         __builtin_amdgcn_sched_barrier(0);
-        process(w + NW * (i + 1), TB);
+        if (tb >= ntiles) break;
+        const int nb = claim();
+        process(tb, TB);
+        tb = nb;
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(w + NW * (i + 3), TB);
+        load_tile(tb, TB);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (i < cnt) process(w + NW * i, TA);
-    if (i + 1 < cnt) process(w + NW * (i + 1), TB);
-    // after this wave's own tile stores (slot n may lie in its last tile)
-    if (h2o && own_new && lc < G && lg == 0) logit[(size_t)lc * lstride + n] = s_new;
+    // slot n outside every tile (n a multiple of 32): its logit slot is free
+    if (h2o && own_new && (n % kTile) == 0 && lc < G && lg == 0) logit[(size_t)lc * lstride + n] = s_new;
 
     // ---- merge: lane groups (sum of l), hi + lo columns, then waves -------
     {

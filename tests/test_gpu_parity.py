@@ -120,3 +120,44 @@ def test_initial_scores():
     rng = np.random.default_rng(5)
     init = rng.random((sum(lens), w.n_kv_heads)) * 0.01
     P().run_parity(w, 40, lens=lens, init_scores=init)
+
+
+# ------------------------------------------------ matrix-core path (G = 4, 8)
+def test_gqa_ragged_units_cross_tile_edges():
+    # units start at 5, 64 (a whole number of 32-slot tiles), 95 and 130 slots
+    # and grow by one a step, so n passes multiples of 32 and partial tiles
+    w = WL.LLAMA_GQA.scaled(batch=4, budget_fixed=100, hh_fixed=48)
+    rep = P().run_parity(w, 60, lens=[5, 64, 95, 130])
+    assert rep.evictions > 0
+
+
+def test_gqa_unfused_tiles_compaction():
+    # bulk hole fill and single moves in the operand-order layout
+    w = WL.LLAMA_GQA.scaled(batch=2, budget_fixed=200, hh_fixed=96)
+    rep = P().run_parity(w, 40, lens=[300, 150], fused=False)
+    assert rep.evictions > 0
+
+
+def test_gqa_logits_in_global_scratch():
+    # 8 heads x 2624 slots of logits exceed the LDS budget: global scratch
+    w = WL.LLAMA_GQA.scaled(batch=1, budget_fixed=2600, hh_fixed=1300)
+    rep = P().run_parity(w, 12, lens=[2700])
+    assert rep.evictions >= 8 * 100
+
+
+def test_gqa_group_of_four_h2o_fp32_scores():
+    w = WL.OPT_LAYER.scaled(batch=2, n_q_heads=8, n_kv_heads=2)
+    rep = P().run_parity(w, 40, lens=[400, 257])
+    assert rep.evictions > 0
+
+
+# ------------------------------------------------ FMA path with G >= 4
+def test_paged_group_of_four():
+    w = WL.PAGED_MIXED.scaled(batch=2, n_q_heads=8, n_kv_heads=2)
+    P().run_parity(w, 30, lens=[300, 700])
+
+
+def test_fp32_rows_group_of_eight():
+    w = WL.TINY_H2O.scaled(batch=2, n_q_heads=16, n_kv_heads=2)
+    rep = P().run_parity(w, 60, lens=[90, 200])
+    assert rep.evictions > 0
