@@ -43,7 +43,8 @@ from kv_cache_eviction_h2o_amd import workloads as WL  # noqa: E402
 
 METRIC = "retained KV tokens processed/sec per decode step (attn+evict+compact); % HBM peak"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc", "h2o_kernels.hip")
+CSRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc")
+KERNEL_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -142,8 +143,20 @@ class HipEvents:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every device source (a counter summary is valid for this value only)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def step_kernel_name(w) -> str:
+    """The step kernel the library launches for a workload: GQA groups of 4 or 8
+    over bf16 rows of 128 in contiguous slots run on the matrix cores."""
+    if w.kv_dtype == "bf16" and w.head_dim == 128 and not w.page_size and w.group in (4, 8):
+        return "mfma_step_kernel"
+    return "step_kernel"
 
 
 def retained_schedule(w, P: int, n_steps: int):
@@ -165,10 +178,10 @@ def retained_schedule(w, P: int, n_steps: int):
     return out
 
 
-def traffic_from_profiles(workload: str):
+def traffic_from_profiles(w):
     """Measured HBM bytes per launch from a committed counter summary, if it was
     taken on the current kernel source (else None)."""
-    path = os.path.join(PROFILES, f"h2o_step_kernel_{workload}_counters.md")
+    path = os.path.join(PROFILES, f"h2o_{step_kernel_name(w)}_{w.name}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -334,10 +347,10 @@ def main():
                 hev.destroy(e0)
                 hev.destroy(e1)
         achieved = float((launch_b[:, None] * np.ones((1, layers))).sum() / dur.sum()) / 1e9
-        traffic = traffic_from_profiles(w.name)
+        traffic = traffic_from_profiles(w)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "h2o step kernel (h2o_step_compact launch)", "timing": events,
+                "kernel": step_kernel_name(w), "timing": events,
                 "mean_launch_us": round(float(dur.mean()) * 1e6, 3),
                 "algorithmic_bytes_per_launch": int(launch_b.mean())}
 
