@@ -180,6 +180,23 @@ def prompt_kv(r: Recipe, layer: int, prompt_lens, n_kv_heads: int):
     return K, V
 
 
+def prompt_queries(r: Recipe, layer: int, prompt_lens, n_q_heads: int) -> np.ndarray:
+    """Packed prompt queries [sum P_b][Hq][D] float32: position p of sequence b has
+    the query a decode step at position p would have (the same stream)."""
+    lens = [int(x) for x in prompt_lens]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    Q = np.empty((int(off[-1]), n_q_heads, r.head_dim), dtype=np.float32)
+    u = unit_vector(r)
+
+    def work(b):
+        for g in range(n_q_heads):
+            Q[off[b]:off[b + 1], g] = queries(r, layer, b, g, 0, lens[b], u=u)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(len(lens))))
+    return Q
+
+
 def step_window(r: Recipe, layer: int, t0, n_steps: int, n_q_heads: int, n_kv_heads: int):
     """Inputs of n_steps decode steps; sequence b's first step appends position t0[b].
 
@@ -243,6 +260,21 @@ def device_prompt_kv(r: Recipe, layer: int, prompt_lens, n_kv_heads: int, device
                                      dtype=torch.float32).to(dt)
         off += P
     return K, V
+
+
+def device_prompt_queries(r: Recipe, layer: int, prompt_lens, n_q_heads: int, device="cuda"):
+    """Packed prompt queries [sum P_b][Hq][D] fp32 as a torch device tensor."""
+    import torch
+    lens = [int(x) for x in prompt_lens]
+    u = torch.from_numpy(unit_vector(r)).to(device)
+    Q = torch.empty((sum(lens), n_q_heads, r.head_dim), dtype=torch.float32, device=device)
+    off = 0
+    for b, P in enumerate(lens):
+        g = torch.Generator(device=device)
+        g.manual_seed(_torch_seed(r.seed, KIND_Q, layer, b, 1 << 19))
+        Q[off:off + P] = torch.randn((P, n_q_heads, r.head_dim), generator=g, device=device) + r.q_boost * u
+        off += P
+    return Q
 
 
 def device_step_window(r: Recipe, layer: int, t0, n_steps: int, n_q_heads: int, n_kv_heads: int,

@@ -28,6 +28,8 @@ def _bind(lib):
     lib.orc_new.restype = C.c_void_p
     lib.orc_new.argtypes = [C.POINTER(OrcCfg), C.c_int, C.c_int, C.c_int, C.c_int, _dp, _dp, _dp]
     lib.orc_free.argtypes = [C.c_void_p]
+    lib.orc_colsum.restype = C.c_int
+    lib.orc_colsum.argtypes = [C.POINTER(OrcCfg), C.c_int, C.c_int, _dp, _dp, C.c_int, _dp]
     lib.orc_schedule.argtypes = [C.POINTER(OrcCfg), C.c_int, _ip, _ip, _ip]
     lib.orc_attend.restype = C.c_int
     lib.orc_attend.argtypes = [C.c_void_p, _dp, _dp, _dp, _dp, _dp]
@@ -95,6 +97,21 @@ def schedule(cfg: OrcCfg, length: int, lib=None):
     K, HH, W = C.c_int32(), C.c_int32(), C.c_int32()
     lib.orc_schedule(C.byref(cfg), length, C.byref(K), C.byref(HH), C.byref(W))
     return K.value, HH.value, W.value
+
+
+def colsum(cfg: OrcCfg, q, k, row_lo: int = 0, per_head: bool = False, lib=None) -> np.ndarray:
+    """Causal-attention column sums of one unit's prompt (orc_colsum): q [P][G][D],
+    k [P][D] -> [P] (summed over the group) or [G][P] (per_head)."""
+    lib = lib or load()
+    G, D = cfg.group, cfg.head_dim
+    q = _f64(q).reshape(-1, G, D)
+    P = q.shape[0]
+    k = _f64(k).reshape(P, D)
+    out = np.empty((G, P) if per_head else (P,), dtype=np.float64)
+    rc = lib.orc_colsum(C.byref(cfg), P, int(row_lo), _p(q), _p(k), 1 if per_head else 0, _p(out))
+    if rc != 0:
+        raise OracleError(f"orc_colsum failed ({rc})")
+    return out
 
 
 def philox4x64_10(ctr, key, lib=None):

@@ -420,3 +420,52 @@ int orc_step_many(orc_unit **u, int n, const double *const *q, const double *con
     free(th);
     return rc;
 }
+
+/* ---- prompt column sums -------------------------------------------------- */
+/* Plain definition, one query row at a time: the row's logits over the keys
+ * it may see (j <= i), the softmax of that row, then each weight added to its
+ * key's column. */
+int orc_colsum(const orc_cfg *c, int P, int row_lo, const double *q, const double *k,
+               int per_head, double *out)
+{
+    if (!c || P < 0 || row_lo < 0 || row_lo > P || !q || !k || !out) return ORC_EARG;
+    const int D = c->head_dim, G = c->group;
+    if (D <= 0 || G <= 0) return ORC_EARG;
+    const double scale = c->scale == 0.0 ? 1.0 / sqrt((double)D) : c->scale;
+    const size_t n_out = per_head ? (size_t)G * P : (size_t)P;
+    for (size_t x = 0; x < n_out; ++x) out[x] = 0.0;
+    double *w = (double *)malloc(sizeof(double) * (P > 0 ? (size_t)P : 1));
+    if (!w) return ORC_ENOMEM;
+    int rc = ORC_OK;
+    for (int i = row_lo; i < P && rc == ORC_OK; ++i) {
+        for (int g = 0; g < G; ++g) {
+            const double *qi = q + ((size_t)i * G + g) * D;
+            double m = -INFINITY;
+            for (int j = 0; j <= i; ++j) {
+                const double *kj = k + (size_t)j * D;
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) s += qi[d] * kj[d];
+                w[j] = scale * s;
+                if (w[j] > m) m = w[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j <= i; ++j) {
+                w[j] = exp(w[j] - m);
+                z += w[j];
+            }
+            double total = 0.0;
+            double *o = per_head ? out + (size_t)g * P : out;
+            for (int j = 0; j <= i; ++j) {
+                const double p = w[j] / z;
+                total += p;
+                o[j] += p;
+            }
+            if (fabs(total - 1.0) > 1e-12) {
+                rc = ORC_ECHECK;
+                break;
+            }
+        }
+    }
+    free(w);
+    return rc;
+}

@@ -91,6 +91,21 @@ int orc_length(const orc_unit *u);
 int orc_step_many(orc_unit **u, int n, const double *const *q, const double *const *k,
                   const double *const *v, double *const *out, int nthreads);
 
+/* Causal-attention column sums of one unit's prompt (P positions):
+ * for every query row i in [row_lo, P), every query head g of the group and
+ * every key j <= i, the weight softmax_{j' <= i}(scale * q[i][g] . k[j'])[j]
+ * is added to out[j] (per_head = 0, summed over the group: out is [P]) or to
+ * out[g * P + j] (per_head = 1: out is [G][P]).  out is overwritten.
+ *   row_lo = 0, summed: the cumulative attention score each prompt token would
+ *     hold had the prompt been scored like decode steps ("Attention Sinks and
+ *     KV cache eviction", sec. 4.2 cumulative score, and sec. 4.3 on scores
+ *     gathered only during decode);
+ *   row_lo = P - w, per head: SnapKV's observation-window vote (sec. 4.3).
+ * q: [P][G][D]; k: [P][D].  Returns ORC_OK, or ORC_EARG / ORC_ECHECK (a row's
+ * weights not summing to one within 1e-12). */
+int orc_colsum(const orc_cfg *c, int P, int row_lo, const double *q, const double *k,
+               int per_head, double *out);
+
 /* Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11). */
 void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
 

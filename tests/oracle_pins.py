@@ -355,6 +355,50 @@ def pin_golden_cache_manager_sizes(lib):
         assert (len(sinks), len(heavy), len(recent)) == tuple(g["layout_sizes"])
 
 
+def pin_colsum_identical_keys(lib):
+    """Identical keys make every causal row uniform: row i gives 1/(i+1) to each
+    j <= i, so column j collects H(P) - H(max(j, row_lo)) per query head (H the
+    harmonic numbers); the total is G * (P - row_lo) (each row sums to one)."""
+    D, G, P = 16, 3, 23
+    cfg = O.make_cfg(head_dim=D, group=G)
+    rng = np.random.default_rng(11)
+    k = np.tile(rng.standard_normal(D), (P, 1))
+    q = rng.standard_normal((P, G, D)) * 3.0
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, P + 1))])
+    for row_lo in (0, 7):
+        out = O.colsum(cfg, q, k, row_lo=row_lo, lib=lib)
+        per = O.colsum(cfg, q, k, row_lo=row_lo, per_head=True, lib=lib)
+        want = np.array([H[P] - H[max(j, row_lo)] for j in range(P)])
+        assert np.allclose(out, G * want, rtol=0, atol=1e-12)
+        assert np.allclose(per, np.tile(want, (G, 1)), rtol=0, atol=1e-12)
+        assert abs(out.sum() - G * (P - row_lo)) < 1e-9
+
+
+def pin_colsum_equals_decode_accumulation(lib):
+    """Scoring the prompt's causal rows is the decode accumulation run over the
+    prompt: a unit started from the first token and stepped over positions
+    1..P-1 with a budget it never reaches holds, for every position j, the sum
+    over rows i >= max(j, 1) of row i's weight on j -- column sums from row 1."""
+    D, G, P = 32, 2, 40
+    rng = np.random.default_rng(12)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    k = rng.standard_normal((P, D))
+    k[[0, 5, 17, 30]] += 2.5 * u
+    v = rng.standard_normal((P, D))
+    q = rng.standard_normal((P, G, D)) + 1.5 * u
+    dec = O.make_cfg(head_dim=D, group=G, budget_fixed=P + 8, hh_fixed=2)
+    unit = _unit(lib, dec, k[:1], v[:1], P + 1)
+    for t in range(1, P):
+        unit.step(q[t], k[t], v[t])
+    pos, sc, em = unit.state()
+    assert list(pos) == list(range(P)) and em == 0.0
+    want = O.colsum(O.make_cfg(head_dim=D, group=G), q, k, row_lo=1, lib=lib)
+    assert np.allclose(sc, want, rtol=1e-12, atol=1e-14)
+    per = O.colsum(O.make_cfg(head_dim=D, group=G), q, k, row_lo=1, per_head=True, lib=lib)
+    assert np.allclose(per.sum(axis=0), want, rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [
     pin_attention_full_cache,
     pin_scores_and_selection_recomputed,
@@ -367,4 +411,6 @@ ALL_PINS = [
     pin_random_uniform_and_independent,
     pin_golden_streaming_layout,
     pin_golden_cache_manager_sizes,
+    pin_colsum_identical_keys,
+    pin_colsum_equals_decode_accumulation,
 ]

@@ -40,6 +40,14 @@ MUTANTS = {
     "philox_weyl_before_first_round": ("        if (r > 0) {\n            k0 += W0;", "        if (r >= 0) {\n            k0 += W0;"),
     "random_evicts_prompt": ("if (u->R[i] >= u->prompt_len) {", "if (u->R[i] >= 0) {"),
     "random_counter_step_word": ("(uint64_t)u->h, (uint64_t)t,", "(uint64_t)u->h, (uint64_t)(t + 1),"),
+    "colsum_rows_from_zero": ("for (int i = row_lo; i < P && rc == ORC_OK; ++i)",
+                              "for (int i = 0; i < P && rc == ORC_OK; ++i)"),
+    "colsum_no_scale": ("w[j] = scale * s;", "w[j] = s;"),
+    "colsum_first_head_only": ("for (int g = 0; g < G; ++g) {\n            const double *qi",
+                               "for (int g = 0; g < 1; ++g) {\n            const double *qi"),
+    "colsum_key_is_query_row": ("const double *kj = k + (size_t)j * D;", "const double *kj = k + (size_t)i * D;"),
+    "colsum_head_major_query": ("const double *qi = q + ((size_t)i * G + g) * D;",
+                                "const double *qi = q + ((size_t)g * P + i) * D;"),
     "random_largest_words": ("    if (x->key < y->key) return -1;\n    if (x->key > y->key) return 1;",
                              "    if (x->key > y->key) return -1;\n    if (x->key < y->key) return 1;"),
 }
