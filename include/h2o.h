@@ -148,7 +148,30 @@ int h2o_info(const h2o_ctx *ctx, int32_t *slot_capacity, int32_t *steps_done,
 /* Free the context and its device memory (waits for the device). NULL is a no-op. */
 void h2o_destroy(h2o_ctx *ctx);
 
-/* Message of the last error on ctx, or of the last failed h2o_init when ctx is NULL. */
+/* Prefill-scored initial scores: the cumulative attention score each prompt
+ * token would hold had every prompt position's query been scored like a decode
+ * step ("Attention Sinks and KV cache eviction", sec. 4.2: the score sums a
+ * token's attention weights over the queries that saw it; sec. 4.3: scores
+ * gathered only during decode start from nothing).  For sequence b, KV head h
+ * and prompt position j, with off_b = P_0 + ... + P_{b-1}:
+ *   out[(off_b + j) * Hkv + h] = sum over positions i in [j, P_b) and the G
+ *       query heads g of h of the causal softmax weight of key j in row i,
+ *       softmax over j' <= i of scale * q[off_b + i][h G + g] . k[off_b + j'][h].
+ * The result is h2o_init's init_scores.
+ *   cfg         batch, n_q_heads, n_kv_heads, head_dim, kv_dtype and scale are used.
+ *   prompt_len  host [B]: P_b >= 1; 1 <= batch <= 128.
+ *   prompt_q    device [sum P_b][Hq][D] fp32.
+ *   prompt_k    device [sum P_b][Hkv][D] kv_dtype: the packed prompt h2o_init takes.
+ *   out         device [sum P_b][Hkv] fp64; every element is written.
+ * Supported: kv_dtype H2O_BF16 with head_dim 128, G in {1, 2, 4, 8}.
+ * Scratch of about the size of prompt_q is taken with hipMallocAsync on
+ * `stream` and returned on it.  Errors: H2O_EINVAL, H2O_ENOMEM, H2O_EDEVICE;
+ * the message is h2o_last_error(NULL). */
+int h2o_prefill_scores(const h2o_config *cfg, const int32_t *prompt_len, const float *prompt_q,
+                       const void *prompt_k, double *out, void *stream);
+
+/* Message of the last error on ctx, or, when ctx is NULL, of the last failed call
+ * made without a context (h2o_init, h2o_prefill_scores). */
 const char *h2o_last_error(const h2o_ctx *ctx);
 
 #ifdef __cplusplus

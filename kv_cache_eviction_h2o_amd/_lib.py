@@ -23,7 +23,7 @@ PAGE_SIZE = 16
 
 # Every symbol include/h2o.h declares.
 SYMBOLS = ("h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
-           "h2o_info", "h2o_destroy", "h2o_last_error")
+           "h2o_info", "h2o_destroy", "h2o_prefill_scores", "h2o_last_error")
 
 
 class H2OConfig(C.Structure):
@@ -73,6 +73,8 @@ def load_library(path: str = LIB):
     lib.h2o_info.argtypes = [vp, i32p, i32p, i32p]
     lib.h2o_destroy.restype = None
     lib.h2o_destroy.argtypes = [vp]
+    lib.h2o_prefill_scores.restype = C.c_int
+    lib.h2o_prefill_scores.argtypes = [C.POINTER(H2OConfig), i32p, vp, vp, vp, vp]
     lib.h2o_last_error.restype = C.c_char_p
     lib.h2o_last_error.argtypes = [vp]
     _lib = lib
@@ -115,6 +117,28 @@ def pages_needed(prompt_lens, steps: int, cfg: H2OConfig) -> int:
         else:
             grow += (min(end, p + cfg.rand_k + cfg.rand_r) + ps - 1) // ps + 1
     return max(first, grow) + len(prompt_lens)
+
+
+def prefill_scores(cfg: H2OConfig, prompt_lens, prompt_q, prompt_k, out=None, stream=None):
+    """Prefill-scored initial scores (h2o_prefill_scores): returns out, a cuda float64
+    tensor [sum P_b][Hkv] usable as H2OCache's init_scores."""
+    import torch
+    lib = load_library()
+    lens = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    if lens.shape != (cfg.batch,):
+        raise ValueError("prompt_lens must have one entry per sequence")
+    total = int(lens.sum())
+    kv = torch.bfloat16 if cfg.kv_dtype == BF16 else torch.float32
+    H2OCache._check_tensor("prompt_q", prompt_q, (total, cfg.n_q_heads, cfg.head_dim), torch.float32)
+    H2OCache._check_tensor("prompt_k", prompt_k, (total, cfg.n_kv_heads, cfg.head_dim), kv)
+    if out is None:
+        out = torch.empty((total, cfg.n_kv_heads), dtype=torch.float64, device=prompt_q.device)
+    H2OCache._check_tensor("out", out, (total, cfg.n_kv_heads), torch.float64)
+    rc = lib.h2o_prefill_scores(C.byref(cfg), lens.ctypes.data_as(C.POINTER(C.c_int32)), _ptr(prompt_q),
+                                _ptr(prompt_k), _ptr(out), _stream_handle(stream))
+    if rc != H2O_OK:
+        raise H2OError(rc, lib.h2o_last_error(None).decode(errors="replace"))
+    return out
 
 
 def _stream_handle(stream):

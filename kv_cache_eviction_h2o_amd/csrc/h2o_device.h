@@ -417,6 +417,30 @@ struct SlotMap {
     }
 };
 
+// ------------------------------------------- bf16 matrix-instruction tiles
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ inline bf16x8 as_bf16x8(const uint4& v)
+{
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ inline f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The bf16 part of x that a B column holds: x rounded to bf16 (hi column) or
+// the rounding residual rounded to bf16 (lo column).
+__device__ inline __bf16 split_part(float x, bool lo)
+{
+    const __bf16 hi = (__bf16)x;
+    return lo ? (__bf16)(x - (float)hi) : hi;
+}
+
 // ------------------------------------------------------- K/V slot layouts
 // A slot index si (the unit's first slot + slot, or the page-derived index)
 // names one token's K row and V row.  Rows move as 16 chunks of 16 bytes;

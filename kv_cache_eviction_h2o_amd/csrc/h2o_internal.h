@@ -119,9 +119,26 @@ struct GatherArgs {
     double* osc;      // [B*Hkv][capo]
 };
 
+// Causal-attention column sums of packed prompts (h2o_prefill.hip): rows
+// [seq_lo[b], seq_p[b]) of every unit, bf16 K rows of 128, fp32 q.
+struct ColsumArgs {
+    int B, Hq, Hkv, G;
+    int nt8;          // 8-position tiles per unit in the scratch (ceil(max P / 8))
+    float qscale;     // logit scale * log2(e)
+    int per_head;     // 1: out[(off_b + j) * Hq + h * G + g]; 0: out[(off_b + j) * Hkv + h]
+    const float* q;   // [sum P][Hq][128]
+    const void* k;    // [sum P][Hkv][128] bf16
+    uint4* qs;        // scratch [unit][nt8][G][4][64] 16-byte A-operand pieces of q (hi/lo)
+    float2* st;       // scratch [unit][nt8][G][8] (row max, 1 / row sum), log2 domain
+    double* out;
+    int32_t seq_p[kMaxArgBatch], seq_lo[kMaxArgBatch];
+    int64_t seq_off[kMaxArgBatch];
+};
+
 // Launchers (h2o_kernels.hip unless noted).  Each returns the launch's hipError_t.
 hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st);
 hipError_t launch_step_mfma(const StepArgs& a, int max_n_att, hipStream_t st);  // h2o_mfma.hip
+hipError_t launch_colsum(const ColsumArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
 hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);

@@ -37,33 +37,10 @@
 namespace h2o {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-
 constexpr int kMNT = 512;  // threads per unit (8 waves, 2 per SIMD)
 constexpr int kMNW = kMNT / 64;
 constexpr int kMPF = 3;    // slots per thread whose score and position are fetched up front
 constexpr int kTile = 32;  // slots per tile
-
-__device__ inline bf16x8 as_bf16x8(const uint4& v)
-{
-    bf16x8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
-
-__device__ inline f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// The bf16 part of x that a B column holds: x rounded to bf16 (hi column) or
-// the rounding residual rounded to bf16 (lo column).
-__device__ inline __bf16 split_part(float x, bool lo)
-{
-    const __bf16 hi = (__bf16)x;
-    return lo ? (__bf16)(x - (float)hi) : hi;
-}
 
 __device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }

@@ -263,6 +263,70 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     return H2O_OK;
 }
 
+
+// Causal-attention column sums of packed prompts (h2o_prefill_scores): validate,
+// take stream-ordered scratch, launch the two passes, return the scratch.
+int colsum_run(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo, const float* q,
+               const void* k, int per_head, double* out, void* stream)
+{
+    if (!cfg || !plen) return fail(nullptr, H2O_EINVAL, "null config or prompt lengths");
+    const int B = cfg->batch, Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    if (B < 1 || B > kMaxArgBatch)
+        return fail(nullptr, H2O_EINVAL, "prompt column sums take 1 to 128 sequences");
+    if (Hkv < 1 || Hq < Hkv || Hq % Hkv != 0)
+        return fail(nullptr, H2O_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+    const int G = Hq / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(nullptr, H2O_EINVAL, "group size must be 1, 2, 4 or 8");
+    if (cfg->head_dim != 128 || cfg->kv_dtype != H2O_BF16)
+        return fail(nullptr, H2O_EINVAL, "prompt column sums need bf16 K rows of head_dim 128");
+    if (!(cfg->scale >= 0.f)) return fail(nullptr, H2O_EINVAL, "scale must be >= 0");
+    ColsumArgs a{};
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.per_head = per_head ? 1 : 0;
+    int maxP = 0;
+    long long off = 0;
+    for (int b = 0; b < B; ++b) {
+        const int P = plen[b];
+        const int lo = row_lo ? row_lo[b] : 0;
+        if (P < 1) return fail(nullptr, H2O_EINVAL, "prompt lengths must be >= 1");
+        if (lo < 0 || lo >= P) return fail(nullptr, H2O_EINVAL, "first row must lie in [0, P_b)");
+        a.seq_p[b] = P;
+        a.seq_lo[b] = lo;
+        a.seq_off[b] = off;
+        off += P;
+        maxP = std::max(maxP, P);
+    }
+    if (off > (1LL << 31)) return fail(nullptr, H2O_EINVAL, "too many prompt positions");
+    if (!q || !k || !out) return fail(nullptr, H2O_EINVAL, "null prompt_q, prompt_k or out");
+    const double scale = cfg->scale > 0.f ? (double)cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
+    a.qscale = (float)(scale * 1.4426950408889634);
+    a.q = q;
+    a.k = k;
+    a.out = out;
+    a.nt8 = (maxP + 7) / 8;
+    const size_t units = (size_t)B * Hkv;
+    const size_t qs_bytes = units * a.nt8 * G * 256 * sizeof(uint4);
+    const size_t st_bytes = units * a.nt8 * G * 8 * sizeof(float2);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = hipMallocAsync((void**)&a.qs, qs_bytes, st)) != hipSuccess)
+        return hip_fail(nullptr, e, "prompt column sums: scratch for q");
+    if ((e = hipMallocAsync((void**)&a.st, st_bytes, st)) != hipSuccess) {
+        (void)hipFreeAsync(a.qs, st);
+        return hip_fail(nullptr, e, "prompt column sums: scratch for row statistics");
+    }
+    e = launch_colsum(a, maxP, st);
+    const hipError_t e1 = hipFreeAsync(a.qs, st), e2 = hipFreeAsync(a.st, st);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "prompt column sums: launch");
+    if (e1 != hipSuccess || e2 != hipSuccess)
+        return hip_fail(nullptr, e1 != hipSuccess ? e1 : e2, "prompt column sums: scratch release");
+    return H2O_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -525,6 +589,12 @@ void h2o_destroy(h2o_ctx* c)
         free_all(c);
     }
     delete c;
+}
+
+int h2o_prefill_scores(const h2o_config* cfg, const int32_t* prompt_len, const float* prompt_q,
+                       const void* prompt_k, double* out, void* stream)
+{
+    return colsum_run(cfg, prompt_len, nullptr, prompt_q, prompt_k, 0, out, stream);
 }
 
 const char* h2o_last_error(const h2o_ctx* c)

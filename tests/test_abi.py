@@ -127,3 +127,31 @@ def test_page_pool_sizing_host_logic():
     lens = [4096, 65536]
     need = L.pages_needed(lens, 65, cfg)
     assert need >= sum((p + 15) // 16 for p in lens)
+
+
+def _prefill(lib, cfg, lens, ptr=16):
+    arr = (C.c_int32 * len(lens))(*lens)
+    p = C.c_void_p(ptr) if ptr else None
+    return lib.h2o_prefill_scores(C.byref(cfg), arr, p, p, p, None)
+
+
+@pytest.mark.parametrize("bad,lens,msg", [
+    (dict(), [0, 10], ">= 1"),
+    (dict(n_q_heads=7), [10, 10], "multiple"),
+    (dict(n_q_heads=32, n_kv_heads=2), [10, 10], "group size"),
+    (dict(head_dim=64), [10, 10], "head_dim 128"),
+    (dict(kv_dtype="f32"), [10, 10], "bf16"),
+    (dict(scale=-1.0), [10, 10], "scale"),
+    (dict(batch=129), [10] * 129, "128 sequences"),
+])
+def test_prefill_scores_rejects_before_device(lib, bad, lens, msg):
+    cfg = L.make_config(**{**GOOD, **bad})
+    assert _prefill(lib, cfg, lens) == L.H2O_EINVAL
+    assert msg in lib.h2o_last_error(None).decode()
+
+
+def test_prefill_scores_null_arguments(lib):
+    cfg = L.make_config(**GOOD)
+    assert lib.h2o_prefill_scores(None, None, None, None, None, None) == L.H2O_EINVAL
+    assert _prefill(lib, cfg, [10, 10], ptr=0) == L.H2O_EINVAL
+    assert "null" in lib.h2o_last_error(None).decode()
