@@ -44,7 +44,7 @@ from kv_cache_eviction_h2o_amd import workloads as WL  # noqa: E402
 METRIC = "retained KV tokens processed/sec per decode step (attn+evict+compact); % HBM peak"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc")
-KERNEL_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip")
+KERNEL_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip", "h2o_prefill.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -105,6 +105,9 @@ def parse():
                          "back to back, so the per-launch time is the step time over the layers, "
                          "dispatch gaps included), around every launch (markers between kernels "
                          "slow the step), or none")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time h2o_prefill_scores (prefill-scored initial scores) over the "
+                         "workload's prompts instead of the decode step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -231,6 +234,93 @@ def cpu_baseline(w, n_att: int, seconds: float):
                        f"threads; {t_used:.1f} s of CPU step time (input conversion excluded)")}
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def colsum_cpu_baseline(w, lens, seconds: float):
+    """The oracle's column sums (orc_colsum, as it stands) on whole units of the
+    workload's first sequence, all host cores, until about `seconds` have passed."""
+    import oracle as O
+    from concurrent.futures import ThreadPoolExecutor
+    G, Hkv, P = w.group, w.n_kv_heads, lens[0]
+    K, _ = S.prompt_kv(w.recipe, 0, [P], Hkv)
+    Q = S.prompt_queries(w.recipe, 0, [P], w.n_q_heads)
+    cfg = O.make_cfg(head_dim=w.head_dim, group=G)
+    qs = [Q[:, h * G:(h + 1) * G].astype(np.float64) for h in range(Hkv)]
+    ks = [S.cache_to_f64(w.recipe, K[:, h]) for h in range(Hkv)]
+    threads = min(os.cpu_count() or 1, Hkv)
+    done, t_used = 0, 0.0
+    with ThreadPoolExecutor(threads) as ex:
+        while t_used < seconds:
+            t0 = time.perf_counter()
+            list(ex.map(lambda h: O.colsum(cfg, qs[h], ks[h]), range(Hkv)))
+            t_used += time.perf_counter() - t0
+            done += 1
+    return {"value": done * P / t_used, "unit": "prompt tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"sequence 0 ({P} prompt positions) x {Hkv} KV heads x {G} query heads, "
+                       f"{done} repetitions, fp64 oracle column sums on {threads} threads; "
+                       f"{t_used:.1f} s of CPU time")}
+
+
+def prefill_main(args, w):
+    """--prefill: h2o_prefill_scores over the workload's prompts (one layer)."""
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+    lens = WL.prompt_lengths(w)
+    B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    dev = torch.device("cuda")
+    L.load_library()
+    pk, _ = S.device_prompt_kv(w.recipe, 0, lens, Hkv, dev)
+    pq = S.device_prompt_queries(w.recipe, 0, lens, Hq, dev)
+    cfg = L.config_from_workload(w, max_len=max(lens) + 1)
+    out = torch.empty((sum(lens), Hkv), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        L.prefill_scores(cfg, lens, pq, pk, out)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    sh = C.c_void_p(stream.cuda_stream)
+    e0, e1 = hev.create(), hev.create()
+    t0 = time.perf_counter()
+    hev.record(e0, sh)
+    for _ in range(args.steps):
+        L.prefill_scores(cfg, lens, pq, pk, out)
+    hev.record(e1, sh)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_call = hev.elapsed_s(e0, e1) / args.steps
+    hev.destroy(e0)
+    hev.destroy(e1)
+    total = float(out.sum().item())
+    expect = float(sum(lens)) * Hq  # every row's weights sum to one
+    if abs(total - expect) > 1e-4 * expect:
+        raise SystemExit(f"column sums add up to {total}, expected {expect}")
+    pairs = sum(P * (P + 1) // 2 for P in lens)
+    flops = 2.0 * D * Hq * pairs  # the causal logits, once
+    tokens = float(sum(lens))
+    cpu = None if args.no_cpu_baseline else colsum_cpu_baseline(w, lens, args.cpu_seconds)
+    line = {
+        "metric": "prompt tokens scored/sec (prefill-scored initial scores, h2o_prefill_scores)",
+        "value": round(tokens / per_call, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (q as hi+lo)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+                   "prompt_lens": lens if len(set(lens)) > 1 else lens[0],
+                   "entry_point": "h2o_prefill_scores", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / per_call / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / per_call / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "mean_call_us": round(per_call * 1e6, 2), "algorithmic_flops": flops,
+                     "executed_over_algorithmic": 4,
+                     "note": "algorithmic = the causal logits q.k once; the kernels compute them in "
+                             "two passes, each on the bf16 hi and lo parts of q"},
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace or args.summarize_counters:
@@ -246,6 +336,9 @@ def main():
     from kv_cache_eviction_h2o_amd import _lib as L
 
     w = next(x for x in WL.ALL if x.name == args.workload)
+    if args.prefill:
+        prefill_main(args, w)
+        return
     layers = args.layers or w.layers
     K_steps, W_steps = args.steps, args.warmup
     s0 = min(args.window_start, w.decode_steps - K_steps)

@@ -9,15 +9,16 @@
 //
 // A row's weights need its softmax maximum and sum over all of its keys
 // before any column can take them, so there are two passes:
-//   rows   one workgroup per (unit, 32 query positions), one wave per 8:
+//   rows   one workgroup per (unit, 4 waves x 8 PT query positions; PT = 4 / G
+//          for small groups, else 1):
 //          S = Q_tile (8 positions x hi/lo = 16 rows) . K_tile^T (16 keys)
 //          with v_mfma_f32_16x16x32_bf16 over 4 k-steps, hi + lo added in the
 //          lane (rows 2p and 2p+1 of the C layout); online max / sum per lane
 //          over the causal key tiles, then combined over the 16 key lanes by
 //          DPP.  Writes the row statistics and the split q tiles (the A
 //          operand, so the second pass reads it without converting again).
-//   cols   one workgroup per (unit, 64 keys), one wave per 16 keys held as the
-//          B operand: every query tile from the keys onwards gives
+//   cols   one workgroup per (unit, 256 keys), one wave per 64 keys held as
+//          four B operands: every query tile from the keys onwards gives
 //          p = 2^(s - M_i) / L_i, summed per key lane (fp32 per tile, fp64
 //          across tiles), then over the lane groups.  Each output element has
 //          one writer; nothing needs clearing first.
@@ -48,83 +49,121 @@ __device__ inline void ms_stage(float& m, float& l)
     m = M;
 }
 
+// query tiles of 8 positions per wave: more for small groups so a K tile load
+// feeds more products (qop holds PT * G * 16 registers)
+template <int G>
+struct RowsTune {
+    static constexpr int PT = G >= 4 ? 1 : 4 / G;
+};
+
 template <int G>
 __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
 {
+    constexpr int PT = RowsTune<G>::PT;
     const int unit = blockIdx.y, b = unit / a.Hkv, h = unit - b * a.Hkv;
     const int P = a.seq_p[b], lo = a.seq_lo[b];
     const int64_t off = a.seq_off[b];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lc = lane & 15, lg = lane >> 4;
-    const int base8 = blockIdx.x * 32 + 8 * w;  // this wave's first position
-    if (base8 >= P || base8 + 8 <= lo) return;  // no row of this wave counts
-    const int t8 = base8 / 8;
+    const int base = (blockIdx.x * 4 + w) * 8 * PT;  // this wave's first position
+    if (base >= P || base + 8 * PT <= lo) return;   // no row of this wave counts
 
-    // A operand: lane (lg, lc) holds d = 32 kb + 8 lg .. +8 of row lc, i.e. of
-    // position base8 + lc / 2, part lc & 1 (hi / lo)
-    const int prow = min(base8 + (lc >> 1), P - 1);
+    // A operands: tile pt, lane (lg, lc) holds d = 32 kb + 8 lg .. +8 of row lc,
+    // i.e. of position base + 8 pt + lc / 2, part lc & 1 (hi / lo)
     const bool lo_part = (lc & 1) != 0;
-    bf16x8 qop[G][4];
+    bf16x8 qop[PT][G][4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float* qr = a.q + ((size_t)(off + prow) * a.Hq + (size_t)h * G + g) * 128;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const float4 x0 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg);
-            const float4 x1 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg + 4);
-            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qop[g][kb][i] = split_part(x[i] * a.qscale, lo_part);
-            a.qs[(((size_t)unit * a.nt8 + t8) * G + g) * 256 + kb * 64 + lane] = as_u4(qop[g][kb]);
-        }
-    }
-
-    // online row statistics over the causal key tiles; lane lc sees key 16 kt + lc
-    const int last = min(base8 + 7, P - 1);
-    const int nkt = last / 16 + 1;
-    const int pos0 = base8 + 2 * lg, pos1 = pos0 + 1;  // this lane's rows (C rows 4 lg .. +3)
-    const uint4* kp = reinterpret_cast<const uint4*>(a.k);
-    float m[G][2], l[G][2];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g][0] = m[g][1] = kFloor;
-        l[g][0] = l[g][1] = 0.f;
-    }
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int key = 16 * kt + lc;
-        const int kr = min(key, P - 1);
-        uint4 kt4[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kt4[kb] = kp[((size_t)(off + kr) * a.Hkv + h) * kRowVecs + 4 * kb + lg];
+    for (int pt = 0; pt < PT; ++pt) {
+        const int t8 = base / 8 + pt;
+        const int prow = min(base + 8 * pt + (lc >> 1), P - 1);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            const float* qr = a.q + ((size_t)(off + prow) * a.Hq + (size_t)h * G + g) * 128;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) c = mma(qop[g][kb], as_bf16x8(kt4[kb]), c);
-            const float s[2] = {key <= pos0 ? c[0] + c[1] : -INFINITY, key <= pos1 ? c[2] + c[3] : -INFINITY};
+            for (int kb = 0; kb < 4; ++kb) {
+                const float4 x0 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg);
+                const float4 x1 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg + 4);
+                const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const float M = fmaxf(m[g][r], s[r]);
-                l[g][r] = l[g][r] * fast_exp2(m[g][r] - M) + fast_exp2(s[r] - M);
-                m[g][r] = M;
+                for (int i = 0; i < 8; ++i) qop[pt][g][kb][i] = split_part(x[i] * a.qscale, lo_part);
+                if (t8 < a.nt8)
+                    a.qs[(((size_t)unit * a.nt8 + t8) * G + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
             }
         }
     }
+
+    // online row statistics over the causal key tiles; lane lc sees key 16 kt + lc;
+    // the next tile's K is requested before this one is used
+    const int last = min(base + 8 * PT - 1, P - 1);
+    const int nkt = last / 16 + 1;
+    const uint4* kp = reinterpret_cast<const uint4*>(a.k);
+    float m[PT][G][2], l[PT][G][2];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            ms_stage<0xB1>(m[g][r], l[g][r]);
-            ms_stage<0x4E>(m[g][r], l[g][r]);
-            ms_stage<0x141>(m[g][r], l[g][r]);
-            ms_stage<0x140>(m[g][r], l[g][r]);
-        }
-    if (lc == 0) {
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float4* sp = reinterpret_cast<float4*>(a.st + (((size_t)unit * a.nt8 + t8) * G + g) * 8 + 2 * lg);
-            *sp = make_float4(m[g][0], 1.0f / l[g][0], m[g][1], 1.0f / l[g][1]);
+            m[pt][g][0] = m[pt][g][1] = kFloor;
+            l[pt][g][0] = l[pt][g][1] = 0.f;
+        }
+    auto load_k = [&](int kt, uint4 (&t)[4]) {
+        const int kr = min(16 * kt + lc, P - 1);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) t[kb] = kp[((size_t)(off + kr) * a.Hkv + h) * kRowVecs + 4 * kb + lg];
+    };
+    auto rows = [&](int kt, const uint4 (&t)[4]) {
+        const int key = 16 * kt + lc;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int pos0 = base + 8 * pt + 2 * lg, pos1 = pos0 + 1;  // C rows 4 lg .. +3
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) c = mma(qop[pt][g][kb], as_bf16x8(t[kb]), c);
+                const float s[2] = {key <= pos0 ? c[0] + c[1] : -INFINITY,
+                                    key <= pos1 ? c[2] + c[3] : -INFINITY};
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const float M = fmaxf(m[pt][g][r], s[r]);
+                    l[pt][g][r] = l[pt][g][r] * fast_exp2(m[pt][g][r] - M) + fast_exp2(s[r] - M);
+                    m[pt][g][r] = M;
+                }
+            }
+        }
+    };
+    uint4 ka[4], kb4[4];
+    load_k(0, ka);
+    int kt = 0;
+    for (; kt + 2 <= nkt; kt += 2) {
+        load_k(kt + 1, kb4);
+        rows(kt, ka);
+        load_k(min(kt + 2, nkt - 1), ka);
+        rows(kt + 1, kb4);
+    }
+    if (kt < nkt) rows(kt, ka);
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                ms_stage<0xB1>(m[pt][g][r], l[pt][g][r]);
+                ms_stage<0x4E>(m[pt][g][r], l[pt][g][r]);
+                ms_stage<0x141>(m[pt][g][r], l[pt][g][r]);
+                ms_stage<0x140>(m[pt][g][r], l[pt][g][r]);
+            }
+    if (lc == 0) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int t8 = base / 8 + pt;
+            if (t8 >= a.nt8) continue;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float4* sp =
+                    reinterpret_cast<float4*>(a.st + (((size_t)unit * a.nt8 + t8) * G + g) * 8 + 2 * lg);
+                *sp = make_float4(m[pt][g][0], 1.0f / l[pt][g][0], m[pt][g][1], 1.0f / l[pt][g][1]);
+            }
         }
     }
 }
@@ -139,6 +178,8 @@ __device__ inline double xrow_add(double v, bool x32)
     return a + c;
 }
 
+constexpr int kKT = 4;  // 16-key B tiles per wave (64 keys)
+
 template <int G, bool PH>
 __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
 {
@@ -149,26 +190,31 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lc = lane & 15, lg = lane >> 4;
-    const int k0 = blockIdx.x * 64 + 16 * w;  // this wave's first key
+    const int k0 = (blockIdx.x * 4 + w) * 16 * kKT;  // this wave's first key
     if (k0 >= P) return;
-    const int key = k0 + lc;
     const uint4* kp = reinterpret_cast<const uint4*>(a.k);
-    const int kr = min(key, P - 1);
-    uint4 kt4[4];
+    uint4 kt4[kKT][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kt4[kb] = kp[((size_t)(off + kr) * a.Hkv + h) * kRowVecs + 4 * kb + lg];
+    for (int x = 0; x < kKT; ++x) {
+        const int kr = min(k0 + 16 * x + lc, P - 1);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) kt4[x][kb] = kp[((size_t)(off + kr) * a.Hkv + h) * kRowVecs + 4 * kb + lg];
+    }
 
-    double acc[NA];
+    double acc[kKT][NA];
 #pragma unroll
-    for (int x = 0; x < NA; ++x) acc[x] = 0.0;
+    for (int x = 0; x < kKT; ++x)
+#pragma unroll
+        for (int y = 0; y < NA; ++y) acc[x][y] = 0.0;
     const int t_first = max(k0, lo) / 8, t_last = (P - 1) / 8;
     for (int t8 = t_first; t8 <= t_last; ++t8) {
         const int pos0 = 8 * t8 + 2 * lg, pos1 = pos0 + 1;
-        const bool v0 = key <= pos0 && pos0 < P && pos0 >= lo;
-        const bool v1 = key <= pos1 && pos1 < P && pos1 >= lo;
-        float tacc[NA];
+        const bool r0 = pos0 < P && pos0 >= lo, r1 = pos1 < P && pos1 >= lo;
+        float tacc[kKT][NA];
 #pragma unroll
-        for (int x = 0; x < NA; ++x) tacc[x] = 0.f;
+        for (int x = 0; x < kKT; ++x)
+#pragma unroll
+            for (int y = 0; y < NA; ++y) tacc[x][y] = 0.f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const uint4* qa = a.qs + (((size_t)unit * a.nt8 + t8) * G + g) * 256 + lane;
@@ -177,28 +223,38 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
             for (int kb = 0; kb < 4; ++kb) q4[kb] = qa[kb * 64];
             const float4 sv =
                 *reinterpret_cast<const float4*>(a.st + (((size_t)unit * a.nt8 + t8) * G + g) * 8 + 2 * lg);
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) c = mma(as_bf16x8(q4[kb]), as_bf16x8(kt4[kb]), c);
-            const float p0 = v0 ? fast_exp2(c[0] + c[1] - sv.x) * sv.y : 0.f;
-            const float p1 = v1 ? fast_exp2(c[2] + c[3] - sv.z) * sv.w : 0.f;
-            tacc[PH ? g : 0] += p0 + p1;
+            for (int x = 0; x < kKT; ++x) {
+                const int key = k0 + 16 * x + lc;
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) c = mma(as_bf16x8(q4[kb]), as_bf16x8(kt4[x][kb]), c);
+                const float p0 = (r0 && key <= pos0) ? fast_exp2(c[0] + c[1] - sv.x) * sv.y : 0.f;
+                const float p1 = (r1 && key <= pos1) ? fast_exp2(c[2] + c[3] - sv.z) * sv.w : 0.f;
+                tacc[x][PH ? g : 0] += p0 + p1;
+            }
         }
 #pragma unroll
-        for (int x = 0; x < NA; ++x) acc[x] += (double)tacc[x];
+        for (int x = 0; x < kKT; ++x)
+#pragma unroll
+            for (int y = 0; y < NA; ++y) acc[x][y] += (double)tacc[x][y];
     }
     // sum over the four lane groups (the rows); every lane then holds its key's total
 #pragma unroll
-    for (int x = 0; x < NA; ++x) {
-        acc[x] = xrow_add(acc[x], false);
-        acc[x] = xrow_add(acc[x], true);
-    }
-    if (lg == 0 && key < P) {
-        if constexpr (PH) {
+    for (int x = 0; x < kKT; ++x) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) a.out[(size_t)(off + key) * a.Hq + (size_t)h * G + g] = acc[g];
-        } else {
-            a.out[(size_t)(off + key) * a.Hkv + h] = acc[0];
+        for (int y = 0; y < NA; ++y) {
+            acc[x][y] = xrow_add(acc[x][y], false);
+            acc[x][y] = xrow_add(acc[x][y], true);
+        }
+        const int key = k0 + 16 * x + lc;
+        if (lg == 0 && key < P) {
+            if constexpr (PH) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) a.out[(size_t)(off + key) * a.Hq + (size_t)h * G + g] = acc[x][g];
+            } else {
+                a.out[(size_t)(off + key) * a.Hkv + h] = acc[x][0];
+            }
         }
     }
 }
@@ -207,13 +263,16 @@ template <int G>
 hipError_t launch_colsum_g(const ColsumArgs& a, int max_p, hipStream_t st)
 {
     const unsigned units = (unsigned)(a.B * a.Hkv);
-    hipLaunchKernelGGL((colsum_rows_kernel<G>), dim3((max_p + 31) / 32, units), dim3(kCNT), 0, st, a);
+    const int rows_per_wg = 4 * 8 * RowsTune<G>::PT, keys_per_wg = 4 * 16 * kKT;
+    hipLaunchKernelGGL((colsum_rows_kernel<G>), dim3((max_p + rows_per_wg - 1) / rows_per_wg, units),
+                       dim3(kCNT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const dim3 gc((max_p + keys_per_wg - 1) / keys_per_wg, units);
     if (a.per_head)
-        hipLaunchKernelGGL((colsum_cols_kernel<G, true>), dim3((max_p + 63) / 64, units), dim3(kCNT), 0, st, a);
+        hipLaunchKernelGGL((colsum_cols_kernel<G, true>), gc, dim3(kCNT), 0, st, a);
     else
-        hipLaunchKernelGGL((colsum_cols_kernel<G, false>), dim3((max_p + 63) / 64, units), dim3(kCNT), 0, st, a);
+        hipLaunchKernelGGL((colsum_cols_kernel<G, false>), gc, dim3(kCNT), 0, st, a);
     return hipGetLastError();
 }
 
