@@ -29,6 +29,10 @@ def _bind(lib):
     lib.orc_new.argtypes = [C.POINTER(OrcCfg), C.c_int, C.c_int, C.c_int, C.c_int, _dp, _dp, _dp]
     lib.orc_free.argtypes = [C.c_void_p]
     lib.orc_colsum.restype = C.c_int
+    lib.orc_snapkv_select.restype = C.c_int
+    lib.orc_snapkv_select.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _dp, _ip]
+    lib.orc_snapkv.restype = C.c_int
+    lib.orc_snapkv.argtypes = [C.POINTER(OrcCfg), C.c_int, C.c_int, C.c_int, C.c_int, _dp, _dp, _dp, _ip]
     lib.orc_colsum.argtypes = [C.POINTER(OrcCfg), C.c_int, C.c_int, _dp, _dp, C.c_int, _dp]
     lib.orc_schedule.argtypes = [C.POINTER(OrcCfg), C.c_int, _ip, _ip, _ip]
     lib.orc_attend.restype = C.c_int
@@ -112,6 +116,34 @@ def colsum(cfg: OrcCfg, q, k, row_lo: int = 0, per_head: bool = False, lib=None)
     if rc != 0:
         raise OracleError(f"orc_colsum failed ({rc})")
     return out
+
+
+def snapkv_select(votes, w: int, pool: int, keep: int, lib=None) -> np.ndarray:
+    """SnapKV's kept positions of one unit from its votes [G][P] (orc_snapkv_select)."""
+    lib = lib or load()
+    v = _f64(votes)
+    G, P = v.shape
+    kept = np.empty(P, dtype=np.int32)
+    n = lib.orc_snapkv_select(G, P, int(w), int(pool), int(keep), _p(v), kept.ctypes.data_as(_ip))
+    if n < 0:
+        raise OracleError(f"orc_snapkv_select failed ({n})")
+    return kept[:n].copy()
+
+
+def snapkv(cfg: OrcCfg, q, k, w: int, pool: int, keep: int, lib=None):
+    """(kept positions, votes [G][P]) of one unit's prompt (orc_snapkv)."""
+    lib = lib or load()
+    G, D = cfg.group, cfg.head_dim
+    q = _f64(q).reshape(-1, G, D)
+    P = q.shape[0]
+    k = _f64(k).reshape(P, D)
+    votes = np.empty((G, P), dtype=np.float64)
+    kept = np.empty(P, dtype=np.int32)
+    n = lib.orc_snapkv(C.byref(cfg), P, int(w), int(pool), int(keep), _p(q), _p(k), _p(votes),
+                       kept.ctypes.data_as(_ip))
+    if n < 0:
+        raise OracleError(f"orc_snapkv failed ({n})")
+    return kept[:n].copy(), votes
 
 
 def philox4x64_10(ctr, key, lib=None):

@@ -469,3 +469,64 @@ int orc_colsum(const orc_cfg *c, int P, int row_lo, const double *q, const doubl
     free(w);
     return rc;
 }
+
+/* ---- SnapKV selection ----------------------------------------------------- */
+typedef struct {
+    double v;
+    int pos;
+} vote_pos;
+
+/* Keep order: higher vote first; on equal votes the lower position first. */
+static int cmp_vote_keep(const void *a, const void *b)
+{
+    const vote_pos *x = (const vote_pos *)a, *y = (const vote_pos *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->pos < y->pos) ? -1 : (x->pos > y->pos) ? 1 : 0;
+}
+
+int orc_snapkv_select(int G, int P, int w, int pool, int keep, const double *votes, int32_t *kept)
+{
+    if (G < 1 || P < 1 || w < 1 || w > P || pool < 1 || pool % 2 == 0 || keep < 0 || !votes || !kept)
+        return ORC_EARG;
+    const int Pp = P - w, r = pool / 2;
+    char *mark = (char *)calloc((size_t)P, 1);
+    vote_pos *cand = (vote_pos *)malloc(sizeof(vote_pos) * (Pp > 0 ? (size_t)Pp : 1));
+    if (!mark || !cand) {
+        free(mark);
+        free(cand);
+        return ORC_ENOMEM;
+    }
+    for (int g = 0; g < G; ++g) {
+        const double *vg = votes + (size_t)g * P;
+        for (int j = 0; j < Pp; ++j) {
+            double m = -INFINITY;
+            for (int x = j - r; x <= j + r; ++x)
+                if (x >= 0 && x < Pp && vg[x] > m) m = vg[x];
+            cand[j].v = m;
+            cand[j].pos = j;
+        }
+        qsort(cand, (size_t)Pp, sizeof(vote_pos), cmp_vote_keep);
+        const int kk = keep < Pp ? keep : Pp;
+        for (int i = 0; i < kk; ++i) mark[cand[i].pos] = 1;
+    }
+    for (int j = Pp; j < P; ++j) mark[j] = 1;
+    int n = 0;
+    for (int j = 0; j < P; ++j)
+        if (mark[j]) kept[n++] = j;
+    free(mark);
+    free(cand);
+    return n;
+}
+
+int orc_snapkv(const orc_cfg *c, int P, int w, int pool, int keep, const double *q, const double *k,
+               double *votes, int32_t *kept)
+{
+    if (!c || P < 1 || w < 1 || w > P) return ORC_EARG;
+    double *v = votes ? votes : (double *)malloc(sizeof(double) * (size_t)c->group * P);
+    if (!v) return ORC_ENOMEM;
+    int rc = orc_colsum(c, P, P - w, q, k, 1, v);
+    if (rc == ORC_OK) rc = orc_snapkv_select(c->group, P, w, pool, keep, v, kept);
+    if (!votes) free(v);
+    return rc;
+}

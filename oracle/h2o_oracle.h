@@ -106,6 +106,23 @@ int orc_step_many(orc_unit **u, int n, const double *const *q, const double *con
 int orc_colsum(const orc_cfg *c, int P, int row_lo, const double *q, const double *k,
                int per_head, double *out);
 
+/* SnapKV's prompt selection for one unit ("Attention Sinks and KV cache
+ * eviction", sec. 4.3): the prompt's last w positions form the observation
+ * window; each query head g votes for the prefix positions j < P - w with
+ * votes[g][j] (its window rows' attention weights on j, orc_colsum with
+ * row_lo = P - w, per head); the votes are max-pooled over the positions
+ * within pool / 2 of j (pool odd, clipped at the prefix ends); each head keeps
+ * its `keep` prefix positions of highest pooled vote (equal votes: the lower
+ * position first); the unit keeps the union over its heads plus the window.
+ * votes: [G][P] (entries j >= P - w unused).  kept: receives the kept
+ * positions in ascending order (at most P).  Returns the count, or ORC_EARG. */
+int orc_snapkv_select(int G, int P, int w, int pool, int keep, const double *votes, int32_t *kept);
+
+/* orc_colsum (row_lo = P - w, per head) followed by orc_snapkv_select; votes
+ * receives the [G][P] votes when not NULL.  Returns the count or an error. */
+int orc_snapkv(const orc_cfg *c, int P, int w, int pool, int keep, const double *q, const double *k,
+               double *votes, int32_t *kept);
+
 /* Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11). */
 void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
 

@@ -399,6 +399,70 @@ def pin_colsum_equals_decode_accumulation(lib):
     assert np.allclose(per.sum(axis=0), want, rtol=1e-12, atol=1e-14)
 
 
+def pin_snapkv_pooling_and_union(lib):
+    """A vote spike at j0 pooled with kernel 7 covers [j0 - 3, j0 + 3] (clipped at the
+    prefix ends); keep = 7 keeps exactly that range; two heads with spikes at
+    different places keep the union of both ranges; the window is always kept."""
+    P, w = 40, 6
+    Pp = P - w
+    window = list(range(Pp, P))
+    v = np.zeros((1, P))
+    v[0, 12] = 1.0
+    assert list(O.snapkv_select(v, w, 7, 7, lib=lib)) == list(range(9, 16)) + window
+    # clipped at position 0: pooled 1 on 0..3, then the zeros go lowest position first
+    v = np.zeros((1, P))
+    v[0, 0] = 0.5
+    assert list(O.snapkv_select(v, w, 7, 6, lib=lib)) == list(range(0, 6)) + window
+    # window votes never enter the pooling: a spike 6 before the window pools onto
+    # Pp-9..Pp-3, and keep = 4 takes the lowest four of that range, not the last
+    # prefix positions next to the window's large votes
+    v = np.zeros((1, P))
+    v[0, Pp - 6] = 2.0
+    v[0, Pp:] = 9.0
+    assert list(O.snapkv_select(v, w, 7, 4, lib=lib)) == list(range(Pp - 9, Pp - 5)) + window
+    v = np.zeros((2, P))
+    v[0, 5] = 1.0
+    v[1, 25] = 1.0
+    assert list(O.snapkv_select(v, w, 7, 7, lib=lib)) == list(range(2, 9)) + list(range(22, 29)) + window
+
+
+def pin_snapkv_topk_matches_library(lib):
+    """Random votes: pooled by scipy's maximum_filter1d (constant -inf border),
+    top-k per head by numpy's stable sort of the negated pooled votes, union + window."""
+    from scipy.ndimage import maximum_filter1d
+    rng = np.random.default_rng(21)
+    G, P, w, pool, keep = 3, 60, 10, 7, 9
+    v = rng.random((G, P))
+    Pp = P - w
+    want = set(range(Pp, P))
+    for g in range(G):
+        pooled = maximum_filter1d(v[g, :Pp], size=pool, mode="constant", cval=-np.inf)
+        want |= set(np.argsort(-pooled, kind="stable")[:keep].tolist())
+    assert list(O.snapkv_select(v, w, pool, keep, lib=lib)) == sorted(want)
+    # keep >= prefix: everything kept
+    assert list(O.snapkv_select(v, w, pool, Pp + 3, lib=lib)) == list(range(P))
+
+
+def pin_snapkv_ties_keep_lower_positions(lib):
+    """Equal votes everywhere: each head keeps the `keep` lowest positions."""
+    v = np.ones((2, 30))
+    assert list(O.snapkv_select(v, 4, 5, 3, lib=lib)) == [0, 1, 2] + list(range(26, 30))
+
+
+def pin_snapkv_votes_are_window_weights(lib):
+    """The votes of orc_snapkv are the window rows' weights: per head they add up
+    to w (each row sums to one) and equal orc_colsum from row P - w."""
+    D, G, P, w = 16, 2, 50, 8
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((P, G, D)) * 2.0
+    k = rng.standard_normal((P, D))
+    cfg = O.make_cfg(head_dim=D, group=G)
+    kept, votes = O.snapkv(cfg, q, k, w, 7, 5, lib=lib)
+    assert np.allclose(votes.sum(axis=1), w, rtol=0, atol=1e-10)
+    assert np.allclose(votes, O.colsum(cfg, q, k, row_lo=P - w, per_head=True, lib=lib), rtol=0, atol=0)
+    assert list(kept) == list(O.snapkv_select(votes, w, 7, 5, lib=lib))
+
+
 ALL_PINS = [
     pin_attention_full_cache,
     pin_scores_and_selection_recomputed,
@@ -413,4 +477,8 @@ ALL_PINS = [
     pin_golden_cache_manager_sizes,
     pin_colsum_identical_keys,
     pin_colsum_equals_decode_accumulation,
+    pin_snapkv_pooling_and_union,
+    pin_snapkv_topk_matches_library,
+    pin_snapkv_ties_keep_lower_positions,
+    pin_snapkv_votes_are_window_weights,
 ]

@@ -48,6 +48,15 @@ MUTANTS = {
     "colsum_key_is_query_row": ("const double *kj = k + (size_t)j * D;", "const double *kj = k + (size_t)i * D;"),
     "colsum_head_major_query": ("const double *qi = q + ((size_t)i * G + g) * D;",
                                 "const double *qi = q + ((size_t)g * P + i) * D;"),
+    "snapkv_pool_radius": ("const int Pp = P - w, r = pool / 2;", "const int Pp = P - w, r = pool / 2 + 1;"),
+    "snapkv_ties_keep_higher": ("    return (x->pos < y->pos) ? -1 : (x->pos > y->pos) ? 1 : 0;\n}\n\nint orc_snapkv_select",
+                                "    return (x->pos > y->pos) ? -1 : (x->pos < y->pos) ? 1 : 0;\n}\n\nint orc_snapkv_select"),
+    "snapkv_drop_window": ("    for (int j = Pp; j < P; ++j) mark[j] = 1;\n", ""),
+    "snapkv_pool_into_window": ("if (x >= 0 && x < Pp && vg[x] > m)", "if (x >= 0 && x < P && vg[x] > m)"),
+    "snapkv_lowest_votes": ("    if (x->v > y->v) return -1;\n    if (x->v < y->v) return 1;",
+                            "    if (x->v < y->v) return -1;\n    if (x->v > y->v) return 1;"),
+    "snapkv_first_head_only": ("for (int g = 0; g < G; ++g) {\n        const double *vg",
+                               "for (int g = 0; g < 1; ++g) {\n        const double *vg"),
     "random_largest_words": ("    if (x->key < y->key) return -1;\n    if (x->key > y->key) return 1;",
                              "    if (x->key > y->key) return -1;\n    if (x->key < y->key) return 1;"),
 }
