@@ -170,8 +170,32 @@ void h2o_destroy(h2o_ctx *ctx);
 int h2o_prefill_scores(const h2o_config *cfg, const int32_t *prompt_len, const float *prompt_q,
                        const void *prompt_k, double *out, void *stream);
 
+/* SnapKV's prompt selection ("Attention Sinks and KV cache eviction",
+ * sec. 4.3), per sequence b and KV head h, with w_b = min(window, P_b) and the
+ * prefix [0, P_b - w_b):
+ *   votes     for each query head g of h and prompt position j, the sum over
+ *             the window rows i in [P_b - w_b, P_b) of row i's causal softmax
+ *             weight on key j (rows as in h2o_prefill_scores, one sum per head);
+ *   pooling   each prefix vote replaced by the largest vote of the prefix
+ *             positions within pool / 2 of it;
+ *   keep      each query head keeps its `keep` prefix positions of highest
+ *             pooled vote (equal votes: the lower position);
+ *   kept set  the union over the G query heads of h, plus the window.
+ *   prompt_q, prompt_k  as h2o_prefill_scores.
+ *   votes       device [sum P_b][Hq] fp64 (query head h G + g in column h G + g;
+ *               entries of window positions are the window rows' weights on
+ *               them), or NULL to use scratch.
+ *   kept        device [B][Hkv][cap] int32: kept positions ascending, -1 after.
+ *   kept_count  device [B][Hkv] int32.
+ *   cap         >= min(P_b, w_b + G min(keep, P_b - w_b)) for every b.
+ *   window >= 1, pool odd >= 1, keep >= 0; P_b <= 524288.
+ * Supported shapes and errors as h2o_prefill_scores. */
+int h2o_snapkv_select(const h2o_config *cfg, const int32_t *prompt_len, int32_t window, int32_t pool,
+                      int32_t keep, const float *prompt_q, const void *prompt_k, double *votes,
+                      int32_t *kept, int32_t *kept_count, int32_t cap, void *stream);
+
 /* Message of the last error on ctx, or, when ctx is NULL, of the last failed call
- * made without a context (h2o_init, h2o_prefill_scores). */
+ * made without a context (h2o_init, h2o_prefill_scores, h2o_snapkv_select). */
 const char *h2o_last_error(const h2o_ctx *ctx);
 
 #ifdef __cplusplus

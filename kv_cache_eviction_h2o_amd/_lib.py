@@ -23,7 +23,7 @@ PAGE_SIZE = 16
 
 # Every symbol include/h2o.h declares.
 SYMBOLS = ("h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
-           "h2o_info", "h2o_destroy", "h2o_prefill_scores", "h2o_last_error")
+           "h2o_info", "h2o_destroy", "h2o_prefill_scores", "h2o_snapkv_select", "h2o_last_error")
 
 
 class H2OConfig(C.Structure):
@@ -75,6 +75,9 @@ def load_library(path: str = LIB):
     lib.h2o_destroy.argtypes = [vp]
     lib.h2o_prefill_scores.restype = C.c_int
     lib.h2o_prefill_scores.argtypes = [C.POINTER(H2OConfig), i32p, vp, vp, vp, vp]
+    lib.h2o_snapkv_select.restype = C.c_int
+    lib.h2o_snapkv_select.argtypes = [C.POINTER(H2OConfig), i32p, C.c_int32, C.c_int32, C.c_int32, vp, vp, vp,
+                                      vp, vp, C.c_int32, vp]
     lib.h2o_last_error.restype = C.c_char_p
     lib.h2o_last_error.argtypes = [vp]
     _lib = lib
@@ -139,6 +142,33 @@ def prefill_scores(cfg: H2OConfig, prompt_lens, prompt_q, prompt_k, out=None, st
     if rc != H2O_OK:
         raise H2OError(rc, lib.h2o_last_error(None).decode(errors="replace"))
     return out
+
+
+def snapkv_select(cfg: H2OConfig, prompt_lens, prompt_q, prompt_k, window: int, pool: int, keep: int,
+                  stream=None):
+    """SnapKV's prompt selection (h2o_snapkv_select): returns (kept [B][Hkv][cap] int32
+    cuda, ascending, -1 after the count; kept_count [B][Hkv]; votes [sum P][Hq] fp64)."""
+    import torch
+    lib = load_library()
+    lens = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    if lens.shape != (cfg.batch,):
+        raise ValueError("prompt_lens must have one entry per sequence")
+    total = int(lens.sum())
+    kv = torch.bfloat16 if cfg.kv_dtype == BF16 else torch.float32
+    H2OCache._check_tensor("prompt_q", prompt_q, (total, cfg.n_q_heads, cfg.head_dim), torch.float32)
+    H2OCache._check_tensor("prompt_k", prompt_k, (total, cfg.n_kv_heads, cfg.head_dim), kv)
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    cap = max(1, max(min(P, min(window, P) + G * min(keep, P - min(window, P))) for P in lens))
+    dev = prompt_q.device
+    votes = torch.empty((total, cfg.n_q_heads), dtype=torch.float64, device=dev)
+    kept = torch.empty((cfg.batch, cfg.n_kv_heads, cap), dtype=torch.int32, device=dev)
+    count = torch.empty((cfg.batch, cfg.n_kv_heads), dtype=torch.int32, device=dev)
+    rc = lib.h2o_snapkv_select(C.byref(cfg), lens.ctypes.data_as(C.POINTER(C.c_int32)), int(window),
+                               int(pool), int(keep), _ptr(prompt_q), _ptr(prompt_k), _ptr(votes),
+                               _ptr(kept), _ptr(count), int(cap), _stream_handle(stream))
+    if rc != H2O_OK:
+        raise H2OError(rc, lib.h2o_last_error(None).decode(errors="replace"))
+    return kept, count, votes
 
 
 def _stream_handle(stream):

@@ -135,10 +135,25 @@ struct ColsumArgs {
     int64_t seq_off[kMaxArgBatch];
 };
 
+// SnapKV's prompt selection from per-head window votes (h2o_prefill.hip).
+struct SnapArgs {
+    int B, Hq, Hkv, G;
+    int pool_r;             // max pooling over positions within pool_r of j
+    int keep;               // prefix positions kept per query head
+    int cap;                // entries per unit in kept
+    const double* votes;    // [sum P][Hq]
+    double* pooled;         // scratch [sum P][Hq] (prefix positions only)
+    int32_t* kept;          // [B * Hkv][cap] ascending positions, -1 past the count
+    int32_t* count;         // [B * Hkv]
+    int32_t seq_p[kMaxArgBatch], seq_w[kMaxArgBatch];
+    int64_t seq_off[kMaxArgBatch];
+};
+
 // Launchers (h2o_kernels.hip unless noted).  Each returns the launch's hipError_t.
 hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st);
 hipError_t launch_step_mfma(const StepArgs& a, int max_n_att, hipStream_t st);  // h2o_mfma.hip
 hipError_t launch_colsum(const ColsumArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
+hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
 hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);

@@ -276,7 +276,91 @@ hipError_t launch_colsum_g(const ColsumArgs& a, int max_p, hipStream_t st)
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ SnapKV
+// ("Attention Sinks and KV cache eviction", sec. 4.3) from the per-head window
+// votes: max pooling over the prefix, each query head's top `keep` prefix
+// positions, the union over the unit's heads, plus the window.
+__global__ void __launch_bounds__(256) snapkv_pool_kernel(const SnapArgs a)
+{
+    const int b = blockIdx.y;
+    const int P = a.seq_p[b], Pp = P - a.seq_w[b];
+    const int64_t off = a.seq_off[b];
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // (j, query head)
+    if (idx >= (long long)Pp * a.Hq) return;
+    const int j = (int)(idx / a.Hq), hq = (int)(idx - (long long)j * a.Hq);
+    const int x0 = max(0, j - a.pool_r), x1 = min(Pp - 1, j + a.pool_r);
+    double m = -INFINITY;
+    for (int x = x0; x <= x1; ++x) m = fmax(m, a.votes[(size_t)(off + x) * a.Hq + hq]);
+    a.pooled[(size_t)(off + j) * a.Hq + hq] = m;
+}
+
+constexpr int kSNT = 256;
+
+__global__ void __launch_bounds__(kSNT) snapkv_select_kernel(const SnapArgs a)
+{
+    extern __shared__ unsigned bits[];  // one bit per prompt position: kept
+    __shared__ RadixSmem s_rad;
+    __shared__ ScanSmem s_scan;
+    const int unit = blockIdx.x, b = unit / a.Hkv, h = unit - b * a.Hkv;
+    const int P = a.seq_p[b], Pp = P - a.seq_w[b];
+    const int64_t off = a.seq_off[b];
+    const int tid = threadIdx.x;
+    const int nw = (P + 31) / 32;
+    for (int i = tid; i < nw; i += kSNT) bits[i] = 0u;
+    __syncthreads();
+    const int e = Pp - a.keep;  // prefix positions each head leaves out
+    for (int g = 0; g < a.G; ++g) {
+        const int hq = h * a.G + g;
+        // keys as in the decode step's bulk selection: (vote bits, ~position);
+        // the e smallest go, so equal votes keep the lower position
+        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
+            const unsigned long long u = ord64(a.pooled[(size_t)(off + j) * a.Hq + hq]);
+            wk[2] = (unsigned)(u >> 32);
+            wk[1] = (unsigned)u;
+            wk[0] = ~(unsigned)j;
+            return true;
+        };
+        if (e > 0) {
+            radix_select<kSNT>(key_of, Pp, e, 0, s_rad);
+            for (int j = tid; j < Pp; j += kSNT) {
+                unsigned wk[3];
+                key_of(j, wk);
+                if (!key_le(wk, s_rad)) atomicOr(&bits[j >> 5], 1u << (j & 31));
+            }
+        } else {
+            for (int j = tid; j < Pp; j += kSNT) atomicOr(&bits[j >> 5], 1u << (j & 31));
+        }
+        __syncthreads();
+    }
+    for (int j = Pp + tid; j < P; j += kSNT) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    __syncthreads();
+    int* out = a.kept + (size_t)unit * a.cap;
+    const int n = collect<kSNT>(0, P, [&](int j) { return ((bits[j >> 5] >> (j & 31)) & 1u) != 0; }, out,
+                                s_scan);
+    for (int i = n + tid; i < a.cap; i += kSNT) out[i] = -1;
+    if (tid == 0) a.count[unit] = n;
+}
+
 }  // namespace
+
+hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
+{
+    if (max_p <= 0) return hipSuccess;
+    const long long cells = (long long)max_p * a.Hq;
+    hipLaunchKernelGGL(snapkv_pool_kernel, dim3((unsigned)((cells + 255) / 256), a.B), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t dyn = (size_t)((max_p + 31) / 32) * 4;
+    static size_t dyn_set = 48 * 1024;
+    if (dyn > dyn_set) {
+        e = hipFuncSetAttribute((const void*)snapkv_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)dyn);
+        if (e != hipSuccess) return e;
+        dyn_set = dyn;
+    }
+    hipLaunchKernelGGL(snapkv_select_kernel, dim3(a.B * a.Hkv), dim3(kSNT), dyn, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_colsum(const ColsumArgs& a, int max_p, hipStream_t st)
 {

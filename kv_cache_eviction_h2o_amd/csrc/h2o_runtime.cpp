@@ -327,6 +327,74 @@ int colsum_run(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo
     return H2O_OK;
 }
 
+// SnapKV's selection (h2o_snapkv_select): validate, per-head window votes by the
+// column-sum passes, then pooling and the per-unit selection.
+int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool, int keep, const float* q,
+               const void* k, double* votes, int32_t* kept, int32_t* count, int cap, void* stream)
+{
+    if (!cfg || !plen) return fail(nullptr, H2O_EINVAL, "null config or prompt lengths");
+    const int B = cfg->batch, Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
+    if (B < 1 || B > kMaxArgBatch)
+        return fail(nullptr, H2O_EINVAL, "prompt column sums take 1 to 128 sequences");
+    if (Hkv < 1 || Hq < Hkv || Hq % Hkv != 0)
+        return fail(nullptr, H2O_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+    if (window < 1) return fail(nullptr, H2O_EINVAL, "observation window must be >= 1");
+    if (pool < 1 || pool % 2 == 0) return fail(nullptr, H2O_EINVAL, "pooling kernel must be odd and >= 1");
+    if (keep < 0) return fail(nullptr, H2O_EINVAL, "keep must be >= 0");
+    const int G = Hq / Hkv;
+    std::vector<int32_t> lo(B);
+    SnapArgs a{};
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.pool_r = pool / 2;
+    a.keep = keep;
+    a.cap = cap;
+    long long off = 0, total = 0;
+    int maxP = 0;
+    for (int b = 0; b < B; ++b) {
+        const int P = plen[b];
+        if (P < 1) return fail(nullptr, H2O_EINVAL, "prompt lengths must be >= 1");
+        if (P > (1 << 19)) return fail(nullptr, H2O_EINVAL, "SnapKV selection takes prompts up to 524288");
+        const int w = std::min(window, P);
+        lo[b] = P - w;
+        const long long most = std::min<long long>(P, (long long)w + (long long)G * std::min(keep, P - w));
+        if (cap < most) return fail(nullptr, H2O_EINVAL, "cap is below the largest kept set");
+        a.seq_p[b] = P;
+        a.seq_w[b] = w;
+        a.seq_off[b] = off;
+        off += P;
+        maxP = std::max(maxP, P);
+    }
+    total = off;
+    if (!kept || !count) return fail(nullptr, H2O_EINVAL, "null kept or kept_count");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    double* vb = votes;
+    if (!vb && (e = hipMallocAsync((void**)&vb, (size_t)total * Hq * sizeof(double), st)) != hipSuccess)
+        return hip_fail(nullptr, e, "SnapKV: scratch for votes");
+    int rc = colsum_run(cfg, plen, lo.data(), q, k, 1, vb, stream);
+    if (rc != H2O_OK) {
+        if (!votes) (void)hipFreeAsync(vb, st);
+        return rc;
+    }
+    a.votes = vb;
+    if ((e = hipMallocAsync((void**)&a.pooled, (size_t)total * Hq * sizeof(double), st)) != hipSuccess) {
+        if (!votes) (void)hipFreeAsync(vb, st);
+        return hip_fail(nullptr, e, "SnapKV: scratch for pooled votes");
+    }
+    a.kept = kept;
+    a.count = count;
+    e = launch_snapkv(a, maxP, st);
+    const hipError_t e1 = hipFreeAsync(a.pooled, st);
+    const hipError_t e2 = votes ? hipSuccess : hipFreeAsync(vb, st);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV: launch");
+    if (e1 != hipSuccess || e2 != hipSuccess)
+        return hip_fail(nullptr, e1 != hipSuccess ? e1 : e2, "SnapKV: scratch release");
+    return H2O_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -595,6 +663,14 @@ int h2o_prefill_scores(const h2o_config* cfg, const int32_t* prompt_len, const f
                        const void* prompt_k, double* out, void* stream)
 {
     return colsum_run(cfg, prompt_len, nullptr, prompt_q, prompt_k, 0, out, stream);
+}
+
+int h2o_snapkv_select(const h2o_config* cfg, const int32_t* prompt_len, int32_t window, int32_t pool,
+                      int32_t keep, const float* prompt_q, const void* prompt_k, double* votes,
+                      int32_t* kept, int32_t* kept_count, int32_t cap, void* stream)
+{
+    return snapkv_run(cfg, prompt_len, window, pool, keep, prompt_q, prompt_k, votes, kept, kept_count, cap,
+                      stream);
 }
 
 const char* h2o_last_error(const h2o_ctx* c)

@@ -155,3 +155,23 @@ def test_prefill_scores_null_arguments(lib):
     assert lib.h2o_prefill_scores(None, None, None, None, None, None) == L.H2O_EINVAL
     assert _prefill(lib, cfg, [10, 10], ptr=0) == L.H2O_EINVAL
     assert "null" in lib.h2o_last_error(None).decode()
+
+
+def _snap(lib, cfg, lens, window=32, pool=7, keep=16, cap=4096, ptr=16):
+    arr = (C.c_int32 * len(lens))(*lens)
+    p = C.c_void_p(ptr) if ptr else None
+    return lib.h2o_snapkv_select(C.byref(cfg), arr, window, pool, keep, p, p, None, p, p, cap, None)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(window=0), "window"),
+    (dict(pool=4), "odd"),
+    (dict(pool=0), "odd"),
+    (dict(keep=-1), "keep"),
+    (dict(cap=10), "cap"),
+    (dict(ptr=0), "null"),
+])
+def test_snapkv_select_rejects_before_device(lib, kw, msg):
+    cfg = L.make_config(**GOOD)
+    assert _snap(lib, cfg, [100, 200], **kw) == L.H2O_EINVAL
+    assert msg in lib.h2o_last_error(None).decode()
