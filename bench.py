@@ -108,6 +108,9 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="time h2o_prefill_scores (prefill-scored initial scores) over the "
                          "workload's prompts instead of the decode step")
+    ap.add_argument("--snapkv", action="store_true",
+                    help="time h2o_snapkv_select (window 32, pooling 7, 20%% of each prompt kept per "
+                         "query head) over the workload's prompts instead of the decode step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -321,6 +324,62 @@ def prefill_main(args, w):
     print(json.dumps(line), flush=True)
 
 
+def snapkv_main(args, w):
+    """--snapkv: h2o_snapkv_select over the workload's prompts (one layer)."""
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+    lens = WL.prompt_lengths(w)
+    B, Hq, Hkv, D, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    window, pool = 32, 7
+    keep = max(1, min(lens) // 5)
+    dev = torch.device("cuda")
+    L.load_library()
+    pk, _ = S.device_prompt_kv(w.recipe, 0, lens, Hkv, dev)
+    pq = S.device_prompt_queries(w.recipe, 0, lens, Hq, dev)
+    cfg = L.config_from_workload(w, max_len=max(lens) + 1)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        kept, count, votes = L.snapkv_select(cfg, lens, pq, pk, window, pool, keep)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    sh = C.c_void_p(stream.cuda_stream)
+    e0, e1 = hev.create(), hev.create()
+    t0 = time.perf_counter()
+    hev.record(e0, sh)
+    for _ in range(args.steps):
+        kept, count, votes = L.snapkv_select(cfg, lens, pq, pk, window, pool, keep)
+    hev.record(e1, sh)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_call = hev.elapsed_s(e0, e1) / args.steps
+    hev.destroy(e0)
+    hev.destroy(e1)
+    c = count.cpu().numpy()
+    if not (np.all(c >= window + keep) and np.all(c <= window + G * keep)):
+        raise SystemExit(f"kept counts out of range: {c.min()}..{c.max()}")
+    tokens = float(sum(lens))
+    rows = sum(sum(i + 1 for i in range(P - min(window, P), P)) for P in lens)
+    flops = 2.0 * D * Hq * rows
+    line = {
+        "metric": "prompt tokens selected/sec (SnapKV, h2o_snapkv_select)",
+        "value": round(tokens / per_call, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (q as hi+lo)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+                   "prompt_lens": lens if len(set(lens)) > 1 else lens[0], "window": window, "pool": pool,
+                   "keep_per_head": keep, "mean_kept": round(float(c.mean()), 1),
+                   "entry_point": "h2o_snapkv_select", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / per_call / 1e12, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / per_call / 1e12 / PEAK_BF16_TFLOPS, 5),
+                     "traffic": None, "mean_call_us": round(per_call * 1e6, 2), "algorithmic_flops": flops,
+                     "note": "the window rows' causal logits once; the call also pools and selects"},
+        "cpu_baseline": None,
+        "kernel_source_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace or args.summarize_counters:
@@ -338,6 +397,9 @@ def main():
     w = next(x for x in WL.ALL if x.name == args.workload)
     if args.prefill:
         prefill_main(args, w)
+        return
+    if args.snapkv:
+        snapkv_main(args, w)
         return
     layers = args.layers or w.layers
     K_steps, W_steps = args.steps, args.warmup
