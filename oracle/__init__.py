@@ -146,6 +146,36 @@ def snapkv(cfg: OrcCfg, q, k, w: int, pool: int, keep: int, lib=None):
     return kept[:n].copy(), votes
 
 
+def quantize_rows(x):
+    """Int8 K/V rows with one scale per row: x [n][D] (any float dtype, taken as
+    float32) -> (codes int8 [n][D], scale float32 [n]).
+
+    Definition (the pages name INT8 K/V storage without fixing a scheme -- "KV
+    cache eviction policies" page, section on alternatives used together with
+    eviction (INT4/INT8 K/V, orthogonal to eviction); "Attention Sinks and KV
+    cache eviction", sec. 1.2 (compressing each token's K/V by quantisation)):
+    per row, in float32,
+    a = max |x_d|, scale = a / 127, code_d = rint(x_d / scale) (round half to
+    even) clamped to [-127, 127]; a row of zeros has scale 0 and codes 0.  The
+    row stands for code_d * scale."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("rows [n][D] expected")
+    a = np.max(np.abs(x), axis=1)
+    scale = (a / np.float32(127.0)).astype(np.float32)
+    codes = np.zeros(x.shape, dtype=np.int8)
+    nz = scale > 0
+    if np.any(nz):
+        q = np.rint(x[nz] / scale[nz, None]).astype(np.float32)
+        codes[nz] = np.clip(q, -127, 127).astype(np.int8)
+    return codes, scale
+
+
+def dequantize_rows(codes, scale) -> np.ndarray:
+    """float64 rows code * scale (exact)."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
 def philox4x64_10(ctr, key, lib=None):
     lib = lib or load()
     c = (C.c_uint64 * 4)(*[int(x) & 0xFFFFFFFFFFFFFFFF for x in ctr])

@@ -463,6 +463,37 @@ def pin_snapkv_votes_are_window_weights(lib):
     assert list(kept) == list(O.snapkv_select(votes, w, 7, 5, lib=lib))
 
 
+def pin_int8_rows(lib):
+    """Int8 row quantisation (oracle.quantize_rows): the bounds and special cases
+    the definition fixes -- scale = max|x| / 127; the largest element maps to
+    +-127; every element is reproduced within half a scale step; signs and zeros
+    are kept; a zero row has scale 0; scaling a row by a power of two scales the
+    scale alone; a row already on the grid (integers up to 127 times a step) is
+    stored exactly."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((64, 128)) * np.exp(rng.uniform(-4, 4, (64, 1)))).astype(np.float32)
+    x[5] = 0.0
+    x[6, :] = 0.0
+    x[6, 17] = -3.5
+    codes, scale = O.quantize_rows(x)
+    a = np.max(np.abs(x), axis=1)
+    assert np.array_equal(scale, (a / np.float32(127.0)).astype(np.float32))
+    assert scale[5] == 0.0 and not codes[5].any()
+    assert codes[6, 17] == -127 and np.count_nonzero(codes[6]) == 1
+    big = np.argmax(np.abs(x), axis=1)
+    nz = a > 0
+    assert np.all(np.abs(codes[nz, big[nz]]) == 127)
+    err = np.abs(O.dequantize_rows(codes, scale) - x.astype(np.float64))
+    assert np.all(err <= 0.5 * scale[:, None].astype(np.float64) * (1 + 1e-6))
+    assert np.all((codes > 0) <= (x > 0)) and np.all((codes < 0) <= (x < 0))
+    c2, s2 = O.quantize_rows(x * np.float32(8.0))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scale * np.float32(8.0))
+    grid = rng.integers(-127, 128, (8, 128)).astype(np.float32)
+    grid[:, 0] = 127.0
+    cg, sg = O.quantize_rows(grid * np.float32(0.25))
+    assert np.all(sg == np.float32(0.25)) and np.array_equal(cg.astype(np.float32), grid)
+
+
 ALL_PINS = [
     pin_attention_full_cache,
     pin_scores_and_selection_recomputed,
@@ -481,4 +512,5 @@ ALL_PINS = [
     pin_snapkv_topk_matches_library,
     pin_snapkv_ties_keep_lower_positions,
     pin_snapkv_votes_are_window_weights,
+    pin_int8_rows,
 ]
