@@ -94,7 +94,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=WL.OPT_LAYER.name,
-                    choices=[w.name for w in WL.ALL])
+                    choices=[w.name for w in WL.ALL + WL.VARIANTS])
     ap.add_argument("--layers", type=int, default=0, help="layer instances (0 = workload default)")
     ap.add_argument("--window-start", type=int, default=512,
                     help="decode step at which the timed window starts")
@@ -394,7 +394,7 @@ def main():
     import torch
     from kv_cache_eviction_h2o_amd import _lib as L
 
-    w = next(x for x in WL.ALL if x.name == args.workload)
+    w = next(x for x in WL.ALL + WL.VARIANTS if x.name == args.workload)
     if args.prefill:
         prefill_main(args, w)
         return
@@ -431,7 +431,7 @@ def main():
         outs.append(torch.empty((B, Hq, D), dtype=torch.float32, device=dev))
         del pk, pv
     torch.cuda.synchronize()
-    q_stride, kv_stride = B * Hq * D * 4, B * Hkv * D * (2 if w.kv_dtype == "bf16" else 4)
+    q_stride, kv_stride = B * Hq * D * 4, B * Hkv * D * (2 if w.recipe.kv_dtype == "bf16" else 4)
     ctxs = [c.ctx for c in caches]
     qb = [q.data_ptr() for q in qs]
     kb = [k.data_ptr() for k in ks]
@@ -486,9 +486,10 @@ def main():
     sbytes = 8 if w.score_dtype == "f64" else 4
     if w.selector == "random":
         sbytes = 0
-    kv_elem = 2 if w.kv_dtype == "bf16" else 4
+    kv_elem = 2 if w.recipe.kv_dtype == "bf16" else 4
     launch_b = np.array([M.launch_bytes(win[:, i], n_kv_heads=Hkv, head_dim=D, kv_elem=kv_elem,
-                                        group=G, score_bytes=sbytes) for i in range(K_steps)])
+                                        group=G, score_bytes=sbytes, int8_rows=w.kv_dtype == "i8")
+                        for i in range(K_steps)])
     step_bytes = float(launch_b.sum()) * layers
     roof = None
     if use_ev:

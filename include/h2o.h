@@ -41,8 +41,15 @@
  *   - Positions: sequence b's prompt holds positions 0..P_b-1; its s-th
  *     decode step (s = 0, 1, ...) appends position t = P_b + s.  All sequences
  *     step together.
- *   - Supported shapes: (kv_dtype, head_dim) = (H2O_BF16, 128) or
- *     (H2O_F32, 64); G in {1, 2, 4, 8}.
+ *   - Supported shapes: (kv_dtype, head_dim) = (H2O_BF16, 128), (H2O_I8, 128)
+ *     or (H2O_F32, 64); G in {1, 2, 4, 8}.
+ *   - H2O_I8 (compressed state; "KV cache eviction policies", section on
+ *     alternatives used with eviction: INT8 K/V storage is orthogonal to
+ *     eviction; "Attention Sinks and KV cache eviction", sec. 1.2): prompts
+ *     and new tokens arrive as bf16 and are stored as int8 rows of 128 with
+ *     one fp32 scale per (token, KV head) row: scale = max |x| / 127,
+ *     code = rint(x / scale) in [-127, 127], all in fp32 (a zero row has
+ *     scale 0).  Attention, also over the new token, uses code * scale.
  *   - Errors: every call returns an h2o_status.  Arguments are validated
  *     before anything is enqueued; on error nothing is enqueued and the
  *     context is unchanged (H2O_EDEVICE aside).  h2o_last_error() gives the
@@ -73,14 +80,14 @@ typedef enum {
 } h2o_status;
 
 enum { H2O_SEL_H2O = 0, H2O_SEL_RANDOM = 1 };
-enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F64 = 2 };
+enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F64 = 2, H2O_I8 = 3 };
 
 typedef struct {
     int32_t batch;         /* B sequences */
     int32_t n_q_heads;     /* Hq */
     int32_t n_kv_heads;    /* Hkv; Hq must be a multiple */
     int32_t head_dim;      /* D */
-    int32_t kv_dtype;      /* H2O_BF16 or H2O_F32 */
+    int32_t kv_dtype;      /* H2O_BF16, H2O_F32, or H2O_I8 (bf16 inputs stored as int8 rows) */
     int32_t score_dtype;   /* H2O: H2O_F32 or H2O_F64 cumulative scores */
     float scale;           /* logit scale; 0 -> 1/sqrt(D) */
     int32_t selector;      /* H2O_SEL_H2O or H2O_SEL_RANDOM */
@@ -140,6 +147,18 @@ int h2o_step_compact(h2o_ctx *ctx, const float *q, const void *k_new, const void
  * H2O_EDEVICE. */
 int h2o_read_indices(h2o_ctx *ctx, int32_t *pos, int32_t *count, double *scores,
                      double *evicted_mass, size_t cap, void *stream);
+
+/* Read the stored K/V rows of the retained tokens back to the host, in the
+ * order h2o_read_indices gives positions (ascending); waits for `stream`.
+ *   k_rows, v_rows    host [B][Hkv][cap][row bytes]: rows as stored, in natural
+ *                     element order -- bf16 bits or fp32 (256 bytes), or int8
+ *                     codes (128 bytes); entries past the count are zeroed.
+ *   k_scale, v_scale  host [B][Hkv][cap] fp32 row scales (H2O_I8; ignored and
+ *                     may be NULL otherwise).
+ *   cap               entries per (b, h); must be >= every count.
+ * Errors: H2O_EINVAL, H2O_ESTATE (a compaction is pending), H2O_EDEVICE. */
+int h2o_read_kv(h2o_ctx *ctx, void *k_rows, void *v_rows, float *k_scale, float *v_scale, size_t cap,
+                void *stream);
 
 /* Slot capacity per (b, h) unit and the current step index s (host-side, no sync). */
 int h2o_info(const h2o_ctx *ctx, int32_t *slot_capacity, int32_t *steps_done,

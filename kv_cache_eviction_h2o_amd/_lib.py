@@ -16,14 +16,15 @@ from .build import LIB
 
 H2O_OK, H2O_EINVAL, H2O_ENOMEM, H2O_EDEVICE, H2O_ESTATE = 0, -1, -2, -3, -4
 SEL_H2O, SEL_RANDOM = 0, 1
-F32, BF16, F64 = 0, 1, 2
+F32, BF16, F64, I8 = 0, 1, 2, 3
 _STATUS = {H2O_EINVAL: "H2O_EINVAL", H2O_ENOMEM: "H2O_ENOMEM", H2O_EDEVICE: "H2O_EDEVICE",
            H2O_ESTATE: "H2O_ESTATE"}
 PAGE_SIZE = 16
 
 # Every symbol include/h2o.h declares.
 SYMBOLS = ("h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
-           "h2o_info", "h2o_destroy", "h2o_prefill_scores", "h2o_snapkv_select", "h2o_last_error")
+           "h2o_info", "h2o_read_kv", "h2o_destroy", "h2o_prefill_scores", "h2o_snapkv_select",
+           "h2o_last_error")
 
 
 class H2OConfig(C.Structure):
@@ -69,6 +70,8 @@ def load_library(path: str = LIB):
     lib.h2o_compact.argtypes = [vp, vp]
     lib.h2o_read_indices.restype = C.c_int
     lib.h2o_read_indices.argtypes = [vp, i32p, i32p, f64p, f64p, C.c_size_t, vp]
+    lib.h2o_read_kv.restype = C.c_int
+    lib.h2o_read_kv.argtypes = [vp, vp, vp, vp, vp, C.c_size_t, vp]
     lib.h2o_info.restype = C.c_int
     lib.h2o_info.argtypes = [vp, i32p, i32p, i32p]
     lib.h2o_destroy.restype = None
@@ -88,7 +91,7 @@ def make_config(*, batch, n_q_heads, n_kv_heads, head_dim, kv_dtype="bf16", scor
                 scale=0.0, selector="h2o", n_sink=4, budget_fixed=0, hh_fixed=0, budget_num=1,
                 budget_den=5, rand_k=0, rand_r=0, seed=0, page_size=0, max_pages=0,
                 max_len) -> H2OConfig:
-    dt = {"f32": F32, "bf16": BF16, "f64": F64}
+    dt = {"f32": F32, "bf16": BF16, "f64": F64, "i8": I8}
     return H2OConfig(batch, n_q_heads, n_kv_heads, head_dim, dt[kv_dtype], dt[score_dtype],
                      float(scale), SEL_RANDOM if selector == "random" else SEL_H2O, n_sink,
                      budget_fixed, hh_fixed, budget_num, budget_den, rand_k, rand_r,
@@ -131,7 +134,7 @@ def prefill_scores(cfg: H2OConfig, prompt_lens, prompt_q, prompt_k, out=None, st
     if lens.shape != (cfg.batch,):
         raise ValueError("prompt_lens must have one entry per sequence")
     total = int(lens.sum())
-    kv = torch.bfloat16 if cfg.kv_dtype == BF16 else torch.float32
+    kv = torch.bfloat16 if cfg.kv_dtype in (BF16, I8) else torch.float32
     H2OCache._check_tensor("prompt_q", prompt_q, (total, cfg.n_q_heads, cfg.head_dim), torch.float32)
     H2OCache._check_tensor("prompt_k", prompt_k, (total, cfg.n_kv_heads, cfg.head_dim), kv)
     if out is None:
@@ -154,7 +157,7 @@ def snapkv_select(cfg: H2OConfig, prompt_lens, prompt_q, prompt_k, window: int, 
     if lens.shape != (cfg.batch,):
         raise ValueError("prompt_lens must have one entry per sequence")
     total = int(lens.sum())
-    kv = torch.bfloat16 if cfg.kv_dtype == BF16 else torch.float32
+    kv = torch.bfloat16 if cfg.kv_dtype in (BF16, I8) else torch.float32
     H2OCache._check_tensor("prompt_q", prompt_q, (total, cfg.n_q_heads, cfg.head_dim), torch.float32)
     H2OCache._check_tensor("prompt_k", prompt_k, (total, cfg.n_kv_heads, cfg.head_dim), kv)
     G = cfg.n_q_heads // cfg.n_kv_heads
@@ -199,7 +202,7 @@ class H2OCache:
         self.lib = load_library()
         self.cfg = cfg
         self.B, self.Hq, self.Hkv, self.D = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-        self.kv_torch = torch.bfloat16 if cfg.kv_dtype == BF16 else torch.float32
+        self.kv_torch = torch.bfloat16 if cfg.kv_dtype in (BF16, I8) else torch.float32  # inputs
         lens = np.ascontiguousarray(prompt_lens, dtype=np.int32)
         if lens.shape != (self.B,):
             raise ValueError("prompt_lens must have one entry per sequence")
@@ -267,6 +270,25 @@ class H2OCache:
                                        _stream_handle(stream))
         _check(self.lib, self.ctx, rc)
         return pos, cnt, sc, em
+
+    def read_kv(self, cap=None, stream=None):
+        """Stored rows of the retained tokens, ascending positions: (K rows, V rows,
+        K scales, V scales); rows [B][Hkv][cap][D] as uint16 bf16 bits, float32, or
+        int8 codes; scales [B][Hkv][cap] float32 for int8 storage, else None."""
+        if cap is None:
+            cap = self.info()[0]
+        i8 = self.cfg.kv_dtype == I8
+        rb = 128 if i8 else 256
+        kr = np.empty((self.B, self.Hkv, cap, rb), dtype=np.uint8)
+        vr = np.empty_like(kr)
+        ks = np.empty((self.B, self.Hkv, cap), dtype=np.float32) if i8 else None
+        vs = np.empty_like(ks) if i8 else None
+        rc = self.lib.h2o_read_kv(self.ctx, kr.ctypes.data, vr.ctypes.data,
+                                  ks.ctypes.data if i8 else None, vs.ctypes.data if i8 else None, cap,
+                                  _stream_handle(stream))
+        _check(self.lib, self.ctx, rc)
+        view = np.int8 if i8 else (np.uint16 if self.cfg.kv_dtype == BF16 else np.float32)
+        return kr.view(view), vr.view(view), ks, vs
 
     def close(self):
         if getattr(self, "ctx", None) and self.ctx.value:

@@ -16,8 +16,12 @@ namespace h2o {
 namespace {
 
 // ---------------------------------------------------------------- row formats
+// A row is read by 16 lanes, EPL elements each from one Vec.  SCALED rows
+// stand for code * the row's scale (kept beside the rows).
 struct RowBf16 {  // 8 bf16 per 16-byte vector; widening is exact
     static constexpr int EPL = 8;
+    static constexpr bool SCALED = false;
+    using Vec = uint4;
     __device__ static inline void unpack(const uint4& r, float (&x)[8])
     {
         x[0] = __uint_as_float(r.x << 16);
@@ -33,6 +37,8 @@ struct RowBf16 {  // 8 bf16 per 16-byte vector; widening is exact
 
 struct RowF32 {  // 4 fp32 per 16-byte vector
     static constexpr int EPL = 4;
+    static constexpr bool SCALED = false;
+    using Vec = uint4;
     __device__ static inline void unpack(const uint4& r, float (&x)[4])
     {
         x[0] = __uint_as_float(r.x);
@@ -42,11 +48,35 @@ struct RowF32 {  // 4 fp32 per 16-byte vector
     }
 };
 
+struct RowI8 {  // 8 int8 codes per 8-byte vector; the row's scale multiplies them
+    static constexpr int EPL = 8;
+    static constexpr bool SCALED = true;
+    using Vec = uint2;
+    __device__ static inline void unpack(const uint2& r, float (&x)[8])
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = (float)(signed char)(r.x >> (8 * i));
+            x[4 + i] = (float)(signed char)(r.y >> (8 * i));
+        }
+    }
+};
+
 // -------------------------------------------------------------- reductions
 template <int CTRL>
 __device__ inline float dpp(float v)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum over each row of 16 lanes (same DPP stages as sum16).
+__device__ inline float max16(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return v;
 }
 
 // Sum over each row of 16 lanes, result in every lane of the row:
@@ -101,6 +131,13 @@ constexpr int kBufWord3 = 0x00020000;
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ inline uint2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    uint2 v;
+    __builtin_memcpy(&v, &x, 8);
+    return v;
 }
 __device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
@@ -454,14 +491,51 @@ struct KvRows {
         reinterpret_cast<uint4*>(kc)[kvec(si, c)] = k;
         reinterpret_cast<uint4*>(vc)[kvec(si, c)] = v;
     }
-    __device__ static inline void copy(void* kc, void* vc, size_t src, size_t dst, int c)
+    __device__ static inline void copy(const State& S, size_t src, size_t dst, int c)
     {
-        uint4* K = reinterpret_cast<uint4*>(kc);
-        uint4* V = reinterpret_cast<uint4*>(vc);
+        uint4* K = reinterpret_cast<uint4*>(S.kc);
+        uint4* V = reinterpret_cast<uint4*>(S.vc);
         K[kvec(dst, c)] = K[kvec(src, c)];
         V[kvec(dst, c)] = V[kvec(src, c)];
     }
 };
+
+// KvRows8: int8 rows of 128 codes, 16 chunks of 8 bytes; scales beside.
+struct KvRows8 {
+    __device__ static inline size_t kvec(size_t si, int c) { return si * kRowVecs + (size_t)c; }
+    __device__ static inline void copy(const State& S, size_t src, size_t dst, int c)
+    {
+        uint2* K = reinterpret_cast<uint2*>(S.kc);
+        uint2* V = reinterpret_cast<uint2*>(S.vc);
+        K[kvec(dst, c)] = K[kvec(src, c)];
+        V[kvec(dst, c)] = V[kvec(src, c)];
+        if (c == 0) {
+            S.kss[dst] = S.kss[src];
+            S.vss[dst] = S.vss[src];
+        }
+    }
+};
+
+// Int8 quantisation of one row of 128 held by the 16 lanes of a row group,
+// 8 values x[] per lane: scale = max |x| / 127, code = rint(x / scale) in
+// [-127, 127] (fp32 throughout; a zero row has scale 0 and codes 0).
+__device__ inline void quantize_row8(const float (&x)[8], uint2& codes, float& scale)
+{
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+    a = max16(a);
+    scale = a / 127.0f;
+    unsigned w[2] = {0u, 0u};
+    if (scale > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q = fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f);
+            w[i >> 2] |= ((unsigned)(int)q & 0xffu) << (8 * (i & 3));
+        }
+    }
+    codes = make_uint2(w[0], w[1]);
+}
 
 // KvTiles (bf16 rows of 128, contiguous slots, unit capacity a multiple of
 // 32): the operand orders of the 16x16x32 bf16 matrix instruction.
@@ -494,11 +568,11 @@ struct KvTiles {
 #pragma unroll
         for (int e = 0; e < 8; ++e) V[velem(si, 8 * c + e)] = (unsigned short)(w4[e >> 1] >> (16 * (e & 1)));
     }
-    __device__ static inline void copy(void* kc, void* vc, size_t src, size_t dst, int c)
+    __device__ static inline void copy(const State& S, size_t src, size_t dst, int c)
     {
-        uint4* K = reinterpret_cast<uint4*>(kc);
+        uint4* K = reinterpret_cast<uint4*>(S.kc);
         K[kvec(dst, c)] = K[kvec(src, c)];
-        unsigned short* V = reinterpret_cast<unsigned short*>(vc);
+        unsigned short* V = reinterpret_cast<unsigned short*>(S.vc);
 #pragma unroll
         for (int e = 0; e < 8; ++e) V[velem(dst, 8 * c + e)] = V[velem(src, 8 * c + e)];
     }
@@ -526,7 +600,7 @@ __device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n
     const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;
     for (int i = grp; i < nh; i += NT / 16) {
         const size_t src = sidx(ll[i]), dst = sidx(hl[i]);
-        KV::copy(s.kc, s.vc, src, dst, sub);
+        KV::copy(s, src, dst, sub);
         if (sub == 0) {
             if (has_scores) sc[dst] = sc[src];
             ps[dst] = ps[src];
@@ -558,22 +632,23 @@ struct TailSmem {
 //   bulk (e > 1, Random Attention events): radix select of the e smallest
 //        keys, victims marked, holes filled when fused.
 // pf_s / pf_p: score and position of slots tid + k * NT (k < PF), fetched
-// early by the caller; knr / vnr: chunk tid of the new token's K / V row in
-// threads tid < 16; emass0: the unit's evicted mass before the step.
+// early by the caller; write_new(si): every thread calls it to store the new
+// token's row at slot index si (the writer picks its threads); emass0: the
+// unit's evicted mass before the step.
 // Definitions: "Attention Sinks and KV cache eviction" sec. 4.2 (cumulative
 // score; sinks, heavy hitters and recent window), "H2O: Heavy-Hitter Oracle"
 // (greedy eviction under budget K), "Random Attention" (method).
-template <int NT, int G, int PF, typename ST, bool PAGED, typename KV>
+template <int NT, int G, int PF, typename ST, bool PAGED, typename KV, typename WriteNew>
 __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, TailSmem<ST, NT / 64>& sm,
                                  int unit, int b, int h, int P, int t, int n, int e, bool inplace_new,
                                  const float* logit, int lstride, const float (&Mg)[G],
                                  const float (&invLg)[G], const ST (&pf_s)[PF], const int (&pf_p)[PF],
-                                 uint4 knr, uint4 vnr, double emass0)
+                                 WriteNew write_new, double emass0)
 {
     constexpr int NW = NT / 64;
     const Geometry& gm = a.g;
     const State& S = a.s;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, sub = tid & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n_att = n + 1;
     const bool h2o = a.sc.selector == 0;
     ST* scp = reinterpret_cast<ST*>(S.sc);
@@ -655,7 +730,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             const bool owner = (vj - tid) % NT == 0;
             if (a.fused) {
                 if (vj != n) {
-                    if (tid < 16) KV::store(S.kc, S.vc, sidx(vj), sub, knr, vnr);
+                    write_new(sidx(vj));
                     if (owner) {
                         scp[sidx(vj)] = sm.new_score;
                         psp[sidx(vj)] = t;

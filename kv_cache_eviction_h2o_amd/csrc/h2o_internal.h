@@ -11,6 +11,7 @@ namespace h2o {
 constexpr int kPageShift = 4;           // 16-token KV pages
 constexpr int kPageSize = 1 << kPageShift;
 constexpr int kRowBytes = 256;          // one K or V row: 128 x bf16 or 64 x fp32
+constexpr int kRowBytesI8 = 128;        // one int8 row of 128 (plus its scale)
 constexpr int kRowVecs = kRowBytes / 16;  // 16-byte vectors per row = lanes per row
 constexpr int kMaxArgBatch = 128;       // per-sequence step parameters travel in the kernel args
                                         // (larger batches read them from device memory)
@@ -24,7 +25,8 @@ struct Geometry {
     int cap;        // slots per (b, h) unit (contiguous layout stride; scratch sizing)
     int paged;      // 1 = 16-token pages through the block table
     int maxp;       // paged: block-table row length (pages per sequence)
-    int kv_bf16;    // 1 = bf16 rows, 0 = fp32 rows
+    int kv_bf16;    // 1 = bf16 rows (inputs and storage), 0 = fp32 rows
+    int kv_i8;      // 1 = bf16 inputs stored as int8 rows of 128 with one fp32 scale per row
     int score_f64;  // 1 = fp64 cumulative scores, 0 = fp32
     int kv_tiles;   // 1 = K/V in matrix-instruction operand order (bf16, head_dim 128,
                     //     contiguous, cap a multiple of 32, GQA group of 4 or 8)
@@ -33,6 +35,8 @@ struct Geometry {
 struct State {  // device pointers owned by the context
     void* kc;          // K rows
     void* vc;          // V rows
+    float* kss;        // int8 storage: scale of each K row (else null)
+    float* vss;        // int8 storage: scale of each V row (else null)
     void* sc;          // cumulative scores (H2O)
     int32_t* ps;       // position of each slot; -1 marks a victim awaiting compaction
     int32_t* cnt;      // [B*Hkv] slots in use
@@ -149,6 +153,17 @@ struct SnapArgs {
     int64_t seq_off[kMaxArgBatch];
 };
 
+// Stored rows of the retained slots, in slot order (h2o_read_kv).
+struct RowGatherArgs {
+    Geometry g;
+    State s;
+    int capo;              // entries per unit in the staging buffers
+    unsigned char* ok;     // [B*Hkv][capo][row bytes] K rows as stored (natural element order)
+    unsigned char* ov;     // [B*Hkv][capo][row bytes] V rows
+    float* oks;            // [B*Hkv][capo] row scales (int8 storage; else null)
+    float* ovs;
+};
+
 // Launchers (h2o_kernels.hip unless noted).  Each returns the launch's hipError_t.
 hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st);
 hipError_t launch_step_mfma(const StepArgs& a, int max_n_att, hipStream_t st);  // h2o_mfma.hip
@@ -157,5 +172,6 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st);  // h2o_
 hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+hipError_t launch_gather_rows(const RowGatherArgs& a, hipStream_t st);
 
 }  // namespace h2o

@@ -117,11 +117,43 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     }
     const uint4 knr = reinterpret_cast<const uint4*>(a.kn)[(size_t)unit * kRowVecs + sub];
     const uint4 vnr = reinterpret_cast<const uint4*>(a.vn)[(size_t)unit * kRowVecs + sub];
-    const uint4* kc = reinterpret_cast<const uint4*>(S.kc);
-    const uint4* vc = reinterpret_cast<const uint4*>(S.vc);
+    using Vec = typename Row::Vec;
+    using KVL = std::conditional_t<Row::SCALED, KvRows8, KvRows>;  // stored row layout
+    constexpr unsigned RB = Row::SCALED ? kRowBytesI8 : kRowBytes;  // stored row bytes
+    constexpr unsigned VBY = sizeof(Vec);                           // bytes of a row per lane
+    const Vec* kc = reinterpret_cast<const Vec*>(S.kc);
+    const Vec* vc = reinterpret_cast<const Vec*>(S.vc);
     // evicted mass of the unit, read now so its update at the end is no round trip
     const double emass0 = S.emass[unit];
     __builtin_amdgcn_sched_barrier(0);  // keep q and the new token ahead of the K/V stream
+    // the new token's row as stored; int8 rows are quantised here, and the
+    // cache then holds -- and this step attends over -- exactly that row
+    Vec knv, vnv;
+    float kns = 1.f, vns = 1.f;
+    if constexpr (Row::SCALED) {
+        float xk[8], xv[8];
+        RowBf16::unpack(knr, xk);
+        RowBf16::unpack(vnr, xv);
+        quantize_row8(xk, knv, kns);
+        quantize_row8(xv, vnv, vns);
+    } else {
+        knv = knr;
+        vnv = vnr;
+    }
+    auto write_new = [&](size_t si) {  // the new token's row into slot index si
+        if (tid < 16) {
+            if constexpr (Row::SCALED) {
+                reinterpret_cast<uint2*>(S.kc)[si * kRowVecs + sub] = knv;
+                reinterpret_cast<uint2*>(S.vc)[si * kRowVecs + sub] = vnv;
+                if (sub == 0) {
+                    S.kss[si] = kns;
+                    S.vss[si] = vns;
+                }
+            } else {
+                KvRows::store(S.kc, S.vc, si, sub, knr, vnr);
+            }
+        }
+    };
 
     // Rows j >= n are masked out by their logit; the new token (j == n) is
     // folded in after the loop.  Every load is unconditional (a conditional
@@ -129,33 +161,58 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     // serialise the pipeline).  Contiguous layout: raw buffer loads over the
     // unit's n rows, so rows past them read as zero without a memory access.
     // Paged layout: rows past n read slot 0 (a cache hit).
-    __amdgpu_buffer_rsrc_t rk, rv;
+    __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;
     if constexpr (!PAGED) {
-        const size_t ub = sidx.base * kRowBytes;
-        rk = make_rsrc(reinterpret_cast<const char*>(S.kc) + ub, (unsigned)n * kRowBytes);
-        rv = make_rsrc(reinterpret_cast<const char*>(S.vc) + ub, (unsigned)n * kRowBytes);
+        const size_t ub = sidx.base * RB;
+        rk = make_rsrc(reinterpret_cast<const char*>(S.kc) + ub, (unsigned)n * RB);
+        rv = make_rsrc(reinterpret_cast<const char*>(S.vc) + ub, (unsigned)n * RB);
+        if constexpr (Row::SCALED) {
+            rks = make_rsrc(S.kss + sidx.base, (unsigned)n * 4u);
+            rvs = make_rsrc(S.vss + sidx.base, (unsigned)n * 4u);
+        }
     }
-    auto load_batch = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U]) {
+    auto ld = [](__amdgpu_buffer_rsrc_t r, unsigned off) -> Vec {
+        if constexpr (sizeof(Vec) == 16) return buf_load16(r, off);
+        else return buf_load8(r, off);
+    };
+    // rows (and, for int8 rows, their scales) of one batch
+    auto load_batch = [&](int base, Vec (&kr)[U], Vec (&vr)[U], float (&ks)[U], float (&vs)[U]) {
         if constexpr (!PAGED) {
-            const unsigned off0 = (unsigned)(base + grp) * kRowBytes + (unsigned)sub * 16u;
+            const unsigned off0 = (unsigned)(base + grp) * RB + (unsigned)sub * VBY;
 #pragma unroll
-            for (int u = 0; u < U; ++u) kr[u] = buf_load16(rk, off0 + (unsigned)(u * NGRP * kRowBytes));
+            for (int u = 0; u < U; ++u) kr[u] = ld(rk, off0 + (unsigned)(u * NGRP) * RB);
 #pragma unroll
-            for (int u = 0; u < U; ++u) vr[u] = buf_load16(rv, off0 + (unsigned)(u * NGRP * kRowBytes));
+            for (int u = 0; u < U; ++u) vr[u] = ld(rv, off0 + (unsigned)(u * NGRP) * RB);
+            if constexpr (Row::SCALED) {
+                const unsigned so = (unsigned)(base + grp) * 4u;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (int)(so + u * NGRP * 4), 0, 0));
+                    vs[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (int)(so + u * NGRP * 4), 0, 0));
+                }
+            }
         } else {
             size_t r[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + grp + NGRP * u;
-                r[u] = sidx(j < n ? j : 0) * kRowVecs + sub;
-                kr[u] = kc[r[u]];
+                r[u] = sidx(j < n ? j : 0);
+                kr[u] = kc[r[u] * kRowVecs + sub];
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) vr[u] = vc[r[u]];
+            for (int u = 0; u < U; ++u) vr[u] = vc[r[u] * kRowVecs + sub];
+            if constexpr (Row::SCALED) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    ks[u] = S.kss[r[u]];
+                    vs[u] = S.vss[r[u]];
+                }
+            }
         }
     };
-    uint4 ka[U], va[U], kb[U], vb[U];
-    load_batch(0, ka, va);
+    Vec ka[U], va[U], kb[U], vb[U];
+    float ksa[U], vsa[U], ksb[U], vsb[U];
+    load_batch(0, ka, va, ksa, vsa);
     __builtin_amdgcn_sched_barrier(0);
 
     // scores and positions of this thread's first PF phase-2 slots
@@ -194,8 +251,8 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     }
 
     // logits of nr rows (K), running max, then P.V (V); rows with !valid[u]
-    // take no weight
-    auto accumulate = [&](float (&s)[U][G], const uint4 (&vr)[U], int nr) {
+    // take no weight; vs: the V rows' scales (int8 rows)
+    auto accumulate = [&](float (&s)[U][G], const Vec (&vr)[U], const float (&vs)[U], int nr) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float mx = m[g];
@@ -217,12 +274,13 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
             for (int g = 0; g < G; ++g) {
                 const float p = fast_exp2(s[u][g] - m[g]);  // 2^-inf = 0 for masked rows
                 l[g] += p;
+                const float pv = Row::SCALED ? p * vs[u] : p;
 #pragma unroll
-                for (int i = 0; i < EPL; ++i) o[g][i] = fmaf(p, vx[i], o[g][i]);
+                for (int i = 0; i < EPL; ++i) o[g][i] = fmaf(pv, vx[i], o[g][i]);
             }
         }
     };
-    auto logits = [&](const uint4 (&kr)[U], float (&s)[U][G]) {
+    auto logits = [&](const Vec (&kr)[U], const float (&ks)[U], float (&s)[U][G]) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float acc[U];
@@ -236,12 +294,13 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
             }
             sum16_n<U>(acc);
 #pragma unroll
-            for (int u = 0; u < U; ++u) s[u][g] = acc[u];
+            for (int u = 0; u < U; ++u) s[u][g] = Row::SCALED ? acc[u] * ks[u] : acc[u];
         }
     };
-    auto process = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+    auto process = [&](int base, const Vec (&kr)[U], const Vec (&vr)[U], const float (&ks)[U],
+                       const float (&vs)[U]) {
         float s[U][G];
-        logits(kr, s);
+        logits(kr, ks, s);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + grp + NGRP * u;
@@ -256,25 +315,28 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                 for (int g = 0; g < G; ++g) s[u][g] = -INFINITY;
             }
         }
-        accumulate(s, vr, U);
+        accumulate(s, vr, vs, U);
     };
     // the new token (position t, slot n) is lane group 0's first row; this
     // runs while the first K/V batch is still in flight
     if (grp == 0) {
-        uint4 kn1[U], vn1[U];
+        Vec kn1[U], vn1[U];
+        float ks1[U], vs1[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            kn1[u] = knr;
-            vn1[u] = vnr;
+            kn1[u] = knv;
+            vn1[u] = vnv;
+            ks1[u] = kns;
+            vs1[u] = vns;
         }
         float s1[U][G];
-        logits(kn1, s1);
+        logits(kn1, ks1, s1);
         if (h2o) {
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 if (sub == g) logit[(size_t)g * lstride + n] = s1[0][g];
         }
-        accumulate(s1, vn1, 1);
+        accumulate(s1, vn1, vs1, 1);
     }
     // Batch b+1 is requested before batch b is consumed.  Two register sets
     // alternate (no copies, which would wait for the loads in flight) and the
@@ -283,20 +345,20 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     const int nbatch = (n_att + BR - 1) / BR;
     int bi = 0;
     for (; bi + 2 < nbatch; bi += 2) {
-        load_batch((bi + 1) * BR, kb, vb);
-        process(bi * BR, ka, va);
-        load_batch((bi + 2) * BR, ka, va);
-        process((bi + 1) * BR, kb, vb);
+        load_batch((bi + 1) * BR, kb, vb, ksb, vsb);
+        process(bi * BR, ka, va, ksa, vsa);
+        load_batch((bi + 2) * BR, ka, va, ksa, vsa);
+        process((bi + 1) * BR, kb, vb, ksb, vsb);
     }
     if (bi + 1 < nbatch) {
-        load_batch((bi + 1) * BR, kb, vb);
-        process(bi * BR, ka, va);
-        process((bi + 1) * BR, kb, vb);
+        load_batch((bi + 1) * BR, kb, vb, ksb, vsb);
+        process(bi * BR, ka, va, ksa, vsa);
+        process((bi + 1) * BR, kb, vb, ksb, vsb);
     } else {
-        process(bi * BR, ka, va);
+        process(bi * BR, ka, va, ksa, vsa);
     }
     // the new token's row goes to slot n unless it fills a victim's hole later
-    if (!inplace_new && tid < 16) KvRows::store(S.kc, S.vc, sidx(n), sub, knr, vnr);
+    if (!inplace_new) write_new(sidx(n));
 
     // merge the four lane groups (rows) of each wave with permlane swaps,
     // then the waves through LDS: one barrier, after which every thread
@@ -363,8 +425,8 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                                 acc[4 * i + 2] * invLg[g], acc[4 * i + 3] * invLg[g]);
     }
 
-    step_tail<NT, G, PF, ST, PAGED, KvRows>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit,
-                                            lstride, Mg, invLg, pf_s, pf_p, knr, vnr, emass0);
+    step_tail<NT, G, PF, ST, PAGED, KVL>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit, lstride,
+                                         Mg, invLg, pf_s, pf_p, write_new, emass0);
 }
 
 // ---------------------------------------------------------- compact kernel
@@ -392,7 +454,7 @@ __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a
         if (v != last && v >= 0) {
             const int sub = threadIdx.x & 15;
             const size_t src = sidx(last), dst = sidx(v);
-            if (threadIdx.x < 16) KV::copy(S.kc, S.vc, src, dst, sub);
+            if (threadIdx.x < 16) KV::copy(S, src, dst, sub);
             if (threadIdx.x == 0) {
                 if (has_scores) ((ST*)S.sc)[dst] = ((ST*)S.sc)[src];
                 S.ps[dst] = S.ps[src];
@@ -431,8 +493,26 @@ __global__ void __launch_bounds__(256) load_kernel(const LoadArgs a)
     sidx.Hkv = gm.Hkv;
     const size_t src = ((size_t)(S.poff[b] + tok) * gm.Hkv + h) * kRowVecs + c;
     const size_t si = sidx(tok);
-    KV::store(S.kc, S.vc, si, c, reinterpret_cast<const uint4*>(a.pk)[src],
-              reinterpret_cast<const uint4*>(a.pv)[src]);
+    const uint4 kin = reinterpret_cast<const uint4*>(a.pk)[src];
+    const uint4 vin = reinterpret_cast<const uint4*>(a.pv)[src];
+    if constexpr (std::is_same<KV, KvRows8>::value) {
+        // the 16 threads of a row are the 16 lanes of a DPP row (idx % 16 == c)
+        float xk[8], xv[8];
+        RowBf16::unpack(kin, xk);
+        RowBf16::unpack(vin, xv);
+        uint2 kq, vq;
+        float ks, vs;
+        quantize_row8(xk, kq, ks);
+        quantize_row8(xv, vq, vs);
+        reinterpret_cast<uint2*>(S.kc)[si * kRowVecs + c] = kq;
+        reinterpret_cast<uint2*>(S.vc)[si * kRowVecs + c] = vq;
+        if (c == 0) {
+            S.kss[si] = ks;
+            S.vss[si] = vs;
+        }
+    } else {
+        KV::store(S.kc, S.vc, si, c, kin, vin);
+    }
     if (c == 0) {
         if (S.sc)
             ((ST*)S.sc)[si] = a.init_scores
@@ -475,6 +555,49 @@ __global__ void __launch_bounds__(256) gather_kernel(const GatherArgs a)
     }
 }
 
+// ------------------------------------------------------------ row gather
+// Every retained slot's stored K and V rows to staging, slot order, natural
+// element order whatever the layout (16 chunks per row).
+template <typename KV, bool PAGED>
+__global__ void __launch_bounds__(256) gather_rows_kernel(const RowGatherArgs a)
+{
+    const Geometry& gm = a.g;
+    const State& S = a.s;
+    const int unit = blockIdx.x;
+    const int b = unit / gm.Hkv, h = unit - b * gm.Hkv;
+    SlotMap<PAGED> sidx;
+    sidx.base = (size_t)unit * gm.cap;
+    sidx.bt = S.bt + (size_t)b * gm.maxp;
+    sidx.h = h;
+    sidx.Hkv = gm.Hkv;
+    const int n = min(S.cnt[unit], a.capo);
+    for (int idx = threadIdx.x; idx < n * kRowVecs; idx += 256) {
+        const int j = idx / kRowVecs, c = idx - j * kRowVecs;
+        const size_t si = sidx(j);
+        const size_t o = (size_t)unit * a.capo + j;
+        if constexpr (std::is_same<KV, KvRows8>::value) {
+            reinterpret_cast<uint2*>(a.ok)[o * kRowVecs + c] = reinterpret_cast<const uint2*>(S.kc)[si * kRowVecs + c];
+            reinterpret_cast<uint2*>(a.ov)[o * kRowVecs + c] = reinterpret_cast<const uint2*>(S.vc)[si * kRowVecs + c];
+            if (c == 0) {
+                a.oks[o] = S.kss[si];
+                a.ovs[o] = S.vss[si];
+            }
+        } else if constexpr (std::is_same<KV, KvTiles>::value) {
+            reinterpret_cast<uint4*>(a.ok)[o * kRowVecs + c] = reinterpret_cast<const uint4*>(S.kc)[KvTiles::kvec(si, c)];
+            const unsigned short* V = reinterpret_cast<const unsigned short*>(S.vc);
+            unsigned w4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w4[e] = (unsigned)V[KvTiles::velem(si, 8 * c + 2 * e)] |
+                        ((unsigned)V[KvTiles::velem(si, 8 * c + 2 * e + 1)] << 16);
+            reinterpret_cast<uint4*>(a.ov)[o * kRowVecs + c] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        } else {
+            reinterpret_cast<uint4*>(a.ok)[o * kRowVecs + c] = reinterpret_cast<const uint4*>(S.kc)[si * kRowVecs + c];
+            reinterpret_cast<uint4*>(a.ov)[o * kRowVecs + c] = reinterpret_cast<const uint4*>(S.vc)[si * kRowVecs + c];
+        }
+    }
+}
+
 // --------------------------------------------------------------- dispatch
 template <typename Row, int G, typename ST, bool PAGED, bool LLDS>
 hipError_t launch_step_t(const StepArgs& a, size_t dyn, hipStream_t st)
@@ -495,7 +618,7 @@ template <typename Row, int G, typename ST>
 hipError_t dispatch_pl(const StepArgs& a, bool llds, size_t dyn, hipStream_t st)
 {
     if (a.g.paged) {
-        if constexpr (std::is_same<Row, RowBf16>::value) {  // pages hold bf16 rows only
+        if constexpr (!std::is_same<Row, RowF32>::value) {  // pages hold bf16 or int8 rows of 128
             return llds ? launch_step_t<Row, G, ST, true, true>(a, dyn, st)
                         : launch_step_t<Row, G, ST, true, false>(a, dyn, st);
         }
@@ -528,6 +651,10 @@ hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st)
     if (a.g.paged) dyn += (size_t)a.npg_lds * 4;
     dyn = (dyn + 15) & ~(size_t)15;
     if (!llds && a.s.lscr == nullptr) return hipErrorInvalidValue;
+    if (a.g.kv_i8) {
+        return a.g.score_f64 ? dispatch_g<RowI8, double>(a, llds, dyn, st)
+                             : dispatch_g<RowI8, float>(a, llds, dyn, st);
+    }
     if (a.g.kv_bf16) {
         return a.g.score_f64 ? dispatch_g<RowBf16, double>(a, llds, dyn, st)
                              : dispatch_g<RowBf16, float>(a, llds, dyn, st);
@@ -539,7 +666,15 @@ hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st)
 hipError_t launch_compact(const CompactArgs& a, int /*max_slots*/, hipStream_t st)
 {
     const dim3 grid(a.g.B * a.g.Hkv), block(kCompactNT);
-    if (a.g.paged) {
+    if (a.g.kv_i8) {
+        if (a.g.paged) {
+            if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, true, KvRows8>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((compact_kernel<float, true, KvRows8>), grid, block, 0, st, a);
+        } else {
+            if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, false, KvRows8>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((compact_kernel<float, false, KvRows8>), grid, block, 0, st, a);
+        }
+    } else if (a.g.paged) {
         if (a.g.score_f64) hipLaunchKernelGGL((compact_kernel<double, true, KvRows>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((compact_kernel<float, true, KvRows>), grid, block, 0, st, a);
     } else if (a.g.kv_tiles) {
@@ -556,7 +691,15 @@ hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st)
 {
     const long long per_seq = (long long)max_prompt * a.g.Hkv * kRowVecs;
     const dim3 grid((unsigned)((per_seq + 255) / 256), a.g.B), block(256);
-    if (a.g.paged) {
+    if (a.g.kv_i8) {
+        if (a.g.paged) {
+            if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, true, KvRows8>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((load_kernel<float, true, KvRows8>), grid, block, 0, st, a);
+        } else {
+            if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, false, KvRows8>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((load_kernel<float, false, KvRows8>), grid, block, 0, st, a);
+        }
+    } else if (a.g.paged) {
         if (a.g.score_f64) hipLaunchKernelGGL((load_kernel<double, true, KvRows>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((load_kernel<float, true, KvRows>), grid, block, 0, st, a);
     } else if (a.g.kv_tiles) {
@@ -582,5 +725,20 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t st)
     return hipGetLastError();
 }
 
-}  // namespace h2o
+hipError_t launch_gather_rows(const RowGatherArgs& a, hipStream_t st)
+{
+    const dim3 grid(a.g.B * a.g.Hkv), block(256);
+    if (a.g.kv_i8) {
+        if (a.g.paged) hipLaunchKernelGGL((gather_rows_kernel<KvRows8, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((gather_rows_kernel<KvRows8, false>), grid, block, 0, st, a);
+    } else if (a.g.kv_tiles) {
+        hipLaunchKernelGGL((gather_rows_kernel<KvTiles, false>), grid, block, 0, st, a);
+    } else if (a.g.paged) {
+        hipLaunchKernelGGL((gather_rows_kernel<KvRows, true>), grid, block, 0, st, a);
+    } else {
+        hipLaunchKernelGGL((gather_rows_kernel<KvRows, false>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
 
+}  // namespace h2o

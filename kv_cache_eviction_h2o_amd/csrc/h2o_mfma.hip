@@ -349,10 +349,13 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
         for (int k = 0; k < EPT; ++k) op[k] = acc[k] * il;
     }
     // the new token's rows go to slot n unless they fill a victim's hole later
-    if (!inplace_new && tid < 16) KvTiles::store(S.kc, S.vc, sidx(n), tid, knr, vnr);
+    auto write_new = [&](size_t si) {  // the new token's row into slot index si
+        if (tid < 16) KvTiles::store(S.kc, S.vc, si, tid, knr, vnr);
+    };
+    if (!inplace_new) write_new(sidx(n));
 
     step_tail<NT, G, PF, ST, false, KvTiles>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit,
-                                             lstride, Mg, invLg, pf_s, pf_p, knr, vnr, emass0);
+                                             lstride, Mg, invLg, pf_s, pf_p, write_new, emass0);
 }
 
 template <int G, typename ST, bool LLDS>

@@ -115,9 +115,9 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     if (c->n_q_heads % c->n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
     const int G = c->n_q_heads / c->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8) return bad("query group size must be 1, 2, 4 or 8");
-    const bool bf = c->kv_dtype == H2O_BF16, f32 = c->kv_dtype == H2O_F32;
-    if (!(bf && c->head_dim == 128) && !(f32 && c->head_dim == 64))
-        return bad("supported (kv_dtype, head_dim): (bf16, 128) or (f32, 64)");
+    const bool bf = c->kv_dtype == H2O_BF16, f32 = c->kv_dtype == H2O_F32, i8 = c->kv_dtype == H2O_I8;
+    if (!((bf || i8) && c->head_dim == 128) && !(f32 && c->head_dim == 64))
+        return bad("supported (kv_dtype, head_dim): (bf16, 128), (i8, 128) or (f32, 64)");
     if (!(c->scale >= 0.f) || !std::isfinite(c->scale)) return bad("scale must be finite and >= 0");
     if (c->max_len < 2) return bad("max_len must be >= 2");
     int maxP = 0;
@@ -150,7 +150,7 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     }
     if (c->page_size != 0 && c->page_size != kPageSize) return bad("page_size must be 0 or 16");
     if (c->page_size) {
-        if (!bf) return bad("the paged layout needs bf16 rows");
+        if (!bf && !i8) return bad("the paged layout needs bf16 or i8 rows");
         if (c->batch > kMaxArgBatch) return bad("paged layout supports at most 128 sequences");
         if (c->max_pages < 1) return bad("paged layout needs max_pages >= 1");
     }
@@ -428,6 +428,7 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
     g.paged = cfg->page_size ? 1 : 0;
     g.maxp = g.paged ? (g.cap + kPageSize - 1) / kPageSize : 0;
     g.kv_bf16 = cfg->kv_dtype == H2O_BF16;
+    g.kv_i8 = cfg->kv_dtype == H2O_I8;
     g.score_f64 = cfg->selector == H2O_SEL_H2O && cfg->score_dtype == H2O_F64;
     // GQA groups of 4 or 8 over bf16 rows of 128 run on the matrix cores, with
     // K / V stored in operand order in whole 32-slot tiles
@@ -470,8 +471,11 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
     State& s = c->s;
     int32_t* t0 = nullptr;
     int64_t* poff = nullptr;
-    if ((rc = dalloc(c, &s.kc, slots_total * kRowBytes, "alloc K cache")) ||
-        (rc = dalloc(c, &s.vc, slots_total * kRowBytes, "alloc V cache")) ||
+    const size_t row_bytes = g.kv_i8 ? kRowBytesI8 : kRowBytes;
+    if ((rc = dalloc(c, &s.kc, slots_total * row_bytes, "alloc K cache")) ||
+        (rc = dalloc(c, &s.vc, slots_total * row_bytes, "alloc V cache")) ||
+        (g.kv_i8 && (rc = dalloc(c, &s.kss, slots_total * 4, "alloc K row scales"))) ||
+        (g.kv_i8 && (rc = dalloc(c, &s.vss, slots_total * 4, "alloc V row scales"))) ||
         (cfg->selector == H2O_SEL_H2O && (rc = dalloc(c, &s.sc, slots_total * sw, "alloc scores"))) ||
         (rc = dalloc(c, &s.ps, slots_total * 4, "alloc positions")) ||
         (rc = dalloc(c, &s.cnt, units * 4, "alloc counts")) ||
@@ -632,6 +636,103 @@ int h2o_read_indices(h2o_ctx* c, int32_t* pos, int32_t* count, double* scores, d
         if (evicted_mass) evicted_mass[u] = hem[u];
     }
     for (int b = 0; b < B; ++b) count[b] = c->count[b];
+    return H2O_OK;
+}
+
+int h2o_read_kv(h2o_ctx* c, void* k_rows, void* v_rows, float* k_scale, float* v_scale, size_t cap,
+                void* stream)
+{
+    if (!c) return H2O_EINVAL;
+    if (c->pending) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
+    if (!k_rows || !v_rows) return fail(c, H2O_EINVAL, "null k_rows or v_rows");
+    if (c->g.kv_i8 && (!k_scale || !v_scale)) return fail(c, H2O_EINVAL, "i8 storage needs k_scale and v_scale");
+    const int B = c->g.B, Hkv = c->g.Hkv;
+    int maxc = 0;
+    for (int b = 0; b < B; ++b) maxc = std::max(maxc, c->count[b]);
+    if (cap < (size_t)maxc || cap == 0 || cap > (size_t)(1 << 30))
+        return fail(c, H2O_EINVAL, "cap is smaller than a retained count");
+    DeviceGuard dg(c->device);
+    const size_t units = (size_t)B * Hkv;
+    const size_t rb = c->g.kv_i8 ? kRowBytesI8 : kRowBytes;
+    std::vector<void*> tmp;
+    auto dfree = [&]() {
+        for (void* p : tmp) (void)hipFree(p);
+    };
+    auto dmal = [&](void** p, size_t bytes) {
+        hipError_t e = hipMalloc(p, bytes);
+        if (e == hipSuccess) tmp.push_back(*p);
+        return e;
+    };
+    int32_t* dpos = nullptr;
+    double* dsc = nullptr;
+    unsigned char *dk = nullptr, *dv = nullptr;
+    float *dks = nullptr, *dvs = nullptr;
+    hipError_t e;
+    if ((e = dmal((void**)&dpos, units * cap * 4)) != hipSuccess || (e = dmal((void**)&dsc, units * cap * 8)) != hipSuccess ||
+        (e = dmal((void**)&dk, units * cap * rb)) != hipSuccess || (e = dmal((void**)&dv, units * cap * rb)) != hipSuccess ||
+        (c->g.kv_i8 && ((e = dmal((void**)&dks, units * cap * 4)) != hipSuccess ||
+                        (e = dmal((void**)&dvs, units * cap * 4)) != hipSuccess))) {
+        dfree();
+        return hip_fail(c, e, "read staging");
+    }
+    GatherArgs ga{};
+    ga.g = c->g;
+    ga.s = c->s;
+    ga.selector = c->sc.selector;
+    ga.capo = (int)cap;
+    ga.opos = dpos;
+    ga.osc = dsc;
+    RowGatherArgs ra{};
+    ra.g = c->g;
+    ra.s = c->s;
+    ra.capo = (int)cap;
+    ra.ok = dk;
+    ra.ov = dv;
+    ra.oks = dks;
+    ra.ovs = dvs;
+    std::vector<int32_t> hpos(units * cap);
+    std::vector<unsigned char> hk(units * cap * rb), hv(units * cap * rb);
+    std::vector<float> hks(c->g.kv_i8 ? units * cap : 0), hvs(c->g.kv_i8 ? units * cap : 0);
+    hipStream_t st = (hipStream_t)stream;
+    if ((e = launch_gather(ga, st)) != hipSuccess || (e = launch_gather_rows(ra, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(hpos.data(), dpos, units * cap * 4, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(hk.data(), dk, units * cap * rb, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(hv.data(), dv, units * cap * rb, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (c->g.kv_i8 &&
+         ((e = hipMemcpyAsync(hks.data(), dks, units * cap * 4, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+          (e = hipMemcpyAsync(hvs.data(), dvs, units * cap * 4, hipMemcpyDeviceToHost, st)) != hipSuccess)) ||
+        (e = hipStreamSynchronize(st)) != hipSuccess) {
+        dfree();
+        return hip_fail(c, e, "read back");
+    }
+    dfree();
+    unsigned char* K = (unsigned char*)k_rows;
+    unsigned char* V = (unsigned char*)v_rows;
+    std::vector<int> order;
+    for (size_t u = 0; u < units; ++u) {
+        const int n = c->count[u / Hkv];
+        order.resize(n);
+        for (int i = 0; i < n; ++i) order[i] = i;
+        const int32_t* Pp = &hpos[u * cap];
+        std::sort(order.begin(), order.end(), [&](int x, int y) { return Pp[x] < Pp[y]; });
+        for (size_t i = 0; i < cap; ++i) {
+            unsigned char* kd = K + (u * cap + i) * rb;
+            unsigned char* vd = V + (u * cap + i) * rb;
+            if ((int)i < n) {
+                const size_t from = u * cap + order[i];
+                std::memcpy(kd, &hk[from * rb], rb);
+                std::memcpy(vd, &hv[from * rb], rb);
+                if (c->g.kv_i8) {
+                    k_scale[u * cap + i] = hks[from];
+                    v_scale[u * cap + i] = hvs[from];
+                }
+            } else {
+                std::memset(kd, 0, rb);
+                std::memset(vd, 0, rb);
+                if (c->g.kv_i8) k_scale[u * cap + i] = v_scale[u * cap + i] = 0.f;
+            }
+        }
+    }
     return H2O_OK;
 }
 

@@ -27,16 +27,21 @@ def score_state_bytes(n_tokens: int, batch: int = 1, score_bytes: int = 4) -> in
     return n_tokens * batch * score_bytes
 
 
-def unit_step_bytes(n_att, *, head_dim: int, kv_elem: int, group: int, score_bytes: int):
-    """Algorithmic bytes of one unit-step (n_att may be an array)."""
-    row = head_dim * kv_elem
+def unit_step_bytes(n_att, *, head_dim: int, kv_elem: int, group: int, score_bytes: int,
+                    int8_rows: bool = False):
+    """Algorithmic bytes of one unit-step (n_att may be an array): the retained K and V
+    rows read once, the new token's rows read from the input and written to the cache,
+    each score read and written, q read and the output written.  int8_rows: stored rows
+    are head_dim int8 codes plus a 4-byte scale; the inputs stay head_dim * kv_elem."""
+    row_in = head_dim * kv_elem
+    row = head_dim + 4 if int8_rows else row_in
     n = np.asarray(n_att, dtype=np.int64)
-    return (n - 1) * 2 * row + 4 * row + n * 2 * score_bytes + 2 * group * head_dim * 4
+    return (n - 1) * 2 * row + 2 * row_in + 2 * row + n * 2 * score_bytes + 2 * group * head_dim * 4
 
 
 def launch_bytes(n_att_per_seq, *, n_kv_heads: int, head_dim: int, kv_elem: int, group: int,
-                 score_bytes: int) -> int:
+                 score_bytes: int, int8_rows: bool = False) -> int:
     """Algorithmic bytes of one step launch: every head of sequence b holds n_att[b] slots."""
     per = unit_step_bytes(n_att_per_seq, head_dim=head_dim, kv_elem=kv_elem, group=group,
-                          score_bytes=score_bytes)
+                          score_bytes=score_bytes, int8_rows=int8_rows)
     return int(np.sum(per) * n_kv_heads)

@@ -22,7 +22,7 @@ class Workload:
     n_q_heads: int
     n_kv_heads: int
     head_dim: int
-    kv_dtype: str                 # "f32" | "bf16"
+    kv_dtype: str                 # storage: "f32" | "bf16" | "i8" (inputs in recipe.kv_dtype)
     score_dtype: str              # "f32" | "f64" (unused by the Random selector)
     selector: str                 # "h2o" | "random"
     n_sink: int = 4
@@ -79,6 +79,12 @@ PAGED_MIXED = Workload(
     recipe=Recipe(seed=0xC5, head_dim=128, kv_dtype="bf16", boost_frac=0.03))
 
 ALL = (TINY_H2O, OPT_LAYER, LLAMA_GQA, RANDOM_ATTN, PAGED_MIXED)
+
+# Compressed state: the OPT layer with its K/V stored as int8 rows of 128 plus
+# one fp32 scale per row (inputs stay bf16; see oracle.quantize_rows for the
+# quantisation), the INT8 K/V storage the pages list beside eviction.
+OPT_LAYER_I8 = OPT_LAYER.scaled(name="opt6.7b_layer_20pct_int8", kv_dtype="i8")
+VARIANTS = (OPT_LAYER_I8,)
 
 
 def prompt_lengths(w: Workload):

@@ -9,7 +9,12 @@ Acceptance (per step, per checked (sequence, KV head) unit):
   way); the oracle then adopts the GPU's set so later steps stay comparable.
   Random Attention has no exemption: its sets must be identical;
 * cumulative scores of the retained tokens: |gpu - oracle| <= 2e-3 * oracle + 1e-9;
-* evicted mass: |gpu - oracle| <= 2e-3 * max(1, oracle).
+* evicted mass: |gpu - oracle| <= 2e-3 * max(1, oracle);
+* stored rows (after the last step): every retained position's K and V row as
+  the library holds it equals, bit for bit, the generator's row for that
+  position -- its bf16 / fp32 bits, or for int8 storage the oracle's
+  quantisation of it (codes and scale).  This pins the compaction: a row moved
+  to the wrong slot or half-moved would show here.
 """
 from __future__ import annotations
 
@@ -30,6 +35,15 @@ GAP = 1e-5
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def oracle_rows(w: WL.Workload, x) -> np.ndarray:
+    """The fp64 rows the oracle attends over for generator rows x (recipe dtype):
+    the exact values, or for int8 storage their quantise-dequantise image."""
+    if w.kv_dtype == "i8":
+        x2 = S.bf16_to_f32(np.asarray(x)).reshape(-1, w.head_dim)
+        return O.dequantize_rows(*O.quantize_rows(x2)).reshape(np.shape(x))
+    return S.cache_to_f64(w.recipe, x)
 
 
 def to_dev(x, kv_dtype):
@@ -61,7 +75,7 @@ def make_cache(w: WL.Workload, lens, n_steps: int, layer: int = 0, init_scores=N
     isc = None
     if init_scores is not None:
         isc = torch.from_numpy(np.ascontiguousarray(init_scores, dtype=np.float64)).cuda()
-    cache = L.H2OCache(cfg, lens, to_dev(K, w.kv_dtype), to_dev(V, w.kv_dtype), init_scores=isc)
+    cache = L.H2OCache(cfg, lens, to_dev(K, w.recipe.kv_dtype), to_dev(V, w.recipe.kv_dtype), init_scores=isc)
     return cache, K, V
 
 
@@ -81,18 +95,21 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
     orc = {}
     for (b, h) in units:
         isc = None if init_scores is None else init_scores[off[b]:off[b + 1], h]
-        orc[(b, h)] = O.Unit(ocfg, b, h, S.cache_to_f64(w.recipe, K[off[b]:off[b + 1], h]),
-                             S.cache_to_f64(w.recipe, V[off[b]:off[b + 1], h]),
+        orc[(b, h)] = O.Unit(ocfg, b, h, oracle_rows(w, K[off[b]:off[b + 1], h]),
+                             oracle_rows(w, V[off[b]:off[b + 1], h]),
                              lens[b] + n_steps + 1, init_scores=isc)
     rep = ParityReport(units=len(units))
     cap = cache.info()[0]
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     win = 256
+    gen_k, gen_v = [], []  # generated rows of the decode steps, for the stored-row check
     for s0 in range(0, n_steps, win):
         ns = min(win, n_steps - s0)
         q, k, v = S.step_window(w.recipe, layer, [p + s0 for p in lens], ns, Hq, Hkv)
+        gen_k.append(k)
+        gen_v.append(v)
         qd = torch.from_numpy(q).cuda()
-        kd, vd = to_dev(k, w.kv_dtype), to_dev(v, w.kv_dtype)
+        kd, vd = to_dev(k, w.recipe.kv_dtype), to_dev(v, w.recipe.kv_dtype)
         for i in range(ns):
             s = s0 + i
             if fused:
@@ -104,15 +121,15 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
             if not check:
                 # the oracle still has to take the step (its own choice)
                 for (b, h) in units:
-                    orc[(b, h)].step(q[i, b, h * G:(h + 1) * G], S.cache_to_f64(w.recipe, k[i, b, h]),
-                                     S.cache_to_f64(w.recipe, v[i, b, h]))
+                    orc[(b, h)].step(q[i, b, h * G:(h + 1) * G], oracle_rows(w, k[i, b, h]),
+                                     oracle_rows(w, v[i, b, h]))
                 continue
             o_gpu = out.cpu().numpy()
             pos, cnt, sc, em = cache.read_indices(cap)
             for (b, h) in units:
                 u = orc[(b, h)]
-                o_ref = u.attend(q[i, b, h * G:(h + 1) * G], S.cache_to_f64(w.recipe, k[i, b, h]),
-                                 S.cache_to_f64(w.recipe, v[i, b, h]))
+                o_ref = u.attend(q[i, b, h * G:(h + 1) * G], oracle_rows(w, k[i, b, h]),
+                                 oracle_rows(w, v[i, b, h]))
                 og = o_gpu[b, h * G:(h + 1) * G].astype(np.float64)
                 err = np.max(np.abs(og - o_ref), axis=1) / np.maximum(np.max(np.abs(o_ref), axis=1), 1e-30)
                 rep.max_out_err = max(rep.max_out_err, float(err.max()))
@@ -149,8 +166,32 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
                     assert abs(em[b, h] - o_em) <= SCORE_TOL * max(1.0, o_em), \
                         f"step {s} unit {(b, h)}: evicted mass {em[b, h]} vs {o_em}"
             rep.steps += 1
+    check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v)
     cache.close()
     say(f"[parity] ok: checked {rep.steps} steps x {rep.units} units, max out err "
         f"{rep.max_out_err:.2e}, max score err {rep.max_score_err:.2e}, evictions {rep.evictions}, "
         f"near-ties adopted {rep.adopted}")
     return rep
+
+
+def check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v):
+    """The library's stored rows of every retained position against the generator."""
+    pos, cnt, _, _ = cache.read_indices()
+    kr, vr, ks, vs = cache.read_kv()
+    off = np.concatenate([[0], np.cumsum(lens)])
+    gk = np.concatenate(gen_k) if gen_k else None  # [steps][B][Hkv][D]
+    gv = np.concatenate(gen_v) if gen_v else None
+    for (b, h) in units:
+        n = int(cnt[b])
+        for i, p in enumerate(pos[b, h, :n]):
+            P = lens[b]
+            kx = K[off[b] + p, h] if p < P else gk[p - P, b, h]
+            vx = V[off[b] + p, h] if p < P else gv[p - P, b, h]
+            if w.kv_dtype == "i8":
+                for x, rows, sc, name in ((kx, kr, ks, "K"), (vx, vr, vs, "V")):
+                    codes, scale = O.quantize_rows(S.bf16_to_f32(x).reshape(1, -1))
+                    assert np.array_equal(rows[b, h, i], codes[0]), f"unit {(b, h)} pos {p}: stored {name} codes"
+                    assert sc[b, h, i] == scale[0], f"unit {(b, h)} pos {p}: stored {name} scale"
+            else:
+                assert np.array_equal(kr[b, h, i], kx), f"unit {(b, h)} pos {p}: stored K row"
+                assert np.array_equal(vr[b, h, i], vx), f"unit {(b, h)} pos {p}: stored V row"

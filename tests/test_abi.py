@@ -72,6 +72,7 @@ GOOD = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kv_dtype="bf16", s
     (dict(n_q_heads=32, n_kv_heads=2), "group size"),
     (dict(head_dim=64), "head_dim"),
     (dict(kv_dtype="f32", head_dim=128), "head_dim"),
+    (dict(kv_dtype="i8", head_dim=64), "head_dim"),
     (dict(hh_fixed=61), "hh_fixed"),
     (dict(budget_fixed=0, budget_num=3, budget_den=2), "proportional"),
     (dict(budget_fixed=0, budget_num=1, budget_den=500), "below n_sink"),

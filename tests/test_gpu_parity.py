@@ -161,3 +161,25 @@ def test_fp32_rows_group_of_eight():
     w = WL.TINY_H2O.scaled(batch=2, n_q_heads=16, n_kv_heads=2)
     rep = P().run_parity(w, 60, lens=[90, 200])
     assert rep.evictions > 0
+
+
+# ------------------------------------------------ compressed state (int8 rows)
+@pytest.mark.parametrize("fused", [True, False], ids=["step_compact", "step+compact"])
+def test_int8_opt_layer_reduced_full_trace(fused):
+    w = WL.OPT_LAYER_I8.scaled(batch=2, n_q_heads=8, n_kv_heads=8)
+    rep = P().run_parity(w, w.decode_steps if fused else 200, fused=fused)
+    assert rep.evictions > 0
+
+
+def test_int8_paged_mixed():
+    w = WL.PAGED_MIXED.scaled(kv_dtype="i8", batch=3, n_q_heads=4, n_kv_heads=4)
+    P().run_parity(w, 30, lens=[300, 517, 1500])
+
+
+def test_int8_gqa_group_of_four_and_random():
+    w = WL.LLAMA_GQA.scaled(kv_dtype="i8", batch=1, n_q_heads=16, n_kv_heads=4, prompt_len=1100)
+    P().run_parity(w, 40)
+    wr = WL.RANDOM_ATTN.scaled(kv_dtype="i8", batch=2, n_q_heads=8, n_kv_heads=2, rand_k=64, rand_r=16,
+                               prompt_len=40)
+    rep = P().run_parity(wr, 120)
+    assert rep.evictions == 4 * 3 * 16  # events after steps 79, 95, 111 (K + r = 80 generated)
