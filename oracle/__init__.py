@@ -12,7 +12,7 @@ import numpy as np
 
 from .build import LIB, build
 
-ORC_H2O, ORC_RANDOM = 0, 1
+ORC_H2O, ORC_RANDOM, ORC_BLOCK = 0, 1, 2
 _dp = C.POINTER(C.c_double)
 _ip = C.POINTER(C.c_int32)
 
@@ -29,6 +29,10 @@ def _bind(lib):
     lib.orc_new.argtypes = [C.POINTER(OrcCfg), C.c_int, C.c_int, C.c_int, C.c_int, _dp, _dp, _dp]
     lib.orc_free.argtypes = [C.c_void_p]
     lib.orc_colsum.restype = C.c_int
+    lib.orc_block_select.restype = C.c_int
+    lib.orc_block_rank.restype = C.c_int
+    lib.orc_block_rank.argtypes = [C.POINTER(OrcCfg), C.c_int, C.c_int, C.c_int, C.POINTER(C.c_ubyte), _dp, _ip]
+    lib.orc_block_select.argtypes = [C.POINTER(C.c_void_p), C.c_int, C.c_int, _ip]
     lib.orc_snapkv_select.restype = C.c_int
     lib.orc_snapkv_select.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _dp, _ip]
     lib.orc_snapkv.restype = C.c_int
@@ -87,7 +91,7 @@ def make_cfg(*, head_dim, group=1, scale=0.0, selector=ORC_H2O, n_sink=4, budget
 
 def cfg_from_workload(w, **over) -> OrcCfg:
     """Oracle parameters of a workload description (attributes read by name)."""
-    sel = ORC_RANDOM if w.selector == "random" else ORC_H2O
+    sel = {"random": ORC_RANDOM, "block": ORC_BLOCK}.get(w.selector, ORC_H2O)
     kw = dict(head_dim=w.head_dim, group=w.n_q_heads // w.n_kv_heads, selector=sel,
               n_sink=w.n_sink, budget_fixed=w.budget_fixed, hh_fixed=w.hh_fixed,
               budget_num=w.budget_num, budget_den=w.budget_den, rand_k=w.rand_k,
@@ -174,6 +178,32 @@ def quantize_rows(x):
 def dequantize_rows(codes, scale) -> np.ndarray:
     """float64 rows code * scale (exact)."""
     return np.asarray(codes, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+def block_select(units, page: int = 16, lib=None) -> np.ndarray:
+    """Victim positions (whole blocks) of one sequence's KV-head units (orc_block_select)."""
+    lib = lib or load()
+    arr = (C.c_void_p * len(units))(*[u.ptr for u in units])
+    vic = np.empty(units[0].length() + 1, dtype=np.int32)
+    e = lib.orc_block_select(arr, len(units), int(page), vic.ctypes.data_as(_ip))
+    if e < 0:
+        raise OracleError(f"orc_block_select failed ({e})")
+    return vic[:e].copy()
+
+
+def block_rank(cfg: OrcCfg, length: int, live, scores, page: int = 16, lib=None) -> np.ndarray:
+    """orc_block_rank: the block rule on given scores [n_heads][length] over the
+    retained set live[length] (nonzero = retained); victim positions."""
+    lib = lib or load()
+    lv = np.ascontiguousarray(live, dtype=np.uint8).reshape(-1)
+    sc = _f64(scores).reshape(-1, int(length))
+    assert lv.size == length
+    vic = np.empty(int(length) + 1, dtype=np.int32)
+    e = lib.orc_block_rank(C.byref(cfg), int(length), int(page), sc.shape[0],
+                           lv.ctypes.data_as(C.POINTER(C.c_ubyte)), _p(sc), vic.ctypes.data_as(_ip))
+    if e < 0:
+        raise OracleError(f"orc_block_rank failed ({e})")
+    return vic[:e].copy()
 
 
 def philox4x64_10(ctr, key, lib=None):

@@ -51,7 +51,7 @@ orc_unit *orc_new(const orc_cfg *c, int b, int h, int prompt_len, int cap,
 {
     if (c->head_dim <= 0 || c->group <= 0 || prompt_len < 0 || cap < prompt_len)
         return NULL;
-    if (c->selector == ORC_H2O) {
+    if (c->selector == ORC_H2O || c->selector == ORC_BLOCK) {
         if (c->n_sink < 0) return NULL;
         if (c->budget_fixed > 0 &&
             (c->hh_fixed < 0 || c->budget_fixed - c->n_sink - c->hh_fixed < 0))
@@ -163,7 +163,7 @@ int orc_attend(orc_unit *u, const double *q, const double *k, const double *v,
         }
         if (probs)
             for (int i = 0; i < n; ++i) probs[(size_t)g * n + i] = u->w[i];
-        if (u->c.selector == ORC_H2O)
+        if (u->c.selector != ORC_RANDOM)  /* H2O and block eviction rank by it */
             for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];
     }
     u->steps += 1;
@@ -246,6 +246,10 @@ int orc_select(orc_unit *u, int32_t *victims, double *tau)
     cand *cs = (cand *)malloc(sizeof(cand) * ((size_t)n + 1));
     if (!cs) return ORC_ENOMEM;
     int nc = 0, e = 0;
+    if (u->c.selector == ORC_BLOCK) {  /* chosen per sequence: orc_block_select */
+        free(cs);
+        return 0;
+    }
     if (u->c.selector == ORC_H2O) {
         int K, HH, W;
         orc_schedule(&u->c, len, &K, &HH, &W);
@@ -319,10 +323,11 @@ int orc_check(const orc_unit *u)
 {
     int n = 0;
     for (int p = 0; p < u->len; ++p) n += u->live[p];
-    if (u->c.selector == ORC_H2O) {
+    if (u->c.selector == ORC_H2O || u->c.selector == ORC_BLOCK) {
         int K, HH, W;
         orc_schedule(&u->c, u->len, &K, &HH, &W);
-        if (u->steps > 0 && n > K) return ORC_ECHECK;
+        /* block eviction bounds the count per sequence (orc_block_select) */
+        if (u->c.selector == ORC_H2O && u->steps > 0 && n > K) return ORC_ECHECK;
         for (int p = 0; p < u->c.n_sink && p < u->len; ++p)
             if (!u->live[p]) return ORC_ECHECK;
         for (int p = u->len - W; p < u->len; ++p)
@@ -529,4 +534,103 @@ int orc_snapkv(const orc_cfg *c, int P, int w, int pool, int keep, const double 
     if (rc == ORC_OK) rc = orc_snapkv_select(c->group, P, w, pool, keep, v, kept);
     if (!votes) free(v);
     return rc;
+}
+
+/* ---- block-granular eviction ------------------------------------------------ */
+typedef struct {
+    int imp, block;
+} block_rank;
+
+/* Eviction order of candidate blocks: lower importance first, then the older block. */
+static int cmp_block(const void *a, const void *b)
+{
+    const block_rank *x = (const block_rank *)a, *y = (const block_rank *)b;
+    if (x->imp != y->imp) return x->imp < y->imp ? -1 : 1;
+    return (x->block < y->block) ? -1 : (x->block > y->block) ? 1 : 0;
+}
+
+int orc_block_rank(const orc_cfg *c, int len, int page, int n_units, const unsigned char *live,
+                   const double *scores, int32_t *victims)
+{
+    if (!c || len < 0 || page < 1 || n_units < 1 || !live || !scores || !victims) return ORC_EARG;
+    int K, HH, W;
+    orc_schedule(c, len, &K, &HH, &W);
+    int n = 0;
+    for (int p = 0; p < len; ++p) n += live[p] != 0;
+    if (n <= K) return 0;
+    const int nb = (len + page - 1) / page;
+    char *cand = (char *)calloc((size_t)nb + 1, 1);
+    int *imp = (int *)calloc((size_t)nb + 1, sizeof(int));
+    vote_pos *tok = (vote_pos *)malloc(sizeof(vote_pos) * ((size_t)len + 1));
+    block_rank *br = (block_rank *)malloc(sizeof(block_rank) * ((size_t)nb + 1));
+    if (!cand || !imp || !tok || !br) {
+        free(cand);
+        free(imp);
+        free(tok);
+        free(br);
+        return ORC_ENOMEM;
+    }
+    /* candidates: whole retained blocks outside the sinks and the recent window */
+    int ncand = 0;
+    for (int k = 0; k < nb; ++k) {
+        const int lo = k * page, hi = lo + page - 1;
+        int full = hi < len;
+        for (int p = lo; full && p <= hi && p < len; ++p) full = live[p] != 0;
+        cand[k] = full && lo >= c->n_sink && hi < len - W;
+        ncand += cand[k];
+    }
+    /* importance: per head, its HH best candidate tokens count once each */
+    for (int i = 0; i < n_units; ++i) {
+        const double *sc = scores + (size_t)i * len;
+        int nt = 0;
+        for (int p = 0; p < len; ++p)
+            if (cand[p / page]) {
+                tok[nt].v = sc[p];
+                tok[nt].pos = p;
+                ++nt;
+            }
+        qsort(tok, (size_t)nt, sizeof(vote_pos), cmp_vote_keep);
+        const int hh = HH < nt ? HH : nt;
+        for (int x = 0; x < hh; ++x) imp[tok[x].pos / page] += 1;
+    }
+    /* the least important candidate blocks go, older first on equal importance */
+    int nr = 0;
+    for (int k = 0; k < nb; ++k)
+        if (cand[k]) {
+            br[nr].imp = imp[k];
+            br[nr].block = k;
+            ++nr;
+        }
+    qsort(br, (size_t)nr, sizeof(block_rank), cmp_block);
+    const int need = (n - K + page - 1) / page;
+    const int m = need < ncand ? need : ncand;
+    for (int k = 0; k < nb; ++k) cand[k] = 0; /* reused: the evicted blocks */
+    for (int x = 0; x < m; ++x) cand[br[x].block] = 1;
+    int e = 0;
+    for (int p = 0; p < len; ++p)
+        if (cand[p / page]) victims[e++] = p;
+    free(cand);
+    free(imp);
+    free(tok);
+    free(br);
+    return e;
+}
+
+int orc_block_select(orc_unit *const *u, int n_units, int page, int32_t *victims)
+{
+    if (!u || n_units < 1 || page < 1 || !victims) return ORC_EARG;
+    const orc_unit *u0 = u[0];
+    const int len = u0->len;
+    for (int i = 1; i < n_units; ++i) {
+        if (u[i]->len != len) return ORC_EARG;
+        for (int p = 0; p < len; ++p)
+            if (u[i]->live[p] != u0->live[p]) return ORC_EARG;
+    }
+    double *sc = (double *)malloc(sizeof(double) * ((size_t)n_units * len + 1));
+    if (!sc) return ORC_ENOMEM;
+    for (int i = 0; i < n_units; ++i)
+        memcpy(sc + (size_t)i * len, u[i]->score, sizeof(double) * (size_t)len);
+    const int e = orc_block_rank(&u0->c, len, page, n_units, u0->live, sc, victims);
+    free(sc);
+    return e;
 }

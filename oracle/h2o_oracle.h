@@ -31,14 +31,14 @@
 extern "C" {
 #endif
 
-enum { ORC_H2O = 0, ORC_RANDOM = 1 };
+enum { ORC_H2O = 0, ORC_RANDOM = 1, ORC_BLOCK = 2 };
 enum { ORC_OK = 0, ORC_EARG = -1, ORC_ECHECK = -2, ORC_ENOMEM = -3 };
 
 typedef struct {
     int head_dim;      /* D */
     int group;         /* G: query heads per KV head */
     double scale;      /* logit scale; 0 -> 1/sqrt(D) */
-    int selector;      /* ORC_H2O or ORC_RANDOM */
+    int selector;      /* ORC_H2O, ORC_RANDOM or ORC_BLOCK (see orc_block_select) */
     int n_sink;        /* H2O: positions 0..n_sink-1 are never evicted */
     int budget_fixed;  /* H2O: > 0 -> budget K fixed ...            */
     int hh_fixed;      /*        ... with this many heavy hitters   */
@@ -90,6 +90,32 @@ int orc_length(const orc_unit *u);
 /* orc_step on n units, spread over nthreads POSIX threads; returns first error. */
 int orc_step_many(orc_unit **u, int n, const double *const *q, const double *const *k,
                   const double *const *v, double *const *out, int nthreads);
+
+/* Block-granular eviction of one sequence ("Attention Sinks and KV cache
+ * eviction", sec. 5.1: KV lives in fixed-size blocks, so eviction frees whole
+ * blocks; blocks with the lowest share of important tokens go first).  The n
+ * units are the KV heads of one sequence (selector ORC_BLOCK, all with the same
+ * positions appended and retained; orc_step / orc_select of such a unit never
+ * evict).  Block k holds positions [k page, (k + 1) page).  At current length
+ * len with budget K, heavy hitters HH and window W (orc_schedule):
+ *   - nothing goes while the retained count n <= K;
+ *   - candidates: blocks with all `page` positions retained, none of them a
+ *     sink (< n_sink) or in the recent window (>= len - W);
+ *   - a (token, head) pair is important when the token is among that head's
+ *     HH highest-scored candidate tokens (equal scores: the lower position
+ *     first), i.e. the heavy hitters token-level eviction would keep;
+ *   - a block's importance is its count of important pairs; the
+ *     m = min(#candidates, ceil((n - K) / page)) candidates of lowest
+ *     importance go (equal importance: the older block first).
+ * victims receives the evicted positions in ascending order (at most n);
+ * returns their count, or ORC_EARG. */
+int orc_block_select(orc_unit *const *u, int n, int page, int32_t *victims);
+
+/* The same rule on given data: n_units score rows of len positions (row i =
+ * the scores of head i by position) over the shared retained set live[len]
+ * (nonzero = retained) under configuration c's schedule at length len. */
+int orc_block_rank(const orc_cfg *c, int len, int page, int n_units, const unsigned char *live,
+                   const double *scores, int32_t *victims);
 
 /* Causal-attention column sums of one unit's prompt (P positions):
  * for every query row i in [row_lo, P), every query head g of the group and

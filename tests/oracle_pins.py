@@ -494,6 +494,165 @@ def pin_int8_rows(lib):
     assert np.all(sg == np.float32(0.25)) and np.array_equal(cg.astype(np.float32), grid)
 
 
+# --------------------------------------------------- block-granular eviction
+def _block_expect(length, live, scores, n_sink, K, HH, page):
+    """Brute force for one block-eviction decision: importance per block from
+    each head's HH best candidate tokens (numpy.lexsort on (position, -score)),
+    then the m-subset of candidate blocks with the least total importance,
+    equal totals going to the lexicographically first (oldest) block list."""
+    W = K - n_sink - HH
+    n = int(np.count_nonzero(live))
+    if n <= K:
+        return []
+    nb = (length + page - 1) // page
+    cand = [k for k in range(nb)
+            if (k + 1) * page <= length and all(live[k * page:(k + 1) * page])
+            and k * page >= n_sink and (k + 1) * page - 1 < length - W]
+    imp = {k: 0 for k in cand}
+    toks = np.array([p for k in cand for p in range(k * page, (k + 1) * page)], dtype=np.int64)
+    for sc in scores:
+        if toks.size == 0:
+            break
+        order = np.lexsort((toks, -np.asarray(sc)[toks]))
+        for p in toks[order[:max(0, min(HH, toks.size))]]:
+            imp[int(p) // page] += 1
+    m = min(len(cand), -(-(n - K) // page))
+    best = min(itertools.combinations(cand, m), key=lambda sub: (sum(imp[k] for k in sub), sub))
+    return [p for k in sorted(best) for p in range(k * page, (k + 1) * page)]
+
+
+def pin_block_bruteforce(lib):
+    """Block-granular eviction ("Attention Sinks and KV cache eviction",
+    section 5: blocks with the lowest share of important tokens go first),
+    against brute force over every m-subset of candidate blocks on tiny inputs:
+    random retained sets (holes make a block ineligible), 1 to 3 heads, scores
+    rounded to one decimal so that ties occur, pages of 2 and 3."""
+    rng = np.random.default_rng(41)
+    for trial in range(60):
+        page = 2 + trial % 2
+        length = int(rng.integers(12, 22))
+        n_sink = int(rng.integers(0, 3))
+        HH = int(rng.integers(0, 6))
+        W = int(rng.integers(0, 5))
+        K = n_sink + HH + W
+        live = (rng.random(length) < 0.85).astype(np.uint8)
+        live[:n_sink] = 1
+        live[length - W:] = 1
+        heads = int(rng.integers(1, 4))
+        scores = np.round(rng.random((heads, length)), 1)
+        cfg = O.make_cfg(head_dim=4, selector=O.ORC_BLOCK, n_sink=n_sink, budget_fixed=max(K, 1),
+                         hh_fixed=HH)
+        if K < 1:
+            continue
+        got = O.block_rank(cfg, length, live, scores, page=page, lib=lib)
+        want = _block_expect(length, live, scores, n_sink, K, HH, page)
+        assert list(got) == want, f"trial {trial}: {list(got)} vs {want}"
+
+
+def pin_block_equal_scores(lib):
+    """All scores equal: each head's heavy hitters are its HH oldest candidate
+    tokens, so the first HH // page candidate blocks are fully important, one
+    is partly, and the rest have importance zero; the victims are the oldest
+    zero-importance blocks, and when more must go the partly important block
+    follows before the fully important ones (oldest first among those)."""
+    page, n_sink, HH, W = 4, 2, 10, 5
+    K = n_sink + HH + W
+    length = 40
+    live = np.ones(length, dtype=np.uint8)
+    cfg = O.make_cfg(head_dim=4, selector=O.ORC_BLOCK, n_sink=n_sink, budget_fixed=K, hh_fixed=HH)
+    blocks = lambda ks: [p for k in ks for p in range(4 * k, 4 * k + 4)]
+    # candidates: blocks 1..7 (block 0 holds sinks, block 8 reaches position 35 of the
+    # window [35, 40)); importance over 3 heads: b1 = b2 = 12, b3 = 6, b4..b7 = 0;
+    # n - K = 23 -> 6 blocks: the four zeros, then b3, then b1 (older than b2)
+    got = O.block_rank(cfg, length, live, np.ones((3, length)), page=page, lib=lib)
+    assert list(got) == blocks((1, 3, 4, 5, 6, 7))
+    live2 = live.copy()
+    live2[20:28] = 0  # blocks 5 and 6 already gone: n - K = 15 -> 4 of 1, 2, 3, 4, 7
+    got = O.block_rank(cfg, length, live2, np.ones((3, length)), page=page, lib=lib)
+    assert list(got) == blocks((1, 3, 4, 7))
+    # n <= K: nothing goes
+    live3 = np.zeros(length, dtype=np.uint8)
+    live3[:K] = 1
+    assert O.block_rank(cfg, length, live3, np.ones((1, length)), page=page, lib=lib).size == 0
+
+
+def pin_block_page1_single_head_is_h2o(lib):
+    """With pages of one token and one head, the block rule is H2O's token rule:
+    once H2O runs, the retained set is sinks + candidates + the whole window, so
+    the unimportant candidates are exactly the n - K lowest-scored ones.  An H2O
+    unit and a block unit fed the same steps keep the same positions."""
+    rng = np.random.default_rng(42)
+    D, P, steps = 8, 30, 40
+    pk, pv = rng.standard_normal((P, D)), rng.standard_normal((P, D))
+    kw = dict(head_dim=D, n_sink=2, budget_fixed=14, hh_fixed=5)
+    uh = _unit(lib, O.make_cfg(**kw), pk, pv, P + steps)
+    ub = _unit(lib, O.make_cfg(selector=O.ORC_BLOCK, **kw), pk, pv, P + steps)
+    for s in range(steps):
+        q, k, v = rng.standard_normal((1, D)) * 2, rng.standard_normal(D), rng.standard_normal(D)
+        uh.step(q, k, v)
+        ub.attend(q, k, v)
+        ub.evict(O.block_select([ub], page=1, lib=lib))
+        ub.check()
+        ph, sh, eh = uh.state()
+        pb, sb, eb = ub.state()
+        assert list(ph) == list(pb), f"step {s}"
+        assert np.array_equal(sh, sb) and abs(eh - eb) <= 1e-12 * max(1.0, eh), f"step {s}"
+
+
+def pin_block_run_invariants(lib):
+    """A run of block eviction over two heads (units stepped, then
+    orc_block_select on both): victims are the brute-force choice on the two
+    units' scores, and they are whole blocks the units share, never
+    a sink's block and never one reaching into the recent window; each step
+    leaves n <= K unless no candidate block is left; and the evicted mass plus
+    the retained scores add up to the total weight handed out (one per query
+    head per step, plus the prompt's initial scores)."""
+    rng = np.random.default_rng(43)
+    D, G, P, steps, page = 8, 2, 80, 60, 4
+    K, HH = 40, 24
+    W = K - 3 - HH
+    cfg = O.make_cfg(head_dim=D, group=G, selector=O.ORC_BLOCK, n_sink=3, budget_fixed=K, hh_fixed=HH)
+    units = []
+    for h in range(2):
+        init = rng.random(P)
+        units.append(_unit(lib, cfg, rng.standard_normal((P, D)), rng.standard_normal((P, D)),
+                           P + steps, h=h, init=init))
+    total0 = [float(np.sum(u.state()[1])) for u in units]
+    evicted_blocks = 0
+    for s in range(steps):
+        for u in units:
+            u.attend(rng.standard_normal((G, D)) * 2, rng.standard_normal(D), rng.standard_normal(D))
+        length = P + s + 1
+        pre = units[0].state()[0]
+        vic = O.block_select(units, page=page, lib=lib)
+        live = np.zeros(length, dtype=np.uint8)
+        live[pre] = 1
+        scores = np.zeros((len(units), length))
+        for i, u in enumerate(units):
+            pos_i, sc_i, _ = u.state()
+            scores[i, pos_i] = sc_i
+        assert list(vic) == _block_expect(length, live, scores, 3, K, HH, page), f"step {s}"
+        assert len(vic) % page == 0
+        for i in range(0, len(vic), page):
+            blk = vic[i:i + page]
+            assert blk[0] % page == 0 and list(blk) == list(range(blk[0], blk[0] + page))
+            assert blk[0] >= 3 and blk[-1] < length - W
+        for u in units:
+            u.evict(vic)
+            u.check()
+        evicted_blocks += len(vic) // page
+        post = units[0].state()[0]
+        left = [k for k in range(length // page)
+                if all(p in set(post.tolist()) for p in range(k * page, k * page + page))
+                and k * page >= 3 and k * page + page - 1 < length - W]
+        assert len(post) <= K or not left, f"step {s}: {len(post)} > {K} with {len(left)} candidates"
+        assert len(pre) - len(post) == len(vic)
+        for i, u in enumerate(units):
+            _, sc, em = u.state()
+            assert abs(float(np.sum(sc)) + em - total0[i] - G * (s + 1)) < 1e-9
+    assert evicted_blocks > 5
+
+
 ALL_PINS = [
     pin_attention_full_cache,
     pin_scores_and_selection_recomputed,
@@ -513,4 +672,8 @@ ALL_PINS = [
     pin_snapkv_ties_keep_lower_positions,
     pin_snapkv_votes_are_window_weights,
     pin_int8_rows,
+    pin_block_bruteforce,
+    pin_block_equal_scores,
+    pin_block_page1_single_head_is_h2o,
+    pin_block_run_invariants,
 ]

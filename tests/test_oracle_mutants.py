@@ -24,8 +24,8 @@ MUTANTS = {
     "value_rows_are_keys": ("const double *vj = u->V +", "const double *vj = u->K +"),
     "slot_index_for_position": ("const double *kj = u->K + (size_t)u->R[i] * D;",
                                 "const double *kj = u->K + (size_t)i * D;"),
-    "score_only_first_query_head": ("if (u->c.selector == ORC_H2O)\n            for (int i = 0; i < n; ++i) u->score",
-                                    "if (u->c.selector == ORC_H2O && g == 0)\n            for (int i = 0; i < n; ++i) u->score"),
+    "score_only_first_query_head": ("if (u->c.selector != ORC_RANDOM)  /* H2O and block eviction rank by it */\n",
+                                    "if (u->c.selector != ORC_RANDOM && g == 0)\n"),
     "score_missing_new_token": ("for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];",
                                 "for (int i = 0; i < n - 1; ++i) u->score[u->R[i]] += u->w[i];"),
     "tie_keeps_higher_position": ("    return (x->pos > y->pos) ? -1 : (x->pos < y->pos) ? 1 : 0;\n}\n\nstatic int cmp_key",
@@ -57,6 +57,22 @@ MUTANTS = {
                             "    if (x->v < y->v) return -1;\n    if (x->v > y->v) return 1;"),
     "snapkv_first_head_only": ("for (int g = 0; g < G; ++g) {\n        const double *vg",
                                "for (int g = 0; g < 1; ++g) {\n        const double *vg"),
+    "block_evict_most_important": ("    if (x->imp != y->imp) return x->imp < y->imp ? -1 : 1;",
+                                   "    if (x->imp != y->imp) return x->imp > y->imp ? -1 : 1;"),
+    "block_ties_newer_first": ("    return (x->block < y->block) ? -1 : (x->block > y->block) ? 1 : 0;",
+                               "    return (x->block > y->block) ? -1 : (x->block < y->block) ? 1 : 0;"),
+    "block_sink_block_eligible": ("cand[k] = full && lo >= c->n_sink && hi < len - W;",
+                                  "cand[k] = full && hi >= c->n_sink && hi < len - W;"),
+    "block_window_off_by_one": ("cand[k] = full && lo >= c->n_sink && hi < len - W;",
+                                "cand[k] = full && lo >= c->n_sink && hi <= len - W;"),
+    "block_holes_ignored": ("full = live[p] != 0;", "full = 1;"),
+    "block_first_head_only": ("    for (int i = 0; i < n_units; ++i) {\n        const double *sc = scores",
+                              "    for (int i = 0; i < 1; ++i) {\n        const double *sc = scores"),
+    "block_hh_plus_one": ("const int hh = HH < nt ? HH : nt;\n        for (int x = 0; x < hh; ++x) imp",
+                          "const int hh = HH + 1 < nt ? HH + 1 : nt;\n        for (int x = 0; x < hh; ++x) imp"),
+    "block_counts_lowest_scores": ("imp[tok[x].pos / page] += 1;", "imp[tok[nt - 1 - x].pos / page] += 1;"),
+    "block_need_rounds_down": ("const int need = (n - K + page - 1) / page;", "const int need = (n - K) / page;"),
+    "block_select_own_scores_first_unit": ("memcpy(sc + (size_t)i * len, u[i]->score,", "memcpy(sc + (size_t)i * len, u[0]->score,"),
     "random_largest_words": ("    if (x->key < y->key) return -1;\n    if (x->key > y->key) return 1;",
                              "    if (x->key > y->key) return -1;\n    if (x->key < y->key) return 1;"),
 }
