@@ -44,7 +44,8 @@ from kv_cache_eviction_h2o_amd import workloads as WL  # noqa: E402
 METRIC = "retained KV tokens processed/sec per decode step (attn+evict+compact); % HBM peak"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc")
-KERNEL_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip", "h2o_prefill.hip")
+KERNEL_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip", "h2o_prefill.hip",
+               "h2o_block.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -166,22 +167,9 @@ def step_kernel_name(w) -> str:
 
 
 def retained_schedule(w, P: int, n_steps: int):
-    """n_att (slots attended) at each decode step for one sequence with prompt P.
-
-    Host arithmetic mirroring the budget rule: the count after a step is
-    min(n_att, K_t) for H2O and drops by r at each Random Attention event."""
-    out = np.empty(n_steps, dtype=np.int64)
-    count = P
-    for s in range(n_steps):
-        t = P + s
-        n_att = count + 1
-        out[s] = n_att
-        if w.selector == "h2o":
-            K = w.budget_fixed if w.budget_fixed > 0 else ((t + 1) * w.budget_num) // w.budget_den
-            count = min(n_att, K)
-        else:
-            count = n_att - (w.rand_r if n_att - P == w.rand_k + w.rand_r else 0)
-    return out
+    """n_att (slots attended) at each decode step for one sequence with prompt P
+    (the host mirror of the budget rule in metrics.retained_counts)."""
+    return M.retained_counts(w, P, n_steps)["n_att"]
 
 
 def traffic_from_profiles(w):
@@ -479,7 +467,8 @@ def main():
     elapsed = time.perf_counter() - t0
 
     # ---- accounting
-    sched = np.stack([retained_schedule(w, P, total_steps) for P in lens])  # [B][steps]
+    counts = [M.retained_counts(w, P, total_steps) for P in lens]
+    sched = np.stack([c["n_att"] for c in counts])  # [B][steps]
     win = sched[:, s0:s0 + K_steps]  # n_att per sequence per timed step
     tokens = float(win.sum()) * layers
     value = tokens / elapsed
@@ -490,6 +479,13 @@ def main():
     launch_b = np.array([M.launch_bytes(win[:, i], n_kv_heads=Hkv, head_dim=D, kv_elem=kv_elem,
                                         group=G, score_bytes=sbytes, int8_rows=w.kv_dtype == "i8")
                         for i in range(K_steps)])
+    if w.selector == "block":  # the page-eviction launches that follow a step
+        for i in range(K_steps):
+            s = s0 + i
+            hit = [c for c in counts if c["pages"][s] > 0]
+            launch_b[i] += M.block_launch_bytes([c["cand"][s] for c in hit], [c["pages"][s] for c in hit],
+                                                [c["n_att"][s] for c in hit], n_kv_heads=Hkv,
+                                                score_bytes=sbytes)
     step_bytes = float(launch_b.sum()) * layers
     roof = None
     if use_ev:
@@ -511,14 +507,8 @@ def main():
                 "algorithmic_bytes_per_launch": int(launch_b.mean())}
 
     # sanity: the library's counts equal the schedule used for the accounting
-    _, cnt, _, _ = caches[0].read_indices()
-    if w.selector == "h2o":
-        def budget(length):
-            return w.budget_fixed if w.budget_fixed > 0 else length * w.budget_num // w.budget_den
-        expect = np.array([min(int(sched[b, -1]), budget(lens[b] + total_steps)) for b in range(B)])
-    else:
-        last = sched[:, -1]
-        expect = last - np.where(last - np.array(lens) == w.rand_k + w.rand_r, w.rand_r, 0)
+    expect = np.array([c["count"][-1] for c in counts])
+    _, cnt, _, _ = caches[0].read_indices(int(expect.max()))
     if not np.array_equal(cnt, expect):
         raise SystemExit(f"retained counts {cnt[:4]} differ from the schedule {expect[:4]}")
 

@@ -14,6 +14,10 @@
  *               (the prompt is never evicted);
  *   a7 compact  the retained slots are made contiguous again in place
  *               (paged layout: whole 16-token pages are released).
+ *   Block eviction (H2O_SEL_BLOCK, paged layout only): a5 as for H2O, no
+ *               token goes in a6; after the step whole 16-token pages go
+ *               instead (see H2O_SEL_BLOCK below) and a7 only rewrites the
+ *               block table -- nothing in the cache moves.
  *
  * Where the operation is defined (titles of the pages describing the method):
  *   "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of LLMs",
@@ -79,7 +83,22 @@ typedef enum {
     H2O_ESTATE = -4    /* call out of order (e.g. h2o_step while a compaction is pending) */
 } h2o_status;
 
-enum { H2O_SEL_H2O = 0, H2O_SEL_RANDOM = 1 };
+/* Selectors.  H2O_SEL_BLOCK: block-granular eviction ("Attention Sinks and KV
+ * cache eviction", sec. 5: the cache is managed in blocks, so eviction frees
+ * whole blocks, those with the lowest share of important tokens first).  With
+ * the paged layout, at length len = t + 1 and the H2O schedule (K, HH, W):
+ * when the retained count n exceeds K, the candidates are the sequence's
+ * whole retained pages holding no sink position (< n_sink) and ending before
+ * the recent window (positions < len - W); a token is important for a KV head
+ * when it is among that head's HH highest-scored candidate tokens (equal
+ * scores: the older token); a page's importance is its count of important
+ * (token, head) pairs over the sequence's KV heads; the
+ * min(#candidates, ceil((n - K) / 16)) pages of lowest importance go (equal
+ * importance: the older page first).  Pages hold 16 consecutive positions and
+ * never move, so after a step a sequence holds either <= K tokens or no
+ * candidate page.  Slot capacity: max(P, K_max + 16 * ceil(n_sink / 16) + 15) + 1
+ * tokens, at most 5120 pages per sequence. */
+enum { H2O_SEL_H2O = 0, H2O_SEL_RANDOM = 1, H2O_SEL_BLOCK = 2 };
 enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F64 = 2, H2O_I8 = 3 };
 
 typedef struct {
@@ -88,9 +107,9 @@ typedef struct {
     int32_t n_kv_heads;    /* Hkv; Hq must be a multiple */
     int32_t head_dim;      /* D */
     int32_t kv_dtype;      /* H2O_BF16, H2O_F32, or H2O_I8 (bf16 inputs stored as int8 rows) */
-    int32_t score_dtype;   /* H2O: H2O_F32 or H2O_F64 cumulative scores */
+    int32_t score_dtype;   /* H2O, block: H2O_F32 or H2O_F64 cumulative scores */
     float scale;           /* logit scale; 0 -> 1/sqrt(D) */
-    int32_t selector;      /* H2O_SEL_H2O or H2O_SEL_RANDOM */
+    int32_t selector;      /* H2O_SEL_H2O, H2O_SEL_RANDOM or H2O_SEL_BLOCK (needs page_size 16) */
     int32_t n_sink;        /* H2O: positions 0..n_sink-1 are never evicted (4 on the pages) */
     int32_t budget_fixed;  /* H2O: > 0 -> fixed budget K ...                          */
     int32_t hh_fixed;      /*        ... of which hh_fixed heavy hitters; recent window
@@ -127,7 +146,8 @@ int h2o_step(h2o_ctx *ctx, const float *q, const void *k_new, const void *v_new,
              void *stream);
 
 /* Step a7 for the pending step: move retained slots into the victims' holes,
- * set the retained counts, release pages no longer used.
+ * set the retained counts, release pages no longer used (block eviction:
+ * choose and release the step's pages, see H2O_SEL_BLOCK).
  * Errors: H2O_ESTATE (no step pending), H2O_EDEVICE. */
 int h2o_compact(h2o_ctx *ctx, void *stream);
 
@@ -143,8 +163,10 @@ int h2o_step_compact(h2o_ctx *ctx, const float *q, const void *k_new, const void
  *   scores        host [B][Hkv][cap] fp64, aligned with pos; NULL to skip.
  *   evicted_mass  host [B][Hkv] fp64 summed scores of evicted tokens; NULL to skip.
  *   cap           entries per (b, h) in pos/scores; must be >= every count.
- * Errors: H2O_EINVAL (cap too small), H2O_ESTATE (a compaction is pending),
- * H2O_EDEVICE. */
+ * With block eviction a pending step may be read: the state after the append,
+ * before any page goes (the scores the page ranking will use).
+ * Errors: H2O_EINVAL (cap too small), H2O_ESTATE (a compaction is pending,
+ * block eviction aside), H2O_EDEVICE. */
 int h2o_read_indices(h2o_ctx *ctx, int32_t *pos, int32_t *count, double *scores,
                      double *evicted_mass, size_t cap, void *stream);
 
@@ -156,7 +178,9 @@ int h2o_read_indices(h2o_ctx *ctx, int32_t *pos, int32_t *count, double *scores,
  *   k_scale, v_scale  host [B][Hkv][cap] fp32 row scales (H2O_I8; ignored and
  *                     may be NULL otherwise).
  *   cap               entries per (b, h); must be >= every count.
- * Errors: H2O_EINVAL, H2O_ESTATE (a compaction is pending), H2O_EDEVICE. */
+ * A pending block-eviction step reads as in h2o_read_indices.
+ * Errors: H2O_EINVAL, H2O_ESTATE (a compaction is pending, block eviction
+ * aside), H2O_EDEVICE. */
 int h2o_read_kv(h2o_ctx *ctx, void *k_rows, void *v_rows, float *k_scale, float *v_scale, size_t cap,
                 void *stream);
 

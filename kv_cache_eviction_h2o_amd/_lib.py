@@ -15,7 +15,8 @@ import numpy as np
 from .build import LIB
 
 H2O_OK, H2O_EINVAL, H2O_ENOMEM, H2O_EDEVICE, H2O_ESTATE = 0, -1, -2, -3, -4
-SEL_H2O, SEL_RANDOM = 0, 1
+SEL_H2O, SEL_RANDOM, SEL_BLOCK = 0, 1, 2
+_SELECTORS = {"h2o": SEL_H2O, "random": SEL_RANDOM, "block": SEL_BLOCK}
 F32, BF16, F64, I8 = 0, 1, 2, 3
 _STATUS = {H2O_EINVAL: "H2O_EINVAL", H2O_ENOMEM: "H2O_ENOMEM", H2O_EDEVICE: "H2O_EDEVICE",
            H2O_ESTATE: "H2O_ESTATE"}
@@ -93,7 +94,7 @@ def make_config(*, batch, n_q_heads, n_kv_heads, head_dim, kv_dtype="bf16", scor
                 max_len) -> H2OConfig:
     dt = {"f32": F32, "bf16": BF16, "f64": F64, "i8": I8}
     return H2OConfig(batch, n_q_heads, n_kv_heads, head_dim, dt[kv_dtype], dt[score_dtype],
-                     float(scale), SEL_RANDOM if selector == "random" else SEL_H2O, n_sink,
+                     float(scale), _SELECTORS[selector], n_sink,
                      budget_fixed, hh_fixed, budget_num, budget_den, rand_k, rand_r,
                      int(seed) & 0xFFFFFFFFFFFFFFFF, page_size, max_pages, max_len)
 
@@ -117,8 +118,10 @@ def pages_needed(prompt_lens, steps: int, cfg: H2OConfig) -> int:
     grow = 0
     for p in prompt_lens:
         end = p + steps
-        if cfg.selector == SEL_H2O:
+        if cfg.selector in (SEL_H2O, SEL_BLOCK):
             k = cfg.budget_fixed if cfg.budget_fixed > 0 else end * cfg.budget_num // cfg.budget_den
+            if cfg.selector == SEL_BLOCK:  # whole pages: up to a page past the sinks' and the window's
+                k = max(p, k + ps * ((cfg.n_sink + ps - 1) // ps) + ps - 1)
             grow += (min(end, k + 1) + ps - 1) // ps + 1
         else:
             grow += (min(end, p + cfg.rand_k + cfg.rand_r) + ps - 1) // ps + 1

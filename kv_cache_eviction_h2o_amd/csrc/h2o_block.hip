@@ -1,0 +1,251 @@
+// Block-granular eviction on the paged layout ("Attention Sinks and KV cache
+// eviction", sec. 5): the cache is managed in 16-token pages, so eviction frees
+// whole pages, and the pages whose share of important tokens is lowest go
+// first.  A token is important for a KV head when it is among that head's HH
+// highest-scored candidate tokens (the heavy hitters of sec. 4.2, equal scores
+// favouring the older token); a page's importance is its count of important
+// (token, head) pairs over the sequence's KV heads; equal importance sends the
+// older page first.
+//
+// Pages hold 16 consecutive positions and nothing ever moves inside the cache:
+// the retained set is a union of whole pages, the block-table row lists them in
+// position order, and each page carries its slots' scores and positions.  An
+// eviction therefore rewrites one block-table row and hands the pages back;
+// no K/V row, score or position is copied.  The candidates -- whole pages past
+// the pages holding sink positions and clear of the recent window -- are the
+// row entries [js, js + ncand); the host knows ncand and how many pages go (m)
+// from the schedule alone (the window's start never moves back, so every page
+// evicted so far lay before it), which keeps the host's page accounting exact
+// without reading anything back.
+//
+//   block_importance_kernel  one workgroup per (sequence, KV head): radix
+//       select of the head's (c - HH)-th smallest candidate key (score, then
+//       newer first; c = 16 ncand tokens), then per candidate page the count
+//       of keys above it -> bimp[unit][page entry].
+//   block_evict_kernel  one workgroup per sequence: importance summed over the
+//       heads, radix select of the m smallest (importance, entry) keys, the
+//       row compacted (kept entries in order), the freed pages pushed on the
+//       free stack, and per head the evicted score mass added and the freed
+//       slots' positions cleared.
+#include "h2o_device.h"
+
+namespace h2o {
+namespace {
+
+constexpr int kBNT = 256;  // threads per workgroup (4 waves)
+
+template <typename ST>
+__device__ inline void score_key(ST v, unsigned (&wk)[3])
+{
+    if constexpr (sizeof(ST) == 4) {
+        wk[2] = 0;
+        wk[1] = ord32((float)v);
+    } else {
+        const unsigned long long u = ord64((double)v);
+        wk[2] = (unsigned)(u >> 32);
+        wk[1] = (unsigned)u;
+    }
+}
+
+template <typename ST>
+__global__ __launch_bounds__(kBNT) void block_importance_kernel(const BlockArgs a)
+{
+    extern __shared__ int32_t cpage[];  // [ncand] page of each candidate entry
+    __shared__ RadixSmem rs;
+    const Geometry& gm = a.g;
+    const State& S = a.s;
+    const int i = blockIdx.x / gm.Hkv, h = blockIdx.x - i * gm.Hkv;
+    const int b = a.seq_b[i], nc = a.seq_c[i];
+    const int tid = threadIdx.x;
+    const int32_t* row = S.bt + (size_t)b * gm.maxp + a.js;
+    for (int j = tid; j < nc; j += kBNT) cpage[j] = row[j];
+    __syncthreads();
+    int K, HH, W;
+    schedule(a.sc, a.seq_len[i], K, HH, W);
+    const int c = nc * kPageSize;
+    const int e = c - HH;  // candidate tokens that are not heavy hitters of this head
+    const ST* scp = reinterpret_cast<const ST*>(S.sc);
+    const int Hkv = gm.Hkv;
+    // key of candidate token jl (entry jl / 16, slot jl % 16): score, then the
+    // newer token first (~jl: entries are in position order)
+    auto key_of = [&](int jl, unsigned (&wk)[3]) -> bool {
+        score_key(scp[((size_t)cpage[jl >> kPageShift] * Hkv + h) * kPageSize + (jl & (kPageSize - 1))], wk);
+        wk[0] = ~(unsigned)jl;
+        return true;
+    };
+    const bool all_imp = e <= 0, none_imp = e >= c;
+    if (!all_imp && !none_imp) radix_select<kBNT>(key_of, c, e, sizeof(ST) == 4 ? 4 : 0, rs);
+    uint8_t* out = S.bimp + ((size_t)b * Hkv + h) * gm.maxp;
+    for (int jb = tid; jb < nc; jb += kBNT) {
+        int cnt = all_imp ? kPageSize : 0;
+        if (!all_imp && !none_imp) {
+#pragma unroll 4
+            for (int r = 0; r < kPageSize; ++r) {
+                unsigned wk[3];
+                key_of(jb * kPageSize + r, wk);
+                cnt += key_le(wk, rs) ? 0 : 1;
+            }
+        }
+        out[jb] = (uint8_t)cnt;
+    }
+}
+
+struct EvictSmem {
+    RadixSmem rs;
+    ScanSmem scan;
+};
+
+template <typename ST>
+__global__ __launch_bounds__(kBNT) void block_evict_kernel(const BlockArgs a)
+{
+    extern __shared__ int32_t dsm[];  // row[npg] | imp[ncand] | freed[m]
+    __shared__ EvictSmem sm;
+    const Geometry& gm = a.g;
+    const State& S = a.s;
+    const int i = blockIdx.x;
+    const int b = a.seq_b[i], n = a.seq_n[i], nc = a.seq_c[i], m = a.seq_m[i];
+    const int js = a.js, Hkv = gm.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int NW = kBNT / 64;
+    const int npg = (n + kPageSize - 1) >> kPageShift;
+    int32_t* row = dsm;
+    int32_t* imp = row + npg;
+    int32_t* freed = imp + nc;
+    int32_t* grow = S.bt + (size_t)b * gm.maxp;
+    for (int j = tid; j < npg; j += kBNT) row[j] = grow[j];
+    for (int jb = tid; jb < nc; jb += kBNT) {
+        int x = 0;
+        for (int h = 0; h < Hkv; ++h) x += S.bimp[((size_t)b * Hkv + h) * gm.maxp + jb];
+        imp[jb] = x;
+    }
+    __syncthreads();
+
+    // the host's candidate range, checked against the stored positions (head
+    // 0's; every head of a page holds the same positions): its first page starts
+    // past the sinks on a page boundary, its last ends before the recent
+    // window, the entry after it reaches into the window, the one before it
+    // holds a sink
+    {
+        int K, HH, W;
+        schedule(a.sc, a.seq_len[i], K, HH, W);
+        const int wlo = a.seq_len[i] - W;  // first window position
+        auto pos0 = [&](int j) { return S.ps[(size_t)row[j] * Hkv * kPageSize]; };
+        bool ok = m >= 1 && m <= nc && js + nc <= npg;
+        if (ok) {
+            const int first = pos0(js);
+            const int last = S.ps[(size_t)row[js + nc - 1] * Hkv * kPageSize + kPageSize - 1];
+            ok = first >= a.sc.n_sink && (first & (kPageSize - 1)) == 0 && last < wlo &&
+                 last - first >= nc * kPageSize - 1;
+            if (ok && js + nc < npg) ok = pos0(js + nc) + kPageSize - 1 >= wlo;
+            if (ok && js > 0) ok = pos0(js - 1) < a.sc.n_sink;
+        }
+        if (!ok) {
+            if (tid == 0) atomicOr(S.err, kErrBlock);
+            return;
+        }
+    }
+
+    auto key_of = [&](int jb, unsigned (&wk)[3]) -> bool {
+        wk[2] = 0;
+        wk[1] = (unsigned)imp[jb];
+        wk[0] = (unsigned)jb;  // older entry first on equal importance
+        return true;
+    };
+    const bool all = m >= nc;
+    if (!all) radix_select<kBNT>(key_of, nc, m, 4, sm.rs);
+    auto gone = [&](int jb) {
+        if (all) return true;
+        unsigned wk[3];
+        key_of(jb, wk);
+        return key_le(wk, sm.rs);
+    };
+
+    // ordered compaction of the candidate entries: thread chunks, block scan
+    const int chunk = (nc + kBNT - 1) / kBNT;
+    const int lo = tid * chunk, hi = min(nc, lo + chunk);
+    int kept = 0;
+    for (int jb = lo; jb < hi; ++jb) kept += gone(jb) ? 0 : 1;
+    int kept_total;
+    int koff = block_excl_scan<kBNT>(kept, sm.scan, &kept_total);
+    int voff = (lo < nc ? lo : nc) - koff;  // freed entries before this chunk
+    for (int jb = lo; jb < hi; ++jb) {
+        const int pg = row[js + jb];
+        if (gone(jb)) {
+            if (voff < m) {  // exactly m keys are selected (the keys are distinct)
+                freed[voff] = pg;
+                S.fstack[a.seq_push[i] + voff] = pg;
+            }
+            ++voff;
+        } else {
+            grow[js + koff] = pg;
+            ++koff;
+        }
+    }
+    if (kept_total != nc - m) {
+        if (tid == 0) atomicOr(S.err, kErrBlock);
+        return;
+    }
+    for (int j = js + nc + tid; j < npg; j += kBNT) grow[j - m] = row[j];
+    for (int j = npg - m + tid; j < npg; j += kBNT) grow[j] = -1;
+    __syncthreads();  // freed[] complete
+
+    // per head: evicted mass, freed slots' positions cleared, retained count
+    ST* scp = reinterpret_cast<ST*>(S.sc);
+    const int nf = m * kPageSize;
+    for (int h = w; h < Hkv; h += NW) {
+        double s = 0.0;
+        for (int q = lane; q < nf; q += 64) {
+            const size_t si = ((size_t)freed[q >> kPageShift] * Hkv + h) * kPageSize + (q & (kPageSize - 1));
+            s += (double)scp[si];
+            S.ps[si] = -1;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+        if (lane == 0) {
+            const size_t u = (size_t)b * Hkv + h;
+            S.emass[u] += s;
+            S.cnt[u] = n - nf;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_block(const BlockArgs& a, hipStream_t st)
+{
+    if (a.nseq <= 0) return hipSuccess;
+    int max_c = 1, max_dyn = 1;
+    for (int i = 0; i < a.nseq; ++i) {
+        const int npg = (a.seq_n[i] + kPageSize - 1) >> kPageShift;
+        max_c = max(max_c, a.seq_c[i]);
+        max_dyn = max(max_dyn, npg + a.seq_c[i] + a.seq_m[i]);
+    }
+    const size_t dyn1 = (size_t)max_c * 4, dyn2 = (size_t)max_dyn * 4;
+    const bool f64 = a.g.score_f64 != 0;
+    const void* k1 = f64 ? (const void*)block_importance_kernel<double> : (const void*)block_importance_kernel<float>;
+    const void* k2 = f64 ? (const void*)block_evict_kernel<double> : (const void*)block_evict_kernel<float>;
+    hipError_t e;
+    static size_t set1[2] = {48 * 1024, 48 * 1024}, set2[2] = {48 * 1024, 48 * 1024};
+    if (dyn1 > set1[f64]) {
+        if ((e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn1)) != hipSuccess)
+            return e;
+        set1[f64] = dyn1;
+    }
+    if (dyn2 > set2[f64]) {
+        if ((e = hipFuncSetAttribute(k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn2)) != hipSuccess)
+            return e;
+        set2[f64] = dyn2;
+    }
+    if (f64)
+        hipLaunchKernelGGL(block_importance_kernel<double>, dim3(a.nseq * a.g.Hkv), dim3(kBNT), dyn1, st, a);
+    else
+        hipLaunchKernelGGL(block_importance_kernel<float>, dim3(a.nseq * a.g.Hkv), dim3(kBNT), dyn1, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (f64)
+        hipLaunchKernelGGL(block_evict_kernel<double>, dim3(a.nseq), dim3(kBNT), dyn2, st, a);
+    else
+        hipLaunchKernelGGL(block_evict_kernel<float>, dim3(a.nseq), dim3(kBNT), dyn2, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace h2o

@@ -650,7 +650,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
     const State& S = a.s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n_att = n + 1;
-    const bool h2o = a.sc.selector == 0;
+    const bool h2o = scored(a.sc.selector);
     ST* scp = reinterpret_cast<ST*>(S.sc);
     int32_t* psp = S.ps;
 

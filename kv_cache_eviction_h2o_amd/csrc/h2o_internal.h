@@ -16,9 +16,18 @@ constexpr int kRowVecs = kRowBytes / 16;  // 16-byte vectors per row = lanes per
 constexpr int kMaxArgBatch = 128;       // per-sequence step parameters travel in the kernel args
                                         // (larger batches read them from device memory)
 constexpr int kLogitLdsBytes = 64 * 1024;  // logits kept in LDS up to this size per unit
+constexpr int kMaxBlockPages = 5120;  // block eviction: block-table row held in LDS (with
+                                      // importance and freed lists: 12 bytes per entry)
 
 // Error bits a kernel may raise in State::err (checked by h2o_read_indices).
-enum : int { kErrSelectCount = 1, kErrNoCandidate = 2, kErrCompact = 4 };
+enum : int { kErrSelectCount = 1, kErrNoCandidate = 2, kErrCompact = 4, kErrBlock = 8 };
+
+// Selectors (the values of h2o_config::selector).
+enum : int { kSelH2O = 0, kSelRandom = 1, kSelBlock = 2 };
+
+// Selectors that keep cumulative attention scores: H2O ranks tokens by them,
+// block eviction ranks whole pages by its heads' heavy hitters among them.
+__host__ __device__ inline bool scored(int selector) { return selector != kSelRandom; }
 
 struct Geometry {
     int B, Hq, Hkv, G, D;
@@ -43,6 +52,8 @@ struct State {  // device pointers owned by the context
     double* emass;     // [B*Hkv] evicted score mass
     int32_t* vinfo;    // [B*Hkv][2] pending (e, victim slot) for the compaction kernel
     int32_t* bt;       // paged: [B][maxp] page of each 16-slot block
+    int32_t* fstack;   // block eviction: [max_pages] free-page stack (depth kept by the host)
+    uint8_t* bimp;     // block eviction: [B*Hkv][maxp] important tokens of each head in each block
     const int32_t* t0; // [B] prompt lengths
     const int64_t* poff;  // [B+1] prompt offsets into the packed prompt arrays
     float* lscr;       // [B*Hkv][G][cap] logits when they do not fit LDS (or null)
@@ -51,7 +62,7 @@ struct State {  // device pointers owned by the context
 };
 
 struct Sched {
-    int selector;  // 0 = H2O, 1 = Random
+    int selector;  // kSelH2O, kSelRandom or kSelBlock
     int n_sink, budget_fixed, hh_fixed, budget_num, budget_den;
     int rand_k, rand_r;
     unsigned long long seed;
@@ -74,11 +85,12 @@ __host__ __device__ inline void schedule(const Sched& s, int len, int& K, int& H
 // slots after the append and prompt length P.
 __host__ __device__ inline int evict_count(const Sched& s, int t, int P, int n_att)
 {
-    if (s.selector == 0) {
+    if (s.selector == kSelH2O) {
         int K, HH, W;
         schedule(s, t + 1, K, HH, W);
         return n_att > K ? n_att - K : 0;
     }
+    if (s.selector == kSelBlock) return 0;  // whole pages go after the step (launch_block)
     return (n_att - P == s.rand_k + s.rand_r) ? s.rand_r : 0;
 }
 
@@ -98,7 +110,27 @@ struct StepArgs {
     int seq_in_args;                // 1: seq_n / seq_p below are valid (B <= kMaxArgBatch)
     int32_t seq_n[kMaxArgBatch];    // retained slots of sequence b before the step
     int32_t seq_p[kMaxArgBatch];    // prompt length of sequence b
-    int32_t newpage[kMaxArgBatch];  // paged: page for the append slot of sequence b, or -1
+    int32_t newpage[kMaxArgBatch];  // paged: page for the append slot of sequence b, or -1;
+                                    // with pop_stack, the free-stack entry that holds it
+    int pop_stack;                  // 1: newpage[b] indexes State::fstack
+};
+
+// Block-granular eviction after a step (h2o_block.hip), for the nseq sequences
+// that lose pages: candidate blocks are block-table entries [js, js + ncand)
+// (whole pages past the sinks' pages and clear of the recent window), m of
+// them go, their pages pushed on the free stack at push[i]...
+struct BlockArgs {
+    Geometry g;
+    State s;
+    Sched sc;
+    int nseq;
+    int js;                        // block-table entries holding sink positions
+    int32_t seq_b[kMaxArgBatch];   // the sequence
+    int32_t seq_len[kMaxArgBatch]; // its length after the step (t + 1)
+    int32_t seq_n[kMaxArgBatch];   // its retained slots after the append (n_att)
+    int32_t seq_c[kMaxArgBatch];   // candidate blocks
+    int32_t seq_m[kMaxArgBatch];   // blocks to evict (1 <= m <= ncand)
+    int32_t seq_push[kMaxArgBatch];  // first free-stack entry its pages go to
 };
 
 struct CompactArgs {
@@ -173,5 +205,6 @@ hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 hipError_t launch_gather_rows(const RowGatherArgs& a, hipStream_t st);
+hipError_t launch_block(const BlockArgs& a, hipStream_t st);  // h2o_block.hip
 
 }  // namespace h2o

@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     const int t = P + a.step;
     const int n = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_n[b] : S.cnt[unit]);
     const int n_att = n + 1;
-    const bool h2o = a.sc.selector == 0;
+    const bool h2o = scored(a.sc.selector);
     const int e = evict_count(a.sc, t, P, n_att);
     const bool inplace_new = a.fused && h2o && e == 1;  // new token goes straight into the hole
 
@@ -86,7 +86,8 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         const int npg = (n + kPageSize - 1) >> kPageShift;
         for (int i = tid; i < npg; i += NT) bts[i] = S.bt[(size_t)b * gm.maxp + i];
         if (!inplace_new && (n & (kPageSize - 1)) == 0) {
-            const int np = a.newpage[b];
+            // the append page: from the host, or (pop_stack) the free-stack entry it names
+            const int np = a.newpage[b] < 0 ? -1 : (a.pop_stack ? S.fstack[a.newpage[b]] : a.newpage[b]);
             if (np < 0) {  // the host did not provide the append page: do nothing
                 if (tid == 0) atomicOr(S.err, kErrCompact);
                 return;
@@ -548,7 +549,7 @@ __global__ void __launch_bounds__(256) gather_kernel(const GatherArgs a)
         if (j < n) {
             const size_t si = sidx(j);
             p = S.ps[si];
-            if (S.sc && a.selector == 0) s = (double)((const ST*)S.sc)[si];
+            if (S.sc && scored(a.selector)) s = (double)((const ST*)S.sc)[si];
         }
         a.opos[(size_t)unit * a.capo + j] = p;
         a.osc[(size_t)unit * a.capo + j] = s;

@@ -77,7 +77,7 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     const int P = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_p[b] : S.t0[b]);
     const int t = P + a.step;
     const int n = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_n[b] : S.cnt[unit]);
-    const bool h2o = a.sc.selector == 0;
+    const bool h2o = scored(a.sc.selector);
     const int e = evict_count(a.sc, t, P, n + 1);
     const bool inplace_new = a.fused && h2o && e == 1;
 

@@ -5,7 +5,9 @@
 // host knows each step's eviction count e_b -- and so the page demand of the
 // paged layout -- without reading anything back from the device: a step is
 // pure enqueue work.  Pages are handed out and taken back here; a new page id
-// travels to the kernel in its arguments.
+// travels to the kernel in its arguments.  Under block eviction the device
+// picks which pages go, so free pages live on a device stack; the host still
+// knows how many pages each step takes and frees, and so the stack's depth.
 #include "h2o.h"
 #include "h2o_internal.h"
 
@@ -35,6 +37,13 @@ struct h2o_ctx {
     std::vector<int> pend_e;  // e_b of the pending step
     std::vector<std::vector<int>> pages;  // paged: page ids of each sequence, in slot order
     std::vector<int> free_pages;
+    // block eviction: pages are tracked by count (the device stack holds the ids)
+    bool block = false;
+    int js = 0;                // block-table entries holding sink positions
+    int ftop = 0;              // depth of the device free-page stack
+    std::vector<int> evb;      // pages evicted so far per sequence
+    BlockArgs pend_blk{};      // the pending step's block eviction (h2o_compact)
+    std::vector<int> pend_n;   // block eviction, step pending: counts before the eviction
     std::vector<void*> allocs;
     std::string err;
 };
@@ -90,13 +99,20 @@ Sched make_sched(const h2o_config& c)
     return s;
 }
 
+// Block-table entries that hold sink positions (block eviction never takes them).
+int sink_pages(int n_sink) { return (n_sink + kPageSize - 1) >> kPageShift; }
+
 // Most slots a (b, h) unit can hold during the run (the pre-eviction set).
 long long slot_capacity(const h2o_config& c, int maxP)
 {
     long long cap;
-    if (c.selector == H2O_SEL_H2O) {
+    if (c.selector == H2O_SEL_H2O || c.selector == H2O_SEL_BLOCK) {
         long long kmax = c.budget_fixed > 0 ? c.budget_fixed
                                              : ((long long)c.max_len * c.budget_num) / c.budget_den;
+        // block eviction: after a step either n <= K, or every candidate page is
+        // gone and what is left is the sinks' pages plus the pages from the
+        // window's first full page on (at most W + 15 positions), W <= K
+        if (c.selector == H2O_SEL_BLOCK) kmax += (long long)sink_pages(c.n_sink) * kPageSize + kPageSize - 1;
         cap = std::max<long long>(maxP, kmax) + 1;
     } else {
         cap = (long long)maxP + c.rand_k + c.rand_r;
@@ -126,7 +142,9 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
         if (plen[b] >= c->max_len) return bad("prompt length must be < max_len");
         maxP = std::max(maxP, (int)plen[b]);
     }
-    if (c->selector == H2O_SEL_H2O) {
+    if (c->selector == H2O_SEL_BLOCK && c->page_size != kPageSize)
+        return bad("block eviction needs the paged layout (page_size 16)");
+    if (c->selector == H2O_SEL_H2O || c->selector == H2O_SEL_BLOCK) {
         if (c->score_dtype != H2O_F32 && c->score_dtype != H2O_F64)
             return bad("score_dtype must be f32 or f64");
         if (c->n_sink < 0) return bad("n_sink must be >= 0");
@@ -156,6 +174,8 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     }
     const long long cap = slot_capacity(*c, maxP);
     if (cap > (1LL << 30)) return bad("slot capacity too large");
+    if (c->selector == H2O_SEL_BLOCK && (cap + kPageSize - 1) / kPageSize > kMaxBlockPages)
+        return bad("block eviction supports at most 5120 pages (81920 slots) per sequence");
     return H2O_OK;
 }
 
@@ -186,6 +206,54 @@ void free_all(h2o_ctx* c)
 {
     for (void* p : c->allocs) (void)hipFree(p);
     c->allocs.clear();
+}
+
+// Retained slots of sequence b as the device holds them now: with a block
+// eviction pending, the step's appended state before any page goes.
+int visible_count(const h2o_ctx* c, int b)
+{
+    return (c->pending && c->block) ? c->pend_n[b] : c->count[b];
+}
+
+// Block eviction after the step that appends position t_b = P_b + step (see
+// h2o_block.hip): per sequence, the candidate pages are the whole pages past
+// the sinks' pages that end before the recent window, less those evicted so
+// far (all of them lay before the window, whose start never moves back), and
+// min(candidates, ceil((n - K) / 16)) of them go.  Updates the host's counts,
+// evicted pages and free-stack depth; returns the launch arguments.
+BlockArgs plan_blocks(h2o_ctx* c)
+{
+    BlockArgs ba{};
+    ba.g = c->g;
+    ba.s = c->s;
+    ba.sc = c->sc;
+    ba.js = c->js;
+    int pushed = 0;
+    for (int b = 0; b < c->g.B; ++b) {
+        const int len = c->plen[b] + c->step + 1;
+        const int n_att = c->count[b] + 1;
+        int K, HH, W;
+        schedule(c->sc, len, K, HH, W);
+        int m = 0, nc = 0;
+        if (n_att > K) {
+            const int kb = len - W > 0 ? (len - W) >> kPageShift : 0;  // pages ending before the window
+            nc = std::max(0, kb - c->js) - c->evb[b];
+            m = std::min(nc, (n_att - K + kPageSize - 1) >> kPageShift);
+        }
+        c->count[b] = n_att - m * kPageSize;
+        if (m <= 0) continue;
+        const int i = ba.nseq++;
+        ba.seq_b[i] = b;
+        ba.seq_len[i] = len;
+        ba.seq_n[i] = n_att;
+        ba.seq_c[i] = nc;
+        ba.seq_m[i] = m;
+        ba.seq_push[i] = c->ftop + pushed;
+        pushed += m;
+        c->evb[b] += m;
+    }
+    c->ftop += pushed;
+    return ba;
 }
 
 int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* out, void* stream,
@@ -227,7 +295,17 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
             a.seq_p[b] = c->plen[b];
         }
     std::vector<int> got;  // pages taken in this call (rolled back on failure)
-    if (c->g.paged) {
+    if (c->block) {
+        // every block-table entry but the last is full: a sequence needs a page
+        // when its count is a multiple of 16; pages come off the device stack
+        int demand = 0;
+        for (int b = 0; b < B; ++b) demand += (c->count[b] & (kPageSize - 1)) == 0 ? 1 : 0;
+        if (demand > c->ftop) return fail(c, H2O_ENOMEM, "KV page pool exhausted");
+        a.pop_stack = 1;
+        int k = 0;
+        for (int b = 0; b < B; ++b)
+            if ((c->count[b] & (kPageSize - 1)) == 0) a.newpage[b] = c->ftop - 1 - k++;
+    } else if (c->g.paged) {
         int demand = 0;
         std::vector<char> need(B, 0);
         for (int b = 0; b < B; ++b) {
@@ -250,6 +328,24 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     }
     hipError_t err = launch_step(a, max_n_att, (hipStream_t)stream);
     if (err != hipSuccess) return hip_fail(c, err, "step kernel launch");
+    if (c->block) {
+        for (int b = 0; b < B; ++b) c->ftop -= (c->count[b] & (kPageSize - 1)) == 0 ? 1 : 0;
+        BlockArgs ba = plan_blocks(c);  // updates counts, evicted pages and the stack depth
+        if (c->ftop > c->cfg.max_pages)  // the pool's pages are all accounted for: cannot happen
+            return fail(c, H2O_EDEVICE, "free-page accounting out of range");
+        if (fused) {
+            if ((err = launch_block(ba, (hipStream_t)stream)) != hipSuccess)
+                return hip_fail(c, err, "block eviction launch");
+            c->step += 1;
+        } else {
+            c->pending = true;
+            c->pend_blk = ba;
+            c->pend_n.resize(B);
+            for (int b = 0; b < B; ++b) c->pend_n[b] = c->count[b];
+            for (int i = 0; i < ba.nseq; ++i) c->pend_n[ba.seq_b[i]] = ba.seq_n[i];
+        }
+        return H2O_OK;
+    }
     if (fused) {
         for (int b = 0; b < B; ++b) {
             c->count[b] = c->count[b] + 1 - e[b];
@@ -429,12 +525,15 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
     g.maxp = g.paged ? (g.cap + kPageSize - 1) / kPageSize : 0;
     g.kv_bf16 = cfg->kv_dtype == H2O_BF16;
     g.kv_i8 = cfg->kv_dtype == H2O_I8;
-    g.score_f64 = cfg->selector == H2O_SEL_H2O && cfg->score_dtype == H2O_F64;
+    g.score_f64 = scored(cfg->selector) && cfg->score_dtype == H2O_F64;
     // GQA groups of 4 or 8 over bf16 rows of 128 run on the matrix cores, with
     // K / V stored in operand order in whole 32-slot tiles
     g.kv_tiles = g.kv_bf16 && g.D == 128 && !g.paged && (g.G == 4 || g.G == 8);
     if (g.kv_tiles) g.cap = (g.cap + 31) & ~31;
     c->sc = make_sched(*cfg);
+    c->block = cfg->selector == H2O_SEL_BLOCK;
+    c->js = sink_pages(cfg->n_sink);
+    c->evb.assign(B, 0);
     const double scale = cfg->scale > 0.f ? (double)cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
     c->qscale = (float)(scale * 1.4426950408889634);  // log2(e)
 
@@ -476,7 +575,7 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
         (rc = dalloc(c, &s.vc, slots_total * row_bytes, "alloc V cache")) ||
         (g.kv_i8 && (rc = dalloc(c, &s.kss, slots_total * 4, "alloc K row scales"))) ||
         (g.kv_i8 && (rc = dalloc(c, &s.vss, slots_total * 4, "alloc V row scales"))) ||
-        (cfg->selector == H2O_SEL_H2O && (rc = dalloc(c, &s.sc, slots_total * sw, "alloc scores"))) ||
+        (scored(cfg->selector) && (rc = dalloc(c, &s.sc, slots_total * sw, "alloc scores"))) ||
         (rc = dalloc(c, &s.ps, slots_total * 4, "alloc positions")) ||
         (rc = dalloc(c, &s.cnt, units * 4, "alloc counts")) ||
         (rc = dalloc(c, &s.emass, units * 8, "alloc evicted mass")) ||
@@ -484,8 +583,12 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
         (rc = dalloc(c, &s.err, 4, "alloc error word")) ||
         (rc = dalloc(c, &t0, (size_t)B * 4, "alloc prompt lengths")) ||
         (rc = dalloc(c, &poff, (size_t)(B + 1) * 8, "alloc prompt offsets")) ||
-        (rc = dalloc(c, &s.iscr, units * 2 * (size_t)g.cap * 4, "alloc compaction lists")) ||
+        (cfg->selector != H2O_SEL_BLOCK &&
+         (rc = dalloc(c, &s.iscr, units * 2 * (size_t)g.cap * 4, "alloc compaction lists"))) ||
         (g.paged && (rc = dalloc(c, &s.bt, (size_t)B * g.maxp * 4, "alloc block table"))) ||
+        (cfg->selector == H2O_SEL_BLOCK &&
+         ((rc = dalloc(c, &s.fstack, (size_t)cfg->max_pages * 4, "alloc free-page stack")) ||
+          (rc = dalloc(c, &s.bimp, units * (size_t)g.maxp, "alloc page importance")))) ||
         ((size_t)g.G * g.cap * 4 > (size_t)kLogitLdsBytes &&
          (rc = dalloc(c, &s.lscr, units * g.G * (size_t)g.cap * 4, "alloc logit scratch")))) {
         std::string why_alloc = c->err;
@@ -511,11 +614,19 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
         std::vector<int32_t> bt((size_t)B * g.maxp, -1);
         for (int b = 0; b < B; ++b)
             for (size_t i = 0; i < c->pages[b].size(); ++i) bt[(size_t)b * g.maxp + i] = c->pages[b][i];
-        if ((e = hipMemcpy(s.bt, bt.data(), bt.size() * 4, hipMemcpyHostToDevice)) != hipSuccess) {
+        if ((e = hipMemcpy(s.bt, bt.data(), bt.size() * 4, hipMemcpyHostToDevice)) != hipSuccess ||
+            (c->block && !c->free_pages.empty() &&
+             (e = hipMemcpy(s.fstack, c->free_pages.data(), c->free_pages.size() * 4, hipMemcpyHostToDevice)) !=
+                 hipSuccess)) {
             int r = hip_fail(nullptr, e, "block table upload");
             free_all(c);
             delete c;
             return r;
+        }
+        if (c->block) {  // from here on the device stack holds the free ids
+            c->ftop = (int)c->free_pages.size();
+            c->free_pages.clear();
+            c->pages.clear();
         }
     }
     LoadArgs la{};
@@ -552,6 +663,13 @@ int h2o_compact(h2o_ctx* c, void* stream)
     if (!c) return H2O_EINVAL;
     if (!c->pending) return fail(c, H2O_ESTATE, "no step is pending compaction");
     DeviceGuard dg(c->device);
+    if (c->block) {
+        hipError_t err = launch_block(c->pend_blk, (hipStream_t)stream);
+        if (err != hipSuccess) return hip_fail(c, err, "block eviction launch");
+        c->pending = false;
+        c->step += 1;
+        return H2O_OK;
+    }
     CompactArgs a{};
     a.g = c->g;
     a.s = c->s;
@@ -570,11 +688,11 @@ int h2o_read_indices(h2o_ctx* c, int32_t* pos, int32_t* count, double* scores, d
                      size_t cap, void* stream)
 {
     if (!c) return H2O_EINVAL;
-    if (c->pending) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
+    if (c->pending && !c->block) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
     if (!pos || !count) return fail(c, H2O_EINVAL, "null pos or count");
     const int B = c->g.B, Hkv = c->g.Hkv;
     int maxc = 0;
-    for (int b = 0; b < B; ++b) maxc = std::max(maxc, c->count[b]);
+    for (int b = 0; b < B; ++b) maxc = std::max(maxc, visible_count(c, b));
     if (cap < (size_t)maxc || cap == 0 || cap > (size_t)(1 << 30))
         return fail(c, H2O_EINVAL, "cap is smaller than a retained count");
     DeviceGuard dg(c->device);
@@ -619,7 +737,7 @@ int h2o_read_indices(h2o_ctx* c, int32_t* pos, int32_t* count, double* scores, d
     std::vector<int> order;
     for (size_t u = 0; u < units; ++u) {
         const int b = (int)(u / Hkv);
-        const int n = c->count[b];
+        const int n = visible_count(c, b);
         if (dcnt[u] != n) return fail(c, H2O_EDEVICE, "device retained count differs from the schedule");
         order.resize(n);
         for (int i = 0; i < n; ++i) order[i] = i;
@@ -635,7 +753,7 @@ int h2o_read_indices(h2o_ctx* c, int32_t* pos, int32_t* count, double* scores, d
         }
         if (evicted_mass) evicted_mass[u] = hem[u];
     }
-    for (int b = 0; b < B; ++b) count[b] = c->count[b];
+    for (int b = 0; b < B; ++b) count[b] = visible_count(c, b);
     return H2O_OK;
 }
 
@@ -643,12 +761,12 @@ int h2o_read_kv(h2o_ctx* c, void* k_rows, void* v_rows, float* k_scale, float* v
                 void* stream)
 {
     if (!c) return H2O_EINVAL;
-    if (c->pending) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
+    if (c->pending && !c->block) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
     if (!k_rows || !v_rows) return fail(c, H2O_EINVAL, "null k_rows or v_rows");
     if (c->g.kv_i8 && (!k_scale || !v_scale)) return fail(c, H2O_EINVAL, "i8 storage needs k_scale and v_scale");
     const int B = c->g.B, Hkv = c->g.Hkv;
     int maxc = 0;
-    for (int b = 0; b < B; ++b) maxc = std::max(maxc, c->count[b]);
+    for (int b = 0; b < B; ++b) maxc = std::max(maxc, visible_count(c, b));
     if (cap < (size_t)maxc || cap == 0 || cap > (size_t)(1 << 30))
         return fail(c, H2O_EINVAL, "cap is smaller than a retained count");
     DeviceGuard dg(c->device);
@@ -710,7 +828,7 @@ int h2o_read_kv(h2o_ctx* c, void* k_rows, void* v_rows, float* k_scale, float* v
     unsigned char* V = (unsigned char*)v_rows;
     std::vector<int> order;
     for (size_t u = 0; u < units; ++u) {
-        const int n = c->count[u / Hkv];
+        const int n = visible_count(c, (int)(u / Hkv));
         order.resize(n);
         for (int i = 0; i < n; ++i) order[i] = i;
         const int32_t* Pp = &hpos[u * cap];
@@ -743,7 +861,10 @@ int h2o_info(const h2o_ctx* c, int32_t* slot_capacity, int32_t* steps_done, int3
     if (steps_done) *steps_done = c->step;
     if (pages_in_use) {
         long long n = 0;
-        for (const auto& p : c->pages) n += (long long)p.size();
+        if (c->block)  // every block-table entry but the last is full
+            for (int b = 0; b < c->g.B; ++b) n += (visible_count(c, b) + kPageSize - 1) >> kPageShift;
+        else
+            for (const auto& p : c->pages) n += (long long)p.size();
         *pages_in_use = (int32_t)n;
     }
     return H2O_OK;

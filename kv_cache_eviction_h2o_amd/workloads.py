@@ -24,7 +24,7 @@ class Workload:
     head_dim: int
     kv_dtype: str                 # storage: "f32" | "bf16" | "i8" (inputs in recipe.kv_dtype)
     score_dtype: str              # "f32" | "f64" (unused by the Random selector)
-    selector: str                 # "h2o" | "random"
+    selector: str                 # "h2o" | "random" | "block" (paged only)
     n_sink: int = 4
     budget_fixed: int = 0         # > 0: fixed budget K
     hh_fixed: int = 0             #        with this many heavy hitters
@@ -84,7 +84,12 @@ ALL = (TINY_H2O, OPT_LAYER, LLAMA_GQA, RANDOM_ATTN, PAGED_MIXED)
 # one fp32 scale per row (inputs stay bf16; see oracle.quantize_rows for the
 # quantisation), the INT8 K/V storage the pages list beside eviction.
 OPT_LAYER_I8 = OPT_LAYER.scaled(name="opt6.7b_layer_20pct_int8", kv_dtype="i8")
-VARIANTS = (OPT_LAYER_I8,)
+
+# Block-granular eviction: the paged workload with whole 16-token pages evicted,
+# those with the fewest heavy-hitter tokens over the sequence's KV heads first
+# ("Attention Sinks and KV cache eviction", section 5).
+PAGED_BLOCK = PAGED_MIXED.scaled(name="paged_mixed_4k-64k_20pct_block", selector="block")
+VARIANTS = (OPT_LAYER_I8, PAGED_BLOCK)
 
 
 def prompt_lengths(w: Workload):

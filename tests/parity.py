@@ -174,10 +174,10 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
     return rep
 
 
-def check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v):
+def check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v, cap=None):
     """The library's stored rows of every retained position against the generator."""
-    pos, cnt, _, _ = cache.read_indices()
-    kr, vr, ks, vs = cache.read_kv()
+    pos, cnt, _, _ = cache.read_indices(cap)
+    kr, vr, ks, vs = cache.read_kv(cap)
     off = np.concatenate([[0], np.cumsum(lens)])
     gk = np.concatenate(gen_k) if gen_k else None  # [steps][B][Hkv][D]
     gv = np.concatenate(gen_v) if gen_v else None
@@ -195,3 +195,213 @@ def check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v):
             else:
                 assert np.array_equal(kr[b, h, i], kx), f"unit {(b, h)} pos {p}: stored K row"
                 assert np.array_equal(vr[b, h, i], vx), f"unit {(b, h)} pos {p}: stored V row"
+
+
+def run_block_parity(w: WL.Workload, n_steps: int, *, lens=None, seqs=None, fused=True, layer=0,
+                     init_scores=None, read_every=1, check_scores=True, device_inputs=False,
+                     stored_rows=True) -> ParityReport:
+    """Block-granular eviction: GPU path vs oracle for whole sequences (every KV
+    head of each checked sequence, since the pages that go depend on all of
+    them).  Per checked step and sequence: outputs, retained positions (the
+    same for every head, whole pages), scores and evicted mass as in
+    run_parity.  The GPU's victim pages must be the oracle's; unfused runs also
+    read the step's pending state (after the append, before any page goes) and
+    check it against the oracle, and a different page choice is accepted only
+    when the oracle's rule applied to the GPU's own pre-eviction scores picks
+    exactly the GPU's pages (a near-tie that fp32 scores resolve the other way);
+    the oracle then adopts them.
+
+    device_inputs: prompts and steps drawn on the device (the benchmark's
+    generator, for full-size batches); the checked sequences' rows are copied
+    back for the oracle.  The cache is left open in the report (rep.cache) for
+    further checks; the caller closes it."""
+    import torch
+    from kv_cache_eviction_h2o_amd import metrics as M
+    assert w.selector == "block" and w.page_size == 16
+    lens = list(lens) if lens is not None else WL.prompt_lengths(w)
+    B, Hq, Hkv, G, D = w.batch, w.n_q_heads, w.n_kv_heads, w.group, w.head_dim
+    assert len(lens) == B
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    say(f"[block parity] {w.name} B={B} Hq={Hq} Hkv={Hkv} lens={lens[:6]}{'...' if B > 6 else ''} "
+        f"steps={n_steps} fused={fused} seqs={seqs if len(seqs) <= 8 else len(seqs)}")
+    off = np.concatenate([[0], np.cumsum(lens)])
+    if device_inputs:
+        from kv_cache_eviction_h2o_amd import _lib as L
+        pk, pv = S.device_prompt_kv(w.recipe, layer, lens, Hkv)
+        cfg = L.config_from_workload(w, max_len=max(lens) + n_steps + 1)
+        cfg.max_pages = L.pages_needed(lens, n_steps, cfg)
+        cache = L.H2OCache(cfg, lens, pk, pv)
+        K = _Rows(off, {b: _host_bits(pk[off[b]:off[b + 1]]) for b in seqs})
+        V = _Rows(off, {b: _host_bits(pv[off[b]:off[b + 1]]) for b in seqs})
+        del pk, pv
+    else:
+        cache, K, V = make_cache(w, lens, n_steps, layer, init_scores)
+    units = [(b, h) for b in seqs for h in range(Hkv)]
+    ocfg = O.cfg_from_workload(w)
+    orc = {}
+    for (b, h) in units:
+        isc = None if init_scores is None else init_scores[off[b]:off[b + 1], h]
+        orc[(b, h)] = O.Unit(ocfg, b, h, oracle_rows(w, K[off[b]:off[b + 1], h]),
+                             oracle_rows(w, V[off[b]:off[b + 1], h]),
+                             lens[b] + n_steps + 1, init_scores=isc)
+    rep = ParityReport(units=len(units))
+    # reads sized by the host mirror of the counts (the library rejects a short cap)
+    mirror = [M.retained_counts(w, P, n_steps) for P in lens]
+    cap = int(max(c["count"].max() for c in mirror))
+    cap_pre = int(max(c["n_att"].max() for c in mirror))
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    win = 256
+    gen_k, gen_v = [], []
+    for s0 in range(0, n_steps, win):
+        ns = min(win, n_steps - s0)
+        t0 = [p + s0 for p in lens]
+        if device_inputs:
+            qd, kd, vd = S.device_step_window(w.recipe, layer, t0, ns, Hq, Hkv)
+            q, k, v = qd.cpu().numpy(), _host_bits(kd), _host_bits(vd)
+        else:
+            q, k, v = S.step_window(w.recipe, layer, t0, ns, Hq, Hkv)
+            qd = torch.from_numpy(q).cuda()
+            kd, vd = to_dev(k, w.recipe.kv_dtype), to_dev(v, w.recipe.kv_dtype)
+        gen_k.append(k)
+        gen_v.append(v)
+        for i in range(ns):
+            s = s0 + i
+            check = (s % read_every == 0) or s == n_steps - 1
+            pre = None
+            if fused:
+                cache.step_compact(qd[i], kd[i], vd[i], out)
+            else:
+                cache.step(qd[i], kd[i], vd[i], out)
+                if check:
+                    pre = cache.read_indices(cap_pre)
+                cache.compact()
+            if not check:
+                for (b, h) in units:
+                    orc[(b, h)].attend(q[i, b, h * G:(h + 1) * G], oracle_rows(w, k[i, b, h]),
+                                       oracle_rows(w, v[i, b, h]))
+                for b in seqs:
+                    us = [orc[(b, h)] for h in range(Hkv)]
+                    vic = O.block_select(us, page=16)
+                    for u in us:
+                        u.evict(vic)
+                continue
+            o_gpu = out.cpu().numpy()
+            pos, cnt, sc, em = cache.read_indices(cap)
+            for (b, h) in units:
+                u = orc[(b, h)]
+                o_ref = u.attend(q[i, b, h * G:(h + 1) * G], oracle_rows(w, k[i, b, h]),
+                                 oracle_rows(w, v[i, b, h]))
+                og = o_gpu[b, h * G:(h + 1) * G].astype(np.float64)
+                err = np.max(np.abs(og - o_ref), axis=1) / np.maximum(np.max(np.abs(o_ref), axis=1), 1e-30)
+                rep.max_out_err = max(rep.max_out_err, float(err.max()))
+                assert np.all(err <= OUT_TOL), f"step {s} unit {(b, h)}: output rel err {err.max():.3g}"
+            for b in seqs:
+                us = [orc[(b, h)] for h in range(Hkv)]
+                length = lens[b] + s + 1
+                pre_pos = us[0].state()[0]
+                if pre is not None:  # the pending state: the append done, no page gone yet
+                    ppos, pcnt, psc, _ = pre
+                    npre = int(pcnt[b])
+                    for h, u in enumerate(us):
+                        o_pos, o_sc, _ = u.state()
+                        assert np.array_equal(ppos[b, h, :npre], o_pos), f"step {s} seq {b} head {h}: pending set"
+                        if check_scores:
+                            serr = np.abs(psc[b, h, :npre] - o_sc)
+                            assert np.all(serr <= SCORE_TOL * np.abs(o_sc) + 1e-9), \
+                                f"step {s} seq {b} head {h}: pending score err"
+                n = int(cnt[b])
+                gpos = pos[b, 0, :n]
+                for h in range(1, Hkv):
+                    assert np.array_equal(pos[b, h, :n], gpos), f"step {s} seq {b}: heads retain different sets"
+                assert set(gpos.tolist()) <= set(pre_pos.tolist()), f"step {s} seq {b}: unknown positions"
+                gvic = sorted(set(pre_pos.tolist()) - set(gpos.tolist()))
+                ovic = O.block_select(us, page=16)
+                if list(ovic) != gvic:
+                    assert pre is not None, (
+                        f"step {s} seq {b}: victim pages differ (fused run; oracle "
+                        f"{sorted(set(np.asarray(ovic) // 16))[:8]} gpu {sorted(set(np.asarray(gvic) // 16))[:8]})")
+                    ppos, pcnt, psc, _ = pre
+                    npre = int(pcnt[b])
+                    live = np.zeros(length, dtype=np.uint8)
+                    live[ppos[b, 0, :npre]] = 1
+                    gsc = np.zeros((Hkv, length))
+                    for h in range(Hkv):
+                        gsc[h, ppos[b, h, :npre]] = psc[b, h, :npre]
+                    replay = O.block_rank(ocfg, length, live, gsc, page=16)
+                    assert list(replay) == gvic, (f"step {s} seq {b}: GPU pages are not the rule's choice "
+                                                  f"on its own scores")
+                    vic = np.array(gvic, dtype=np.int32)
+                    rep.adopted += 1
+                else:
+                    vic = ovic
+                for h, u in enumerate(us):
+                    u.evict(vic)
+                    u.check()
+                    o_pos, o_sc, o_em = u.state()
+                    assert np.array_equal(o_pos, pos[b, h, :n]), f"step {s} seq {b} head {h}: retained sets differ"
+                    if check_scores:
+                        serr = np.abs(sc[b, h, :n] - o_sc)
+                        assert np.all(serr <= SCORE_TOL * np.abs(o_sc) + 1e-9), \
+                            f"step {s} seq {b} head {h}: score err {np.max(serr / (np.abs(o_sc) + 1e-9)):.3g}"
+                        rep.max_score_err = max(rep.max_score_err,
+                                                float(np.max(serr / np.maximum(np.abs(o_sc), 1e-30))))
+                        assert abs(em[b, h] - o_em) <= SCORE_TOL * max(1.0, o_em), \
+                            f"step {s} seq {b} head {h}: evicted mass {em[b, h]} vs {o_em}"
+                rep.evictions += len(gvic) * Hkv
+            rep.steps += 1
+    if stored_rows:
+        check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v, cap=cap)
+    rep.cache = cache
+    say(f"[block parity] ok: checked {rep.steps} steps x {len(seqs)} sequences, max out err "
+        f"{rep.max_out_err:.2e}, max score err {rep.max_score_err:.2e}, evicted tokens x heads "
+        f"{rep.evictions}, near-ties adopted {rep.adopted}")
+    return rep
+
+
+class _Rows:
+    """Packed prompt rows [sum P_b][Hkv][D] of a few sequences (the rest absent),
+    indexed like the full array."""
+
+    def __init__(self, off, parts):
+        self.off, self.parts = off, parts
+
+    def __getitem__(self, idx):
+        r, h = idx
+        if isinstance(r, slice):
+            b = int(np.searchsorted(self.off, r.start, side="right") - 1)
+            assert r.stop == self.off[b + 1]
+            return self.parts[b][:, h]
+        b = int(np.searchsorted(self.off, r, side="right") - 1)
+        return self.parts[b][r - self.off[b], h]
+
+
+def _host_bits(t):
+    """A bf16 / fp32 device tensor as host cache-dtype values (bf16 as uint16 bits)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def block_properties(w: WL.Workload, cache, lens, steps_done: int, cap=None):
+    """What holds for every sequence after any step of block eviction, at any
+    size: every head retains the same positions; they are whole 16-position
+    pages (the last may be partial); the sinks and the recent window are all
+    retained; and the count is <= K_t unless no candidate page is left."""
+    pos, cnt, _, _ = cache.read_indices(cap)
+    ocfg = O.cfg_from_workload(w)
+    for b in range(w.batch):
+        n = int(cnt[b])
+        length = lens[b] + steps_done
+        p = pos[b, 0, :n]
+        assert all(np.array_equal(pos[b, h, :n], p) for h in range(w.n_kv_heads)), f"seq {b}: head sets differ"
+        K, HH, W = O.schedule(ocfg, length)
+        pages = p // 16
+        up, c = np.unique(pages, return_counts=True)
+        last = p[n - c[-1]:]
+        assert np.all(c[:-1] == 16) and np.array_equal(last, up[-1] * 16 + np.arange(c[-1])), \
+            f"seq {b}: a page is not whole"
+        assert set(range(min(w.n_sink, length))) <= set(p.tolist()), f"seq {b}: a sink is gone"
+        assert set(range(max(0, length - W), length)) <= set(p.tolist()), f"seq {b}: the window is not whole"
+        cands = [k for k in up if k * 16 >= w.n_sink and k * 16 + 15 < length - W]
+        assert n <= K or not cands, f"seq {b}: {n} > K = {K} with {len(cands)} candidate pages"

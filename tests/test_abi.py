@@ -82,6 +82,11 @@ GOOD = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kv_dtype="bf16", s
     (dict(page_size=16, kv_dtype="f32", head_dim=64, max_pages=64), "bf16"),
     (dict(max_len=100), "max_len"),
     (dict(scale=-1.0), "scale"),
+    (dict(selector="block"), "paged layout"),
+    (dict(selector="block", page_size=16, max_pages=64, hh_fixed=61), "hh_fixed"),
+    (dict(selector="block", page_size=16, max_pages=64, score_dtype="bf16"), "score_dtype"),
+    (dict(selector="block", page_size=16, max_pages=64, budget_fixed=0, budget_num=1, budget_den=5,
+          max_len=500000), "5120 pages"),
 ])
 def test_invalid_config_rejected_before_device(lib, bad, msg):
     cfg = L.make_config(**{**GOOD, **bad})
@@ -128,6 +133,16 @@ def test_page_pool_sizing_host_logic():
     lens = [4096, 65536]
     need = L.pages_needed(lens, 65, cfg)
     assert need >= sum((p + 15) // 16 for p in lens)
+
+
+def test_block_pool_sizing_covers_capacity():
+    # block eviction holds up to K + a sink page + a page past the window's start
+    cfg = L.make_config(**{**GOOD, "selector": "block", "budget_fixed": 0, "budget_num": 1,
+                           "budget_den": 5, "page_size": 16, "max_pages": 1, "max_len": 70000})
+    lens = [4096, 65536]
+    need = L.pages_needed(lens, 65, cfg)
+    k_end = [(p + 65) // 5 for p in lens]
+    assert need >= sum((max(p, k + 16 + 15) + 1 + 15) // 16 for p, k in zip(lens, k_end))
 
 
 def _prefill(lib, cfg, lens, ptr=16):

@@ -3,8 +3,10 @@ import json
 import os
 
 import numpy as np
+import pytest
 
 from kv_cache_eviction_h2o_amd import metrics as M
+from kv_cache_eviction_h2o_amd import workloads as WL
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -41,3 +43,35 @@ def test_step_bytes_model():
                          score_bytes=4)
     assert tot == 3 * int(M.unit_step_bytes(10, head_dim=128, kv_elem=2, group=1, score_bytes=4)
                           + M.unit_step_bytes(20, head_dim=128, kv_elem=2, group=1, score_bytes=4))
+
+
+@pytest.mark.parametrize("kw,lens,steps", [
+    (dict(), [300, 517, 1100], 80),
+    (dict(n_sink=0, budget_fixed=64, hh_fixed=0), [100, 333], 120),
+    (dict(n_sink=20, budget_fixed=96, hh_fixed=76), [90, 260], 120),
+    (dict(budget_fixed=200, hh_fixed=100), [40, 700], 150),
+])
+def test_block_count_mirror_matches_oracle(kw, lens, steps):
+    """The host's count mirror under block eviction (which the library's page
+    accounting shares: the number of candidate pages from the schedule alone)
+    against oracle runs that choose pages from real scores."""
+    import oracle as O
+    from kv_cache_eviction_h2o_amd import synth as S
+    w = WL.PAGED_BLOCK.scaled(batch=len(lens), n_q_heads=2, n_kv_heads=2, head_dim=64,
+                              kv_dtype="f32", recipe=S.Recipe(seed=5, head_dim=64, kv_dtype="f32"), **kw)
+    K, V = S.prompt_kv(w.recipe, 0, lens, 2)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    cfg = O.cfg_from_workload(w)
+    q, k, v = S.step_window(w.recipe, 0, lens, steps, 2, 2)
+    for b, P in enumerate(lens):
+        us = [O.Unit(cfg, b, h, K[off[b]:off[b + 1], h], V[off[b]:off[b + 1], h], P + steps + 1)
+              for h in range(2)]
+        mirror = M.retained_counts(w, P, steps)
+        for s in range(steps):
+            for h, u in enumerate(us):
+                u.attend(q[s, b, h:h + 1], k[s, b, h], v[s, b, h])
+            vic = O.block_select(us, page=16)
+            assert len(vic) == 16 * mirror["pages"][s], f"seq {b} step {s}"
+            for u in us:
+                u.evict(vic)
+            assert len(us[0].state()[0]) == mirror["count"][s], f"seq {b} step {s}"
