@@ -97,7 +97,7 @@ typedef enum {
  * importance: the older page first).  Pages hold 16 consecutive positions and
  * never move, so after a step a sequence holds either <= K tokens or no
  * candidate page.  Slot capacity: max(P, K_max + 16 * ceil(n_sink / 16) + 15) + 1
- * tokens, at most 5120 pages per sequence. */
+ * tokens, at most 5120 pages per sequence; at most 1024 KV heads. */
 enum { H2O_SEL_H2O = 0, H2O_SEL_RANDOM = 1, H2O_SEL_BLOCK = 2 };
 enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F64 = 2, H2O_I8 = 3 };
 

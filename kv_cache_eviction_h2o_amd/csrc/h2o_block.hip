@@ -25,8 +25,9 @@
 //   block_evict_kernel  one workgroup per sequence: importance summed over the
 //       heads, radix select of the m smallest (importance, entry) keys, the
 //       row compacted (kept entries in order), the freed pages pushed on the
-//       free stack, and per head the evicted score mass added and the freed
-//       slots' positions cleared.
+//       free stack, and per head the evicted score mass added and the count
+//       set.  A freed page's slots keep their old contents until an append
+//       reuses them; nothing reads a slot past a unit's count.
 #include "h2o_device.h"
 
 namespace h2o {
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kBNT) void block_importance_kernel(const BlockArgs 
     };
     const bool all_imp = e <= 0, none_imp = e >= c;
     if (!all_imp && !none_imp) radix_select<kBNT>(key_of, c, e, sizeof(ST) == 4 ? 4 : 0, rs);
-    uint8_t* out = S.bimp + ((size_t)b * Hkv + h) * gm.maxp;
+    uint8_t* out = S.bimp + ((size_t)b * Hkv + h) * bimp_stride(gm.maxp);
     for (int jb = tid; jb < nc; jb += kBNT) {
         int cnt = all_imp ? kPageSize : 0;
         if (!all_imp && !none_imp) {
@@ -98,25 +99,41 @@ struct EvictSmem {
 template <typename ST>
 __global__ __launch_bounds__(kBNT) void block_evict_kernel(const BlockArgs a)
 {
-    extern __shared__ int32_t dsm[];  // row[npg] | imp[ncand] | freed[m]
+    // dynamic LDS: hsum[Hkv] (fp64) | row[npg] | imp[ncand] | freed[m]
+    extern __shared__ double dsm_d[];
     __shared__ EvictSmem sm;
     const Geometry& gm = a.g;
     const State& S = a.s;
     const int i = blockIdx.x;
     const int b = a.seq_b[i], n = a.seq_n[i], nc = a.seq_c[i], m = a.seq_m[i];
     const int js = a.js, Hkv = gm.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    constexpr int NW = kBNT / 64;
+    const int tid = threadIdx.x;
     const int npg = (n + kPageSize - 1) >> kPageShift;
-    int32_t* row = dsm;
+    double* hsum = dsm_d;
+    int32_t* row = reinterpret_cast<int32_t*>(hsum + Hkv);
     int32_t* imp = row + npg;
     int32_t* freed = imp + nc;
     int32_t* grow = S.bt + (size_t)b * gm.maxp;
     for (int j = tid; j < npg; j += kBNT) row[j] = grow[j];
-    for (int jb = tid; jb < nc; jb += kBNT) {
-        int x = 0;
-        for (int h = 0; h < Hkv; ++h) x += S.bimp[((size_t)b * Hkv + h) * gm.maxp + jb];
-        imp[jb] = x;
+    for (int h = tid; h < Hkv; h += kBNT) hsum[h] = 0.0;
+    // importance of each candidate entry: the heads' counts (bytes, rows of
+    // bimp_stride) read four entries per word and summed in two 16-bit lanes
+    // per word (even entries, odd entries): a count is at most 16 per head
+    const int bstr = bimp_stride(gm.maxp);
+    const uint32_t* bw = reinterpret_cast<const uint32_t*>(S.bimp + (size_t)b * Hkv * bstr);
+    for (int wj = tid; wj < (nc + 3) / 4; wj += kBNT) {
+        uint32_t ev = 0, od = 0;
+#pragma unroll 8
+        for (int h = 0; h < Hkv; ++h) {
+            const uint32_t x = bw[(size_t)h * (bstr / 4) + wj];
+            ev += x & 0x00ff00ffu;
+            od += (x >> 8) & 0x00ff00ffu;
+        }
+        const int j0 = 4 * wj;
+        const int v[4] = {(int)(ev & 0xffffu), (int)(od & 0xffffu), (int)(ev >> 16), (int)(od >> 16)};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (j0 + k < nc) imp[j0 + k] = v[k];
     }
     __syncthreads();
 
@@ -145,14 +162,22 @@ __global__ __launch_bounds__(kBNT) void block_evict_kernel(const BlockArgs a)
         }
     }
 
+    // key: importance, then the entry (older first), packed in one word; the
+    // radix passes start at the key's highest nonzero byte
+    constexpr int kEntryBits = 13;  // entries < kMaxBlockPages <= 8192
+    static_assert(kMaxBlockPages <= (1 << kEntryBits), "entry field too narrow");
     auto key_of = [&](int jb, unsigned (&wk)[3]) -> bool {
         wk[2] = 0;
-        wk[1] = (unsigned)imp[jb];
-        wk[0] = (unsigned)jb;  // older entry first on equal importance
+        wk[1] = 0;
+        wk[0] = ((unsigned)imp[jb] << kEntryBits) | (unsigned)jb;
         return true;
     };
     const bool all = m >= nc;
-    if (!all) radix_select<kBNT>(key_of, nc, m, 4, sm.rs);
+    if (!all) {
+        const unsigned top = ((unsigned)(kPageSize * Hkv) << kEntryBits) | ((1u << kEntryBits) - 1);
+        const int bytes = (32 - __builtin_clz(top) + 7) / 8;  // 1..4
+        radix_select<kBNT>(key_of, nc, m, 12 - bytes, sm.rs);
+    }
     auto gone = [&](int jb) {
         if (all) return true;
         unsigned wk[3];
@@ -189,23 +214,28 @@ __global__ __launch_bounds__(kBNT) void block_evict_kernel(const BlockArgs a)
     for (int j = npg - m + tid; j < npg; j += kBNT) grow[j] = -1;
     __syncthreads();  // freed[] complete
 
-    // per head: evicted mass, freed slots' positions cleared, retained count
-    ST* scp = reinterpret_cast<ST*>(S.sc);
+    // evicted score mass per head over all (head, freed slot) pairs at once;
+    // a thread's run of pairs within one head is summed before it goes to LDS
+    const ST* scp = reinterpret_cast<const ST*>(S.sc);
     const int nf = m * kPageSize;
-    for (int h = w; h < Hkv; h += NW) {
-        double s = 0.0;
-        for (int q = lane; q < nf; q += 64) {
-            const size_t si = ((size_t)freed[q >> kPageShift] * Hkv + h) * kPageSize + (q & (kPageSize - 1));
-            s += (double)scp[si];
-            S.ps[si] = -1;
+    const long long pairs = (long long)Hkv * nf;
+    double acc = 0.0;
+    int hc = -1;
+    for (long long idx = tid; idx < pairs; idx += kBNT) {
+        const int h = (int)(idx / nf), q = (int)(idx - (long long)h * nf);
+        if (h != hc) {
+            if (hc >= 0) atomicAdd(&hsum[hc], acc);
+            acc = 0.0;
+            hc = h;
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-        if (lane == 0) {
-            const size_t u = (size_t)b * Hkv + h;
-            S.emass[u] += s;
-            S.cnt[u] = n - nf;
-        }
+        acc += (double)scp[((size_t)freed[q >> kPageShift] * Hkv + h) * kPageSize + (q & (kPageSize - 1))];
+    }
+    if (hc >= 0) atomicAdd(&hsum[hc], acc);
+    __syncthreads();
+    for (int h = tid; h < Hkv; h += kBNT) {
+        const size_t u = (size_t)b * Hkv + h;
+        S.emass[u] += hsum[h];
+        S.cnt[u] = n - nf;
     }
 }
 
@@ -220,7 +250,7 @@ hipError_t launch_block(const BlockArgs& a, hipStream_t st)
         max_c = max(max_c, a.seq_c[i]);
         max_dyn = max(max_dyn, npg + a.seq_c[i] + a.seq_m[i]);
     }
-    const size_t dyn1 = (size_t)max_c * 4, dyn2 = (size_t)max_dyn * 4;
+    const size_t dyn1 = (size_t)max_c * 4, dyn2 = (size_t)a.g.Hkv * 8 + (size_t)max_dyn * 4;
     const bool f64 = a.g.score_f64 != 0;
     const void* k1 = f64 ? (const void*)block_importance_kernel<double> : (const void*)block_importance_kernel<float>;
     const void* k2 = f64 ? (const void*)block_evict_kernel<double> : (const void*)block_evict_kernel<float>;

@@ -18,6 +18,8 @@ constexpr int kMaxArgBatch = 128;       // per-sequence step parameters travel i
 constexpr int kLogitLdsBytes = 64 * 1024;  // logits kept in LDS up to this size per unit
 constexpr int kMaxBlockPages = 5120;  // block eviction: block-table row held in LDS (with
                                       // importance and freed lists: 12 bytes per entry)
+// Row stride of State::bimp: whole 16-byte groups, so rows can be read in words.
+__host__ __device__ inline int bimp_stride(int maxp) { return (maxp + 15) & ~15; }
 
 // Error bits a kernel may raise in State::err (checked by h2o_read_indices).
 enum : int { kErrSelectCount = 1, kErrNoCandidate = 2, kErrCompact = 4, kErrBlock = 8 };
@@ -53,7 +55,8 @@ struct State {  // device pointers owned by the context
     int32_t* vinfo;    // [B*Hkv][2] pending (e, victim slot) for the compaction kernel
     int32_t* bt;       // paged: [B][maxp] page of each 16-slot block
     int32_t* fstack;   // block eviction: [max_pages] free-page stack (depth kept by the host)
-    uint8_t* bimp;     // block eviction: [B*Hkv][maxp] important tokens of each head in each block
+    uint8_t* bimp;     // block eviction: [B*Hkv][bimp_stride(maxp)] important tokens of each
+                       // head in each candidate block-table entry
     const int32_t* t0; // [B] prompt lengths
     const int64_t* poff;  // [B+1] prompt offsets into the packed prompt arrays
     float* lscr;       // [B*Hkv][G][cap] logits when they do not fit LDS (or null)

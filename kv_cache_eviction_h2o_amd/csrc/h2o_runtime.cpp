@@ -144,6 +144,8 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     }
     if (c->selector == H2O_SEL_BLOCK && c->page_size != kPageSize)
         return bad("block eviction needs the paged layout (page_size 16)");
+    if (c->selector == H2O_SEL_BLOCK && c->n_kv_heads > 1024)
+        return bad("block eviction supports at most 1024 KV heads");
     if (c->selector == H2O_SEL_H2O || c->selector == H2O_SEL_BLOCK) {
         if (c->score_dtype != H2O_F32 && c->score_dtype != H2O_F64)
             return bad("score_dtype must be f32 or f64");
@@ -588,7 +590,7 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
         (g.paged && (rc = dalloc(c, &s.bt, (size_t)B * g.maxp * 4, "alloc block table"))) ||
         (cfg->selector == H2O_SEL_BLOCK &&
          ((rc = dalloc(c, &s.fstack, (size_t)cfg->max_pages * 4, "alloc free-page stack")) ||
-          (rc = dalloc(c, &s.bimp, units * (size_t)g.maxp, "alloc page importance")))) ||
+          (rc = dalloc(c, &s.bimp, units * (size_t)bimp_stride(g.maxp), "alloc page importance")))) ||
         ((size_t)g.G * g.cap * 4 > (size_t)kLogitLdsBytes &&
          (rc = dalloc(c, &s.lscr, units * g.G * (size_t)g.cap * 4, "alloc logit scratch")))) {
         std::string why_alloc = c->err;

@@ -83,6 +83,7 @@ GOOD = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kv_dtype="bf16", s
     (dict(max_len=100), "max_len"),
     (dict(scale=-1.0), "scale"),
     (dict(selector="block"), "paged layout"),
+    (dict(selector="block", page_size=16, max_pages=64, n_q_heads=2048, n_kv_heads=2048), "1024 KV heads"),
     (dict(selector="block", page_size=16, max_pages=64, hh_fixed=61), "hh_fixed"),
     (dict(selector="block", page_size=16, max_pages=64, score_dtype="bf16"), "score_dtype"),
     (dict(selector="block", page_size=16, max_pages=64, budget_fixed=0, budget_num=1, budget_den=5,
