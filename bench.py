@@ -203,7 +203,8 @@ def cpu_baseline(w, n_att: int, seconds: float):
             units.append(O.Unit(cfg, b, h, S.cache_to_f64(w.recipe, Kp[b * K:(b + 1) * K, h]),
                                 S.cache_to_f64(w.recipe, Vp[b * K:(b + 1) * K, h]), K + max_steps + 1))
     threads = min(os.cpu_count() or 1, len(units))
-    done, t_used = 0, 0.0
+    block = w.selector == "block"
+    done, t_used, tokens = 0, 0.0, 0
     win = 32
     while t_used < seconds and done < max_steps:
         q, k, v = S.step_window(w.recipe, 0, [K + done] * B, win, Hq, Hkv)
@@ -212,17 +213,26 @@ def cpu_baseline(w, n_att: int, seconds: float):
             ks = [S.cache_to_f64(w.recipe, k[i, b, h]) for b in range(B) for h in range(Hkv)]
             vs = [S.cache_to_f64(w.recipe, v[i, b, h]) for b in range(B) for h in range(Hkv)]
             qs = [np.ascontiguousarray(x, np.float64) for x in qs]
+            tokens += sum(len(units[b * Hkv].state()[0]) + 1 for b in range(B))
             t0 = time.perf_counter()
             O.step_many(units, qs, ks, vs, threads)
+            if block:  # whole pages go per sequence, chosen over its heads
+                for b in range(B):
+                    us = units[b * Hkv:(b + 1) * Hkv]
+                    vic = O.block_select(us)
+                    for u in us:
+                        u.evict(vic)
             t_used += time.perf_counter() - t0
             done += 1
             if t_used >= seconds:
                 break
-    tokens = done * B * n_att
+    how = ("then the block selection of every sequence (one thread)" if block
+           else "one token evicted per unit and step")
     return {"value": tokens / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"one layer ({B} sequences x {Hkv} KV heads) at the window's retained "
-                       f"length n_att={n_att}, {done} decode steps, fp64 oracle on {threads} "
-                       f"threads; {t_used:.1f} s of CPU step time (input conversion excluded)")}
+            "sample": (f"one layer ({B} sequences x {Hkv} KV heads) with a fixed budget at the "
+                       f"window's retained length n_att={n_att}, {done} decode steps, fp64 oracle "
+                       f"steps on {threads} threads, {how}; {t_used:.1f} s of CPU step time "
+                       f"(input conversion excluded)")}
 
 
 PEAK_BF16_TFLOPS = 2500.0
