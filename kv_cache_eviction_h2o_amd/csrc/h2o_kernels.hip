@@ -407,23 +407,14 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         Mg[g] = M;
         invLg[g] = 1.0f / L;
     }
-    for (int idx = tid; idx < G * 16; idx += NT) {
-        const int g = idx >> 4, sb = idx & 15;
-        float acc[EPL];
+    // the output: one element per thread, the waves' partial sums rescaled to
+    // the common maximum (consecutive threads read consecutive LDS words)
+    for (int idx = tid; idx < G * DR; idx += NT) {
+        const int g = idx / DR, d = idx - g * DR;
+        float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float f = fast_exp2(red_m[ww][g] - Mg[g]);
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) acc[i] += red_o[ww][g][sb * EPL + i] * f;
-        }
-        float4* op = reinterpret_cast<float4*>(a.out + ((size_t)b * gm.Hq + (size_t)h * G + g) * DR +
-                                               sb * EPL);
-#pragma unroll
-        for (int i = 0; i < EPL / 4; ++i)
-            op[i] = make_float4(acc[4 * i] * invLg[g], acc[4 * i + 1] * invLg[g],
-                                acc[4 * i + 2] * invLg[g], acc[4 * i + 3] * invLg[g]);
+        for (int ww = 0; ww < NW; ++ww) acc += red_o[ww][g][d] * fast_exp2(red_m[ww][g] - Mg[g]);
+        a.out[((size_t)b * gm.Hq + (size_t)h * G + g) * DR + d] = acc * invLg[g];
     }
 
     step_tail<NT, G, PF, ST, PAGED, KVL>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit, lstride,
