@@ -56,47 +56,60 @@ struct RowsTune {
     static constexpr int PT = G >= 4 ? 1 : 4 / G;
 };
 
+constexpr int kRCK = 4;  // rows pass: 16-key tiles per LDS chunk
+
 template <int G>
 __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
 {
     constexpr int PT = RowsTune<G>::PT;
-    const int unit = blockIdx.y, b = unit / a.Hkv, h = unit - b * a.Hkv;
+    // K chunks in B-operand order: [buffer][tile][k-step][lane], lane (lg, lc)
+    // holding key 16 tile + lc, elements 32 kb + 8 lg .. +8
+    __shared__ uint4 ksm[2][kRCK][4][64];
+    // workgroups go to the XCDs round-robin by linear id: with the unit as the
+    // fast grid index every XCD gets every position block of an eighth of the
+    // units; the longest causal prefixes (the last blocks) are dispatched first
+    const int unit = blockIdx.x, b = unit / a.Hkv, h = unit - b * a.Hkv;
+    const int pblk = (int)gridDim.y - 1 - (int)blockIdx.y;
     const int P = a.seq_p[b], lo = a.seq_lo[b];
     const int64_t off = a.seq_off[b];
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lc = lane & 15, lg = lane >> 4;
-    const int base = (blockIdx.x * 4 + w) * 8 * PT;  // this wave's first position
-    if (base >= P || base + 8 * PT <= lo) return;   // no row of this wave counts
+    const int wg_base = pblk * 4 * 8 * PT;
+    if (wg_base >= P || wg_base + 4 * 8 * PT <= lo) return;  // no row of this workgroup counts
+    const int base = wg_base + w * 8 * PT;                   // this wave's first position
+    const bool active = base < P && base + 8 * PT > lo;      // uniform over the wave
 
     // A operands: tile pt, lane (lg, lc) holds d = 32 kb + 8 lg .. +8 of row lc,
     // i.e. of position base + 8 pt + lc / 2, part lc & 1 (hi / lo)
     const bool lo_part = (lc & 1) != 0;
     bf16x8 qop[PT][G][4];
+    if (active) {
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-        const int t8 = base / 8 + pt;
-        const int prow = min(base + 8 * pt + (lc >> 1), P - 1);
+        for (int pt = 0; pt < PT; ++pt) {
+            const int t8 = base / 8 + pt;
+            const int prow = min(base + 8 * pt + (lc >> 1), P - 1);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float* qr = a.q + ((size_t)(off + prow) * a.Hq + (size_t)h * G + g) * 128;
+            for (int g = 0; g < G; ++g) {
+                const float* qr = a.q + ((size_t)(off + prow) * a.Hq + (size_t)h * G + g) * 128;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const float4 x0 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg);
-                const float4 x1 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg + 4);
-                const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                for (int kb = 0; kb < 4; ++kb) {
+                    const float4 x0 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg);
+                    const float4 x1 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg + 4);
+                    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) qop[pt][g][kb][i] = split_part(x[i] * a.qscale, lo_part);
-                if (t8 < a.nt8)
-                    a.qs[(((size_t)unit * a.nt8 + t8) * G + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
+                    for (int i = 0; i < 8; ++i) qop[pt][g][kb][i] = split_part(x[i] * a.qscale, lo_part);
+                    if (t8 < a.nt8)
+                        a.qs[(((size_t)unit * a.nt8 + t8) * G + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
+                }
             }
         }
     }
 
-    // online row statistics over the causal key tiles; lane lc sees key 16 kt + lc;
-    // the next tile's K is requested before this one is used
-    const int last = min(base + 8 * PT - 1, P - 1);
-    const int nkt = last / 16 + 1;
+    // online row statistics over the causal key tiles; lane lc sees key 16 kt + lc
+    const int wg_last = min(wg_base + 4 * 8 * PT - 1, P - 1);
+    const int nkt = wg_last / 16 + 1;                                      // the workgroup's tiles
+    const int nkt_w = active ? min(base + 8 * PT - 1, P - 1) / 16 + 1 : 0;  // this wave's
     const uint4* kp = reinterpret_cast<const uint4*>(a.k);
     float m[PT][G][2], l[PT][G][2];
 #pragma unroll
@@ -106,13 +119,34 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
             m[pt][g][0] = m[pt][g][1] = kFloor;
             l[pt][g][0] = l[pt][g][1] = 0.f;
         }
-    auto load_k = [&](int kt, uint4 (&t)[4]) {
-        const int kr = min(16 * kt + lc, P - 1);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) t[kb] = kp[((size_t)(off + kr) * a.Hkv + h) * kRowVecs + 4 * kb + lg];
-    };
-    auto rows = [&](int kt, const uint4 (&t)[4]) {
+    // chunk c (keys 64 c .. +64): wave w moves tile w, lane (lg, lc) fetching
+    // key 16 tile + lc's vectors 4 kb + lg (one per k-step) into registers and
+    // then into the B-operand slots it will read.  The loads for chunk c + 1
+    // are issued right after a barrier and stay in flight while chunk c is
+    // used; the barriers wait for LDS only.
+    static_assert(kRCK == 4, "one tile per wave");
+    uint4 st0, st1, st2, st3;
+#define H2O_ROWS_FETCH(c)                                                                        \
+    do {                                                                                         \
+        const int key_ = min((c) * 16 * kRCK + 16 * w + lc, P - 1);                               \
+        const uint4* src_ = kp + ((size_t)(off + key_) * a.Hkv + h) * kRowVecs + lg;              \
+        st0 = src_[0];                                                                           \
+        st1 = src_[4];                                                                           \
+        st2 = src_[8];                                                                           \
+        st3 = src_[12];                                                                          \
+    } while (0)
+#define H2O_ROWS_PUT(buf)                                                                        \
+    do {                                                                                         \
+        ksm[buf][w][0][lane] = st0;                                                              \
+        ksm[buf][w][1][lane] = st1;                                                              \
+        ksm[buf][w][2][lane] = st2;                                                              \
+        ksm[buf][w][3][lane] = st3;                                                              \
+    } while (0)
+    auto rows = [&](int kt, int buf) {
         const int key = 16 * kt + lc;
+        bf16x8 bt[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) bt[kb] = as_bf16x8(ksm[buf][kt % kRCK][kb][lane]);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const int pos0 = base + 8 * pt + 2 * lg, pos1 = pos0 + 1;  // C rows 4 lg .. +3
@@ -120,7 +154,7 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
             for (int g = 0; g < G; ++g) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) c = mma(qop[pt][g][kb], as_bf16x8(t[kb]), c);
+                for (int kb = 0; kb < 4; ++kb) c = mma(qop[pt][g][kb], bt[kb], c);
                 const float s[2] = {key <= pos0 ? c[0] + c[1] : -INFINITY,
                                     key <= pos1 ? c[2] + c[3] : -INFINITY};
 #pragma unroll
@@ -132,16 +166,24 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
             }
         }
     };
-    uint4 ka[4], kb4[4];
-    load_k(0, ka);
-    int kt = 0;
-    for (; kt + 2 <= nkt; kt += 2) {
-        load_k(kt + 1, kb4);
-        rows(kt, ka);
-        load_k(min(kt + 2, nkt - 1), ka);
-        rows(kt + 1, kb4);
+    const int nch = (nkt + kRCK - 1) / kRCK;
+    H2O_ROWS_FETCH(0);
+    H2O_ROWS_PUT(0);
+    lds_barrier();
+    if (nch > 1) H2O_ROWS_FETCH(1);
+    for (int c = 0; c < nch; ++c) {
+        const int buf = c & 1;
+        const int kt_end = min((c + 1) * kRCK, nkt_w);
+        for (int kt = c * kRCK; kt < kt_end; ++kt) rows(kt, buf);
+        // chunk c + 1 into the other buffer, which every wave finished reading
+        // before the previous barrier
+        if (c + 1 < nch) H2O_ROWS_PUT(buf ^ 1);
+        lds_barrier();
+        if (c + 2 < nch) H2O_ROWS_FETCH(c + 2);
     }
-    if (kt < nkt) rows(kt, ka);
+#undef H2O_ROWS_FETCH
+#undef H2O_ROWS_PUT
+    if (!active) return;
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -180,25 +222,48 @@ __device__ inline double xrow_add(double v, bool x32)
 
 constexpr int kKT = 4;  // 16-key B tiles per wave (64 keys)
 
+// columns pass: query tiles (8 positions, all G heads) per LDS chunk
+template <int G>
+struct ColsTune {
+    static constexpr int CQ = G >= 4 ? 1 : 4 / G;
+};
+
 template <int G, bool PH>
 __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
 {
     constexpr int NA = PH ? G : 1;
-    const int unit = blockIdx.y, b = unit / a.Hkv, h = unit - b * a.Hkv;
+    constexpr int CQ = ColsTune<G>::CQ;
+    // query chunks as the rows pass left them: [buffer][tile][head][k-step][lane]
+    // A operands, and each (tile, head)'s row statistics
+    __shared__ uint4 qsm[2][CQ][G][4][64];
+    __shared__ float4 ssm[2][CQ][G][4];
+    // lambdas below index the buffers through these (the host pass drops the
+    // kernel's launch stub when a lambda names these dependent-size arrays)
+    uint4* const qsm0 = &qsm[0][0][0][0][0];
+    float4* const ssm0 = &ssm[0][0][0][0];
+    constexpr int QB = CQ * G * 4 * 64, SB = CQ * G * 4;  // per buffer: 16-byte q vectors, statistics
+    // the unit is the fast grid index (every XCD gets every key block of an
+    // eighth of the units); the first key blocks, which walk the most query
+    // tiles, are dispatched first
+    const int unit = blockIdx.x, b = unit / a.Hkv, h = unit - b * a.Hkv;
     const int P = a.seq_p[b], lo = a.seq_lo[b];
     const int64_t off = a.seq_off[b];
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lc = lane & 15, lg = lane >> 4;
-    const int k0 = (blockIdx.x * 4 + w) * 16 * kKT;  // this wave's first key
-    if (k0 >= P) return;
+    const int wk0 = blockIdx.y * 4 * 16 * kKT;  // the workgroup's first key
+    if (wk0 >= P) return;
+    const int k0 = wk0 + w * 16 * kKT;  // this wave's first key
+    const bool active = k0 < P;
     const uint4* kp = reinterpret_cast<const uint4*>(a.k);
     uint4 kt4[kKT][4];
+    if (active) {
 #pragma unroll
-    for (int x = 0; x < kKT; ++x) {
-        const int kr = min(k0 + 16 * x + lc, P - 1);
+        for (int x = 0; x < kKT; ++x) {
+            const int kr = min(k0 + 16 * x + lc, P - 1);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kt4[x][kb] = kp[((size_t)(off + kr) * a.Hkv + h) * kRowVecs + 4 * kb + lg];
+            for (int kb = 0; kb < 4; ++kb) kt4[x][kb] = kp[((size_t)(off + kr) * a.Hkv + h) * kRowVecs + 4 * kb + lg];
+        }
     }
 
     double acc[kKT][NA];
@@ -206,8 +271,58 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
     for (int x = 0; x < kKT; ++x)
 #pragma unroll
         for (int y = 0; y < NA; ++y) acc[x][y] = 0.0;
-    const int t_first = max(k0, lo) / 8, t_last = (P - 1) / 8;
-    for (int t8 = t_first; t8 <= t_last; ++t8) {
+    // the workgroup walks query tiles from its first key (or row lo) to the end;
+    // a wave skips the tiles wholly before its own keys
+    const int t_first = max(wk0, lo) / 8, t_last = (P - 1) / 8;
+    const int t_first_w = active ? max(k0, lo) / 8 : t_last + 1;
+    const uint4* qg = a.qs + (size_t)unit * a.nt8 * G * 256;
+    const float4* sg = reinterpret_cast<const float4*>(a.st + (size_t)unit * a.nt8 * G * 8);
+    // a chunk (CQ tiles of G heads: CQ G 4 k-steps of 1 KB, plus CQ G 4 float4
+    // of row statistics) is copied in the same order: every thread moves
+    // vectors tid + 256 r through registers.  The loads for chunk c + 1 are
+    // issued right after a barrier and stay in flight while chunk c is used;
+    // the barriers wait for LDS only.
+    constexpr int NV = CQ * G;  // 16-byte vectors per thread (CQ G 4 64 per chunk)
+    static_assert(CQ * G * 4 <= 256, "statistics: one vector per thread");
+    static_assert(NV == 4 || NV == 8, "staging registers");
+    // named registers: an array here ends up in scratch memory
+    uint4 s0, s1, s2, s3, s4, s5, s6, s7;
+    float4 ss;
+    auto qvec = [&](int t0, int r) {
+        const int q = tid + 256 * r;
+        const int t8 = min(t0 + q / (G * 256), t_last);
+        return qg[(size_t)t8 * G * 256 + (q % (G * 256))];
+    };
+#define H2O_COLS_FETCH(t0)                                                                              \
+    do {                                                                                                \
+        s0 = qvec((t0), 0);                                                                             \
+        s1 = qvec((t0), 1);                                                                             \
+        s2 = qvec((t0), 2);                                                                             \
+        s3 = qvec((t0), 3);                                                                             \
+        if constexpr (NV == 8) {                                                                        \
+            s4 = qvec((t0), 4);                                                                         \
+            s5 = qvec((t0), 5);                                                                         \
+            s6 = qvec((t0), 6);                                                                         \
+            s7 = qvec((t0), 7);                                                                         \
+        }                                                                                               \
+        if (tid < CQ * G * 4) ss = sg[(size_t)min((t0) + tid / (G * 4), t_last) * G * 4 + tid % (G * 4)]; \
+    } while (0)
+#define H2O_COLS_PUT(buf)                                                                               \
+    do {                                                                                                \
+        uint4* qd_ = qsm0 + (buf) * QB + tid;                                                           \
+        qd_[0] = s0;                                                                                    \
+        qd_[256] = s1;                                                                                  \
+        qd_[512] = s2;                                                                                  \
+        qd_[768] = s3;                                                                                  \
+        if constexpr (NV == 8) {                                                                        \
+            qd_[1024] = s4;                                                                             \
+            qd_[1280] = s5;                                                                             \
+            qd_[1536] = s6;                                                                             \
+            qd_[1792] = s7;                                                                             \
+        }                                                                                               \
+        if (tid < CQ * G * 4) ssm0[(buf) * SB + tid] = ss;                                              \
+    } while (0)
+    auto tile = [&](int t8, int ci, int buf) {
         const int pos0 = 8 * t8 + 2 * lg, pos1 = pos0 + 1;
         const bool r0 = pos0 < P && pos0 >= lo, r1 = pos1 < P && pos1 >= lo;
         float tacc[kKT][NA];
@@ -217,18 +332,16 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
             for (int y = 0; y < NA; ++y) tacc[x][y] = 0.f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const uint4* qa = a.qs + (((size_t)unit * a.nt8 + t8) * G + g) * 256 + lane;
-            uint4 q4[4];
+            bf16x8 q4[4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) q4[kb] = qa[kb * 64];
-            const float4 sv =
-                *reinterpret_cast<const float4*>(a.st + (((size_t)unit * a.nt8 + t8) * G + g) * 8 + 2 * lg);
+            for (int kb = 0; kb < 4; ++kb) q4[kb] = as_bf16x8(qsm0[buf * QB + ((ci * G + g) * 4 + kb) * 64 + lane]);
+            const float4 sv = ssm0[buf * SB + (ci * G + g) * 4 + lg];
 #pragma unroll
             for (int x = 0; x < kKT; ++x) {
                 const int key = k0 + 16 * x + lc;
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) c = mma(as_bf16x8(q4[kb]), as_bf16x8(kt4[x][kb]), c);
+                for (int kb = 0; kb < 4; ++kb) c = mma(q4[kb], as_bf16x8(kt4[x][kb]), c);
                 const float p0 = (r0 && key <= pos0) ? fast_exp2(c[0] + c[1] - sv.x) * sv.y : 0.f;
                 const float p1 = (r1 && key <= pos1) ? fast_exp2(c[2] + c[3] - sv.z) * sv.w : 0.f;
                 tacc[x][PH ? g : 0] += p0 + p1;
@@ -238,7 +351,28 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
         for (int x = 0; x < kKT; ++x)
 #pragma unroll
             for (int y = 0; y < NA; ++y) acc[x][y] += (double)tacc[x][y];
+    };
+    const int nch = (t_last - t_first) / CQ + 1;
+    H2O_COLS_FETCH(t_first);
+    H2O_COLS_PUT(0);
+    lds_barrier();
+    if (nch > 1) H2O_COLS_FETCH(t_first + CQ);
+    for (int c = 0; c < nch; ++c) {
+        const int buf = c & 1, t0 = t_first + c * CQ;
+#pragma unroll
+        for (int ci = 0; ci < CQ; ++ci) {
+            const int t8 = t0 + ci;
+            if (t8 >= t_first_w && t8 <= t_last) tile(t8, ci, buf);
+        }
+        // chunk c + 1 into the other buffer, which every wave finished reading
+        // before the previous barrier
+        if (c + 1 < nch) H2O_COLS_PUT(buf ^ 1);
+        lds_barrier();
+        if (c + 2 < nch) H2O_COLS_FETCH(t0 + 2 * CQ);
     }
+#undef H2O_COLS_FETCH
+#undef H2O_COLS_PUT
+    if (!active) return;
     // sum over the four lane groups (the rows); every lane then holds its key's total
 #pragma unroll
     for (int x = 0; x < kKT; ++x) {
@@ -264,11 +398,11 @@ hipError_t launch_colsum_g(const ColsumArgs& a, int max_p, hipStream_t st)
 {
     const unsigned units = (unsigned)(a.B * a.Hkv);
     const int rows_per_wg = 4 * 8 * RowsTune<G>::PT, keys_per_wg = 4 * 16 * kKT;
-    hipLaunchKernelGGL((colsum_rows_kernel<G>), dim3((max_p + rows_per_wg - 1) / rows_per_wg, units),
+    hipLaunchKernelGGL((colsum_rows_kernel<G>), dim3(units, (max_p + rows_per_wg - 1) / rows_per_wg),
                        dim3(kCNT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 gc((max_p + keys_per_wg - 1) / keys_per_wg, units);
+    const dim3 gc(units, (max_p + keys_per_wg - 1) / keys_per_wg);
     if (a.per_head)
         hipLaunchKernelGGL((colsum_cols_kernel<G, true>), gc, dim3(kCNT), 0, st, a);
     else
