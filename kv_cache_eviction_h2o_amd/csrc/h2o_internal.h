@@ -113,10 +113,14 @@ struct StepArgs {
     int seq_in_args;                // 1: seq_n / seq_p below are valid (B <= kMaxArgBatch)
     int32_t seq_n[kMaxArgBatch];    // retained slots of sequence b before the step
     int32_t seq_p[kMaxArgBatch];    // prompt length of sequence b
+    uint8_t seq_order[kMaxArgBatch];  // with seq_in_args: the sequences longest first (workgroup
+                                      // i takes the unit (seq_order[i / Hkv], i % Hkv))
     int32_t newpage[kMaxArgBatch];  // paged: page for the append slot of sequence b, or -1;
                                     // with pop_stack, the free-stack entry that holds it
     int pop_stack;                  // 1: newpage[b] indexes State::fstack
 };
+
+static_assert(sizeof(StepArgs) <= 4096, "kernel arguments are limited to 4 KB");
 
 // Block-granular eviction after a step (h2o_block.hip), for the nseq sequences
 // that lose pages: candidate blocks are block-table entries [js, js + ncand)

@@ -57,8 +57,12 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
 
     const Geometry& gm = a.g;
     const State& S = a.s;
-    const int unit = blockIdx.x;
-    const int b = unit / gm.Hkv, h = unit - b * gm.Hkv;
+    // workgroups reach the XCDs round-robin: with the head as the fast index
+    // every XCD gets the same heads of every sequence, and within an XCD the
+    // longest sequences are dispatched first
+    const int sq = (int)blockIdx.x / gm.Hkv, h = (int)blockIdx.x - sq * gm.Hkv;
+    const int b = a.seq_in_args ? (int)a.seq_order[sq] : sq;
+    const int unit = b * gm.Hkv + h;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, sub = tid & 15, grp = tid >> 4;
 
     // the host knows every sequence's prompt length and retained count: taking

@@ -64,8 +64,10 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
 
     const Geometry& gm = a.g;
     const State& S = a.s;
-    const int unit = blockIdx.x;
-    const int b = unit / gm.Hkv, h = unit - b * gm.Hkv;
+    // the head is the fast index (XCDs round-robin), sequences longest first
+    const int sq = (int)blockIdx.x / gm.Hkv, h = (int)blockIdx.x - sq * gm.Hkv;
+    const int b = a.seq_in_args ? (int)a.seq_order[sq] : sq;
+    const int unit = b * gm.Hkv + h;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar)
     const int lc = lane & 15, lg = lane >> 4;  // C column, lane group

@@ -291,11 +291,17 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     a.npg_lds = (max_n_att + kPageSize - 1) >> kPageShift;
     for (int i = 0; i < kMaxArgBatch; ++i) a.newpage[i] = -1;
     a.seq_in_args = B <= kMaxArgBatch ? 1 : 0;
-    if (a.seq_in_args)
+    if (a.seq_in_args) {
         for (int b = 0; b < B; ++b) {
             a.seq_n[b] = c->count[b];
             a.seq_p[b] = c->plen[b];
         }
+        // workgroups of the longest sequences first (a workgroup's time grows with its count)
+        std::vector<int> ord(B);
+        for (int b = 0; b < B; ++b) ord[b] = b;
+        std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return c->count[x] > c->count[y]; });
+        for (int i = 0; i < B; ++i) a.seq_order[i] = (uint8_t)ord[i];
+    }
     std::vector<int> got;  // pages taken in this call (rolled back on failure)
     if (c->block) {
         // every block-table entry but the last is full: a sequence needs a page
