@@ -50,18 +50,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def summarize(args) -> None:
-    """Markdown summary of rocprofv3 CSV output for the step kernel (see --help)."""
+    """Summary of rocprofv3 CSV output for one kernel (default: the step kernel; see --help)."""
     import csv
     n_last = args.steps * (args.layers or 32)
+    kname = args.summarize_kernel
     out = [f"kernel_source_sha256_16: {kernel_hash()}"]
     if args.summarize_trace:
-        rows = [r for r in csv.DictReader(open(args.summarize_trace)) if "step_kernel" in r["Kernel_Name"]]
+        rows = [r for r in csv.DictReader(open(args.summarize_trace)) if kname in r["Kernel_Name"]]
         d = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows], dtype=np.float64)
         s0 = np.array([int(r["Start_Timestamp"]) for r in rows], dtype=np.int64)
         e0 = np.array([int(r["End_Timestamp"]) for r in rows], dtype=np.int64)
         w = d[-n_last:]
         gaps = (s0[-n_last + 1:] - e0[-n_last:-1]) / 1e3
-        out += [f"step_kernel launches in trace: {len(d)}",
+        out += [f"{kname} launches in trace: {len(d)}",
                 f"all launches: mean {d.mean() / 1e3:.3f} us",
                 f"timed window (last {n_last} launches): mean {w.mean() / 1e3:.3f} us, "
                 f"median {np.median(w) / 1e3:.3f} us, p10 {np.percentile(w, 10) / 1e3:.3f} us, "
@@ -72,7 +73,7 @@ def summarize(args) -> None:
         res = {}
         for name, f in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
             rows = list(csv.DictReader(open(f)))
-            st = [float(r["Counter_Value"]) for r in rows if "step_kernel" in r["Kernel_Name"]
+            st = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]
                   and r["Counter_Name"] == name]
             cal = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
                       and r["Counter_Name"] == name)
@@ -91,6 +92,9 @@ def parse():
                     help="print a summary of a rocprofv3 kernel trace of this benchmark and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="with FETCH_SIZE / WRITE_SIZE counter CSVs: HBM bytes per launch")
+    ap.add_argument("--summarize-kernel", default="step_kernel", metavar="NAME",
+                    help="kernel the summaries cover (a substring of its name; the timed window is "
+                         "the last steps x layers of its launches)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
@@ -276,16 +280,28 @@ def prefill_main(args, w):
     cfg = L.config_from_workload(w, max_len=max(lens) + 1)
     out = torch.empty((sum(lens), Hkv), dtype=torch.float64, device=dev)
     stream = torch.cuda.current_stream()
+    L.prefill_scores(cfg, lens, pq, pk, out)  # checked wrapper once
+    # then the C entry point on the same buffers, so the loop measures the device work
+    lib = L.load_library()
+    lens_c = (C.c_int32 * B)(*lens)
+    argv = (C.byref(cfg), lens_c, C.c_void_p(pq.data_ptr()), C.c_void_p(pk.data_ptr()),
+            C.c_void_p(out.data_ptr()))
+    sh = C.c_void_p(stream.cuda_stream)
+
+    def call():
+        rc = lib.h2o_prefill_scores(*argv, sh)
+        if rc != 0:
+            raise L.H2OError(rc, lib.h2o_last_error(None).decode())
+
     for _ in range(args.warmup):
-        L.prefill_scores(cfg, lens, pq, pk, out)
+        call()
     torch.cuda.synchronize()
     hev = HipEvents()
-    sh = C.c_void_p(stream.cuda_stream)
     e0, e1 = hev.create(), hev.create()
     t0 = time.perf_counter()
     hev.record(e0, sh)
     for _ in range(args.steps):
-        L.prefill_scores(cfg, lens, pq, pk, out)
+        call()
     hev.record(e1, sh)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -336,16 +352,30 @@ def snapkv_main(args, w):
     pq = S.device_prompt_queries(w.recipe, 0, lens, Hq, dev)
     cfg = L.config_from_workload(w, max_len=max(lens) + 1)
     stream = torch.cuda.current_stream()
+    kept, count, votes = L.snapkv_select(cfg, lens, pq, pk, window, pool, keep)  # checked wrapper once
+    # then the C entry point on the same buffers, so the loop measures the device work
+    lib = L.load_library()
+    cap = kept.shape[2]
+    lens_c = (C.c_int32 * B)(*lens)
+    argv = (C.byref(cfg), lens_c, int(window), int(pool), int(keep), C.c_void_p(pq.data_ptr()),
+            C.c_void_p(pk.data_ptr()), C.c_void_p(votes.data_ptr()), C.c_void_p(kept.data_ptr()),
+            C.c_void_p(count.data_ptr()), int(cap))
+    sh = C.c_void_p(stream.cuda_stream)
+
+    def call():
+        rc = lib.h2o_snapkv_select(*argv, sh)
+        if rc != 0:
+            raise L.H2OError(rc, lib.h2o_last_error(None).decode())
+
     for _ in range(args.warmup):
-        kept, count, votes = L.snapkv_select(cfg, lens, pq, pk, window, pool, keep)
+        call()
     torch.cuda.synchronize()
     hev = HipEvents()
-    sh = C.c_void_p(stream.cuda_stream)
     e0, e1 = hev.create(), hev.create()
     t0 = time.perf_counter()
     hev.record(e0, sh)
     for _ in range(args.steps):
-        kept, count, votes = L.snapkv_select(cfg, lens, pq, pk, window, pool, keep)
+        call()
     hev.record(e1, sh)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0

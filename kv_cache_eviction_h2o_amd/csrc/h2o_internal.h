@@ -166,7 +166,8 @@ struct GatherArgs {
 // [seq_lo[b], seq_p[b]) of every unit, bf16 K rows of 128, fp32 q.
 struct ColsumArgs {
     int B, Hq, Hkv, G;
-    int nt8;          // 8-position tiles per unit in the scratch (ceil(max P / 8))
+    int nt8;          // 8-position tiles per unit in the scratch: tiles seq_lo[b] / 8 on, at
+                      // most max_b (ceil(P_b / 8) - seq_lo[b] / 8)
     float qscale;     // logit scale * log2(e)
     int per_head;     // 1: out[(off_b + j) * Hq + h * G + g]; 0: out[(off_b + j) * Hkv + h]
     const float* q;   // [sum P][Hq][128]

@@ -99,8 +99,9 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
                     const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
                     for (int i = 0; i < 8; ++i) qop[pt][g][kb][i] = split_part(x[i] * a.qscale, lo_part);
-                    if (t8 < a.nt8)
-                        a.qs[(((size_t)unit * a.nt8 + t8) * G + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
+                    const int ts = t8 - lo / 8;  // the scratch keeps tiles from row lo's on
+                    if (ts >= 0 && ts < a.nt8)
+                        a.qs[(((size_t)unit * a.nt8 + ts) * G + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
                 }
             }
         }
@@ -198,12 +199,12 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
     if (lc == 0) {
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const int t8 = base / 8 + pt;
-            if (t8 >= a.nt8) continue;
+            const int ts = base / 8 + pt - lo / 8;
+            if (ts < 0 || ts >= a.nt8) continue;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float4* sp =
-                    reinterpret_cast<float4*>(a.st + (((size_t)unit * a.nt8 + t8) * G + g) * 8 + 2 * lg);
+                    reinterpret_cast<float4*>(a.st + (((size_t)unit * a.nt8 + ts) * G + g) * 8 + 2 * lg);
                 *sp = make_float4(m[pt][g][0], 1.0f / l[pt][g][0], m[pt][g][1], 1.0f / l[pt][g][1]);
             }
         }
@@ -288,10 +289,11 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
     // named registers: an array here ends up in scratch memory
     uint4 s0, s1, s2, s3, s4, s5, s6, s7;
     float4 ss;
+    const int t8lo = lo / 8;  // the scratch keeps tiles from row lo's on
     auto qvec = [&](int t0, int r) {
         const int q = tid + 256 * r;
         const int t8 = min(t0 + q / (G * 256), t_last);
-        return qg[(size_t)t8 * G * 256 + (q % (G * 256))];
+        return qg[(size_t)(t8 - t8lo) * G * 256 + (q % (G * 256))];
     };
 #define H2O_COLS_FETCH(t0)                                                                              \
     do {                                                                                                \
@@ -305,7 +307,7 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
             s6 = qvec((t0), 6);                                                                         \
             s7 = qvec((t0), 7);                                                                         \
         }                                                                                               \
-        if (tid < CQ * G * 4) ss = sg[(size_t)min((t0) + tid / (G * 4), t_last) * G * 4 + tid % (G * 4)]; \
+        if (tid < CQ * G * 4) ss = sg[(size_t)(min((t0) + tid / (G * 4), t_last) - t8lo) * G * 4 + tid % (G * 4)]; \
     } while (0)
 #define H2O_COLS_PUT(buf)                                                                               \
     do {                                                                                                \

@@ -411,7 +411,8 @@ int colsum_run(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo
     a.q = q;
     a.k = k;
     a.out = out;
-    a.nt8 = (maxP + 7) / 8;
+    a.nt8 = 0;  // scratch tiles per unit: those from row lo_b's on
+    for (int b = 0; b < B; ++b) a.nt8 = std::max(a.nt8, (a.seq_p[b] + 7) / 8 - a.seq_lo[b] / 8);
     const size_t units = (size_t)B * Hkv;
     const size_t qs_bytes = units * a.nt8 * G * 256 * sizeof(uint4);
     const size_t st_bytes = units * a.nt8 * G * 8 * sizeof(float2);
