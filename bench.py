@@ -233,10 +233,25 @@ def cpu_baseline(w, n_att: int, seconds: float):
     how = ("then the block selection of every sequence (one thread)" if block
            else "one token evicted per unit and step")
     return {"value": tokens / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host": host_cpu(),
             "sample": (f"one layer ({B} sequences x {Hkv} KV heads) with a fixed budget at the "
                        f"window's retained length n_att={n_att}, {done} decode steps, fp64 oracle "
                        f"steps on {threads} threads, {how}; {t_used:.1f} s of CPU step time "
                        f"(input conversion excluded)")}
+
+
+def host_cpu() -> str:
+    """The host's CPU model and logical core count (for the CPU baseline's record)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical cores"
 
 
 PEAK_BF16_TFLOPS = 2500.0
@@ -262,6 +277,7 @@ def colsum_cpu_baseline(w, lens, seconds: float):
             t_used += time.perf_counter() - t0
             done += 1
     return {"value": done * P / t_used, "unit": "prompt tokens/s", "cores": threads, "kind": "oracle",
+            "host": host_cpu(),
             "sample": (f"sequence 0 ({P} prompt positions) x {Hkv} KV heads x {G} query heads, "
                        f"{done} repetitions, fp64 oracle column sums on {threads} threads; "
                        f"{t_used:.1f} s of CPU time")}
@@ -566,6 +582,7 @@ def main():
                    "layers": layers, "prompt_len": lens[0] if len(set(lens)) == 1 else "mixed",
                    "window_steps": [s0, s0 + K_steps], "mean_n_att": round(float(win.mean()), 1),
                    "entry_point": "h2o_step_compact", "parallelism": "single GPU"},
+        "token_heads_per_s": round(value * Hkv, 1),
         "hbm_frac_step": round(step_bytes / elapsed / (HBM_PEAK_GBS * 1e9), 4),
         "roofline": roof,
         "cpu_baseline": cpu,

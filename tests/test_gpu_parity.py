@@ -65,6 +65,15 @@ def test_random_attention_reduced():
     assert rep.evictions == 4 * 8 * 16  # 4 units x 8 events x r
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["step_compact", "step+compact"])
+def test_random_attention_paged(fused):
+    # events drop r tokens at once: holes filled from the tail, whole pages released
+    w = WL.RANDOM_ATTN.scaled(batch=3, n_q_heads=8, n_kv_heads=2, rand_k=64, rand_r=16, prompt_len=40,
+                              page_size=16)
+    rep = P().run_parity(w, 200, lens=[40, 23, 57], fused=fused)
+    assert rep.evictions == 3 * 2 * 8 * 16  # 6 units x 8 events x r
+
+
 def test_random_attention_full_shape_sampled_units():
     w = WL.RANDOM_ATTN.scaled(rand_k=256)
     rep = P().run_parity(w, 400, units=[(0, 0), (31, 7), (12, 3)])
