@@ -368,10 +368,68 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
 }
 
 
-// Causal-attention column sums of packed prompts (h2o_prefill_scores): validate,
-// take stream-ordered scratch, launch the two passes, return the scratch.
-int colsum_run(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo, const float* q,
-               const void* k, int per_head, double* out, void* stream)
+// Scratch of the prompt calls (h2o_prefill_scores, h2o_snapkv_select): one
+// grow-only device buffer per device, kept until the process ends, so a call
+// allocates nothing once a call at least as large has run (a stream-ordered
+// allocation and release per call cost more host time than the kernels take).
+// The mutex orders the calls that use it.  Every call records an event on its
+// stream once its kernels are enqueued; a call on another stream than the
+// previous one first makes its stream wait for that event.
+struct PromptScratch {
+    std::mutex mu;
+    char* base = nullptr;
+    size_t bytes = 0;
+    bool used = false;
+    hipStream_t last = nullptr;
+    hipEvent_t ev = nullptr;
+};
+constexpr int kMaxDevices = 64;
+PromptScratch g_prompt_scratch[kMaxDevices];
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// With s.mu held: at least `need` bytes of s, usable by work enqueued on st next.
+hipError_t scratch_take(PromptScratch& s, size_t need, hipStream_t st, char** out)
+{
+    hipError_t e;
+    if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
+    if (s.used && s.last != st && (e = hipStreamWaitEvent(st, s.ev, 0)) != hipSuccess) return e;
+    if (need > s.bytes) {
+        const size_t grow = std::max(need, s.bytes + s.bytes / 2);
+        if (s.base && (e = hipFreeAsync(s.base, st)) != hipSuccess) return e;
+        s.base = nullptr;
+        s.bytes = 0;
+        if ((e = hipMallocAsync((void**)&s.base, grow, st)) != hipSuccess) return e;
+        s.bytes = grow;
+    }
+    *out = s.base;
+    return hipSuccess;
+}
+
+// With s.mu held, once everything of the call that uses s is enqueued on st
+// (also after a failed launch): later calls on other streams wait for it.
+hipError_t scratch_done(PromptScratch& s, hipStream_t st)
+{
+    s.last = st;
+    s.used = true;
+    return hipEventRecord(s.ev, st);
+}
+
+PromptScratch* prompt_scratch(std::string& why)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        why = "no HIP device (or device index above 63)";
+        return nullptr;
+    }
+    return &g_prompt_scratch[dev];
+}
+
+// Causal-attention column sums of packed prompts: validate and fill the
+// launch arguments (the caller checks and sets `out`); scratch_bytes = the
+// scratch the two passes need.
+int colsum_setup(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo, const float* q,
+                 const void* k, int per_head, double* out, ColsumArgs& a, int& maxP, size_t& scratch_bytes)
 {
     if (!cfg || !plen) return fail(nullptr, H2O_EINVAL, "null config or prompt lengths");
     const int B = cfg->batch, Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
@@ -385,13 +443,13 @@ int colsum_run(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo
     if (cfg->head_dim != 128 || cfg->kv_dtype != H2O_BF16)
         return fail(nullptr, H2O_EINVAL, "prompt column sums need bf16 K rows of head_dim 128");
     if (!(cfg->scale >= 0.f)) return fail(nullptr, H2O_EINVAL, "scale must be >= 0");
-    ColsumArgs a{};
+    a = ColsumArgs{};
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = G;
     a.per_head = per_head ? 1 : 0;
-    int maxP = 0;
+    maxP = 0;
     long long off = 0;
     for (int b = 0; b < B; ++b) {
         const int P = plen[b];
@@ -405,7 +463,7 @@ int colsum_run(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo
         maxP = std::max(maxP, P);
     }
     if (off > (1LL << 31)) return fail(nullptr, H2O_EINVAL, "too many prompt positions");
-    if (!q || !k || !out) return fail(nullptr, H2O_EINVAL, "null prompt_q, prompt_k or out");
+    if (!q || !k) return fail(nullptr, H2O_EINVAL, "null prompt_q or prompt_k");
     const double scale = cfg->scale > 0.f ? (double)cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
     a.qscale = (float)(scale * 1.4426950408889634);
     a.q = q;
@@ -414,21 +472,40 @@ int colsum_run(const h2o_config* cfg, const int32_t* plen, const int32_t* row_lo
     a.nt8 = 0;  // scratch tiles per unit: those from row lo_b's on
     for (int b = 0; b < B; ++b) a.nt8 = std::max(a.nt8, (a.seq_p[b] + 7) / 8 - a.seq_lo[b] / 8);
     const size_t units = (size_t)B * Hkv;
-    const size_t qs_bytes = units * a.nt8 * G * 256 * sizeof(uint4);
-    const size_t st_bytes = units * a.nt8 * G * 8 * sizeof(float2);
+    scratch_bytes = align256(units * a.nt8 * G * 256 * sizeof(uint4)) + align256(units * a.nt8 * G * 8 * sizeof(float2));
+    return H2O_OK;
+}
+
+// The two column-sum passes with their scratch at sp (colsum_setup's size).
+hipError_t colsum_launch(ColsumArgs& a, int maxP, char* sp, hipStream_t st)
+{
+    const size_t units = (size_t)a.B * a.Hkv;
+    a.qs = reinterpret_cast<uint4*>(sp);
+    a.st = reinterpret_cast<float2*>(sp + align256(units * a.nt8 * a.G * 256 * sizeof(uint4)));
+    return launch_colsum(a, maxP, st);
+}
+
+int colsum_run(const h2o_config* cfg, const int32_t* plen, const float* q, const void* k, double* out,
+               void* stream)
+{
+    ColsumArgs a;
+    int maxP = 0;
+    size_t need = 0;
+    int rc = colsum_setup(cfg, plen, nullptr, q, k, 0, out, a, maxP, need);
+    if (rc != H2O_OK) return rc;
+    if (!out) return fail(nullptr, H2O_EINVAL, "null out");
+    std::string why;
+    PromptScratch* ps = prompt_scratch(why);
+    if (!ps) return fail(nullptr, H2O_EDEVICE, why);
+    std::lock_guard<std::mutex> lk(ps->mu);
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e;
-    if ((e = hipMallocAsync((void**)&a.qs, qs_bytes, st)) != hipSuccess)
-        return hip_fail(nullptr, e, "prompt column sums: scratch for q");
-    if ((e = hipMallocAsync((void**)&a.st, st_bytes, st)) != hipSuccess) {
-        (void)hipFreeAsync(a.qs, st);
-        return hip_fail(nullptr, e, "prompt column sums: scratch for row statistics");
-    }
-    e = launch_colsum(a, maxP, st);
-    const hipError_t e1 = hipFreeAsync(a.qs, st), e2 = hipFreeAsync(a.st, st);
+    char* sp = nullptr;
+    hipError_t e = scratch_take(*ps, need, st, &sp);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "prompt column sums: scratch");
+    e = colsum_launch(a, maxP, sp, st);
+    const hipError_t e2 = scratch_done(*ps, st);
     if (e != hipSuccess) return hip_fail(nullptr, e, "prompt column sums: launch");
-    if (e1 != hipSuccess || e2 != hipSuccess)
-        return hip_fail(nullptr, e1 != hipSuccess ? e1 : e2, "prompt column sums: scratch release");
+    if (e2 != hipSuccess) return hip_fail(nullptr, e2, "prompt column sums: scratch event");
     return H2O_OK;
 }
 
@@ -474,29 +551,35 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     }
     total = off;
     if (!kept || !count) return fail(nullptr, H2O_EINVAL, "null kept or kept_count");
+    // scratch: [votes (when the caller passes none)] [pooled votes] [column-sum passes]
+    const size_t vbytes = align256((size_t)total * Hq * sizeof(double));
+    std::string why;
+    PromptScratch* ps = prompt_scratch(why);
+    if (!ps) return fail(nullptr, H2O_EDEVICE, why);
+    std::lock_guard<std::mutex> lk(ps->mu);
+    const size_t vown = votes ? 0 : vbytes;
+    ColsumArgs ca;
+    int maxPc = 0;
+    size_t cbytes = 0;
+    int rc = colsum_setup(cfg, plen, lo.data(), q, k, 1, votes, ca, maxPc, cbytes);
+    if (rc != H2O_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e;
-    double* vb = votes;
-    if (!vb && (e = hipMallocAsync((void**)&vb, (size_t)total * Hq * sizeof(double), st)) != hipSuccess)
-        return hip_fail(nullptr, e, "SnapKV: scratch for votes");
-    int rc = colsum_run(cfg, plen, lo.data(), q, k, 1, vb, stream);
-    if (rc != H2O_OK) {
-        if (!votes) (void)hipFreeAsync(vb, st);
-        return rc;
+    char* sp = nullptr;
+    hipError_t e = scratch_take(*ps, vown + vbytes + cbytes, st, &sp);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV: scratch");
+    double* vb = votes ? votes : reinterpret_cast<double*>(sp);
+    ca.out = vb;  // the votes: the caller's buffer, else the scratch's first part
+    e = colsum_launch(ca, maxPc, sp + vown + vbytes, st);
+    if (e == hipSuccess) {
+        a.votes = vb;
+        a.pooled = reinterpret_cast<double*>(sp + vown);
+        a.kept = kept;
+        a.count = count;
+        e = launch_snapkv(a, maxP, st);
     }
-    a.votes = vb;
-    if ((e = hipMallocAsync((void**)&a.pooled, (size_t)total * Hq * sizeof(double), st)) != hipSuccess) {
-        if (!votes) (void)hipFreeAsync(vb, st);
-        return hip_fail(nullptr, e, "SnapKV: scratch for pooled votes");
-    }
-    a.kept = kept;
-    a.count = count;
-    e = launch_snapkv(a, maxP, st);
-    const hipError_t e1 = hipFreeAsync(a.pooled, st);
-    const hipError_t e2 = votes ? hipSuccess : hipFreeAsync(vb, st);
+    const hipError_t e2 = scratch_done(*ps, st);
     if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV: launch");
-    if (e1 != hipSuccess || e2 != hipSuccess)
-        return hip_fail(nullptr, e1 != hipSuccess ? e1 : e2, "SnapKV: scratch release");
+    if (e2 != hipSuccess) return hip_fail(nullptr, e2, "SnapKV: scratch event");
     return H2O_OK;
 }
 
@@ -893,7 +976,7 @@ void h2o_destroy(h2o_ctx* c)
 int h2o_prefill_scores(const h2o_config* cfg, const int32_t* prompt_len, const float* prompt_q,
                        const void* prompt_k, double* out, void* stream)
 {
-    return colsum_run(cfg, prompt_len, nullptr, prompt_q, prompt_k, 0, out, stream);
+    return colsum_run(cfg, prompt_len, prompt_q, prompt_k, out, stream);
 }
 
 int h2o_snapkv_select(const h2o_config* cfg, const int32_t* prompt_len, int32_t window, int32_t pool,
