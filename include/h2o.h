@@ -38,7 +38,9 @@
  * Conventions
  *   - Every call except h2o_read_indices and h2o_destroy is asynchronous on
  *     `stream` (a hipStream_t; NULL = the device's null stream).  Pointers
- *     named "device" must stay valid until the stream has run the work.
+ *     named "device" must stay valid until the stream has run the work and
+ *     be 16-byte aligned (the kernels use 16-byte vector accesses; a
+ *     misaligned one is rejected with H2O_EINVAL before anything runs).
  *   - Layouts (row-major): q and out [B][Hq][D] fp32; k_new, v_new
  *     [B][Hkv][D] in kv_dtype (bf16 = raw bf16 bits); query head j belongs to
  *     KV head j / G, G = Hq / Hkv.

@@ -64,6 +64,9 @@ int fail(h2o_ctx* c, int code, const std::string& msg)
     return code;
 }
 
+// Device arguments are read and written with 16-byte vector accesses.
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 int hip_fail(h2o_ctx* c, hipError_t e, const char* what)
 {
     std::string m = std::string(what) + ": " + hipGetErrorString(e);
@@ -264,6 +267,8 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     if (!c) return H2O_EINVAL;
     if (c->pending) return fail(c, H2O_ESTATE, "a compaction is pending: call h2o_compact first");
     if (!q || !kn || !vn || !out) return fail(c, H2O_EINVAL, "null q, k_new, v_new or out");
+    if (misaligned(q) || misaligned(kn) || misaligned(vn) || misaligned(out))
+        return fail(c, H2O_EINVAL, "q, k_new, v_new and out must be 16-byte aligned");
     const int B = c->g.B;
     std::vector<int> e(B);
     int max_n_att = 0;
@@ -464,6 +469,8 @@ int colsum_setup(const h2o_config* cfg, const int32_t* plen, const int32_t* row_
     }
     if (off > (1LL << 31)) return fail(nullptr, H2O_EINVAL, "too many prompt positions");
     if (!q || !k) return fail(nullptr, H2O_EINVAL, "null prompt_q or prompt_k");
+    if (misaligned(q) || misaligned(k) || misaligned(out))
+        return fail(nullptr, H2O_EINVAL, "prompt_q, prompt_k and the output must be 16-byte aligned");
     const double scale = cfg->scale > 0.f ? (double)cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
     a.qscale = (float)(scale * 1.4426950408889634);
     a.q = q;
@@ -551,6 +558,8 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     }
     total = off;
     if (!kept || !count) return fail(nullptr, H2O_EINVAL, "null kept or kept_count");
+    if (misaligned(kept) || misaligned(count))
+        return fail(nullptr, H2O_EINVAL, "kept and kept_count must be 16-byte aligned");
     // scratch: [votes (when the caller passes none)] [pooled votes] [column-sum passes]
     const size_t vbytes = align256((size_t)total * Hq * sizeof(double));
     std::string why;
@@ -596,6 +605,8 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
     int rc = validate(cfg, prompt_len, why);
     if (rc != H2O_OK) return fail(nullptr, rc, why);
     if (!prompt_k || !prompt_v) return fail(nullptr, H2O_EINVAL, "null prompt_k or prompt_v");
+    if (misaligned(prompt_k) || misaligned(prompt_v) || misaligned(init_scores))
+        return fail(nullptr, H2O_EINVAL, "prompt_k, prompt_v and init_scores must be 16-byte aligned");
 
     h2o_ctx* c = new h2o_ctx();
     c->cfg = *cfg;

@@ -116,6 +116,17 @@ def test_null_arguments(lib):
     assert lib.h2o_init(C.byref(ctx), C.byref(cfg), arr, None, None, None, None) == L.H2O_EINVAL
 
 
+def test_init_rejects_misaligned_device_pointers(lib):
+    cfg = L.make_config(**GOOD)
+    arr = (C.c_int32 * 2)(10, 20)
+    ctx = C.c_void_p()
+    for k, v, s in ((20, 16, None), (16, 8, None), (16, 16, 4)):
+        rc = lib.h2o_init(C.byref(ctx), C.byref(cfg), arr, C.c_void_p(k), C.c_void_p(v),
+                          C.c_void_p(s) if s else None, None)
+        assert rc == L.H2O_EINVAL and not ctx.value
+        assert "16-byte aligned" in lib.h2o_last_error(None).decode()
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
     mod = importlib.import_module("kv_cache_eviction_h2o_amd._lib")
@@ -167,6 +178,12 @@ def test_prefill_scores_rejects_before_device(lib, bad, lens, msg):
     assert msg in lib.h2o_last_error(None).decode()
 
 
+def test_prefill_scores_rejects_misaligned_pointers(lib):
+    cfg = L.make_config(**GOOD)
+    assert _prefill(lib, cfg, [10, 10], ptr=20) == L.H2O_EINVAL
+    assert "16-byte aligned" in lib.h2o_last_error(None).decode()
+
+
 def test_prefill_scores_null_arguments(lib):
     cfg = L.make_config(**GOOD)
     assert lib.h2o_prefill_scores(None, None, None, None, None, None) == L.H2O_EINVAL
@@ -187,6 +204,7 @@ def _snap(lib, cfg, lens, window=32, pool=7, keep=16, cap=4096, ptr=16):
     (dict(keep=-1), "keep"),
     (dict(cap=10), "cap"),
     (dict(ptr=0), "null"),
+    (dict(ptr=24), "16-byte aligned"),
 ])
 def test_snapkv_select_rejects_before_device(lib, kw, msg):
     cfg = L.make_config(**GOOD)

@@ -1,0 +1,125 @@
+"""Error paths of the C ABI on a live context: every rejected call returns its
+status before anything is enqueued and leaves the context as it was.  Two
+contexts take the same valid calls; one also takes the rejected ones, and the
+two must end bit-identical (outputs, positions, scores, evicted mass)."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+from kv_cache_eviction_h2o_amd import synth as S
+from kv_cache_eviction_h2o_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_eviction_h2o_amd import _lib
+    _lib.load_library()
+
+
+def _setup(w, lens, steps, **cfg_over):
+    import parity
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+    K, V = S.prompt_kv(w.recipe, 0, lens, w.n_kv_heads)
+    # max_len admits exactly `steps` steps of the longest prompt
+    cfg = L.config_from_workload(w, max_len=max(lens) + steps, **cfg_over)
+    if w.page_size and not cfg.max_pages:
+        cfg.max_pages = L.pages_needed(lens, steps, cfg)
+    mk = lambda: L.H2OCache(cfg, lens, parity.to_dev(K, w.recipe.kv_dtype), parity.to_dev(V, w.recipe.kv_dtype))
+    q, k, v = S.step_window(w.recipe, 0, lens, steps, w.n_q_heads, w.n_kv_heads)
+    qd = torch.from_numpy(q).cuda()
+    kd, vd = parity.to_dev(k, w.recipe.kv_dtype), parity.to_dev(v, w.recipe.kv_dtype)
+    return cfg, mk, qd, kd, vd
+
+
+def _same(a, b):
+    pa, ca, sa, ea = a.read_indices()
+    pb, cb, sb, eb = b.read_indices()
+    assert np.array_equal(ca, cb) and np.array_equal(pa, pb)
+    assert np.array_equal(sa, sb) and np.array_equal(ea, eb)
+    assert a.info() == b.info()
+
+
+@pytest.mark.parametrize("wname", ["gqa_tiles", "opt_rows", "paged"])
+def test_rejected_calls_leave_the_context_unchanged(wname):
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+    w = {"gqa_tiles": WL.LLAMA_GQA.scaled(batch=2, budget_fixed=100, hh_fixed=48),
+         "opt_rows": WL.OPT_LAYER.scaled(batch=2, n_q_heads=4, n_kv_heads=4),
+         "paged": WL.PAGED_MIXED.scaled(batch=2, n_q_heads=4, n_kv_heads=4)}[wname]
+    lens, steps = [150, 90], 14
+    cfg, mk, qd, kd, vd = _setup(w, lens, steps)
+    a, b = mk(), mk()
+    lib = a.lib
+    oa = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    # a buffer whose start is 4 bytes past an aligned address, for each argument in turn
+    qx = torch.empty(qd[0].numel() + 4, dtype=torch.float32, device="cuda")
+    sh = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: C.c_void_p(t.data_ptr())
+    for i in range(steps):
+        if i == 2:  # misaligned q, k_new, v_new, out: rejected by both entry points
+            for fn in (lib.h2o_step, lib.h2o_step_compact):
+                args = [ptr(qd[i]), ptr(kd[i]), ptr(vd[i]), ptr(ob)]
+                for j in range(4):
+                    bad = list(args)
+                    bad[j] = C.c_void_p(qx.data_ptr() + 4)
+                    assert fn(b.ctx, *bad, sh) == L.H2O_EINVAL
+                    assert "16-byte aligned" in lib.h2o_last_error(b.ctx).decode()
+        if i == 4:  # nothing pending
+            assert lib.h2o_compact(b.ctx, sh) == L.H2O_ESTATE
+        if i == 6 or i == 9:  # a step pending: a second step, and reads, are refused
+            a.step(qd[i], kd[i], vd[i], oa)
+            b.step(qd[i], kd[i], vd[i], ob)
+            for fn in (lib.h2o_step, lib.h2o_step_compact):
+                assert fn(b.ctx, ptr(qd[i]), ptr(kd[i]), ptr(vd[i]), ptr(ob), sh) == L.H2O_ESTATE
+            with pytest.raises(L.H2OError) as ex:
+                b.read_indices()
+            assert ex.value.code == L.H2O_ESTATE
+            a.compact()
+            b.compact()
+        else:
+            a.step_compact(qd[i], kd[i], vd[i], oa)
+            b.step_compact(qd[i], kd[i], vd[i], ob)
+        assert torch.equal(oa, ob), i
+    # a read with too small a cap
+    with pytest.raises(L.H2OError) as ex:
+        b.read_indices(cap=1)
+    assert ex.value.code == L.H2O_EINVAL
+    _same(a, b)
+    # the next step would pass max_len
+    assert lib.h2o_step_compact(b.ctx, ptr(qd[0]), ptr(kd[0]), ptr(vd[0]), ptr(ob), sh) == L.H2O_EINVAL
+    assert "max_len" in lib.h2o_last_error(b.ctx).decode()
+    _same(a, b)
+    a.close()
+    b.close()
+
+
+def test_page_pool_exhaustion_is_refused_and_recoverable_state():
+    """Paged layout with a pool exactly as large as the prompts' pages and a
+    budget above every length: the first step that needs a new page is
+    refused with H2O_ENOMEM, and the context still reads back unchanged."""
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+    w = WL.PAGED_MIXED.scaled(batch=2, n_q_heads=4, n_kv_heads=4, budget_fixed=4096, hh_fixed=2000)
+    lens = [32, 20]  # 2 + 2 pages; sequence 0 needs a third page at its first step
+    cfg, mk, qd, kd, vd = _setup(w, lens, 4, max_pages=4)
+    c = mk()
+    before = c.read_indices()
+    assert c.info()[1:] == (0, 4)
+    o = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    for fused in (True, False):
+        with pytest.raises(L.H2OError) as ex:
+            (c.step_compact if fused else c.step)(qd[0], kd[0], vd[0], o)
+        assert ex.value.code == L.H2O_ENOMEM
+        assert c.info()[1:] == (0, 4)
+    after = c.read_indices()
+    for x, y in zip(before, after):
+        assert np.array_equal(x, y)
+    c.close()
