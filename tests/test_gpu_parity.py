@@ -131,6 +131,36 @@ def test_initial_scores():
     P().run_parity(w, 40, lens=lens, init_scores=init)
 
 
+# -------------------------------------- more sequences than the kernel arguments hold
+# Above 128 sequences the step kernels read each sequence's prompt length and
+# retained count from device memory instead of their arguments, and take the
+# units in plain order.  Prompts from 1 token on (below the sinks and budget).
+def _many_lens(n, seed):
+    r = np.random.default_rng(seed)
+    lens = [int(x) for x in r.integers(1, 90, size=n)]
+    lens[0], lens[1] = 1, 2
+    return lens
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["step_compact", "step+compact"])
+def test_batch_above_argument_limit_fma_path(fused):
+    w = WL.OPT_LAYER.scaled(batch=131, n_q_heads=2, n_kv_heads=2, budget_fixed=40, hh_fixed=16)
+    rep = P().run_parity(w, 30, lens=_many_lens(131, 1), fused=fused)
+    assert rep.evictions > 0
+
+
+def test_batch_above_argument_limit_matrix_core_path():
+    w = WL.LLAMA_GQA.scaled(batch=130, n_q_heads=8, n_kv_heads=2, budget_fixed=40, hh_fixed=16)
+    rep = P().run_parity(w, 30, lens=_many_lens(130, 2))
+    assert rep.evictions > 0
+
+
+def test_batch_above_argument_limit_random_attention():
+    w = WL.RANDOM_ATTN.scaled(batch=129, n_q_heads=8, n_kv_heads=2, rand_k=12, rand_r=4)
+    rep = P().run_parity(w, 40, lens=_many_lens(129, 3))
+    assert rep.evictions > 0
+
+
 # ------------------------------------------------ matrix-core path (G = 4, 8)
 def test_gqa_ragged_units_cross_tile_edges():
     # units start at 5, 64 (a whole number of 32-slot tiles), 95 and 130 slots
