@@ -11,6 +11,7 @@ from kv_cache_eviction_h2o_amd import _lib as L
 from kv_cache_eviction_h2o_amd.build import INCLUDE, LIB, build
 
 HEADER = os.path.join(INCLUDE, "h2o.h")
+HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 @pytest.fixture(scope="module")
@@ -125,6 +126,17 @@ def test_init_rejects_misaligned_device_pointers(lib):
                           C.c_void_p(s) if s else None, None)
         assert rc == L.H2O_EINVAL and not ctx.value
         assert "16-byte aligned" in lib.h2o_last_error(None).decode()
+
+
+def test_c_client_compiles_against_the_header(tmp_path):
+    """The C client check (run on a GPU by test_gpu_c_client.py) builds with gcc
+    against include/h2o.h and the library, warning-free."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("c_build", os.path.join(HERE, "c", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    r = subprocess.run(mod.command(str(tmp_path / "h2o_c_check")) + ["-Werror"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
