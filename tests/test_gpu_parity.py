@@ -161,6 +161,18 @@ def test_batch_above_argument_limit_random_attention():
     assert rep.evictions > 0
 
 
+# ----------------------------------- FMA path with logits in global scratch
+# G x n_att x 4 bytes above 64 KB: the FMA step kernel keeps its logits in
+# global scratch instead of LDS (contiguous and paged layouts).
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+@pytest.mark.parametrize("fused", [True, False], ids=["step_compact", "step+compact"])
+def test_fma_logits_in_global_scratch(paged, fused):
+    base = WL.PAGED_MIXED if paged else WL.OPT_LAYER
+    w = base.scaled(batch=2, n_q_heads=2, n_kv_heads=1, budget_fixed=17000, hh_fixed=8000)
+    rep = P().run_parity(w, 12, lens=[17100, 9000], fused=fused)
+    assert rep.evictions > 0
+
+
 # ------------------------------------------------ matrix-core path (G = 4, 8)
 def test_gqa_ragged_units_cross_tile_edges():
     # units start at 5, 64 (a whole number of 32-slot tiles), 95 and 130 slots
