@@ -124,7 +124,21 @@ typedef struct {
     int32_t page_size;     /* 0 = contiguous slots per (b, h); 16 = paged */
     int32_t max_pages;     /* paged: size of the page pool (pages of Hkv x 16 tokens) */
     int32_t max_len;       /* most positions any sequence will reach (prompt + steps) */
+    void *workspace;       /* device memory for the context's state, or NULL (the library
+                              allocates it).  Non-NULL: 256-byte aligned and at least
+                              h2o_workspace_size() bytes; the caller owns it, keeps it
+                              until h2o_destroy has returned, and h2o_destroy leaves it
+                              alone.  Lets an allocator that owns device memory (a
+                              framework's caching allocator) hold the cache. */
+    uint64_t workspace_bytes;  /* size of workspace (ignored when it is NULL) */
 } h2o_config;
+
+/* Device bytes the context of (cfg, prompt_len) keeps for its state: the K/V
+ * cache, scores, positions, counts, page tables and scratch -- the size a
+ * caller-provided h2o_config::workspace must have.  Validates as h2o_init does
+ * and touches no device.  Errors: H2O_EINVAL (config/shape), H2O_ENOMEM (paged:
+ * the prompts need more pages than max_pages). */
+int h2o_workspace_size(const h2o_config *cfg, const int32_t *prompt_len, uint64_t *bytes);
 
 /* Create a context and load the prompts.
  *   prompt_len  host [B]: P_b >= 1.
@@ -132,8 +146,9 @@ typedef struct {
  *   init_scores device [sum_b P_b][Hkv] fp64 initial cumulative scores, or NULL = 0.
  * The prompts are copied; the caller may reuse its buffers once the stream has
  * run the copy.  On success *out receives the context.
- * Errors: H2O_EINVAL (config/shape), H2O_ENOMEM (device memory or page pool),
- * H2O_EDEVICE. */
+ * With cfg->workspace the state is carved from it and nothing is allocated.
+ * Errors: H2O_EINVAL (config/shape; a workspace below h2o_workspace_size),
+ * H2O_ENOMEM (device memory or page pool), H2O_EDEVICE. */
 int h2o_init(h2o_ctx **out, const h2o_config *cfg, const int32_t *prompt_len,
              const void *prompt_k, const void *prompt_v, const double *init_scores,
              void *stream);

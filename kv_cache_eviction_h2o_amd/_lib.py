@@ -23,7 +23,7 @@ _STATUS = {H2O_EINVAL: "H2O_EINVAL", H2O_ENOMEM: "H2O_ENOMEM", H2O_EDEVICE: "H2O
 PAGE_SIZE = 16
 
 # Every symbol include/h2o.h declares.
-SYMBOLS = ("h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
+SYMBOLS = ("h2o_workspace_size", "h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
            "h2o_info", "h2o_read_kv", "h2o_destroy", "h2o_prefill_scores", "h2o_snapkv_select",
            "h2o_last_error")
 
@@ -35,7 +35,7 @@ class H2OConfig(C.Structure):
                 ("budget_fixed", C.c_int32), ("hh_fixed", C.c_int32), ("budget_num", C.c_int32),
                 ("budget_den", C.c_int32), ("rand_k", C.c_int32), ("rand_r", C.c_int32),
                 ("seed", C.c_uint64), ("page_size", C.c_int32), ("max_pages", C.c_int32),
-                ("max_len", C.c_int32)]
+                ("max_len", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64)]
 
 
 class H2OError(RuntimeError):
@@ -61,6 +61,8 @@ def load_library(path: str = LIB):
                            "(python -c 'import __graft_entry__ as g; g.build()')")
     lib = C.CDLL(path)
     vp, i32p, f64p = C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)
+    lib.h2o_workspace_size.restype = C.c_int
+    lib.h2o_workspace_size.argtypes = [C.POINTER(H2OConfig), i32p, C.POINTER(C.c_uint64)]
     lib.h2o_init.restype = C.c_int
     lib.h2o_init.argtypes = [C.POINTER(vp), C.POINTER(H2OConfig), i32p, vp, vp, vp, vp]
     for name in ("h2o_step", "h2o_step_compact"):
@@ -177,6 +179,20 @@ def snapkv_select(cfg: H2OConfig, prompt_lens, prompt_q, prompt_k, window: int, 
     return kept, count, votes
 
 
+def workspace_size(cfg: H2OConfig, prompt_lens) -> int:
+    """Device bytes a context keeps for its state (h2o_workspace_size): the size of
+    a caller-provided workspace (see H2OCache's `workspace`)."""
+    lib = load_library()
+    lens = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    if lens.shape != (cfg.batch,):
+        raise ValueError("prompt_lens must have one entry per sequence")
+    n = C.c_uint64()
+    rc = lib.h2o_workspace_size(C.byref(cfg), lens.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(n))
+    if rc != H2O_OK:
+        raise H2OError(rc, lib.h2o_last_error(None).decode(errors="replace"))
+    return int(n.value)
+
+
 def _stream_handle(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -196,11 +212,13 @@ class H2OCache:
     """One decode-step context: retained K/V, cumulative scores, positions.
 
     prompt_k / prompt_v: cuda tensors [sum P_b][Hkv][D] (bfloat16 or float32);
-    init_scores: optional cuda float64 [sum P_b][Hkv].
+    init_scores: optional cuda float64 [sum P_b][Hkv];
+    workspace: optional contiguous cuda uint8 tensor of at least workspace_size(cfg,
+    prompt_lens) bytes holding the context's state (kept alive by the cache).
     """
 
     def __init__(self, cfg: H2OConfig, prompt_lens, prompt_k, prompt_v, init_scores=None,
-                 stream=None):
+                 stream=None, workspace=None):
         import torch
         self.lib = load_library()
         self.cfg = cfg
@@ -214,6 +232,15 @@ class H2OCache:
             self._check_tensor(name, t, (total, self.Hkv, self.D), self.kv_torch)
         if init_scores is not None:
             self._check_tensor("init_scores", init_scores, (total, self.Hkv), torch.float64)
+        self._ws = None
+        if workspace is not None:
+            if not (workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous()):
+                raise ValueError("workspace: expected a contiguous cuda uint8 tensor")
+            cfg = H2OConfig.from_buffer_copy(cfg)
+            cfg.workspace = workspace.data_ptr()
+            cfg.workspace_bytes = workspace.numel()
+            self.cfg = cfg
+            self._ws = workspace
         self.ctx = C.c_void_p()
         rc = self.lib.h2o_init(C.byref(self.ctx), C.byref(cfg),
                                lens.ctypes.data_as(C.POINTER(C.c_int32)), _ptr(prompt_k),

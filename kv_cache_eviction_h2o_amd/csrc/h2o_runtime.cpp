@@ -44,7 +44,13 @@ struct h2o_ctx {
     std::vector<int> evb;      // pages evicted so far per sequence
     BlockArgs pend_blk{};      // the pending step's block eviction (h2o_compact)
     std::vector<int> pend_n;   // block eviction, step pending: counts before the eviction
-    std::vector<void*> allocs;
+    std::vector<void*> allocs;   // hipMalloc'd state (none when the caller gave a workspace)
+    // state placement: measure only (h2o_workspace_size), carve from the
+    // caller's workspace, or hipMalloc each buffer
+    bool measure = false;
+    size_t need = 0;
+    char* ws = nullptr;
+    size_t ws_bytes = 0, ws_used = 0;
     std::string err;
 };
 
@@ -172,6 +178,8 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
         return bad("unknown selector");
     }
     if (c->page_size != 0 && c->page_size != kPageSize) return bad("page_size must be 0 or 16");
+    if (c->workspace && (reinterpret_cast<uintptr_t>(c->workspace) & 255) != 0)
+        return bad("workspace must be 256-byte aligned");
     if (c->page_size) {
         if (!bf && !i8) return bad("the paged layout needs bf16 or i8 rows");
         if (c->batch > kMaxArgBatch) return bad("paged layout supports at most 128 sequences");
@@ -184,11 +192,25 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     return H2O_OK;
 }
 
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 template <typename T>
 int dalloc(h2o_ctx* c, T** p, size_t bytes, const char* what)
 {
     *p = nullptr;
     if (bytes == 0) return H2O_OK;
+    if (c->measure) {  // buffers start on 256-byte boundaries, as carved below
+        c->need = align256(c->need) + bytes;
+        return H2O_OK;
+    }
+    if (c->ws) {
+        const size_t off = align256(c->ws_used);
+        if (off > c->ws_bytes || bytes > c->ws_bytes - off)
+            return fail(c, H2O_EINVAL, std::string(what) + ": workspace too small");
+        *p = (T*)(c->ws + off);
+        c->ws_used = off + bytes;
+        return H2O_OK;
+    }
     void* v = nullptr;
     hipError_t e = hipMalloc(&v, bytes);
     if (e != hipSuccess) return hip_fail(c, e, what);
@@ -391,7 +413,6 @@ struct PromptScratch {
 constexpr int kMaxDevices = 64;
 PromptScratch g_prompt_scratch[kMaxDevices];
 
-constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // With s.mu held: at least `need` bytes of s, usable by work enqueued on st next.
 hipError_t scratch_take(PromptScratch& s, size_t need, hipStream_t st, char** out)
@@ -596,26 +617,16 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
 
 extern "C" {
 
-int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, const void* prompt_k,
-             const void* prompt_v, const double* init_scores, void* stream)
+// A context's host state and geometry from a validated configuration (no
+// device work): slots_total = K/V slots of the cache, maxP = longest prompt.
+int setup_ctx(h2o_ctx* c, const h2o_config* cfg, const int32_t* prompt_len, size_t& slots_total, int& maxP,
+              std::string& why)
 {
-    if (!out) return fail(nullptr, H2O_EINVAL, "null output pointer");
-    *out = nullptr;
-    std::string why;
-    int rc = validate(cfg, prompt_len, why);
-    if (rc != H2O_OK) return fail(nullptr, rc, why);
-    if (!prompt_k || !prompt_v) return fail(nullptr, H2O_EINVAL, "null prompt_k or prompt_v");
-    if (misaligned(prompt_k) || misaligned(prompt_v) || misaligned(init_scores))
-        return fail(nullptr, H2O_EINVAL, "prompt_k, prompt_v and init_scores must be 16-byte aligned");
-
-    h2o_ctx* c = new h2o_ctx();
     c->cfg = *cfg;
     const int B = cfg->batch, Hkv = cfg->n_kv_heads;
     c->plen.assign(prompt_len, prompt_len + B);
     c->count = c->plen;
-    int maxP = *std::max_element(c->plen.begin(), c->plen.end());
-    long long sumP = 0;
-    for (int p : c->plen) sumP += p;
+    maxP = *std::max_element(c->plen.begin(), c->plen.end());
 
     Geometry& g = c->g;
     g.B = B;
@@ -640,19 +651,13 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
     const double scale = cfg->scale > 0.f ? (double)cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
     c->qscale = (float)(scale * 1.4426950408889634);  // log2(e)
 
-    if (hipGetDevice(&c->device) != hipSuccess) {
-        delete c;
-        return fail(nullptr, H2O_EDEVICE, "no HIP device");
-    }
-
     // paged: the prompts' pages, from the pool
-    size_t slots_total;
     if (g.paged) {
         long long demand = 0;
         for (int p : c->plen) demand += (p + kPageSize - 1) / kPageSize;
         if (demand > cfg->max_pages) {
-            delete c;
-            return fail(nullptr, H2O_ENOMEM, "KV page pool too small for the prompts");
+            why = "KV page pool too small for the prompts";
+            return H2O_ENOMEM;
         }
         for (int p = cfg->max_pages - 1; p >= 0; --p) c->free_pages.push_back(p);
         c->pages.resize(B);
@@ -668,11 +673,21 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
         slots_total = (size_t)B * Hkv * g.cap;
     }
 
-    const size_t units = (size_t)B * Hkv;
-    const size_t sw = g.score_f64 ? 8 : 4;
+    return H2O_OK;
+}
+
+// Every device buffer of a context, in one list: sized (c->measure), carved from
+// the caller's workspace (c->ws) or allocated one by one.  t0 / poff receive the
+// prompt lengths' and offsets' buffers.
+int alloc_state(h2o_ctx* c, size_t slots_total, int32_t** t0, int64_t** poff)
+{
+    int rc = H2O_OK;
     State& s = c->s;
-    int32_t* t0 = nullptr;
-    int64_t* poff = nullptr;
+    const Geometry& g = c->g;
+    const h2o_config* cfg = &c->cfg;
+    const int B = g.B;
+    const size_t units = (size_t)B * g.Hkv;
+    const size_t sw = g.score_f64 ? 8 : 4;
     const size_t row_bytes = g.kv_i8 ? kRowBytesI8 : kRowBytes;
     if ((rc = dalloc(c, &s.kc, slots_total * row_bytes, "alloc K cache")) ||
         (rc = dalloc(c, &s.vc, slots_total * row_bytes, "alloc V cache")) ||
@@ -684,8 +699,8 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
         (rc = dalloc(c, &s.emass, units * 8, "alloc evicted mass")) ||
         (rc = dalloc(c, &s.vinfo, units * 8, "alloc victim info")) ||
         (rc = dalloc(c, &s.err, 4, "alloc error word")) ||
-        (rc = dalloc(c, &t0, (size_t)B * 4, "alloc prompt lengths")) ||
-        (rc = dalloc(c, &poff, (size_t)(B + 1) * 8, "alloc prompt offsets")) ||
+        (rc = dalloc(c, t0, (size_t)B * 4, "alloc prompt lengths")) ||
+        (rc = dalloc(c, poff, (size_t)(B + 1) * 8, "alloc prompt offsets")) ||
         (cfg->selector != H2O_SEL_BLOCK &&
          (rc = dalloc(c, &s.iscr, units * 2 * (size_t)g.cap * 4, "alloc compaction lists"))) ||
         (g.paged && (rc = dalloc(c, &s.bt, (size_t)B * g.maxp * 4, "alloc block table"))) ||
@@ -694,6 +709,55 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
           (rc = dalloc(c, &s.bimp, units * (size_t)bimp_stride(g.maxp), "alloc page importance")))) ||
         ((size_t)g.G * g.cap * 4 > (size_t)kLogitLdsBytes &&
          (rc = dalloc(c, &s.lscr, units * g.G * (size_t)g.cap * 4, "alloc logit scratch")))) {
+        return rc;
+    }
+    return H2O_OK;
+}
+
+int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, const void* prompt_k,
+             const void* prompt_v, const double* init_scores, void* stream)
+{
+    if (!out) return fail(nullptr, H2O_EINVAL, "null output pointer");
+    *out = nullptr;
+    std::string why;
+    int rc = validate(cfg, prompt_len, why);
+    if (rc != H2O_OK) return fail(nullptr, rc, why);
+    if (!prompt_k || !prompt_v) return fail(nullptr, H2O_EINVAL, "null prompt_k or prompt_v");
+    if (misaligned(prompt_k) || misaligned(prompt_v) || misaligned(init_scores))
+        return fail(nullptr, H2O_EINVAL, "prompt_k, prompt_v and init_scores must be 16-byte aligned");
+
+    h2o_ctx* c = new h2o_ctx();
+    size_t slots_total = 0;
+    int maxP = 0;
+    if ((rc = setup_ctx(c, cfg, prompt_len, slots_total, maxP, why)) != H2O_OK) {
+        delete c;
+        return fail(nullptr, rc, why);
+    }
+    const Geometry& g = c->g;
+    const int B = g.B;
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        return fail(nullptr, H2O_EDEVICE, "no HIP device");
+    }
+    if (cfg->workspace) {  // the caller's memory: check its size first, then carve
+        int32_t* t0m = nullptr;
+        int64_t* poffm = nullptr;
+        c->measure = true;
+        (void)alloc_state(c, slots_total, &t0m, &poffm);
+        c->measure = false;
+        if (cfg->workspace_bytes < c->need) {
+            const std::string m = "workspace_bytes " + std::to_string(cfg->workspace_bytes) +
+                                  " is below h2o_workspace_size (" + std::to_string(c->need) + ")";
+            delete c;
+            return fail(nullptr, H2O_EINVAL, m);
+        }
+        c->ws = static_cast<char*>(cfg->workspace);
+        c->ws_bytes = (size_t)cfg->workspace_bytes;
+    }
+    State& s = c->s;
+    int32_t* t0 = nullptr;
+    int64_t* poff = nullptr;
+    if ((rc = alloc_state(c, slots_total, &t0, &poff)) != H2O_OK) {
         std::string why_alloc = c->err;
         free_all(c);
         delete c;
@@ -744,8 +808,26 @@ int h2o_init(h2o_ctx** out, const h2o_config* cfg, const int32_t* prompt_len, co
         delete c;
         return r;
     }
-    (void)sumP;
     *out = c;
+    return H2O_OK;
+}
+
+int h2o_workspace_size(const h2o_config* cfg, const int32_t* prompt_len, uint64_t* bytes)
+{
+    if (!bytes) return fail(nullptr, H2O_EINVAL, "null bytes");
+    *bytes = 0;
+    std::string why;
+    int rc = validate(cfg, prompt_len, why);
+    if (rc != H2O_OK) return fail(nullptr, rc, why);
+    h2o_ctx c;
+    size_t slots_total = 0;
+    int maxP = 0;
+    if ((rc = setup_ctx(&c, cfg, prompt_len, slots_total, maxP, why)) != H2O_OK) return fail(nullptr, rc, why);
+    int32_t* t0 = nullptr;
+    int64_t* poff = nullptr;
+    c.measure = true;
+    (void)alloc_state(&c, slots_total, &t0, &poff);
+    *bytes = (uint64_t)c.need;
     return H2O_OK;
 }
 

@@ -139,6 +139,33 @@ def test_c_client_compiles_against_the_header(tmp_path):
     assert r.returncode == 0, r.stderr
 
 
+def test_workspace_size_host_logic(lib):
+    """h2o_workspace_size validates like h2o_init, needs no device, covers at
+    least the K and V rows of every slot, and grows with the batch."""
+    cfg = L.make_config(**GOOD)
+    n2 = L.workspace_size(cfg, [100, 200])
+    assert n2 >= 2 * 2 * 2 * 200 * 256  # K and V, 2 sequences x 2 KV heads x >= 200 slots x 256 B
+    cfg3 = L.make_config(**{**GOOD, "batch": 3})
+    assert L.workspace_size(cfg3, [100, 200, 300]) > n2
+    paged = L.make_config(**{**GOOD, "page_size": 16, "max_pages": 64})
+    assert L.workspace_size(paged, [100, 200]) >= 64 * 2 * 16 * 256 * 2
+    with pytest.raises(L.H2OError) as ex:
+        L.workspace_size(L.make_config(**{**GOOD, "page_size": 16, "max_pages": 4}), [100, 200])
+    assert ex.value.code == L.H2O_ENOMEM
+    with pytest.raises(L.H2OError) as ex:
+        L.workspace_size(L.make_config(**{**GOOD, "n_q_heads": 7}), [100, 200])
+    assert ex.value.code == L.H2O_EINVAL
+
+
+def test_init_rejects_misaligned_workspace(lib):
+    cfg = L.make_config(**GOOD)
+    cfg.workspace = 4096 + 128
+    cfg.workspace_bytes = 1 << 30
+    rc, ctx = _init(lib, cfg, [10, 20])
+    assert rc == L.H2O_EINVAL and not ctx.value
+    assert "256-byte aligned" in lib.h2o_last_error(None).decode()
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
     mod = importlib.import_module("kv_cache_eviction_h2o_amd._lib")

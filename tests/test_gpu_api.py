@@ -123,3 +123,53 @@ def test_page_pool_exhaustion_is_refused_and_recoverable_state():
     for x, y in zip(before, after):
         assert np.array_equal(x, y)
     c.close()
+
+
+@pytest.mark.parametrize("wname", ["opt_rows", "gqa_tiles", "paged", "block", "random", "int8"])
+def test_workspace_context_matches_library_allocated(wname):
+    """A context whose state lives in a caller's workspace (filled with 0xAB
+    first, so nothing may rely on zeroed memory) steps bit-identically to one
+    whose state the library allocates; a workspace one byte short is refused."""
+    import torch
+    from kv_cache_eviction_h2o_amd import _lib as L
+    w = {"opt_rows": WL.OPT_LAYER.scaled(batch=2, n_q_heads=4, n_kv_heads=4),
+         "gqa_tiles": WL.LLAMA_GQA.scaled(batch=2, budget_fixed=100, hh_fixed=48),
+         "paged": WL.PAGED_MIXED.scaled(batch=2, n_q_heads=4, n_kv_heads=4),
+         "block": WL.PAGED_BLOCK.scaled(batch=2, n_q_heads=4, n_kv_heads=4),
+         "random": WL.RANDOM_ATTN.scaled(batch=2, n_q_heads=8, n_kv_heads=2, rand_k=24, rand_r=8),
+         "int8": WL.OPT_LAYER_I8.scaled(batch=2, n_q_heads=4, n_kv_heads=4)}[wname]
+    lens, steps = ([400, 150] if wname != "random" else [40, 30]), 40
+    import parity
+    K, V = S.prompt_kv(w.recipe, 0, lens, w.n_kv_heads)
+    cfg = L.config_from_workload(w, max_len=max(lens) + steps + 1)
+    if w.page_size:
+        cfg.max_pages = L.pages_needed(lens, steps, cfg)
+    dk, dv = parity.to_dev(K, w.recipe.kv_dtype), parity.to_dev(V, w.recipe.kv_dtype)
+    n = L.workspace_size(cfg, lens)
+    print(f"[workspace] {wname}: {n} bytes", flush=True)
+    with pytest.raises(L.H2OError) as ex:
+        L.H2OCache(cfg, lens, dk, dv, workspace=torch.empty(n - 1, dtype=torch.uint8, device="cuda"))
+    assert ex.value.code == L.H2O_EINVAL and "h2o_workspace_size" in str(ex.value)
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+    a = L.H2OCache(cfg, lens, dk, dv)
+    b = L.H2OCache(cfg, lens, dk, dv, workspace=ws)
+    q, k, v = S.step_window(w.recipe, 0, lens, steps, w.n_q_heads, w.n_kv_heads)
+    qd = torch.from_numpy(q).cuda()
+    kd, vd = parity.to_dev(k, w.recipe.kv_dtype), parity.to_dev(v, w.recipe.kv_dtype)
+    oa = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    for i in range(steps):
+        if i % 3 == 2:
+            for c, o in ((a, oa), (b, ob)):
+                c.step(qd[i], kd[i], vd[i], o)
+                c.compact()
+        else:
+            a.step_compact(qd[i], kd[i], vd[i], oa)
+            b.step_compact(qd[i], kd[i], vd[i], ob)
+        assert torch.equal(oa, ob), i
+    _same(a, b)
+    for x, y in zip(a.read_kv(), b.read_kv()):
+        assert (x is None and y is None) or np.array_equal(x, y)
+    a.close()
+    b.close()
+    assert int(ws[:16].sum()) >= 0  # the caller's memory is still the caller's
