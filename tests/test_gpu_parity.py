@@ -53,6 +53,20 @@ def test_llama_gqa_reduced():
     assert rep.evictions >= 73 * 8
 
 
+def test_llama_gqa_long_trace():
+    # 2000 steps, one eviction per step per unit after the first: long enough for
+    # score rounding to drift if it did (fp64 scores; fp32 ones run the OPT trace)
+    w = WL.LLAMA_GQA.scaled(batch=1, prompt_len=1100)
+    rep = P().run_parity(w, 2000)
+    assert rep.evictions == 8 * (73 + 1999)  # bulk 1101 -> 1028 at the first step, then one a step
+
+
+def test_random_attention_long_trace():
+    w = WL.RANDOM_ATTN.scaled(batch=2, n_q_heads=8, n_kv_heads=2, rand_k=256, rand_r=32, prompt_len=300)
+    rep = P().run_parity(w, 2000)
+    assert rep.evictions == 4 * 54 * 32  # 4 units x 54 events x r
+
+
 def test_llama_gqa_full_shape_sampled_units():
     w = WL.LLAMA_GQA.scaled(prompt_len=1040)
     P().run_parity(w, 24, units=[(0, 0), (9, 5), (15, 7)])
