@@ -113,6 +113,12 @@ def test_block_int8_rows():
     assert rep.evictions > 0
 
 
+def test_block_long_trace():
+    # 2000 fused steps: pages evicted, pushed on the free stack and popped again
+    rep = _run(PB.scaled(batch=3, n_q_heads=4, n_kv_heads=4), 2000, [700, 1500, 3000])
+    assert rep.evictions > 0
+
+
 def test_block_full_shape_sampled_sequences():
     """The benchmark's shape and launch configuration (64 sequences of 4k-64k
     prompts, 32 heads, fused entry point, device-drawn inputs): the two

@@ -67,6 +67,14 @@ def test_random_attention_long_trace():
     assert rep.evictions == 4 * 54 * 32  # 4 units x 54 events x r
 
 
+def test_paged_mixed_long_trace():
+    # 2000 steps at the 20 % budget: four evictions every five steps, pages
+    # returned and reused throughout
+    w = WL.PAGED_MIXED.scaled(batch=3, n_q_heads=4, n_kv_heads=4)
+    rep = P().run_parity(w, 2000, lens=[700, 1500, 3000])
+    assert rep.evictions > 0
+
+
 def test_llama_gqa_full_shape_sampled_units():
     w = WL.LLAMA_GQA.scaled(prompt_len=1040)
     P().run_parity(w, 24, units=[(0, 0), (9, 5), (15, 7)])
