@@ -192,8 +192,8 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
                 const unsigned so = (unsigned)(base + grp) * 4u;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (int)(so + u * NGRP * 4), 0, 0));
-                    vs[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (int)(so + u * NGRP * 4), 0, 0));
+                    ks[u] = buf_load4f(rks, so + (unsigned)(u * NGRP * 4));
+                    vs[u] = buf_load4f(rvs, so + (unsigned)(u * NGRP * 4));
                 }
             }
         } else {
@@ -202,15 +202,15 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
             for (int u = 0; u < U; ++u) {
                 const int j = base + grp + NGRP * u;
                 r[u] = sidx(j < n ? j : 0);
-                kr[u] = kc[r[u] * kRowVecs + sub];
+                kr[u] = stream_load(kc + r[u] * kRowVecs + sub);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) vr[u] = vc[r[u] * kRowVecs + sub];
+            for (int u = 0; u < U; ++u) vr[u] = stream_load(vc + r[u] * kRowVecs + sub);
             if constexpr (Row::SCALED) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    ks[u] = S.kss[r[u]];
-                    vs[u] = S.vss[r[u]];
+                    ks[u] = stream_load(S.kss + r[u]);
+                    vs[u] = stream_load(S.vss + r[u]);
                 }
             }
         }
