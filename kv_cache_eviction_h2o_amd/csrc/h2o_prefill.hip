@@ -26,6 +26,8 @@
 // exactly; logits keep ~16 significant bits of q.
 #include "h2o_device.h"
 
+#include <algorithm>
+
 namespace h2o {
 namespace {
 
@@ -431,10 +433,14 @@ __global__ void __launch_bounds__(256) snapkv_pool_kernel(const SnapArgs a)
 }
 
 constexpr int kSNT = 256;
+constexpr int kSnapStage = 4096;  // prefix positions whose pooled votes are staged in LDS
 
 __global__ void __launch_bounds__(kSNT) snapkv_select_kernel(const SnapArgs a)
 {
-    extern __shared__ unsigned bits[];  // one bit per prompt position: kept
+    // one bit per prompt position (kept), then the pooled votes of the head in
+    // hand when the prefix has at most a.stage_n positions: the radix passes
+    // read them from LDS instead of a strided global column each pass
+    extern __shared__ __align__(16) unsigned bits[];
     __shared__ RadixSmem s_rad;
     __shared__ ScanSmem s_scan;
     const int unit = blockIdx.x, b = unit / a.Hkv, h = unit - b * a.Hkv;
@@ -442,15 +448,21 @@ __global__ void __launch_bounds__(kSNT) snapkv_select_kernel(const SnapArgs a)
     const int64_t off = a.seq_off[b];
     const int tid = threadIdx.x;
     const int nw = (P + 31) / 32;
+    double* stage = reinterpret_cast<double*>(bits + a.bits_words);
+    const bool staged = Pp <= a.stage_n;
     for (int i = tid; i < nw; i += kSNT) bits[i] = 0u;
     __syncthreads();
     const int e = Pp - a.keep;  // prefix positions each head leaves out
     for (int g = 0; g < a.G; ++g) {
         const int hq = h * a.G + g;
+        if (staged && e > 0) {
+            for (int j = tid; j < Pp; j += kSNT) stage[j] = a.pooled[(size_t)(off + j) * a.Hq + hq];
+            __syncthreads();
+        }
         // keys as in the decode step's bulk selection: (vote bits, ~position);
         // the e smallest go, so equal votes keep the lower position
         auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
-            const unsigned long long u = ord64(a.pooled[(size_t)(off + j) * a.Hq + hq]);
+            const unsigned long long u = ord64(staged ? stage[j] : a.pooled[(size_t)(off + j) * a.Hq + hq]);
             wk[2] = (unsigned)(u >> 32);
             wk[1] = (unsigned)u;
             wk[0] = ~(unsigned)j;
@@ -486,7 +498,13 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
     hipLaunchKernelGGL(snapkv_pool_kernel, dim3((unsigned)((cells + 255) / 256), a.B), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t dyn = (size_t)((max_p + 31) / 32) * 4;
+    // bits of the longest prompt, then the staged votes of prefixes up to kSnapStage
+    SnapArgs b = a;
+    b.bits_words = ((max_p + 31) / 32 + 3) & ~3;  // whole 16-byte groups, so the votes stay aligned
+    int max_pp = 0;
+    for (int i = 0; i < a.B; ++i) max_pp = std::max(max_pp, a.seq_p[i] - a.seq_w[i]);
+    b.stage_n = std::min(max_pp, kSnapStage);
+    const size_t dyn = (size_t)b.bits_words * 4 + (size_t)b.stage_n * 8;
     static size_t dyn_set = 48 * 1024;
     if (dyn > dyn_set) {
         e = hipFuncSetAttribute((const void*)snapkv_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -494,7 +512,7 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
         if (e != hipSuccess) return e;
         dyn_set = dyn;
     }
-    hipLaunchKernelGGL(snapkv_select_kernel, dim3(a.B * a.Hkv), dim3(kSNT), dyn, st, a);
+    hipLaunchKernelGGL(snapkv_select_kernel, dim3(a.B * a.Hkv), dim3(kSNT), dyn, st, b);
     return hipGetLastError();
 }
 
