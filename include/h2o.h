@@ -61,9 +61,13 @@
  *     context is unchanged (H2O_EDEVICE aside).  h2o_last_error() gives the
  *     message.  One context must not be used from two threads at once;
  *     different contexts are independent.
- *   - Ownership: the library owns the context and all its device state
- *     (allocated with hipMalloc on the device current at h2o_init);
- *     h2o_destroy frees it.  The caller owns every pointer it passes.
+ *   - Ownership: the library owns the context and its device state,
+ *     allocated with hipMalloc on the device current at h2o_init and freed
+ *     by h2o_destroy -- unless h2o_config::workspace is given, in which case
+ *     the state is carved from that caller-owned memory and nothing is
+ *     allocated.  The prompt calls (h2o_prefill_scores, h2o_snapkv_select)
+ *     keep one scratch buffer per device for the life of the process.  The
+ *     caller owns every pointer it passes.
  */
 #ifndef H2O_H
 #define H2O_H
