@@ -329,7 +329,7 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
         std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return c->count[x] > c->count[y]; });
         for (int i = 0; i < B; ++i) a.seq_order[i] = (uint8_t)ord[i];
     }
-    std::vector<int> got;  // pages taken in this call (rolled back on failure)
+    std::vector<int> got;  // sequences given a page in this call (returned if the launch fails)
     if (c->block) {
         // every block-table entry but the last is full: a sequence needs a page
         // when its count is a multiple of 16; pages come off the device stack
@@ -359,10 +359,17 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
                 c->free_pages.pop_back();
                 c->pages[b].push_back(p);
                 a.newpage[b] = p;
+                got.push_back(b);
             }
     }
     hipError_t err = launch_step(a, max_n_att, (hipStream_t)stream);
-    if (err != hipSuccess) return hip_fail(c, err, "step kernel launch");
+    if (err != hipSuccess) {  // nothing ran: the pages go back as they came
+        for (auto it = got.rbegin(); it != got.rend(); ++it) {
+            c->free_pages.push_back(c->pages[*it].back());
+            c->pages[*it].pop_back();
+        }
+        return hip_fail(c, err, "step kernel launch");
+    }
     if (c->block) {
         for (int b = 0; b < B; ++b) c->ftop -= (c->count[b] & (kPageSize - 1)) == 0 ? 1 : 0;
         BlockArgs ba = plan_blocks(c);  // updates counts, evicted pages and the stack depth
