@@ -185,7 +185,9 @@ int h2o_step_compact(h2o_ctx *ctx, const float *q, const void *k_new, const void
  *   evicted_mass  host [B][Hkv] fp64 summed scores of evicted tokens; NULL to skip.
  *   cap           entries per (b, h) in pos/scores; must be >= every count.
  * With block eviction a pending step may be read: the state after the append,
- * before any page goes (the scores the page ranking will use).
+ * before any page goes (the scores the page ranking will use).  A read is not
+ * a hot-path call: it allocates device staging of 12 bytes per entry
+ * (B x Hkv x cap) for its duration, also for a context in a caller workspace.
  * Errors: H2O_EINVAL (cap too small), H2O_ESTATE (a compaction is pending,
  * block eviction aside), H2O_EDEVICE. */
 int h2o_read_indices(h2o_ctx *ctx, int32_t *pos, int32_t *count, double *scores,
@@ -199,7 +201,8 @@ int h2o_read_indices(h2o_ctx *ctx, int32_t *pos, int32_t *count, double *scores,
  *   k_scale, v_scale  host [B][Hkv][cap] fp32 row scales (H2O_I8; ignored and
  *                     may be NULL otherwise).
  *   cap               entries per (b, h); must be >= every count.
- * A pending block-eviction step reads as in h2o_read_indices.
+ * A pending block-eviction step reads as in h2o_read_indices.  Allocates
+ * device staging for the rows (and positions) for its duration.
  * Errors: H2O_EINVAL, H2O_ESTATE (a compaction is pending, block eviction
  * aside), H2O_EDEVICE. */
 int h2o_read_kv(h2o_ctx *ctx, void *k_rows, void *v_rows, float *k_scale, float *v_scale, size_t cap,
