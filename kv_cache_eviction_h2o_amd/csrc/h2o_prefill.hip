@@ -145,7 +145,10 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
         ksm[buf][w][2][lane] = st2;                                                              \
         ksm[buf][w][3][lane] = st3;                                                              \
     } while (0)
-    auto rows = [&](int kt, int buf) {
+    // masked: the tile may hold keys after some of the wave's positions
+    // (the causal diagonal); the other tiles skip the per-score test
+    auto rows = [&](int kt, int buf, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
         const int key = 16 * kt + lc;
         bf16x8 bt[4];
 #pragma unroll
@@ -158,8 +161,8 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) c = mma(qop[pt][g][kb], bt[kb], c);
-                const float s[2] = {key <= pos0 ? c[0] + c[1] : -INFINITY,
-                                    key <= pos1 ? c[2] + c[3] : -INFINITY};
+                const float s[2] = {(!MASK || key <= pos0) ? c[0] + c[1] : -INFINITY,
+                                    (!MASK || key <= pos1) ? c[2] + c[3] : -INFINITY};
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const float M = fmaxf(m[pt][g][r], s[r]);
@@ -177,7 +180,10 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
     for (int c = 0; c < nch; ++c) {
         const int buf = c & 1;
         const int kt_end = min((c + 1) * kRCK, nkt_w);
-        for (int kt = c * kRCK; kt < kt_end; ++kt) rows(kt, buf);
+        for (int kt = c * kRCK; kt < kt_end; ++kt) {
+            if (16 * kt + 15 <= base) rows(kt, buf, std::false_type{});  // every key before every row
+            else rows(kt, buf, std::true_type{});
+        }
         // chunk c + 1 into the other buffer, which every wave finished reading
         // before the previous barrier
         if (c + 1 < nch) H2O_ROWS_PUT(buf ^ 1);
@@ -326,7 +332,10 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
         }                                                                                               \
         if (tid < CQ * G * 4) ssm0[(buf) * SB + tid] = ss;                                              \
     } while (0)
-    auto tile = [&](int t8, int ci, int buf) {
+    // masked: the tile may hold rows before some of the wave's keys, or rows
+    // outside [lo, P); the other tiles skip the per-score test
+    auto tile = [&](int t8, int ci, int buf, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
         const int pos0 = 8 * t8 + 2 * lg, pos1 = pos0 + 1;
         const bool r0 = pos0 < P && pos0 >= lo, r1 = pos1 < P && pos1 >= lo;
         float tacc[kKT][NA];
@@ -346,8 +355,8 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) c = mma(q4[kb], as_bf16x8(kt4[x][kb]), c);
-                const float p0 = (r0 && key <= pos0) ? fast_exp2(c[0] + c[1] - sv.x) * sv.y : 0.f;
-                const float p1 = (r1 && key <= pos1) ? fast_exp2(c[2] + c[3] - sv.z) * sv.w : 0.f;
+                const float p0 = (!MASK || (r0 && key <= pos0)) ? fast_exp2(c[0] + c[1] - sv.x) * sv.y : 0.f;
+                const float p1 = (!MASK || (r1 && key <= pos1)) ? fast_exp2(c[2] + c[3] - sv.z) * sv.w : 0.f;
                 tacc[x][PH ? g : 0] += p0 + p1;
             }
         }
@@ -366,7 +375,11 @@ __global__ void __launch_bounds__(kCNT) colsum_cols_kernel(const ColsumArgs a)
 #pragma unroll
         for (int ci = 0; ci < CQ; ++ci) {
             const int t8 = t0 + ci;
-            if (t8 >= t_first_w && t8 <= t_last) tile(t8, ci, buf);
+            if (t8 >= t_first_w && t8 <= t_last) {
+                // rows 8 t8 .. +7 all after the wave's last key and inside [lo, P)
+                if (8 * t8 >= k0 + 16 * kKT - 1 && 8 * t8 >= lo && 8 * t8 + 7 < P) tile(t8, ci, buf, std::false_type{});
+                else tile(t8, ci, buf, std::true_type{});
+            }
         }
         // chunk c + 1 into the other buffer, which every wave finished reading
         // before the previous barrier
