@@ -44,8 +44,10 @@ from kv_cache_eviction_h2o_amd import workloads as WL  # noqa: E402
 METRIC = "retained KV tokens processed/sec per decode step (attn+evict+compact); % HBM peak"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc")
-KERNEL_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip", "h2o_prefill.hip",
-               "h2o_block.hip")
+# device sources of the decode-step kernels, and of the prompt calls' kernels
+STEP_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip", "h2o_block.hip")
+PROMPT_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_prefill.hip")
+PROMPT_KERNELS = ("colsum_", "snapkv_")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -54,7 +56,7 @@ def summarize(args) -> None:
     import csv
     n_last = args.steps * (args.layers or 32)
     kname = args.summarize_kernel
-    out = [f"kernel_source_sha256_16: {kernel_hash()}"]
+    out = [f"kernel_source_sha256_16: {kernel_hash(prompt=kname.startswith(PROMPT_KERNELS))}"]
     if args.summarize_trace:
         rows = [r for r in csv.DictReader(open(args.summarize_trace)) if kname in r["Kernel_Name"]]
         d = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows], dtype=np.float64)
@@ -153,10 +155,11 @@ class HipEvents:
         self.lib.hipEventDestroy(e)
 
 
-def kernel_hash() -> str:
-    """Hash of every device source (a counter summary is valid for this value only)."""
+def kernel_hash(prompt: bool = False) -> str:
+    """Hash of the device sources the decode-step kernels (or, with prompt, the
+    prompt calls' kernels) are built from: a summary is valid for this value only."""
     h = hashlib.sha256()
-    for name in KERNEL_SRCS:
+    for name in PROMPT_SRCS if prompt else STEP_SRCS:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -349,7 +352,7 @@ def prefill_main(args, w):
                      "note": "algorithmic = the causal logits q.k once; the kernels compute them in "
                              "two passes, each on the bf16 hi and lo parts of q"},
         "cpu_baseline": cpu,
-        "kernel_source_sha256_16": kernel_hash(),
+        "kernel_source_sha256_16": kernel_hash(prompt=True),
     }
     print(json.dumps(line), flush=True)
 
@@ -419,7 +422,7 @@ def snapkv_main(args, w):
                      "traffic": None, "mean_call_us": round(per_call * 1e6, 2), "algorithmic_flops": flops,
                      "note": "the window rows' causal logits once; the call also pools and selects"},
         "cpu_baseline": None,
-        "kernel_source_sha256_16": kernel_hash(),
+        "kernel_source_sha256_16": kernel_hash(prompt=True),
     }
     print(json.dumps(line), flush=True)
 
