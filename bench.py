@@ -434,7 +434,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build runs the decode step on a single MI355X "
+        print(f"bench.py measures one GPU: the library runs the decode step on a single MI355X "
               f"and has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
               file=sys.stderr)
         sys.exit(2)

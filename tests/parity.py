@@ -80,17 +80,41 @@ def make_cache(w: WL.Workload, lens, n_steps: int, layer: int = 0, init_scores=N
 
 
 def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=True, layer=0,
-               init_scores=None, read_every=1, check_scores=True) -> ParityReport:
-    """Run n_steps on the GPU and in the oracle (for `units`, default all)."""
+               init_scores=None, read_every=1, check_scores=True, device_inputs=False,
+               stored_rows=True, properties=False) -> ParityReport:
+    """Run n_steps on the GPU and in the oracle (for `units`, default all).
+
+    device_inputs: prompts and steps drawn on the device (the benchmark's
+    generator, for full-size batches); the checked units' rows are copied back
+    for the oracle, and reads are sized by the host mirror of the counts.
+    stored_rows: check the stored rows of the checked units at the end.
+    properties: after the last step, check every unit for what holds at any
+    size (h2o_properties)."""
     import torch
     lens = list(lens) if lens is not None else WL.prompt_lengths(w)
     B, Hq, Hkv, G, D = w.batch, w.n_q_heads, w.n_kv_heads, w.group, w.head_dim
     assert len(lens) == B
     say(f"[parity] {w.name} B={B} Hq={Hq} Hkv={Hkv} D={D} lens={lens[:6]}{'...' if B > 6 else ''} "
         f"steps={n_steps} fused={fused} units={'all' if units is None else len(units)}")
-    cache, K, V = make_cache(w, lens, n_steps, layer, init_scores)
     off = np.concatenate([[0], np.cumsum(lens)])
     units = [(b, h) for b in range(B) for h in range(Hkv)] if units is None else list(units)
+    if device_inputs:
+        from kv_cache_eviction_h2o_amd import _lib as L
+        from kv_cache_eviction_h2o_amd import metrics as M
+        assert init_scores is None
+        pk, pv = S.device_prompt_kv(w.recipe, layer, lens, Hkv)
+        cfg = L.config_from_workload(w, max_len=max(lens) + n_steps + 1)
+        if w.page_size:
+            cfg.max_pages = L.pages_needed(lens, n_steps, cfg)
+        cache = L.H2OCache(cfg, lens, pk, pv)
+        seqs = sorted({b for b, _ in units})
+        K = _Rows(off, {b: _host_bits(pk[off[b]:off[b + 1]]) for b in seqs})
+        V = _Rows(off, {b: _host_bits(pv[off[b]:off[b + 1]]) for b in seqs})
+        del pk, pv
+        cap = int(max(M.retained_counts(w, P, n_steps)["count"].max() for P in lens))
+    else:
+        cache, K, V = make_cache(w, lens, n_steps, layer, init_scores)
+        cap = cache.info()[0]
     ocfg = O.cfg_from_workload(w)
     orc = {}
     for (b, h) in units:
@@ -99,17 +123,21 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
                              oracle_rows(w, V[off[b]:off[b + 1], h]),
                              lens[b] + n_steps + 1, init_scores=isc)
     rep = ParityReport(units=len(units))
-    cap = cache.info()[0]
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     win = 256
     gen_k, gen_v = [], []  # generated rows of the decode steps, for the stored-row check
     for s0 in range(0, n_steps, win):
         ns = min(win, n_steps - s0)
-        q, k, v = S.step_window(w.recipe, layer, [p + s0 for p in lens], ns, Hq, Hkv)
+        t0 = [p + s0 for p in lens]
+        if device_inputs:
+            qd, kd, vd = S.device_step_window(w.recipe, layer, t0, ns, Hq, Hkv)
+            q, k, v = qd.cpu().numpy(), _host_bits(kd), _host_bits(vd)
+        else:
+            q, k, v = S.step_window(w.recipe, layer, t0, ns, Hq, Hkv)
+            qd = torch.from_numpy(q).cuda()
+            kd, vd = to_dev(k, w.recipe.kv_dtype), to_dev(v, w.recipe.kv_dtype)
         gen_k.append(k)
         gen_v.append(v)
-        qd = torch.from_numpy(q).cuda()
-        kd, vd = to_dev(k, w.recipe.kv_dtype), to_dev(v, w.recipe.kv_dtype)
         for i in range(ns):
             s = s0 + i
             if fused:
@@ -166,7 +194,10 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
                     assert abs(em[b, h] - o_em) <= SCORE_TOL * max(1.0, o_em), \
                         f"step {s} unit {(b, h)}: evicted mass {em[b, h]} vs {o_em}"
             rep.steps += 1
-    check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v)
+    if stored_rows:
+        check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v, cap=cap)
+    if properties:
+        h2o_properties(w, cache, lens, n_steps, cap=cap)
     cache.close()
     say(f"[parity] ok: checked {rep.steps} steps x {rep.units} units, max out err "
         f"{rep.max_out_err:.2e}, max score err {rep.max_score_err:.2e}, evictions {rep.evictions}, "
@@ -381,6 +412,35 @@ def _host_bits(t):
     if t.dtype == torch.bfloat16:
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     return t.contiguous().cpu().numpy()
+
+
+def h2o_properties(w: WL.Workload, cache, lens, steps_done: int, cap=None):
+    """What holds for every (sequence, KV head) unit after steps_done steps of
+    token-level H2O with no initial scores, at any size: the count is the host
+    mirror's min(n_att, K_t) at every step; positions are ascending, distinct
+    and before the sequence's length; the sinks and the recent window are all
+    retained; and retained scores plus evicted mass equal G x steps_done (each
+    query head's softmax adds a total weight of 1 per step)."""
+    from kv_cache_eviction_h2o_amd import metrics as M
+    assert w.selector == "h2o"
+    pos, cnt, sc, em = cache.read_indices(cap)
+    ocfg = O.cfg_from_workload(w)
+    for b in range(w.batch):
+        length = lens[b] + steps_done
+        n = int(cnt[b])
+        assert n == int(M.retained_counts(w, lens[b], steps_done)["count"][-1]), f"seq {b}: count {n}"
+        _, _, W = O.schedule(ocfg, length)
+        p = pos[b, :, :n].astype(np.int64)  # [Hkv][n]
+        assert np.all(np.diff(p, axis=1) > 0), f"seq {b}: positions not ascending"
+        assert p.min() >= 0 and p.max() < length, f"seq {b}: position out of range"
+        ns = min(w.n_sink, length)
+        assert np.all(p[:, :ns] == np.arange(ns)), f"seq {b}: a sink is missing"
+        nw = min(W, length)
+        assert nw == 0 or np.all(p[:, n - nw:] == np.arange(length - nw, length)), f"seq {b}: window incomplete"
+        mass = sc[b, :, :n].sum(axis=1) + em[b]
+        want = float(w.group * steps_done)
+        assert np.all(np.abs(mass - want) <= 1e-4 * want), f"seq {b}: mass {mass.min()}..{mass.max()}, want {want}"
+    say(f"[parity] properties ok for {w.batch} x {w.n_kv_heads} units after {steps_done} steps")
 
 
 def block_properties(w: WL.Workload, cache, lens, steps_done: int, cap=None):

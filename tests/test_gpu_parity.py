@@ -256,3 +256,18 @@ def test_int8_gqa_group_of_four_and_random():
                                prompt_len=40)
     rep = P().run_parity(wr, 120)
     assert rep.evictions == 4 * 3 * 16  # events after steps 79, 95, 111 (K + r = 80 generated)
+
+
+# ------------------------------------------- paged workload at its full shape
+def test_paged_mixed_full_shape_sampled_units():
+    """The paged workload's shape and launch configuration (64 sequences of
+    4k-64k prompts, 32 KV heads, fused entry point, device-drawn inputs): three
+    heads of each of the two shortest sequences against the oracle, then every
+    unit for the properties that hold at any size."""
+    w = WL.PAGED_MIXED
+    lens = WL.prompt_lengths(w)
+    seqs = [int(x) for x in np.argsort(lens)[:2]]
+    units = [(b, h) for b in seqs for h in (0, 13, w.n_kv_heads - 1)]
+    rep = P().run_parity(w, 24, lens=lens, units=units, device_inputs=True, stored_rows=False,
+                         read_every=4, properties=True)
+    assert rep.evictions > 0
