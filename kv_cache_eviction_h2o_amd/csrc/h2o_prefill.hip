@@ -10,7 +10,7 @@
 // A row's weights need its softmax maximum and sum over all of its keys
 // before any column can take them, so there are two passes:
 //   rows   one workgroup per (unit, 4 waves x 8 PT query positions; PT = 4 / G
-//          for small groups, else 1):
+//          for small groups, else 1, and 1 when at most a 128-row window is scored):
 //          S = Q_tile (8 positions x hi/lo = 16 rows) . K_tile^T (16 keys)
 //          with v_mfma_f32_16x16x32_bf16 over 4 k-steps, hi + lo added in the
 //          lane (rows 2p and 2p+1 of the C layout); online max / sum per lane
@@ -56,14 +56,17 @@ __device__ inline void ms_stage(float& m, float& l)
 template <int G>
 struct RowsTune {
     static constexpr int PT = G >= 4 ? 1 : 4 / G;
+    // with only a window of rows to score (at most 128 per sequence, as for
+    // SnapKV's observation window) one tile per wave: the window's rows then
+    // spread over all four waves of a workgroup instead of landing on one
+    static constexpr int PT_WINDOW = 1;
 };
 
 constexpr int kRCK = 4;  // rows pass: 16-key tiles per LDS chunk
 
-template <int G>
+template <int G, int PT>
 __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
 {
-    constexpr int PT = RowsTune<G>::PT;
     // K chunks in B-operand order: [buffer][tile][k-step][lane], lane (lg, lc)
     // holding key 16 tile + lc, elements 32 kb + 8 lg .. +8
     __shared__ uint4 ksm[2][kRCK][4][64];
@@ -163,11 +166,16 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
                 for (int kb = 0; kb < 4; ++kb) c = mma(qop[pt][g][kb], bt[kb], c);
                 const float s[2] = {(!MASK || key <= pos0) ? c[0] + c[1] : -INFINITY,
                                     (!MASK || key <= pos1) ? c[2] + c[3] : -INFINITY};
+                // one exp2 per score: with d = s - m, either the sum takes
+                // 2^d (d <= 0, the maximum stays) or it is rescaled by 2^-d
+                // and takes 2^0 = 1 (d > 0, s is the new maximum)
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const float M = fmaxf(m[pt][g][r], s[r]);
-                    l[pt][g][r] = l[pt][g][r] * fast_exp2(m[pt][g][r] - M) + fast_exp2(s[r] - M);
-                    m[pt][g][r] = M;
+                    const float d = s[r] - m[pt][g][r];
+                    const float e = fast_exp2(-fabsf(d));
+                    const bool up = d > 0.f;
+                    l[pt][g][r] = up ? fmaf(l[pt][g][r], e, 1.f) : l[pt][g][r] + e;
+                    m[pt][g][r] = up ? s[r] : m[pt][g][r];
                 }
             }
         }
@@ -414,9 +422,14 @@ template <int G>
 hipError_t launch_colsum_g(const ColsumArgs& a, int max_p, hipStream_t st)
 {
     const unsigned units = (unsigned)(a.B * a.Hkv);
-    const int rows_per_wg = 4 * 8 * RowsTune<G>::PT, keys_per_wg = 4 * 16 * kKT;
-    hipLaunchKernelGGL((colsum_rows_kernel<G>), dim3(units, (max_p + rows_per_wg - 1) / rows_per_wg),
-                       dim3(kCNT), 0, st, a);
+    constexpr int PTF = RowsTune<G>::PT, PTW = RowsTune<G>::PT_WINDOW;
+    const bool window = a.nt8 <= 16;  // at most 128 rows per sequence from row lo on
+    const int rows_per_wg = 4 * 8 * (window ? PTW : PTF), keys_per_wg = 4 * 16 * kKT;
+    const dim3 gr(units, (max_p + rows_per_wg - 1) / rows_per_wg);
+    if (window)
+        hipLaunchKernelGGL((colsum_rows_kernel<G, PTW>), gr, dim3(kCNT), 0, st, a);
+    else
+        hipLaunchKernelGGL((colsum_rows_kernel<G, PTF>), gr, dim3(kCNT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gc(units, (max_p + keys_per_wg - 1) / keys_per_wg);
