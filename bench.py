@@ -260,6 +260,21 @@ def host_cpu() -> str:
 PEAK_BF16_TFLOPS = 2500.0
 
 
+def call_roofline(nbytes: float, flops: float, per_call: float, note: str) -> dict:
+    """Roofline of one whole prompt call: the bound is whichever of HBM (the
+    algorithmic bytes at 8 TB/s) and the bf16 matrix peak (the algorithmic
+    flops at 2.5 PFLOP/s) takes longer; the other is reported beside it."""
+    t_mem, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12)
+    hbm = {"bound": "hbm", "achieved": round(nbytes / per_call / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(t_mem / per_call, 4)}
+    mfma = {"bound": "mfma", "achieved": round(flops / per_call / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(t_mfma / per_call, 4)}
+    main, other = (hbm, mfma) if t_mem >= t_mfma else (mfma, hbm)
+    return {**main, "traffic": None, "mean_call_us": round(per_call * 1e6, 2), "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops, f"{other['bound']}_frac": other["frac"],
+            f"{other['bound']}_achieved": other["achieved"], "note": note}
+
+
 def colsum_cpu_baseline(w, lens, seconds: float):
     """The oracle's column sums (orc_colsum, as it stands) on whole units of the
     workload's first sequence, all host cores, until about `seconds` have passed."""
@@ -334,6 +349,7 @@ def prefill_main(args, w):
     pairs = sum(P * (P + 1) // 2 for P in lens)
     flops = 2.0 * D * Hq * pairs  # the causal logits, once
     tokens = float(sum(lens))
+    nbytes = tokens * (Hq * D * 4 + Hkv * D * 2 + Hkv * 8)  # q, K, the sums
     cpu = None if args.no_cpu_baseline else colsum_cpu_baseline(w, lens, args.cpu_seconds)
     line = {
         "metric": "prompt tokens scored/sec (prefill-scored initial scores, h2o_prefill_scores)",
@@ -344,13 +360,11 @@ def prefill_main(args, w):
         "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
                    "prompt_lens": lens if len(set(lens)) > 1 else lens[0],
                    "entry_point": "h2o_prefill_scores", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(flops / per_call / 1e12, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops / per_call / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "mean_call_us": round(per_call * 1e6, 2), "algorithmic_flops": flops,
-                     "executed_over_algorithmic": 4,
-                     "note": "algorithmic = the causal logits q.k once; the kernels compute them in "
-                             "two passes, each on the bf16 hi and lo parts of q"},
+        "roofline": call_roofline(
+            nbytes, flops, per_call,
+            "whole call; algorithmic bytes = fp32 q, bf16 K and the fp64 sums once; algorithmic flops = "
+            "the causal logits q.k once (the kernels compute them 4x: two passes, each on the bf16 hi "
+            "and lo parts of q)"),
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_hash(prompt=True),
     }
@@ -407,6 +421,8 @@ def snapkv_main(args, w):
     tokens = float(sum(lens))
     rows = sum(sum(i + 1 for i in range(P - min(window, P), P)) for P in lens)
     flops = 2.0 * D * Hq * rows
+    nbytes = (sum(min(window, P) for P in lens) * Hq * D * 4 + tokens * (Hkv * D * 2 + Hq * 8)
+              + B * Hkv * cap * 4 + B * 4)  # window q, K, votes, kept positions and counts
     line = {
         "metric": "prompt tokens selected/sec (SnapKV, h2o_snapkv_select)",
         "value": round(tokens / per_call, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -417,10 +433,11 @@ def snapkv_main(args, w):
                    "prompt_lens": lens if len(set(lens)) > 1 else lens[0], "window": window, "pool": pool,
                    "keep_per_head": keep, "mean_kept": round(float(c.mean()), 1),
                    "entry_point": "h2o_snapkv_select", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(flops / per_call / 1e12, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(flops / per_call / 1e12 / PEAK_BF16_TFLOPS, 5),
-                     "traffic": None, "mean_call_us": round(per_call * 1e6, 2), "algorithmic_flops": flops,
-                     "note": "the window rows' causal logits once; the call also pools and selects"},
+        "roofline": call_roofline(
+            nbytes, flops, per_call,
+            "whole call; algorithmic bytes = the window rows' fp32 q, bf16 K, the fp64 votes and the kept "
+            "positions once; algorithmic flops = the window rows' causal logits once; the call also "
+            "pools and selects"),
         "cpu_baseline": None,
         "kernel_source_sha256_16": kernel_hash(prompt=True),
     }

@@ -187,8 +187,9 @@ struct SnapArgs {
     int cap;                // entries per unit in kept
     const double* votes;    // [sum P][Hq]
     double* pooled;         // scratch [sum P][Hq] (prefix positions only)
-    int bits_words;         // selection kernel: LDS words of the kept-position bitmap
+    int bits_words;         // selection: words of a kept-position bitmap (LDS, and hbits' stride)
     int stage_n;            // selection kernel: prefixes up to this length are staged in LDS
+    unsigned* hbits;        // G > 1: scratch [B * Hkv][G][bits_words], each query head's kept bits
     int32_t* kept;          // [B * Hkv][cap] ascending positions, -1 past the count
     int32_t* count;         // [B * Hkv]
     int32_t seq_p[kMaxArgBatch], seq_w[kMaxArgBatch];

@@ -461,11 +461,58 @@ __global__ void __launch_bounds__(256) snapkv_pool_kernel(const SnapArgs a)
 constexpr int kSNT = 256;
 constexpr int kSnapStage = 4096;  // prefix positions whose pooled votes are staged in LDS
 
+// One query head's selection: the bits of its `keep` highest-voted prefix
+// positions OR-ed into the LDS bitmap.  Keys as in the decode step's bulk
+// selection, (vote bits, ~position): the e smallest go, so equal votes keep
+// the lower position.  stage: the head's pooled votes are copied there first
+// when `staged` (the radix passes then read LDS instead of a strided column).
+__device__ inline void snap_head(const SnapArgs& a, int hq, int Pp, int64_t off, bool staged, double* stage,
+                                 unsigned* bits, RadixSmem& s_rad)
+{
+    const int tid = threadIdx.x;
+    const int e = Pp - a.keep;  // prefix positions each head leaves out
+    if (staged && e > 0) {
+        for (int j = tid; j < Pp; j += kSNT) stage[j] = a.pooled[(size_t)(off + j) * a.Hq + hq];
+        __syncthreads();
+    }
+    auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
+        const unsigned long long u = ord64(staged ? stage[j] : a.pooled[(size_t)(off + j) * a.Hq + hq]);
+        wk[2] = (unsigned)(u >> 32);
+        wk[1] = (unsigned)u;
+        wk[0] = ~(unsigned)j;
+        return true;
+    };
+    if (e > 0) {
+        radix_select<kSNT>(key_of, Pp, e, 0, s_rad);
+        for (int j = tid; j < Pp; j += kSNT) {
+            unsigned wk[3];
+            key_of(j, wk);
+            if (!key_le(wk, s_rad)) atomicOr(&bits[j >> 5], 1u << (j & 31));
+        }
+    } else {
+        for (int j = tid; j < Pp; j += kSNT) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+}
+
+// The window's positions added to the unit's bitmap, then the kept positions
+// in ascending order, -1 past the count.
+__device__ inline void snap_finish(const SnapArgs& a, int unit, int P, int Pp, unsigned* bits, ScanSmem& s_scan)
+{
+    const int tid = threadIdx.x;
+    for (int j = Pp + tid; j < P; j += kSNT) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    __syncthreads();
+    int* out = a.kept + (size_t)unit * a.cap;
+    const int n = collect<kSNT>(0, P, [&](int j) { return ((bits[j >> 5] >> (j & 31)) & 1u) != 0; }, out,
+                                s_scan);
+    for (int i = n + tid; i < a.cap; i += kSNT) out[i] = -1;
+    if (tid == 0) a.count[unit] = n;
+}
+
+// G = 1: one workgroup per unit does the whole selection.
 __global__ void __launch_bounds__(kSNT) snapkv_select_kernel(const SnapArgs a)
 {
-    // one bit per prompt position (kept), then the pooled votes of the head in
-    // hand when the prefix has at most a.stage_n positions: the radix passes
-    // read them from LDS instead of a strided global column each pass
+    // one bit per prompt position (kept), then the staged pooled votes
     extern __shared__ __align__(16) unsigned bits[];
     __shared__ RadixSmem s_rad;
     __shared__ ScanSmem s_scan;
@@ -475,44 +522,51 @@ __global__ void __launch_bounds__(kSNT) snapkv_select_kernel(const SnapArgs a)
     const int tid = threadIdx.x;
     const int nw = (P + 31) / 32;
     double* stage = reinterpret_cast<double*>(bits + a.bits_words);
-    const bool staged = Pp <= a.stage_n;
     for (int i = tid; i < nw; i += kSNT) bits[i] = 0u;
     __syncthreads();
-    const int e = Pp - a.keep;  // prefix positions each head leaves out
-    for (int g = 0; g < a.G; ++g) {
-        const int hq = h * a.G + g;
-        if (staged && e > 0) {
-            for (int j = tid; j < Pp; j += kSNT) stage[j] = a.pooled[(size_t)(off + j) * a.Hq + hq];
-            __syncthreads();
-        }
-        // keys as in the decode step's bulk selection: (vote bits, ~position);
-        // the e smallest go, so equal votes keep the lower position
-        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
-            const unsigned long long u = ord64(staged ? stage[j] : a.pooled[(size_t)(off + j) * a.Hq + hq]);
-            wk[2] = (unsigned)(u >> 32);
-            wk[1] = (unsigned)u;
-            wk[0] = ~(unsigned)j;
-            return true;
-        };
-        if (e > 0) {
-            radix_select<kSNT>(key_of, Pp, e, 0, s_rad);
-            for (int j = tid; j < Pp; j += kSNT) {
-                unsigned wk[3];
-                key_of(j, wk);
-                if (!key_le(wk, s_rad)) atomicOr(&bits[j >> 5], 1u << (j & 31));
-            }
-        } else {
-            for (int j = tid; j < Pp; j += kSNT) atomicOr(&bits[j >> 5], 1u << (j & 31));
-        }
-        __syncthreads();
-    }
-    for (int j = Pp + tid; j < P; j += kSNT) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    for (int g = 0; g < a.G; ++g) snap_head(a, h * a.G + g, Pp, off, Pp <= a.stage_n, stage, bits, s_rad);
+    snap_finish(a, unit, P, Pp, bits, s_scan);
+}
+
+// G > 1, first kernel: one workgroup per (unit, query head) selects that
+// head's positions and writes its bitmap to hbits[unit][g][bits_words].
+__global__ void __launch_bounds__(kSNT) snapkv_head_kernel(const SnapArgs a)
+{
+    extern __shared__ __align__(16) unsigned bits[];
+    __shared__ RadixSmem s_rad;
+    const int unit = blockIdx.x, g = blockIdx.y, b = unit / a.Hkv, h = unit - b * a.Hkv;
+    const int P = a.seq_p[b], Pp = P - a.seq_w[b];
+    const int64_t off = a.seq_off[b];
+    const int tid = threadIdx.x;
+    const int nw = (Pp + 31) / 32;
+    double* stage = reinterpret_cast<double*>(bits + a.bits_words);
+    for (int i = tid; i < nw; i += kSNT) bits[i] = 0u;
     __syncthreads();
-    int* out = a.kept + (size_t)unit * a.cap;
-    const int n = collect<kSNT>(0, P, [&](int j) { return ((bits[j >> 5] >> (j & 31)) & 1u) != 0; }, out,
-                                s_scan);
-    for (int i = n + tid; i < a.cap; i += kSNT) out[i] = -1;
-    if (tid == 0) a.count[unit] = n;
+    snap_head(a, h * a.G + g, Pp, off, Pp <= a.stage_n, stage, bits, s_rad);
+    unsigned* hb = a.hbits + ((size_t)unit * a.G + g) * a.bits_words;
+    for (int i = tid; i < nw; i += kSNT) hb[i] = bits[i];
+}
+
+// G > 1, second kernel: one workgroup per unit ORs its heads' bitmaps (the
+// launch boundary orders them after the first kernel's stores), adds the
+// window and compacts.
+__global__ void __launch_bounds__(kSNT) snapkv_union_kernel(const SnapArgs a)
+{
+    extern __shared__ __align__(16) unsigned bits[];
+    __shared__ ScanSmem s_scan;
+    const int unit = blockIdx.x, b = unit / a.Hkv;
+    const int P = a.seq_p[b], Pp = P - a.seq_w[b];
+    const int tid = threadIdx.x;
+    const int nwp = (Pp + 31) / 32, nw = (P + 31) / 32;
+    const unsigned* hb = a.hbits + (size_t)unit * a.G * a.bits_words;
+    for (int i = tid; i < nw; i += kSNT) {
+        unsigned x = 0u;
+        if (i < nwp)
+            for (int g = 0; g < a.G; ++g) x |= hb[(size_t)g * a.bits_words + i];
+        bits[i] = x;
+    }
+    __syncthreads();
+    snap_finish(a, unit, P, Pp, bits, s_scan);
 }
 
 }  // namespace
@@ -524,21 +578,31 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
     hipLaunchKernelGGL(snapkv_pool_kernel, dim3((unsigned)((cells + 255) / 256), a.B), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // bits of the longest prompt, then the staged votes of prefixes up to kSnapStage
+    // LDS: the bitmap (a.bits_words words), then the staged votes of prefixes up to kSnapStage
     SnapArgs b = a;
-    b.bits_words = ((max_p + 31) / 32 + 3) & ~3;  // whole 16-byte groups, so the votes stay aligned
     int max_pp = 0;
     for (int i = 0; i < a.B; ++i) max_pp = std::max(max_pp, a.seq_p[i] - a.seq_w[i]);
     b.stage_n = std::min(max_pp, kSnapStage);
     const size_t dyn = (size_t)b.bits_words * 4 + (size_t)b.stage_n * 8;
-    static size_t dyn_set = 48 * 1024;
-    if (dyn > dyn_set) {
-        e = hipFuncSetAttribute((const void*)snapkv_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)dyn);
-        if (e != hipSuccess) return e;
-        dyn_set = dyn;
+    const size_t dyn_u = (size_t)b.bits_words * 4;  // the union kernel: the bitmap only
+    // above the default 48 KB of dynamic LDS the kernel's limit is raised on
+    // the current device first (only prompts beyond ~130k positions need it)
+    auto allow = [](const void* kern, size_t bytes) {
+        return bytes > 48 * 1024 ? hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)
+                                 : hipSuccess;
+    };
+    const unsigned units = (unsigned)(a.B * a.Hkv);
+    if (a.G == 1) {
+        if ((e = allow((const void*)snapkv_select_kernel, dyn)) != hipSuccess) return e;
+        hipLaunchKernelGGL(snapkv_select_kernel, dim3(units), dim3(kSNT), dyn, st, b);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL(snapkv_select_kernel, dim3(a.B * a.Hkv), dim3(kSNT), dyn, st, b);
+    if ((e = allow((const void*)snapkv_head_kernel, dyn)) != hipSuccess) return e;
+    if ((e = allow((const void*)snapkv_union_kernel, dyn_u)) != hipSuccess) return e;
+    hipLaunchKernelGGL(snapkv_head_kernel, dim3(units, (unsigned)a.G), dim3(kSNT), dyn, st, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(snapkv_union_kernel, dim3(units), dim3(kSNT), dyn_u, st, b);
     return hipGetLastError();
 }
 

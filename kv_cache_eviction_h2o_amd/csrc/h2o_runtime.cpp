@@ -589,7 +589,10 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     if (misaligned(kept) || misaligned(count))
         return fail(nullptr, H2O_EINVAL, "kept and kept_count must be 16-byte aligned");
     // scratch: [votes (when the caller passes none)] [pooled votes] [column-sum passes]
+    // [per-head kept bitmaps (G > 1)]
     const size_t vbytes = align256((size_t)total * Hq * sizeof(double));
+    a.bits_words = ((maxP + 31) / 32 + 3) & ~3;  // whole 16-byte groups, so staged votes stay aligned
+    const size_t hbytes = G > 1 ? align256((size_t)B * Hq * a.bits_words * sizeof(unsigned)) : 0;
     std::string why;
     PromptScratch* ps = prompt_scratch(why);
     if (!ps) return fail(nullptr, H2O_EDEVICE, why);
@@ -602,7 +605,7 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     if (rc != H2O_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     char* sp = nullptr;
-    hipError_t e = scratch_take(*ps, vown + vbytes + cbytes, st, &sp);
+    hipError_t e = scratch_take(*ps, vown + vbytes + cbytes + hbytes, st, &sp);
     if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV: scratch");
     double* vb = votes ? votes : reinterpret_cast<double*>(sp);
     ca.out = vb;  // the votes: the caller's buffer, else the scratch's first part
@@ -610,6 +613,7 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     if (e == hipSuccess) {
         a.votes = vb;
         a.pooled = reinterpret_cast<double*>(sp + vown);
+        a.hbits = G > 1 ? reinterpret_cast<unsigned*>(sp + vown + vbytes + cbytes) : nullptr;
         a.kept = kept;
         a.count = count;
         e = launch_snapkv(a, maxP, st);
