@@ -9,8 +9,10 @@
 //
 // A row's weights need its softmax maximum and sum over all of its keys
 // before any column can take them, so there are two passes:
-//   rows   one workgroup per (unit, 4 waves x 8 PT query positions; PT = 4 / G
-//          for small groups, else 1, and 1 when at most a 128-row window is scored):
+//   rows   one workgroup per (unit, 4 waves x 8 PT query positions, GW query
+//          heads; PT = 4 / G for small groups, else 1, and 1 when at most a
+//          128-row window is scored; GW = G up to 4, else 4, and at most 2 for
+//          a window):
 //          S = Q_tile (8 positions x hi/lo = 16 rows) . K_tile^T (16 keys)
 //          with v_mfma_f32_16x16x32_bf16 over 4 k-steps, hi + lo added in the
 //          lane (rows 2p and 2p+1 of the C layout); online max / sum per lane
@@ -51,20 +53,27 @@ __device__ inline void ms_stage(float& m, float& l)
     m = M;
 }
 
-// query tiles of 8 positions per wave: more for small groups so a K tile load
-// feeds more products (qop holds PT * G * 16 registers)
+// PT query tiles of 8 positions per wave: more for small groups so a K tile
+// load feeds more products; GW of the group's G query heads per workgroup: a
+// group of 8 in two workgroups of 4 keeps the kernel at 3 waves per SIMD
+// instead of 2 (qop holds PT * GW * 16 registers)
 template <int G>
 struct RowsTune {
     static constexpr int PT = G >= 4 ? 1 : 4 / G;
+    static constexpr int GW = G > 4 ? 4 : G;
     // with only a window of rows to score (at most 128 per sequence, as for
-    // SnapKV's observation window) one tile per wave: the window's rows then
-    // spread over all four waves of a workgroup instead of landing on one
+    // SnapKV's observation window) one tile per wave, so the window's rows
+    // spread over all four waves of a workgroup instead of landing on one, and
+    // at most two query heads per workgroup, so a large group spreads over
+    // G / 2 workgroups instead of running on one
     static constexpr int PT_WINDOW = 1;
+    static constexpr int GW_WINDOW = G < 2 ? G : 2;
 };
 
 constexpr int kRCK = 4;  // rows pass: 16-key tiles per LDS chunk
 
-template <int G, int PT>
+// GW query heads per workgroup: heads GW z .. GW z + GW - 1 of the unit's a.G
+template <int GW, int PT>
 __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
 {
     // K chunks in B-operand order: [buffer][tile][k-step][lane], lane (lg, lc)
@@ -88,15 +97,16 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
     // A operands: tile pt, lane (lg, lc) holds d = 32 kb + 8 lg .. +8 of row lc,
     // i.e. of position base + 8 pt + lc / 2, part lc & 1 (hi / lo)
     const bool lo_part = (lc & 1) != 0;
-    bf16x8 qop[PT][G][4];
+    const int g0 = (int)blockIdx.z * GW;  // the workgroup's first query head in the group
+    bf16x8 qop[PT][GW][4];
     if (active) {
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const int t8 = base / 8 + pt;
             const int prow = min(base + 8 * pt + (lc >> 1), P - 1);
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float* qr = a.q + ((size_t)(off + prow) * a.Hq + (size_t)h * G + g) * 128;
+            for (int g = 0; g < GW; ++g) {
+                const float* qr = a.q + ((size_t)(off + prow) * a.Hq + (size_t)h * a.G + g0 + g) * 128;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     const float4 x0 = *reinterpret_cast<const float4*>(qr + 32 * kb + 8 * lg);
@@ -106,7 +116,7 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
                     for (int i = 0; i < 8; ++i) qop[pt][g][kb][i] = split_part(x[i] * a.qscale, lo_part);
                     const int ts = t8 - lo / 8;  // the scratch keeps tiles from row lo's on
                     if (ts >= 0 && ts < a.nt8)
-                        a.qs[(((size_t)unit * a.nt8 + ts) * G + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
+                        a.qs[(((size_t)unit * a.nt8 + ts) * a.G + g0 + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
                 }
             }
         }
@@ -117,11 +127,11 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
     const int nkt = wg_last / 16 + 1;                                      // the workgroup's tiles
     const int nkt_w = active ? min(base + 8 * PT - 1, P - 1) / 16 + 1 : 0;  // this wave's
     const uint4* kp = reinterpret_cast<const uint4*>(a.k);
-    float m[PT][G][2], l[PT][G][2];
+    float m[PT][GW][2], l[PT][GW][2];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < GW; ++g) {
             m[pt][g][0] = m[pt][g][1] = kFloor;
             l[pt][g][0] = l[pt][g][1] = 0.f;
         }
@@ -160,7 +170,7 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
         for (int pt = 0; pt < PT; ++pt) {
             const int pos0 = base + 8 * pt + 2 * lg, pos1 = pos0 + 1;  // C rows 4 lg .. +3
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int g = 0; g < GW; ++g) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) c = mma(qop[pt][g][kb], bt[kb], c);
@@ -204,7 +214,7 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < GW; ++g)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 ms_stage<0xB1>(m[pt][g][r], l[pt][g][r]);
@@ -218,9 +228,9 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
             const int ts = base / 8 + pt - lo / 8;
             if (ts < 0 || ts >= a.nt8) continue;
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int g = 0; g < GW; ++g) {
                 float4* sp =
-                    reinterpret_cast<float4*>(a.st + (((size_t)unit * a.nt8 + ts) * G + g) * 8 + 2 * lg);
+                    reinterpret_cast<float4*>(a.st + (((size_t)unit * a.nt8 + ts) * a.G + g0 + g) * 8 + 2 * lg);
                 *sp = make_float4(m[pt][g][0], 1.0f / l[pt][g][0], m[pt][g][1], 1.0f / l[pt][g][1]);
             }
         }
@@ -422,14 +432,15 @@ template <int G>
 hipError_t launch_colsum_g(const ColsumArgs& a, int max_p, hipStream_t st)
 {
     const unsigned units = (unsigned)(a.B * a.Hkv);
-    constexpr int PTF = RowsTune<G>::PT, PTW = RowsTune<G>::PT_WINDOW;
+    constexpr int PTF = RowsTune<G>::PT, GWF = RowsTune<G>::GW;
+    constexpr int PTW = RowsTune<G>::PT_WINDOW, GWW = RowsTune<G>::GW_WINDOW;
     const bool window = a.nt8 <= 16;  // at most 128 rows per sequence from row lo on
     const int rows_per_wg = 4 * 8 * (window ? PTW : PTF), keys_per_wg = 4 * 16 * kKT;
-    const dim3 gr(units, (max_p + rows_per_wg - 1) / rows_per_wg);
+    const unsigned pblocks = (unsigned)((max_p + rows_per_wg - 1) / rows_per_wg);
     if (window)
-        hipLaunchKernelGGL((colsum_rows_kernel<G, PTW>), gr, dim3(kCNT), 0, st, a);
+        hipLaunchKernelGGL((colsum_rows_kernel<GWW, PTW>), dim3(units, pblocks, G / GWW), dim3(kCNT), 0, st, a);
     else
-        hipLaunchKernelGGL((colsum_rows_kernel<G, PTF>), gr, dim3(kCNT), 0, st, a);
+        hipLaunchKernelGGL((colsum_rows_kernel<GWF, PTF>), dim3(units, pblocks, G / GWF), dim3(kCNT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gc(units, (max_p + keys_per_wg - 1) / keys_per_wg);
