@@ -232,11 +232,13 @@ void h2o_destroy(h2o_ctx *ctx);
  *   out         device [sum P_b][Hkv] fp64; every element is written.
  * Supported: kv_dtype H2O_BF16 with head_dim 128, G in {1, 2, 4, 8}.
  * Scratch: the library keeps one device buffer per device for this call and
- * h2o_snapkv_select (about the size of prompt_q; SnapKV adds 16 bytes per
- * prompt position and query head), grown with hipMallocAsync on `stream` when
- * a call needs more and held until the process ends.  Calls on one device are
- * ordered through it: a call on another stream than the previous call makes
- * its stream wait for the previous call's work.  Errors: H2O_EINVAL,
+ * h2o_snapkv_select (about the size of prompt_q; SnapKV adds up to 16 bytes
+ * per prompt position and query head, and with G > 1 one bit per position of
+ * the longest prompt for each sequence and query head), grown with
+ * hipMallocAsync on `stream` when a call needs more and held until the
+ * process ends.  Calls on one device are ordered through it: a call on
+ * another stream than the previous call makes its stream wait for the
+ * previous call's work.  Errors: H2O_EINVAL,
  * H2O_ENOMEM, H2O_EDEVICE; the message is h2o_last_error(NULL). */
 int h2o_prefill_scores(const h2o_config *cfg, const int32_t *prompt_len, const float *prompt_q,
                        const void *prompt_k, double *out, void *stream);
