@@ -87,3 +87,30 @@ def test_snapkv_edge_cases():
 def test_snapkv_opt_layer_full_shape():
     w = WL.OPT_LAYER
     run_snapkv(w, WL.prompt_lengths(w), window=32, pool=7, keep=172, vote_units=[(0, 0), (5, 13), (7, 31)])
+
+
+def test_snapkv_gqa_edge_cases():
+    """G = 4 (each query head selected in its own workgroup, then the union):
+    prompts no longer than the window, keep beyond the prefix, keep 0, pool 1."""
+    w = WL.LLAMA_GQA.scaled(n_q_heads=8, n_kv_heads=2)
+    _, c = run_snapkv(w, [20, 32, 33, 100], window=32, pool=7, keep=200)
+    assert list(c[:, 0]) == [20, 32, 33, 100]
+    _, c = run_snapkv(w, [50, 90], window=16, pool=1, keep=0)
+    assert np.all(c == 16)
+
+
+@pytest.mark.parametrize("g", [1, 4])
+def test_snapkv_long_prefix_unstaged(g):
+    """A prefix beyond the 4096 positions whose pooled votes the selection
+    stages in LDS (its radix passes then read global memory), beside a short
+    one that is staged."""
+    w = WL.LLAMA_GQA.scaled(n_q_heads=2 * g, n_kv_heads=2)
+    run_snapkv(w, [5000, 700], window=32, pool=7, keep=900)
+
+
+@pytest.mark.parametrize("g", [1, 2])
+def test_snapkv_prompt_beyond_48k_of_lds(g):
+    """A 140,000-position prompt: the selection's bitmap and vote staging
+    exceed 48 KB of LDS, so the kernel's dynamic LDS limit is raised first."""
+    w = WL.LLAMA_GQA.scaled(n_q_heads=g, n_kv_heads=1)
+    run_snapkv(w, [140000], window=32, pool=7, keep=28000)
