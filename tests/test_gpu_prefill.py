@@ -65,9 +65,12 @@ def test_prefill_scores_gqa_groups(g):
     run_prefill(w, [700, 129])
 
 
-def test_prefill_scores_ragged_short_prompts():
-    # one position, fewer than one 8-row tile, exact tiles, one past a 64-key block
-    w = WL.OPT_LAYER.scaled(n_q_heads=2, n_kv_heads=2)
+@pytest.mark.parametrize("g", [1, 8])
+def test_prefill_scores_ragged_short_prompts(g):
+    # one position, fewer than one 8-row tile, exact tiles, one past a 64-key
+    # block; prompts of at most 128 positions take the rows pass's window
+    # tiling (one tile per wave; G = 8: four workgroups of two query heads)
+    w = WL.OPT_LAYER.scaled(n_q_heads=2 * g, n_kv_heads=2)
     run_prefill(w, [1, 7, 8, 16, 33, 64, 65])
 
 
