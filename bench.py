@@ -85,6 +85,19 @@ def summarize(args) -> None:
                        f"copy reads {cal:.1f} KiB on this counter -> scale x{factor:.4f}")
         hbm = sum(v * f * 1024 for v, f, _ in res.values())
         out.append(f"hbm_bytes_per_launch: {hbm:.6e}")
+    if args.summarize_pmc:
+        by = {}
+        for r in csv.DictReader(open(args.summarize_pmc)):
+            if kname in r["Kernel_Name"]:
+                by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        mean = {k: float(np.mean(v[-n_last:])) for k, v in by.items()}
+        for k in sorted(mean):
+            out.append(f"{k}: timed-window mean {mean[k]:.6g} per launch ({len(by[k])} launches)")
+        wc = mean.get("SQ_WAVE_CYCLES")
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VMEM",
+                  "SQ_ACTIVE_INST_VALU"):
+            if wc and k in mean:
+                out.append(f"{k} / SQ_WAVE_CYCLES: {mean[k] / wc:.3f}")
     print("\n".join(out))
 
 
@@ -94,6 +107,8 @@ def parse():
                     help="print a summary of a rocprofv3 kernel trace of this benchmark and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="with FETCH_SIZE / WRITE_SIZE counter CSVs: HBM bytes per launch")
+    ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
+                    help="with a rocprofv3 --pmc counter CSV: each counter's mean per launch")
     ap.add_argument("--summarize-kernel", default="step_kernel", metavar="NAME",
                     help="kernel the summaries cover (a substring of its name; the timed window is "
                          "the last steps x layers of its launches)")
@@ -446,7 +461,7 @@ def snapkv_main(args, w):
 
 def main():
     args = parse()
-    if args.summarize_trace or args.summarize_counters:
+    if args.summarize_trace or args.summarize_counters or args.summarize_pmc:
         summarize(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
