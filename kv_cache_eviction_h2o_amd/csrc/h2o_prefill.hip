@@ -475,15 +475,35 @@ constexpr int kSnapStage = 4096;  // prefix positions whose pooled votes are sta
 // One query head's selection: the bits of its `keep` highest-voted prefix
 // positions OR-ed into the LDS bitmap.  Keys as in the decode step's bulk
 // selection, (vote bits, ~position): the e smallest go, so equal votes keep
-// the lower position.  stage: the head's pooled votes are copied there first
-// when `staged` (the radix passes then read LDS instead of a strided column).
+// the lower position.  When `staged` the head's votes are copied to `stage`
+// and max-pooled there (through registers, then back in place), and the radix
+// passes read LDS; otherwise they read the pooling kernel's output.
 __device__ inline void snap_head(const SnapArgs& a, int hq, int Pp, int64_t off, bool staged, double* stage,
                                  unsigned* bits, RadixSmem& s_rad)
 {
     const int tid = threadIdx.x;
     const int e = Pp - a.keep;  // prefix positions each head leaves out
     if (staged && e > 0) {
-        for (int j = tid; j < Pp; j += kSNT) stage[j] = a.pooled[(size_t)(off + j) * a.Hq + hq];
+        for (int j = tid; j < Pp; j += kSNT) stage[j] = a.votes[(size_t)(off + j) * a.Hq + hq];
+        __syncthreads();
+        constexpr int NPT = kSnapStage / kSNT;  // staged positions per thread
+        double pv[NPT];
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+            const int j = tid + k * kSNT;
+            double m = -INFINITY;
+            if (j < Pp) {
+                const int x0 = max(0, j - a.pool_r), x1 = min(Pp - 1, j + a.pool_r);
+                for (int x = x0; x <= x1; ++x) m = fmax(m, stage[x]);
+            }
+            pv[k] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+            const int j = tid + k * kSNT;
+            if (j < Pp) stage[j] = pv[k];
+        }
         __syncthreads();
     }
     auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
@@ -585,14 +605,19 @@ __global__ void __launch_bounds__(kSNT) snapkv_union_kernel(const SnapArgs a)
 hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
 {
     if (max_p <= 0) return hipSuccess;
-    const long long cells = (long long)max_p * a.Hq;
-    hipLaunchKernelGGL(snapkv_pool_kernel, dim3((unsigned)((cells + 255) / 256), a.B), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // LDS: the bitmap (a.bits_words words), then the staged votes of prefixes up to kSnapStage
-    SnapArgs b = a;
+    hipError_t e = hipSuccess;
     int max_pp = 0;
     for (int i = 0; i < a.B; ++i) max_pp = std::max(max_pp, a.seq_p[i] - a.seq_w[i]);
+    // prefixes up to kSnapStage are pooled inside the selection; the pooling
+    // kernel serves the longer ones
+    if (max_pp > kSnapStage) {
+        const long long cells = (long long)max_p * a.Hq;
+        hipLaunchKernelGGL(snapkv_pool_kernel, dim3((unsigned)((cells + 255) / 256), a.B), dim3(256), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // LDS: the bitmap (a.bits_words words), then the staged votes of prefixes up to kSnapStage
+    SnapArgs b = a;
     b.stage_n = std::min(max_pp, kSnapStage);
     const size_t dyn = (size_t)b.bits_words * 4 + (size_t)b.stage_n * 8;
     const size_t dyn_u = (size_t)b.bits_words * 4;  // the union kernel: the bitmap only
