@@ -1,0 +1,43 @@
+"""Host-side logic of bench.py that needs no GPU: the roofline bound of the
+prompt calls, the source hashes the counter summaries are tied to, and the
+counter summarizer on a synthetic rocprofv3 CSV."""
+import csv
+import types
+
+import bench
+
+
+def test_call_roofline_picks_the_slower_resource():
+    # 200 MB at 8 TB/s = 25 us against 10 GFLOP at 2.5 PFLOP/s = 4 us: HBM
+    r = bench.call_roofline(200e6, 10e9, 100e-6, "x")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["frac"] - 0.25) < 1e-9 and abs(r["achieved"] - 2000.0) < 1e-6
+    assert abs(r["mfma_frac"] - 0.04) < 1e-9
+    # 1 MB (0.125 us) against 100 GFLOP (40 us): the matrix cores
+    r = bench.call_roofline(1e6, 100e9, 80e-6, "x")
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert abs(r["frac"] - 0.5) < 1e-9 and abs(r["hbm_frac"] - 0.125e-6 / 80e-6) < 1e-4
+
+
+def test_source_hashes_cover_their_own_kernels():
+    assert set(bench.STEP_SRCS) & set(bench.PROMPT_SRCS) == {"h2o_internal.h", "h2o_device.h"}
+    assert "h2o_prefill.hip" not in bench.STEP_SRCS and "h2o_prefill.hip" in bench.PROMPT_SRCS
+    assert bench.kernel_hash() != bench.kernel_hash(prompt=True)
+
+
+def test_summarize_pmc_means_over_the_timed_window(tmp_path, capsys):
+    f = tmp_path / "c.csv"
+    with open(f, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i in range(10):  # launches 0..9; the timed window is the last steps x layers = 4
+            w.writerow(["h2o::step_kernel<...>", "SQ_WAVE_CYCLES", 100 + i])
+            w.writerow(["h2o::step_kernel<...>", "SQ_WAIT_ANY", 50])
+            w.writerow(["other_kernel", "SQ_WAVE_CYCLES", 1e9])
+    args = types.SimpleNamespace(steps=2, layers=2, summarize_kernel="step_kernel", summarize_trace=None,
+                                 summarize_counters=None, summarize_pmc=str(f))
+    bench.summarize(args)
+    out = capsys.readouterr().out
+    assert f"kernel_source_sha256_16: {bench.kernel_hash()}" in out
+    assert "SQ_WAVE_CYCLES: timed-window mean 107.5 per launch (10 launches)" in out
+    assert "SQ_WAIT_ANY / SQ_WAVE_CYCLES: 0.465" in out
