@@ -41,3 +41,13 @@ def test_summarize_pmc_means_over_the_timed_window(tmp_path, capsys):
     assert f"kernel_source_sha256_16: {bench.kernel_hash()}" in out
     assert "SQ_WAVE_CYCLES: timed-window mean 107.5 per launch (10 launches)" in out
     assert "SQ_WAIT_ANY / SQ_WAVE_CYCLES: 0.465" in out
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
