@@ -34,3 +34,25 @@ def test_default_bench_line_has_every_field():
     assert "traffic" in rf
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+@pytest.mark.parametrize("mode", ["--prefill", "--snapkv"])
+def test_prompt_call_bench_lines(mode):
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), mode, "--steps", "8", "--warmup", "2",
+                        "--cpu-seconds", "1"], cwd=root, capture_output=True, text=True, timeout=170)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0])
+    assert d["n_gpus"] == 1 and d["steps"] == 8 and d["value"] > 0
+    assert d["config"]["entry_point"] == ("h2o_prefill_scores" if mode == "--prefill" else "h2o_snapkv_select")
+    rf = d["roofline"]
+    # both calls are HBM-bound on the roofline: fp32 q and bf16 K outweigh the causal logits
+    assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and 0 < rf["frac"] < 1
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3 and 0 < rf["mfma_frac"] < rf["frac"]
+    if mode == "--prefill":
+        assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
