@@ -316,6 +316,33 @@ def colsum_cpu_baseline(w, lens, seconds: float):
                        f"{t_used:.1f} s of CPU time")}
 
 
+def snapkv_cpu_baseline(w, lens, window: int, pool: int, keep: int, seconds: float):
+    """The oracle's SnapKV selection (orc_snapkv, as it stands: window votes,
+    pooling, per-head top-k, union) on whole units of the workload's first
+    sequence, all host cores, until about `seconds` have passed."""
+    import oracle as O
+    from concurrent.futures import ThreadPoolExecutor
+    G, Hkv, P = w.group, w.n_kv_heads, lens[0]
+    K, _ = S.prompt_kv(w.recipe, 0, [P], Hkv)
+    Q = S.prompt_queries(w.recipe, 0, [P], w.n_q_heads)
+    cfg = O.make_cfg(head_dim=w.head_dim, group=G)
+    qs = [Q[:, h * G:(h + 1) * G].astype(np.float64) for h in range(Hkv)]
+    ks = [S.cache_to_f64(w.recipe, K[:, h]) for h in range(Hkv)]
+    threads = min(os.cpu_count() or 1, Hkv)
+    done, t_used = 0, 0.0
+    with ThreadPoolExecutor(threads) as ex:
+        while t_used < seconds:
+            t0 = time.perf_counter()
+            list(ex.map(lambda h: O.snapkv(cfg, qs[h], ks[h], min(window, P), pool, keep), range(Hkv)))
+            t_used += time.perf_counter() - t0
+            done += 1
+    return {"value": done * P / t_used, "unit": "prompt tokens/s", "cores": threads, "kind": "oracle",
+            "host": host_cpu(),
+            "sample": (f"sequence 0 ({P} prompt positions) x {Hkv} KV heads x {G} query heads, "
+                       f"{done} repetitions, fp64 oracle SnapKV selection on {threads} threads; "
+                       f"{t_used:.1f} s of CPU time")}
+
+
 def prefill_main(args, w):
     """--prefill: h2o_prefill_scores over the workload's prompts (one layer)."""
     import torch
@@ -453,7 +480,8 @@ def snapkv_main(args, w):
             "whole call; algorithmic bytes = the window rows' fp32 q, bf16 K, the fp64 votes and the kept "
             "positions once; algorithmic flops = the window rows' causal logits once; the call also "
             "pools and selects"),
-        "cpu_baseline": None,
+        "cpu_baseline": (None if args.no_cpu_baseline
+                         else snapkv_cpu_baseline(w, lens, window, pool, keep, args.cpu_seconds)),
         "kernel_source_sha256_16": kernel_hash(prompt=True),
     }
     print(json.dumps(line), flush=True)
