@@ -411,16 +411,27 @@ int orc_step_many(orc_unit **u, int n, const double *const *q, const double *con
         free(th);
         return ORC_ENOMEM;
     }
+    /* started[i]: job i runs on its own thread; a job whose thread could not be
+     * created runs here instead, so every unit is stepped exactly once */
+    unsigned char *started = (unsigned char *)calloc((size_t)nthreads, 1);
+    if (!started) {
+        free(jobs);
+        free(th);
+        return ORC_ENOMEM;
+    }
     for (int i = 0; i < nthreads; ++i) {
         jobs[i] = (job){u, q, k, v, out, n, nthreads, i, ORC_OK};
-        if (i > 0) pthread_create(&th[i], NULL, run_job, &jobs[i]);
+        if (i > 0) started[i] = pthread_create(&th[i], NULL, run_job, &jobs[i]) == 0;
     }
     run_job(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i)
+        if (!started[i]) run_job(&jobs[i]);
     int rc = jobs[0].rc;
     for (int i = 1; i < nthreads; ++i) {
-        pthread_join(th[i], NULL);
+        if (started[i]) pthread_join(th[i], NULL);
         if (rc == ORC_OK) rc = jobs[i].rc;
     }
+    free(started);
     free(jobs);
     free(th);
     return rc;

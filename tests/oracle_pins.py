@@ -653,7 +653,36 @@ def pin_block_run_invariants(lib):
     assert evicted_blocks > 5
 
 
+# ------------------------------------------------ many units on threads
+def pin_step_many_equals_sequential(lib):
+    """orc_step_many (the CPU baseline's threaded driver) over N units equals N
+    plain orc_step calls, bit for bit, whatever the thread count: outputs,
+    retained positions, scores and evicted mass after every step.  A stride or
+    join slip that skips or repeats a unit changes one of them."""
+    rng = np.random.default_rng(29)
+    D, G, P, steps, N = 8, 2, 14, 6, 7
+    cfg = O.make_cfg(head_dim=D, group=G, n_sink=2, budget_fixed=10, hh_fixed=4)
+    pk = [rng.standard_normal((P, D)) for _ in range(N)]
+    pv = [rng.standard_normal((P, D)) for _ in range(N)]
+    ins = [[(rng.standard_normal((G, D)), rng.standard_normal(D), rng.standard_normal(D))
+            for _ in range(N)] for _ in range(steps)]
+    ref = [_unit(lib, cfg, pk[i], pv[i], P + steps + 1, b=i, h=i % 3) for i in range(N)]
+    ref_out = [[u.step(*ins[s][i]) for i, u in enumerate(ref)] for s in range(steps)]
+    for nthreads in (1, 3, N + 2):
+        us = [_unit(lib, cfg, pk[i], pv[i], P + steps + 1, b=i, h=i % 3) for i in range(N)]
+        for s in range(steps):
+            outs = O.step_many(us, [x[0] for x in ins[s]], [x[1] for x in ins[s]], [x[2] for x in ins[s]],
+                               nthreads)
+            for i in range(N):
+                assert np.array_equal(outs[i], ref_out[s][i]), f"{nthreads} threads: unit {i} output"
+        for i in range(N):
+            a, b = us[i].state(), ref[i].state()
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2], \
+                f"{nthreads} threads: unit {i} state"
+
+
 ALL_PINS = [
+    pin_step_many_equals_sequential,
     pin_attention_full_cache,
     pin_scores_and_selection_recomputed,
     pin_streaming_llm_and_sliding_window,

@@ -73,6 +73,8 @@ MUTANTS = {
     "block_counts_lowest_scores": ("imp[tok[x].pos / page] += 1;", "imp[tok[nt - 1 - x].pos / page] += 1;"),
     "block_need_rounds_down": ("const int need = (n - K + page - 1) / page;", "const int need = (n - K) / page;"),
     "block_select_own_scores_first_unit": ("memcpy(sc + (size_t)i * len, u[i]->score,", "memcpy(sc + (size_t)i * len, u[0]->score,"),
+    "step_many_skips_units": ("for (int i = j->first; i < j->n; i += j->stride)",
+                              "for (int i = j->first; i < j->n; i += 2 * j->stride)"),
     "random_largest_words": ("    if (x->key < y->key) return -1;\n    if (x->key > y->key) return 1;",
                              "    if (x->key > y->key) return -1;\n    if (x->key < y->key) return 1;"),
 }
