@@ -36,11 +36,27 @@
  *       eviction; eviction period K and buffer r).
  *
  * Conventions
- *   - Every call except h2o_read_indices and h2o_destroy is asynchronous on
- *     `stream` (a hipStream_t; NULL = the device's null stream).  Pointers
- *     named "device" must stay valid until the stream has run the work and
- *     be 16-byte aligned (the kernels use 16-byte vector accesses; a
- *     misaligned one is rejected with H2O_EINVAL before anything runs).
+ *   - The decode calls (h2o_step, h2o_compact, h2o_step_compact) and the
+ *     prompt calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *     device's null stream): they only enqueue work.  h2o_init enqueues the
+ *     prompt load on `stream` but first uploads its small host tables (prompt
+ *     lengths and offsets, the block table) with blocking copies, so it
+ *     returns once those are on the device.  h2o_read_indices and h2o_read_kv
+ *     wait for `stream`; h2o_destroy waits for the device.  Pointers named
+ *     "device" must stay valid until the stream has run the work and be
+ *     16-byte aligned (the kernels use 16-byte vector accesses; a misaligned
+ *     one is rejected with H2O_EINVAL before anything runs).
+ *   - Inputs must be finite: q, K and V values that are NaN or infinite give
+ *     unspecified outputs, scores and selections (the prompt calls are built
+ *     on the assumption that no NaN occurs).  Nothing checks this.
+ *   - Kernel self-checks: the step kernels record inconsistencies they detect
+ *     (a selection that found a different number of victims than scheduled,
+ *     no evictable candidate, a compaction whose holes and live tail slots
+ *     do not pair up, a block-eviction range that does not match the stored
+ *     positions) in an error word of the context.  Nothing in the decode loop
+ *     reads it back: the next h2o_read_indices reports it as H2O_EDEVICE
+ *     ("kernel consistency check failed"), so a loop that never reads does
+ *     not see it.
  *   - Layouts (row-major): q and out [B][Hq][D] fp32; k_new, v_new
  *     [B][Hkv][D] in kv_dtype (bf16 = raw bf16 bits); query head j belongs to
  *     KV head j / G, G = Hq / Hkv.
@@ -60,7 +76,10 @@
  *     before anything is enqueued; on error nothing is enqueued and the
  *     context is unchanged (H2O_EDEVICE aside).  h2o_last_error() gives the
  *     message.  One context must not be used from two threads at once;
- *     different contexts are independent.
+ *     different contexts are independent and may be driven from different
+ *     threads at the same time (the library's shared host records -- kernel
+ *     launch limits, the prompt calls' scratch, the last context-free error
+ *     -- are guarded).
  *   - Ownership: the library owns the context and its device state,
  *     allocated with hipMalloc on the device current at h2o_init and freed
  *     by h2o_destroy -- unless h2o_config::workspace is given, in which case
@@ -143,6 +162,19 @@ typedef struct {
  * and touches no device.  Errors: H2O_EINVAL (config/shape), H2O_ENOMEM (paged:
  * the prompts need more pages than max_pages). */
 int h2o_workspace_size(const h2o_config *cfg, const int32_t *prompt_len, uint64_t *bytes);
+
+/* Page pool size for the paged layout: the pages (of Hkv x 16 tokens) that
+ * cover the prompts and `steps` decode steps of every sequence under the
+ * configured selector and budget ("Attention Sinks and KV cache eviction",
+ * sec. 5: the cache is managed in fixed-size blocks).  It is the sum over the
+ * sequences of the most pages each holds at any point: ceil(P_b / 16) after
+ * the prompt load, and ceil(n_att / 16) while a step runs (the appended
+ * token's page is taken before anything is evicted).  A pool of this size
+ * (h2o_config::max_pages) never runs out in those steps.  cfg->max_pages is
+ * ignored; host arithmetic only, no device is touched.
+ * Errors: H2O_EINVAL (config/shape, page_size != 16, steps < 0, or a prompt
+ * plus `steps` past max_len). */
+int h2o_pool_pages(const h2o_config *cfg, const int32_t *prompt_len, int32_t steps, int32_t *pages);
 
 /* Create a context and load the prompts.
  *   prompt_len  host [B]: P_b >= 1.

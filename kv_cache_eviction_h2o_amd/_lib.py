@@ -20,10 +20,9 @@ _SELECTORS = {"h2o": SEL_H2O, "random": SEL_RANDOM, "block": SEL_BLOCK}
 F32, BF16, F64, I8 = 0, 1, 2, 3
 _STATUS = {H2O_EINVAL: "H2O_EINVAL", H2O_ENOMEM: "H2O_ENOMEM", H2O_EDEVICE: "H2O_EDEVICE",
            H2O_ESTATE: "H2O_ESTATE"}
-PAGE_SIZE = 16
 
 # Every symbol include/h2o.h declares.
-SYMBOLS = ("h2o_workspace_size", "h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
+SYMBOLS = ("h2o_workspace_size", "h2o_pool_pages", "h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
            "h2o_info", "h2o_read_kv", "h2o_destroy", "h2o_prefill_scores", "h2o_snapkv_select",
            "h2o_last_error")
 
@@ -63,6 +62,8 @@ def load_library(path: str = LIB):
     vp, i32p, f64p = C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_double)
     lib.h2o_workspace_size.restype = C.c_int
     lib.h2o_workspace_size.argtypes = [C.POINTER(H2OConfig), i32p, C.POINTER(C.c_uint64)]
+    lib.h2o_pool_pages.restype = C.c_int
+    lib.h2o_pool_pages.argtypes = [C.POINTER(H2OConfig), i32p, C.c_int32, i32p]
     lib.h2o_init.restype = C.c_int
     lib.h2o_init.argtypes = [C.POINTER(vp), C.POINTER(H2OConfig), i32p, vp, vp, vp, vp]
     for name in ("h2o_step", "h2o_step_compact"):
@@ -114,20 +115,16 @@ def config_from_workload(w, *, max_len, max_pages=0, **over) -> H2OConfig:
 
 
 def pages_needed(prompt_lens, steps: int, cfg: H2OConfig) -> int:
-    """Pool size that covers the prompts and any later growth (host arithmetic)."""
-    ps = PAGE_SIZE
-    first = sum((p + ps - 1) // ps for p in prompt_lens)
-    grow = 0
-    for p in prompt_lens:
-        end = p + steps
-        if cfg.selector in (SEL_H2O, SEL_BLOCK):
-            k = cfg.budget_fixed if cfg.budget_fixed > 0 else end * cfg.budget_num // cfg.budget_den
-            if cfg.selector == SEL_BLOCK:  # whole pages: up to a page past the sinks' and the window's
-                k = max(p, k + ps * ((cfg.n_sink + ps - 1) // ps) + ps - 1)
-            grow += (min(end, k + 1) + ps - 1) // ps + 1
-        else:
-            grow += (min(end, p + cfg.rand_k + cfg.rand_r) + ps - 1) // ps + 1
-    return max(first, grow) + len(prompt_lens)
+    """Page pool that covers the prompts and `steps` decode steps (h2o_pool_pages)."""
+    lib = load_library()
+    lens = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    if lens.shape != (cfg.batch,):
+        raise ValueError("prompt_lens must have one entry per sequence")
+    n = C.c_int32()
+    rc = lib.h2o_pool_pages(C.byref(cfg), lens.ctypes.data_as(C.POINTER(C.c_int32)), int(steps), C.byref(n))
+    if rc != H2O_OK:
+        raise H2OError(rc, lib.h2o_last_error(None).decode(errors="replace"))
+    return int(n.value)
 
 
 def prefill_scores(cfg: H2OConfig, prompt_lens, prompt_q, prompt_k, out=None, stream=None):

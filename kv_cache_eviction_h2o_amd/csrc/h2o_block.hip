@@ -255,17 +255,8 @@ hipError_t launch_block(const BlockArgs& a, hipStream_t st)
     const void* k1 = f64 ? (const void*)block_importance_kernel<double> : (const void*)block_importance_kernel<float>;
     const void* k2 = f64 ? (const void*)block_evict_kernel<double> : (const void*)block_evict_kernel<float>;
     hipError_t e;
-    static size_t set1[2] = {48 * 1024, 48 * 1024}, set2[2] = {48 * 1024, 48 * 1024};
-    if (dyn1 > set1[f64]) {
-        if ((e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn1)) != hipSuccess)
-            return e;
-        set1[f64] = dyn1;
-    }
-    if (dyn2 > set2[f64]) {
-        if ((e = hipFuncSetAttribute(k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn2)) != hipSuccess)
-            return e;
-        set2[f64] = dyn2;
-    }
+    static DynLdsLimit lim1[2], lim2[2];  // per kernel: [fp32 scores, fp64 scores]
+    if ((e = lim1[f64].allow(k1, dyn1)) != hipSuccess || (e = lim2[f64].allow(k2, dyn2)) != hipSuccess) return e;
     if (f64)
         hipLaunchKernelGGL(block_importance_kernel<double>, dim3(a.nseq * a.g.Hkv), dim3(kBNT), dyn1, st, a);
     else

@@ -6,6 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace h2o {
 
 constexpr int kPageShift = 4;           // 16-token KV pages
@@ -18,6 +21,39 @@ constexpr int kMaxArgBatch = 128;       // per-sequence step parameters travel i
 constexpr int kLogitLdsBytes = 64 * 1024;  // logits kept in LDS up to this size per unit
 constexpr int kMaxBlockPages = 5120;  // block eviction: block-table row held in LDS (with
                                       // importance and freed lists: 12 bytes per entry)
+constexpr int kMaxDevices = 64;        // devices the per-device host records cover
+
+// Dynamic LDS above the default 48 KB needs the kernel's limit raised on the
+// device it runs on.  One record per kernel keeps the largest size granted on
+// each device; raising it takes a mutex, so threads driving different contexts
+// may launch the same kernel at once.
+class DynLdsLimit {
+public:
+    DynLdsLimit()
+    {
+        for (auto& g : granted_) g.store(48 * 1024, std::memory_order_relaxed);
+    }
+    hipError_t allow(const void* kern, size_t bytes)
+    {
+        if (bytes <= 48 * 1024) return hipSuccess;
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        if (bytes <= granted_[dev].load(std::memory_order_acquire)) return hipSuccess;
+        std::lock_guard<std::mutex> lk(mu_);
+        if (bytes <= granted_[dev].load(std::memory_order_relaxed)) return hipSuccess;
+        if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)) != hipSuccess)
+            return e;
+        granted_[dev].store(bytes, std::memory_order_release);
+        return hipSuccess;
+    }
+
+private:
+    std::mutex mu_;
+    std::atomic<size_t> granted_[kMaxDevices];
+};
+
 // Row stride of State::bimp: whole 16-byte groups, so rows can be read in words.
 __host__ __device__ inline int bimp_stride(int maxp) { return (maxp + 15) & ~15; }
 

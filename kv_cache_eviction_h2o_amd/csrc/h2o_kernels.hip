@@ -599,13 +599,9 @@ template <typename Row, int G, typename ST, bool PAGED, bool LLDS>
 hipError_t launch_step_t(const StepArgs& a, size_t dyn, hipStream_t st)
 {
     auto k = step_kernel<Row, G, ST, PAGED, LLDS>;
-    static size_t dyn_set = 48 * 1024;  // largest dynamic LDS size granted so far
-    if (dyn > dyn_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)k,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-        if (err != hipSuccess) return err;
-        dyn_set = dyn;
-    }
+    static DynLdsLimit lim;
+    const hipError_t err = lim.allow((const void*)k, dyn);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k, dim3(a.g.B * a.g.Hkv), dim3(StepTune<G>::NT), dyn, st, a);
     return hipGetLastError();
 }

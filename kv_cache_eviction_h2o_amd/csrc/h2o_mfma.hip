@@ -364,13 +364,9 @@ template <int G, typename ST, bool LLDS>
 hipError_t launch_mfma_t(const StepArgs& a, size_t dyn, hipStream_t st)
 {
     auto k = mfma_step_kernel<G, ST, LLDS>;
-    static size_t dyn_set = 48 * 1024;  // largest dynamic LDS size granted so far
-    if (dyn > dyn_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)k,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-        if (err != hipSuccess) return err;
-        dyn_set = dyn;
-    }
+    static DynLdsLimit lim;
+    const hipError_t err = lim.allow((const void*)k, dyn);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k, dim3(a.g.B * a.g.Hkv), dim3(kMNT), dyn, st, a);
     return hipGetLastError();
 }

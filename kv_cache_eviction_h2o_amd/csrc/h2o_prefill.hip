@@ -623,18 +623,15 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
     const size_t dyn_u = (size_t)b.bits_words * 4;  // the union kernel: the bitmap only
     // above the default 48 KB of dynamic LDS the kernel's limit is raised on
     // the current device first (only prompts beyond ~130k positions need it)
-    auto allow = [](const void* kern, size_t bytes) {
-        return bytes > 48 * 1024 ? hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)
-                                 : hipSuccess;
-    };
+    static DynLdsLimit lim_sel, lim_head, lim_union;
     const unsigned units = (unsigned)(a.B * a.Hkv);
     if (a.G == 1) {
-        if ((e = allow((const void*)snapkv_select_kernel, dyn)) != hipSuccess) return e;
+        if ((e = lim_sel.allow((const void*)snapkv_select_kernel, dyn)) != hipSuccess) return e;
         hipLaunchKernelGGL(snapkv_select_kernel, dim3(units), dim3(kSNT), dyn, st, b);
         return hipGetLastError();
     }
-    if ((e = allow((const void*)snapkv_head_kernel, dyn)) != hipSuccess) return e;
-    if ((e = allow((const void*)snapkv_union_kernel, dyn_u)) != hipSuccess) return e;
+    if ((e = lim_head.allow((const void*)snapkv_head_kernel, dyn)) != hipSuccess) return e;
+    if ((e = lim_union.allow((const void*)snapkv_union_kernel, dyn_u)) != hipSuccess) return e;
     hipLaunchKernelGGL(snapkv_head_kernel, dim3(units, (unsigned)a.G), dim3(kSNT), dyn, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -187,6 +187,11 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     }
     const long long cap = slot_capacity(*c, maxP);
     if (cap > (1LL << 30)) return bad("slot capacity too large");
+    // contiguous units are read through raw buffer descriptors whose size and
+    // offsets are 32-bit: a unit's rows must stay below 2^31 bytes
+    if (!c->page_size && cap * (long long)(i8 ? kRowBytesI8 : kRowBytes) >= (1LL << 31))
+        return bad("contiguous slot capacity too large: a unit's K (or V) rows must stay below 2^31 bytes "
+                   "(use the paged layout)");
     if (c->selector == H2O_SEL_BLOCK && (cap + kPageSize - 1) / kPageSize > kMaxBlockPages)
         return bad("block eviction supports at most 5120 pages (81920 slots) per sequence");
     return H2O_OK;
@@ -417,7 +422,6 @@ struct PromptScratch {
     hipStream_t last = nullptr;
     hipEvent_t ev = nullptr;
 };
-constexpr int kMaxDevices = 64;
 PromptScratch g_prompt_scratch[kMaxDevices];
 
 
@@ -839,6 +843,54 @@ int h2o_workspace_size(const h2o_config* cfg, const int32_t* prompt_len, uint64_
     c.measure = true;
     (void)alloc_state(&c, slots_total, &t0, &poff);
     *bytes = (uint64_t)c.need;
+    return H2O_OK;
+}
+
+int h2o_pool_pages(const h2o_config* cfg, const int32_t* prompt_len, int32_t steps, int32_t* pages)
+{
+    if (!pages) return fail(nullptr, H2O_EINVAL, "null pages");
+    *pages = 0;
+    if (!cfg) return fail(nullptr, H2O_EINVAL, "null config or prompt_len");
+    if (cfg->page_size != kPageSize) return fail(nullptr, H2O_EINVAL, "pool sizing needs the paged layout (page_size 16)");
+    h2o_config c = *cfg;
+    c.max_pages = 1;  // the size being computed: any valid value for the check
+    c.workspace = nullptr;
+    std::string why;
+    const int rc = validate(&c, prompt_len, why);
+    if (rc != H2O_OK) return fail(nullptr, rc, why);
+    if (steps < 0) return fail(nullptr, H2O_EINVAL, "steps must be >= 0");
+    const Sched sc = make_sched(c);
+    const int js = sink_pages(c.n_sink);
+    long long total = 0;
+    for (int b = 0; b < c.batch; ++b) {
+        const int P = prompt_len[b];
+        if ((long long)P + steps > c.max_len) return fail(nullptr, H2O_EINVAL, "a sequence would pass max_len");
+        // the host mirror of one sequence: a step holds ceil(n_att / 16) pages
+        // while it runs (the append's page is taken before anything is evicted)
+        long long most = (P + kPageSize - 1) >> kPageShift;
+        int cnt = P, evb = 0;
+        for (int s = 0; s < steps; ++s) {
+            const int t = P + s, n_att = cnt + 1;
+            most = std::max<long long>(most, (n_att + kPageSize - 1) >> kPageShift);
+            if (c.selector == H2O_SEL_BLOCK) {
+                int K, HH, W;
+                schedule(sc, t + 1, K, HH, W);
+                int m = 0;
+                if (n_att > K) {
+                    const int kb = t + 1 - W > 0 ? (t + 1 - W) >> kPageShift : 0;
+                    const int nc = std::max(0, kb - js) - evb;
+                    m = std::min(nc, (n_att - K + kPageSize - 1) >> kPageShift);
+                }
+                evb += std::max(m, 0);
+                cnt = n_att - std::max(m, 0) * kPageSize;
+            } else {
+                cnt = n_att - evict_count(sc, t, P, n_att);
+            }
+        }
+        total += most;
+    }
+    if (total > INT32_MAX) return fail(nullptr, H2O_EINVAL, "page pool larger than 2^31 pages");
+    *pages = (int32_t)total;
     return H2O_OK;
 }
 

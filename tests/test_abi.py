@@ -178,22 +178,58 @@ def test_binding_fails_loudly_without_library(tmp_path):
         mod._lib = saved
 
 
-def test_page_pool_sizing_host_logic():
-    cfg = L.make_config(**{**GOOD, "budget_fixed": 0, "budget_num": 1, "budget_den": 5,
-                           "page_size": 16, "max_pages": 1, "max_len": 70000})
-    lens = [4096, 65536]
-    need = L.pages_needed(lens, 65, cfg)
-    assert need >= sum((p + 15) // 16 for p in lens)
+def test_contiguous_unit_past_32bit_descriptor_rejected(lib):
+    """Contiguous units are read through 32-bit buffer descriptors: a unit whose
+    K rows reach 2^31 bytes is refused (the paged layout has no such limit)."""
+    big = dict(budget_fixed=(1 << 23), hh_fixed=1000, max_len=(1 << 23) + 10)
+    rc, ctx = _init(lib, L.make_config(**{**GOOD, **big}), [100, 200])
+    assert rc == L.H2O_EINVAL and not ctx.value
+    assert "2^31 bytes" in lib.h2o_last_error(None).decode()
+    ok = dict(budget_fixed=(1 << 23) - 2, hh_fixed=1000, max_len=(1 << 23) + 10)
+    n = C.c_uint64()
+    arr = (C.c_int32 * 2)(100, 200)
+    assert lib.h2o_workspace_size(C.byref(L.make_config(**{**GOOD, **ok})), arr, C.byref(n)) == L.H2O_OK
+    paged = dict(big, page_size=16, max_pages=64)
+    assert lib.h2o_workspace_size(C.byref(L.make_config(**{**GOOD, **paged})), arr, C.byref(n)) == L.H2O_OK
 
 
-def test_block_pool_sizing_covers_capacity():
-    # block eviction holds up to K + a sink page + a page past the window's start
-    cfg = L.make_config(**{**GOOD, "selector": "block", "budget_fixed": 0, "budget_num": 1,
-                           "budget_den": 5, "page_size": 16, "max_pages": 1, "max_len": 70000})
-    lens = [4096, 65536]
-    need = L.pages_needed(lens, 65, cfg)
-    k_end = [(p + 65) // 5 for p in lens]
-    assert need >= sum((max(p, k + 16 + 15) + 1 + 15) // 16 for p, k in zip(lens, k_end))
+def _pool_mirror(w, lens, steps):
+    """Sum over sequences of the most pages each holds: ceil(P / 16) after the
+    prompt, ceil(n_att / 16) while a step runs (metrics' host mirror)."""
+    from kv_cache_eviction_h2o_amd import metrics as M
+    tot = 0
+    for P in lens:
+        n_att = M.retained_counts(w, P, steps)["n_att"]
+        tot += max((P + 15) // 16, int(((n_att + 15) // 16).max()) if steps else 0)
+    return tot
+
+
+@pytest.mark.parametrize("selector", ["h2o", "block", "random"])
+def test_page_pool_sizing_matches_mirror(lib, selector):
+    """h2o_pool_pages equals the sum of each sequence's largest page count under
+    the selector's schedule (host mirror in metrics.retained_counts)."""
+    from kv_cache_eviction_h2o_amd import workloads as WL
+    if selector == "random":
+        w = WL.RANDOM_ATTN.scaled(batch=3, n_q_heads=8, n_kv_heads=2, rand_k=64, rand_r=16, page_size=16)
+    else:
+        w = WL.PAGED_MIXED.scaled(batch=3, n_q_heads=4, n_kv_heads=4, selector=selector)
+    lens, steps = [40, 1500, 4097], 300
+    cfg = L.config_from_workload(w, max_len=max(lens) + steps + 1, max_pages=1)
+    assert L.pages_needed(lens, steps, cfg) == _pool_mirror(w, lens, steps)
+    assert L.pages_needed(lens, 0, cfg) == sum((p + 15) // 16 for p in lens)
+
+
+def test_page_pool_sizing_rejects(lib):
+    base = {**GOOD, "budget_fixed": 0, "budget_num": 1, "budget_den": 5, "page_size": 16, "max_len": 5000}
+    arr = (C.c_int32 * 2)(100, 200)
+    n = C.c_int32()
+    assert lib.h2o_pool_pages(C.byref(L.make_config(**{**base, "page_size": 0})), arr, 10, C.byref(n)) == L.H2O_EINVAL
+    assert "paged layout" in lib.h2o_last_error(None).decode()
+    assert lib.h2o_pool_pages(C.byref(L.make_config(**base)), arr, -1, C.byref(n)) == L.H2O_EINVAL
+    assert lib.h2o_pool_pages(C.byref(L.make_config(**base)), arr, 4900, C.byref(n)) == L.H2O_EINVAL
+    assert "max_len" in lib.h2o_last_error(None).decode()
+    assert lib.h2o_pool_pages(C.byref(L.make_config(**base)), arr, 10, None) == L.H2O_EINVAL
+    assert lib.h2o_pool_pages(C.byref(L.make_config(**base)), arr, 10, C.byref(n)) == L.H2O_OK and n.value > 0
 
 
 def _prefill(lib, cfg, lens, ptr=16):
