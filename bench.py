@@ -1,13 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the H2O decode step (attention + evict + compact) on one MI355X.
 
-Default workload: an OPT-6.7B-shaped layer (batch 8, 32 heads x 128, bf16 K/V,
-fp32 cumulative scores, 4 sinks, budget 20 % of the current length split
-between heavy hitters and the recent window), prompt 1024 then 1024 decode
-steps, stepped through 32 independent layer instances in turn as one decode
-step of the model does (so the working set leaves the 256 MB Infinity Cache).
-The timed window starts at decode step 512 of the trace; the steps before it
-are run untimed to reach that state.
+Default workload: the paged mixed-length batch -- 64 sequences with prompts
+uniform on [4096, 65536] tokens, 32 heads x 128, bf16 K/V in 16-token pages
+with a block table, fp32 cumulative scores, 4 sinks and a budget of 20 % of the
+current length split between heavy hitters and the recent window (the largest
+single-GPU workload: ~2.2 M prompt tokens, ~36 GB of prompt K/V).  Its first
+decode step bulk-evicts every sequence from its prompt to the budget and frees
+~80 % of the pages; it runs untimed, then the warm-up steps, then the timed
+window of steady steps (one eviction per sequence and head on four of every
+five steps).  Other workloads (--workload): the OPT-6.7B layer stepped through
+32 layer instances, the LLaMA-2-70B GQA layer through 80, Random Attention, the
+tiny correctness workload, int8 rows and block eviction; the steps before each
+one's window are run untimed to reach its state.
 
 Metric: retained KV tokens processed per second (a retained token counts once
 per sequence per layer-step), with the step's algorithmic bytes as a fraction
@@ -18,7 +23,7 @@ layers' launches back to back, so this per-launch time includes the short
 dispatch gap between launches).  `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -54,7 +59,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 def summarize(args) -> None:
     """Summary of rocprofv3 CSV output for one kernel (default: the step kernel; see --help)."""
     import csv
-    n_last = args.steps * (args.layers or 32)
+    line = None
+    if args.summarize_bench_line:  # the JSON line the profiled run printed: its window and bytes
+        with open(args.summarize_bench_line) as f:
+            line = json.loads([x for x in f.read().splitlines() if x.startswith("{")][-1])
+        n_last = line["steps"] * line["config"].get("layers", 1)
+    else:
+        if args.steps is None:
+            raise SystemExit("--summarize-* needs --steps (and --layers) or --summarize-bench-line")
+        n_last = args.steps * (args.layers or 1)
     kname = args.summarize_kernel
     out = [f"kernel_source_sha256_16: {kernel_hash(prompt=kname.startswith(PROMPT_KERNELS))}"]
     if args.summarize_trace:
@@ -85,6 +98,12 @@ def summarize(args) -> None:
                        f"copy reads {cal:.1f} KiB on this counter -> scale x{factor:.4f}")
         hbm = sum(v * f * 1024 for v, f, _ in res.values())
         out.append(f"hbm_bytes_per_launch: {hbm:.6e}")
+        if line is not None and line.get("roofline"):
+            alg = line["roofline"]["algorithmic_bytes_per_launch"]
+            out += [f"workload: {line['config']['workload']}",
+                    f"window_steps: {json.dumps(line['config']['window_steps'])}",
+                    f"algorithmic_bytes_per_launch: {alg:.6e}",
+                    f"measured / algorithmic: {hbm / alg:.4f}"]
     if args.summarize_pmc:
         by = {}
         for r in csv.DictReader(open(args.summarize_pmc)):
@@ -109,17 +128,21 @@ def parse():
                     help="with FETCH_SIZE / WRITE_SIZE counter CSVs: HBM bytes per launch")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
                     help="with a rocprofv3 --pmc counter CSV: each counter's mean per launch")
+    ap.add_argument("--summarize-bench-line", metavar="JSON_LINE_FILE",
+                    help="the output of the profiled bench run: its timed window (steps x layers "
+                         "launches at the end of the trace) and algorithmic bytes per launch")
     ap.add_argument("--summarize-kernel", default="step_kernel", metavar="NAME",
                     help="kernel the summaries cover (a substring of its name; the timed window is "
                          "the last steps x layers of its launches)")
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default=WL.OPT_LAYER.name,
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: per workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: per workload)")
+    ap.add_argument("--workload", default=WL.PAGED_MIXED.name,
                     choices=[w.name for w in WL.ALL + WL.VARIANTS])
     ap.add_argument("--layers", type=int, default=0, help="layer instances (0 = workload default)")
-    ap.add_argument("--window-start", type=int, default=512,
-                    help="decode step at which the timed window starts")
+    ap.add_argument("--window-start", type=int, default=None,
+                    help="decode step at which the timed window starts (default: per workload; the "
+                         "paged workloads start right after the bulk first step and the warm-up)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--events", choices=["step", "launch", "none"], default="step",
@@ -180,6 +203,39 @@ def kernel_hash(prompt: bool = False) -> str:
     return h.hexdigest()[:16]
 
 
+# Timed window of each workload when the command line names none: (steps,
+# warm-up steps, first timed step or None = the bulk first step, then the
+# warm-up).  OPT layer: steps 512-767 of its 1024-step trace; GQA layer: its
+# steady state (every step attends 1029 slots and evicts one from step 4 on);
+# Random Attention: a window holding two eviction events (steps 2303, 2431).
+WINDOWS = {
+    WL.TINY_H2O.name: (64, 16, 128),
+    WL.OPT_LAYER.name: (256, 16, 512),
+    WL.OPT_LAYER_I8.name: (256, 16, 512),
+    WL.LLAMA_GQA.name: (256, 16, 16),
+    WL.RANDOM_ATTN.name: (256, 16, 2176),
+    WL.PAGED_MIXED.name: (60, 4, None),
+    WL.PAGED_BLOCK.name: (60, 4, None),
+}
+
+
+def bench_window(w, steps=None, warmup=None, start=None):
+    """(timed steps K, warm-up W, first timed step s0) for a workload: the
+    command line's values where given, else the workload's defaults.  The steps
+    before s0 run untimed (the last W of them are the warm-up); contiguous
+    workloads keep the window inside their trace, the paged ones may run past
+    their 65 nominal steps (the budget rule goes on)."""
+    K0, W0, S0 = WINDOWS[w.name]
+    K = K0 if steps is None else steps
+    W = W0 if warmup is None else warmup
+    s0 = start if start is not None else (S0 if S0 is not None else 1 + W)
+    if not w.page_size:
+        s0 = min(s0, w.decode_steps - K)
+    if s0 < W or K < 1 or W < 0:
+        raise SystemExit("window does not fit the trace: lower --steps or --warmup")
+    return K, W, s0
+
+
 def step_kernel_name(w) -> str:
     """The step kernel the library launches for a workload: GQA groups of 4 or 8
     over bf16 rows of 128 in contiguous slots run on the matrix cores."""
@@ -194,68 +250,92 @@ def retained_schedule(w, P: int, n_steps: int):
     return M.retained_counts(w, P, n_steps)["n_att"]
 
 
-def traffic_from_profiles(w):
-    """Measured HBM bytes per launch from a committed counter summary, if it was
-    taken on the current kernel source (else None)."""
+def traffic_from_profiles(w, alg_bytes: float):
+    """Measured HBM bytes per launch for this line, from a committed counter
+    summary taken on the current kernel source (else None).  The summary holds
+    the counters' bytes per launch and the algorithmic bytes per launch of the
+    window it was taken over; the line's own window gets the same ratio of
+    measured to algorithmic bytes, applied to its algorithmic bytes."""
     path = os.path.join(PROFILES, f"h2o_{step_kernel_name(w)}_{w.name}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    a = re.search(r"algorithmic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    win = re.search(r"window_steps:\s*(\[[0-9, ]+\])", text)
     if not m or not t or m.group(1) != kernel_hash():
         return None
-    return float(t.group(1))
+    hbm = float(t.group(1))
+    if not a:
+        return {"bytes": hbm, "ratio": None, "window": None}
+    ratio = hbm / float(a.group(1))
+    return {"bytes": ratio * alg_bytes, "ratio": ratio, "window": json.loads(win.group(1)) if win else None}
 
 
-def cpu_baseline(w, n_att: int, seconds: float):
-    """The fp64 oracle (as it stands) on one layer of the workload at the
-    window's retained length, all host cores, for about `seconds`."""
+def cpu_baseline(w, n_att: int, seconds: float, max_slots: int = 600_000):
+    """The fp64 oracle (as it stands) on a bounded sample of one layer of the
+    workload at the window's retained length: as many whole sequences (every KV
+    head) as keep the sample within max_slots retained slots, all host cores
+    for about `seconds`, then one core for a third of that."""
     import oracle as O
     B, Hkv, Hq, G, D = w.batch, w.n_kv_heads, w.n_q_heads, w.group, w.head_dim
     K = n_att - 1  # fixed budget: every step attends n_att slots and evicts one
     ws = w.scaled(budget_fixed=K, hh_fixed=(K - w.n_sink) // 2)
-    lens = [K] * B
+    nseq = max(1, min(B, max_slots // max(1, Hkv * n_att)))
+    lens = [K] * nseq
     Kp, Vp = S.prompt_kv(w.recipe, 0, lens, Hkv)
     cfg = O.cfg_from_workload(ws)
-    max_steps = 4096
+    max_steps = 2048
     units = []
-    for b in range(B):
+    for b in range(nseq):
         for h in range(Hkv):
             units.append(O.Unit(cfg, b, h, S.cache_to_f64(w.recipe, Kp[b * K:(b + 1) * K, h]),
                                 S.cache_to_f64(w.recipe, Vp[b * K:(b + 1) * K, h]), K + max_steps + 1))
+    del Kp, Vp
     threads = min(os.cpu_count() or 1, len(units))
     block = w.selector == "block"
-    done, t_used, tokens = 0, 0.0, 0
+    done = 0
     win = 32
-    while t_used < seconds and done < max_steps:
-        q, k, v = S.step_window(w.recipe, 0, [K + done] * B, win, Hq, Hkv)
-        for i in range(win):
-            qs = [q[i, b, h * G:(h + 1) * G] for b in range(B) for h in range(Hkv)]
-            ks = [S.cache_to_f64(w.recipe, k[i, b, h]) for b in range(B) for h in range(Hkv)]
-            vs = [S.cache_to_f64(w.recipe, v[i, b, h]) for b in range(B) for h in range(Hkv)]
-            qs = [np.ascontiguousarray(x, np.float64) for x in qs]
-            tokens += sum(len(units[b * Hkv].state()[0]) + 1 for b in range(B))
-            t0 = time.perf_counter()
-            O.step_many(units, qs, ks, vs, threads)
-            if block:  # whole pages go per sequence, chosen over its heads
-                for b in range(B):
-                    us = units[b * Hkv:(b + 1) * Hkv]
-                    vic = O.block_select(us)
-                    for u in us:
-                        u.evict(vic)
-            t_used += time.perf_counter() - t0
-            done += 1
-            if t_used >= seconds:
-                break
+
+    def run(nthreads, budget):
+        nonlocal done
+        t_used, tokens = 0.0, 0
+        while t_used < budget and done < max_steps:
+            q, k, v = S.step_window(w.recipe, 0, [K + done] * nseq, win, Hq, Hkv)
+            for i in range(win):
+                qs = [np.ascontiguousarray(q[i, b, h * G:(h + 1) * G], np.float64)
+                      for b in range(nseq) for h in range(Hkv)]
+                ks = [S.cache_to_f64(w.recipe, k[i, b, h]) for b in range(nseq) for h in range(Hkv)]
+                vs = [S.cache_to_f64(w.recipe, v[i, b, h]) for b in range(nseq) for h in range(Hkv)]
+                tokens += nseq * n_att
+                t0 = time.perf_counter()
+                O.step_many(units, qs, ks, vs, nthreads)
+                if block:  # whole pages go per sequence, chosen over its heads
+                    for b in range(nseq):
+                        us = units[b * Hkv:(b + 1) * Hkv]
+                        vic = O.block_select(us)
+                        for u in us:
+                            u.evict(vic)
+                t_used += time.perf_counter() - t0
+                done += 1
+                if t_used >= budget or done >= max_steps:
+                    break
+        return tokens / t_used, t_used
+
+    value, t_all = run(threads, seconds)
+    steps_all = done
+    value1, t_one = run(1, seconds / 3)
     how = ("then the block selection of every sequence (one thread)" if block
            else "one token evicted per unit and step")
-    return {"value": tokens / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "host": host_cpu(),
-            "sample": (f"one layer ({B} sequences x {Hkv} KV heads) with a fixed budget at the "
-                       f"window's retained length n_att={n_att}, {done} decode steps, fp64 oracle "
-                       f"steps on {threads} threads, {how}; {t_used:.1f} s of CPU step time "
-                       f"(input conversion excluded)")}
+            "one_core": {"value": value1, "cores": 1, "seconds": round(t_one, 1),
+                         "steps": done - steps_all},
+            "sample": (f"{nseq} of the layer's {B} sequences x {Hkv} KV heads ({nseq * Hkv} units) with a "
+                       f"fixed budget at the window's retained length n_att={n_att}; {steps_all} decode steps "
+                       f"of fp64 oracle steps on {threads} threads ({t_all:.1f} s of CPU step time), then "
+                       f"{done - steps_all} on one thread ({t_one:.1f} s), {how}; input conversion excluded")}
 
 
 def host_cpu() -> str:
@@ -502,17 +582,15 @@ def main():
     from kv_cache_eviction_h2o_amd import _lib as L
 
     w = next(x for x in WL.ALL + WL.VARIANTS if x.name == args.workload)
-    if args.prefill:
-        prefill_main(args, w)
-        return
-    if args.snapkv:
-        snapkv_main(args, w)
+    if args.prefill or args.snapkv:
+        if args.workload == WL.PAGED_MIXED.name and "--workload" not in sys.argv:
+            w = WL.OPT_LAYER  # the prompt calls' default: one OPT-6.7B layer's prompts
+        args.steps = 256 if args.steps is None else args.steps
+        args.warmup = 16 if args.warmup is None else args.warmup
+        (prefill_main if args.prefill else snapkv_main)(args, w)
         return
     layers = args.layers or w.layers
-    K_steps, W_steps = args.steps, args.warmup
-    s0 = min(args.window_start, w.decode_steps - K_steps)
-    if s0 < W_steps or K_steps < 1:
-        raise SystemExit("window does not fit the trace: lower --steps or --warmup")
+    K_steps, W_steps, s0 = bench_window(w, args.steps, args.warmup, args.window_start)
     total_steps = s0 + K_steps
     lens = WL.prompt_lengths(w)
     B, Hq, Hkv, D, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
@@ -524,12 +602,13 @@ def main():
     # ---- set-up (untimed): layer instances, inputs of every step in HBM
     t_setup = time.perf_counter()
     caches, qs, ks, vs, outs = [], [], [], [], []
-    max_len = max(lens) + w.decode_steps + 1
+    n_trace = max(w.decode_steps, total_steps)
+    max_len = max(lens) + n_trace + 1
     for l in range(layers):
         pk, pv = S.device_prompt_kv(w.recipe, l, lens, Hkv, dev)
         cfg = L.config_from_workload(w, max_len=max_len)
         if w.page_size:
-            cfg.max_pages = L.pages_needed(lens, w.decode_steps, cfg)
+            cfg.max_pages = L.pages_needed(lens, n_trace, cfg)
         caches.append(L.H2OCache(cfg, lens, pk, pv))
         q, k, v = S.device_step_window(w.recipe, l, lens, total_steps, Hq, Hkv, dev)
         qs.append(q)
@@ -618,12 +697,17 @@ def main():
                 hev.destroy(e0)
                 hev.destroy(e1)
         achieved = float((launch_b[:, None] * np.ones((1, layers))).sum() / dur.sum()) / 1e9
-        traffic = traffic_from_profiles(w)
+        tr = traffic_from_profiles(w, float(launch_b.mean()))
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr["bytes"]),
                 "kernel": step_kernel_name(w), "timing": events,
                 "mean_launch_us": round(float(dur.mean()) * 1e6, 3),
                 "algorithmic_bytes_per_launch": int(launch_b.mean())}
+        if tr is not None and tr["ratio"] is not None:
+            roof["traffic_over_algorithmic"] = round(tr["ratio"], 4)
+            roof["traffic_note"] = (f"FETCH_SIZE + WRITE_SIZE per launch over the counter profile's window "
+                                    f"(steps {tr['window']}), as a ratio to that window's algorithmic bytes, "
+                                    f"applied to this window's")
 
     # sanity: the library's counts equal the schedule used for the accounting
     expect = np.array([c["count"][-1] for c in counts])

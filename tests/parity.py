@@ -61,6 +61,7 @@ class ParityReport:
     max_out_err: float = 0.0
     max_score_err: float = 0.0
     evictions: int = 0
+    max_swapped: int = 0
     notes: list = field(default_factory=list)
 
 
@@ -79,18 +80,31 @@ def make_cache(w: WL.Workload, lens, n_steps: int, layer: int = 0, init_scores=N
     return cache, K, V
 
 
+def _oracle_threads(n_units: int) -> int:
+    import os
+    return max(1, min(16, os.cpu_count() or 1, n_units))
+
+
 def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=True, layer=0,
-               init_scores=None, read_every=1, check_scores=True, device_inputs=False,
-               stored_rows=True, properties=False) -> ParityReport:
+               init_scores=None, read_every=1, check_steps=(), check_scores=True, device_inputs=False,
+               stored_rows=True, properties=False, max_swapped=None) -> ParityReport:
     """Run n_steps on the GPU and in the oracle (for `units`, default all).
 
+    Checked steps: every read_every-th, those in check_steps, and the last.
     device_inputs: prompts and steps drawn on the device (the benchmark's
     generator, for full-size batches); the checked units' rows are copied back
     for the oracle, and reads are sized by the host mirror of the counts.
     stored_rows: check the stored rows of the checked units at the end.
     properties: after the last step, check every unit for what holds at any
-    size (h2o_properties)."""
+    size (h2o_properties).
+    max_swapped: at most this many tokens of a unit-step may differ from the
+    oracle's victims under the near-tie rule (a check stricter than the rule:
+    when scores are far below the absolute gap, as after the bulk first step of
+    long prompts, the rule alone would accept any candidate).
+    The oracle steps its units on POSIX threads (orc_step_many) between checked
+    steps, and attends them on a thread pool at checked steps."""
     import torch
+    from concurrent.futures import ThreadPoolExecutor
     lens = list(lens) if lens is not None else WL.prompt_lengths(w)
     B, Hq, Hkv, G, D = w.batch, w.n_q_heads, w.n_kv_heads, w.group, w.head_dim
     assert len(lens) == B
@@ -126,6 +140,10 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     win = 256
     gen_k, gen_v = [], []  # generated rows of the decode steps, for the stored-row check
+    check_steps = set(check_steps)
+    nthr = _oracle_threads(len(units))
+    pool = ThreadPoolExecutor(nthr)
+    ulist = [orc[bh] for bh in units]
     for s0 in range(0, n_steps, win):
         ns = min(win, n_steps - s0)
         t0 = [p + s0 for p in lens]
@@ -145,19 +163,21 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
             else:
                 cache.step(qd[i], kd[i], vd[i], out)
                 cache.compact()
-            check = (s % read_every == 0) or s == n_steps - 1
+            check = (s % read_every == 0) or s in check_steps or s == n_steps - 1
             if not check:
                 # the oracle still has to take the step (its own choice)
-                for (b, h) in units:
-                    orc[(b, h)].step(q[i, b, h * G:(h + 1) * G], oracle_rows(w, k[i, b, h]),
-                                     oracle_rows(w, v[i, b, h]))
+                O.step_many(ulist, [q[i, b, h * G:(h + 1) * G] for (b, h) in units],
+                            [oracle_rows(w, k[i, b, h]) for (b, h) in units],
+                            [oracle_rows(w, v[i, b, h]) for (b, h) in units], nthr)
                 continue
             o_gpu = out.cpu().numpy()
             pos, cnt, sc, em = cache.read_indices(cap)
-            for (b, h) in units:
+            o_refs = list(pool.map(lambda bh: orc[bh].attend(q[i, bh[0], bh[1] * G:(bh[1] + 1) * G],
+                                                             oracle_rows(w, k[i, bh[0], bh[1]]),
+                                                             oracle_rows(w, v[i, bh[0], bh[1]])), units))
+            for ui, (b, h) in enumerate(units):
                 u = orc[(b, h)]
-                o_ref = u.attend(q[i, b, h * G:(h + 1) * G], oracle_rows(w, k[i, b, h]),
-                                 oracle_rows(w, v[i, b, h]))
+                o_ref = o_refs[ui]
                 og = o_gpu[b, h * G:(h + 1) * G].astype(np.float64)
                 err = np.max(np.abs(og - o_ref), axis=1) / np.maximum(np.max(np.abs(o_ref), axis=1), 1e-30)
                 rep.max_out_err = max(rep.max_out_err, float(err.max()))
@@ -176,6 +196,9 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
                     assert ok, (f"step {s} unit {(b, h)}: victims differ: oracle-only "
                                 f"{sorted(set(vic.tolist()) - set(gvic))[:8]} gpu-only "
                                 f"{sorted(set(gvic) - set(vic.tolist()))[:8]} tau={tau}")
+                    assert max_swapped is None or len(diff) // 2 <= max_swapped, \
+                        f"step {s} unit {(b, h)}: {len(diff) // 2} victims swapped under the near-tie rule"
+                    rep.max_swapped = max(rep.max_swapped, len(diff) // 2)
                     u.evict(np.array(gvic, dtype=np.int32))
                     rep.adopted += 1
                 else:
@@ -194,6 +217,7 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
                     assert abs(em[b, h] - o_em) <= SCORE_TOL * max(1.0, o_em), \
                         f"step {s} unit {(b, h)}: evicted mass {em[b, h]} vs {o_em}"
             rep.steps += 1
+    pool.shutdown()
     if stored_rows:
         check_stored_rows(w, cache, units, lens, K, V, gen_k, gen_v, cap=cap)
     if properties:
@@ -201,7 +225,7 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
     cache.close()
     say(f"[parity] ok: checked {rep.steps} steps x {rep.units} units, max out err "
         f"{rep.max_out_err:.2e}, max score err {rep.max_score_err:.2e}, evictions {rep.evictions}, "
-        f"near-ties adopted {rep.adopted}")
+        f"near-ties adopted {rep.adopted} (most tokens swapped in one: {rep.max_swapped})")
     return rep
 
 

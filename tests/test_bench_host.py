@@ -35,7 +35,7 @@ def test_summarize_pmc_means_over_the_timed_window(tmp_path, capsys):
             w.writerow(["h2o::step_kernel<...>", "SQ_WAIT_ANY", 50])
             w.writerow(["other_kernel", "SQ_WAVE_CYCLES", 1e9])
     args = types.SimpleNamespace(steps=2, layers=2, summarize_kernel="step_kernel", summarize_trace=None,
-                                 summarize_counters=None, summarize_pmc=str(f))
+                                 summarize_counters=None, summarize_pmc=str(f), summarize_bench_line=None)
     bench.summarize(args)
     out = capsys.readouterr().out
     assert f"kernel_source_sha256_16: {bench.kernel_hash()}" in out
@@ -51,3 +51,62 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_default_window_is_the_paged_workload_after_its_bulk_step():
+    """With no flags the bench measures the paged mixed-length workload (the
+    largest single-GPU one); its window starts after the bulk first step and the
+    warm-up, whatever --steps / --warmup say."""
+    from kv_cache_eviction_h2o_amd import workloads as WL
+    args = bench_args([])
+    assert args.workload == WL.PAGED_MIXED.name
+    w = WL.PAGED_MIXED
+    assert bench.bench_window(w) == (60, 4, 5)
+    assert bench.bench_window(w, 20, 5) == (20, 5, 6)
+    assert bench.bench_window(WL.OPT_LAYER, 20, 5) == (20, 5, 512)
+    # contiguous traces keep the window inside them
+    assert bench.bench_window(WL.OPT_LAYER, 600, 16) == (600, 16, 424)
+
+
+def bench_args(argv):
+    import sys
+    saved = sys.argv
+    try:
+        sys.argv = ["bench.py", *argv]
+        return bench.parse()
+    finally:
+        sys.argv = saved
+
+
+def test_summary_records_window_and_traffic_scales_to_the_line(tmp_path, capsys, monkeypatch):
+    """The counter summary keeps the profiled window's algorithmic bytes; a bench
+    line on another window reports the same measured/algorithmic ratio applied
+    to its own algorithmic bytes."""
+    import json
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    for path, name, val in ((fetch, "FETCH_SIZE", 500.0), (write, "WRITE_SIZE", 100.0)):
+        with open(path, "w", newline="") as fh:
+            cw = csv.writer(fh)
+            cw.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+            cw.writerow(["copyBuffer", name, 524288.0 if name == "FETCH_SIZE" else 1048576.0])
+            for _ in range(3):
+                cw.writerow(["h2o::step_kernel<...>", name, val])
+    line = tmp_path / "line.json"
+    line.write_text("noise\n" + json.dumps({"steps": 3, "config": {"workload": "paged_mixed_4k-64k_20pct",
+                                                                    "layers": 1, "window_steps": [6, 9]},
+                                            "roofline": {"algorithmic_bytes_per_launch": 1000 * 1024}}) + "\n")
+    args = types.SimpleNamespace(steps=None, layers=0, summarize_kernel="step_kernel", summarize_trace=None,
+                                 summarize_counters=[str(fetch), str(write)], summarize_pmc=None,
+                                 summarize_bench_line=str(line))
+    bench.summarize(args)
+    out = capsys.readouterr().out
+    # FETCH_SIZE counts half the bytes read (x2), WRITE_SIZE all of them: 1100 KiB per launch
+    assert "hbm_bytes_per_launch: 1.126400e+06" in out
+    assert "window_steps: [6, 9]" in out and "measured / algorithmic: 1.1000" in out
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "h2o_step_kernel_paged_mixed_4k-64k_20pct_counters.md").write_text(out)
+    monkeypatch.setattr(bench, "PROFILES", str(prof))
+    from kv_cache_eviction_h2o_amd import workloads as WL
+    tr = bench.traffic_from_profiles(WL.PAGED_MIXED, 2000.0)
+    assert abs(tr["ratio"] - 1.1) < 1e-9 and abs(tr["bytes"] - 2200.0) < 1e-6 and tr["window"] == [6, 9]

@@ -173,3 +173,68 @@ def test_workspace_context_matches_library_allocated(wname):
     a.close()
     b.close()
     assert int(ws[:16].sum()) >= 0  # the caller's memory is still the caller's
+
+
+def _two_thread_check():
+    """Two contexts stepped at once from two host threads, each on its own
+    stream, then twins of both stepped one after the other on one thread: every
+    step's outputs and the final states must be bit-identical.  Both kernels keep
+    more than the default 48 KB of dynamic LDS (their logits: the matrix-core
+    kernel 8 heads x 1728 slots, the FMA kernel 1 head x 14101 slots), so in a
+    fresh process the two threads race to raise the same launch limits."""
+    import threading
+
+    import torch
+    ws = [WL.LLAMA_GQA.scaled(batch=2, budget_fixed=1700, hh_fixed=800),
+          WL.OPT_LAYER.scaled(batch=2, n_q_heads=2, n_kv_heads=2, budget_fixed=14000, hh_fixed=7000)]
+    lens = [[1750, 1600], [14100, 9000]]
+    steps = 24
+    setups = [_setup(w, l, steps) for w, l in zip(ws, lens)]
+    outs = [[None] * steps for _ in ws]
+    caches = [mk() for (_, mk, _, _, _) in setups]
+    torch.cuda.synchronize()
+    errors = []
+
+    def drive(i):
+        try:
+            _, _, qd, kd, vd = setups[i]
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                o = torch.empty((ws[i].batch, ws[i].n_q_heads, ws[i].head_dim), dtype=torch.float32,
+                                device="cuda")
+                for s in range(steps):
+                    caches[i].step_compact(qd[s], kd[s], vd[s], o)
+                    outs[i][s] = o.clone()
+            st.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    th = [threading.Thread(target=drive, args=(i,)) for i in range(len(ws))]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    for i, w in enumerate(ws):
+        _, mk, qd, kd, vd = setups[i]
+        twin = mk()
+        o = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        for s in range(steps):
+            twin.step_compact(qd[s], kd[s], vd[s], o)
+            assert torch.equal(o, outs[i][s]), f"context {i} step {s}: outputs differ"
+        _same(caches[i], twin)
+    print("two-thread check ok", flush=True)
+
+
+def test_two_threads_drive_two_contexts():
+    """_two_thread_check in a fresh process, so that the dynamic-LDS launch
+    limits start unraised and both threads reach them together."""
+    import os
+    import subprocess
+    import sys
+    tests = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(tests)
+    code = (f"import sys; sys.path[:0] = [{root!r}, {tests!r}]; "
+            "import test_gpu_api as t; t._two_thread_check()")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "two-thread check ok" in r.stdout, (r.stdout[-2000:], r.stderr[-3000:])

@@ -27,13 +27,16 @@ def test_default_bench_line_has_every_field():
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 8 and d["warmup"] == 2 and d["value"] > 0
     assert d["higher_is_better"] is True and d["data"] == "synthetic"
-    assert d["config"]["workload"] == "opt6.7b_layer_20pct"
+    # the default is the largest single-GPU workload, timed after its bulk first step and the warm-up
+    assert d["config"]["workload"] == "paged_mixed_4k-64k_20pct"
+    assert d["config"]["window_steps"] == [3, 11]
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert "traffic" in rf
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["one_core"]["cores"] == 1 and cb["one_core"]["value"] > 0
 
 
 @pytest.mark.parametrize("mode", ["--prefill", "--snapkv"])

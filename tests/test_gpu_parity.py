@@ -53,12 +53,17 @@ def test_llama_gqa_reduced():
     assert rep.evictions >= 73 * 8
 
 
-def test_llama_gqa_long_trace():
-    # 2000 steps, one eviction per step per unit after the first: long enough for
-    # score rounding to drift if it did (fp64 scores; fp32 ones run the OPT trace)
-    w = WL.LLAMA_GQA.scaled(batch=1, prompt_len=1100)
-    rep = P().run_parity(w, 2000)
-    assert rep.evictions == 8 * (73 + 1999)  # bulk 1101 -> 1028 at the first step, then one a step
+def test_llama_gqa_full_context_trace():
+    """The GQA layer's whole trace at batch 1: prompt 1024, then 31,744 decode
+    steps until the context reaches 32,768 tokens, every step against the oracle
+    (fp64 scores; one eviction per unit and step from t = 1028 on).  Long enough
+    for score rounding to drift if it did: the heavy hitters' scores reach
+    thousands while the eviction boundary sits at scores of order one."""
+    w = WL.LLAMA_GQA.scaled(batch=1)
+    n = w.decode_steps
+    assert w.prompt_len + n == 32768
+    rep = P().run_parity(w, n, stored_rows=True)
+    assert rep.steps == n and rep.evictions == 8 * (n - 4)  # K = 1028: the first eviction at step 4
 
 
 def test_random_attention_long_trace():
@@ -100,6 +105,19 @@ def test_random_attention_full_shape_sampled_units():
     w = WL.RANDOM_ATTN.scaled(rand_k=256)
     rep = P().run_parity(w, 400, units=[(0, 0), (31, 7), (12, 3)])
     assert rep.evictions == 3 * 128  # the event at 384 generated tokens
+
+
+def test_random_attention_stated_config_two_events():
+    """Random Attention exactly as stated: 32 sequences, 32 query / 8 KV heads,
+    a 2048-token prompt kept, K = 2048 generated tokens kept, buffer r = 128.
+    The first event fires at step 2175 (2176 generated tokens after the append),
+    the second 128 steps later; four sampled units are checked every 128 steps
+    and around both events, their victim sets identical to the oracle's."""
+    w = WL.RANDOM_ATTN
+    assert (w.batch, w.n_q_heads, w.n_kv_heads, w.prompt_len, w.rand_k, w.rand_r) == (32, 32, 8, 2048, 2048, 128)
+    units = [(0, 0), (31, 7), (12, 3), (5, 5)]
+    rep = P().run_parity(w, 2304, units=units, read_every=128, check_steps={2174, 2175, 2176, 2302, 2303})
+    assert rep.evictions == len(units) * 2 * 128
 
 
 def test_paged_mixed_reduced():
@@ -262,12 +280,21 @@ def test_int8_gqa_group_of_four_and_random():
 def test_paged_mixed_full_shape_sampled_units():
     """The paged workload's shape and launch configuration (64 sequences of
     4k-64k prompts, 32 KV heads, fused entry point, device-drawn inputs): three
-    heads of each of the two shortest sequences against the oracle, then every
-    unit for the properties that hold at any size."""
+    heads of each of the two shortest and the two longest sequences against the
+    oracle at every step -- the first step bulk-evicts the longest units from
+    ~65K slots to ~13K through the radix select and the hole fill -- then every
+    unit for the properties that hold at any size.  After the first step the
+    scores are single softmax weights (~1e-5), all within the near-tie rule's
+    absolute gap of each other, so the number of victims a unit-step may swap
+    under that rule is also capped."""
     w = WL.PAGED_MIXED
     lens = WL.prompt_lengths(w)
-    seqs = [int(x) for x in np.argsort(lens)[:2]]
+    order = np.argsort(lens)
+    seqs = [int(x) for x in order[:2]] + [int(x) for x in order[-2:]]
+    assert max(lens[b] for b in seqs) > 60000
     units = [(b, h) for b in seqs for h in (0, 13, w.n_kv_heads - 1)]
-    rep = P().run_parity(w, 24, lens=lens, units=units, device_inputs=True, stored_rows=False,
-                         read_every=4, properties=True)
-    assert rep.evictions > 0
+    rep = P().run_parity(w, 16, lens=lens, units=units, device_inputs=True, stored_rows=False,
+                         read_every=1, properties=True, max_swapped=8)
+    # the bulk first step alone evicts len + 1 - floor((len + 1) / 5) tokens per unit
+    bulk = sum(3 * (lens[b] + 1 - (lens[b] + 1) // 5) for b in seqs)
+    assert rep.evictions > bulk
