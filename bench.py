@@ -98,8 +98,8 @@ def summarize(args) -> None:
                        f"copy reads {cal:.1f} KiB on this counter -> scale x{factor:.4f}")
         hbm = sum(v * f * 1024 for v, f, _ in res.values())
         out.append(f"hbm_bytes_per_launch: {hbm:.6e}")
-        if line is not None and line.get("roofline"):
-            alg = line["roofline"]["algorithmic_bytes_per_launch"]
+        if line is not None and line.get("algorithmic_bytes_per_launch"):
+            alg = line["algorithmic_bytes_per_launch"]
             out += [f"workload: {line['config']['workload']}",
                     f"window_steps: {json.dumps(line['config']['window_steps'])}",
                     f"algorithmic_bytes_per_launch: {alg:.6e}",
@@ -730,6 +730,7 @@ def main():
                    "window_steps": [s0, s0 + K_steps], "mean_n_att": round(float(win.mean()), 1),
                    "entry_point": "h2o_step_compact", "parallelism": "single GPU"},
         "token_heads_per_s": round(value * Hkv, 1),
+        "algorithmic_bytes_per_launch": int(launch_b.mean()),
         "hbm_frac_step": round(step_bytes / elapsed / (HBM_PEAK_GBS * 1e9), 4),
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -94,7 +94,7 @@ def test_summary_records_window_and_traffic_scales_to_the_line(tmp_path, capsys,
     line = tmp_path / "line.json"
     line.write_text("noise\n" + json.dumps({"steps": 3, "config": {"workload": "paged_mixed_4k-64k_20pct",
                                                                     "layers": 1, "window_steps": [6, 9]},
-                                            "roofline": {"algorithmic_bytes_per_launch": 1000 * 1024}}) + "\n")
+                                            "algorithmic_bytes_per_launch": 1000 * 1024}) + "\n")
     args = types.SimpleNamespace(steps=None, layers=0, summarize_kernel="step_kernel", summarize_trace=None,
                                  summarize_counters=[str(fetch), str(write)], summarize_pmc=None,
                                  summarize_bench_line=str(line))
