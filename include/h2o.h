@@ -299,6 +299,26 @@ int h2o_snapkv_select(const h2o_config *cfg, const int32_t *prompt_len, int32_t 
                       int32_t keep, const float *prompt_q, const void *prompt_k, double *votes,
                       int32_t *kept, int32_t *kept_count, int32_t cap, void *stream);
 
+/* h2o_snapkv_select without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops that must not
+ * call hipMalloc, harnesses that forbid it.  Arguments, result and errors as
+ * h2o_snapkv_select.  Its scratch is a fixed array of 64 MiB (67108864 bytes)
+ * in the library, one copy per device, held until the process ends; a call
+ * whose scratch need is larger returns H2O_EINVAL with the size in the message
+ * before anything is enqueued.  The need is, in bytes, rounded up to 256 each:
+ * (votes == NULL ? 8 sum P_b Hq : 0) + 8 sum P_b Hq (pooled votes)
+ * + 4160 B Hkv G T (window q tiles and row statistics, T = the most 8-row
+ * tiles a window spans, ceil(w_b / 8) + 1 at most) + (G > 1 ?
+ * 4 B Hq ceil(max P_b / 128) * 4 : 0) (per-head kept bitmaps).  Calls on one
+ * device share that array: two calls whose work overlaps on the device (on
+ * different streams, with nothing ordering them) race and give undefined
+ * results.  Nothing is cleared between calls (no part of the scratch needs to
+ * start at zero).  Errors: H2O_EINVAL, H2O_EDEVICE; the message is
+ * h2o_last_error(NULL). */
+int h2o_snapkv_select_noalloc(const h2o_config *cfg, const int32_t *prompt_len, int32_t window, int32_t pool,
+                              int32_t keep, const float *prompt_q, const void *prompt_k, double *votes,
+                              int32_t *kept, int32_t *kept_count, int32_t cap, void *stream);
+
 /* Message of the last error on ctx, or, when ctx is NULL, of the last failed call
  * made without a context (h2o_init, h2o_prefill_scores, h2o_snapkv_select). */
 const char *h2o_last_error(const h2o_ctx *ctx);

@@ -24,7 +24,7 @@ _STATUS = {H2O_EINVAL: "H2O_EINVAL", H2O_ENOMEM: "H2O_ENOMEM", H2O_EDEVICE: "H2O
 # Every symbol include/h2o.h declares.
 SYMBOLS = ("h2o_workspace_size", "h2o_pool_pages", "h2o_init", "h2o_step", "h2o_compact", "h2o_step_compact", "h2o_read_indices",
            "h2o_info", "h2o_read_kv", "h2o_destroy", "h2o_prefill_scores", "h2o_snapkv_select",
-           "h2o_last_error")
+           "h2o_snapkv_select_noalloc", "h2o_last_error")
 
 
 class H2OConfig(C.Structure):
@@ -82,9 +82,11 @@ def load_library(path: str = LIB):
     lib.h2o_destroy.argtypes = [vp]
     lib.h2o_prefill_scores.restype = C.c_int
     lib.h2o_prefill_scores.argtypes = [C.POINTER(H2OConfig), i32p, vp, vp, vp, vp]
-    lib.h2o_snapkv_select.restype = C.c_int
-    lib.h2o_snapkv_select.argtypes = [C.POINTER(H2OConfig), i32p, C.c_int32, C.c_int32, C.c_int32, vp, vp, vp,
-                                      vp, vp, C.c_int32, vp]
+    for name in ("h2o_snapkv_select", "h2o_snapkv_select_noalloc"):
+        f = getattr(lib, name)
+        f.restype = C.c_int
+        f.argtypes = [C.POINTER(H2OConfig), i32p, C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, vp, vp, C.c_int32,
+                      vp]
     lib.h2o_last_error.restype = C.c_char_p
     lib.h2o_last_error.argtypes = [vp]
     _lib = lib

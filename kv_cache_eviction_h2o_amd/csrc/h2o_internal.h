@@ -248,6 +248,12 @@ hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st);
 hipError_t launch_step_mfma(const StepArgs& a, int max_n_att, hipStream_t st);  // h2o_mfma.hip
 hipError_t launch_colsum(const ColsumArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
 hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
+
+// Fixed scratch of h2o_snapkv_select_noalloc: a file-scope device array in
+// h2o_prefill.hip, one copy per device, kept until the process ends.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// This device's copy of that array (its address looked up once per device).
+hipError_t noalloc_scratch(char** ptr);  // h2o_prefill.hip
 hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);

@@ -600,7 +600,31 @@ __global__ void __launch_bounds__(kSNT) snapkv_union_kernel(const SnapArgs a)
     snap_finish(a, unit, P, Pp, bits, s_scan);
 }
 
+// Scratch of h2o_snapkv_select_noalloc, for callers that cannot allocate:
+// every device the library runs on holds its own copy of this array until the
+// process ends.  In host code its name is only a stand-in for the symbol; the
+// device address of the current device's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 }  // namespace
+
+hipError_t noalloc_scratch(char** ptr)
+{
+    static std::mutex mu;
+    static char* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {  // first call on this device, with it current
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        addr[dev] = static_cast<char*>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
 {

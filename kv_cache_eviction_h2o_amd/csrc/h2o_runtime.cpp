@@ -550,8 +550,19 @@ int colsum_run(const h2o_config* cfg, const int32_t* plen, const float* q, const
 
 // SnapKV's selection (h2o_snapkv_select): validate, per-head window votes by the
 // column-sum passes, then pooling and the per-unit selection.
-int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool, int keep, const float* q,
-               const void* k, double* votes, int32_t* kept, int32_t* count, int cap, void* stream)
+// SnapKV's selection, validated and sized: the launch arguments of both
+// passes and the scratch they need, laid out as [votes (when the caller passes
+// none)] [pooled votes] [column-sum passes] [per-head kept bitmaps (G > 1)].
+struct SnapPlan {
+    SnapArgs a{};
+    ColsumArgs ca{};
+    int maxP = 0, maxPc = 0;
+    size_t vown = 0, vbytes = 0, cbytes = 0, hbytes = 0;
+    size_t scratch_bytes() const { return vown + vbytes + cbytes + hbytes; }
+};
+
+int snapkv_plan(const h2o_config* cfg, const int32_t* plen, int window, int pool, int keep, const float* q,
+                const void* k, double* votes, int32_t* kept, int32_t* count, int cap, SnapPlan& pl)
 {
     if (!cfg || !plen) return fail(nullptr, H2O_EINVAL, "null config or prompt lengths");
     const int B = cfg->batch, Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads;
@@ -564,7 +575,8 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     if (keep < 0) return fail(nullptr, H2O_EINVAL, "keep must be >= 0");
     const int G = Hq / Hkv;
     std::vector<int32_t> lo(B);
-    SnapArgs a{};
+    SnapArgs& a = pl.a;
+    a = SnapArgs{};
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -572,8 +584,8 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     a.pool_r = pool / 2;
     a.keep = keep;
     a.cap = cap;
-    long long off = 0, total = 0;
-    int maxP = 0;
+    long long off = 0;
+    pl.maxP = 0;
     for (int b = 0; b < B; ++b) {
         const int P = plen[b];
         if (P < 1) return fail(nullptr, H2O_EINVAL, "prompt lengths must be >= 1");
@@ -586,45 +598,80 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
         a.seq_w[b] = w;
         a.seq_off[b] = off;
         off += P;
-        maxP = std::max(maxP, P);
+        pl.maxP = std::max(pl.maxP, P);
     }
-    total = off;
+    const long long total = off;
     if (!kept || !count) return fail(nullptr, H2O_EINVAL, "null kept or kept_count");
     if (misaligned(kept) || misaligned(count))
         return fail(nullptr, H2O_EINVAL, "kept and kept_count must be 16-byte aligned");
-    // scratch: [votes (when the caller passes none)] [pooled votes] [column-sum passes]
-    // [per-head kept bitmaps (G > 1)]
-    const size_t vbytes = align256((size_t)total * Hq * sizeof(double));
-    a.bits_words = ((maxP + 31) / 32 + 3) & ~3;  // whole 16-byte groups, so staged votes stay aligned
-    const size_t hbytes = G > 1 ? align256((size_t)B * Hq * a.bits_words * sizeof(unsigned)) : 0;
+    a.kept = kept;
+    a.count = count;
+    pl.vbytes = align256((size_t)total * Hq * sizeof(double));
+    a.bits_words = ((pl.maxP + 31) / 32 + 3) & ~3;  // whole 16-byte groups, so staged votes stay aligned
+    pl.hbytes = G > 1 ? align256((size_t)B * Hq * a.bits_words * sizeof(unsigned)) : 0;
+    pl.vown = votes ? 0 : pl.vbytes;
+    return colsum_setup(cfg, plen, lo.data(), q, k, 1, votes, pl.ca, pl.maxPc, pl.cbytes);
+}
+
+// Both passes of a planned selection, on scratch sp of pl.scratch_bytes().
+hipError_t snapkv_enqueue(SnapPlan& pl, double* votes, char* sp, hipStream_t st)
+{
+    double* vb = votes ? votes : reinterpret_cast<double*>(sp);
+    pl.ca.out = vb;  // the votes: the caller's buffer, else the scratch's first part
+    hipError_t e = colsum_launch(pl.ca, pl.maxPc, sp + pl.vown + pl.vbytes, st);
+    if (e != hipSuccess) return e;
+    pl.a.votes = vb;
+    pl.a.pooled = reinterpret_cast<double*>(sp + pl.vown);
+    pl.a.hbits = pl.a.G > 1 ? reinterpret_cast<unsigned*>(sp + pl.vown + pl.vbytes + pl.cbytes) : nullptr;
+    return launch_snapkv(pl.a, pl.maxP, st);
+}
+
+// SnapKV's selection (h2o_snapkv_select): validate, per-head window votes by the
+// column-sum passes, then pooling and the per-unit selection, on the grow-only
+// per-device scratch.
+int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool, int keep, const float* q,
+               const void* k, double* votes, int32_t* kept, int32_t* count, int cap, void* stream)
+{
+    SnapPlan pl;
+    int rc = snapkv_plan(cfg, plen, window, pool, keep, q, k, votes, kept, count, cap, pl);
+    if (rc != H2O_OK) return rc;
     std::string why;
     PromptScratch* ps = prompt_scratch(why);
     if (!ps) return fail(nullptr, H2O_EDEVICE, why);
     std::lock_guard<std::mutex> lk(ps->mu);
-    const size_t vown = votes ? 0 : vbytes;
-    ColsumArgs ca;
-    int maxPc = 0;
-    size_t cbytes = 0;
-    int rc = colsum_setup(cfg, plen, lo.data(), q, k, 1, votes, ca, maxPc, cbytes);
-    if (rc != H2O_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     char* sp = nullptr;
-    hipError_t e = scratch_take(*ps, vown + vbytes + cbytes + hbytes, st, &sp);
+    hipError_t e = scratch_take(*ps, pl.scratch_bytes(), st, &sp);
     if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV: scratch");
-    double* vb = votes ? votes : reinterpret_cast<double*>(sp);
-    ca.out = vb;  // the votes: the caller's buffer, else the scratch's first part
-    e = colsum_launch(ca, maxPc, sp + vown + vbytes, st);
-    if (e == hipSuccess) {
-        a.votes = vb;
-        a.pooled = reinterpret_cast<double*>(sp + vown);
-        a.hbits = G > 1 ? reinterpret_cast<unsigned*>(sp + vown + vbytes + cbytes) : nullptr;
-        a.kept = kept;
-        a.count = count;
-        e = launch_snapkv(a, maxP, st);
-    }
+    e = snapkv_enqueue(pl, votes, sp, st);
     const hipError_t e2 = scratch_done(*ps, st);
     if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV: launch");
     if (e2 != hipSuccess) return hip_fail(nullptr, e2, "SnapKV: scratch event");
+    return H2O_OK;
+}
+
+// The same selection on the library's fixed per-device scratch array: nothing
+// is allocated, and no event orders it against other calls.
+int snapkv_run_noalloc(const h2o_config* cfg, const int32_t* plen, int window, int pool, int keep,
+                       const float* q, const void* k, double* votes, int32_t* kept, int32_t* count, int cap,
+                       void* stream)
+{
+    SnapPlan pl;
+    int rc = snapkv_plan(cfg, plen, window, pool, keep, q, k, votes, kept, count, cap, pl);
+    if (rc != H2O_OK) return rc;
+    if (pl.scratch_bytes() > kNoAllocScratchBytes) {
+        char m[200];
+        std::snprintf(m, sizeof m,
+                      "SnapKV without allocation: the call needs %zu bytes of scratch, above the fixed %zu "
+                      "(pass votes, or fewer or shorter prompts)",
+                      pl.scratch_bytes(), (size_t)kNoAllocScratchBytes);
+        return fail(nullptr, H2O_EINVAL, m);
+    }
+    char* sp = nullptr;
+    hipError_t e = noalloc_scratch(&sp);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV without allocation: scratch address");
+    e = snapkv_enqueue(pl, votes, sp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV without allocation: launch");
     return H2O_OK;
 }
 
@@ -1141,6 +1188,14 @@ int h2o_snapkv_select(const h2o_config* cfg, const int32_t* prompt_len, int32_t 
 {
     return snapkv_run(cfg, prompt_len, window, pool, keep, prompt_q, prompt_k, votes, kept, kept_count, cap,
                       stream);
+}
+
+int h2o_snapkv_select_noalloc(const h2o_config* cfg, const int32_t* prompt_len, int32_t window, int32_t pool,
+                              int32_t keep, const float* prompt_q, const void* prompt_k, double* votes,
+                              int32_t* kept, int32_t* kept_count, int32_t cap, void* stream)
+{
+    return snapkv_run_noalloc(cfg, prompt_len, window, pool, keep, prompt_q, prompt_k, votes, kept, kept_count,
+                              cap, stream);
 }
 
 const char* h2o_last_error(const h2o_ctx* c)
