@@ -21,7 +21,8 @@ class OrcCfg(C.Structure):
     _fields_ = [("head_dim", C.c_int), ("group", C.c_int), ("scale", C.c_double),
                 ("selector", C.c_int), ("n_sink", C.c_int), ("budget_fixed", C.c_int),
                 ("hh_fixed", C.c_int), ("budget_num", C.c_int), ("budget_den", C.c_int),
-                ("rand_k", C.c_int), ("rand_r", C.c_int), ("seed", C.c_uint64)]
+                ("rand_k", C.c_int), ("rand_r", C.c_int), ("seed", C.c_uint64),
+                ("decay", C.c_double), ("score_f16", C.c_int)]
 
 
 def _bind(lib):
@@ -60,6 +61,12 @@ def _bind(lib):
                                   C.POINTER(_dp), C.POINTER(_dp), C.POINTER(_dp), C.c_int]
     lib.orc_philox4x64_10.argtypes = [C.POINTER(C.c_uint64), C.POINTER(C.c_uint64),
                                       C.POINTER(C.c_uint64)]
+    lib.orc_round_f16.restype = C.c_double
+    lib.orc_round_f16.argtypes = [C.c_double]
+    lib.orc_round_f16_many.restype = None
+    lib.orc_round_f16_many.argtypes = [_dp, _dp, C.c_int]
+    lib.orc_set_scores.restype = C.c_int
+    lib.orc_set_scores.argtypes = [C.c_void_p, _ip, _dp, C.c_int]
     return lib
 
 
@@ -84,9 +91,11 @@ def _f64(a) -> np.ndarray:
 
 
 def make_cfg(*, head_dim, group=1, scale=0.0, selector=ORC_H2O, n_sink=4, budget_fixed=0,
-             hh_fixed=0, budget_num=1, budget_den=5, rand_k=0, rand_r=0, seed=0) -> OrcCfg:
+             hh_fixed=0, budget_num=1, budget_den=5, rand_k=0, rand_r=0, seed=0, decay=1.0,
+             score_f16=False) -> OrcCfg:
     return OrcCfg(head_dim, group, scale, selector, n_sink, budget_fixed, hh_fixed,
-                  budget_num, budget_den, rand_k, rand_r, seed & 0xFFFFFFFFFFFFFFFF)
+                  budget_num, budget_den, rand_k, rand_r, seed & 0xFFFFFFFFFFFFFFFF, float(decay),
+                  1 if score_f16 else 0)
 
 
 def cfg_from_workload(w, **over) -> OrcCfg:
@@ -95,7 +104,8 @@ def cfg_from_workload(w, **over) -> OrcCfg:
     kw = dict(head_dim=w.head_dim, group=w.n_q_heads // w.n_kv_heads, selector=sel,
               n_sink=w.n_sink, budget_fixed=w.budget_fixed, hh_fixed=w.hh_fixed,
               budget_num=w.budget_num, budget_den=w.budget_den, rand_k=w.rand_k,
-              rand_r=w.rand_r, seed=w.recipe.seed)
+              rand_r=w.rand_r, seed=w.recipe.seed, decay=getattr(w, "score_decay", 1.0),
+              score_f16=getattr(w, "score_dtype", "f32") == "f16")
     kw.update(over)
     return make_cfg(**kw)
 
@@ -215,6 +225,15 @@ def philox4x64_10(ctr, key, lib=None):
     return [int(x) for x in o]
 
 
+def round_f16(x, lib=None) -> np.ndarray:
+    """orc_round_f16 elementwise: the nearest IEEE binary16 values, as float64."""
+    lib = lib or load()
+    a = _f64(x).ravel().copy()
+    out = np.empty_like(a)
+    lib.orc_round_f16_many(_p(a), _p(out), len(a))
+    return out.reshape(np.shape(x))
+
+
 class OracleError(RuntimeError):
     pass
 
@@ -294,6 +313,14 @@ class Unit:
         em = C.c_double()
         n = self.lib.orc_state(self.ptr, pos.ctypes.data_as(_ip), _p(sc), C.byref(em))
         return pos[:n].copy(), sc[:n].copy(), em.value
+
+    def set_scores(self, pos, scores):
+        """Adopt these scores for retained positions pos (lockstep with an
+        implementation whose stored scores are rounded differently)."""
+        p = np.ascontiguousarray(pos, dtype=np.int32)
+        sc = _f64(scores)
+        if self.lib.orc_set_scores(self.ptr, p.ctypes.data_as(_ip), _p(sc), len(p)) != 0:
+            raise OracleError("orc_set_scores: a position is not retained")
 
     def score_of(self, pos: int) -> float:
         return self.lib.orc_score_of(self.ptr, int(pos))

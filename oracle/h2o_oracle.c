@@ -20,6 +20,7 @@ struct orc_unit {
     int steps;            /* decode steps taken */
     double init_mass;     /* sum of initial scores */
     double evicted_mass;  /* sum of scores of evicted tokens */
+    double kept_expect;   /* retained score mass the update rule implies (decay < 1) */
     int *R;               /* scratch: retained positions */
     double *w;            /* scratch: one softmax row */
 };
@@ -62,11 +63,14 @@ orc_unit *orc_new(const orc_cfg *c, int b, int h, int prompt_len, int cap,
     } else {
         return NULL;
     }
+    if (!(c->decay == 0.0 || (c->decay > 0.0 && c->decay <= 1.0))) return NULL;
+    if (c->score_f16 != 0 && c->score_f16 != 1) return NULL;
     orc_unit *u = (orc_unit *)calloc(1, sizeof(*u));
     if (!u) return NULL;
     const size_t D = (size_t)c->head_dim;
     u->c = *c;
     if (u->c.scale == 0.0) u->c.scale = 1.0 / sqrt((double)c->head_dim);
+    if (u->c.decay == 0.0) u->c.decay = 1.0;
     u->b = b;
     u->h = h;
     u->prompt_len = prompt_len;
@@ -88,8 +92,10 @@ orc_unit *orc_new(const orc_cfg *c, int b, int h, int prompt_len, int cap,
     for (int p = 0; p < prompt_len; ++p) {
         u->live[p] = 1;
         u->score[p] = init_scores ? init_scores[p] : 0.0;
+        if (u->c.score_f16) u->score[p] = orc_round_f16(u->score[p]);
         u->init_mass += u->score[p];
     }
+    u->kept_expect = u->init_mass;
     u->len = prompt_len;
     return u;
 }
@@ -133,6 +139,12 @@ int orc_attend(orc_unit *u, const double *q, const double *k, const double *v,
     u->len = t + 1;
 
     const int n = retained(u, u->R);
+    const int scored = u->c.selector != ORC_RANDOM;  /* H2O and block eviction rank by scores */
+    /* moving sum: the retained scores decay once per step, before the step's
+     * weights are added (the new token starts from zero) */
+    const double lam = u->c.decay;
+    if (scored)
+        for (int i = 0; i < n; ++i) u->score[u->R[i]] *= lam;
     for (int g = 0; g < G; ++g) {
         const double *qg = q + (size_t)g * D;
         double m = -INFINITY;
@@ -163,9 +175,13 @@ int orc_attend(orc_unit *u, const double *q, const double *k, const double *v,
         }
         if (probs)
             for (int i = 0; i < n; ++i) probs[(size_t)g * n + i] = u->w[i];
-        if (u->c.selector != ORC_RANDOM)  /* H2O and block eviction rank by it */
+        if (scored)
             for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];
     }
+    /* binary16 storage: each updated score is rounded once */
+    if (scored && u->c.score_f16)
+        for (int i = 0; i < n; ++i) u->score[u->R[i]] = orc_round_f16(u->score[u->R[i]]);
+    u->kept_expect = lam * u->kept_expect + (double)G;  /* each query head's weights sum to one */
     u->steps += 1;
     return n;
 }
@@ -313,6 +329,7 @@ int orc_evict(orc_unit *u, const int32_t *victims, int e)
     for (int i = 0; i < e; ++i) {
         u->live[victims[i]] = 0;
         u->evicted_mass += u->score[victims[i]];
+        u->kept_expect -= u->score[victims[i]];
     }
     for (int i = 0; i < e; ++i)   /* a repeated victim shows up here */
         if (u->live[victims[i]]) return ORC_EARG;
@@ -335,9 +352,16 @@ int orc_check(const orc_unit *u)
         double kept = 0.0;
         for (int p = 0; p < u->len; ++p)
             if (u->live[p]) kept += u->score[p];
-        const double expect = u->init_mass + (double)u->c.group * u->steps;
-        if (fabs(kept + u->evicted_mass - expect) > 1e-9 * (expect > 1.0 ? expect : 1.0))
-            return ORC_ECHECK;
+        if (u->c.decay == 1.0 && !u->c.score_f16) {
+            /* exact sums: retained + evicted mass = initial mass + G per step */
+            const double expect = u->init_mass + (double)u->c.group * u->steps;
+            if (fabs(kept + u->evicted_mass - expect) > 1e-9 * (expect > 1.0 ? expect : 1.0))
+                return ORC_ECHECK;
+        } else if (!u->c.score_f16) {
+            /* moving sum: retained mass = decay x previous retained mass + G, less the victims */
+            const double ex = u->kept_expect;
+            if (fabs(kept - ex) > 1e-9 * (ex > 1.0 ? ex : 1.0)) return ORC_ECHECK;
+        }
     } else {
         for (int p = 0; p < u->prompt_len; ++p)
             if (!u->live[p]) return ORC_ECHECK;
@@ -371,6 +395,42 @@ int orc_state(const orc_unit *u, int32_t *pos, double *scores, double *evicted_m
         }
     if (evicted_mass) *evicted_mass = u->evicted_mass;
     return n;
+}
+
+/* binary16 (IEEE 754): 1 sign bit, 5 exponent bits, 10 fraction bits; normal
+ * values 2^-14 .. 65504, subnormals multiples of 2^-24.  A finite value whose
+ * leading bit is 2^e is a multiple of the quantum 2^(max(e, -14) - 10), so the
+ * nearest value is the quantum times x / quantum rounded to an integer (ties
+ * to even: rint in the default rounding mode).  65520, half a quantum above
+ * the largest value, and anything larger round to infinity. */
+double orc_round_f16(double x)
+{
+    if (x != x) return x;
+    const double a = fabs(x);
+    if (a >= 65520.0) return copysign(INFINITY, x);
+    if (a == 0.0) return x;
+    int E;
+    (void)frexp(a, &E);  /* a = m 2^E with m in [0.5, 1): the leading bit is 2^(E - 1) */
+    int e = E - 1;
+    if (e < -14) e = -14;
+    const double q = ldexp(1.0, e - 10);
+    return copysign(rint(a / q) * q, x);
+}
+
+void orc_round_f16_many(const double *in, double *out, int n)
+{
+    for (int i = 0; i < n; ++i) out[i] = orc_round_f16(in[i]);
+}
+
+int orc_set_scores(orc_unit *u, const int32_t *pos, const double *scores, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (pos[i] < 0 || pos[i] >= u->len || !u->live[pos[i]]) return ORC_EARG;
+    for (int i = 0; i < n; ++i) {
+        u->kept_expect += scores[i] - u->score[pos[i]];
+        u->score[pos[i]] = scores[i];
+    }
+    return ORC_OK;
 }
 
 double orc_score_of(const orc_unit *u, int pos)

@@ -47,6 +47,14 @@ typedef struct {
     int rand_k;        /* Random: generated tokens kept after an event (K) */
     int rand_r;        /* Random: buffer r; an event fires at K + r generated */
     uint64_t seed;     /* Random: Philox key word 0 */
+    /* Compressed score state (attention-sinks page sec. 6.2: fp32 score state
+     * costs 4 MB per 1M tokens; deployments quantise it to FP16/INT8 or replace
+     * the exact sum by a moving average): */
+    double decay;      /* 0 or 1: exact cumulative sum; else in (0, 1): every retained
+                          score is multiplied by decay once per step before that
+                          step's weights are added (a moving sum) */
+    int score_f16;     /* 1: every score is rounded to IEEE binary16 (nearest, ties to
+                          even) after each update, and initial scores on entry */
 } orc_cfg;
 
 typedef struct orc_unit orc_unit;
@@ -151,6 +159,18 @@ int orc_snapkv(const orc_cfg *c, int P, int w, int pool, int keep, const double 
 
 /* Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11). */
 void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
+
+/* x rounded to the nearest IEEE binary16 value (ties to even), returned as a
+ * double; magnitudes from 65520 on become infinite, as in IEEE rounding to
+ * nearest.  out[i] = that of in[i] for i < n. */
+double orc_round_f16(double x);
+void orc_round_f16_many(const double *in, double *out, int n);
+
+/* Replace the scores of retained positions pos[0..n) by scores[0..n) (the
+ * test's lockstep adoption of another implementation's stored, rounded
+ * scores, so that its next step starts from the same state).  Each position
+ * must be retained.  Returns ORC_OK or ORC_EARG. */
+int orc_set_scores(orc_unit *u, const int32_t *pos, const double *scores, int n);
 
 #ifdef __cplusplus
 }

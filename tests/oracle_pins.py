@@ -105,10 +105,17 @@ def pin_scores_and_selection_recomputed(lib):
     own selection (numpy.lexsort: score ascending, then position descending,
     over the candidates outside sinks and recent window).  The oracle must
     agree on the retained set, every score and the evicted mass, and the mass
-    must add up to G * steps."""
+    must add up to G * steps.  Then the same with a moving sum (decay 0.85:
+    every retained score is multiplied by the decay once per step before the
+    step's weights are added)."""
+    _recomputed(lib, 1.0)
+    _recomputed(lib, 0.85)
+
+
+def _recomputed(lib, lam):
     rng = np.random.default_rng(12)
     D, G, P, steps = 8, 2, 57, 41
-    cfg = O.make_cfg(head_dim=D, group=G, n_sink=4, budget_num=1, budget_den=5)
+    cfg = O.make_cfg(head_dim=D, group=G, n_sink=4, budget_num=1, budget_den=5, decay=lam)
     pk, pv = rng.standard_normal((P, D)), rng.standard_normal((P, D))
     pk[3] += 2.5  # a heavy direction on a few keys
     u = _unit(lib, cfg, pk, pv, P + steps)
@@ -126,7 +133,7 @@ def pin_scores_and_selection_recomputed(lib):
         R = sorted(live)
         rows = _softmax_rows(q, np.array([Kall[p] for p in R]), scale)
         for i, p in enumerate(R):
-            score[p] += rows[:, i].sum()
+            score[p] = lam * score[p] + rows[:, i].sum()
         out = u.attend(q, k, v)
         length = t + 1
         K, HH, W = _budget_20pct(length)
@@ -147,7 +154,8 @@ def pin_scores_and_selection_recomputed(lib):
         assert list(pos) == sorted(live)
         assert np.max(np.abs(sc - np.array([score[p] for p in pos]))) < 1e-12
         assert abs(em - evicted) < 1e-12
-        assert abs(sc.sum() + em - G * (s + 1)) < 1e-9, "retained + evicted mass != G*steps"
+        if lam == 1.0:
+            assert abs(sc.sum() + em - G * (s + 1)) < 1e-9, "retained + evicted mass != G*steps"
         assert len(pos) <= K
 
 
@@ -681,7 +689,86 @@ def pin_step_many_equals_sequential(lib):
                 f"{nthreads} threads: unit {i} state"
 
 
+# ------------------------------------------------- compressed score state
+def pin_f16_rounding_matches_numpy(lib):
+    """orc_round_f16 (binary16 storage of the scores) against numpy's float64
+    -> float16 conversion, a library routine that rounds once, to nearest with
+    ties to even: random values over the whole exponent range (subnormal,
+    normal, overflowing), exact midpoints between neighbouring binary16 values
+    and their fp64 neighbours, negative values, and the edges (0, the smallest
+    subnormal and half of it, 65504, 65520)."""
+    rng = np.random.default_rng(31)
+    x = np.ldexp(rng.random(20000) + 0.5, rng.integers(-30, 18, 20000))
+    h16 = np.arange(0, 0x7BFF, 7, dtype=np.uint16).view(np.float16)
+    lo, hi = h16.astype(np.float64), np.nextafter(h16, np.float16(np.inf)).astype(np.float64)
+    mids = (lo + hi) / 2  # exact: both have at most 11 significant bits
+    edges = np.array([0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25, 6.1e-5, 65504.0, 65519.99, 65520.0, 1e6])
+    allx = np.concatenate([x, -x[:200], mids, np.nextafter(mids, 0.0), np.nextafter(mids, np.inf), edges])
+    with np.errstate(over="ignore"):
+        want = allx.astype(np.float16).astype(np.float64)
+    got = O.round_f16(allx, lib=lib)
+    assert np.array_equal(got, want), f"{int(np.sum(got != want))} values rounded differently from numpy"
+    assert O.round_f16(np.array([np.nan]), lib=lib)[0] != O.round_f16(np.array([np.nan]), lib=lib)[0]
+
+
+def pin_decay_closed_forms(lib):
+    """Moving sum with decay lam, in closed form.  With zero queries every
+    retained token takes the weight 1/n_att from each of the G query heads, and
+    with no heavy hitters (4 sinks + window W, StreamingLLM) n_att = K + 1 at
+    every step; a token that has taken m steps' weights then holds the
+    geometric series G/(K+1) (1 - lam^m) / (1 - lam) (G m/(K+1) for lam = 1):
+    the sinks m = T after T steps, a generated token m = T - s after its
+    append at step s, and each step evicts the token leaving the window, the
+    prompt's at m = s + 1 and the generated ones at m = W + 1.  Binary16
+    storage (G = 1): every sink score equals numpy's float16 replay of
+    s <- f16(lam s + 1/(K+1)), and initial scores enter rounded.  Adopting
+    given scores (orc_set_scores) replaces them and refuses a position not
+    retained."""
+    rng = np.random.default_rng(33)
+    D, K, W, steps = 4, 12, 8, 30
+    P = K
+    pk, pv = rng.standard_normal((P, D)), rng.standard_normal((P, D))
+    for G, lam in ((2, 1.0), (2, 0.9), (3, 0.75)):
+        cfg = O.make_cfg(head_dim=D, group=G, n_sink=4, budget_fixed=K, hh_fixed=0, decay=lam)
+        u = _unit(lib, cfg, pk, pv, P + steps)
+
+        def geo(m):
+            return G / (K + 1) * (m if lam == 1.0 else (1 - lam ** m) / (1 - lam))
+        for s in range(steps):
+            u.step(np.zeros((G, D)), rng.standard_normal(D), rng.standard_normal(D))
+            T = s + 1
+            pos, sc, em = u.state()
+            ages = np.array([T - (p - P) if p >= P else T for p in pos])
+            ref = np.array([geo(a) for a in ages])
+            assert np.max(np.abs(sc - ref) / ref) < 1e-12, f"G={G} decay={lam} step {s}: scores"
+            em_ref = sum(geo(min(i + 1, W + 1)) for i in range(T))
+            assert abs(em - em_ref) <= 1e-12 * em_ref, f"G={G} decay={lam} step {s}: evicted mass"
+    lam = 0.9375
+    init = rng.random(P) * 3.0
+    cfg = O.make_cfg(head_dim=D, group=1, n_sink=4, budget_fixed=K, hh_fixed=0, decay=lam, score_f16=True)
+    u = _unit(lib, cfg, pk, pv, P + steps, init=init)
+    _, sc0, _ = u.state()
+    assert np.array_equal(sc0, init.astype(np.float16).astype(np.float64)), "initial scores not rounded"
+    sink = init[:4].astype(np.float16).astype(np.float64)
+    for s in range(steps):
+        u.step(np.zeros((1, D)), rng.standard_normal(D), rng.standard_normal(D))
+        sink = (lam * sink + 1.0 / (K + 1)).astype(np.float16).astype(np.float64)
+        _, sc, _ = u.state()
+        assert np.array_equal(sc[:4], sink), f"binary16 step {s}: sink scores"
+    pos, sc, _ = u.state()
+    u.set_scores(pos[:3], [0.5, 0.25, 0.125])
+    assert list(u.state()[1][:3]) == [0.5, 0.25, 0.125]
+    try:
+        u.set_scores([P + steps - W - 1], [1.0])  # evicted long ago
+    except O.OracleError:
+        pass
+    else:
+        raise AssertionError("set_scores accepted a position that is not retained")
+
+
 ALL_PINS = [
+    pin_f16_rounding_matches_numpy,
+    pin_decay_closed_forms,
     pin_step_many_equals_sequential,
     pin_attention_full_cache,
     pin_scores_and_selection_recomputed,

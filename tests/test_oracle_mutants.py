@@ -24,8 +24,8 @@ MUTANTS = {
     "value_rows_are_keys": ("const double *vj = u->V +", "const double *vj = u->K +"),
     "slot_index_for_position": ("const double *kj = u->K + (size_t)u->R[i] * D;",
                                 "const double *kj = u->K + (size_t)i * D;"),
-    "score_only_first_query_head": ("if (u->c.selector != ORC_RANDOM)  /* H2O and block eviction rank by it */\n",
-                                    "if (u->c.selector != ORC_RANDOM && g == 0)\n"),
+    "score_only_first_query_head": ("        if (scored)\n            for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];",
+                                    "        if (scored && g == 0)\n            for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];"),
     "score_missing_new_token": ("for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];",
                                 "for (int i = 0; i < n - 1; ++i) u->score[u->R[i]] += u->w[i];"),
     "tie_keeps_higher_position": ("    return (x->pos > y->pos) ? -1 : (x->pos < y->pos) ? 1 : 0;\n}\n\nstatic int cmp_key",
@@ -75,6 +75,19 @@ MUTANTS = {
     "block_select_own_scores_first_unit": ("memcpy(sc + (size_t)i * len, u[i]->score,", "memcpy(sc + (size_t)i * len, u[0]->score,"),
     "step_many_skips_units": ("for (int i = j->first; i < j->n; i += j->stride)",
                               "for (int i = j->first; i < j->n; i += 2 * j->stride)"),
+    "decay_not_applied": ("for (int i = 0; i < n; ++i) u->score[u->R[i]] *= lam;",
+                          "for (int i = 0; i < n; ++i) u->score[u->R[i]] *= 1.0;"),
+    "decay_per_query_head": ("            for (int i = 0; i < n; ++i) u->score[u->R[i]] += u->w[i];",
+                             "            for (int i = 0; i < n; ++i) u->score[u->R[i]] = lam * u->score[u->R[i]] + u->w[i];"),
+    "decay_squared": ("u->score[u->R[i]] *= lam;", "u->score[u->R[i]] *= lam * lam;"),
+    "f16_rounds_toward_zero": ("return copysign(rint(a / q) * q, x);", "return copysign(floor(a / q) * q, x);"),
+    "f16_ties_away_from_zero": ("return copysign(rint(a / q) * q, x);", "return copysign(round(a / q) * q, x);"),
+    "f16_no_subnormal_floor": ("    if (e < -14) e = -14;\n", ""),
+    "f16_overflow_saturates": ("if (a >= 65520.0) return copysign(INFINITY, x);", "if (a >= 65520.0) return copysign(65504.0, x);"),
+    "f16_eleven_fraction_bits": ("const double q = ldexp(1.0, e - 10);", "const double q = ldexp(1.0, e - 11);"),
+    "f16_scores_not_rounded": ("        for (int i = 0; i < n; ++i) u->score[u->R[i]] = orc_round_f16(u->score[u->R[i]]);",
+                               "        for (int i = 0; i < n; ++i) u->score[u->R[i]] = u->score[u->R[i]];"),
+    "f16_initial_scores_not_rounded": ("        if (u->c.score_f16) u->score[p] = orc_round_f16(u->score[p]);\n", ""),
     "random_largest_words": ("    if (x->key < y->key) return -1;\n    if (x->key > y->key) return 1;",
                              "    if (x->key > y->key) return -1;\n    if (x->key < y->key) return 1;"),
 }
