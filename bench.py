@@ -50,7 +50,8 @@ METRIC = "retained KV tokens processed/sec per decode step (attn+evict+compact);
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "kv_cache_eviction_h2o_amd", "csrc")
 # device sources of the decode-step kernels, and of the prompt calls' kernels
-STEP_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_kernels.hip", "h2o_mfma.hip", "h2o_block.hip")
+STEP_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_step.h", "h2o_step_f32.hip", "h2o_step_f64.hip",
+             "h2o_step_f16.hip", "h2o_kernels.hip", "h2o_mfma.hip", "h2o_block.hip")
 PROMPT_SRCS = ("h2o_internal.h", "h2o_device.h", "h2o_prefill.hip")
 PROMPT_KERNELS = ("colsum_", "snapkv_")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -212,6 +213,7 @@ WINDOWS = {
     WL.TINY_H2O.name: (64, 16, 128),
     WL.OPT_LAYER.name: (256, 16, 512),
     WL.OPT_LAYER_I8.name: (256, 16, 512),
+    WL.OPT_LAYER_F16.name: (256, 16, 512),
     WL.LLAMA_GQA.name: (256, 16, 16),
     WL.RANDOM_ATTN.name: (256, 16, 2176),
     WL.PAGED_MIXED.name: (60, 4, None),
@@ -670,7 +672,7 @@ def main():
     win = sched[:, s0:s0 + K_steps]  # n_att per sequence per timed step
     tokens = float(win.sum()) * layers
     value = tokens / elapsed
-    sbytes = 8 if w.score_dtype == "f64" else 4
+    sbytes = {"f64": 8, "f16": 2}.get(w.score_dtype, 4)
     if w.selector == "random":
         sbytes = 0
     kv_elem = 2 if w.recipe.kv_dtype == "bf16" else 4
@@ -726,6 +728,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "kv_dtype": w.kv_dtype, "score_dtype": w.score_dtype if sbytes else None,
+                   "score_decay": w.score_decay if sbytes else None,
                    "layers": layers, "prompt_len": lens[0] if len(set(lens)) == 1 else "mixed",
                    "window_steps": [s0, s0 + K_steps], "mean_n_att": round(float(win.mean()), 1),
                    "entry_point": "h2o_step_compact", "parallelism": "single GPU"},

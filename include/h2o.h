@@ -72,6 +72,20 @@
  *     one fp32 scale per (token, KV head) row: scale = max |x| / 127,
  *     code = rint(x / scale) in [-127, 127], all in fp32 (a zero row has
  *     scale 0).  Attention, also over the new token, uses code * scale.
+ *   - Compressed score state ("Attention Sinks and KV cache eviction",
+ *     sec. 6.2: the fp32 per-token score state costs 4 MB per 1M tokens, and
+ *     deployments quantise it to FP16/INT8 or replace the exact sum by a
+ *     moving average).  score_decay lam in (0, 1) turns the cumulative sum
+ *     into a moving sum: at every step each retained score becomes
+ *     lam * score + (the step's weights summed over the group), evaluated as
+ *     one fused multiply-add in the score's precision (fp32 for H2O_F16), the
+ *     new token starting from zero; lam = 1 is the exact sum.  The moving sum
+ *     stays below G / (1 - lam).  score_dtype H2O_F16 stores each score as
+ *     IEEE binary16, rounded to nearest (ties to even) after every update and
+ *     on entry (initial scores), so a score past 65504 becomes infinite and is
+ *     never evicted; with lam <= 1 - G / 65504 that cannot happen.  The
+ *     selection ranks the stored values (equal values: the lower position is
+ *     kept), and evicted_mass sums them in fp64.
  *   - Errors: every call returns an h2o_status.  Arguments are validated
  *     before anything is enqueued; on error nothing is enqueued and the
  *     context is unchanged (H2O_EDEVICE aside).  h2o_last_error() gives the
@@ -124,7 +138,7 @@ typedef enum {
  * candidate page.  Slot capacity: max(P, K_max + 16 * ceil(n_sink / 16) + 15) + 1
  * tokens, at most 5120 pages per sequence; at most 1024 KV heads. */
 enum { H2O_SEL_H2O = 0, H2O_SEL_RANDOM = 1, H2O_SEL_BLOCK = 2 };
-enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F64 = 2, H2O_I8 = 3 };
+enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F64 = 2, H2O_I8 = 3, H2O_F16 = 4 };
 
 typedef struct {
     int32_t batch;         /* B sequences */
@@ -132,7 +146,8 @@ typedef struct {
     int32_t n_kv_heads;    /* Hkv; Hq must be a multiple */
     int32_t head_dim;      /* D */
     int32_t kv_dtype;      /* H2O_BF16, H2O_F32, or H2O_I8 (bf16 inputs stored as int8 rows) */
-    int32_t score_dtype;   /* H2O, block: H2O_F32 or H2O_F64 cumulative scores */
+    int32_t score_dtype;   /* H2O, block: H2O_F32 or H2O_F64 cumulative scores; H2O also
+                              H2O_F16 (compressed state, see score_decay) */
     float scale;           /* logit scale; 0 -> 1/sqrt(D) */
     int32_t selector;      /* H2O_SEL_H2O, H2O_SEL_RANDOM or H2O_SEL_BLOCK (needs page_size 16) */
     int32_t n_sink;        /* H2O: positions 0..n_sink-1 are never evicted (4 on the pages) */
@@ -154,6 +169,8 @@ typedef struct {
                               alone.  Lets an allocator that owns device memory (a
                               framework's caching allocator) hold the cache. */
     uint64_t workspace_bytes;  /* size of workspace (ignored when it is NULL) */
+    float score_decay;     /* H2O, block: 0 or 1 = the exact cumulative sum; else in (0, 1):
+                              a moving sum, see the compressed-state note above */
 } h2o_config;
 
 /* Device bytes the context of (cfg, prompt_len) keeps for its state: the K/V

@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libh2o.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["h2o_kernels.hip", "h2o_mfma.hip", "h2o_prefill.hip", "h2o_block.hip", "h2o_runtime.cpp"]
+SOURCES = ["h2o_step_f32.hip", "h2o_step_f64.hip", "h2o_step_f16.hip", "h2o_kernels.hip", "h2o_mfma.hip",
+           "h2o_prefill.hip", "h2o_block.hip", "h2o_runtime.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -633,11 +633,16 @@ __device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n
 
 
 // ------------------------------------------------------------ step tail
+// Scores are compared (arg-min, radix keys) in MinT: binary16 scores widen
+// exactly to fp32, the others compare as stored.
+template <typename ST>
+using MinT = std::conditional_t<sizeof(ST) == 2, float, ST>;
+
 // Shared memory of the tail.
 template <typename ST, int NW>
 struct TailSmem {
     ST new_score;
-    ST bs[NW];
+    MinT<ST> bs[NW];
     int bp[NW], bj[NW];
     double dsum[NW];
     int isum[NW];
@@ -649,7 +654,10 @@ struct TailSmem {
 // of every query head of the group are known (all threads call it):
 //   H2O: p = 2^(s - M) / L per slot (logits in the log2 domain at
 //        logit[g * lstride + j], the new token at j = n), summed over the
-//        group, added to the cumulative score; with one token to go, the
+//        group, added to the cumulative score after the score is multiplied
+//        by the decay (a moving sum; decay 1 is the exact sum), as one fused
+//        multiply-add in the score's precision (fp32 for binary16 scores,
+//        rounded to nearest once when stored); with one token to go, the
 //        arg-min over the candidates (score ascending, position descending)
 //        names the victim, which the new token replaces in place when fused.
 //   bulk (e > 1, Random Attention events): radix select of the e smallest
@@ -659,8 +667,10 @@ struct TailSmem {
 // token's row at slot index si (the writer picks its threads); emass0: the
 // unit's evicted mass before the step.
 // Definitions: "Attention Sinks and KV cache eviction" sec. 4.2 (cumulative
-// score; sinks, heavy hitters and recent window), "H2O: Heavy-Hitter Oracle"
-// (greedy eviction under budget K), "Random Attention" (method).
+// score; sinks, heavy hitters and recent window) and sec. 6.2 (compressed
+// score state: FP16 storage, a moving average instead of the exact sum),
+// "H2O: Heavy-Hitter Oracle" (greedy eviction under budget K), "Random
+// Attention" (method).
 template <int NT, int G, int PF, typename ST, bool PAGED, typename KV, typename WriteNew>
 __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, TailSmem<ST, NT / 64>& sm,
                                  int unit, int b, int h, int P, int t, int n, int e, bool inplace_new,
@@ -683,16 +693,21 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
 
     // ---- phase 2 (H2O): accumulate scores; arg-min when one token goes ---
     if (h2o) {
-        ST bs = (ST)INFINITY;
+        using MT = MinT<ST>;
+        const float lam = a.sc.decay;
+        MT bs = (MT)INFINITY;
         int bp = -1, bj = -1;
-        // slot j: add its weights of this step (summed over the group) to its
-        // score; the new token (j == n) starts from zero
+        // slot j: decay its score and add its weights of this step (summed over
+        // the group); the new token (j == n) starts from zero.  With decay 1 the
+        // fused multiply-add is the plain sum, rounded once.
         auto visit = [&](int j, ST old, int pos) {
             float p = 0.f;
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 p += fast_exp2(logit[(size_t)g * lstride + j] - Mg[g]) * invLg[g];
-            const ST nw = old + (ST)p;
+            ST nw;
+            if constexpr (sizeof(ST) == 8) nw = fma((double)lam, old, (double)p);
+            else nw = (ST)fmaf(lam, (float)old, p);
             if (j < n) {
                 scp[sidx(j)] = nw;
             } else {
@@ -703,7 +718,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
                     psp[si] = t;
                 }
             }
-            if (e == 1 && pos >= lo_c && pos < hi_c) take_better(bs, bp, bj, nw, pos, j);
+            if (e == 1 && pos >= lo_c && pos < hi_c) take_better(bs, bp, bj, (MT)nw, pos, j);
         };
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
@@ -729,12 +744,12 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             // lanes 0..NW-1 of every wave take one wave's best; three DPP
             // stages within 8 lanes leave the workgroup's best in lane 0
             static_assert(NW <= 8, "cross-wave arg-min covers up to 8 waves");
-            ST vs = lane < NW ? sm.bs[lane] : (ST)INFINITY;
+            MT vs = lane < NW ? sm.bs[lane] : (MT)INFINITY;
             int vp = lane < NW ? sm.bp[lane] : -1, vjj = lane < NW ? sm.bj[lane] : -1;
             argmin_step<0xB1>(vs, vp, vjj);
             argmin_step<0x4E>(vs, vp, vjj);
             argmin_step<0x141>(vs, vp, vjj);
-            if constexpr (sizeof(ST) == 4) {
+            if constexpr (sizeof(MT) == 4) {
                 vs = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vs)));
             } else {
                 const long long u = __double_as_longlong(vs);
@@ -795,7 +810,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             const size_t si = sidx(j);
             const int pos = psp[si];
             if (pos < lo_c || pos >= hi_c) return false;
-            if constexpr (sizeof(ST) == 4) {
+            if constexpr (sizeof(ST) <= 4) {
                 wk[2] = 0;
                 wk[1] = ord32((float)scp[si]);
             } else {
@@ -806,7 +821,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             wk[0] = ~(unsigned)pos;
             return true;
         };
-        d0 = sizeof(ST) == 4 ? 4 : 0;
+        d0 = sizeof(ST) <= 4 ? 4 : 0;
         radix_select<NT>(key_of, n_att, e, d0, sm.rad);
         for (int j = tid; j < n_att; j += NT) {
             unsigned wk[3];

@@ -74,7 +74,8 @@ struct Geometry {
     int maxp;       // paged: block-table row length (pages per sequence)
     int kv_bf16;    // 1 = bf16 rows (inputs and storage), 0 = fp32 rows
     int kv_i8;      // 1 = bf16 inputs stored as int8 rows of 128 with one fp32 scale per row
-    int score_f64;  // 1 = fp64 cumulative scores, 0 = fp32
+    int score_f64;  // 1 = fp64 cumulative scores
+    int score_f16;  // 1 = IEEE binary16 cumulative scores (H2O only); neither: fp32
     int kv_tiles;   // 1 = K/V in matrix-instruction operand order (bf16, head_dim 128,
                     //     contiguous, cap a multiple of 32, GQA group of 4 or 8)
 };
@@ -105,6 +106,7 @@ struct Sched {
     int n_sink, budget_fixed, hh_fixed, budget_num, budget_den;
     int rand_k, rand_r;
     unsigned long long seed;
+    float decay;  // moving-sum decay of the scores per step (1 = exact cumulative sum)
 };
 
 // Budget K_t, heavy hitters HH_t and recent window W_t at length len = t + 1.
@@ -187,6 +189,7 @@ struct LoadArgs {
     const void* pk;
     const void* pv;
     const double* init_scores;
+    int max_prompt;  // longest prompt (the grid's x extent covers its rows)
 };
 
 struct GatherArgs {
@@ -246,6 +249,11 @@ struct RowGatherArgs {
 // Launchers (h2o_kernels.hip unless noted).  Each returns the launch's hipError_t.
 hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st);
 hipError_t launch_step_mfma(const StepArgs& a, int max_n_att, hipStream_t st);  // h2o_mfma.hip
+// The FMA step kernel for one cumulative-score type (h2o_step_f32/f64/f16.hip);
+// llds: logits in LDS (dyn bytes of dynamic LDS), else in State::lscr.
+hipError_t launch_step_f32(const StepArgs& a, bool llds, size_t dyn, hipStream_t st);
+hipError_t launch_step_f64(const StepArgs& a, bool llds, size_t dyn, hipStream_t st);
+hipError_t launch_step_f16(const StepArgs& a, bool llds, size_t dyn, hipStream_t st);
 hipError_t launch_colsum(const ColsumArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
 hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
 

@@ -400,7 +400,9 @@ hipError_t launch_step_mfma(const StepArgs& a0, int max_n_att, hipStream_t st)
         if (llds) dyn = (size_t)g.G * a.lds_n * 4;
         else if (a.s.lscr == nullptr) return hipErrorInvalidValue;
     }
-    return g.score_f64 ? launch_mfma_s<double>(a, llds, dyn, st) : launch_mfma_s<float>(a, llds, dyn, st);
+    if (g.score_f64) return launch_mfma_s<double>(a, llds, dyn, st);
+    if (g.score_f16) return launch_mfma_s<_Float16>(a, llds, dyn, st);
+    return launch_mfma_s<float>(a, llds, dyn, st);
 }
 
 }  // namespace h2o

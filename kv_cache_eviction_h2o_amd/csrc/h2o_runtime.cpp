@@ -105,6 +105,7 @@ Sched make_sched(const h2o_config& c)
     s.rand_k = c.rand_k;
     s.rand_r = c.rand_r;
     s.seed = (unsigned long long)c.seed;
+    s.decay = c.score_decay > 0.f ? c.score_decay : 1.0f;
     return s;
 }
 
@@ -156,8 +157,12 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
     if (c->selector == H2O_SEL_BLOCK && c->n_kv_heads > 1024)
         return bad("block eviction supports at most 1024 KV heads");
     if (c->selector == H2O_SEL_H2O || c->selector == H2O_SEL_BLOCK) {
-        if (c->score_dtype != H2O_F32 && c->score_dtype != H2O_F64)
-            return bad("score_dtype must be f32 or f64");
+        if (c->score_dtype == H2O_F16 && c->selector != H2O_SEL_H2O)
+            return bad("binary16 scores (score_dtype f16) need the H2O selector");
+        if (c->score_dtype != H2O_F32 && c->score_dtype != H2O_F64 && c->score_dtype != H2O_F16)
+            return bad("score_dtype must be f32, f64 or f16");
+        if (!(c->score_decay >= 0.f && c->score_decay <= 1.f))
+            return bad("score_decay must be 0 (exact sum) or in (0, 1]");
         if (c->n_sink < 0) return bad("n_sink must be >= 0");
         if (c->budget_fixed > 0) {
             if (c->hh_fixed < 0 || c->budget_fixed - c->n_sink - c->hh_fixed < 0)
@@ -702,6 +707,7 @@ int setup_ctx(h2o_ctx* c, const h2o_config* cfg, const int32_t* prompt_len, size
     g.kv_bf16 = cfg->kv_dtype == H2O_BF16;
     g.kv_i8 = cfg->kv_dtype == H2O_I8;
     g.score_f64 = scored(cfg->selector) && cfg->score_dtype == H2O_F64;
+    g.score_f16 = scored(cfg->selector) && cfg->score_dtype == H2O_F16;
     // GQA groups of 4 or 8 over bf16 rows of 128 run on the matrix cores, with
     // K / V stored in operand order in whole 32-slot tiles
     g.kv_tiles = g.kv_bf16 && g.D == 128 && !g.paged && (g.G == 4 || g.G == 8);
@@ -749,7 +755,7 @@ int alloc_state(h2o_ctx* c, size_t slots_total, int32_t** t0, int64_t** poff)
     const h2o_config* cfg = &c->cfg;
     const int B = g.B;
     const size_t units = (size_t)B * g.Hkv;
-    const size_t sw = g.score_f64 ? 8 : 4;
+    const size_t sw = g.score_f64 ? 8 : (g.score_f16 ? 2 : 4);
     const size_t row_bytes = g.kv_i8 ? kRowBytesI8 : kRowBytes;
     if ((rc = dalloc(c, &s.kc, slots_total * row_bytes, "alloc K cache")) ||
         (rc = dalloc(c, &s.vc, slots_total * row_bytes, "alloc V cache")) ||

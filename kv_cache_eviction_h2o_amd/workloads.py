@@ -23,13 +23,14 @@ class Workload:
     n_kv_heads: int
     head_dim: int
     kv_dtype: str                 # storage: "f32" | "bf16" | "i8" (inputs in recipe.kv_dtype)
-    score_dtype: str              # "f32" | "f64" (unused by the Random selector)
+    score_dtype: str              # "f32" | "f64" | "f16" (unused by the Random selector)
     selector: str                 # "h2o" | "random" | "block" (paged only)
     n_sink: int = 4
     budget_fixed: int = 0         # > 0: fixed budget K
     hh_fixed: int = 0             #        with this many heavy hitters
     budget_num: int = 1           # else K_t = floor(len * num / den)
     budget_den: int = 5
+    score_decay: float = 1.0      # 1 = exact cumulative sum; < 1 = moving sum (decay per step)
     rand_k: int = 0
     rand_r: int = 0
     prompt_len: int = 0           # > 0: every sequence has this prompt
@@ -89,7 +90,13 @@ OPT_LAYER_I8 = OPT_LAYER.scaled(name="opt6.7b_layer_20pct_int8", kv_dtype="i8")
 # those with the fewest heavy-hitter tokens over the sequence's KV heads first
 # ("Attention Sinks and KV cache eviction", section 5).
 PAGED_BLOCK = PAGED_MIXED.scaled(name="paged_mixed_4k-64k_20pct_block", selector="block")
-VARIANTS = (OPT_LAYER_I8, PAGED_BLOCK)
+# Compressed score state ("Attention Sinks and KV cache eviction", section 6.2):
+# the OPT layer with its cumulative scores stored as IEEE binary16 and the exact
+# sum replaced by a moving sum that decays by 1 - 2^-8 per step (an effective
+# memory of ~256 steps, a quarter of the trace; binary16 and this decay keep the
+# largest score below G / (1 - decay) = 256).
+OPT_LAYER_F16 = OPT_LAYER.scaled(name="opt6.7b_layer_20pct_f16", score_dtype="f16", score_decay=1.0 - 2.0 ** -8)
+VARIANTS = (OPT_LAYER_I8, PAGED_BLOCK, OPT_LAYER_F16)
 
 
 def prompt_lengths(w: Workload):

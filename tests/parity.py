@@ -10,6 +10,15 @@ Acceptance (per step, per checked (sequence, KV head) unit):
   Random Attention has no exemption: its sets must be identical;
 * cumulative scores of the retained tokens: |gpu - oracle| <= 2e-3 * oracle + 1e-9;
 * evicted mass: |gpu - oracle| <= 2e-3 * max(1, oracle);
+* binary16 scores (the compressed state): the GPU rounds its fp32 update and
+  the oracle its fp64 update, so a stored value may sit one binary16 unit in
+  the last place (ulp) away: every score must be within one ulp of the
+  oracle's, a different victim set is accepted when every token in the
+  symmetric difference lies within two ulps (plus the gap above) of the
+  oracle's e-th smallest score, and after each checked step the oracle adopts
+  the GPU's stored scores (lockstep, as for adopted victims) so that the next
+  step starts from the same state -- the check is then of each step's update
+  and selection, which is what a rounded state can be held to;
 * stored rows (after the last step): every retained position's K and V row as
   the library holds it equals, bit for bit, the generator's row for that
   position -- its bf16 / fp32 bits, or for int8 storage the oracle's
@@ -30,6 +39,14 @@ from kv_cache_eviction_h2o_amd import workloads as WL
 OUT_TOL = 2e-3
 SCORE_TOL = 2e-3
 GAP = 1e-5
+
+
+def ulp16(x) -> np.ndarray:
+    """Spacing of IEEE binary16 values at |x|: 2^(e - 10) for a leading bit 2^e
+    (e >= -14), 2^-24 below (subnormals)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return np.ldexp(1.0, (e - 10).astype(np.int64))
 
 
 def say(*a):
@@ -141,6 +158,8 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
     win = 256
     gen_k, gen_v = [], []  # generated rows of the decode steps, for the stored-row check
     check_steps = set(check_steps)
+    f16 = w.score_dtype == "f16" and w.selector == "h2o"
+    assert not f16 or read_every == 1, "binary16 scores are checked in lockstep: every step"
     nthr = _oracle_threads(len(units))
     pool = ThreadPoolExecutor(nthr)
     ulist = [orc[bh] for bh in units]
@@ -191,8 +210,9 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
                 gvic = sorted(set(pre_pos.tolist()) - gset)
                 if sorted(vic.tolist()) != gvic:
                     diff = set(vic.tolist()) ^ set(gvic)
+                    gap = GAP + (2 * float(ulp16(tau)) if f16 else 0.0)
                     ok = (w.selector == "h2o" and len(gvic) == len(vic)
-                          and all(abs(u.score_of(p) - tau) < GAP for p in diff))
+                          and all(abs(u.score_of(p) - tau) < gap for p in diff))
                     assert ok, (f"step {s} unit {(b, h)}: victims differ: oracle-only "
                                 f"{sorted(set(vic.tolist()) - set(gvic))[:8]} gpu-only "
                                 f"{sorted(set(gvic) - set(vic.tolist()))[:8]} tau={tau}")
@@ -210,12 +230,19 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
                 if check_scores and w.selector == "h2o":
                     g_sc = sc[b, h, :n]
                     serr = np.abs(g_sc - o_sc)
+                    if f16:
+                        assert np.all(serr <= ulp16(o_sc) * (1 + 1e-12)), \
+                            f"step {s} unit {(b, h)}: binary16 scores more than one ulp apart"
+                        assert np.array_equal(g_sc, g_sc.astype(np.float16).astype(np.float64)), \
+                            f"step {s} unit {(b, h)}: stored scores are not binary16 values"
                     assert np.all(serr <= SCORE_TOL * np.abs(o_sc) + 1e-9), \
                         f"step {s} unit {(b, h)}: score err {np.max(serr / (np.abs(o_sc) + 1e-9)):.3g}"
                     rep.max_score_err = max(rep.max_score_err,
                                             float(np.max(serr / np.maximum(np.abs(o_sc), 1e-30))))
                     assert abs(em[b, h] - o_em) <= SCORE_TOL * max(1.0, o_em), \
                         f"step {s} unit {(b, h)}: evicted mass {em[b, h]} vs {o_em}"
+                if f16:  # lockstep: the next step starts from the GPU's stored scores
+                    u.set_scores(gpos, sc[b, h, :n])
             rep.steps += 1
     pool.shutdown()
     if stored_rows:

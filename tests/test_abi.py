@@ -87,6 +87,10 @@ GOOD = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kv_dtype="bf16", s
     (dict(selector="block", page_size=16, max_pages=64, n_q_heads=2048, n_kv_heads=2048), "1024 KV heads"),
     (dict(selector="block", page_size=16, max_pages=64, hh_fixed=61), "hh_fixed"),
     (dict(selector="block", page_size=16, max_pages=64, score_dtype="bf16"), "score_dtype"),
+    (dict(selector="block", page_size=16, max_pages=64, score_dtype="f16"), "H2O selector"),
+    (dict(score_dtype="i8"), "score_dtype"),
+    (dict(score_decay=1.5), "score_decay"),
+    (dict(score_decay=-0.5), "score_decay"),
     (dict(selector="block", page_size=16, max_pages=64, budget_fixed=0, budget_num=1, budget_den=5,
           max_len=500000), "5120 pages"),
 ])

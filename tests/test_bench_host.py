@@ -66,6 +66,10 @@ def test_default_window_is_the_paged_workload_after_its_bulk_step():
     assert bench.bench_window(WL.OPT_LAYER, 20, 5) == (20, 5, 512)
     # contiguous traces keep the window inside them
     assert bench.bench_window(WL.OPT_LAYER, 600, 16) == (600, 16, 424)
+    # every workload bench.py accepts has a default window
+    for wl in WL.ALL + WL.VARIANTS:
+        K, W, s0 = bench.bench_window(wl)
+        assert K >= 1 and s0 >= W
 
 
 def bench_args(argv):

@@ -135,3 +135,12 @@ def test_block_full_shape_sampled_sequences():
     P().block_properties(w, rep.cache, lens, steps, cap=cap)
     rep.cache.close()
     assert rep.evictions > 0
+
+
+def test_block_moving_sum_scores():
+    """Block eviction ranks pages by heavy hitters of moving-sum scores (decay
+    0.99 per step, fp32 and fp64): the same rule on the decayed scores."""
+    for sd in ("f32", "f64"):
+        w = PB.scaled(batch=3, n_q_heads=4, n_kv_heads=4, score_dtype=sd, score_decay=0.99)
+        rep = _run(w, 60, [300, 517, 1100], fused=(sd == "f32"))
+        assert rep.evictions > 0

@@ -298,3 +298,48 @@ def test_paged_mixed_full_shape_sampled_units():
     # the bulk first step alone evicts len + 1 - floor((len + 1) / 5) tokens per unit
     bulk = sum(3 * (lens[b] + 1 - (lens[b] + 1) // 5) for b in seqs)
     assert rep.evictions > bulk
+
+
+# ------------------------------------- compressed score state (moving sum, binary16)
+# "Attention Sinks and KV cache eviction", section 6.2: the per-token score state
+# is quantised to FP16, or the exact sum replaced by a moving average.  Binary16
+# runs are checked in lockstep at every step (parity.py).
+@pytest.mark.parametrize("fused", [True, False], ids=["step_compact", "step+compact"])
+def test_f16_moving_sum_opt_layer_reduced_full_trace(fused):
+    w = WL.OPT_LAYER_F16.scaled(batch=2, n_q_heads=8, n_kv_heads=8)
+    assert w.score_dtype == "f16" and 0 < w.score_decay < 1
+    rep = P().run_parity(w, w.decode_steps if fused else 200, fused=fused)
+    assert rep.evictions > 0
+
+
+def test_f16_exact_sum_paged_bulk_first_step():
+    # decay 1 (the exact sum, rounded to binary16 each step), paged, bulk first step
+    w = WL.PAGED_MIXED.scaled(batch=3, n_q_heads=4, n_kv_heads=4, score_dtype="f16")
+    rep = P().run_parity(w, 40, lens=[300, 517, 1500])
+    assert rep.evictions > 0
+
+
+def test_f16_gqa_matrix_core_path():
+    # the matrix-core kernel (G = 8) with binary16 scores: bulk eviction at the
+    # first step through the radix select on widened binary16 keys, then one a step
+    w = WL.LLAMA_GQA.scaled(batch=2, prompt_len=1100, score_dtype="f16", score_decay=0.998)
+    rep = P().run_parity(w, 96)
+    assert rep.evictions >= 2 * 8 * (73 + 95)
+
+
+def test_f16_int8_rows_and_initial_scores():
+    w = WL.OPT_LAYER_I8.scaled(batch=2, n_q_heads=4, n_kv_heads=4, score_dtype="f16", score_decay=0.99)
+    P().run_parity(w, 60, lens=[400, 257])
+    wt = WL.TINY_H2O.scaled(batch=2, score_dtype="f16", score_decay=0.995)
+    lens = [100, 90]
+    init = np.random.default_rng(7).random((sum(lens), wt.n_kv_heads)) * 0.5
+    P().run_parity(wt, 40, lens=lens, init_scores=init)
+
+
+@pytest.mark.parametrize("score_dtype", ["f32", "f64"])
+def test_moving_sum_fp32_fp64_scores(score_dtype):
+    w = WL.OPT_LAYER.scaled(batch=2, n_q_heads=8, n_kv_heads=4, score_dtype=score_dtype, score_decay=0.99)
+    rep = P().run_parity(w, 300, lens=[700, 333])
+    assert rep.evictions > 0
+    wg = WL.LLAMA_GQA.scaled(batch=1, prompt_len=1100, score_dtype=score_dtype, score_decay=0.995)
+    P().run_parity(wg, 60)
