@@ -444,6 +444,99 @@ __device__ inline bool key_le(const unsigned (&w)[3], const RadixSmem& rs)
     return a0 <= rs.p[0];
 }
 
+// Slots j in [lo, hi), thread tid taking lo + tid, lo + tid + NT, ..., fetched
+// UNR at a time: fetch(j) issues slot j's loads and returns them unconsumed,
+// then body(j, fetched) runs for each, so a thread keeps UNR slots' loads in
+// flight instead of waiting on one dependent load per slot.  Past hi the
+// fetch repeats an in-range slot and the body is skipped.
+template <int NT, int UNR, typename Fetch, typename Body>
+__device__ inline void for_slots_batched(int lo, int hi, Fetch fetch, Body body)
+{
+    using Raw = decltype(fetch(lo));
+    for (int j0 = lo + (int)threadIdx.x; j0 < hi; j0 += NT * UNR) {
+        Raw r[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int j = j0 + u * NT;
+            r[u] = fetch(j < hi ? j : j0);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int j = j0 + u * NT;
+            if (j < hi) body(j, r[u]);
+        }
+    }
+}
+
+// radix_select with the candidates' data fetched UNR slots at a time:
+// src.fetch(j) returns slot j's raw data, src.key(raw, w) its 96-bit key
+// (false: not a candidate).  Same contract and result as radix_select.
+template <int NT, int UNR, typename Src>
+__device__ void radix_select_batched(const Src& src, int n_att, int e, int d0, RadixSmem& rs)
+{
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        rs.p[0] = rs.p[1] = rs.p[2] = 0;
+        rs.mk[0] = rs.mk[1] = rs.mk[2] = 0;
+        rs.rem = (unsigned)e;
+        rs.sel_bin = rs.sel_below = rs.sel_cnt = 0;
+        rs.done = 0;
+    }
+    __syncthreads();
+    for (int d = d0; d < 12; ++d) {
+        for (int i = tid; i < 256; i += NT) rs.hist[i] = 0;
+        __syncthreads();
+        const int wi = 2 - (d >> 2);
+        const int sh = 24 - 8 * (d & 3);
+        const unsigned p0 = rs.p[0], p1 = rs.p[1], p2 = rs.p[2];
+        const unsigned m0 = rs.mk[0], m1 = rs.mk[1], m2 = rs.mk[2];
+        for_slots_batched<NT, UNR>(
+            0, n_att, [&](int j) { return src.fetch(j); },
+            [&](int, const auto& r) {
+                unsigned w[3];
+                if (src.key(r, w) && (w[0] & m0) == p0 && (w[1] & m1) == p1 && (w[2] & m2) == p2) {
+                    const unsigned word = wi == 2 ? w[2] : (wi == 1 ? w[1] : w[0]);
+                    atomicAdd(&rs.hist[(word >> sh) & 255u], 1u);
+                }
+            });
+        __syncthreads();
+        if (tid < 64) {
+            unsigned c[4], loc = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[k] = rs.hist[tid * 4 + k];
+                loc += c[k];
+            }
+            unsigned inc = loc;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned y = __shfl_up(inc, off);
+                if (tid >= off) inc += y;
+            }
+            unsigned run = inc - loc;
+            const unsigned rem = rs.rem;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (run < rem && rem <= run + c[k]) {
+                    rs.sel_bin = (unsigned)(tid * 4 + k);
+                    rs.sel_below = run;
+                    rs.sel_cnt = c[k];
+                }
+                run += c[k];
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            rs.rem -= rs.sel_below;
+            rs.p[wi] |= rs.sel_bin << sh;
+            rs.mk[wi] |= 255u << sh;
+            if (rs.sel_cnt == rs.rem) rs.done = 1;
+        }
+        __syncthreads();
+        if (rs.done) break;
+    }
+}
+
 // ------------------------------------------------------------- hole fill
 // Writes, in slot order, the slots j in [lo, hi) for which pred(j) holds into
 // list[0..count), returns count (in every thread).  Contains barriers.
@@ -460,6 +553,23 @@ __device__ int collect(int lo, int hi, Pred pred, int32_t* list, ScanSmem& ss)
     int off = block_excl_scan<NT>(c, ss, &total);
     for (int j = a; j < z; ++j)
         if (pred(j)) list[off++] = j;
+    return total;
+}
+
+// The slots j in [lo, hi) with test(fetch(j)) into list[0..count), in a fixed
+// order (thread-major over for_slots_batched's assignment); returns count (in
+// every thread).  Two batched passes: count, block scan, write.  Contains
+// barriers.
+template <int NT, int UNR, typename Fetch, typename Test>
+__device__ int collect_batched(int lo, int hi, Fetch fetch, Test test, int32_t* list, ScanSmem& ss)
+{
+    int c = 0;
+    for_slots_batched<NT, UNR>(lo, hi, fetch, [&](int, const auto& v) { c += test(v) ? 1 : 0; });
+    int total;
+    int off = block_excl_scan<NT>(c, ss, &total);
+    for_slots_batched<NT, UNR>(lo, hi, fetch, [&](int j, const auto& v) {
+        if (test(v)) list[off++] = j;
+    });
     return total;
 }
 
@@ -521,6 +631,19 @@ struct KvRows {
         K[kvec(dst, c)] = K[kvec(src, c)];
         V[kvec(dst, c)] = V[kvec(src, c)];
     }
+    // copy split in two, so several moves' loads can be in flight
+    struct Chunk {
+        uint4 k, v;
+    };
+    __device__ static inline Chunk fetch(const State& S, size_t si, int c)
+    {
+        return {reinterpret_cast<const uint4*>(S.kc)[kvec(si, c)], reinterpret_cast<const uint4*>(S.vc)[kvec(si, c)]};
+    }
+    __device__ static inline void put(const State& S, size_t si, int c, const Chunk& x)
+    {
+        reinterpret_cast<uint4*>(S.kc)[kvec(si, c)] = x.k;
+        reinterpret_cast<uint4*>(S.vc)[kvec(si, c)] = x.v;
+    }
 };
 
 // KvRows8: int8 rows of 128 codes, 16 chunks of 8 bytes; scales beside.
@@ -535,6 +658,28 @@ struct KvRows8 {
         if (c == 0) {
             S.kss[dst] = S.kss[src];
             S.vss[dst] = S.vss[src];
+        }
+    }
+    struct Chunk {
+        uint2 k, v;
+        float ks, vs;  // chunk 0 only
+    };
+    __device__ static inline Chunk fetch(const State& S, size_t si, int c)
+    {
+        Chunk x;
+        x.k = reinterpret_cast<const uint2*>(S.kc)[kvec(si, c)];
+        x.v = reinterpret_cast<const uint2*>(S.vc)[kvec(si, c)];
+        x.ks = c == 0 ? S.kss[si] : 0.f;
+        x.vs = c == 0 ? S.vss[si] : 0.f;
+        return x;
+    }
+    __device__ static inline void put(const State& S, size_t si, int c, const Chunk& x)
+    {
+        reinterpret_cast<uint2*>(S.kc)[kvec(si, c)] = x.k;
+        reinterpret_cast<uint2*>(S.vc)[kvec(si, c)] = x.v;
+        if (c == 0) {
+            S.kss[si] = x.ks;
+            S.vss[si] = x.vs;
         }
     }
 };
@@ -599,6 +744,26 @@ struct KvTiles {
 #pragma unroll
         for (int e = 0; e < 8; ++e) V[velem(dst, 8 * c + e)] = V[velem(src, 8 * c + e)];
     }
+    struct Chunk {
+        uint4 k;
+        unsigned short v[8];
+    };
+    __device__ static inline Chunk fetch(const State& S, size_t si, int c)
+    {
+        Chunk x;
+        x.k = reinterpret_cast<const uint4*>(S.kc)[kvec(si, c)];
+        const unsigned short* V = reinterpret_cast<const unsigned short*>(S.vc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x.v[e] = V[velem(si, 8 * c + e)];
+        return x;
+    }
+    __device__ static inline void put(const State& S, size_t si, int c, const Chunk& x)
+    {
+        reinterpret_cast<uint4*>(S.kc)[kvec(si, c)] = x.k;
+        unsigned short* V = reinterpret_cast<unsigned short*>(S.vc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) V[velem(si, 8 * c + e)] = x.v[e];
+    }
 };
 
 // In-place compaction of one unit: live slots of [n2, n_att) move into the
@@ -612,21 +777,45 @@ __device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n
     int32_t* hl = s.iscr + (size_t)unit * 2 * cap;
     int32_t* ll = hl + cap;
     int32_t* ps = s.ps;
-    const int nh = collect<NT>(0, n2, [&](int j) { return ps[sidx(j)] < 0; }, hl, ss);
-    const int nl = collect<NT>(n2, n_att, [&](int j) { return ps[sidx(j)] >= 0; }, ll, ss);
+    auto pos_at = [&](int j) { return ps[sidx(j)]; };
+    const int nh = collect_batched<NT, 8>(0, n2, pos_at, [](int p) { return p < 0; }, hl, ss);
+    const int nl = collect_batched<NT, 8>(n2, n_att, pos_at, [](int p) { return p >= 0; }, ll, ss);
     __syncthreads();
     if (nh != nl) {
         if (threadIdx.x == 0) atomicOr(s.err, kErrCompact);
         return;
     }
+    // moves: a 16-lane group per move, MU moves' loads in flight before their
+    // stores (sources and destinations are disjoint, so no move reads another's
+    // destination)
+    constexpr int MU = 4, NG = NT / 16;
     ST* sc = (ST*)s.sc;
     const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;
-    for (int i = grp; i < nh; i += NT / 16) {
-        const size_t src = sidx(ll[i]), dst = sidx(hl[i]);
-        KV::copy(s, src, dst, sub);
-        if (sub == 0) {
-            if (has_scores) sc[dst] = sc[src];
-            ps[dst] = ps[src];
+    for (int i0 = grp; i0 < nh; i0 += NG * MU) {
+        size_t src[MU], dst[MU];
+#pragma unroll
+        for (int u = 0; u < MU; ++u) {
+            const int i = min(i0 + u * NG, nh - 1);
+            src[u] = sidx(ll[i]);
+            dst[u] = sidx(hl[i]);
+        }
+        typename KV::Chunk ch[MU];
+        ST scv[MU];
+        int32_t psv[MU];
+#pragma unroll
+        for (int u = 0; u < MU; ++u) {
+            ch[u] = KV::fetch(s, src[u], sub);
+            scv[u] = has_scores ? sc[src[u]] : ST(0);
+            psv[u] = ps[src[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < MU; ++u) {
+            if (i0 + u * NG >= nh) continue;
+            KV::put(s, dst[u], sub, ch[u]);
+            if (sub == 0) {
+                if (has_scores) sc[dst[u]] = scv[u];
+                ps[dst[u]] = psv[u];
+            }
         }
     }
 }
@@ -698,13 +887,12 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
         MT bs = (MT)INFINITY;
         int bp = -1, bj = -1;
         // slot j: decay its score and add its weights of this step (summed over
-        // the group); the new token (j == n) starts from zero.  With decay 1 the
-        // fused multiply-add is the plain sum, rounded once.
-        auto visit = [&](int j, ST old, int pos) {
+        // the group; lg = its G logits); the new token (j == n) starts from
+        // zero.  With decay 1 the fused multiply-add is the plain sum, rounded once.
+        auto visit = [&](int j, ST old, int pos, const float (&lg)[G]) {
             float p = 0.f;
 #pragma unroll
-            for (int g = 0; g < G; ++g)
-                p += fast_exp2(logit[(size_t)g * lstride + j] - Mg[g]) * invLg[g];
+            for (int g = 0; g < G; ++g) p += fast_exp2(lg[g] - Mg[g]) * invLg[g];
             ST nw;
             if constexpr (sizeof(ST) == 8) nw = fma((double)lam, old, (double)p);
             else nw = (ST)fmaf(lam, (float)old, p);
@@ -720,19 +908,43 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             }
             if (e == 1 && pos >= lo_c && pos < hi_c) take_better(bs, bp, bj, (MT)nw, pos, j);
         };
+        auto logits_of = [&](int j, float (&lg)[G]) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) lg[g] = logit[(size_t)g * lstride + j];
+        };
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
             const int j = tid + k * NT;
-            if (j < n_att) visit(j, j < n ? pf_s[k] : (ST)0, j < n ? pf_p[k] : t);
-        }
-        for (int j = tid + PF * NT; j < n_att; j += NT) {
-            if (j < n) {
-                const size_t si = sidx(j);
-                visit(j, scp[si], psp[si]);
-            } else {
-                visit(j, (ST)0, t);
+            if (j < n_att) {
+                float lg[G];
+                logits_of(j, lg);
+                visit(j, j < n ? pf_s[k] : (ST)0, j < n ? pf_p[k] : t, lg);
             }
         }
+        // the rest four slots at a time (score, position and logits of each
+        // fetched before any is used: long units would otherwise wait on one
+        // dependent load per slot)
+        struct Slot {
+            ST s;
+            int p;
+            float lg[G];
+        };
+        for_slots_batched<NT, 4>(
+            PF * NT, n_att,
+            [&](int j) {
+                // slot n is the append slot, which has no page yet when the new
+                // token is to fill a hole in place: slot 0 stands in (unused)
+                const size_t si = sidx(j < n ? j : 0);
+                Slot r;
+                r.s = scp[si];
+                r.p = psp[si];
+                logits_of(j, r.lg);
+                return r;
+            },
+            [&](int j, const Slot& r) {
+                if (j < n) visit(j, r.s, r.p, r.lg);
+                else visit(j, (ST)0, t, r.lg);
+            });
         if (e == 1) {
             wave_argmin(bs, bp, bj);
             if (lane == 0) {
@@ -805,54 +1017,80 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
     int d0;
     double vmass = 0.0;
     int nv = 0;
+    // candidates' keys are built from data fetched UNR slots at a time
+    constexpr int UNR = 8;
     if (h2o) {
-        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
-            const size_t si = sidx(j);
-            const int pos = psp[si];
-            if (pos < lo_c || pos >= hi_c) return false;
-            if constexpr (sizeof(ST) <= 4) {
-                wk[2] = 0;
-                wk[1] = ord32((float)scp[si]);
-            } else {
-                const unsigned long long u = ord64((double)scp[si]);
-                wk[2] = (unsigned)(u >> 32);
-                wk[1] = (unsigned)u;
-            }
-            wk[0] = ~(unsigned)pos;
-            return true;
+        // 64- or 96-bit keys: the score's order-preserving bits, then ~position
+        // (equal scores: the higher position is the smaller key, evicted first)
+        struct Raw {
+            int pos;
+            ST score;
         };
-        d0 = sizeof(ST) <= 4 ? 4 : 0;
-        radix_select<NT>(key_of, n_att, e, d0, sm.rad);
-        for (int j = tid; j < n_att; j += NT) {
-            unsigned wk[3];
-            if (key_of(j, wk) && key_le(wk, sm.rad)) {
+        struct Src {
+            SlotMap<PAGED> sidx;
+            const int32_t* psp;
+            const ST* scp;
+            int lo_c, hi_c;
+            __device__ Raw fetch(int j) const
+            {
                 const size_t si = sidx(j);
-                vmass += (double)scp[si];
-                psp[si] = -1;
-                ++nv;
+                return {psp[si], scp[si]};
             }
-        }
-    } else {
-        const unsigned long long k0 = a.sc.seed;
-        auto key_of = [&](int j, unsigned (&wk)[3]) -> bool {
-            const int pos = psp[sidx(j)];
-            if (pos < P) return false;
-            const unsigned long long x =
-                philox_word0((unsigned long long)b, (unsigned long long)h, (unsigned long long)t,
-                             (unsigned long long)pos, k0, 0ull);
-            wk[2] = (unsigned)(x >> 32);
-            wk[1] = (unsigned)x;
-            wk[0] = ~(unsigned)pos;
-            return true;
+            __device__ bool key(const Raw& r, unsigned (&wk)[3]) const
+            {
+                if (r.pos < lo_c || r.pos >= hi_c) return false;
+                if constexpr (sizeof(ST) <= 4) {
+                    wk[2] = 0;
+                    wk[1] = ord32((float)r.score);
+                } else {
+                    const unsigned long long u = ord64((double)r.score);
+                    wk[2] = (unsigned)(u >> 32);
+                    wk[1] = (unsigned)u;
+                }
+                wk[0] = ~(unsigned)r.pos;
+                return true;
+            }
         };
-        radix_select<NT>(key_of, n_att, e, 0, sm.rad);
-        for (int j = tid; j < n_att; j += NT) {
+        const Src src{sidx, psp, scp, lo_c, hi_c};
+        d0 = sizeof(ST) <= 4 ? 4 : 0;
+        radix_select_batched<NT, UNR>(src, n_att, e, d0, sm.rad);
+        for_slots_batched<NT, UNR>(0, n_att, [&](int j) { return src.fetch(j); }, [&](int j, const Raw& r) {
             unsigned wk[3];
-            if (key_of(j, wk) && key_le(wk, sm.rad)) {
+            if (src.key(r, wk) && key_le(wk, sm.rad)) {
+                vmass += (double)r.score;
                 psp[sidx(j)] = -1;
                 ++nv;
             }
-        }
+        });
+    } else {
+        // Random Attention: word 0 of Philox4x64-10 at counter (b, h, t, position)
+        struct Src {
+            SlotMap<PAGED> sidx;
+            const int32_t* psp;
+            int P, b, h, t;
+            unsigned long long k0;
+            __device__ int fetch(int j) const { return psp[sidx(j)]; }
+            __device__ bool key(int pos, unsigned (&wk)[3]) const
+            {
+                if (pos < P) return false;
+                const unsigned long long x =
+                    philox_word0((unsigned long long)b, (unsigned long long)h, (unsigned long long)t,
+                                 (unsigned long long)pos, k0, 0ull);
+                wk[2] = (unsigned)(x >> 32);
+                wk[1] = (unsigned)x;
+                wk[0] = ~(unsigned)pos;
+                return true;
+            }
+        };
+        const Src src{sidx, psp, P, b, h, t, a.sc.seed};
+        radix_select_batched<NT, UNR>(src, n_att, e, 0, sm.rad);
+        for_slots_batched<NT, UNR>(0, n_att, [&](int j) { return src.fetch(j); }, [&](int j, int pos) {
+            unsigned wk[3];
+            if (src.key(pos, wk) && key_le(wk, sm.rad)) {
+                psp[sidx(j)] = -1;
+                ++nv;
+            }
+        });
     }
     const int nv_all = block_sum_i32<NT>(nv, sm.isum);
     const double vm = block_sum_f64<NT>(vmass, sm.dsum);
