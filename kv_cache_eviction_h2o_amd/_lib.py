@@ -14,6 +14,9 @@ import numpy as np
 
 from .build import LIB
 
+# a test may point the binding at another build of the same sources (a sanitizer build)
+LIB = os.environ.get("H2O_LIB") or LIB
+
 H2O_OK, H2O_EINVAL, H2O_ENOMEM, H2O_EDEVICE, H2O_ESTATE = 0, -1, -2, -3, -4
 SEL_H2O, SEL_RANDOM, SEL_BLOCK = 0, 1, 2
 _SELECTORS = {"h2o": SEL_H2O, "random": SEL_RANDOM, "block": SEL_BLOCK}

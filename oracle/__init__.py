@@ -12,6 +12,9 @@ import numpy as np
 
 from .build import LIB, build
 
+# a test may point the wrapper at another build of the same source (a sanitizer build)
+LIB = os.environ.get("H2O_ORACLE_LIB") or LIB
+
 ORC_H2O, ORC_RANDOM, ORC_BLOCK = 0, 1, 2
 _dp = C.POINTER(C.c_double)
 _ip = C.POINTER(C.c_int32)
