@@ -355,21 +355,46 @@ def host_cpu() -> str:
 
 
 PEAK_BF16_TFLOPS = 2500.0
+# Vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-operations/s
+# of 32-bit VALU instructions (x2 for FMA and x2 for packed fp32 is the 157.3
+# TFLOP/s fp32 vector peak); v_exp_f32 issues at a quarter of that rate, so an
+# exponential costs 4 lane-operation equivalents.
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+EXP_COST = 4.0
+# Lane-operation equivalents per score (one causal (row, key, query head)
+# logit) in the two column-sum passes, from the kernels' hot loops: the rows
+# pass adds the hi and lo products, subtracts the running maximum, takes one
+# exp2, compares, and updates sum and maximum by fma / add and two selects
+# (7 VALU + 1 exp2); the columns pass adds hi and lo, subtracts the row maximum,
+# takes one exp2, scales by 1 / L and accumulates, with a conversion and an
+# fp64 add per two scores (4.75 VALU + 1 exp2).
+ROWS_OPS_PER_SCORE = 7.0 + EXP_COST
+COLS_OPS_PER_SCORE = 4.75 + EXP_COST
 
 
-def call_roofline(nbytes: float, flops: float, per_call: float, note: str) -> dict:
+def call_roofline(nbytes: float, flops: float, per_call: float, note: str, alu_ops: float = 0.0) -> dict:
     """Roofline of one whole prompt call: the bound is whichever of HBM (the
-    algorithmic bytes at 8 TB/s) and the bf16 matrix peak (the algorithmic
-    flops at 2.5 PFLOP/s) takes longer; the other is reported beside it."""
+    algorithmic bytes at 8 TB/s), the bf16 matrix peak (the algorithmic flops
+    at 2.5 PFLOP/s) and the vector ALU (the passes' lane-operation equivalents
+    at 39.3 T/s) takes longest; the others are reported beside it."""
     t_mem, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12)
-    hbm = {"bound": "hbm", "achieved": round(nbytes / per_call / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": round(t_mem / per_call, 4)}
-    mfma = {"bound": "mfma", "achieved": round(flops / per_call / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(t_mfma / per_call, 4)}
-    main, other = (hbm, mfma) if t_mem >= t_mfma else (mfma, hbm)
-    return {**main, "traffic": None, "mean_call_us": round(per_call * 1e6, 2), "algorithmic_bytes": nbytes,
-            "algorithmic_flops": flops, f"{other['bound']}_frac": other["frac"],
-            f"{other['bound']}_achieved": other["achieved"], "note": note}
+    t_alu = alu_ops / (PEAK_VALU_TOPS * 1e12)
+    cands = [("hbm", t_mem, nbytes / per_call / 1e9, HBM_PEAK_GBS, "GB/s"),
+             ("mfma", t_mfma, flops / per_call / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s")]
+    if alu_ops:
+        cands.append(("alu", t_alu, alu_ops / per_call / 1e12, round(PEAK_VALU_TOPS, 2), "T lane-ops/s"))
+    cands.sort(key=lambda c: -c[1])
+    name, t, ach, peak, unit = cands[0]
+    out = {"bound": name, "achieved": round(ach, 2 if name != "hbm" else 1), "peak": peak, "unit": unit,
+           "frac": round(t / per_call, 4), "traffic": None, "mean_call_us": round(per_call * 1e6, 2),
+           "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+    if alu_ops:
+        out["alu_lane_ops"] = alu_ops
+    for oname, ot, oach, _, _ in cands[1:]:
+        out[f"{oname}_frac"] = round(ot / per_call, 4)
+        out[f"{oname}_achieved"] = round(oach, 2)
+    out["note"] = note
+    return out
 
 
 def colsum_cpu_baseline(w, lens, seconds: float):
@@ -472,6 +497,7 @@ def prefill_main(args, w):
         raise SystemExit(f"column sums add up to {total}, expected {expect}")
     pairs = sum(P * (P + 1) // 2 for P in lens)
     flops = 2.0 * D * Hq * pairs  # the causal logits, once
+    alu = Hq * pairs * (ROWS_OPS_PER_SCORE + COLS_OPS_PER_SCORE)  # both passes score every causal pair
     tokens = float(sum(lens))
     nbytes = tokens * (Hq * D * 4 + Hkv * D * 2 + Hkv * 8)  # q, K, the sums
     cpu = None if args.no_cpu_baseline else colsum_cpu_baseline(w, lens, args.cpu_seconds)
@@ -488,7 +514,8 @@ def prefill_main(args, w):
             nbytes, flops, per_call,
             "whole call; algorithmic bytes = fp32 q, bf16 K and the fp64 sums once; algorithmic flops = "
             "the causal logits q.k once (the kernels compute them 4x: two passes, each on the bf16 hi "
-            "and lo parts of q)"),
+            "and lo parts of q); ALU = every causal score in both passes at 11 (rows) + 8.75 (columns) "
+            "lane-operation equivalents (an exp2 counts 4) against 39.3 T/s", alu_ops=alu),
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_hash(prompt=True),
     }
@@ -545,6 +572,7 @@ def snapkv_main(args, w):
     tokens = float(sum(lens))
     rows = sum(sum(i + 1 for i in range(P - min(window, P), P)) for P in lens)
     flops = 2.0 * D * Hq * rows
+    alu = Hq * rows * (ROWS_OPS_PER_SCORE + COLS_OPS_PER_SCORE)  # the window rows' scores, both passes
     nbytes = (sum(min(window, P) for P in lens) * Hq * D * 4 + tokens * (Hkv * D * 2 + Hq * 8)
               + B * Hkv * cap * 4 + B * 4)  # window q, K, votes, kept positions and counts
     line = {
@@ -560,8 +588,9 @@ def snapkv_main(args, w):
         "roofline": call_roofline(
             nbytes, flops, per_call,
             "whole call; algorithmic bytes = the window rows' fp32 q, bf16 K, the fp64 votes and the kept "
-            "positions once; algorithmic flops = the window rows' causal logits once; the call also "
-            "pools and selects"),
+            "positions once; algorithmic flops = the window rows' causal logits once; ALU = the window rows' "
+            "scores in both passes at 11 + 8.75 lane-operation equivalents; the call also pools and "
+            "selects", alu_ops=alu),
         "cpu_baseline": (None if args.no_cpu_baseline
                          else snapkv_cpu_baseline(w, lens, window, pool, keep, args.cpu_seconds)),
         "kernel_source_sha256_16": kernel_hash(prompt=True),

@@ -19,6 +19,15 @@ def test_call_roofline_picks_the_slower_resource():
     assert abs(r["frac"] - 0.5) < 1e-9 and abs(r["hbm_frac"] - 0.125e-6 / 80e-6) < 1e-4
 
 
+def test_call_roofline_alu_bound():
+    # 1 MB (0.125 us) and 1 GFLOP (0.4 us) against 3.93e9 lane-ops (100 us at 39.3 T/s)
+    ops = bench.PEAK_VALU_TOPS * 1e12 * 100e-6
+    r = bench.call_roofline(1e6, 1e9, 200e-6, "x", alu_ops=ops)
+    assert r["bound"] == "alu" and r["unit"] == "T lane-ops/s" and abs(r["peak"] - 39.32) < 0.01
+    assert abs(r["frac"] - 0.5) < 1e-9 and "hbm_frac" in r and "mfma_frac" in r
+    assert abs(bench.PEAK_VALU_TOPS * 2 * 2 - 157.3) < 0.1  # the fp32 vector peak: FMA x packed
+
+
 def test_source_hashes_cover_their_own_kernels():
     assert set(bench.STEP_SRCS) & set(bench.PROMPT_SRCS) == {"h2o_internal.h", "h2o_device.h"}
     assert "h2o_prefill.hip" not in bench.STEP_SRCS and "h2o_prefill.hip" in bench.PROMPT_SRCS
