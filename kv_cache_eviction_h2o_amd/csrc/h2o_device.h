@@ -155,6 +155,13 @@ __device__ inline float buf_load4f(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kStreamPolicy));
 }
+// One double through the vector memory path (counted by vmcnt, so waits for
+// LDS or scalar data never wait for it).
+__device__ inline double load_f64(const double* p)
+{
+    const uint2 v = buf_load8(make_rsrc(p, 8u), 0u);
+    return __hiloint2double((int)v.y, (int)v.x);
+}
 // The same policy on plain global loads (paged rows reached through the block table).
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));

@@ -135,6 +135,16 @@ __host__ __device__ inline int evict_count(const Sched& s, int t, int P, int n_a
     return (n_att - P == s.rand_k + s.rand_r) ? s.rand_r : 0;
 }
 
+// One row of a step launch, read by its workgroups with a single 16-byte
+// load: the sequences go longest first (a workgroup's time grows with its count).
+struct alignas(16) SeqArg {
+    int32_t b;        // the sequence
+    int32_t n;        // its retained slots before the step
+    int32_t p;        // its prompt length
+    int32_t newpage;  // paged: the page for its append slot, or -1 (with pop_stack,
+                      // the free-stack entry that holds it)
+};
+
 struct StepArgs {
     Geometry g;
     State s;
@@ -148,14 +158,9 @@ struct StepArgs {
     int fused;      // 1: the select's holes are filled in the same launch
     int lds_n;      // logit row stride in LDS (>= max n_att of the launch)
     int npg_lds;    // paged: block-table entries staged in LDS per unit
-    int seq_in_args;                // 1: seq_n / seq_p below are valid (B <= kMaxArgBatch)
-    int32_t seq_n[kMaxArgBatch];    // retained slots of sequence b before the step
-    int32_t seq_p[kMaxArgBatch];    // prompt length of sequence b
-    uint8_t seq_order[kMaxArgBatch];  // with seq_in_args: the sequences longest first (workgroup
-                                      // i takes the unit (seq_order[i / Hkv], i % Hkv))
-    int32_t newpage[kMaxArgBatch];  // paged: page for the append slot of sequence b, or -1;
-                                    // with pop_stack, the free-stack entry that holds it
-    int pop_stack;                  // 1: newpage[b] indexes State::fstack
+    int seq_in_args;             // 1: seq below is valid (B <= kMaxArgBatch)
+    int pop_stack;               // 1: SeqArg::newpage indexes State::fstack
+    SeqArg seq[kMaxArgBatch];    // row i: the sequence whose units workgroups i * Hkv .. + Hkv take
 };
 
 static_assert(sizeof(StepArgs) <= 4096, "kernel arguments are limited to 4 KB");

@@ -61,12 +61,29 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     __shared__ float red_m[NW][G], red_l[NW][G];
     __shared__ __align__(16) float red_o[NW][G][D];
     __shared__ TailSmem<ST, NW> tsm;
+    // the group's q rows and the new token's K and V rows, fetched once per
+    // workgroup (every wave needs all of them, each lane a different part)
+    __shared__ __align__(16) float q_s[G * D];
+    __shared__ __align__(16) uint4 kvn_s[2 * kRowVecs];
 
     const Geometry& gm = a.g;
     const State& S = a.s;
     // the head is the fast index (XCDs round-robin), sequences longest first
     const int sq = (int)blockIdx.x / gm.Hkv, h = (int)blockIdx.x - sq * gm.Hkv;
-    const int b = a.seq_in_args ? (int)a.seq_order[sq] : sq;
+    // this row's sequence, retained count and prompt length: scalar loads of
+    // the arguments (without them in the arguments, from the state; those
+    // reads are volatile so that the compiler cannot merge the two paths into
+    // vector loads through a selected pointer)
+    SeqArg sa;
+    if (a.seq_in_args) {
+        sa = a.seq[sq];
+    } else {
+        sa.b = sq;
+        sa.n = *reinterpret_cast<const volatile int32_t*>(S.cnt + (size_t)sq * gm.Hkv + h);
+        sa.p = *reinterpret_cast<const volatile int32_t*>(S.t0 + sq);
+        sa.newpage = -1;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(sa.b);
     const int unit = b * gm.Hkv + h;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar)
@@ -76,9 +93,9 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
 
     // uniform over the workgroup: readfirstlane keeps them (and the buffer
     // descriptors built from them) in scalar registers
-    const int P = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_p[b] : S.t0[b]);
+    const int P = __builtin_amdgcn_readfirstlane(sa.p);
     const int t = P + a.step;
-    const int n = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_n[b] : S.cnt[unit]);
+    const int n = __builtin_amdgcn_readfirstlane(sa.n);
     const bool h2o = scored(a.sc.selector);
     const int e = evict_count(a.sc, t, P, n + 1);
     const bool inplace_new = a.fused && h2o && e == 1;
@@ -94,37 +111,23 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     int32_t* psp = S.ps;
 
     // ---- loads, issued in the order their data is needed ------------------
-    // q of column lc's head: lane (lg, lc) holds d = 32 kb + 8 lg + i
-    const int qh = head < G ? head : 0;
-    const float4* qp =
-        reinterpret_cast<const float4*>(a.q + ((size_t)b * gm.Hq + (size_t)h * G + qh) * D);
-    float4 qraw[8];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        qraw[2 * kb] = qp[8 * kb + 2 * lg];
-        qraw[2 * kb + 1] = qp[8 * kb + 2 * lg + 1];
-    }
-    // the new token: K as an A operand whose 16 rows are all that token, V at
-    // the d = 16 db + 4 lg + r this lane accumulates, and chunk tid % 16 of
-    // both rows for the slot write
-    const uint4* knp = reinterpret_cast<const uint4*>(a.kn) + (size_t)unit * kRowVecs;
-    const uint4* vnp = reinterpret_cast<const uint4*>(a.vn) + (size_t)unit * kRowVecs;
-    uint4 kn4[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kn4[kb] = knp[4 * kb + lg];
-    const uint2* vn2 = reinterpret_cast<const uint2*>(vnp);
-    uint2 vn8[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) vn8[db] = vn2[4 * db + lg];
-    const uint4 knr = knp[tid & 15];
-    const uint4 vnr = vnp[tid & 15];
-    const double emass0 = S.emass[unit];
-    // every wave's q and new-token loads enter the memory queues before any
-    // tile load of the workgroup (the older wave of each SIMD would otherwise
-    // issue all of its tile loads first and the younger one's q would wait
-    // behind them); the barrier waits for LDS only, not for that data
+    // q and the new token's rows: one 16-byte vector per thread (threads past
+    // them read out of range: zero, no memory access), staged in LDS below
+    constexpr int QV = G * D / 4;  // 16-byte vectors of the group's q rows
+    const auto rq = make_rsrc(a.q + ((size_t)b * gm.Hq + (size_t)h * G) * D, (unsigned)QV * 16u);
+    const auto rkn = make_rsrc(reinterpret_cast<const uint4*>(a.kn) + (size_t)unit * kRowVecs, kRowBytes);
+    const auto rvn = make_rsrc(reinterpret_cast<const uint4*>(a.vn) + (size_t)unit * kRowVecs, kRowBytes);
+    const uint4 qv = buf_load16(rq, (unsigned)tid * 16u);
+    const uint4 knv = buf_load16(rkn, min((unsigned)(tid - QV), (unsigned)kRowVecs) * 16u);
+    const uint4 vnv = buf_load16(rvn, min((unsigned)(tid - QV - kRowVecs), (unsigned)kRowVecs) * 16u);
+    // the unit's evicted mass, for its update at the end: a vector load (a
+    // scalar one would hold up the barrier below for a memory round trip)
+    const double emass0 = load_f64(S.emass + unit);
+    // every wave's loads above enter the memory queues before any tile load
+    // of the workgroup (the older wave of a SIMD would otherwise issue all of
+    // its tile loads first); the barrier waits for none of that data
     __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // K / V tiles through raw buffer loads over the unit's first ntiles
@@ -160,12 +163,29 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
         }
     }
 
+    // q and the new token's rows into LDS (their loads, issued before the
+    // tiles', retire first), then every lane reads its parts:
+    // q of column lc's head at d = 32 kb + 8 lg + i, the new token's K as an A
+    // operand whose 16 rows are all that token, its V at d = 16 db + 4 lg + r
+    if (tid < QV) reinterpret_cast<uint4*>(q_s)[tid] = qv;
+    if ((unsigned)(tid - QV) < (unsigned)kRowVecs) kvn_s[tid - QV] = knv;
+    if ((unsigned)(tid - QV - kRowVecs) < (unsigned)kRowVecs) kvn_s[tid - QV] = vnv;
+    lds_barrier();
+    const int qh = head < G ? head : 0;
+    const float4* qs4 = reinterpret_cast<const float4*>(q_s + qh * D);
+    uint4 kn4[4];
+    uint2 vn8[8];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) kn4[kb] = kvn_s[4 * kb + lg];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vn8[db] = reinterpret_cast<const uint2*>(kvn_s + kRowVecs)[4 * db + lg];
+
     // B operand of q.K: column lc = hi (lc < 8) or lo part of head lc & 7
     bf16x8 qop[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const float x[8] = {qraw[2 * kb].x, qraw[2 * kb].y, qraw[2 * kb].z, qraw[2 * kb].w,
-                            qraw[2 * kb + 1].x, qraw[2 * kb + 1].y, qraw[2 * kb + 1].z, qraw[2 * kb + 1].w};
+        const float4 q0 = qs4[8 * kb + 2 * lg], q1 = qs4[8 * kb + 2 * lg + 1];
+        const float x[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             qop[kb][i] = head < G ? split_part(x[i] * a.qscale, lo_col) : (__bf16)0.0f;
@@ -352,7 +372,7 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     }
     // the new token's rows go to slot n unless they fill a victim's hole later
     auto write_new = [&](size_t si) {  // the new token's row into slot index si
-        if (tid < 16) KvTiles::store(S.kc, S.vc, si, tid, knr, vnr);
+        if (tid < 16) KvTiles::store(S.kc, S.vc, si, tid, kvn_s[tid], kvn_s[kRowVecs + tid]);
     };
     if (!inplace_new) write_new(sidx(n));
 

@@ -326,19 +326,10 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     a.fused = fused ? 1 : 0;
     a.lds_n = (max_n_att + 3) & ~3;
     a.npg_lds = (max_n_att + kPageSize - 1) >> kPageShift;
-    for (int i = 0; i < kMaxArgBatch; ++i) a.newpage[i] = -1;
+    int32_t newpage[kMaxArgBatch];
+    for (int i = 0; i < kMaxArgBatch; ++i) newpage[i] = -1;
     a.seq_in_args = B <= kMaxArgBatch ? 1 : 0;
-    if (a.seq_in_args) {
-        for (int b = 0; b < B; ++b) {
-            a.seq_n[b] = c->count[b];
-            a.seq_p[b] = c->plen[b];
-        }
-        // workgroups of the longest sequences first (a workgroup's time grows with its count)
-        std::vector<int> ord(B);
-        for (int b = 0; b < B; ++b) ord[b] = b;
-        std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return c->count[x] > c->count[y]; });
-        for (int i = 0; i < B; ++i) a.seq_order[i] = (uint8_t)ord[i];
-    }
+    a.pop_stack = 0;
     std::vector<int> got;  // sequences given a page in this call (returned if the launch fails)
     if (c->block) {
         // every block-table entry but the last is full: a sequence needs a page
@@ -349,7 +340,7 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
         a.pop_stack = 1;
         int k = 0;
         for (int b = 0; b < B; ++b)
-            if ((c->count[b] & (kPageSize - 1)) == 0) a.newpage[b] = c->ftop - 1 - k++;
+            if ((c->count[b] & (kPageSize - 1)) == 0) newpage[b] = c->ftop - 1 - k++;
     } else if (c->g.paged) {
         int demand = 0;
         std::vector<char> need(B, 0);
@@ -368,9 +359,19 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
                 const int p = c->free_pages.back();
                 c->free_pages.pop_back();
                 c->pages[b].push_back(p);
-                a.newpage[b] = p;
+                newpage[b] = p;
                 got.push_back(b);
             }
+    }
+    if (a.seq_in_args) {
+        // workgroups of the longest sequences first (a workgroup's time grows with its count)
+        std::vector<int> ord(B);
+        for (int b = 0; b < B; ++b) ord[b] = b;
+        std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return c->count[x] > c->count[y]; });
+        for (int i = 0; i < B; ++i) {
+            const int b = ord[i];
+            a.seq[i] = SeqArg{b, c->count[b], c->plen[b], newpage[b]};
+        }
     }
     hipError_t err = launch_step(a, max_n_att, (hipStream_t)stream);
     if (err != hipSuccess) {  // nothing ran: the pages go back as they came

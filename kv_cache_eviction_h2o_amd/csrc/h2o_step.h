@@ -40,7 +40,20 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     // every XCD gets the same heads of every sequence, and within an XCD the
     // longest sequences are dispatched first
     const int sq = (int)blockIdx.x / gm.Hkv, h = (int)blockIdx.x - sq * gm.Hkv;
-    const int b = a.seq_in_args ? (int)a.seq_order[sq] : sq;
+    // this row's sequence, retained count and prompt length: scalar loads of
+    // the arguments (without them in the arguments, from the state; those
+    // reads are volatile so that the compiler cannot merge the two paths into
+    // vector loads through a selected pointer)
+    SeqArg sa;
+    if (a.seq_in_args) {
+        sa = a.seq[sq];
+    } else {
+        sa.b = sq;
+        sa.n = *reinterpret_cast<const volatile int32_t*>(S.cnt + (size_t)sq * gm.Hkv + h);
+        sa.p = *reinterpret_cast<const volatile int32_t*>(S.t0 + sq);
+        sa.newpage = -1;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(sa.b);
     const int unit = b * gm.Hkv + h;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, sub = tid & 15, grp = tid >> 4;
 
@@ -48,9 +61,9 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     // them from the arguments saves a dependent memory round trip at the start
     // uniform over the workgroup: readfirstlane keeps them (and the buffer
     // descriptors built from them) in scalar registers
-    const int P = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_p[b] : S.t0[b]);
+    const int P = __builtin_amdgcn_readfirstlane(sa.p);
     const int t = P + a.step;
-    const int n = __builtin_amdgcn_readfirstlane(a.seq_in_args ? a.seq_n[b] : S.cnt[unit]);
+    const int n = __builtin_amdgcn_readfirstlane(sa.n);
     const int n_att = n + 1;
     const bool h2o = scored(a.sc.selector);
     const int e = evict_count(a.sc, t, P, n_att);
@@ -70,7 +83,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         for (int i = tid; i < npg; i += NT) bts[i] = S.bt[(size_t)b * gm.maxp + i];
         if (!inplace_new && (n & (kPageSize - 1)) == 0) {
             // the append page: from the host, or (pop_stack) the free-stack entry it names
-            const int np = a.newpage[b] < 0 ? -1 : (a.pop_stack ? S.fstack[a.newpage[b]] : a.newpage[b]);
+            const int np = sa.newpage < 0 ? -1 : (a.pop_stack ? S.fstack[sa.newpage] : sa.newpage);
             if (np < 0) {  // the host did not provide the append page: do nothing
                 if (tid == 0) atomicOr(S.err, kErrCompact);
                 return;
@@ -107,8 +120,9 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
     constexpr unsigned VBY = sizeof(Vec);                           // bytes of a row per lane
     const Vec* kc = reinterpret_cast<const Vec*>(S.kc);
     const Vec* vc = reinterpret_cast<const Vec*>(S.vc);
-    // evicted mass of the unit, read now so its update at the end is no round trip
-    const double emass0 = S.emass[unit];
+    // evicted mass of the unit, read now so its update at the end is no round
+    // trip (a vector load: waits for scalar or LDS data never wait for it)
+    const double emass0 = load_f64(S.emass + unit);
     __builtin_amdgcn_sched_barrier(0);  // keep q and the new token ahead of the K/V stream
     // the new token's row as stored; int8 rows are quantised here, and the
     // cache then holds -- and this step attends over -- exactly that row
