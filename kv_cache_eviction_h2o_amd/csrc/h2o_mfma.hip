@@ -335,13 +335,25 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     constexpr int NP = NW * G;  // 32 or 64 pairs
     const int pi = lane % NP;
     const float mi = red_m[pi / G][pi % G], li = red_l[pi / G][pi % G];
-    float Mx = mi;
-#pragma unroll
-    for (int x = G; x < NP; x <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, x));
+    // the butterflies over one head's lanes (partners at xor G, 2G, .. < NP):
+    // row rotations by 4 (G = 4) and 8 within 16 lanes, then the swaps of
+    // 16-lane rows and (G = 8) of 32-lane halves -- register moves, no LDS
+    auto head_reduce = [](float v, auto op) {
+        if constexpr (G == 4) v = op(v, dpp<0x124>(v));  // row_ror:4
+        v = op(v, dpp<0x128>(v));                         // row_ror:8
+        {
+            const Pair x = xrow16(__float_as_uint(v));
+            v = op(__uint_as_float(x.a), __uint_as_float(x.b));
+        }
+        if constexpr (G == 8) {
+            const Pair x = xrow32(__float_as_uint(v));
+            v = op(__uint_as_float(x.a), __uint_as_float(x.b));
+        }
+        return v;
+    };
+    const float Mx = head_reduce(mi, [](float x, float y) { return fmaxf(x, y); });
     const float fi = fast_exp2(mi - Mx);
-    float Lx = li * fi;
-#pragma unroll
-    for (int x = G; x < NP; x <<= 1) Lx += __shfl_xor(Lx, x);
+    const float Lx = head_reduce(li * fi, [](float x, float y) { return x + y; });
     const float il_x = 1.0f / Lx;
     auto bcast = [](float v, int src) {
         return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
