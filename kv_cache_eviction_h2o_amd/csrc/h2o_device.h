@@ -563,21 +563,77 @@ __device__ int collect(int lo, int hi, Pred pred, int32_t* list, ScanSmem& ss)
     return total;
 }
 
-// The slots j in [lo, hi) with test(fetch(j)) into list[0..count), in a fixed
-// order (thread-major over for_slots_batched's assignment); returns count (in
-// every thread).  Two batched passes: count, block scan, write.  Contains
-// barriers.
+// Shared memory of collect_ordered: per round, the count of each (batch
+// index u, wave) cell, then its offset; two buffers alternate between rounds.
+template <int NT, int UNR>
+struct OrderSmem {
+    int off[2][UNR * (NT / 64)];
+    int total[2];
+};
+
+// The slots j in [lo, hi) with test(fetch(j)) into list[0..count) in
+// ascending slot order; returns count (in every thread).  One pass in rounds
+// of NT * UNR slots (slot j0 + u * NT + tid: every load coalesced): each
+// wave ballots its flags, the first wave turns the (u, wave) counts into
+// offsets, and every flagged slot writes itself at its offset plus its rank
+// among the lower lanes.  Two barriers per round.
 template <int NT, int UNR, typename Fetch, typename Test>
-__device__ int collect_batched(int lo, int hi, Fetch fetch, Test test, int32_t* list, ScanSmem& ss)
+__device__ int collect_ordered(int lo, int hi, Fetch fetch, Test test, int32_t* list, OrderSmem<NT, UNR>& os)
 {
-    int c = 0;
-    for_slots_batched<NT, UNR>(lo, hi, fetch, [&](int, const auto& v) { c += test(v) ? 1 : 0; });
-    int total;
-    int off = block_excl_scan<NT>(c, ss, &total);
-    for_slots_batched<NT, UNR>(lo, hi, fetch, [&](int j, const auto& v) {
-        if (test(v)) list[off++] = j;
-    });
-    return total;
+    constexpr int NW = NT / 64, E = UNR * NW, PER = (E + 63) / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    using Raw = decltype(fetch(lo));
+    int base = 0, r = 0;
+    for (int j0 = lo; j0 < hi; j0 += NT * UNR, r ^= 1) {
+        Raw v[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int j = j0 + u * NT + (int)threadIdx.x;
+            v[u] = fetch(j < hi ? j : lo);
+        }
+        unsigned long long m[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int j = j0 + u * NT + (int)threadIdx.x;
+            m[u] = __ballot(j < hi && test(v[u]));
+            if (lane == 0) os.off[r][u * NW + w] = __popcll(m[u]);
+        }
+        __syncthreads();
+        if (w == 0) {  // exclusive scan of the E cells in (u, wave) order, PER per lane
+            int c[PER], sum = 0;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int e = lane * PER + k;
+                c[k] = e < E ? os.off[r][e] : 0;
+                sum += c[k];
+            }
+            int inc = sum;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(inc, d);
+                if (lane >= d) inc += y;
+            }
+            int run = inc - sum;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int e = lane * PER + k;
+                if (e < E) os.off[r][e] = run;
+                run += c[k];
+            }
+            if (lane == 63) os.total[r] = inc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            if ((m[u] >> lane) & 1ull) {
+                const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m[u] >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((unsigned)m[u], 0u));
+                list[base + os.off[r][u * NW + w] + rank] = j0 + u * NT + (int)threadIdx.x;
+            }
+        }
+        base += os.total[r];
+    }
+    return base;
 }
 
 template <bool PAGED>
@@ -776,17 +832,22 @@ struct KvTiles {
 // In-place compaction of one unit: live slots of [n2, n_att) move into the
 // holes (ps == -1) of [0, n2), n2 = n_att - e.  Sources and destinations are
 // disjoint, so every move is independent.  Contains barriers.
+// Unroll of the hole fill's list collection (rounds of NT * kCollectUnroll slots).
+constexpr int kCollectUnroll = 16;
+
 template <int NT, typename ST, typename KV, typename SlotFn>
 __device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n_att, int e,
-                           bool has_scores, ScanSmem& ss)
+                           bool has_scores, OrderSmem<NT, kCollectUnroll>& os)
 {
     const int n2 = n_att - e;
     int32_t* hl = s.iscr + (size_t)unit * 2 * cap;
     int32_t* ll = hl + cap;
     int32_t* ps = s.ps;
     auto pos_at = [&](int j) { return ps[sidx(j)]; };
-    const int nh = collect_batched<NT, 8>(0, n2, pos_at, [](int p) { return p < 0; }, hl, ss);
-    const int nl = collect_batched<NT, 8>(n2, n_att, pos_at, [](int p) { return p >= 0; }, ll, ss);
+    // both lists in ascending slot order: the moves of one round then read and
+    // write neighbouring rows (a few pages), not rows spread over the pool
+    const int nh = collect_ordered<NT, kCollectUnroll>(0, n2, pos_at, [](int p) { return p < 0; }, hl, os);
+    const int nl = collect_ordered<NT, kCollectUnroll>(n2, n_att, pos_at, [](int p) { return p >= 0; }, ll, os);
     __syncthreads();
     if (nh != nl) {
         if (threadIdx.x == 0) atomicOr(s.err, kErrCompact);
@@ -794,17 +855,28 @@ __device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n
     }
     // moves: a 16-lane group per move, MU moves' loads in flight before their
     // stores (sources and destinations are disjoint, so no move reads another's
-    // destination)
-    constexpr int MU = 4, NG = NT / 16;
+    // destination); the list entries of a group's next round are fetched while
+    // the current round's rows are in flight, so a round costs one memory
+    // round trip, not two
+    constexpr int MU = 8, NG = NT / 16;
     ST* sc = (ST*)s.sc;
     const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;
+    int li[MU], hi[MU];
+    auto fetch_lists = [&](int i0) {  // entries past the lists re-read the last one (unused)
+#pragma unroll
+        for (int u = 0; u < MU; ++u) {
+            const int i = max(0, min(i0 + u * NG, nh - 1));
+            li[u] = ll[i];
+            hi[u] = hl[i];
+        }
+    };
+    fetch_lists(grp);
     for (int i0 = grp; i0 < nh; i0 += NG * MU) {
         size_t src[MU], dst[MU];
 #pragma unroll
         for (int u = 0; u < MU; ++u) {
-            const int i = min(i0 + u * NG, nh - 1);
-            src[u] = sidx(ll[i]);
-            dst[u] = sidx(hl[i]);
+            src[u] = sidx(li[u]);
+            dst[u] = sidx(hi[u]);
         }
         typename KV::Chunk ch[MU];
         ST scv[MU];
@@ -815,6 +887,7 @@ __device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n
             scv[u] = has_scores ? sc[src[u]] : ST(0);
             psv[u] = ps[src[u]];
         }
+        fetch_lists(i0 + NG * MU);
 #pragma unroll
         for (int u = 0; u < MU; ++u) {
             if (i0 + u * NG >= nh) continue;
@@ -844,6 +917,7 @@ struct TailSmem {
     int isum[NW];
     ScanSmem scan;
     RadixSmem rad;
+    OrderSmem<NW * 64, kCollectUnroll> ord;
 };
 
 // Everything the step does once the softmax maximum Mg and normaliser 1/L
@@ -1107,7 +1181,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
     }
     if (a.fused) {
         __syncthreads();
-        fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, h2o, sm.scan);
+        fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, h2o, sm.ord);
         if (tid == 0) S.cnt[unit] = n_att - e;
     } else if (tid == 0) {
         S.vinfo[2 * unit] = e;

@@ -36,7 +36,7 @@ constexpr int kCompactNT = 256;
 template <typename ST, bool PAGED, typename KV>
 __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a)
 {
-    __shared__ ScanSmem s_scan;
+    __shared__ OrderSmem<kCompactNT, kCollectUnroll> s_ord;
     const Geometry& gm = a.g;
     const State& S = a.s;
     const int unit = blockIdx.x;
@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a
             }
         }
     } else {
-        fill_holes<kCompactNT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, has_scores, s_scan);
+        fill_holes<kCompactNT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, has_scores, s_ord);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
