@@ -150,18 +150,6 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     load_tile(tb, TB);
     __builtin_amdgcn_sched_barrier(0);
 
-    // scores and positions of this thread's first PF phase-2 slots
-    ST pf_s[PF];
-    int pf_p[PF];
-    if (h2o) {
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
-            const int j = tid + k * NT;
-            const size_t si = sidx(j < n ? j : 0);
-            pf_s[k] = scp[si];
-            pf_p[k] = psp[si];
-        }
-    }
 
     // q and the new token's rows into LDS (their loads, issued before the
     // tiles', retire first), then every lane reads its parts:
@@ -298,6 +286,20 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
         __builtin_amdgcn_sched_barrier(0);
         load_tile(tb + 2 * NW * (i / 2 + 1), TB);
         __builtin_amdgcn_sched_barrier(0);
+    }
+    // scores and positions of this thread's first PF phase-2 slots, requested
+    // after the last tile (the CU's memory queue is served in order: earlier,
+    // they would delay every later tile)
+    ST pf_s[PF];
+    int pf_p[PF];
+    if (h2o) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int j = tid + k * NT;
+            const size_t si = sidx(j < n ? j : 0);
+            pf_s[k] = scp[si];
+            pf_p[k] = psp[si];
+        }
     }
     if (i < cnt) process(ta + 2 * NW * (i / 2), TA);
     if (i + 1 < cnt) process(tb + 2 * NW * (i / 2), TB);
