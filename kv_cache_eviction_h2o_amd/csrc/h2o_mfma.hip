@@ -212,19 +212,28 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
             s[r] = c0[r] + dpp<0x128>(c0[r]);
             s[4 + r] = c1[r] + dpp<0x128>(c1[r]);
         }
-        // slots at or past n take no weight (their K / V may be stale)
+        // slots at or past n take no weight (their K / V may be stale); only
+        // the unit's last tile holds such slots (a wave-uniform test)
         const int j0 = tl * kTile + 4 * lg;
+        const bool last_tile = (tl + 1) * kTile > n;
+        if (last_tile) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (j0 + r >= n) s[r] = -INFINITY;
-            if (j0 + 16 + r >= n) s[4 + r] = -INFINITY;
+            for (int r = 0; r < 4; ++r) {
+                if (j0 + r >= n) s[r] = -INFINITY;
+                if (j0 + 16 + r >= n) s[4 + r] = -INFINITY;
+            }
         }
         if (h2o && lc < G) {  // slot n of this tile (if any) takes the new token's logit
             float4* lp = reinterpret_cast<float4*>(logit + (size_t)lc * lstride + j0);
-            lp[0] = make_float4(j0 == n ? s_new : s[0], j0 + 1 == n ? s_new : s[1],
-                                j0 + 2 == n ? s_new : s[2], j0 + 3 == n ? s_new : s[3]);
-            lp[4] = make_float4(j0 + 16 == n ? s_new : s[4], j0 + 17 == n ? s_new : s[5],
-                                j0 + 18 == n ? s_new : s[6], j0 + 19 == n ? s_new : s[7]);
+            if (last_tile) {
+                lp[0] = make_float4(j0 == n ? s_new : s[0], j0 + 1 == n ? s_new : s[1],
+                                    j0 + 2 == n ? s_new : s[2], j0 + 3 == n ? s_new : s[3]);
+                lp[4] = make_float4(j0 + 16 == n ? s_new : s[4], j0 + 17 == n ? s_new : s[5],
+                                    j0 + 18 == n ? s_new : s[6], j0 + 19 == n ? s_new : s[7]);
+            } else {
+                lp[0] = make_float4(s[0], s[1], s[2], s[3]);
+                lp[4] = make_float4(s[4], s[5], s[6], s[7]);
+            }
         }
         float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                          fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
