@@ -102,7 +102,6 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
     if (active) {
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const int t8 = base / 8 + pt;
             const int prow = min(base + 8 * pt + (lc >> 1), P - 1);
 #pragma unroll
             for (int g = 0; g < GW; ++g) {
@@ -114,9 +113,6 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
                     const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
                     for (int i = 0; i < 8; ++i) qop[pt][g][kb][i] = split_part(x[i] * a.qscale, lo_part);
-                    const int ts = t8 - lo / 8;  // the scratch keeps tiles from row lo's on
-                    if (ts >= 0 && ts < a.nt8)
-                        a.qs[(((size_t)unit * a.nt8 + ts) * a.G + g0 + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
                 }
             }
         }
@@ -211,6 +207,20 @@ __global__ void __launch_bounds__(kCNT) colsum_rows_kernel(const ColsumArgs a)
 #undef H2O_ROWS_FETCH
 #undef H2O_ROWS_PUT
     if (!active) return;
+    // the split q tiles for the columns pass, stored only now: the vector
+    // memory counter retires in order, so stores issued before the key loop
+    // made every wait for a K chunk wait for them as well (storing them right
+    // after the last K fetch instead measured no faster over both passes)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+        const int ts = base / 8 + pt - lo / 8;  // the scratch keeps tiles from row lo's on
+        if (ts < 0 || ts >= a.nt8) continue;
+#pragma unroll
+        for (int g = 0; g < GW; ++g)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                a.qs[(((size_t)unit * a.nt8 + ts) * a.G + g0 + g) * 256 + kb * 64 + lane] = as_u4(qop[pt][g][kb]);
+    }
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
