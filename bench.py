@@ -157,9 +157,6 @@ def parse():
     ap.add_argument("--snapkv", action="store_true",
                     help="time h2o_snapkv_select (window 32, pooling 7, 20%% of each prompt kept per "
                          "query head) over the workload's prompts instead of the decode step")
-    ap.add_argument("--defer-eviction", type=int, choices=[0, 1], default=0,
-                    help="h2o_config.defer_eviction: each single eviction is chosen by the next "
-                         "step's launch (H2O on the matrix-core step: groups of 4 or 8, bf16 rows)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -640,7 +637,7 @@ def main():
     max_len = max(lens) + n_trace + 1
     for l in range(layers):
         pk, pv = S.device_prompt_kv(w.recipe, l, lens, Hkv, dev)
-        cfg = L.config_from_workload(w, max_len=max_len, defer_eviction=args.defer_eviction)
+        cfg = L.config_from_workload(w, max_len=max_len)
         if w.page_size:
             cfg.max_pages = L.pages_needed(lens, n_trace, cfg)
         caches.append(L.H2OCache(cfg, lens, pk, pv))
@@ -763,8 +760,7 @@ def main():
                    "score_decay": w.score_decay if sbytes else None,
                    "layers": layers, "prompt_len": lens[0] if len(set(lens)) == 1 else "mixed",
                    "window_steps": [s0, s0 + K_steps], "mean_n_att": round(float(win.mean()), 1),
-                   "entry_point": "h2o_step_compact", "defer_eviction": bool(args.defer_eviction),
-                   "parallelism": "single GPU"},
+                   "entry_point": "h2o_step_compact", "parallelism": "single GPU"},
         "token_heads_per_s": round(value * Hkv, 1),
         "algorithmic_bytes_per_launch": int(launch_b.mean()),
         "hbm_frac_step": round(step_bytes / elapsed / (HBM_PEAK_GBS * 1e9), 4),

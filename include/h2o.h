@@ -171,18 +171,6 @@ typedef struct {
     uint64_t workspace_bytes;  /* size of workspace (ignored when it is NULL) */
     float score_decay;     /* H2O, block: 0 or 1 = the exact cumulative sum; else in (0, 1):
                               a moving sum, see the compressed-state note above */
-    int32_t defer_eviction;  /* 0 or 1.  1 (H2O selector, contiguous slots, bf16 rows of 128,
-                              query groups of 4 or 8): a fused step whose units each evict at
-                              most one token selects no victim itself; each of its waves
-                              records the best candidate it saw (128 bytes of device state
-                              per unit), and the next fused step's launch reduces those to
-                              the victim -- the same one -- while its first K/V tiles are in
-                              flight, and puts the new token in its slot.  Every other call
-                              that reads or changes the cache (h2o_read_indices,
-                              h2o_read_kv, h2o_step, a bulk step) first applies the pending
-                              eviction (one extra launch on its stream), so every result
-                              equals the non-deferred one; only the slot order and the
-                              rounding order of the attention sums may differ. */
 } h2o_config;
 
 /* Device bytes the context of (cfg, prompt_len) keeps for its state: the K/V

@@ -38,7 +38,7 @@ class H2OConfig(C.Structure):
                 ("budget_den", C.c_int32), ("rand_k", C.c_int32), ("rand_r", C.c_int32),
                 ("seed", C.c_uint64), ("page_size", C.c_int32), ("max_pages", C.c_int32),
                 ("max_len", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64),
-                ("score_decay", C.c_float), ("defer_eviction", C.c_int32)]
+                ("score_decay", C.c_float)]
 
 
 class H2OError(RuntimeError):
@@ -100,13 +100,13 @@ def load_library(path: str = LIB):
 def make_config(*, batch, n_q_heads, n_kv_heads, head_dim, kv_dtype="bf16", score_dtype="f32",
                 scale=0.0, selector="h2o", n_sink=4, budget_fixed=0, hh_fixed=0, budget_num=1,
                 budget_den=5, rand_k=0, rand_r=0, seed=0, page_size=0, max_pages=0,
-                max_len, score_decay=0.0, defer_eviction=0) -> H2OConfig:
+                max_len, score_decay=0.0) -> H2OConfig:
     dt = {"f32": F32, "bf16": BF16, "f64": F64, "i8": I8, "f16": F16}
     return H2OConfig(batch, n_q_heads, n_kv_heads, head_dim, dt[kv_dtype], dt[score_dtype],
                      float(scale), _SELECTORS[selector], n_sink,
                      budget_fixed, hh_fixed, budget_num, budget_den, rand_k, rand_r,
                      int(seed) & 0xFFFFFFFFFFFFFFFF, page_size, max_pages, max_len, None, 0,
-                     float(score_decay), int(defer_eviction))
+                     float(score_decay))
 
 
 def config_from_workload(w, *, max_len, max_pages=0, **over) -> H2OConfig:

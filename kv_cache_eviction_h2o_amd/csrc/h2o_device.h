@@ -907,51 +907,6 @@ __device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n
 template <typename ST>
 using MinT = std::conditional_t<sizeof(ST) == 2, float, ST>;
 
-// The best of lanes 0..7 (the other lanes hold no candidate) under
-// take_better's order, in every lane: three DPP stages within 8 lanes leave
-// it in lane 0, which is then read into scalars.
-template <typename MT>
-__device__ inline void argmin8_bcast(MT& bs, int& bp, int& bj)
-{
-    argmin_step<0xB1>(bs, bp, bj);
-    argmin_step<0x4E>(bs, bp, bj);
-    argmin_step<0x141>(bs, bp, bj);
-    if constexpr (sizeof(MT) == 4) {
-        bs = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bs)));
-    } else {
-        const long long u = __double_as_longlong(bs);
-        const int lo = __builtin_amdgcn_readfirstlane((int)(u & 0xffffffffll));
-        const int hi = __builtin_amdgcn_readfirstlane((int)(u >> 32));
-        bs = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-    }
-    bp = __builtin_amdgcn_readfirstlane(bp);
-    bj = __builtin_amdgcn_readfirstlane(bj);
-}
-
-// The workgroup's best (score, position, slot) under take_better's order from
-// every thread's own best; every thread returns with it.  The waves' bests
-// meet in LDS (s_bs, s_bp, s_bj: one entry per wave); contains one barrier.
-// Lanes 0..NW-1 of every wave take one wave's best, and three DPP stages
-// within 8 lanes leave the workgroup's best in lane 0.
-template <int NT, typename MT>
-__device__ inline void block_argmin(MT& bs, int& bp, int& bj, MT* s_bs, int* s_bp, int* s_bj)
-{
-    constexpr int NW = NT / 64;
-    static_assert(NW <= 8, "cross-wave arg-min covers up to 8 waves");
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    wave_argmin(bs, bp, bj);
-    if (lane == 0) {
-        s_bs[w] = bs;
-        s_bp[w] = bp;
-        s_bj[w] = bj;
-    }
-    lds_barrier();
-    bs = lane < NW ? s_bs[lane] : (MT)INFINITY;
-    bp = lane < NW ? s_bp[lane] : -1;
-    bj = lane < NW ? s_bj[lane] : -1;
-    argmin8_bcast(bs, bp, bj);
-}
-
 // Shared memory of the tail.
 template <typename ST, int NW>
 struct TailSmem {
@@ -988,14 +943,16 @@ struct TailSmem {
 // Attention" (method).
 template <int NT, int G, int PF, typename ST, bool PAGED, typename KV, typename WriteNew>
 __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, TailSmem<ST, NT / 64>& sm,
-                                 int unit, int b, int h, int P, int t, int n, int n_att, int ns, int e,
-                                 bool inplace_new, const float* logit, int lstride, const float (&Mg)[G],
+                                 int unit, int b, int h, int P, int t, int n, int e, bool inplace_new,
+                                 const float* logit, int lstride, const float (&Mg)[G],
                                  const float (&invLg)[G], const ST (&pf_s)[PF], const int (&pf_p)[PF],
-                                 WriteNew write_new, double emass0, bool cand = false)
+                                 WriteNew write_new, double emass0)
 {
+    constexpr int NW = NT / 64;
     const Geometry& gm = a.g;
     const State& S = a.s;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n_att = n + 1;
     const bool h2o = scored(a.sc.selector);
     ST* scp = reinterpret_cast<ST*>(S.sc);
     int32_t* psp = S.ps;
@@ -1011,7 +968,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
         MT bs = (MT)INFINITY;
         int bp = -1, bj = -1;
         // slot j: decay its score and add its weights of this step (summed over
-        // the group; lg = its G logits); the new token (slot ns) starts from
+        // the group; lg = its G logits); the new token (j == n) starts from
         // zero.  With decay 1 the fused multiply-add is the plain sum, rounded once.
         auto visit = [&](int j, ST old, int pos, const float (&lg)[G]) {
             float p = 0.f;
@@ -1020,17 +977,17 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             ST nw;
             if constexpr (sizeof(ST) == 8) nw = fma((double)lam, old, (double)p);
             else nw = (ST)fmaf(lam, (float)old, p);
-            if (j != ns) {
+            if (j < n) {
                 scp[sidx(j)] = nw;
             } else {
                 sm.new_score = nw;
                 if (!inplace_new) {
-                    const size_t si = sidx(ns);
+                    const size_t si = sidx(n);
                     scp[si] = nw;
                     psp[si] = t;
                 }
             }
-            if ((e == 1 || cand) && pos >= lo_c && pos < hi_c) take_better(bs, bp, bj, (MT)nw, pos, j);
+            if (e == 1 && pos >= lo_c && pos < hi_c) take_better(bs, bp, bj, (MT)nw, pos, j);
         };
         auto logits_of = [&](int j, float (&lg)[G]) {
 #pragma unroll
@@ -1042,7 +999,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             if (j < n_att) {
                 float lg[G];
                 logits_of(j, lg);
-                visit(j, j != ns ? pf_s[k] : (ST)0, j != ns ? pf_p[k] : t, lg);
+                visit(j, j < n ? pf_s[k] : (ST)0, j < n ? pf_p[k] : t, lg);
             }
         }
         // the rest four slots at a time (score, position and logits of each
@@ -1066,18 +1023,34 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
                 return r;
             },
             [&](int j, const Slot& r) {
-                if (j != ns) visit(j, r.s, r.p, r.lg);
+                if (j < n) visit(j, r.s, r.p, r.lg);
                 else visit(j, (ST)0, t, r.lg);
             });
-        if (cand) {
-            // deferred eviction: each wave's best candidate, for the next launch
-            wave_argmin(bs, bp, bj);
-            if ((tid & 63) == 0) S.dcand[(size_t)unit * kDeferCands + (tid >> 6)] = DeferCand{(double)bs, bp, bj};
-        }
         if (e == 1) {
-            block_argmin<NT>(bs, bp, bj, sm.bs, sm.bp, sm.bj);
-            const MT vs = bs;
-            const int vj = bj;
+            wave_argmin(bs, bp, bj);
+            if (lane == 0) {
+                sm.bs[w] = bs;
+                sm.bp[w] = bp;
+                sm.bj[w] = bj;
+            }
+            lds_barrier();
+            // lanes 0..NW-1 of every wave take one wave's best; three DPP
+            // stages within 8 lanes leave the workgroup's best in lane 0
+            static_assert(NW <= 8, "cross-wave arg-min covers up to 8 waves");
+            MT vs = lane < NW ? sm.bs[lane] : (MT)INFINITY;
+            int vp = lane < NW ? sm.bp[lane] : -1, vjj = lane < NW ? sm.bj[lane] : -1;
+            argmin_step<0xB1>(vs, vp, vjj);
+            argmin_step<0x4E>(vs, vp, vjj);
+            argmin_step<0x141>(vs, vp, vjj);
+            if constexpr (sizeof(MT) == 4) {
+                vs = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vs)));
+            } else {
+                const long long u = __double_as_longlong(vs);
+                const int lo = __builtin_amdgcn_readfirstlane((int)(u & 0xffffffffll));
+                const int hi = __builtin_amdgcn_readfirstlane((int)(u >> 32));
+                vs = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+            }
+            const int vj = __builtin_amdgcn_readfirstlane(vjj);
             if (vj < 0) {
                 if (tid == 0) atomicOr(S.err, kErrNoCandidate);
                 return;
@@ -1087,7 +1060,7 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
             // wrote its updated score above: same thread, same address, in order
             const bool owner = (vj - tid) % NT == 0;
             if (a.fused) {
-                if (vj != ns) {
+                if (vj != n) {
                     write_new(sidx(vj));
                     if (owner) {
                         scp[sidx(vj)] = sm.new_score;

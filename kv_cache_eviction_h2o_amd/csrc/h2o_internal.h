@@ -80,16 +80,6 @@ struct Geometry {
                     //     contiguous, cap a multiple of 32, GQA group of 4 or 8)
 };
 
-// Deferred eviction: a step that leaves its eviction to the next launch
-// stores, per unit, the best candidate each of its kDeferCands waves saw
-// (score ascending, then the higher position); the next launch reduces them.
-constexpr int kDeferCands = 8;
-struct alignas(16) DeferCand {
-    double s;   // score (exact for every score type)
-    int32_t p;  // position (-1: the wave saw no candidate)
-    int32_t j;  // slot
-};
-
 struct State {  // device pointers owned by the context
     void* kc;          // K rows
     void* vc;          // V rows
@@ -109,7 +99,6 @@ struct State {  // device pointers owned by the context
     float* lscr;       // [B*Hkv][G][cap] logits when they do not fit LDS (or null)
     int32_t* iscr;     // [B*Hkv][2*cap] hole / live lists for bulk compaction
     int32_t* err;      // error bits
-    DeferCand* dcand;  // deferred eviction: [B*Hkv][kDeferCands] (else null)
 };
 
 struct Sched {
@@ -149,12 +138,11 @@ __host__ __device__ inline int evict_count(const Sched& s, int t, int P, int n_a
 // One row of a step launch, read by its workgroups with a single 16-byte
 // load: the sequences go longest first (a workgroup's time grows with its count).
 struct alignas(16) SeqArg {
-    int32_t b;    // the sequence
-    int32_t n;    // its occupied slots before the step
-    int32_t p;    // its prompt length
-    int32_t aux;  // paged: the page for its append slot, or -1 (with pop_stack, the
-                  // free-stack entry that holds it); deferred eviction: the number
-                  // (0 or 1) of the previous step's evictions still to apply
+    int32_t b;        // the sequence
+    int32_t n;        // its retained slots before the step
+    int32_t p;        // its prompt length
+    int32_t newpage;  // paged: the page for its append slot, or -1 (with pop_stack,
+                      // the free-stack entry that holds it)
 };
 
 struct StepArgs {
@@ -171,10 +159,7 @@ struct StepArgs {
     int lds_n;      // logit row stride in LDS (>= max n_att of the launch)
     int npg_lds;    // paged: block-table entries staged in LDS per unit
     int seq_in_args;             // 1: seq below is valid (B <= kMaxArgBatch)
-    int pop_stack;               // 1: SeqArg::aux indexes State::fstack
-    int defer;                   // 1: this step selects no victim; its eviction is applied by
-                                 // the next step's launch (or a finish launch) instead
-    int pending;                 // 1: the previous step's eviction (SeqArg::aux) is applied now
+    int pop_stack;               // 1: SeqArg::newpage indexes State::fstack
     SeqArg seq[kMaxArgBatch];    // row i: the sequence whose units workgroups i * Hkv .. + Hkv take
 };
 
@@ -201,18 +186,6 @@ struct BlockArgs {
 struct CompactArgs {
     Geometry g;
     State s;
-};
-
-// Applying a deferred eviction (finish_kernel): per sequence, its occupied
-// slots, the number of evictions still to apply (0 or 1) and the position
-// appended by the step they belong to.
-struct FinishArgs {
-    Geometry g;
-    State s;
-    Sched sc;
-    int32_t seq_n[kMaxArgBatch];
-    int32_t seq_e[kMaxArgBatch];
-    int32_t seq_t[kMaxArgBatch];
 };
 
 struct LoadArgs {
@@ -295,7 +268,6 @@ constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 // This device's copy of that array (its address looked up once per device).
 hipError_t noalloc_scratch(char** ptr);  // h2o_prefill.hip
 hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
-hipError_t launch_finish(const FinishArgs& a, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 hipError_t launch_gather_rows(const RowGatherArgs& a, hipStream_t st);

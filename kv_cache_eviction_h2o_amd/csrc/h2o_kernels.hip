@@ -72,62 +72,6 @@ __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a
     }
 }
 
-// ------------------------------------------------------ deferred eviction
-// Applies the eviction a deferred step left (mfma_step_kernel with DEFER) when
-// no further step applies it: per unit with one eviction pending, the victim
-// is the arg-min of the scores that step left over its candidates (positions
-// n_sink <= pos < t + 1 - W at its length t + 1, score ascending, the higher
-// position first on equal scores), its score goes to the evicted mass, and
-// the last occupied slot moves into its hole.  One workgroup per unit.
-template <typename ST, typename KV>
-__global__ void __launch_bounds__(kCompactNT) finish_kernel(const FinishArgs a)
-{
-    using MT = MinT<ST>;
-    constexpr int NW = kCompactNT / 64;
-    __shared__ MT s_bs[NW];
-    __shared__ int s_bp[NW], s_bj[NW];
-    const Geometry& gm = a.g;
-    const State& S = a.s;
-    const int unit = blockIdx.x;
-    const int b = unit / gm.Hkv, h = unit - b * gm.Hkv;
-    if (a.seq_e[b] <= 0) return;  // nothing pending for this sequence
-    const int n = a.seq_n[b], t = a.seq_t[b];
-    SlotMap<false> sidx;
-    sidx.base = (size_t)unit * gm.cap;
-    sidx.bt = nullptr;
-    sidx.h = h;
-    sidx.Hkv = gm.Hkv;
-    int K, HH, W;
-    schedule(a.sc, t + 1, K, HH, W);
-    const int lo_c = a.sc.n_sink, hi_c = t + 1 - W;
-    ST* scp = reinterpret_cast<ST*>(S.sc);
-    MT bs = (MT)INFINITY;
-    int bp = -1, bj = -1;
-    for (int j = (int)threadIdx.x; j < n; j += kCompactNT) {
-        const size_t si = sidx(j);
-        const int pos = S.ps[si];
-        if (pos >= lo_c && pos < hi_c) take_better(bs, bp, bj, (MT)scp[si], pos, j);
-    }
-    block_argmin<kCompactNT>(bs, bp, bj, s_bs, s_bp, s_bj);
-    if (bj < 0) {
-        if (threadIdx.x == 0) atomicOr(S.err, kErrNoCandidate);
-        return;
-    }
-    const int v = bj, last = n - 1;
-    if (v != last) {
-        const size_t src = sidx(last), dst = sidx(v);
-        if (threadIdx.x < 16) KV::copy(S, src, dst, (int)threadIdx.x);
-        if (threadIdx.x == 0) {
-            scp[dst] = scp[src];
-            S.ps[dst] = S.ps[src];
-        }
-    }
-    if (threadIdx.x == 0) {
-        S.emass[unit] += (double)bs;
-        S.cnt[unit] = n - 1;
-    }
-}
-
 // ------------------------------------------------------------- prompt load
 template <typename ST, bool PAGED, typename KV>
 __global__ void __launch_bounds__(256) load_kernel(const LoadArgs a)
@@ -260,7 +204,6 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(const RowGatherArgs a)
 hipError_t launch_step(const StepArgs& a, int max_n_att, hipStream_t st)
 {
     if (a.g.kv_tiles) return launch_step_mfma(a, max_n_att, st);
-    if (a.defer) return hipErrorInvalidValue;  // deferred eviction: matrix-core path only
     const bool llds = (size_t)a.g.G * (size_t)max_n_att * 4 <= (size_t)kLogitLdsBytes;
     size_t dyn = 0;
     if (llds) dyn += (size_t)a.g.G * (size_t)a.lds_n * 4;
@@ -319,18 +262,6 @@ struct LoadLaunch {
 hipError_t launch_compact(const CompactArgs& a, int /*max_slots*/, hipStream_t st)
 {
     return launch_by_layout<CompactLaunch>(a, st);
-}
-
-hipError_t launch_finish(const FinishArgs& a, hipStream_t st)
-{
-    if (a.g.paged || a.sc.selector != 0) return hipErrorInvalidValue;  // contiguous H2O only
-    return with_score_type(a.g, [&](auto st_tag) {
-        using ST = decltype(st_tag);
-        if (a.g.kv_i8) return hipErrorInvalidValue;
-        if (a.g.kv_tiles) hipLaunchKernelGGL((finish_kernel<ST, KvTiles>), dim3(a.g.B * a.g.Hkv), dim3(kCompactNT), 0, st, a);
-        else hipLaunchKernelGGL((finish_kernel<ST, KvRows>), dim3(a.g.B * a.g.Hkv), dim3(kCompactNT), 0, st, a);
-        return hipGetLastError();
-    });
 }
 
 hipError_t launch_load(const LoadArgs& a0, int max_prompt, hipStream_t st)

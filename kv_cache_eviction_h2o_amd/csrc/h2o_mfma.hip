@@ -50,14 +50,7 @@ struct MTile {
     uint4 v[8];  // [db]: d 16 db .. +16, the lane group's 8 slots
 };
 
-// DEFER: the step selects no victim of its own; when it evicts one, each
-// wave stores the best candidate it saw (State::dcand) and the next launch
-// applies the eviction.  With a.pending it first applies the previous step's:
-// every wave reduces that step's 8 stored candidates to its victim (the
-// arg-min of the scores it left, over its candidates) while the first tiles
-// are in flight, the victim's old row is masked in the tiles, and the new
-// token's row goes into its slot.
-template <int G, typename ST, bool LLDS, bool DEFER>
+template <int G, typename ST, bool LLDS>
 __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
 {
     static_assert(G == 4 || G == 8, "the matrix-core step takes GQA groups of 4 or 8");
@@ -88,7 +81,7 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
         sa.b = sq;
         sa.n = *reinterpret_cast<const volatile int32_t*>(S.cnt + (size_t)sq * gm.Hkv + h);
         sa.p = *reinterpret_cast<const volatile int32_t*>(S.t0 + sq);
-        sa.aux = -1;
+        sa.newpage = -1;
     }
     const int b = __builtin_amdgcn_readfirstlane(sa.b);
     const int unit = b * gm.Hkv + h;
@@ -104,12 +97,7 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     const int t = P + a.step;
     const int n = __builtin_amdgcn_readfirstlane(sa.n);
     const bool h2o = scored(a.sc.selector);
-    // with DEFER, n counts the previous step's victim (if one is still to go)
-    const int e_prev = DEFER && a.pending && sa.aux > 0 ? 1 : 0;
-    const int e = DEFER ? 0 : evict_count(a.sc, t, P, n + 1);
-    // DEFER: this step's own eviction count (at most 1; the slots it attends
-    // are n + 1 less the previous step's victim)
-    const bool cand_out = DEFER && h2o && evict_count(a.sc, t, P, n + 1 - e_prev) == 1;
+    const int e = evict_count(a.sc, t, P, n + 1);
     const bool inplace_new = a.fused && h2o && e == 1;
 
     float* logit = LLDS ? reinterpret_cast<float*>(dsm) : S.lscr + (size_t)unit * G * gm.cap;
@@ -135,10 +123,6 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     // the unit's evicted mass, for its update at the end: a vector load (a
     // scalar one would hold up the barrier below for a memory round trip)
     const double emass0 = load_f64(S.emass + unit);
-    // the previous step's candidates, one per lane of 0..7 (DEFER, pending)
-    uint4 dc = make_uint4(0u, 0u, 0u, 0u);
-    if (e_prev)
-        dc = buf_load16(make_rsrc(S.dcand + (size_t)unit * kDeferCands, kDeferCands * 16u), (unsigned)lane * 16u);
     // every wave's loads above enter the memory queues before any tile load
     // of the workgroup (the older wave of a SIMD would otherwise issue all of
     // its tile loads first); the barrier waits for none of that data
@@ -195,38 +179,6 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
             qop[kb][i] = head < G ? split_part(x[i] * a.qscale, lo_col) : (__bf16)0.0f;
     }
 
-    // the new token's row into slot index si (staged in LDS above)
-    auto write_new = [&](size_t si) {
-        if (tid < 16) KvTiles::store(S.kc, S.vc, si, tid, kvn_s[tid], kvn_s[kRowVecs + tid]);
-    };
-
-    // the previous step's victim (DEFER with one eviction pending): the best
-    // of the candidates its waves stored (each wave reduces them itself); the
-    // new token then takes the victim's slot (its old row, in the tiles, is
-    // masked below), else it is appended at slot n
-    int vict = -1;
-    MinT<ST> vict_s = 0;
-    if constexpr (DEFER) {
-        if (e_prev) {
-            using MT = MinT<ST>;
-            const bool has = lane < kDeferCands && (int)dc.z >= 0;
-            MT bs = has ? (MT)__longlong_as_double((long long)(((unsigned long long)dc.y << 32) | dc.x)) : (MT)INFINITY;
-            int bp = has ? (int)dc.z : -1, bj = has ? (int)dc.w : -1;
-            argmin8_bcast(bs, bp, bj);
-            if (bj < 0 || bj >= n) {
-                // no candidate (a state the host never schedules): flag it, and
-                // let the last slot stand in so that every write stays below n
-                if (tid == 0) atomicOr(S.err, kErrNoCandidate);
-                bj = n - 1;
-                bs = 0;
-            }
-            vict = bj;
-            vict_s = bs;
-        }
-    }
-    const int ns = vict >= 0 ? vict : n;         // the new token's slot
-    const int n_att = vict >= 0 ? n : n + 1;     // slots attended (the new token's included)
-
     // the new token's logit (every row of the product is that token)
     f32x4 cn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -260,26 +212,24 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
             s[r] = c0[r] + dpp<0x128>(c0[r]);
             s[4 + r] = c1[r] + dpp<0x128>(c1[r]);
         }
-        // slots at or past n take no weight (their K / V may be stale), nor
-        // does a victim whose slot the new token takes; only the unit's last
-        // tile and the victim's hold such slots (wave-uniform tests)
+        // slots at or past n take no weight (their K / V may be stale); only
+        // the unit's last tile holds such slots (a wave-uniform test)
         const int j0 = tl * kTile + 4 * lg;
         const bool last_tile = (tl + 1) * kTile > n;
-        const bool vict_tile = DEFER && vict >= 0 && tl == (vict >> 5);
-        if (last_tile || vict_tile) {
+        if (last_tile) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if (j0 + r >= n || j0 + r == vict) s[r] = -INFINITY;
-                if (j0 + 16 + r >= n || j0 + 16 + r == vict) s[4 + r] = -INFINITY;
+                if (j0 + r >= n) s[r] = -INFINITY;
+                if (j0 + 16 + r >= n) s[4 + r] = -INFINITY;
             }
         }
-        if (h2o && lc < G) {  // the new token's slot (if in this tile) takes its logit
+        if (h2o && lc < G) {  // slot n of this tile (if any) takes the new token's logit
             float4* lp = reinterpret_cast<float4*>(logit + (size_t)lc * lstride + j0);
-            if (last_tile || vict_tile) {
-                lp[0] = make_float4(j0 == ns ? s_new : s[0], j0 + 1 == ns ? s_new : s[1],
-                                    j0 + 2 == ns ? s_new : s[2], j0 + 3 == ns ? s_new : s[3]);
-                lp[4] = make_float4(j0 + 16 == ns ? s_new : s[4], j0 + 17 == ns ? s_new : s[5],
-                                    j0 + 18 == ns ? s_new : s[6], j0 + 19 == ns ? s_new : s[7]);
+            if (last_tile) {
+                lp[0] = make_float4(j0 == n ? s_new : s[0], j0 + 1 == n ? s_new : s[1],
+                                    j0 + 2 == n ? s_new : s[2], j0 + 3 == n ? s_new : s[3]);
+                lp[4] = make_float4(j0 + 16 == n ? s_new : s[4], j0 + 17 == n ? s_new : s[5],
+                                    j0 + 18 == n ? s_new : s[6], j0 + 19 == n ? s_new : s[7]);
             } else {
                 lp[0] = make_float4(s[0], s[1], s[2], s[3]);
                 lp[4] = make_float4(s[4], s[5], s[6], s[7]);
@@ -363,7 +313,7 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
     if (i < cnt) process(ta + 2 * NW * (i / 2), TA);
     if (i + 1 < cnt) process(tb + 2 * NW * (i / 2), TB);
     // slot n outside every tile (n a multiple of 32): its logit slot is free
-    if (h2o && own_new && ns == n && (n % kTile) == 0 && lc < G && lg == 0) logit[(size_t)lc * lstride + n] = s_new;
+    if (h2o && own_new && (n % kTile) == 0 && lc < G && lg == 0) logit[(size_t)lc * lstride + n] = s_new;
 
     // ---- merge: lane groups (sum of l), hi + lo columns, then waves -------
     {
@@ -444,24 +394,19 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
         for (int k = 0; k < EPT; ++k) op[k] = acc[k] * il;
     }
     // the new token's rows go to slot n unless they fill a victim's hole later
-    // (with a deferred victim: into its slot, after the tiles, which mask the
-    // victim's old row whichever of the two rows they read)
-    if (DEFER && vict >= 0) {
-        write_new(sidx(vict));
-        if (tid == 0) S.emass[unit] = emass0 + (double)vict_s;
-    } else if (!inplace_new) {
-        write_new(sidx(n));
-    }
+    auto write_new = [&](size_t si) {  // the new token's row into slot index si
+        if (tid < 16) KvTiles::store(S.kc, S.vc, si, tid, kvn_s[tid], kvn_s[kRowVecs + tid]);
+    };
+    if (!inplace_new) write_new(sidx(n));
 
-    step_tail<NT, G, PF, ST, false, KvTiles>(a, sidx, tsm, unit, b, h, P, t, n, n_att, ns, e, inplace_new,
-                                             logit, lstride, Mg, invLg, pf_s, pf_p, write_new, emass0,
-                                             cand_out);
+    step_tail<NT, G, PF, ST, false, KvTiles>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit,
+                                             lstride, Mg, invLg, pf_s, pf_p, write_new, emass0);
 }
 
-template <int G, typename ST, bool LLDS, bool DEFER>
+template <int G, typename ST, bool LLDS>
 hipError_t launch_mfma_t(const StepArgs& a, size_t dyn, hipStream_t st)
 {
-    auto k = mfma_step_kernel<G, ST, LLDS, DEFER>;
+    auto k = mfma_step_kernel<G, ST, LLDS>;
     static DynLdsLimit lim;
     const hipError_t err = lim.allow((const void*)k, dyn);
     if (err != hipSuccess) return err;
@@ -472,9 +417,7 @@ hipError_t launch_mfma_t(const StepArgs& a, size_t dyn, hipStream_t st)
 template <int G, typename ST>
 hipError_t launch_mfma_g(const StepArgs& a, bool llds, size_t dyn, hipStream_t st)
 {
-    if (a.defer)
-        return llds ? launch_mfma_t<G, ST, true, true>(a, dyn, st) : launch_mfma_t<G, ST, false, true>(a, 0, st);
-    return llds ? launch_mfma_t<G, ST, true, false>(a, dyn, st) : launch_mfma_t<G, ST, false, false>(a, 0, st);
+    return llds ? launch_mfma_t<G, ST, true>(a, dyn, st) : launch_mfma_t<G, ST, false>(a, 0, st);
 }
 
 template <typename ST>
@@ -490,9 +433,6 @@ hipError_t launch_step_mfma(const StepArgs& a0, int max_n_att, hipStream_t st)
     const Geometry& g = a0.g;
     if (!g.kv_tiles || !g.kv_bf16 || g.D != 128 || g.paged || (g.G != 4 && g.G != 8) ||
         (g.cap % kTile) != 0)
-        return hipErrorInvalidValue;
-    // the host defers only fused H2O steps with the sequences in the arguments
-    if (a0.defer && (a0.sc.selector != 0 || !a0.fused || !a0.seq_in_args || !a0.s.dcand))
         return hipErrorInvalidValue;
     StepArgs a = a0;
     a.lds_n = (max_n_att + kTile - 1) / kTile * kTile;  // whole tiles of logits

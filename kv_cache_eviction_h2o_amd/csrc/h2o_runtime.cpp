@@ -35,11 +35,6 @@ struct h2o_ctx {
     int step = 0;             // decode steps completed
     bool pending = false;     // h2o_step done, h2o_compact not yet
     std::vector<int> pend_e;  // e_b of the pending step
-    // deferred eviction (h2o_config::defer_eviction): the last fused step's
-    // evictions (0 or 1 per sequence) are still to be applied -- by the next
-    // deferred step's launch, or by apply_deferred before anything else
-    bool deferred = false;
-    std::vector<int> def_e;
     std::vector<std::vector<int>> pages;  // paged: page ids of each sequence, in slot order
     std::vector<int> free_pages;
     // block eviction: pages are tracked by count (the device stack holds the ids)
@@ -188,14 +183,6 @@ int validate(const h2o_config* c, const int32_t* plen, std::string& why)
         return bad("unknown selector");
     }
     if (c->page_size != 0 && c->page_size != kPageSize) return bad("page_size must be 0 or 16");
-    if (c->defer_eviction != 0 && c->defer_eviction != 1) return bad("defer_eviction must be 0 or 1");
-    if (c->defer_eviction) {
-        if (c->selector != H2O_SEL_H2O || c->page_size)
-            return bad("deferred eviction needs the H2O selector and contiguous slots (page_size 0)");
-        const int G = c->n_kv_heads > 0 ? c->n_q_heads / c->n_kv_heads : 0;
-        if (!bf || c->head_dim != 128 || (G != 4 && G != 8))
-            return bad("deferred eviction runs on the matrix-core step: bf16 rows of 128 and query groups of 4 or 8");
-    }
     if (c->workspace && (reinterpret_cast<uintptr_t>(c->workspace) & 255) != 0)
         return bad("workspace must be 256-byte aligned");
     if (c->page_size) {
@@ -306,27 +293,6 @@ BlockArgs plan_blocks(h2o_ctx* c)
     return ba;
 }
 
-// Applies the evictions the last deferred step left (finish_kernel), so that
-// the device state is the one the non-deferred step would have left.
-int apply_deferred(h2o_ctx* c, void* stream)
-{
-    if (!c->deferred) return H2O_OK;
-    DeviceGuard dg(c->device);
-    FinishArgs fa{};
-    fa.g = c->g;
-    fa.s = c->s;
-    fa.sc = c->sc;
-    for (int b = 0; b < c->g.B; ++b) {
-        fa.seq_n[b] = c->count[b] + c->def_e[b];
-        fa.seq_e[b] = c->def_e[b];
-        fa.seq_t[b] = c->plen[b] + c->step - 1;
-    }
-    const hipError_t err = launch_finish(fa, (hipStream_t)stream);
-    if (err != hipSuccess) return hip_fail(c, err, "deferred eviction launch");
-    c->deferred = false;
-    return H2O_OK;
-}
-
 int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* out, void* stream,
             bool fused)
 {
@@ -346,15 +312,6 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
         e[b] = evict_count(c->sc, t, c->plen[b], n_att);
         max_n_att = std::max(max_n_att, n_att);
     }
-    // deferred eviction: a fused step whose units each evict at most one token
-    // leaves its eviction to the next launch; any other step first applies a
-    // pending one
-    bool defer = fused && c->cfg.defer_eviction && B <= kMaxArgBatch;
-    for (int b = 0; b < B && defer; ++b) defer = e[b] <= 1;
-    if (!defer) {
-        const int rc = apply_deferred(c, stream);
-        if (rc != H2O_OK) return rc;
-    }
     DeviceGuard dg(c->device);
     StepArgs a{};
     a.g = c->g;
@@ -373,8 +330,6 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     for (int i = 0; i < kMaxArgBatch; ++i) newpage[i] = -1;
     a.seq_in_args = B <= kMaxArgBatch ? 1 : 0;
     a.pop_stack = 0;
-    a.defer = defer ? 1 : 0;
-    a.pending = defer && c->deferred ? 1 : 0;
     std::vector<int> got;  // sequences given a page in this call (returned if the launch fails)
     if (c->block) {
         // every block-table entry but the last is full: a sequence needs a page
@@ -415,10 +370,7 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
         std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return c->count[x] > c->count[y]; });
         for (int i = 0; i < B; ++i) {
             const int b = ord[i];
-            if (a.pending)  // the slots still hold the previous step's victim
-                a.seq[i] = SeqArg{b, c->count[b] + c->def_e[b], c->plen[b], c->def_e[b]};
-            else
-                a.seq[i] = SeqArg{b, c->count[b], c->plen[b], newpage[b]};
+            a.seq[i] = SeqArg{b, c->count[b], c->plen[b], newpage[b]};
         }
     }
     hipError_t err = launch_step(a, max_n_att, (hipStream_t)stream);
@@ -451,10 +403,6 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
         for (int b = 0; b < B; ++b) {
             c->count[b] = c->count[b] + 1 - e[b];
             if (c->g.paged) release_pages(c, b);
-        }
-        if (defer) {
-            c->deferred = true;
-            c->def_e = e;
         }
         c->step += 1;
     } else {
@@ -829,9 +777,7 @@ int alloc_state(h2o_ctx* c, size_t slots_total, int32_t** t0, int64_t** poff)
          ((rc = dalloc(c, &s.fstack, (size_t)cfg->max_pages * 4, "alloc free-page stack")) ||
           (rc = dalloc(c, &s.bimp, units * (size_t)bimp_stride(g.maxp), "alloc page importance")))) ||
         ((size_t)g.G * g.cap * 4 > (size_t)kLogitLdsBytes &&
-         (rc = dalloc(c, &s.lscr, units * g.G * (size_t)g.cap * 4, "alloc logit scratch"))) ||
-        (cfg->defer_eviction &&
-         (rc = dalloc(c, &s.dcand, units * kDeferCands * sizeof(DeferCand), "alloc deferred candidates")))) {
+         (rc = dalloc(c, &s.lscr, units * g.G * (size_t)g.cap * 4, "alloc logit scratch")))) {
         return rc;
     }
     return H2O_OK;
@@ -1051,7 +997,6 @@ int h2o_read_indices(h2o_ctx* c, int32_t* pos, int32_t* count, double* scores, d
     for (int b = 0; b < B; ++b) maxc = std::max(maxc, visible_count(c, b));
     if (cap < (size_t)maxc || cap == 0 || cap > (size_t)(1 << 30))
         return fail(c, H2O_EINVAL, "cap is smaller than a retained count");
-    if (const int rc = apply_deferred(c, stream)) return rc;  // a deferred eviction goes first
     DeviceGuard dg(c->device);
     const size_t units = (size_t)B * Hkv;
     int32_t* dpos = nullptr;
@@ -1126,7 +1071,6 @@ int h2o_read_kv(h2o_ctx* c, void* k_rows, void* v_rows, float* k_scale, float* v
     for (int b = 0; b < B; ++b) maxc = std::max(maxc, visible_count(c, b));
     if (cap < (size_t)maxc || cap == 0 || cap > (size_t)(1 << 30))
         return fail(c, H2O_EINVAL, "cap is smaller than a retained count");
-    if (const int rc = apply_deferred(c, stream)) return rc;  // a deferred eviction goes first
     DeviceGuard dg(c->device);
     const size_t units = (size_t)B * Hkv;
     const size_t rb = c->g.kv_i8 ? kRowBytesI8 : kRowBytes;

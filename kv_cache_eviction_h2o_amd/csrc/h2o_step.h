@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         sa.b = sq;
         sa.n = *reinterpret_cast<const volatile int32_t*>(S.cnt + (size_t)sq * gm.Hkv + h);
         sa.p = *reinterpret_cast<const volatile int32_t*>(S.t0 + sq);
-        sa.aux = -1;
+        sa.newpage = -1;
     }
     const int b = __builtin_amdgcn_readfirstlane(sa.b);
     const int unit = b * gm.Hkv + h;
@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         for (int i = tid; i < npg; i += NT) bts[i] = S.bt[(size_t)b * gm.maxp + i];
         if (!inplace_new && (n & (kPageSize - 1)) == 0) {
             // the append page: from the host, or (pop_stack) the free-stack entry it names
-            const int np = sa.aux < 0 ? -1 : (a.pop_stack ? S.fstack[sa.aux] : sa.aux);
+            const int np = sa.newpage < 0 ? -1 : (a.pop_stack ? S.fstack[sa.newpage] : sa.newpage);
             if (np < 0) {  // the host did not provide the append page: do nothing
                 if (tid == 0) atomicOr(S.err, kErrCompact);
                 return;
@@ -414,8 +414,8 @@ __global__ void __launch_bounds__(StepTune<G>::NT) step_kernel(const StepArgs a)
         a.out[((size_t)b * gm.Hq + (size_t)h * G + g) * DR + d] = acc * invLg[g];
     }
 
-    step_tail<NT, G, PF, ST, PAGED, KVL>(a, sidx, tsm, unit, b, h, P, t, n, n_att, n, e, inplace_new, logit,
-                                         lstride, Mg, invLg, pf_s, pf_p, write_new, emass0);
+    step_tail<NT, G, PF, ST, PAGED, KVL>(a, sidx, tsm, unit, b, h, P, t, n, e, inplace_new, logit, lstride,
+                                         Mg, invLg, pf_s, pf_p, write_new, emass0);
 }
 
 // --------------------------------------------------------------- dispatch

@@ -82,12 +82,12 @@ class ParityReport:
     notes: list = field(default_factory=list)
 
 
-def make_cache(w: WL.Workload, lens, n_steps: int, layer: int = 0, init_scores=None, cfg_over=None):
+def make_cache(w: WL.Workload, lens, n_steps: int, layer: int = 0, init_scores=None):
     import torch
     from kv_cache_eviction_h2o_amd import _lib as L
     K, V = S.prompt_kv(w.recipe, layer, lens, w.n_kv_heads)
     max_len = max(lens) + n_steps + 1
-    cfg = L.config_from_workload(w, max_len=max_len, **(cfg_over or {}))
+    cfg = L.config_from_workload(w, max_len=max_len)
     if w.page_size:
         cfg.max_pages = L.pages_needed(lens, n_steps, cfg)
     isc = None
@@ -104,7 +104,7 @@ def _oracle_threads(n_units: int) -> int:
 
 def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=True, layer=0,
                init_scores=None, read_every=1, check_steps=(), check_scores=True, device_inputs=False,
-               stored_rows=True, properties=False, max_swapped=None, cfg_over=None) -> ParityReport:
+               stored_rows=True, properties=False, max_swapped=None) -> ParityReport:
     """Run n_steps on the GPU and in the oracle (for `units`, default all).
 
     Checked steps: every read_every-th, those in check_steps, and the last.
@@ -118,8 +118,6 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
     oracle's victims under the near-tie rule (a check stricter than the rule:
     when scores are far below the absolute gap, as after the bulk first step of
     long prompts, the rule alone would accept any candidate).
-    cfg_over: library configuration fields set on top of the workload's (the
-    oracle's configuration is the workload's either way).
     The oracle steps its units on POSIX threads (orc_step_many) between checked
     steps, and attends them on a thread pool at checked steps."""
     import torch
@@ -136,7 +134,7 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
         from kv_cache_eviction_h2o_amd import metrics as M
         assert init_scores is None
         pk, pv = S.device_prompt_kv(w.recipe, layer, lens, Hkv)
-        cfg = L.config_from_workload(w, max_len=max(lens) + n_steps + 1, **(cfg_over or {}))
+        cfg = L.config_from_workload(w, max_len=max(lens) + n_steps + 1)
         if w.page_size:
             cfg.max_pages = L.pages_needed(lens, n_steps, cfg)
         cache = L.H2OCache(cfg, lens, pk, pv)
@@ -146,7 +144,7 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
         del pk, pv
         cap = int(max(M.retained_counts(w, P, n_steps)["count"].max() for P in lens))
     else:
-        cache, K, V = make_cache(w, lens, n_steps, layer, init_scores, cfg_over)
+        cache, K, V = make_cache(w, lens, n_steps, layer, init_scores)
         cap = cache.info()[0]
     ocfg = O.cfg_from_workload(w)
     orc = {}

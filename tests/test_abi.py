@@ -91,12 +91,6 @@ GOOD = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kv_dtype="bf16", s
     (dict(score_dtype="i8"), "score_dtype"),
     (dict(score_decay=1.5), "score_decay"),
     (dict(score_decay=-0.5), "score_decay"),
-    (dict(defer_eviction=2), "defer_eviction"),
-    (dict(defer_eviction=1, selector="random", rand_k=8, rand_r=8), "H2O selector"),
-    (dict(defer_eviction=1, page_size=16, max_pages=64), "contiguous"),
-    (dict(defer_eviction=1, n_q_heads=4), "matrix-core"),
-    (dict(defer_eviction=1, kv_dtype="f32", head_dim=64), "matrix-core"),
-    (dict(defer_eviction=1, kv_dtype="i8"), "matrix-core"),
     (dict(selector="block", page_size=16, max_pages=64, budget_fixed=0, budget_num=1, budget_den=5,
           max_len=500000), "5120 pages"),
 ])

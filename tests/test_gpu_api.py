@@ -238,42 +238,3 @@ def test_two_threads_drive_two_contexts():
             "import test_gpu_api as t; t._two_thread_check()")
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "two-thread check ok" in r.stdout, (r.stdout[-2000:], r.stderr[-3000:])
-
-
-def test_deferred_eviction_across_calls():
-    """A context with defer_eviction = 1 and one without take the same steps,
-    fused ones mixed with h2o_step + h2o_compact pairs (which first apply a
-    pending eviction); no reads in between.  Outputs agree to rounding order
-    at every step; at the end h2o_read_kv (the first call to see the deferred
-    state) and h2o_read_indices give the same retained tokens and rows."""
-    import torch
-    w = WL.LLAMA_GQA.scaled(batch=2, budget_fixed=200, hh_fixed=96)
-    lens, steps = [230, 199], 60
-    _, mk, qd, kd, vd = _setup(w, lens, steps)
-    _, mkd, _, _, _ = _setup(w, lens, steps, defer_eviction=1)
-    a, d = mk(), mkd()
-    shape = (w.batch, w.n_q_heads, w.head_dim)
-    oa = torch.empty(shape, dtype=torch.float32, device="cuda")
-    od = torch.empty_like(oa)
-    for s in range(steps):
-        for c, o in ((a, oa), (d, od)):
-            if s % 7 == 6:
-                c.step(qd[s], kd[s], vd[s], o)
-                c.compact()
-            else:
-                c.step_compact(qd[s], kd[s], vd[s], o)
-        x, y = oa.cpu().numpy().astype(np.float64), od.cpu().numpy().astype(np.float64)
-        err = np.max(np.abs(x - y)) / max(np.max(np.abs(x)), 1e-30)
-        assert err <= 1e-5, f"step {s}: outputs differ by {err:.3g}"
-    assert a.info() == d.info()
-    kd_rows, vd_rows, _, _ = d.read_kv()
-    ka_rows, va_rows, _, _ = a.read_kv()
-    pa, ca, sa, ea = a.read_indices()
-    pd, cd, sdd, ed = d.read_indices()
-    assert np.array_equal(ca, cd) and np.array_equal(pa, pd)
-    assert np.array_equal(ka_rows, kd_rows) and np.array_equal(va_rows, vd_rows)
-    live = pa >= 0
-    assert np.allclose(sa[live], sdd[live], rtol=1e-5, atol=0)
-    assert np.allclose(ea, ed, rtol=1e-5, atol=0)
-    a.close()
-    d.close()

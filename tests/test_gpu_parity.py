@@ -343,42 +343,3 @@ def test_moving_sum_fp32_fp64_scores(score_dtype):
     assert rep.evictions > 0
     wg = WL.LLAMA_GQA.scaled(batch=1, prompt_len=1100, score_dtype=score_dtype, score_decay=0.995)
     P().run_parity(wg, 60)
-
-
-# ------------------------------------------------ deferred eviction (opt-in)
-@pytest.mark.parametrize("read_every", [1, 5], ids=["read_each_step", "read_every_5"])
-def test_gqa_deferred_eviction(read_every):
-    """defer_eviction = 1 on the 70B layer's group of 8 (fp64 scores): each
-    single eviction is chosen by the next step's launch, or by the flush
-    launch that precedes a read; the bulk first step is not deferred.  With a
-    read every 5 steps, four steps in five take the in-launch path."""
-    w = WL.LLAMA_GQA.scaled(batch=2, prompt_len=1100)
-    rep = P().run_parity(w, 96, read_every=read_every, cfg_over=dict(defer_eviction=1))
-    assert rep.evictions >= 2 * 8 * (73 + 95 // read_every)
-
-
-def test_gqa_deferred_eviction_ragged_group_of_four():
-    """Deferred eviction, groups of 4, fp32 scores, ragged units: one sequence
-    reaches its budget mid-run, one bulk-evicts at the first step (which
-    flushes nothing and is not deferred), one starts evicting at the second
-    step; units pass multiples of the 32-slot tile with a victim in any tile."""
-    w = WL.LLAMA_GQA.scaled(batch=3, n_q_heads=16, n_kv_heads=4, score_dtype="f32",
-                            budget_fixed=200, hh_fixed=96)
-    rep = P().run_parity(w, 80, lens=[150, 260, 199], read_every=3, cfg_over=dict(defer_eviction=1))
-    assert rep.evictions > 0
-
-
-def test_gqa_deferred_eviction_logits_in_global_scratch():
-    # 2600 retained slots (logits past the LDS budget): the stored candidates
-    # cover every slot the tail visits, beyond the prefetched ones
-    w = WL.LLAMA_GQA.scaled(batch=1, budget_fixed=2600, hh_fixed=1300)
-    rep = P().run_parity(w, 24, lens=[2700], read_every=4, cfg_over=dict(defer_eviction=1))
-    assert rep.evictions >= 8 * (100 + 5)
-
-
-def test_f16_gqa_deferred_eviction_flush_path():
-    # binary16 moving sums are checked in lockstep (a read each step): every
-    # deferred eviction is applied by the flush launch
-    w = WL.LLAMA_GQA.scaled(batch=2, prompt_len=1100, score_dtype="f16", score_decay=0.998)
-    rep = P().run_parity(w, 40, cfg_over=dict(defer_eviction=1))
-    assert rep.evictions >= 2 * 8 * (73 + 39)
