@@ -22,7 +22,7 @@
 // column l%16) already is the layout of the P^T B operand, and the V tiles
 // list each lane group's slots in that order, so p never moves between
 // lanes.  K and V tiles are read with wave-wide 16-byte loads of 1 KB each,
-// two tiles in flight per wave.  The new token (slot n, from k_new / v_new)
+// one tile in flight per wave.  The new token (slot n, from k_new / v_new)
 // seeds the running state of wave 0; every wave knows its logit, so the wave
 // that stores the tile holding slot n stores that logit there.  The waves
 // then merge through LDS and the shared tail (h2o_device.h) accumulates
@@ -144,10 +144,8 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
 #pragma unroll
         for (int i = 0; i < 8; ++i) T.v[i] = buf_load16(rv, base + (unsigned)i * 1024u);
     };
-    MTile TA, TB;
-    int ta = w, tb = w + NW;
-    load_tile(ta, TA);
-    load_tile(tb, TB);
+    MTile T;
+    load_tile(w, T);
     __builtin_amdgcn_sched_barrier(0);
 
 
@@ -282,18 +280,16 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
         for (int db = 0; db < 8; ++db) O[db] = mma(as_bf16x8(T.v[db]), pb, O[db]);
     };
 
-    // two tiles in flight: the registers of the tile just consumed take the
-    // tile after next; the tail is peeled so the loop holds no conditional load
+    // one tile in flight per wave (eight per workgroup): the registers of the
+    // tile just consumed take the wave's next; the last tile is peeled so the
+    // loop holds no conditional load.  Two per wave streamed slower: the
+    // CU's memory queue only grows, and the first tiles arrive later.
     const int cnt = w < ntiles ? (ntiles - 1 - w) / NW + 1 : 0;  // this wave's tiles
     int i = 0;
-    for (; i + 2 < cnt; i += 2) {
-        process(ta + 2 * NW * (i / 2), TA);
+    for (; i + 1 < cnt; ++i) {
+        process(w + NW * i, T);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(ta + 2 * NW * (i / 2 + 1), TA);
-        __builtin_amdgcn_sched_barrier(0);
-        process(tb + 2 * NW * (i / 2), TB);
-        __builtin_amdgcn_sched_barrier(0);
-        load_tile(tb + 2 * NW * (i / 2 + 1), TB);
+        load_tile(w + NW * (i + 1), T);
         __builtin_amdgcn_sched_barrier(0);
     }
     // scores and positions of this thread's first PF phase-2 slots, requested
@@ -310,8 +306,7 @@ __global__ void __launch_bounds__(kMNT) mfma_step_kernel(const StepArgs a)
             pf_p[k] = psp[si];
         }
     }
-    if (i < cnt) process(ta + 2 * NW * (i / 2), TA);
-    if (i + 1 < cnt) process(tb + 2 * NW * (i / 2), TB);
+    if (i < cnt) process(w + NW * i, T);
     // slot n outside every tile (n a multiple of 32): its logit slot is free
     if (h2o && own_new && (n % kTile) == 0 && lc < G && lg == 0) logit[(size_t)lc * lstride + n] = s_new;
 
