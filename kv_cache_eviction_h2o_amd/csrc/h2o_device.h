@@ -176,6 +176,16 @@ __device__ inline uint2 stream_load(const uint2* p)
     return make_uint2(x[0], x[1]);
 }
 __device__ inline float stream_load(const float* p) { return __builtin_nontemporal_load(p); }
+// Non-temporal stores, for rows written once and not read again by the same
+// launch (the moves of a compaction).
+__device__ inline void stream_store(uint4* p, const uint4& v)
+{
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+__device__ inline void stream_store(uint2* p, const uint2& v)
+{
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
 
 // Barrier for exchanges through LDS only: waits for this wave's LDS accesses,
 // not for its global stores (which __syncthreads' release fence would wait for).
@@ -694,18 +704,21 @@ struct KvRows {
         K[kvec(dst, c)] = K[kvec(src, c)];
         V[kvec(dst, c)] = V[kvec(src, c)];
     }
-    // copy split in two, so several moves' loads can be in flight
+    // copy split in two, so several moves' loads can be in flight; the rows
+    // moved are read and written once, with the non-temporal policy (paged
+    // bulk first step 10.6 -> 9.8 ms)
     struct Chunk {
         uint4 k, v;
     };
     __device__ static inline Chunk fetch(const State& S, size_t si, int c)
     {
-        return {reinterpret_cast<const uint4*>(S.kc)[kvec(si, c)], reinterpret_cast<const uint4*>(S.vc)[kvec(si, c)]};
+        return {stream_load(reinterpret_cast<const uint4*>(S.kc) + kvec(si, c)),
+                stream_load(reinterpret_cast<const uint4*>(S.vc) + kvec(si, c))};
     }
     __device__ static inline void put(const State& S, size_t si, int c, const Chunk& x)
     {
-        reinterpret_cast<uint4*>(S.kc)[kvec(si, c)] = x.k;
-        reinterpret_cast<uint4*>(S.vc)[kvec(si, c)] = x.v;
+        stream_store(reinterpret_cast<uint4*>(S.kc) + kvec(si, c), x.k);
+        stream_store(reinterpret_cast<uint4*>(S.vc) + kvec(si, c), x.v);
     }
 };
 
@@ -730,16 +743,16 @@ struct KvRows8 {
     __device__ static inline Chunk fetch(const State& S, size_t si, int c)
     {
         Chunk x;
-        x.k = reinterpret_cast<const uint2*>(S.kc)[kvec(si, c)];
-        x.v = reinterpret_cast<const uint2*>(S.vc)[kvec(si, c)];
+        x.k = stream_load(reinterpret_cast<const uint2*>(S.kc) + kvec(si, c));
+        x.v = stream_load(reinterpret_cast<const uint2*>(S.vc) + kvec(si, c));
         x.ks = c == 0 ? S.kss[si] : 0.f;
         x.vs = c == 0 ? S.vss[si] : 0.f;
         return x;
     }
     __device__ static inline void put(const State& S, size_t si, int c, const Chunk& x)
     {
-        reinterpret_cast<uint2*>(S.kc)[kvec(si, c)] = x.k;
-        reinterpret_cast<uint2*>(S.vc)[kvec(si, c)] = x.v;
+        stream_store(reinterpret_cast<uint2*>(S.kc) + kvec(si, c), x.k);
+        stream_store(reinterpret_cast<uint2*>(S.vc) + kvec(si, c), x.v);
         if (c == 0) {
             S.kss[si] = x.ks;
             S.vss[si] = x.vs;
@@ -814,7 +827,7 @@ struct KvTiles {
     __device__ static inline Chunk fetch(const State& S, size_t si, int c)
     {
         Chunk x;
-        x.k = reinterpret_cast<const uint4*>(S.kc)[kvec(si, c)];
+        x.k = stream_load(reinterpret_cast<const uint4*>(S.kc) + kvec(si, c));
         const unsigned short* V = reinterpret_cast<const unsigned short*>(S.vc);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x.v[e] = V[velem(si, 8 * c + e)];
@@ -822,7 +835,7 @@ struct KvTiles {
     }
     __device__ static inline void put(const State& S, size_t si, int c, const Chunk& x)
     {
-        reinterpret_cast<uint4*>(S.kc)[kvec(si, c)] = x.k;
+        stream_store(reinterpret_cast<uint4*>(S.kc) + kvec(si, c), x.k);
         unsigned short* V = reinterpret_cast<unsigned short*>(S.vc);
 #pragma unroll
         for (int e = 0; e < 8; ++e) V[velem(si, 8 * c + e)] = x.v[e];
