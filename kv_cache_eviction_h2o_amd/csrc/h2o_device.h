@@ -842,25 +842,26 @@ struct KvTiles {
     }
 };
 
-// In-place compaction of one unit: live slots of [n2, n_att) move into the
-// holes (ps == -1) of [0, n2), n2 = n_att - e.  Sources and destinations are
-// disjoint, so every move is independent.  Contains barriers.
+// In-place compaction of one unit: the live slots (ps >= 0) of [l0, l1) and
+// then of [l2, l3) move into the holes (ps == -1) of [0, h_end) -- for plain
+// compaction [n2, n_att) into [0, n2), n2 = n_att - e.  Sources and
+// destinations are disjoint, so every move is independent.  Contains barriers.
 // Unroll of the hole fill's list collection (rounds of NT * kCollectUnroll slots).
 constexpr int kCollectUnroll = 16;
 
 template <int NT, typename ST, typename KV, typename SlotFn>
-__device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int n_att, int e,
-                           bool has_scores, OrderSmem<NT, kCollectUnroll>& os)
+__device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int h_end, int l0, int l1, int l2,
+                           int l3, bool has_scores, OrderSmem<NT, kCollectUnroll>& os)
 {
-    const int n2 = n_att - e;
     int32_t* hl = s.iscr + (size_t)unit * 2 * cap;
     int32_t* ll = hl + cap;
     int32_t* ps = s.ps;
     auto pos_at = [&](int j) { return ps[sidx(j)]; };
     // both lists in ascending slot order: the moves of one round then read and
     // write neighbouring rows (a few pages), not rows spread over the pool
-    const int nh = collect_ordered<NT, kCollectUnroll>(0, n2, pos_at, [](int p) { return p < 0; }, hl, os);
-    const int nl = collect_ordered<NT, kCollectUnroll>(n2, n_att, pos_at, [](int p) { return p >= 0; }, ll, os);
+    const int nh = collect_ordered<NT, kCollectUnroll>(0, h_end, pos_at, [](int p) { return p < 0; }, hl, os);
+    int nl = collect_ordered<NT, kCollectUnroll>(l0, l1, pos_at, [](int p) { return p >= 0; }, ll, os);
+    if (l2 < l3) nl += collect_ordered<NT, kCollectUnroll>(l2, l3, pos_at, [](int p) { return p >= 0; }, ll + nl, os);
     __syncthreads();
     if (nh != nl) {
         if (threadIdx.x == 0) atomicOr(s.err, kErrCompact);
@@ -1194,8 +1195,13 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
     }
     if (a.fused) {
         __syncthreads();
-        fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, h2o, sm.ord);
-        if (tid == 0) S.cnt[unit] = n_att - e;
+        const int n2 = n_att - e;
+        WindowRemap r;
+        if (PAGED && a.remap && window_remap(a.sc, t, n_att, e, r))  // the host relinks the pages
+            fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, r.front, r.front, r.src, r.src + r.m, n_att, h2o, sm.ord);
+        else
+            fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, n2, n2, n_att, n_att, n_att, h2o, sm.ord);
+        if (tid == 0) S.cnt[unit] = n2;
     } else if (tid == 0) {
         S.vinfo[2 * unit] = e;
         S.vinfo[2 * unit + 1] = -1;

@@ -135,6 +135,35 @@ __host__ __device__ inline int evict_count(const Sched& s, int t, int P, int n_a
     return (n_att - P == s.rand_k + s.rand_r) ? s.rand_r : 0;
 }
 
+// Bulk compaction of a paged H2O unit whose slots still hold the positions in
+// order (the first decode step): the recent window's whole pages stay where
+// they are and are linked in after a front of whole pages, so only the heavy
+// hitters past the front, and at most 15 window rows at each end of the
+// window, move.  The front, slots [0, front), keeps its survivors and takes
+// every moved row; the window rows [src, src + m) become slots
+// [front, front + m) by relinking their pages.  front and src are multiples
+// of the page size, and the relinked pages do not overlap their destination
+// entries of the block table.  False: plain compaction into [0, n_att - e).
+struct WindowRemap {
+    int front;  // slots kept in place (whole pages)
+    int src;    // first window slot on a page boundary
+    int m;      // window rows linked in
+};
+__host__ __device__ inline bool window_remap(const Sched& s, int t, int n_att, int e, WindowRemap& r)
+{
+    if (s.selector != kSelH2O) return false;
+    int K, HH, W;
+    schedule(s, t + 1, K, HH, W);
+    if (W < 32 || e < 64 || e < 2 * W) return false;
+    const int n2 = n_att - e;
+    const int A = n_att - W;  // the window's first slot: positions t + 1 - W .. t
+    r.src = (A + kPageSize - 1) & ~(kPageSize - 1);
+    r.front = (r.src - e + kPageSize - 1) / kPageSize * kPageSize;  // r.src - e >= n_sink + HH >= 0
+    r.m = n2 - r.front;
+    const int pages = (r.m + kPageSize - 1) / kPageSize;
+    return r.m > 0 && r.m <= n_att - r.src && r.src - r.front >= pages * kPageSize;
+}
+
 // One row of a step launch, read by its workgroups with a single 16-byte
 // load: the sequences go longest first (a workgroup's time grows with its count).
 struct alignas(16) SeqArg {
@@ -160,6 +189,8 @@ struct StepArgs {
     int npg_lds;    // paged: block-table entries staged in LDS per unit
     int seq_in_args;             // 1: seq below is valid (B <= kMaxArgBatch)
     int pop_stack;               // 1: SeqArg::newpage indexes State::fstack
+    int remap;                   // 1: the first decode step of paged H2O: bulk compaction
+                                 // keeps the window's pages (window_remap)
     SeqArg seq[kMaxArgBatch];    // row i: the sequence whose units workgroups i * Hkv .. + Hkv take
 };
 
@@ -268,6 +299,15 @@ constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 // This device's copy of that array (its address looked up once per device).
 hipError_t noalloc_scratch(char** ptr);  // h2o_prefill.hip
 hipError_t launch_compact(const CompactArgs& a, int max_slots, hipStream_t st);
+// Relinking the window pages after a window_remap compaction: per sequence,
+// block-table entries [front, front + cnt) take entries [src, src + cnt).
+struct RemapArgs {
+    int32_t* bt;
+    int maxp;
+    int nseq;
+    int32_t seq_b[kMaxArgBatch], seq_front[kMaxArgBatch], seq_src[kMaxArgBatch], seq_cnt[kMaxArgBatch];
+};
+hipError_t launch_remap(const RemapArgs& a, hipStream_t st);
 hipError_t launch_load(const LoadArgs& a, int max_prompt, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 hipError_t launch_gather_rows(const RowGatherArgs& a, hipStream_t st);

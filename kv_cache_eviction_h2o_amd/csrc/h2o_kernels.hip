@@ -62,7 +62,8 @@ __global__ void __launch_bounds__(kCompactNT) compact_kernel(const CompactArgs a
             }
         }
     } else {
-        fill_holes<kCompactNT, ST, KV>(S, sidx, unit, gm.cap, n_att, e, has_scores, s_ord);
+        fill_holes<kCompactNT, ST, KV>(S, sidx, unit, gm.cap, n_att - e, n_att - e, n_att, n_att, n_att, has_scores,
+                                       s_ord);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -262,6 +263,26 @@ struct LoadLaunch {
 hipError_t launch_compact(const CompactArgs& a, int /*max_slots*/, hipStream_t st)
 {
     return launch_by_layout<CompactLaunch>(a, st);
+}
+
+// ------------------------------------------------------------ page relink
+// After a window_remap compaction (every head of the sequence done, so no
+// workgroup still reads the old entries): entries [front, front + cnt) of the
+// sequence's block-table row take entries [src, src + cnt).  The two ranges
+// are disjoint (window_remap), so the copy is one parallel pass.
+__global__ void __launch_bounds__(256) remap_kernel(const RemapArgs a)
+{
+    const int i = blockIdx.x;
+    int32_t* row = a.bt + (size_t)a.seq_b[i] * a.maxp;
+    const int f = a.seq_front[i], src = a.seq_src[i], cnt = a.seq_cnt[i];
+    for (int k = (int)threadIdx.x; k < cnt; k += 256) row[f + k] = row[src + k];
+}
+
+hipError_t launch_remap(const RemapArgs& a, hipStream_t st)
+{
+    if (a.nseq <= 0 || a.nseq > kMaxArgBatch || !a.bt) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(remap_kernel, dim3(a.nseq), dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_load(const LoadArgs& a0, int max_prompt, hipStream_t st)

@@ -330,6 +330,12 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
     for (int i = 0; i < kMaxArgBatch; ++i) newpage[i] = -1;
     a.seq_in_args = B <= kMaxArgBatch ? 1 : 0;
     a.pop_stack = 0;
+    // the first fused step of paged H2O keeps the recent window's pages where
+    // they are (window_remap) and relinks them after the step
+    a.remap = (c->g.paged && !c->block && fused && c->sc.selector == H2O_SEL_H2O && c->step == 0 &&
+               B <= kMaxArgBatch)
+                  ? 1
+                  : 0;
     std::vector<int> got;  // sequences given a page in this call (returned if the launch fails)
     if (c->block) {
         // every block-table entry but the last is full: a sequence needs a page
@@ -400,10 +406,35 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
         return H2O_OK;
     }
     if (fused) {
+        RemapArgs ra{};
+        ra.bt = c->s.bt;
+        ra.maxp = c->g.maxp;
         for (int b = 0; b < B; ++b) {
+            WindowRemap r;
+            if (a.remap && window_remap(c->sc, c->plen[b] + c->step, c->count[b] + 1, e[b], r)) {
+                // the mirror of the relinked row: the front pages, then the
+                // window's; the pages in between and after go back to the pool
+                auto& pg = c->pages[b];
+                const int f = r.front >> kPageShift, src = r.src >> kPageShift;
+                const int cnt = (r.m + kPageSize - 1) >> kPageShift;
+                if ((size_t)(src + cnt) > pg.size())  // cannot happen: the window lies in the row
+                    return fail(c, H2O_EDEVICE, "page relink out of range");
+                std::vector<int> kept(pg.begin(), pg.begin() + f);
+                kept.insert(kept.end(), pg.begin() + src, pg.begin() + src + cnt);
+                for (int k = (int)pg.size() - 1; k >= 0; --k)
+                    if (k >= src + cnt || (k >= f && k < src)) c->free_pages.push_back(pg[k]);
+                pg.swap(kept);
+                ra.seq_b[ra.nseq] = b;
+                ra.seq_front[ra.nseq] = f;
+                ra.seq_src[ra.nseq] = src;
+                ra.seq_cnt[ra.nseq] = cnt;
+                ++ra.nseq;
+            }
             c->count[b] = c->count[b] + 1 - e[b];
             if (c->g.paged) release_pages(c, b);
         }
+        if (ra.nseq > 0 && (err = launch_remap(ra, (hipStream_t)stream)) != hipSuccess)
+            return hip_fail(c, err, "page relink launch");
         c->step += 1;
     } else {
         c->pending = true;

@@ -125,6 +125,15 @@ def test_paged_mixed_reduced():
     P().run_parity(w, 40, lens=[300, 517, 1024, 2000])
 
 
+def test_paged_first_step_window_relink():
+    # the first fused step keeps the recent window's pages and relinks them
+    # (window W >= 32, e >= 2W); prompts around W = 31 / 32 / 33 and around
+    # page boundaries of the window's first slot and of n2, checked every step
+    w = WL.PAGED_MIXED.scaled(batch=8, n_q_heads=2, n_kv_heads=2)
+    rep = P().run_parity(w, 24, lens=[330, 334, 335, 343, 350, 1023, 1024, 1025], properties=True)
+    assert rep.evictions > 0
+
+
 def test_paged_mixed_reduced_unfused():
     w = WL.PAGED_MIXED.scaled(batch=3, n_q_heads=2, n_kv_heads=2)
     P().run_parity(w, 40, lens=[64, 255, 1500], fused=False)
