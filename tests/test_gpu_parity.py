@@ -132,6 +132,12 @@ def test_paged_first_step_window_relink():
     w = WL.PAGED_MIXED.scaled(batch=8, n_q_heads=2, n_kv_heads=2)
     rep = P().run_parity(w, 24, lens=[330, 334, 335, 343, 350, 1023, 1024, 1025], properties=True)
     assert rep.evictions > 0
+    # a fixed budget (window 100) and prefill-style initial scores
+    wf = WL.PAGED_MIXED.scaled(batch=2, n_q_heads=2, n_kv_heads=2, budget_fixed=200, hh_fixed=96)
+    lens = [700, 1201]
+    init = np.random.default_rng(11).random((sum(lens), wf.n_kv_heads)) * 0.25
+    rep = P().run_parity(wf, 16, lens=lens, init_scores=init)
+    assert rep.evictions >= 2 * (501 + 1001)
 
 
 def test_paged_mixed_reduced_unfused():
