@@ -336,6 +336,15 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
                B <= kMaxArgBatch)
                   ? 1
                   : 0;
+    std::vector<char> relink(B, 0);
+    std::vector<WindowRemap> rmap(B);
+    for (int b = 0; b < B && a.remap; ++b) {
+        relink[b] = window_remap(c->sc, c->plen[b] + c->step, c->count[b] + 1, e[b], rmap[b]) ? 1 : 0;
+        // the window lies in the row (its pages, the appended one included, exist)
+        const size_t rows = (size_t)((c->count[b] + 1 + kPageSize - 1) >> kPageShift);
+        if (relink[b] && (size_t)((rmap[b].src + rmap[b].m + kPageSize - 1) >> kPageShift) > rows)
+            return fail(c, H2O_EDEVICE, "page relink out of range");
+    }
     std::vector<int> got;  // sequences given a page in this call (returned if the launch fails)
     if (c->block) {
         // every block-table entry but the last is full: a sequence needs a page
@@ -410,15 +419,13 @@ int do_step(h2o_ctx* c, const float* q, const void* kn, const void* vn, float* o
         ra.bt = c->s.bt;
         ra.maxp = c->g.maxp;
         for (int b = 0; b < B; ++b) {
-            WindowRemap r;
-            if (a.remap && window_remap(c->sc, c->plen[b] + c->step, c->count[b] + 1, e[b], r)) {
+            if (relink[b]) {
                 // the mirror of the relinked row: the front pages, then the
                 // window's; the pages in between and after go back to the pool
+                const WindowRemap& r = rmap[b];
                 auto& pg = c->pages[b];
                 const int f = r.front >> kPageShift, src = r.src >> kPageShift;
                 const int cnt = (r.m + kPageSize - 1) >> kPageShift;
-                if ((size_t)(src + cnt) > pg.size())  // cannot happen: the window lies in the row
-                    return fail(c, H2O_EDEVICE, "page relink out of range");
                 std::vector<int> kept(pg.begin(), pg.begin() + f);
                 kept.insert(kept.end(), pg.begin() + src, pg.begin() + src + cnt);
                 for (int k = (int)pg.size() - 1; k >= 0; --k)
