@@ -37,11 +37,39 @@ SOURCE_FLAGS = {"h2o_prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-v
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    # the compiler's per-kernel resource report (registers, scratch, occupancy)
+    # is kept beside the object: a kernel that spills to scratch is a regression
+    remarks = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *remarks, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
+    if remarks:
+        with open(obj + ".resources.txt", "w") as f:
+            f.write(r.stderr)
     return obj
+
+
+def kernel_resources() -> dict:
+    """{kernel symbol: {"vgprs", "scratch", "occupancy"}} from the last build's reports."""
+    import re
+    out = {}
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        path = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o.resources.txt")
+        cur = None
+        for line in open(path):
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                cur = out.setdefault(m.group(1), {})
+                continue
+            for key, pat in (("vgprs", r" VGPRs: (\d+)"), ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                             ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)")):
+                m = re.search(pat, line)
+                if m and cur is not None:
+                    cur[key] = int(m.group(1))
+    return out
 
 
 def build(verbose: bool = False) -> str:

@@ -850,8 +850,10 @@ struct KvTiles {
 constexpr int kCollectUnroll = 16;
 
 template <int NT, typename ST, typename KV, typename SlotFn>
-__device__ void fill_holes(const State& s, SlotFn sidx, int unit, int cap, int h_end, int l0, int l1, int l2,
-                           int l3, bool has_scores, OrderSmem<NT, kCollectUnroll>& os)
+__device__ __attribute__((always_inline)) inline void fill_holes(const State& s, SlotFn sidx, int unit, int cap,
+                                                                 int h_end, int l0, int l1, int l2, int l3,
+                                                                 bool has_scores,
+                                                                 OrderSmem<NT, kCollectUnroll>& os)
 {
     int32_t* hl = s.iscr + (size_t)unit * 2 * cap;
     int32_t* ll = hl + cap;
@@ -954,9 +956,11 @@ struct TailSmem {
 // score; sinks, heavy hitters and recent window) and sec. 6.2 (compressed
 // score state: FP16 storage, a moving average instead of the exact sum),
 // "H2O: Heavy-Hitter Oracle" (greedy eviction under budget K), "Random
-// Attention" (method).
+// Attention" (method).  Always inlined: a call would take the address of the
+// launch's argument block, which the compiler then copies to scratch memory.
 template <int NT, int G, int PF, typename ST, bool PAGED, typename KV, typename WriteNew>
-__device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, TailSmem<ST, NT / 64>& sm,
+__device__ __attribute__((always_inline)) inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx,
+                                 TailSmem<ST, NT / 64>& sm,
                                  int unit, int b, int h, int P, int t, int n, int e, bool inplace_new,
                                  const float* logit, int lstride, const float (&Mg)[G],
                                  const float (&invLg)[G], const ST (&pf_s)[PF], const int (&pf_p)[PF],
@@ -1196,11 +1200,16 @@ __device__ inline void step_tail(const StepArgs& a, const SlotMap<PAGED>& sidx, 
     if (a.fused) {
         __syncthreads();
         const int n2 = n_att - e;
+        // holes of [0, h_end) take the live slots of [l0, l1) and [l2, l3)
+        int h_end = n2, l0 = n2, l1 = n_att, l2 = n_att;
         WindowRemap r;
-        if (PAGED && a.remap && window_remap(a.sc, t, n_att, e, r))  // the host relinks the pages
-            fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, r.front, r.front, r.src, r.src + r.m, n_att, h2o, sm.ord);
-        else
-            fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, n2, n2, n_att, n_att, n_att, h2o, sm.ord);
+        if (PAGED && a.remap && window_remap(a.sc, t, n_att, e, r)) {  // the host relinks the pages
+            h_end = r.front;
+            l0 = r.front;
+            l1 = r.src;
+            l2 = r.src + r.m;
+        }
+        fill_holes<NT, ST, KV>(S, sidx, unit, gm.cap, h_end, l0, l1, l2, n_att, h2o, sm.ord);
         if (tid == 0) S.cnt[unit] = n2;
     } else if (tid == 0) {
         S.vinfo[2 * unit] = e;

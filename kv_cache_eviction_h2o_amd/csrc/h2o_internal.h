@@ -110,7 +110,7 @@ struct Sched {
 };
 
 // Budget K_t, heavy hitters HH_t and recent window W_t at length len = t + 1.
-__host__ __device__ inline void schedule(const Sched& s, int len, int& K, int& HH, int& W)
+__host__ __device__ __attribute__((always_inline)) inline void schedule(const Sched& s, int len, int& K, int& HH, int& W)
 {
     if (s.budget_fixed > 0) {
         K = s.budget_fixed;
@@ -124,7 +124,7 @@ __host__ __device__ inline void schedule(const Sched& s, int len, int& K, int& H
 
 // Tokens to evict at the step that appends position t, with n_att retained
 // slots after the append and prompt length P.
-__host__ __device__ inline int evict_count(const Sched& s, int t, int P, int n_att)
+__host__ __device__ __attribute__((always_inline)) inline int evict_count(const Sched& s, int t, int P, int n_att)
 {
     if (s.selector == kSelH2O) {
         int K, HH, W;
@@ -149,7 +149,7 @@ struct WindowRemap {
     int src;    // first window slot on a page boundary
     int m;      // window rows linked in
 };
-__host__ __device__ inline bool window_remap(const Sched& s, int t, int n_att, int e, WindowRemap& r)
+__host__ __device__ __attribute__((always_inline)) inline bool window_remap(const Sched& s, int t, int n_att, int e, WindowRemap& r)
 {
     if (s.selector != kSelH2O) return false;
     int K, HH, W;
