@@ -537,16 +537,17 @@ __device__ inline void snap_head(const SnapArgs& a, int hq, int Pp, int64_t off,
 }
 
 // The window's positions added to the unit's bitmap, then the kept positions
-// in ascending order, -1 past the count.
-__device__ inline void snap_finish(const SnapArgs& a, int unit, int P, int Pp, unsigned* bits, ScanSmem& s_scan)
+// in ascending order, -1 past the count (NT threads).
+template <int NT, typename SA>
+__device__ inline void snap_finish(const SA& a, int unit, int P, int Pp, unsigned* bits, ScanSmem& s_scan)
 {
     const int tid = threadIdx.x;
-    for (int j = Pp + tid; j < P; j += kSNT) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    for (int j = Pp + tid; j < P; j += NT) atomicOr(&bits[j >> 5], 1u << (j & 31));
     __syncthreads();
     int* out = a.kept + (size_t)unit * a.cap;
-    const int n = collect<kSNT>(0, P, [&](int j) { return ((bits[j >> 5] >> (j & 31)) & 1u) != 0; }, out,
-                                s_scan);
-    for (int i = n + tid; i < a.cap; i += kSNT) out[i] = -1;
+    const int n = collect<NT>(0, P, [&](int j) { return ((bits[j >> 5] >> (j & 31)) & 1u) != 0; }, out,
+                              s_scan);
+    for (int i = n + tid; i < a.cap; i += NT) out[i] = -1;
     if (tid == 0) a.count[unit] = n;
 }
 
@@ -566,7 +567,7 @@ __global__ void __launch_bounds__(kSNT) snapkv_select_kernel(const SnapArgs a)
     for (int i = tid; i < nw; i += kSNT) bits[i] = 0u;
     __syncthreads();
     for (int g = 0; g < a.G; ++g) snap_head(a, h * a.G + g, Pp, off, Pp <= a.stage_n, stage, bits, s_rad);
-    snap_finish(a, unit, P, Pp, bits, s_scan);
+    snap_finish<kSNT>(a, unit, P, Pp, bits, s_scan);
 }
 
 // G > 1, first kernel: one workgroup per (unit, query head) selects that
@@ -607,7 +608,392 @@ __global__ void __launch_bounds__(kSNT) snapkv_union_kernel(const SnapArgs a)
         bits[i] = x;
     }
     __syncthreads();
-    snap_finish(a, unit, P, Pp, bits, s_scan);
+    snap_finish<kSNT>(a, unit, P, Pp, bits, s_scan);
+}
+
+// ------------------------------------------------------- SnapKV in one pass
+// Groups of one query head, prompts up to kFusedP positions, observation
+// windows of at most 32 rows: one workgroup per unit reads the unit's K once
+// (the two column-sum passes read it twice and hand the row statistics and
+// the votes over through memory).  Wave v holds the window rows' logits for
+// keys 128 v .. 128 v + 127 in registers (8 tiles of 16 keys, the same
+// matrix-core products as the rows pass); the workgroup merges each row's
+// softmax maximum and sum over the waves in LDS, and each key's vote is the
+// sum over the window rows of its weight (fp32 per query tile, fp64 across
+// them, as the columns pass sums).  The prefix's votes go straight into LDS,
+// from which the selection pools into registers (snap_head_small).
+constexpr int kFNT = 512;                   // threads (8 waves)
+constexpr int kFKT = 8;                     // 16-key tiles per wave
+constexpr int kFusedP = (kFNT / 64) * kFKT * 16;  // 1024 positions
+constexpr int kFQT = 4;                     // query tiles of 8 window rows: 32 rows
+constexpr float kMaskLogit = -1e30f;        // finite: this file assumes no NaN or infinity arithmetic
+
+// Inclusive prefix sum over a wave: DPP row shifts within each row of 16
+// lanes, then row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into
+// rows 2 and 3).
+template <int CTRL, int ROW_MASK>
+__device__ inline unsigned dpp_src(unsigned v)
+{
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ inline unsigned wave_incl_scan(unsigned v)
+{
+    v += dpp_src<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_src<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_src<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_src<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_src<0x142, 0xA>(v);  // row_bcast:15
+    v += dpp_src<0x143, 0xC>(v);  // row_bcast:31
+    return v;
+}
+
+// Selection of the e smallest of n <= NT KPT keys held in registers, element
+// tid + NT i in slot i of thread tid, each key (w2, w1, ~index) as the decode
+// step's and radix_select's (96 bits, unique): the same 8-bit digits from the
+// top, the same early stop (once the chosen bin holds exactly the victims
+// still missing) and the same result, victim <=> (key & mk) <= p.  The keys
+// are read once; a wave whose keys of one digit fall in a single bin counts
+// them with one atomic; every wave scans the histogram itself and keeps the
+// selected prefix in registers, and the histograms rotate over three buffers
+// (one counted, one scanned, one cleared), so a digit costs one barrier.  For
+// n <= 65536 the two top digits of ~index, 0xff for every key, are taken
+// without a pass (such a pass leaves every candidate in the bin, so it can
+// neither narrow the set nor stop the selection).
+struct SmallSelSmem {
+    unsigned hist[3][256];
+};
+
+template <int NT, int KPT>
+__device__ inline void select_small(const unsigned (&w2)[KPT], const unsigned (&w1)[KPT], int n, int e,
+                                    bool (&drop)[KPT], SmallSelSmem& sm)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < 256; i += NT) sm.hist[0][i] = 0u;
+    lds_barrier();
+    unsigned p0 = 0u, p1 = 0u, p2 = 0u, m0 = 0u, m1 = 0u, m2 = 0u;
+    unsigned rem = (unsigned)e;
+    int c = 0;  // passes made: pass c counts into hist[c % 3]
+    for (int d = 0; d < 12; ++d, ++c) {
+        unsigned* h = sm.hist[c % 3];
+        const int wi = 2 - (d >> 2), sh = 24 - 8 * (d & 3);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int j = tid + NT * i;
+            const unsigned k0 = ~(unsigned)j;
+            const bool cand = j < n && (k0 & m0) == p0 && (w1[i] & m1) == p1 && (w2[i] & m2) == p2;
+            const unsigned word = wi == 2 ? w2[i] : (wi == 1 ? w1[i] : k0);
+            const unsigned bin = cand ? (word >> sh) & 255u : 256u;  // 256: not counted
+            const unsigned b0 = __builtin_amdgcn_readfirstlane(bin);
+            const unsigned long long act = __ballot(1);
+            if (__ballot(bin != b0) == 0ull) {
+                if (b0 < 256u && lane == __ffsll((long long)act) - 1) atomicAdd(&h[b0], (unsigned)__popcll(act));
+            } else if (bin < 256u) {
+                atomicAdd(&h[bin], 1u);
+            }
+        }
+        // the next pass's buffer: last scanned two passes ago, before the previous barrier
+        for (int i = tid; i < 256; i += NT) sm.hist[(c + 1) % 3][i] = 0u;
+        lds_barrier();
+        unsigned cb[4], loc = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            cb[k] = h[lane * 4 + k];
+            loc += cb[k];
+        }
+        unsigned run = wave_incl_scan(loc) - loc;
+        int selk = -1;
+        unsigned below = 0u, cnt = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (run < rem && rem <= run + cb[k]) {  // the rem-th smallest candidate is in bin 4 lane + k
+                selk = k;
+                below = run;
+                cnt = cb[k];
+            }
+            run += cb[k];
+        }
+        const unsigned long long fm = __ballot(selk >= 0);
+        const int src = __ffsll((long long)fm) - 1;
+        const unsigned bin = 4u * (unsigned)src + (unsigned)__builtin_amdgcn_readlane(selk, src);
+        rem -= (unsigned)__builtin_amdgcn_readlane((int)below, src);
+        cnt = (unsigned)__builtin_amdgcn_readlane((int)cnt, src);
+        if (wi == 2) {
+            p2 |= bin << sh;
+            m2 |= 255u << sh;
+        } else if (wi == 1) {
+            p1 |= bin << sh;
+            m1 |= 255u << sh;
+        } else {
+            p0 |= bin << sh;
+            m0 |= 255u << sh;
+        }
+        if (cnt == rem) break;
+        if (d == 7 && n <= 65536) {  // digits 8 and 9 of ~index are 0xff for every key
+            p0 |= 0xffff0000u;
+            m0 |= 0xffff0000u;
+            d = 9;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int j = tid + NT * i;
+        const unsigned a2 = w2[i] & m2, a1 = w1[i] & m1, a0 = ~(unsigned)j & m0;
+        const bool le = a2 != p2 ? a2 < p2 : (a1 != p1 ? a1 < p1 : a0 <= p0);
+        drop[i] = j < n && le;
+    }
+}
+
+// snap_head for prefixes of at most NT KPT positions whose votes are staged:
+// each thread max-pools its KPT positions straight into registers, and the
+// selection runs on them (select_small).
+template <int NT, int KPT, typename SA>
+__device__ inline void snap_head_small(const SA& a, int Pp, const double* stage, unsigned* bits, SmallSelSmem& sm)
+{
+    const int tid = threadIdx.x;
+    const int e = Pp - a.keep;  // prefix positions the head leaves out
+    if (e > 0) {
+        unsigned w2[KPT], w1[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int j = tid + NT * i;
+            double m = 0.0;
+            if (j < Pp) {
+                const int x0 = max(0, j - a.pool_r), x1 = min(Pp - 1, j + a.pool_r);
+                m = stage[x0];
+                for (int x = x0 + 1; x <= x1; ++x) m = fmax(m, stage[x]);
+            }
+            const unsigned long long u = ord64(m);
+            w2[i] = (unsigned)(u >> 32);
+            w1[i] = (unsigned)u;
+        }
+        bool drop[KPT];
+        select_small<NT, KPT>(w2, w1, Pp, e, drop, sm);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int j = tid + NT * i;
+            if (j < Pp && !drop[i]) atomicOr(&bits[j >> 5], 1u << (j & 31));
+        }
+    } else {
+        for (int j = tid; j < Pp; j += NT) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+}
+
+// Orders a wave's LDS accesses around an exchange among its own lanes (the
+// LDS serves one wave's accesses in issue order; this keeps the compiler
+// from moving them across).
+__device__ inline void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct SnapFusedArgs {
+    const float* q;  // [sum P][Hq][128], Hq = Hkv
+    const void* k;   // [sum P][Hkv][128] bf16
+    float qscale;    // logit scale * log2(e)
+    int Hq, Hkv;
+    int pool_r, keep, cap;
+    double* votes;          // [sum P][Hq]
+    const double* pooled;  // not read: the votes are staged
+    int32_t* kept;          // [Hkv * B][cap]
+    int32_t* count;
+    int32_t seq_p[kMaxArgBatch], seq_w[kMaxArgBatch];
+    int64_t seq_off[kMaxArgBatch];
+};
+
+__global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs a)
+{
+    __shared__ uint4 qsm[kFQT][4][64];      // A operands of the window rows (hi / lo parts)
+    __shared__ uint4 ktr[kFNT / 64][256];    // per wave: a K tile on its way to B-operand order
+    __shared__ float2 wml[kFNT / 64][kFQT * 8];  // per wave and window row: (max, sum)
+    __shared__ float2 rowf[kFQT * 8];       // per window row: (max, 1 / sum), 1 / sum = 0 past P
+    __shared__ double stage[kFusedP];       // the prefix's votes, then pooled in place
+    __shared__ unsigned bits[kFusedP / 32];
+    __shared__ SmallSelSmem s_sel;
+    __shared__ ScanSmem s_scan;
+    const int unit = blockIdx.x, b = unit / a.Hkv, h = unit - b * a.Hkv;
+    const int P = a.seq_p[b], lo = P - a.seq_w[b];  // window rows [lo, P); prefix [0, lo)
+    const int64_t off = a.seq_off[b];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lc = lane & 15, lg = lane >> 4;
+    const int key0 = 128 * wv;
+    const int nt = min(kFKT, max(0, (P - key0 + 15) / 16));  // tiles holding keys below P (uniform)
+
+    // the window rows' q first (the vector memory counter retires in order, so
+    // the staging below waits for these loads, not for the K tiles after them)
+    float4 qx[4];
+    int qv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int v = tid + kFNT * i;  // A-operand vector (tq, kb, lane)
+        const int ln = v & 63, kb = (v >> 6) & 3, tq = v >> 8;
+        const int pos = min(lo + 8 * tq + ((ln & 15) >> 1), P - 1);
+        const float* qr = a.q + ((size_t)(off + pos) * a.Hq + h) * 128 + 32 * kb + 8 * (ln >> 4);
+        qx[2 * i] = *reinterpret_cast<const float4*>(qr);
+        qx[2 * i + 1] = *reinterpret_cast<const float4*>(qr + 4);
+        qv[i] = v;
+    }
+    for (int i = tid; i < kFusedP / 32; i += kFNT) bits[i] = 0u;
+    // K tiles in whole rows: load i of lane (lg, lc) is key key0 + 16 x + 4 i + lg's
+    // vector lc, so each load instruction reads four 256-byte rows (the B
+    // operand's order, key lc's vectors 4 kb + lg, would read sixteen half rows
+    // per instruction: ~4 us slower at the OPT layer's prompts)
+    const uint4* kp = reinterpret_cast<const uint4*>(a.k) + (size_t)h * kRowVecs + lc;
+    auto fetch = [&](int x, uint4 (&r)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = min(key0 + 16 * x + 4 * i + lg, P - 1);
+            r[i] = stream_load(kp + (size_t)(off + key) * a.Hkv * kRowVecs);
+        }
+    };
+    // then through the wave's LDS tile into B-operand order: element (key 4 i + lg,
+    // vector lc) is k-step lc / 4 of lane (lc % 4, 4 i + lg), i.e. slot
+    // 16 lc + 4 i + lg; each 16-slot block's slots are XOR-ed with the block
+    // number, so that both the writes (16 lanes of one lg, one slot of each
+    // block) and the reads (16 consecutive slots) touch 16 different banks
+    uint4* const kw = &ktr[wv][0];
+    auto swz = [](int sl) { return sl ^ ((sl >> 4) & 15); };
+    auto put_k = [&](const uint4 (&r)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kw[swz(16 * lc + 4 * i + lg)] = r[i];
+    };
+    auto get_b = [&](bf16x8 (&bt)[4]) {
+        wave_lds_sync();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) bt[kb] = as_bf16x8(kw[swz(64 * kb + lane)]);
+        wave_lds_sync();  // the next tile's writes after these reads
+    };
+    uint4 kt0[4], kt1[4], kt2[4], kt3[4];  // four tiles in flight per wave
+    if (nt > 0) fetch(0, kt0);
+    if (nt > 1) fetch(1, kt1);
+    if (nt > 2) fetch(2, kt2);
+    if (nt > 3) fetch(3, kt3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int v = qv[i], ln = v & 63;
+        const bool lo_part = (ln & 1) != 0;
+        const float x[8] = {qx[2 * i].x, qx[2 * i].y, qx[2 * i].z, qx[2 * i].w,
+                            qx[2 * i + 1].x, qx[2 * i + 1].y, qx[2 * i + 1].z, qx[2 * i + 1].w};
+        bf16x8 o;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = split_part(x[j] * a.qscale, lo_part);
+        (&qsm[0][0][0])[v] = as_u4(o);
+    }
+    lds_barrier();
+    bf16x8 qop[kFQT][4];
+#pragma unroll
+    for (int tq = 0; tq < kFQT; ++tq)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qop[tq][kb] = as_bf16x8(qsm[tq][kb][lane]);
+
+    // logits: s[x][tq][r] = row lo + 8 tq + 2 lg + r against key key0 + 16 x + lc,
+    // kMaskLogit after the row (causal), past P, or on a tile past P
+    float s[kFKT][kFQT][2];
+#pragma unroll
+    for (int x = 0; x < kFKT; ++x) {
+        uint4(&cur)[4] = (x & 3) == 0 ? kt0 : (x & 3) == 1 ? kt1 : (x & 3) == 2 ? kt2 : kt3;
+        if (x < nt) {
+            bf16x8 bt[4];
+            put_k(cur);
+            if (x + 4 < nt) fetch(x + 4, cur);
+            get_b(bt);
+            const int key = key0 + 16 * x + lc;
+            // only a tile reaching past the window's first row holds keys after
+            // some row (keys past P are after every row below P); rows past P
+            // are dropped later (their 1 / sum is 0)
+            const bool diag = key0 + 16 * x + 15 > lo;
+#pragma unroll
+            for (int tq = 0; tq < kFQT; ++tq) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) c = mma(qop[tq][kb], bt[kb], c);
+                const int pos0 = lo + 8 * tq + 2 * lg;
+                s[x][tq][0] = c[0] + c[1];
+                s[x][tq][1] = c[2] + c[3];
+                if (diag) {
+                    s[x][tq][0] = key <= pos0 ? s[x][tq][0] : kMaskLogit;
+                    s[x][tq][1] = key <= pos0 + 1 ? s[x][tq][1] : kMaskLogit;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int tq = 0; tq < kFQT; ++tq) s[x][tq][0] = s[x][tq][1] = kMaskLogit;
+        }
+    }
+
+    // each row's maximum over the wave's keys (the lane's 8, then the 16 key
+    // lanes by DPP), the weights relative to it (kept in s), their sum, then
+    // the row's maximum and sum over the waves in LDS
+    float m16[kFQT][2], l16[kFQT * 2];  // l16[2 tq + r]
+#pragma unroll
+    for (int tq = 0; tq < kFQT; ++tq)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float m = s[0][tq][r];
+#pragma unroll
+            for (int x = 1; x < kFKT; ++x) m = fmaxf(m, s[x][tq][r]);
+            m16[tq][r] = max16(m);
+        }
+#pragma unroll
+    for (int tq = 0; tq < kFQT; ++tq)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float l = 0.f;
+#pragma unroll
+            for (int x = 0; x < kFKT; ++x) {
+                s[x][tq][r] = fast_exp2(s[x][tq][r] - m16[tq][r]);
+                l += s[x][tq][r];
+            }
+            l16[2 * tq + r] = l;
+        }
+    sum16_n<kFQT * 2>(l16);
+    if (lc == 0) {
+#pragma unroll
+        for (int tq = 0; tq < kFQT; ++tq)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) wml[wv][8 * tq + 2 * lg + r] = make_float2(m16[tq][r], l16[2 * tq + r]);
+    }
+    lds_barrier();
+    if (tid < kFQT * 8) {
+        float M = wml[0][tid].x;
+#pragma unroll
+        for (int v = 1; v < kFNT / 64; ++v) M = fmaxf(M, wml[v][tid].x);
+        float L = 0.f;
+#pragma unroll
+        for (int v = 0; v < kFNT / 64; ++v) L += wml[v][tid].y * fast_exp2(wml[v][tid].x - M);
+        rowf[tid] = make_float2(M, lo + tid < P ? 1.0f / L : 0.f);
+    }
+    lds_barrier();
+    // a weight is s * 2^(m16 - M) / L: one factor per (lane, row)
+    float f[kFQT][2];
+#pragma unroll
+    for (int tq = 0; tq < kFQT; ++tq)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float2 rf = rowf[8 * tq + 2 * lg + r];
+            f[tq][r] = fast_exp2(m16[tq][r] - rf.x) * rf.y;
+        }
+    // votes: per key, over the lane's rows (fp32 per query tile, fp64 across
+    // tiles), then over the four lane groups
+#pragma unroll
+    for (int x = 0; x < kFKT; ++x) {
+        double acc = 0.0;
+#pragma unroll
+        for (int tq = 0; tq < kFQT; ++tq) acc += (double)(s[x][tq][0] * f[tq][0] + s[x][tq][1] * f[tq][1]);
+        acc = xrow_add(acc, false);
+        acc = xrow_add(acc, true);
+        const int key = key0 + 16 * x + lc;
+        if (lg == 0 && x < nt && key < P) {
+            a.votes[(size_t)(off + key) * a.Hq + h] = acc;
+            if (key < lo) stage[key] = acc;
+        }
+    }
+    lds_barrier();
+    snap_head_small<kFNT, kFusedP / kFNT>(a, lo, stage, bits, s_sel);
+    snap_finish<kFNT>(a, unit, P, lo, bits, s_scan);
 }
 
 // Scratch of h2o_snapkv_select_noalloc, for callers that cannot allocate:
@@ -670,6 +1056,38 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(snapkv_union_kernel, dim3(units), dim3(kSNT), dyn_u, st, b);
+    return hipGetLastError();
+}
+
+bool snapkv_fused_fits(const SnapArgs& a)
+{
+    if (a.G != 1 || a.B < 1 || a.B > kMaxArgBatch) return false;
+    for (int b = 0; b < a.B; ++b)
+        if (a.seq_p[b] > kFusedP || a.seq_w[b] > kFQT * 8) return false;
+    return true;
+}
+
+hipError_t launch_snapkv_fused(const ColsumArgs& ca, const SnapArgs& sa, double* votes, hipStream_t st)
+{
+    if (!snapkv_fused_fits(sa) || ca.G != 1 || ca.B != sa.B || !votes) return hipErrorInvalidValue;
+    SnapFusedArgs f{};
+    f.q = ca.q;
+    f.k = ca.k;
+    f.qscale = ca.qscale;
+    f.Hq = sa.Hq;
+    f.Hkv = sa.Hkv;
+    f.pool_r = sa.pool_r;
+    f.keep = sa.keep;
+    f.cap = sa.cap;
+    f.votes = votes;
+    f.kept = sa.kept;
+    f.count = sa.count;
+    for (int b = 0; b < sa.B; ++b) {
+        f.seq_p[b] = sa.seq_p[b];
+        f.seq_w[b] = sa.seq_w[b];
+        f.seq_off[b] = sa.seq_off[b];
+    }
+    hipLaunchKernelGGL(snapkv_fused_kernel, dim3((unsigned)(sa.B * sa.Hkv)), dim3(kFNT), 0, st, f);
     return hipGetLastError();
 }
 

@@ -592,8 +592,6 @@ int colsum_run(const h2o_config* cfg, const int32_t* plen, const float* q, const
     return H2O_OK;
 }
 
-// SnapKV's selection (h2o_snapkv_select): validate, per-head window votes by the
-// column-sum passes, then pooling and the per-unit selection.
 // SnapKV's selection, validated and sized: the launch arguments of both
 // passes and the scratch they need, laid out as [votes (when the caller passes
 // none)] [pooled votes] [column-sum passes] [per-head kept bitmaps (G > 1)].
@@ -654,13 +652,17 @@ int snapkv_plan(const h2o_config* cfg, const int32_t* plen, int window, int pool
     a.bits_words = ((pl.maxP + 31) / 32 + 3) & ~3;  // whole 16-byte groups, so staged votes stay aligned
     pl.hbytes = G > 1 ? align256((size_t)B * Hq * a.bits_words * sizeof(unsigned)) : 0;
     pl.vown = votes ? 0 : pl.vbytes;
-    return colsum_setup(cfg, plen, lo.data(), q, k, 1, votes, pl.ca, pl.maxPc, pl.cbytes);
+    const int rc = colsum_setup(cfg, plen, lo.data(), q, k, 1, votes, pl.ca, pl.maxPc, pl.cbytes);
+    if (rc == H2O_OK && snapkv_fused_fits(a)) pl.vbytes = pl.cbytes = pl.hbytes = 0;  // one kernel: the votes only
+    return rc;
 }
 
-// Both passes of a planned selection, on scratch sp of pl.scratch_bytes().
+// A planned selection on scratch sp of pl.scratch_bytes(): one kernel when it
+// fits (snapkv_fused_fits), else both column-sum passes, then the selection.
 hipError_t snapkv_enqueue(SnapPlan& pl, double* votes, char* sp, hipStream_t st)
 {
     double* vb = votes ? votes : reinterpret_cast<double*>(sp);
+    if (snapkv_fused_fits(pl.a)) return launch_snapkv_fused(pl.ca, pl.a, vb, st);
     pl.ca.out = vb;  // the votes: the caller's buffer, else the scratch's first part
     hipError_t e = colsum_launch(pl.ca, pl.maxPc, sp + pl.vown + pl.vbytes, st);
     if (e != hipSuccess) return e;

@@ -99,6 +99,21 @@ def test_snapkv_gqa_edge_cases():
     assert np.all(c == 16)
 
 
+def test_snapkv_one_pass_bounds():
+    """Groups of one query head with prompts up to 1024 positions and windows
+    up to 32 rows run as one kernel (8 waves of 128 keys each): prompts at and
+    around the wave and tile edges and a prompt of one position, windows of 32,
+    31 and 1 rows; then just past each bound (1025 positions, a 33-row window),
+    where the two column-sum passes and the selection kernel run."""
+    w = WL.OPT_LAYER.scaled(n_q_heads=2, n_kv_heads=2)
+    run_snapkv(w, [1024, 1023, 897, 129, 128, 17, 1], window=32, pool=7, keep=100)
+    run_snapkv(w, [1024, 513, 40], window=31, pool=5, keep=37)
+    _, c = run_snapkv(w, [1024, 2], window=1, pool=3, keep=500)
+    assert list(c[:, 0]) == [501, 2]
+    run_snapkv(w, [1025, 1024], window=32, pool=7, keep=100)
+    run_snapkv(w, [1024, 600], window=33, pool=7, keep=100)
+
+
 @pytest.mark.parametrize("g", [1, 4])
 def test_snapkv_long_prefix_unstaged(g):
     """A prefix beyond the 4096 positions whose pooled votes the selection
