@@ -370,8 +370,8 @@ EXP_COST = 4.0
 # fp64 add per two scores (4.75 VALU + 1 exp2).
 ROWS_OPS_PER_SCORE = 7.0 + EXP_COST
 COLS_OPS_PER_SCORE = 4.75 + EXP_COST
-# SnapKV in one kernel (groups of one query head, prompts up to 1024 positions,
-# windows up to 32 rows) scores each window row once: it adds the hi and lo
+# SnapKV in one pass (prompts up to 1024 positions, windows up to 32 rows)
+# scores each window row once: it adds the hi and lo
 # products, takes the maximum (a three-way max per two scores), subtracts the
 # row maximum, takes one exp2, adds to the row sum, multiplies by the row's
 # factor and adds, and converts and adds in fp64 per two scores (the mask
@@ -580,7 +580,7 @@ def snapkv_main(args, w):
     tokens = float(sum(lens))
     rows = sum(sum(i + 1 for i in range(P - min(window, P), P)) for P in lens)
     flops = 2.0 * D * Hq * rows
-    one_kernel = G == 1 and max(lens) <= FUSED_SNAP_MAX_P and all(min(window, P) <= FUSED_SNAP_MAX_W for P in lens)
+    one_kernel = max(lens) <= FUSED_SNAP_MAX_P and all(min(window, P) <= FUSED_SNAP_MAX_W for P in lens)
     # the window rows' scores: once in the one-kernel path, else in both passes
     alu = Hq * rows * (FUSED_SNAP_OPS_PER_SCORE if one_kernel else ROWS_OPS_PER_SCORE + COLS_OPS_PER_SCORE)
     nbytes = (sum(min(window, P) for P in lens) * Hq * D * 4 + tokens * (Hkv * D * 2 + Hq * 8)
@@ -599,7 +599,7 @@ def snapkv_main(args, w):
             nbytes, flops, per_call,
             "whole call; algorithmic bytes = the window rows' fp32 q, bf16 K, the fp64 votes and the kept "
             "positions once; algorithmic flops = the window rows' causal logits once; ALU = the window rows' "
-            + ("scores once at 10 lane-operation equivalents (one kernel)" if one_kernel else
+            + ("scores once at 10 lane-operation equivalents (one pass)" if one_kernel else
                "scores in both passes at 11 + 8.75 lane-operation equivalents")
             + "; the call also pools and selects", alu_ops=alu),
         "cpu_baseline": (None if args.no_cpu_baseline

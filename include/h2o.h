@@ -323,11 +323,11 @@ int h2o_snapkv_select(const h2o_config *cfg, const int32_t *prompt_len, int32_t 
  * in the library, one copy per device, held until the process ends; a call
  * whose scratch need is larger returns H2O_EINVAL with the size in the message
  * before anything is enqueued.  The need is, in bytes, rounded up to 256 each:
- * (votes == NULL ? 8 sum P_b Hq : 0), and unless the call runs as one kernel
- * (G = 1, every P_b <= 1024 and w_b <= 32) + 8 sum P_b Hq (pooled votes)
- * + 4160 B Hkv G T (window q tiles and row statistics, T = the most 8-row
- * tiles a window spans, ceil(w_b / 8) + 1 at most) + (G > 1 ?
- * 4 B Hq ceil(max P_b / 128) * 4 : 0) (per-head kept bitmaps).  Calls on one
+ * (votes == NULL ? 8 sum P_b Hq : 0) + (G > 1 ? 4 B Hq ceil(max P_b / 128) * 4
+ * : 0) (per-head kept bitmaps), and unless the call runs in one pass (every
+ * P_b <= 1024 and w_b <= 32) + 8 sum P_b Hq (pooled votes) + 4160 B Hkv G T
+ * (window q tiles and row statistics, T = the most 8-row tiles a window
+ * spans, ceil(w_b / 8) + 1 at most).  Calls on one
  * device share that array: two calls whose work overlaps on the device (on
  * different streams, with nothing ordering them) race and give undefined
  * results.  Nothing is cleared between calls (no part of the scratch needs to

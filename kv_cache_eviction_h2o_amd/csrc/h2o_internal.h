@@ -292,10 +292,11 @@ hipError_t launch_step_f64(const StepArgs& a, bool llds, size_t dyn, hipStream_t
 hipError_t launch_step_f16(const StepArgs& a, bool llds, size_t dyn, hipStream_t st);
 hipError_t launch_colsum(const ColsumArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
 hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st);  // h2o_prefill.hip
-// SnapKV's votes and selection in one kernel (h2o_prefill.hip), for calls
-// that fit it (snapkv_fused_fits: groups of one query head, prompts up to
-// 1024 positions, observation windows up to 32 rows): ca's q, K and scale,
-// sa's selection, the votes written to `votes`.
+// SnapKV's votes and selection in one pass (h2o_prefill.hip), for calls that
+// fit it (snapkv_fused_fits: prompts up to 1024 positions, observation windows
+// up to 32 rows): ca's q, K and scale, sa's selection (and, for groups of more
+// than one query head, sa.hbits and the union kernel), the votes written to
+// `votes`.
 bool snapkv_fused_fits(const SnapArgs& a);
 hipError_t launch_snapkv_fused(const ColsumArgs& ca, const SnapArgs& sa, double* votes, hipStream_t st);
 

@@ -612,8 +612,8 @@ __global__ void __launch_bounds__(kSNT) snapkv_union_kernel(const SnapArgs a)
 }
 
 // ------------------------------------------------------- SnapKV in one pass
-// Groups of one query head, prompts up to kFusedP positions, observation
-// windows of at most 32 rows: one workgroup per unit reads the unit's K once
+// Prompts up to kFusedP positions and observation windows of at most 32 rows:
+// one workgroup per (unit, query head) reads the unit's K once
 // (the two column-sum passes read it twice and hand the row statistics and
 // the votes over through memory).  Wave v holds the window rows' logits for
 // keys 128 v .. 128 v + 127 in registers (8 tiles of 16 keys, the same
@@ -790,15 +790,18 @@ __device__ inline void wave_lds_sync()
 }
 
 struct SnapFusedArgs {
-    const float* q;  // [sum P][Hq][128], Hq = Hkv
+    const float* q;  // [sum P][Hq][128]
     const void* k;   // [sum P][Hkv][128] bf16
     float qscale;    // logit scale * log2(e)
-    int Hq, Hkv;
+    int Hq, Hkv, G;
+    int units;              // B * Hkv
     int pool_r, keep, cap;
     double* votes;          // [sum P][Hq]
     const double* pooled;  // not read: the votes are staged
-    int32_t* kept;          // [Hkv * B][cap]
+    int32_t* kept;          // G = 1: [B * Hkv][cap]
     int32_t* count;
+    unsigned* hbits;        // G > 1: [B * Hkv][G][bits_words], each query head's kept prefix bits
+    int bits_words;
     int32_t seq_p[kMaxArgBatch], seq_w[kMaxArgBatch];
     int64_t seq_off[kMaxArgBatch];
 };
@@ -813,7 +816,14 @@ __global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs 
     __shared__ unsigned bits[kFusedP / 32];
     __shared__ SmallSelSmem s_sel;
     __shared__ ScanSmem s_scan;
-    const int unit = blockIdx.x, b = unit / a.Hkv, h = unit - b * a.Hkv;
+    // one workgroup per (unit, query head g of its group): ids 64 c + 8 g + u
+    // serve unit 8 c + u, so the G workgroups of a unit reach the same XCD
+    // (ids go to the XCDs round-robin) and are dispatched together, and the
+    // unit's K, read by each of them, comes from that XCD's L2 after the first
+    const int id = blockIdx.x, c8 = id / (8 * a.G), r8 = id - c8 * 8 * a.G;
+    const int g = r8 >> 3, unit = 8 * c8 + (r8 & 7);
+    if (unit >= a.units) return;  // the last group of 8 units may be partial
+    const int b = unit / a.Hkv, h = unit - b * a.Hkv, hq = h * a.G + g;
     const int P = a.seq_p[b], lo = P - a.seq_w[b];  // window rows [lo, P); prefix [0, lo)
     const int64_t off = a.seq_off[b];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -831,7 +841,7 @@ __global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs 
         const int v = tid + kFNT * i;  // A-operand vector (tq, kb, lane)
         const int ln = v & 63, kb = (v >> 6) & 3, tq = v >> 8;
         const int pos = min(lo + 8 * tq + ((ln & 15) >> 1), P - 1);
-        const float* qr = a.q + ((size_t)(off + pos) * a.Hq + h) * 128 + 32 * kb + 8 * (ln >> 4);
+        const float* qr = a.q + ((size_t)(off + pos) * a.Hq + hq) * 128 + 32 * kb + 8 * (ln >> 4);
         qx[2 * i] = *reinterpret_cast<const float4*>(qr);
         qx[2 * i + 1] = *reinterpret_cast<const float4*>(qr + 4);
         qv[i] = v;
@@ -987,13 +997,18 @@ __global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs 
         acc = xrow_add(acc, true);
         const int key = key0 + 16 * x + lc;
         if (lg == 0 && x < nt && key < P) {
-            a.votes[(size_t)(off + key) * a.Hq + h] = acc;
+            a.votes[(size_t)(off + key) * a.Hq + hq] = acc;
             if (key < lo) stage[key] = acc;
         }
     }
     lds_barrier();
     snap_head_small<kFNT, kFusedP / kFNT>(a, lo, stage, bits, s_sel);
-    snap_finish<kFNT>(a, unit, P, lo, bits, s_scan);
+    if (a.G == 1) {
+        snap_finish<kFNT>(a, unit, P, lo, bits, s_scan);
+    } else {  // the head's prefix bits; snapkv_union_kernel ORs the group's and adds the window
+        unsigned* hb = a.hbits + ((size_t)unit * a.G + g) * a.bits_words;
+        for (int i = tid; i < (lo + 31) / 32; i += kFNT) hb[i] = bits[i];
+    }
 }
 
 // Scratch of h2o_snapkv_select_noalloc, for callers that cannot allocate:
@@ -1022,6 +1037,18 @@ hipError_t noalloc_scratch(char** ptr)
     return hipSuccess;
 }
 
+// G > 1: the union of each unit's per-head bitmaps (hbits), the window and the
+// kept list (snapkv_union_kernel; dynamic LDS: the bitmap).
+static hipError_t launch_snap_union(const SnapArgs& a, hipStream_t st)
+{
+    static DynLdsLimit lim;
+    const size_t dyn = (size_t)a.bits_words * 4;
+    hipError_t e = lim.allow((const void*)snapkv_union_kernel, dyn);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(snapkv_union_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(kSNT), dyn, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
 {
     if (max_p <= 0) return hipSuccess;
@@ -1040,10 +1067,9 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
     SnapArgs b = a;
     b.stage_n = std::min(max_pp, kSnapStage);
     const size_t dyn = (size_t)b.bits_words * 4 + (size_t)b.stage_n * 8;
-    const size_t dyn_u = (size_t)b.bits_words * 4;  // the union kernel: the bitmap only
     // above the default 48 KB of dynamic LDS the kernel's limit is raised on
     // the current device first (only prompts beyond ~130k positions need it)
-    static DynLdsLimit lim_sel, lim_head, lim_union;
+    static DynLdsLimit lim_sel, lim_head;
     const unsigned units = (unsigned)(a.B * a.Hkv);
     if (a.G == 1) {
         if ((e = lim_sel.allow((const void*)snapkv_select_kernel, dyn)) != hipSuccess) return e;
@@ -1051,17 +1077,15 @@ hipError_t launch_snapkv(const SnapArgs& a, int max_p, hipStream_t st)
         return hipGetLastError();
     }
     if ((e = lim_head.allow((const void*)snapkv_head_kernel, dyn)) != hipSuccess) return e;
-    if ((e = lim_union.allow((const void*)snapkv_union_kernel, dyn_u)) != hipSuccess) return e;
     hipLaunchKernelGGL(snapkv_head_kernel, dim3(units, (unsigned)a.G), dim3(kSNT), dyn, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(snapkv_union_kernel, dim3(units), dim3(kSNT), dyn_u, st, b);
-    return hipGetLastError();
+    return launch_snap_union(b, st);
 }
 
 bool snapkv_fused_fits(const SnapArgs& a)
 {
-    if (a.G != 1 || a.B < 1 || a.B > kMaxArgBatch) return false;
+    if (a.G < 1 || a.B < 1 || a.B > kMaxArgBatch) return false;
     for (int b = 0; b < a.B; ++b)
         if (a.seq_p[b] > kFusedP || a.seq_w[b] > kFQT * 8) return false;
     return true;
@@ -1069,26 +1093,34 @@ bool snapkv_fused_fits(const SnapArgs& a)
 
 hipError_t launch_snapkv_fused(const ColsumArgs& ca, const SnapArgs& sa, double* votes, hipStream_t st)
 {
-    if (!snapkv_fused_fits(sa) || ca.G != 1 || ca.B != sa.B || !votes) return hipErrorInvalidValue;
+    if (!snapkv_fused_fits(sa) || ca.G != sa.G || ca.B != sa.B || !votes || (sa.G > 1 && !sa.hbits))
+        return hipErrorInvalidValue;
     SnapFusedArgs f{};
     f.q = ca.q;
     f.k = ca.k;
     f.qscale = ca.qscale;
     f.Hq = sa.Hq;
     f.Hkv = sa.Hkv;
+    f.G = sa.G;
+    f.units = sa.B * sa.Hkv;
     f.pool_r = sa.pool_r;
     f.keep = sa.keep;
     f.cap = sa.cap;
     f.votes = votes;
     f.kept = sa.kept;
     f.count = sa.count;
+    f.hbits = sa.hbits;
+    f.bits_words = sa.bits_words;
     for (int b = 0; b < sa.B; ++b) {
         f.seq_p[b] = sa.seq_p[b];
         f.seq_w[b] = sa.seq_w[b];
         f.seq_off[b] = sa.seq_off[b];
     }
-    hipLaunchKernelGGL(snapkv_fused_kernel, dim3((unsigned)(sa.B * sa.Hkv)), dim3(kFNT), 0, st, f);
-    return hipGetLastError();
+    const unsigned groups = (unsigned)((f.units + 7) / 8);  // of 8 units, each 8 G workgroups
+    hipLaunchKernelGGL(snapkv_fused_kernel, dim3(groups * 8u * (unsigned)sa.G), dim3(kFNT), 0, st, f);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sa.G == 1) return e;
+    return launch_snap_union(sa, st);
 }
 
 hipError_t launch_colsum(const ColsumArgs& a, int max_p, hipStream_t st)

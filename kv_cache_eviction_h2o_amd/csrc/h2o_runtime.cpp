@@ -653,7 +653,7 @@ int snapkv_plan(const h2o_config* cfg, const int32_t* plen, int window, int pool
     pl.hbytes = G > 1 ? align256((size_t)B * Hq * a.bits_words * sizeof(unsigned)) : 0;
     pl.vown = votes ? 0 : pl.vbytes;
     const int rc = colsum_setup(cfg, plen, lo.data(), q, k, 1, votes, pl.ca, pl.maxPc, pl.cbytes);
-    if (rc == H2O_OK && snapkv_fused_fits(a)) pl.vbytes = pl.cbytes = pl.hbytes = 0;  // one kernel: the votes only
+    if (rc == H2O_OK && snapkv_fused_fits(a)) pl.vbytes = pl.cbytes = 0;  // one pass: votes and head bitmaps only
     return rc;
 }
 
@@ -661,14 +661,14 @@ int snapkv_plan(const h2o_config* cfg, const int32_t* plen, int window, int pool
 // fits (snapkv_fused_fits), else both column-sum passes, then the selection.
 hipError_t snapkv_enqueue(SnapPlan& pl, double* votes, char* sp, hipStream_t st)
 {
-    double* vb = votes ? votes : reinterpret_cast<double*>(sp);
-    if (snapkv_fused_fits(pl.a)) return launch_snapkv_fused(pl.ca, pl.a, vb, st);
-    pl.ca.out = vb;  // the votes: the caller's buffer, else the scratch's first part
-    hipError_t e = colsum_launch(pl.ca, pl.maxPc, sp + pl.vown + pl.vbytes, st);
-    if (e != hipSuccess) return e;
+    double* vb = votes ? votes : reinterpret_cast<double*>(sp);  // the caller's buffer, else the scratch's first part
     pl.a.votes = vb;
     pl.a.pooled = reinterpret_cast<double*>(sp + pl.vown);
     pl.a.hbits = pl.a.G > 1 ? reinterpret_cast<unsigned*>(sp + pl.vown + pl.vbytes + pl.cbytes) : nullptr;
+    if (snapkv_fused_fits(pl.a)) return launch_snapkv_fused(pl.ca, pl.a, vb, st);
+    pl.ca.out = vb;
+    hipError_t e = colsum_launch(pl.ca, pl.maxPc, sp + pl.vown + pl.vbytes, st);
+    if (e != hipSuccess) return e;
     return launch_snapkv(pl.a, pl.maxP, st);
 }
 

@@ -100,11 +100,11 @@ def test_snapkv_gqa_edge_cases():
 
 
 def test_snapkv_one_pass_bounds():
-    """Groups of one query head with prompts up to 1024 positions and windows
-    up to 32 rows run as one kernel (8 waves of 128 keys each): prompts at and
-    around the wave and tile edges and a prompt of one position, windows of 32,
-    31 and 1 rows; then just past each bound (1025 positions, a 33-row window),
-    where the two column-sum passes and the selection kernel run."""
+    """Prompts up to 1024 positions with windows up to 32 rows run in one pass
+    (a workgroup of 8 waves of 128 keys per unit and query head): prompts at
+    and around the wave and tile edges and a prompt of one position, windows
+    of 32, 31 and 1 rows; then just past each bound (1025 positions, a 33-row
+    window), where the two column-sum passes and the selection kernel run."""
     w = WL.OPT_LAYER.scaled(n_q_heads=2, n_kv_heads=2)
     run_snapkv(w, [1024, 1023, 897, 129, 128, 17, 1], window=32, pool=7, keep=100)
     run_snapkv(w, [1024, 513, 40], window=31, pool=5, keep=37)
@@ -112,6 +112,17 @@ def test_snapkv_one_pass_bounds():
     assert list(c[:, 0]) == [501, 2]
     run_snapkv(w, [1025, 1024], window=32, pool=7, keep=100)
     run_snapkv(w, [1024, 600], window=33, pool=7, keep=100)
+
+
+@pytest.mark.parametrize("g", [2, 8])
+def test_snapkv_one_pass_groups(g):
+    """Groups of query heads in one pass (a workgroup per unit and head, each
+    head's bits OR-ed by the union kernel): 3 KV heads, so 9 units leave the
+    last group of 8 units partial; ragged prompts at the bounds."""
+    w = WL.LLAMA_GQA.scaled(n_q_heads=3 * g, n_kv_heads=3)
+    _, c = run_snapkv(w, [1024, 600, 33], window=32, pool=7, keep=60)
+    assert np.all(c >= 32 + 1) and np.all(c <= 32 + g * 60)
+    run_snapkv(w, [1023, 129, 1], window=31, pool=5, keep=40)
 
 
 @pytest.mark.parametrize("g", [1, 4])
