@@ -651,15 +651,16 @@ __device__ inline unsigned wave_incl_scan(unsigned v)
 // tid + NT i in slot i of thread tid, each key (w2, w1, ~index) as the decode
 // step's and radix_select's (96 bits, unique): the same 8-bit digits from the
 // top, the same early stop (once the chosen bin holds exactly the victims
-// still missing) and the same result, victim <=> (key & mk) <= p.  The keys
-// are read once; a wave whose keys of one digit fall in a single bin counts
-// them with one atomic; every wave scans the histogram itself and keeps the
-// selected prefix in registers, and the histograms rotate over three buffers
-// (one counted, one scanned, one cleared), so a digit costs one barrier.  For
-// n <= 65536 the two top digits of ~index, 0xff for every key, are taken
-// without a pass (such a pass leaves every candidate in the bin, so it can
-// neither narrow the set nor stop the selection).
-struct SmallSelSmem {
+// still missing) and the same victims.  Each element keeps two flags, still
+// in the chosen prefix and already below it, updated by one comparison a
+// digit; a wave whose candidates of one digit fall in a single bin counts
+// them with one atomic; every wave scans the histogram itself (one DPP prefix
+// sum, then the chosen lane's four bins on scalars), and the histograms rotate
+// over three buffers (one counted, one scanned, one cleared), so a digit costs
+// one barrier.  For n <= 65536 the two top digits of ~index, 0xff for every
+// key, are taken without a pass (such a pass leaves every candidate in the
+// bin, so it can neither narrow the set nor stop the selection).
+struct alignas(16) SmallSelSmem {
     unsigned hist[3][256];
 };
 
@@ -670,77 +671,74 @@ __device__ inline void select_small(const unsigned (&w2)[KPT], const unsigned (&
     const int tid = threadIdx.x, lane = tid & 63;
     for (int i = tid; i < 256; i += NT) sm.hist[0][i] = 0u;
     lds_barrier();
-    unsigned p0 = 0u, p1 = 0u, p2 = 0u, m0 = 0u, m1 = 0u, m2 = 0u;
+    bool cand[KPT], below[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        cand[i] = tid + NT * i < n;
+        below[i] = false;
+    }
     unsigned rem = (unsigned)e;
     int c = 0;  // passes made: pass c counts into hist[c % 3]
-    for (int d = 0; d < 12; ++d, ++c) {
-        unsigned* h = sm.hist[c % 3];
+#pragma unroll
+    for (int d = 0; d < 12; ++d) {
+        if ((d == 8 || d == 9) && n <= 65536) continue;  // digits 8 and 9 of ~index are 0xff for every key
         const int wi = 2 - (d >> 2), sh = 24 - 8 * (d & 3);
+        unsigned* h = sm.hist[c % 3];
+        unsigned bin[KPT];
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int j = tid + NT * i;
-            const unsigned k0 = ~(unsigned)j;
-            const bool cand = j < n && (k0 & m0) == p0 && (w1[i] & m1) == p1 && (w2[i] & m2) == p2;
-            const unsigned word = wi == 2 ? w2[i] : (wi == 1 ? w1[i] : k0);
-            const unsigned bin = cand ? (word >> sh) & 255u : 256u;  // 256: not counted
-            const unsigned b0 = __builtin_amdgcn_readfirstlane(bin);
+            const unsigned word = wi == 2 ? w2[i] : (wi == 1 ? w1[i] : ~(unsigned)(tid + NT * i));
+            bin[i] = (word >> sh) & 255u;
+            const unsigned b = cand[i] ? bin[i] : 256u;  // 256: not counted
+            const unsigned b0 = __builtin_amdgcn_readfirstlane(b);
             const unsigned long long act = __ballot(1);
-            if (__ballot(bin != b0) == 0ull) {
+            if (__ballot(b != b0) == 0ull) {
                 if (b0 < 256u && lane == __ffsll((long long)act) - 1) atomicAdd(&h[b0], (unsigned)__popcll(act));
-            } else if (bin < 256u) {
-                atomicAdd(&h[bin], 1u);
+            } else if (b < 256u) {
+                atomicAdd(&h[b], 1u);
             }
         }
         // the next pass's buffer: last scanned two passes ago, before the previous barrier
         for (int i = tid; i < 256; i += NT) sm.hist[(c + 1) % 3][i] = 0u;
         lds_barrier();
-        unsigned cb[4], loc = 0u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            cb[k] = h[lane * 4 + k];
-            loc += cb[k];
-        }
-        unsigned run = wave_incl_scan(loc) - loc;
-        int selk = -1;
-        unsigned below = 0u, cnt = 0u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (run < rem && rem <= run + cb[k]) {  // the rem-th smallest candidate is in bin 4 lane + k
-                selk = k;
-                below = run;
-                cnt = cb[k];
+        const uint4 cb = reinterpret_cast<const uint4*>(h)[lane];
+        const unsigned loc = cb.x + cb.y + cb.z + cb.w;
+        const unsigned inc = wave_incl_scan(loc);
+        // the rem-th smallest candidate lies in the first lane whose prefix reaches rem
+        const int src = __ffsll((long long)__ballot(inc >= rem)) - 1;
+        unsigned run = (unsigned)__builtin_amdgcn_readlane((int)(inc - loc), src);
+        const unsigned c0 = (unsigned)__builtin_amdgcn_readlane((int)cb.x, src);
+        const unsigned c1 = (unsigned)__builtin_amdgcn_readlane((int)cb.y, src);
+        const unsigned c2 = (unsigned)__builtin_amdgcn_readlane((int)cb.z, src);
+        const unsigned c3 = (unsigned)__builtin_amdgcn_readlane((int)cb.w, src);
+        unsigned k = 0, cnt = c0;
+        if (rem > run + c0) {
+            run += c0;
+            k = 1;
+            cnt = c1;
+            if (rem > run + c1) {
+                run += c1;
+                k = 2;
+                cnt = c2;
+                if (rem > run + c2) {
+                    run += c2;
+                    k = 3;
+                    cnt = c3;
+                }
             }
-            run += cb[k];
         }
-        const unsigned long long fm = __ballot(selk >= 0);
-        const int src = __ffsll((long long)fm) - 1;
-        const unsigned bin = 4u * (unsigned)src + (unsigned)__builtin_amdgcn_readlane(selk, src);
-        rem -= (unsigned)__builtin_amdgcn_readlane((int)below, src);
-        cnt = (unsigned)__builtin_amdgcn_readlane((int)cnt, src);
-        if (wi == 2) {
-            p2 |= bin << sh;
-            m2 |= 255u << sh;
-        } else if (wi == 1) {
-            p1 |= bin << sh;
-            m1 |= 255u << sh;
-        } else {
-            p0 |= bin << sh;
-            m0 |= 255u << sh;
+        const unsigned sel = 4u * (unsigned)src + k;
+        rem -= run;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            below[i] = below[i] || (cand[i] && bin[i] < sel);
+            cand[i] = cand[i] && bin[i] == sel;
         }
-        if (cnt == rem) break;
-        if (d == 7 && n <= 65536) {  // digits 8 and 9 of ~index are 0xff for every key
-            p0 |= 0xffff0000u;
-            m0 |= 0xffff0000u;
-            d = 9;
-        }
+        ++c;
+        if (cnt == rem) break;  // every candidate left in the bin is a victim
     }
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int j = tid + NT * i;
-        const unsigned a2 = w2[i] & m2, a1 = w1[i] & m1, a0 = ~(unsigned)j & m0;
-        const bool le = a2 != p2 ? a2 < p2 : (a1 != p1 ? a1 < p1 : a0 <= p0);
-        drop[i] = j < n && le;
-    }
+    for (int i = 0; i < KPT; ++i) drop[i] = below[i] || cand[i];
 }
 
 // snap_head for prefixes of at most NT KPT positions whose votes are staged:
