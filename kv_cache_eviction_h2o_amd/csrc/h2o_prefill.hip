@@ -613,9 +613,10 @@ __global__ void __launch_bounds__(kSNT) snapkv_union_kernel(const SnapArgs a)
 
 // ------------------------------------------------------- SnapKV in one pass
 // Prompts up to kFusedP positions and observation windows of at most 32 rows:
-// one workgroup per (unit, query head) reads the unit's K once
-// (the two column-sum passes read it twice and hand the row statistics and
-// the votes over through memory).  Wave v holds the window rows' logits for
+// one workgroup per (unit, query head) streams the unit's K once (the two
+// column-sum passes read it twice and hand the row statistics and the votes
+// over through memory; the G workgroups of a unit share its K through L2,
+// see the id mapping below).  Wave v holds the window rows' logits for
 // keys 128 v .. 128 v + 127 in registers (8 tiles of 16 keys, the same
 // matrix-core products as the rows pass); the workgroup merges each row's
 // softmax maximum and sum over the waves in LDS, and each key's vote is the
