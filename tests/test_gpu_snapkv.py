@@ -89,6 +89,17 @@ def test_snapkv_opt_layer_full_shape():
     run_snapkv(w, WL.prompt_lengths(w), window=32, pool=7, keep=172, vote_units=[(0, 0), (5, 13), (7, 31)])
 
 
+def test_snapkv_gqa_layer_full_shape():
+    """The LLaMA-2-70B layer's prompts as the benchmark selects them (16 x 1024,
+    8 KV heads, groups of 8, window 32, pool 7, 20 % kept per head): every
+    unit's kept set against the oracle's selection of the GPU's votes, and the
+    votes of three sampled units against the oracle's column sums."""
+    w = WL.LLAMA_GQA
+    lens = WL.prompt_lengths(w)
+    keep = max(1, min(lens) // 5)
+    run_snapkv(w, lens, window=32, pool=7, keep=keep, vote_units=[(0, 0), (9, 3), (15, 7)])
+
+
 def test_snapkv_gqa_edge_cases():
     """G = 4 (each query head selected in its own workgroup, then the union):
     prompts no longer than the window, keep beyond the prefix, keep 0, pool 1."""
