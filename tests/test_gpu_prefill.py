@@ -79,6 +79,14 @@ def test_prefill_scores_opt_layer_full_shape_sampled():
     run_prefill(w, WL.prompt_lengths(w), units=[(0, 0), (3, 17), (7, 31)])
 
 
+def test_prefill_scores_gqa_layer_full_shape_sampled():
+    """The LLaMA-2-70B layer's prompts as the benchmark scores them (16 x 1024,
+    8 KV heads, groups of 8: the rows pass runs each group as two workgroups
+    of 4 heads), three units against the oracle element by element."""
+    w = WL.LLAMA_GQA
+    run_prefill(w, WL.prompt_lengths(w), units=[(0, 0), (9, 3), (15, 7)])
+
+
 def test_prefill_scores_then_decode_parity():
     # the GPU's prefill scores seed both sides of a decode parity run
     import parity
