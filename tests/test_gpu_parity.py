@@ -277,6 +277,12 @@ def test_int8_opt_layer_reduced_full_trace(fused):
     assert rep.evictions > 0
 
 
+def test_int8_opt_layer_full_shape_sampled_units():
+    # the benchmarked shape and launch configuration of the int8 variant
+    w = WL.OPT_LAYER_I8
+    P().run_parity(w, 160, units=[(0, 0), (3, 17), (7, 31), (5, 4)])
+
+
 def test_int8_paged_mixed():
     w = WL.PAGED_MIXED.scaled(kv_dtype="i8", batch=3, n_q_heads=4, n_kv_heads=4)
     P().run_parity(w, 30, lens=[300, 517, 1500])
@@ -324,6 +330,13 @@ def test_f16_moving_sum_opt_layer_reduced_full_trace(fused):
     w = WL.OPT_LAYER_F16.scaled(batch=2, n_q_heads=8, n_kv_heads=8)
     assert w.score_dtype == "f16" and 0 < w.score_decay < 1
     rep = P().run_parity(w, w.decode_steps if fused else 200, fused=fused)
+    assert rep.evictions > 0
+
+
+def test_f16_moving_sum_opt_layer_full_shape_sampled_units():
+    # the benchmarked shape and launch configuration of the binary16 variant
+    w = WL.OPT_LAYER_F16
+    rep = P().run_parity(w, 160, units=[(0, 0), (3, 17), (7, 31), (5, 4)])
     assert rep.evictions > 0
 
 
