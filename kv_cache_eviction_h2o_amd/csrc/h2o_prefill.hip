@@ -705,7 +705,8 @@ __device__ inline void select_small(const unsigned (&w2)[KPT], const unsigned (&
         const uint4 cb = reinterpret_cast<const uint4*>(h)[lane];
         const unsigned loc = cb.x + cb.y + cb.z + cb.w;
         const unsigned inc = wave_incl_scan(loc);
-        // the rem-th smallest candidate lies in the first lane whose prefix reaches rem
+        // the rem-th smallest candidate lies in the first lane whose prefix reaches
+        // rem (there is one: rem never exceeds the candidates left, lane 63's prefix)
         const int src = __ffsll((long long)__ballot(inc >= rem)) - 1;
         unsigned run = (unsigned)__builtin_amdgcn_readlane((int)(inc - loc), src);
         const unsigned c0 = (unsigned)__builtin_amdgcn_readlane((int)cb.x, src);
