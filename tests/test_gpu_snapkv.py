@@ -26,13 +26,15 @@ def gpu():
     _lib.load_library()
 
 
-def run_snapkv(w, lens, window, pool, keep, vote_units=None):
+def run_snapkv(w, lens, window, pool, keep, vote_units=None, zero_q=False):
     import torch
     from kv_cache_eviction_h2o_amd import _lib as L
     print(f"[snapkv] {w.name} B={len(lens)} Hq={w.n_q_heads} Hkv={w.n_kv_heads} lens={lens[:6]} "
-          f"window={window} pool={pool} keep={keep}", flush=True)
+          f"window={window} pool={pool} keep={keep}{' zero q' if zero_q else ''}", flush=True)
     K, _ = S.prompt_kv(w.recipe, 0, lens, w.n_kv_heads)
     Q = S.prompt_queries(w.recipe, 0, lens, w.n_q_heads)
+    if zero_q:
+        Q = np.zeros_like(Q)
     cfg = L.config_from_workload(w.scaled(batch=len(lens)), max_len=max(lens) + 1)
     kd = torch.from_numpy(np.ascontiguousarray(K).view(np.int16)).view(torch.bfloat16).cuda()
     kept, count, votes = L.snapkv_select(cfg, lens, torch.from_numpy(Q).cuda(), kd, window, pool, keep)
@@ -134,6 +136,23 @@ def test_snapkv_one_pass_groups(g):
     _, c = run_snapkv(w, [1024, 600, 33], window=32, pool=7, keep=60)
     assert np.all(c >= 32 + 1) and np.all(c <= 32 + g * 60)
     run_snapkv(w, [1023, 129, 1], window=31, pool=5, keep=40)
+
+
+@pytest.mark.parametrize("g,lens", [(1, [1024, 300]), (2, [700, 65]), (1, [1500, 40])])
+def test_snapkv_all_votes_tied(g, lens):
+    """Zero queries: every logit is 0, so every prefix position gets the same
+    vote (each window row spreads its weight evenly over its keys) and the
+    selection must keep the lowest positions, through every vote digit to the
+    position digits.  The one-pass path (prompts up to 1024) and the two-pass
+    path (1500)."""
+    w = WL.LLAMA_GQA.scaled(n_q_heads=2 * g, n_kv_heads=2)
+    keep = 50
+    kept, count = run_snapkv(w, lens, window=32, pool=5, keep=keep, zero_q=True)
+    for b, P in enumerate(lens):
+        wb = min(32, P)
+        want = list(range(min(keep, P - wb))) + list(range(P - wb, P))
+        for h in range(2):
+            assert list(kept[b, h, :count[b, h]]) == want, (b, h)
 
 
 @pytest.mark.parametrize("g", [1, 4])
