@@ -104,7 +104,7 @@ def _oracle_threads(n_units: int) -> int:
 
 def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=True, layer=0,
                init_scores=None, read_every=1, check_steps=(), check_scores=True, device_inputs=False,
-               stored_rows=True, properties=False, max_swapped=None) -> ParityReport:
+               stored_rows=True, properties=False, max_swapped=None, zero_q=False) -> ParityReport:
     """Run n_steps on the GPU and in the oracle (for `units`, default all).
 
     Checked steps: every read_every-th, those in check_steps, and the last.
@@ -118,6 +118,9 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
     oracle's victims under the near-tie rule (a check stricter than the rule:
     when scores are far below the absolute gap, as after the bulk first step of
     long prompts, the rule alone would accept any candidate).
+    zero_q: every decode query is zero, so every step weighs its slots equally
+    and tokens present over the same steps hold exactly equal scores (the
+    tie rule decides).
     The oracle steps its units on POSIX threads (orc_step_many) between checked
     steps, and attends them on a thread pool at checked steps."""
     import torch
@@ -129,6 +132,7 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
         f"steps={n_steps} fused={fused} units={'all' if units is None else len(units)}")
     off = np.concatenate([[0], np.cumsum(lens)])
     units = [(b, h) for b in range(B) for h in range(Hkv)] if units is None else list(units)
+    assert not (zero_q and device_inputs)
     if device_inputs:
         from kv_cache_eviction_h2o_amd import _lib as L
         from kv_cache_eviction_h2o_amd import metrics as M
@@ -171,6 +175,8 @@ def run_parity(w: WL.Workload, n_steps: int, *, lens=None, units=None, fused=Tru
             q, k, v = qd.cpu().numpy(), _host_bits(kd), _host_bits(vd)
         else:
             q, k, v = S.step_window(w.recipe, layer, t0, ns, Hq, Hkv)
+            if zero_q:
+                q = np.zeros_like(q)
             qd = torch.from_numpy(q).cuda()
             kd, vd = to_dev(k, w.recipe.kv_dtype), to_dev(v, w.recipe.kv_dtype)
         gen_k.append(k)
@@ -307,6 +313,7 @@ def run_block_parity(w: WL.Workload, n_steps: int, *, lens=None, seqs=None, fuse
     say(f"[block parity] {w.name} B={B} Hq={Hq} Hkv={Hkv} lens={lens[:6]}{'...' if B > 6 else ''} "
         f"steps={n_steps} fused={fused} seqs={seqs if len(seqs) <= 8 else len(seqs)}")
     off = np.concatenate([[0], np.cumsum(lens)])
+    assert not (zero_q and device_inputs)
     if device_inputs:
         from kv_cache_eviction_h2o_amd import _lib as L
         pk, pv = S.device_prompt_kv(w.recipe, layer, lens, Hkv)
@@ -342,6 +349,8 @@ def run_block_parity(w: WL.Workload, n_steps: int, *, lens=None, seqs=None, fuse
             q, k, v = qd.cpu().numpy(), _host_bits(kd), _host_bits(vd)
         else:
             q, k, v = S.step_window(w.recipe, layer, t0, ns, Hq, Hkv)
+            if zero_q:
+                q = np.zeros_like(q)
             qd = torch.from_numpy(q).cuda()
             kd, vd = to_dev(k, w.recipe.kv_dtype), to_dev(v, w.recipe.kv_dtype)
         gen_k.append(k)

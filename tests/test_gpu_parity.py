@@ -152,6 +152,22 @@ def test_budget_above_length_is_full_attention():
     assert rep.evictions == 0
 
 
+@pytest.mark.parametrize("wname", ["tiny_fma", "gqa_matrix_core"])
+def test_exactly_tied_scores(wname):
+    """Zero queries: every step weighs its slots equally, so every prompt token
+    reaches the bulk first step with exactly the same score and the tie rule
+    alone (equal scores: the lower position is kept) decides which of them
+    stay; later steps keep ties among tokens present over the same steps.
+    Every step is checked against the oracle, and no near-tie may be adopted:
+    the victim sets must be the oracle's exactly."""
+    if wname == "tiny_fma":
+        w = WL.TINY_H2O.scaled(batch=2)
+    else:
+        w = WL.LLAMA_GQA.scaled(batch=2, n_q_heads=16, n_kv_heads=2, budget_fixed=96, hh_fixed=40)
+    rep = P().run_parity(w, 40, lens=[300, 257], zero_q=True)
+    assert rep.evictions > 0 and rep.adopted == 0
+
+
 def test_ragged_prompts_fixed_budget():
     w = WL.TINY_H2O.scaled(batch=4)
     rep = P().run_parity(w, 80, lens=[20, 63, 64, 150])
