@@ -313,7 +313,6 @@ def run_block_parity(w: WL.Workload, n_steps: int, *, lens=None, seqs=None, fuse
     say(f"[block parity] {w.name} B={B} Hq={Hq} Hkv={Hkv} lens={lens[:6]}{'...' if B > 6 else ''} "
         f"steps={n_steps} fused={fused} seqs={seqs if len(seqs) <= 8 else len(seqs)}")
     off = np.concatenate([[0], np.cumsum(lens)])
-    assert not (zero_q and device_inputs)
     if device_inputs:
         from kv_cache_eviction_h2o_amd import _lib as L
         pk, pv = S.device_prompt_kv(w.recipe, layer, lens, Hkv)
@@ -349,8 +348,6 @@ def run_block_parity(w: WL.Workload, n_steps: int, *, lens=None, seqs=None, fuse
             q, k, v = qd.cpu().numpy(), _host_bits(kd), _host_bits(vd)
         else:
             q, k, v = S.step_window(w.recipe, layer, t0, ns, Hq, Hkv)
-            if zero_q:
-                q = np.zeros_like(q)
             qd = torch.from_numpy(q).cuda()
             kd, vd = to_dev(k, w.recipe.kv_dtype), to_dev(v, w.recipe.kv_dtype)
         gen_k.append(k)
