@@ -125,6 +125,12 @@ def test_snapkv_one_pass_bounds():
     assert list(c[:, 0]) == [501, 2]
     run_snapkv(w, [1025, 1024], window=32, pool=7, keep=100)
     run_snapkv(w, [1024, 600], window=33, pool=7, keep=100)
+    # selection boundaries: one prefix position dropped (P = 100: prefix 68,
+    # keep 67), none (keep = the prefix), and a prefix shorter than keep
+    _, c = run_snapkv(w, [100, 64], window=32, pool=3, keep=67)
+    assert list(c[:, 0]) == [99, 64]
+    _, c = run_snapkv(w, [100, 1024], window=32, pool=3, keep=68)
+    assert list(c[:, 0]) == [100, 100]
 
 
 @pytest.mark.parametrize("g", [2, 8])
