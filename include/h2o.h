@@ -287,7 +287,9 @@ void h2o_destroy(h2o_ctx *ctx);
  * hipMallocAsync on `stream` when a call needs more and held until the
  * process ends.  Calls on one device are ordered through it: a call on
  * another stream than the previous call makes its stream wait for the
- * previous call's work.  Errors: H2O_EINVAL,
+ * previous call's work.  A SnapKV call that runs in one pass (every P_b <=
+ * 1024, w_b <= 32) with G = 1 and the caller's votes uses no scratch and
+ * takes no part in this ordering.  Errors: H2O_EINVAL,
  * H2O_ENOMEM, H2O_EDEVICE; the message is h2o_last_error(NULL). */
 int h2o_prefill_scores(const h2o_config *cfg, const int32_t *prompt_len, const float *prompt_q,
                        const void *prompt_k, double *out, void *stream);

@@ -681,11 +681,15 @@ int snapkv_run(const h2o_config* cfg, const int32_t* plen, int window, int pool,
     SnapPlan pl;
     int rc = snapkv_plan(cfg, plen, window, pool, keep, q, k, votes, kept, count, cap, pl);
     if (rc != H2O_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (pl.scratch_bytes() == 0) {  // one pass into the caller's votes: no scratch, nothing to order
+        const hipError_t e = snapkv_enqueue(pl, votes, nullptr, st);
+        return e == hipSuccess ? H2O_OK : hip_fail(nullptr, e, "SnapKV: launch");
+    }
     std::string why;
     PromptScratch* ps = prompt_scratch(why);
     if (!ps) return fail(nullptr, H2O_EDEVICE, why);
     std::lock_guard<std::mutex> lk(ps->mu);
-    hipStream_t st = (hipStream_t)stream;
     char* sp = nullptr;
     hipError_t e = scratch_take(*ps, pl.scratch_bytes(), st, &sp);
     if (e != hipSuccess) return hip_fail(nullptr, e, "SnapKV: scratch");
