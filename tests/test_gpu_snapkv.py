@@ -131,6 +131,10 @@ def test_snapkv_one_pass_bounds():
     assert list(c[:, 0]) == [99, 64]
     _, c = run_snapkv(w, [100, 1024], window=32, pool=3, keep=68)
     assert list(c[:, 0]) == [100, 100]
+    # the most sequences a call takes (128), ragged, one KV head each
+    w1 = WL.OPT_LAYER.scaled(n_q_heads=1, n_kv_heads=1)
+    lens = [33 + (37 * b) % 200 for b in range(128)]
+    run_snapkv(w1, lens, window=32, pool=5, keep=20)
 
 
 @pytest.mark.parametrize("g", [2, 8])
