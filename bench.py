@@ -530,6 +530,36 @@ def prefill_main(args, w):
     print(json.dumps(line), flush=True)
 
 
+def copy_probe(args, dev) -> None:
+    """--copy-probe-mib: one device-to-device copy of that many MiB, the
+    calibration a counter run (FETCH_SIZE, WRITE_SIZE) scales its counts by."""
+    import torch
+    if not args.copy_probe_mib:
+        return
+    n = args.copy_probe_mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    bcp = torch.empty_like(a)
+    torch.cuda.synchronize()
+    bcp.copy_(a)
+    torch.cuda.synchronize()
+    del a, bcp
+
+
+def snapkv_traffic(wname: str):
+    """Measured HBM bytes per h2o_snapkv_select call for this workload's
+    prompts, from a committed counter summary taken on the current prompt
+    kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"h2o_snapkv_kernels_{wname}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_hash(prompt=True):
+        return None
+    return float(t.group(1))
+
+
 def snapkv_main(args, w):
     """--snapkv: h2o_snapkv_select over the workload's prompts (one layer)."""
     import torch
@@ -559,6 +589,7 @@ def snapkv_main(args, w):
         if rc != 0:
             raise L.H2OError(rc, lib.h2o_last_error(None).decode())
 
+    copy_probe(args, dev)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -585,6 +616,17 @@ def snapkv_main(args, w):
     alu = Hq * rows * (FUSED_SNAP_OPS_PER_SCORE if one_kernel else ROWS_OPS_PER_SCORE + COLS_OPS_PER_SCORE)
     nbytes = (sum(min(window, P) for P in lens) * Hq * D * 4 + tokens * (Hkv * D * 2 + Hq * 8)
               + B * Hkv * cap * 4 + B * 4)  # window q, K, votes, kept positions and counts
+    roof = call_roofline(
+        nbytes, flops, per_call,
+        "whole call; algorithmic bytes = the window rows' fp32 q, bf16 K, the fp64 votes and the kept "
+        "positions once; algorithmic flops = the window rows' causal logits once; ALU = the window rows' "
+        + ("scores once at 10 lane-operation equivalents (one pass)" if one_kernel else
+           "scores in both passes at 11 + 8.75 lane-operation equivalents")
+        + "; the call also pools and selects", alu_ops=alu)
+    tr = snapkv_traffic(w.name)  # FETCH_SIZE + WRITE_SIZE of the call's kernels, from profiles/
+    if tr is not None:
+        roof["traffic"] = round(tr)
+        roof["traffic_over_algorithmic"] = round(tr / nbytes, 4)
     line = {
         "metric": "prompt tokens selected/sec (SnapKV, h2o_snapkv_select)",
         "value": round(tokens / per_call, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -595,13 +637,7 @@ def snapkv_main(args, w):
                    "prompt_lens": lens if len(set(lens)) > 1 else lens[0], "window": window, "pool": pool,
                    "keep_per_head": keep, "mean_kept": round(float(c.mean()), 1),
                    "entry_point": "h2o_snapkv_select", "parallelism": "single GPU"},
-        "roofline": call_roofline(
-            nbytes, flops, per_call,
-            "whole call; algorithmic bytes = the window rows' fp32 q, bf16 K, the fp64 votes and the kept "
-            "positions once; algorithmic flops = the window rows' causal logits once; ALU = the window rows' "
-            + ("scores once at 10 lane-operation equivalents (one pass)" if one_kernel else
-               "scores in both passes at 11 + 8.75 lane-operation equivalents")
-            + "; the call also pools and selects", alu_ops=alu),
+        "roofline": roof,
         "cpu_baseline": (None if args.no_cpu_baseline
                          else snapkv_cpu_baseline(w, lens, window, pool, keep, args.cpu_seconds)),
         "kernel_source_sha256_16": kernel_hash(prompt=True),
@@ -685,14 +721,7 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        bcp = torch.empty_like(a)
-        torch.cuda.synchronize()
-        bcp.copy_(a)
-        torch.cuda.synchronize()
-        del a, bcp
+    copy_probe(args, dev)
 
     # ---- timed region
     events = args.events

@@ -123,3 +123,13 @@ def test_summary_records_window_and_traffic_scales_to_the_line(tmp_path, capsys,
     from kv_cache_eviction_h2o_amd import workloads as WL
     tr = bench.traffic_from_profiles(WL.PAGED_MIXED, 2000.0)
     assert abs(tr["ratio"] - 1.1) < 1e-9 and abs(tr["bytes"] - 2200.0) < 1e-6 and tr["window"] == [6, 9]
+
+
+def test_snapkv_traffic_only_for_the_current_prompt_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.snapkv_traffic("w") is None  # no summary
+    f = tmp_path / "h2o_snapkv_kernels_w_counters.md"
+    f.write_text(f"kernel_source_sha256_16: {bench.kernel_hash(prompt=True)}\nhbm_bytes_per_call: 8.5e+07\n")
+    assert bench.snapkv_traffic("w") == 8.5e7
+    f.write_text(f"kernel_source_sha256_16: {bench.kernel_hash()}\nhbm_bytes_per_call: 8.5e+07\n")
+    assert bench.snapkv_traffic("w") is None  # taken on other sources
