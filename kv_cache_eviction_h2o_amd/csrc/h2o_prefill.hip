@@ -820,9 +820,20 @@ __global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs 
     // serve unit 8 c + u, so the G workgroups of a unit reach the same XCD
     // (ids go to the XCDs round-robin) and are dispatched together, and the
     // unit's K, read by each of them, comes from that XCD's L2 after the first
-    const int id = blockIdx.x, c8 = id / (8 * a.G), r8 = id - c8 * 8 * a.G;
-    const int g = r8 >> 3, unit = 8 * c8 + (r8 & 7);
-    if (unit >= a.units) return;  // the last group of 8 units may be partial
+    // (groups of one head: ids 64 c + 8 u + v serve unit 64 c + 8 v + u, so the 8
+    // consecutive units whose votes share 64-byte segments of a vote row write
+    // them from one XCD, whose L2 merges the 8-byte pieces into whole lines)
+    const int id = blockIdx.x;
+    int g, unit;
+    if (a.G == 1) {
+        g = 0;
+        unit = (id & ~63) + 8 * (id & 7) + ((id >> 3) & 7);
+    } else {
+        const int c8 = id / (8 * a.G), r8 = id - c8 * 8 * a.G;
+        g = r8 >> 3;
+        unit = 8 * c8 + (r8 & 7);
+    }
+    if (unit >= a.units) return;  // the last group of units may be partial
     const int b = unit / a.Hkv, h = unit - b * a.Hkv, hq = h * a.G + g;
     const int P = a.seq_p[b], lo = P - a.seq_w[b];  // window rows [lo, P); prefix [0, lo)
     const int64_t off = a.seq_off[b];
@@ -1116,8 +1127,10 @@ hipError_t launch_snapkv_fused(const ColsumArgs& ca, const SnapArgs& sa, double*
         f.seq_w[b] = sa.seq_w[b];
         f.seq_off[b] = sa.seq_off[b];
     }
-    const unsigned groups = (unsigned)((f.units + 7) / 8);  // of 8 units, each 8 G workgroups
-    hipLaunchKernelGGL(snapkv_fused_kernel, dim3(groups * 8u * (unsigned)sa.G), dim3(kFNT), 0, st, f);
+    // G = 1: groups of 64 units; else groups of 8 units, each 8 G workgroups
+    const unsigned wgs = sa.G == 1 ? (unsigned)((f.units + 63) / 64) * 64u
+                                   : (unsigned)((f.units + 7) / 8) * 8u * (unsigned)sa.G;
+    hipLaunchKernelGGL(snapkv_fused_kernel, dim3(wgs), dim3(kFNT), 0, st, f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sa.G == 1) return e;
     return launch_snap_union(sa, st);
