@@ -806,7 +806,10 @@ struct SnapFusedArgs {
     int64_t seq_off[kMaxArgBatch];
 };
 
-__global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs a)
+// Two workgroups per CU (at most 128 VGPRs: the q operands are read from LDS
+// for each tile, and two K tiles are in flight per wave), so that one
+// workgroup's selection overlaps another's K stream.
+__global__ void __launch_bounds__(kFNT, 4) snapkv_fused_kernel(const SnapFusedArgs a)
 {
     __shared__ uint4 qsm[kFQT][4][64];      // A operands of the window rows (hi / lo parts)
     __shared__ uint4 ktr[kFNT / 64][256];    // per wave: a K tile on its way to B-operand order
@@ -887,11 +890,9 @@ __global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs 
         for (int kb = 0; kb < 4; ++kb) bt[kb] = as_bf16x8(kw[swz(64 * kb + lane)]);
         wave_lds_sync();  // the next tile's writes after these reads
     };
-    uint4 kt0[4], kt1[4], kt2[4], kt3[4];  // four tiles in flight per wave
+    uint4 kt0[4], kt1[4];  // two tiles in flight per wave
     if (nt > 0) fetch(0, kt0);
     if (nt > 1) fetch(1, kt1);
-    if (nt > 2) fetch(2, kt2);
-    if (nt > 3) fetch(3, kt3);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int v = qv[i], ln = v & 63;
@@ -904,22 +905,17 @@ __global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs 
         (&qsm[0][0][0])[v] = as_u4(o);
     }
     lds_barrier();
-    bf16x8 qop[kFQT][4];
-#pragma unroll
-    for (int tq = 0; tq < kFQT; ++tq)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qop[tq][kb] = as_bf16x8(qsm[tq][kb][lane]);
 
     // logits: s[x][tq][r] = row lo + 8 tq + 2 lg + r against key key0 + 16 x + lc,
     // kMaskLogit after the row (causal), past P, or on a tile past P
     float s[kFKT][kFQT][2];
 #pragma unroll
     for (int x = 0; x < kFKT; ++x) {
-        uint4(&cur)[4] = (x & 3) == 0 ? kt0 : (x & 3) == 1 ? kt1 : (x & 3) == 2 ? kt2 : kt3;
+        uint4(&cur)[4] = (x & 1) ? kt1 : kt0;
         if (x < nt) {
             bf16x8 bt[4];
             put_k(cur);
-            if (x + 4 < nt) fetch(x + 4, cur);
+            if (x + 2 < nt) fetch(x + 2, cur);
             get_b(bt);
             const int key = key0 + 16 * x + lc;
             // only a tile reaching past the window's first row holds keys after
@@ -930,7 +926,7 @@ __global__ void __launch_bounds__(kFNT) snapkv_fused_kernel(const SnapFusedArgs 
             for (int tq = 0; tq < kFQT; ++tq) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) c = mma(qop[tq][kb], bt[kb], c);
+                for (int kb = 0; kb < 4; ++kb) c = mma(as_bf16x8(qsm[tq][kb][lane]), bt[kb], c);
                 const int pos0 = lo + 8 * tq + 2 * lg;
                 s[x][tq][0] = c[0] + c[1];
                 s[x][tq][1] = c[2] + c[3];
