@@ -289,3 +289,32 @@ def test_snapkv_select_rejects_before_device(lib, kw, msg):
     cfg = L.make_config(**GOOD)
     assert _snap(lib, cfg, [100, 200], **kw) == L.H2O_EINVAL
     assert msg in lib.h2o_last_error(None).decode()
+
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,P,Hq,Hkv", [(8, 16384, 32, 32), (128, 1024, 64, 8)])
+def test_snapkv_noalloc_scratch_need_matches_the_header(lib, B, P, Hq, Hkv):
+    """h2o_snapkv_select_noalloc refuses, on the host and before any device
+    call, a call whose scratch need passes the fixed 64 MiB, and names the
+    need: with the votes in scratch it is 8 sum P Hq bytes, plus the per-head
+    kept bitmaps for groups, plus -- unless the call runs in one pass (every
+    prompt up to 1024 positions, window up to 32) -- the pooled votes and the
+    column-sum passes' window q tiles and row statistics (4160 B Hkv G T)."""
+    G, w = Hq // Hkv, 32
+    cfg = L.make_config(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=128, kv_dtype="bf16",
+                        score_dtype="f32", budget_fixed=64, hh_fixed=28, max_len=P + 1)
+    arr = (C.c_int32 * B)(*([P] * B))
+    p = C.c_void_p(256)  # never touched: the size check comes before anything is enqueued
+    rc = lib.h2o_snapkv_select_noalloc(C.byref(cfg), arr, w, 7, 100, p, p, None, p, p, P, None)
+    assert rc == L.H2O_EINVAL
+    msg = lib.h2o_last_error(None).decode()
+    need = _align256(8 * B * P * Hq)  # the votes
+    if G > 1:
+        need += _align256(4 * B * Hq * ((P + 127) // 128 * 4))
+    if P > 1024:
+        T = (P + 7) // 8 - (P - w) // 8
+        need += _align256(8 * B * P * Hq) + _align256(B * Hkv * T * G * 256 * 16) + _align256(B * Hkv * T * G * 64)
+    assert need > 64 << 20 and f"needs {need} bytes" in msg, (need, msg)
